@@ -1,0 +1,11 @@
+"""CPU oracle for the Sherry 1.25-bit ternary format and its products.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
+leg of the benchmark may import this package.  The GPU library never uses it,
+and this package imports nothing from the GPU library.
+
+Plain, slow, obviously correct: numpy in fp64 (exact integers) with pure-Python
+loops kept to the small reference routines.  See ``sherry_ref`` for the 3:4
+format and ``tern2_ref`` for the 2-bit dense-ternary comparator.
+"""
+from . import sherry_ref, tern2_ref  # noqa: F401

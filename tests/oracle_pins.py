@@ -1,0 +1,319 @@
+"""Pins for the CPU oracle: checks against facts fixed outside the oracle.
+
+Each ``pin_*`` function takes the oracle module (``oracle.sherry_ref`` or a copy
+with a planted mistake) and raises AssertionError when the module disagrees
+with a fact that does not come from the oracle itself:
+  * the counting argument of the format (4 zero slots x 8 sign patterns = 32
+    codes; Sherry paper, Abstract: four weights in five bits);
+  * the code table and packed words derived by hand from the layout readings
+    R2/R3 (derivations written next to each literal);
+  * closed forms (all-ones x, one-hot x, sign flip, linearity);
+  * brute-force loops over the generator's dense ternary matrix, which never
+    passes through the oracle's decoder;
+  * brute-force optimality of the packer over all 32 codes;
+  * exact rational arithmetic for the fp32 / fp16 epilogue rounding.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "sherry_format_hand.txt")
+
+
+def _load_hand_fixture(path=GOLDEN):
+    """Parse tests/golden/sherry_format_hand.txt (hand-derived, see its header)."""
+    sec, table, groups, dots, straddle = None, {}, {}, {}, ()
+    with open(path) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            if line.startswith("["):
+                sec = line.strip("[]")
+                continue
+            tok = line.split()
+            if sec == "table":
+                table[int(tok[0])] = (tuple(int(v) for v in tok[1:5]), int(tok[5], 16))
+            elif sec == "groups":
+                kind = tok[1]
+                codes = {"ramp": list(range(32)), "ramp_down": [31 - j for j in range(32)],
+                         "const0": [0] * 32, "const31": [31] * 32}[kind]
+                groups[tok[0]] = (codes, [int(v, 16) for v in tok[2:7]])
+            elif sec == "dot":
+                dots[tok[0]] = int(tok[1])
+            elif sec == "straddle":
+                straddle = tuple(int(v) for v in tok)
+    assert sorted(table) == list(range(32)) and len(groups) == 4
+    for c, (blk, dw) in table.items():  # the two columns of a row agree
+        assert sum((v & 0xFF) << (8 * i) for i, v in enumerate(blk)) == dw, c
+    return table, groups, dots, straddle
+
+
+_TABLE, HAND_GROUPS, _DOTS, STRADDLING_CODES = _load_hand_fixture()
+HAND_BLOCKS = {c: b for c, (b, _) in _TABLE.items()}
+HAND_DWORDS = [_TABLE[c][1] for c in range(32)]
+RAMP_DOT = _DOTS["ramp"]
+
+
+def dword_of(block) -> int:
+    return sum((int(v) & 0xFF) << (8 * i) for i, v in enumerate(block))
+
+
+def all_blocks():
+    """The 32 valid blocks, enumerated without the oracle: zero slot x signs."""
+    out = []
+    for z in range(4):
+        for signs in itertools.product((1, -1), repeat=3):
+            b = list(signs)
+            b.insert(z, 0)
+            out.append(tuple(b))
+    return out
+
+
+# ----------------------------------------------------------------- format ---
+
+def pin_bijection(ref):
+    decoded = [tuple(ref.decode_block(c)) for c in range(32)]
+    assert len(set(decoded)) == 32, "decode is not injective"
+    assert set(decoded) == set(all_blocks()), "decoded set != the 32 valid 3:4 blocks"
+    for b in decoded:
+        assert b.count(0) == 1 and all(v in (-1, 0, 1) for v in b)
+    for b in all_blocks():
+        c = ref.encode_block(b)
+        assert 0 <= c < 32 and tuple(ref.decode_block(c)) == b
+
+
+def pin_code_table(ref):
+    for c, b in HAND_BLOCKS.items():
+        assert tuple(ref.decode_block(c)) == b, f"code {c}"
+    for c in range(32):
+        assert dword_of(ref.decode_block(c)) == HAND_DWORDS[c], f"code {c}"
+    # vectorised decoder agrees with the hand table
+    codes = np.arange(32, dtype=np.uint8)[None, :]
+    dense = ref.dense_from_codes(codes).reshape(32, 4)
+    for c in range(32):
+        assert dword_of(dense[c]) == HAND_DWORDS[c], f"vectorised code {c}"
+
+
+def pin_packed_groups(ref):
+    for name, (codes, words) in HAND_GROUPS.items():
+        assert list(ref.pack_group(codes)) == words, name
+        assert list(ref.unpack_group(words)) == codes, name
+        v = ref.pack_codes(np.array(codes, dtype=np.uint8)[None, :])
+        assert [int(w) for w in v] == words, f"vectorised pack {name}"
+        u = ref.unpack_codes(np.array(words, dtype=np.uint32), 1, 128)
+        assert [int(c) for c in u[0]] == codes, f"vectorised unpack {name}"
+
+
+def pin_straddles(ref):
+    """A code straddles two words iff flipping it changes two words."""
+    found = []
+    for j in range(32):
+        codes = [0] * 32
+        codes[j] = 31
+        words = ref.pack_group(codes)
+        if sum(1 for w in words if w) == 2:
+            found.append(j)
+    assert tuple(found) == STRADDLING_CODES
+
+
+def pin_size(ref):
+    for n, k in [(1, 128), (3, 256), (256, 1024), (2048, 8192)]:
+        assert ref.packed_bytes(n, k) * 8 == n * k * 5 // 4  # 1.25 bits per weight
+    g = synth.rng(7)
+    t = synth.ternary_34(5, 384, g)
+    words = ref.pack_codes(ref.codes_from_dense(t))
+    assert words.dtype == np.uint32 and words.nbytes == 5 * 384 * 5 // 32
+
+
+def pin_ramp_dot(ref):
+    x = np.array([(k % 127) - 63 for k in range(128)], dtype=np.int8)
+    words = np.array(HAND_GROUPS["ramp"][1], dtype=np.uint32)
+    acc, _ = ref.gemv_i8(words, np.ones(1, np.float32), 1, 128, x, None, np.float32)
+    assert int(acc[0]) == RAMP_DOT
+
+
+# ---------------------------------------------------------- closed forms ---
+
+def pin_closed_forms(ref):
+    g = synth.rng(11)
+    n, k = 37, 384
+    words = synth.random_words(n * (k // 128) * 5, g)
+    codes = ref.unpack_codes(words, n, k)
+    sw = np.ones(n, np.float32)
+    # x = 1: each block adds (#plus - #minus) = 3 - 2 * popcount(sign bits)
+    acc1, _ = ref.gemv_i8(words, sw, n, k, np.ones(k, np.int8), None, np.float32)
+    pop = np.array([[bin(int(c) >> 2).count("1") for c in row] for row in codes])
+    assert np.array_equal(acc1, (3 - 2 * pop).sum(axis=1))
+    # x = e_k picks column k of the matrix: bitstream slice + hand table
+    for col in (0, 1, 2, 3, 127, 128, 255, 383):
+        e = np.zeros(k, np.int8)
+        e[col] = 1
+        acc, _ = ref.gemv_i8(words, sw, n, k, e, None, np.float32)
+        for r in range(n):
+            grp = [int(words[(r * (k // 128) + col // 128) * 5 + i]) for i in range(5)]
+            v = 0
+            for i, w in enumerate(grp):
+                v |= w << (32 * i)
+            c = (v >> (5 * ((col % 128) // 4))) & 31
+            byte = (HAND_DWORDS[c] >> (8 * (col % 4))) & 0xFF  # hand table, not the decoder
+            want = byte - 256 if byte > 127 else byte
+            assert int(acc[r]) == want, (r, col)
+    # flipping every sign bit negates the product
+    x = synth.x_int8_uniform(k, g)
+    flipped = ref.pack_codes(codes ^ np.uint8(0b11100))
+    a, _ = ref.gemv_i8(words, sw, n, k, x, None, np.float32)
+    b, _ = ref.gemv_i8(flipped, sw, n, k, x, None, np.float32)
+    assert np.array_equal(a, -b)
+    # linearity in x (values kept inside int8)
+    x1 = (x // 2).astype(np.int8)
+    x2 = (x - x1).astype(np.int8)
+    a1, _ = ref.gemv_i8(words, sw, n, k, x1, None, np.float32)
+    a2, _ = ref.gemv_i8(words, sw, n, k, x2, None, np.float32)
+    assert np.array_equal(a, a1 + a2)
+
+
+# ------------------------------------------------------------ brute force ---
+
+def naive_gemm(t, x):
+    """Triple loop: acc[m][r] = sum_k x[m][k] * t[r][k] (pure Python ints)."""
+    m, n, k = len(x), len(t), len(t[0])
+    return [[sum(int(x[i][c]) * int(t[r][c]) for c in range(k)) for r in range(n)] for i in range(m)]
+
+
+def pin_brute_force(ref):
+    g = synth.rng(23)
+    for n, k, m in [(1, 128, 1), (3, 128, 2), (7, 256, 5), (64, 128, 1)]:
+        t = synth.ternary_34(n, k, g)  # generator's dense T, never decoded by the oracle
+        words = ref.pack_codes(ref.codes_from_dense(t))
+        x = synth.x_int8_uniform((m, k), g)
+        want = naive_gemm(t.tolist(), x.tolist())
+        sw = np.ones(n, np.float32)
+        acc, _ = ref.gemm_i8(words, sw, n, k, x, np.ones(m, np.float32), np.float32)
+        assert acc.shape == (m, n)
+        assert acc.tolist() == want, (n, k, m)
+        a1, _ = ref.gemv_i8(words, sw, n, k, x[0], None, np.float32)
+        assert a1.tolist() == want[0]
+
+
+def pin_packer(ref):
+    g = synth.rng(31)
+    # brute force: the packed code minimises ||w - a * dec(c)||^2 over all 32 codes
+    for _ in range(300):
+        w4 = g.standard_normal(4)
+        a = float(g.uniform(0.05, 2.0))
+        c = ref.quantize_block(w4)
+        cost = [sum((w4[i] - a * v) ** 2 for i, v in enumerate(b)) for b in (ref.decode_block(cc) for cc in range(32))]
+        assert cost[c] <= min(cost) + 1e-12
+    # ties go to the lowest slot; -0.0 counts as positive
+    assert ref.decode_block(ref.quantize_block([0.5, -0.5, 0.5, 0.5])) == (0, -1, 1, 1)
+    assert ref.decode_block(ref.quantize_block([1.0, 0.25, -0.25, 2.0])) == (1, 0, -1, 1)
+    assert ref.decode_block(ref.quantize_block([-0.0, 0.0, 1.0, -1.0])) == (0, 1, 1, -1)
+    # the row scale is the least-squares scale: perturbing it raises the error
+    n, k = 6, 256
+    w = g.standard_normal((n, k))
+    codes, alpha = ref.quantize(w)
+    t = np.array([[v for c in row for v in ref.decode_block(int(c))] for row in codes], dtype=np.float64)
+    for r in range(n):
+        err = lambda s: float(np.sum((w[r] - s * t[r]) ** 2))  # noqa: E731
+        assert err(alpha[r]) < err(alpha[r] * (1 + 1e-3)) and err(alpha[r]) < err(alpha[r] * (1 - 1e-3))
+        assert math.isclose(alpha[r], float(np.sum(np.abs(w[r]) * (t[r] != 0))) / (3 * k // 4), rel_tol=1e-14)
+    # pack(s * T) recovers T and s exactly (fp32 s; fp64 sums of equal values are exact)
+    t34 = synth.ternary_34(9, 512, g)
+    s = synth.row_scales(9, g, np.float32)
+    words, scales = ref.pack((t34 * s[:, None]).astype(np.float32), np.float32)
+    assert np.array_equal(ref.unpack(words, 9, 512), t34)
+    assert np.array_equal(scales, s)
+
+
+# -------------------------------------------------------- exact rounding ---
+
+def round_to_float(q: Fraction, mant_bits: int, emin: int, emax: int) -> Fraction:
+    """Round a rational to the nearest binary float with ``mant_bits``
+    significant bits (ties to even), normal exponent range [emin, emax];
+    subnormals below emin.  Overflow returns +-inf as a float."""
+    if q == 0:
+        return Fraction(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    e = max(e, emin)
+    ulp = Fraction(2) ** (e - mant_bits + 1)
+    m = a / ulp
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    r = fl * ulp
+    if r >= Fraction(2) ** (emax + 1):
+        return float("inf") * sign
+    return sign * r
+
+
+def f32_exact(q):
+    return round_to_float(Fraction(q), 24, -126, 127)
+
+
+def f16_exact(q):
+    return round_to_float(Fraction(q), 11, -14, 15)
+
+
+def pin_epilogue(ref):
+    g = synth.rng(41)
+    acc = g.integers(-780288, 780289, size=400).astype(np.int32)
+    acc[:4] = [0, 1, -1, 780288]
+    sw = synth.row_scales(400, g, np.float16)
+    sx = np.float32(g.uniform(0.005, 0.05))
+    y = ref.epilogue(acc, sw, sx, np.float16)
+    for i in range(400):
+        t = f32_exact(Fraction(int(acc[i])) * Fraction(float(sw[i])))
+        t = f32_exact(t * Fraction(float(sx)))
+        assert Fraction(float(y[i])) == f16_exact(t), i
+    # inputs where rounding after every product differs from rounding once
+    # (found with numpy, confirmed with exact rationals before use)
+    cand_acc = g.integers(-780288, 780289, size=200000)
+    cand_sw = synth.row_scales(200000, g, np.float16)
+    cand_sx = g.uniform(0.005, 0.05, size=200000).astype(np.float32)
+    chain = ((cand_acc.astype(np.float32) * cand_sw.astype(np.float32)) * cand_sx).astype(np.float16)
+    once = (cand_acc.astype(np.float64) * cand_sw.astype(np.float64) * cand_sx.astype(np.float64)).astype(np.float16)
+    picked = np.nonzero(chain != once)[0][:40]
+    assert picked.size >= 5
+    for i in picked:
+        a, s1, s2 = int(cand_acc[i]), Fraction(float(cand_sw[i])), Fraction(float(cand_sx[i]))
+        want = f16_exact(f32_exact(f32_exact(Fraction(a) * s1) * s2))
+        assert want != f16_exact(Fraction(a) * s1 * s2)
+        got = ref.epilogue(np.array([a], np.int32), cand_sw[i:i + 1], cand_sx[i], np.float16)
+        assert Fraction(float(got[0])) == want, i
+    y32 = ref.epilogue(acc, sw.astype(np.float32), None, np.float32)
+    for i in range(400):
+        assert Fraction(float(y32[i])) == f32_exact(Fraction(int(acc[i])) * Fraction(float(sw[i]))), i
+
+
+def pin_bf16_path(ref):
+    g = synth.rng(43)
+    n, k = 9, 384
+    t = synth.ternary_34(n, k, g)
+    words = ref.pack_codes(ref.codes_from_dense(t))
+    xb = synth.x_bf16_normal(k, g)
+    sw = synth.row_scales(n, g, np.float32)
+    y = ref.gemv_bf16(words, sw, n, k, xb)
+    # bf16 -> value by the definition sign * (1 + m/128) * 2^(e - 127)
+    xv = []
+    for b in xb.tolist():
+        sgn = -1 if b >> 15 else 1
+        e = (b >> 7) & 0xFF
+        m = b & 0x7F
+        xv.append(Fraction(0) if e == 0 and m == 0 else sgn * (1 + Fraction(m, 128)) * Fraction(2) ** (e - 127))
+    for r in range(n):
+        exact = sum(int(t[r, c]) * xv[c] for c in range(k))
+        # one rounding of the exact sum to fp64, one for the scale product
+        assert y[r] == float(exact) * float(sw[r]), r

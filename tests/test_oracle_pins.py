@@ -1,0 +1,104 @@
+"""The CPU oracle against facts fixed outside it (see tests/oracle_pins.py)."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import sherry_ref, tern2_ref
+from tests import oracle_pins as P
+
+
+@pytest.mark.parametrize("pin", [
+    P.pin_bijection, P.pin_code_table, P.pin_packed_groups, P.pin_straddles, P.pin_size,
+    P.pin_ramp_dot, P.pin_closed_forms, P.pin_brute_force, P.pin_packer, P.pin_epilogue,
+    P.pin_bf16_path,
+], ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin(sherry_ref)
+
+
+def test_vectorised_matches_scalar_routines():
+    g = synth.rng(3)
+    n, k = 11, 640
+    words = synth.random_words(n * (k // 128) * 5, g)
+    codes = sherry_ref.unpack_codes(words, n, k)
+    for r in range(n):
+        for grp in range(k // 128):
+            w5 = words[(r * (k // 128) + grp) * 5:(r * (k // 128) + grp + 1) * 5]
+            assert sherry_ref.unpack_group(w5) == codes[r, grp * 32:(grp + 1) * 32].tolist()
+    assert np.array_equal(sherry_ref.pack_codes(codes), words)
+    dense = sherry_ref.dense_from_codes(codes)
+    for r in range(0, n, 3):
+        for j in range(0, k // 4, 7):
+            assert tuple(dense[r, 4 * j:4 * j + 4]) == sherry_ref.decode_block(int(codes[r, j]))
+    assert np.array_equal(sherry_ref.codes_from_dense(dense), codes)
+
+
+def test_quantize_matches_scalar_block_rule():
+    g = synth.rng(5)
+    w = g.standard_normal((4, 256)).astype(np.float32)
+    w[0, :8] = [0.5, -0.5, 0.5, 0.5, -0.0, 0.0, 1.0, -1.0]
+    codes, _ = sherry_ref.quantize(w)
+    for r in range(4):
+        for j in range(64):
+            assert int(codes[r, j]) == sherry_ref.quantize_block(w[r, 4 * j:4 * j + 4])
+
+
+def test_errors():
+    with pytest.raises(ValueError):
+        sherry_ref.check_shape(4, 100)
+    with pytest.raises(ValueError):
+        sherry_ref.decode_block(32)
+    with pytest.raises(ValueError):
+        sherry_ref.encode_block((1, 1, 1, 1))
+    with pytest.raises(ValueError):
+        sherry_ref.codes_from_dense(np.zeros((1, 128), np.int8))
+    with pytest.raises(ValueError):
+        sherry_ref.quantize(np.full((1, 128), np.nan))
+    with pytest.raises(ValueError):
+        tern2_ref.decode_word(0b10)
+
+
+def test_tern2_hand_words():
+    # R8 by hand: (+1, -1, 0, ...0) -> 01 | 11 << 2 = 0b1101 = 0xD
+    assert tern2_ref.encode_word([1, -1] + [0] * 14) == 0xD
+    assert tern2_ref.encode_word([-1] * 16) == 0xFFFFFFFF
+    assert tern2_ref.encode_word([1] * 16) == 0x55555555
+    assert tern2_ref.decode_word(0x55555555) == [1] * 16
+    g = synth.rng(9)
+    t = synth.ternary_dense(5, 256, g)
+    words = tern2_ref.pack(t)
+    assert words.nbytes == tern2_ref.packed_bytes(5, 256) == 5 * 256 // 4
+    assert np.array_equal(tern2_ref.unpack(words, 5, 256), t)
+    for r in range(5):
+        for i in range(16):
+            assert tern2_ref.decode_word(words[r * 16 + i]) == t[r, 16 * i:16 * i + 16].tolist()
+
+
+def test_sherry_and_tern2_agree_on_the_same_matrix():
+    """Two encodings of one ternary matrix give one product, bit for bit."""
+    g = synth.rng(13)
+    n, k, m = 48, 512, 3
+    t = synth.ternary_34(n, k, g)
+    sw = synth.row_scales(n, g, np.float16)
+    xq, sx, _ = synth.act_absmax_int8(m, k, g)
+    w5 = sherry_ref.pack_codes(sherry_ref.codes_from_dense(t))
+    w2 = tern2_ref.pack(t)
+    a5, y5 = sherry_ref.gemm_i8(w5, sw, n, k, xq, sx)
+    a2, y2 = tern2_ref.gemm_i8(w2, sw, n, k, xq, sx)
+    assert np.array_equal(a5, a2) and np.array_equal(y5.view(np.uint16), y2.view(np.uint16))
+    b5, z5 = sherry_ref.gemv_i8(w5, sw, n, k, xq[0], sx[0])
+    b2, z2 = tern2_ref.gemv_i8(w2, sw, n, k, xq[0], sx[0])
+    assert np.array_equal(b5, b2) and np.array_equal(z5.view(np.uint16), z2.view(np.uint16))
+    assert np.array_equal(b5, a5[0])
+
+
+def test_accumulator_bound_at_largest_shape():
+    """The largest reduction (k = 8192) with x = +-127 stays far inside int32
+    and inside fp32's exact-integer range (2^24)."""
+    k = 8192
+    assert 127 * 3 * k // 4 < 2 ** 24
+    t = np.zeros((1, k), np.int8)
+    t[0] = np.tile([0, 1, 1, 1], k // 4)
+    words = sherry_ref.pack_codes(sherry_ref.codes_from_dense(t))
+    acc, _ = sherry_ref.gemv_i8(words, np.ones(1, np.float32), 1, k, np.full(k, 127, np.int8), None, np.float32)
+    assert int(acc[0]) == 127 * 3 * k // 4
