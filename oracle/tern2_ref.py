@@ -9,9 +9,11 @@ keep power-of-two alignment at the cost of wasted bits.  That comparator is
 measured on the same ternary matrices.  Reading taken for its layout (the pages
 do not give one):
   R8  a weight is a 2-bit two's-complement field: 00 = 0, 01 = +1, 11 = -1
-      (10 never produced); 16 weights per little-endian uint32, weight k of a
-      word at bits [2k, 2k + 2) (LSB first along the input axis); row-major,
-      K/16 words per row, K % 128 == 0 to share the Sherry shapes.
+      (10 never produced); 16 weights per little-endian uint32; weight
+      4q + p of a word (q, p in 0..3) at bits [8p + 2q, 8p + 2q + 2), so a
+      shift by 2q and a mask with 0x03030303 leave four consecutive weights in
+      the low bits of the four bytes; row-major, K/16 words per row,
+      K % 128 == 0 to share the Sherry shapes.
 Products and epilogue are the same as the Sherry reference (R7).
 """
 from __future__ import annotations
@@ -25,6 +27,11 @@ _FIELD = {0: 0, 1: 1, -1: 3}
 _VALUE = {0: 0, 1: 1, 3: -1}
 
 
+def bit_offset(i: int) -> int:
+    """Bit offset of weight i (0..15) inside its word: 8 * (i % 4) + 2 * (i // 4)."""
+    return 8 * (i % 4) + 2 * (i // 4)
+
+
 def packed_bytes(n: int, k: int) -> int:
     sherry_ref.check_shape(n, k)
     return n * k // 4
@@ -36,7 +43,7 @@ def encode_word(t16) -> int:
         raise ValueError("need 16 ternary weights")
     w = 0
     for i, v in enumerate(t16):
-        w |= _FIELD[v] << (2 * i)
+        w |= _FIELD[v] << bit_offset(i)
     return w
 
 
@@ -44,7 +51,7 @@ def decode_word(w: int) -> list:
     w = int(w)
     out = []
     for i in range(WEIGHTS_PER_WORD):
-        f = (w >> (2 * i)) & 3
+        f = (w >> bit_offset(i)) & 3
         if f not in _VALUE:
             raise ValueError(f"field 0b10 is not a ternary value (word {w:#010x}, slot {i})")
         out.append(_VALUE[f])
@@ -59,7 +66,7 @@ def pack(t: np.ndarray) -> np.ndarray:
     if np.any((t != -1) & (t != 0) & (t != 1)):
         raise ValueError("entries must be -1, 0 or +1")
     f = np.where(t < 0, 3, t).astype(np.uint64).reshape(n, k // WEIGHTS_PER_WORD, WEIGHTS_PER_WORD)
-    shifts = (2 * np.arange(WEIGHTS_PER_WORD)).astype(np.uint64)
+    shifts = np.array([bit_offset(i) for i in range(WEIGHTS_PER_WORD)], dtype=np.uint64)
     words = np.bitwise_or.reduce(f << shifts, axis=2)
     return words.astype(np.uint32).reshape(-1)
 
@@ -67,7 +74,7 @@ def pack(t: np.ndarray) -> np.ndarray:
 def unpack(words: np.ndarray, n: int, k: int) -> np.ndarray:
     sherry_ref.check_shape(n, k)
     w = np.asarray(words, dtype=np.uint32).reshape(n, k // WEIGHTS_PER_WORD).astype(np.uint64)
-    shifts = (2 * np.arange(WEIGHTS_PER_WORD)).astype(np.uint64)
+    shifts = np.array([bit_offset(i) for i in range(WEIGHTS_PER_WORD)], dtype=np.uint64)
     f = (w[:, :, None] >> shifts) & 3
     if np.any(f == 2):
         raise ValueError("field 0b10 is not a ternary value")

@@ -59,8 +59,19 @@ def test_errors():
 
 
 def test_tern2_hand_words():
-    # R8 by hand: (+1, -1, 0, ...0) -> 01 | 11 << 2 = 0b1101 = 0xD
-    assert tern2_ref.encode_word([1, -1] + [0] * 14) == 0xD
+    # R8 by hand: weight 0 at bits 0-1, weight 1 at bits 8-9, weight 4 at bits 2-3,
+    # weight 15 (q=3, p=3) at bits 30-31.
+    # (+1, -1, 0, ...) -> 01 | 11 << 8 = 0x301
+    assert tern2_ref.encode_word([1, -1] + [0] * 14) == 0x301
+    assert tern2_ref.encode_word([0] * 4 + [-1] + [0] * 11) == 0xC
+    assert tern2_ref.encode_word([0] * 15 + [1]) == 0x40000000
+    # a shift by 2q and mask 0x03030303 yields weights 4q..4q+3, one per byte
+    t16 = [1, -1, 0, 1, 0, 0, -1, 1, -1, -1, 1, 0, 1, 1, 1, -1]
+    w = tern2_ref.encode_word(t16)
+    for q in range(4):
+        sel = (w >> (2 * q)) & 0x03030303
+        got = [{0: 0, 1: 1, 3: -1}[(sel >> (8 * p)) & 3] for p in range(4)]
+        assert got == t16[4 * q:4 * q + 4]
     assert tern2_ref.encode_word([-1] * 16) == 0xFFFFFFFF
     assert tern2_ref.encode_word([1] * 16) == 0x55555555
     assert tern2_ref.decode_word(0x55555555) == [1] * 16
