@@ -1,0 +1,195 @@
+/*
+ * sherry.h - C ABI of libsherry.so: Sherry 1.25-bit (3:4-sparse ternary)
+ * weights on AMD Instinct MI355X (gfx950).
+ *
+ * The format ("Sherry: Hardware-Efficient 1.25-Bit Ternary Quantization via
+ * Fine-grained Sparsification", Abstract; Figure 2 caption): weights are
+ * ternary, {-1, 0, +1}; every block of four consecutive weights holds exactly
+ * one zero (3:4 fine-grained sparsity), so a block has 4 * 2^3 = 32 states and
+ * packs into a 5-bit code, 1.25 bits per weight.  The layout below is this
+ * library's reading of that format (the pages give no bit layout):
+ *
+ *   block j of row r   = W[r, 4j .. 4j+3] (along the reduction axis K)
+ *   code               = z | n0 << 2 | n1 << 3 | n2 << 4
+ *                        z  = slot of the zero (0..3)
+ *                        n0..n2 = sign bits of the three nonzero slots in
+ *                        ascending slot order, 1 = -1, 0 = +1
+ *   group              = 32 codes (128 weights) in 5 little-endian uint32
+ *                        words, one LSB-first 160-bit stream: code j at bits
+ *                        [5j, 5j+5) of d0 + d1*2^32 + ... + d4*2^128
+ *   matrix             = uint32 codes[n][K/128][5], row-major, K % 128 == 0
+ *   scales             = one per output row (fp32 or fp16)
+ *
+ * Products (all accumulate exactly in int32 for int8 activations):
+ *   acc[r]    = sum_k T[r, k] * x[k]
+ *   y[r]      = ydt( (fp32(acc[r]) * fp32(s_w[r])) * s_x )     int8 x
+ *   y[r]      = fp32 accumulation of T[r, k] * x[k], then * fp32(s_w[r])  bf16 x
+ *   Y[m, r]   = ydt( (fp32(acc[m, r]) * fp32(s_w[r])) * s_x[m] )  int8 X
+ * Every multiply is a separate IEEE fp32 round-to-nearest-even step; the
+ * final conversion to fp16 is round-to-nearest-even.
+ *
+ * Conventions for every entry point:
+ *   - Buffers are DEVICE pointers owned by the caller (except where a
+ *     parameter says HOST).  The library allocates no device memory and keeps
+ *     no per-call state; calls are thread-safe.
+ *   - All argument checks run on the host before any HIP call.  On an error
+ *     the call returns a status and enqueues nothing.
+ *   - Work is enqueued on `stream` (asynchronous, no implicit sync).  Errors
+ *     that happen on the device are not reported by the call.
+ *   - Input and output buffers must not overlap.
+ */
+#ifndef SHERRY_H
+#define SHERRY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SHERRY_OK = 0,
+  SHERRY_EINVAL = 1,  /* null pointer where one is required, n/k/m <= 0, bad enum */
+  SHERRY_ESHAPE = 2,  /* k % 128 != 0, leading dimension too small, size overflow */
+  SHERRY_EDTYPE = 3,  /* unsupported dtype combination */
+  SHERRY_EALIGN = 4,  /* a pointer or leading dimension breaks the stated alignment */
+  SHERRY_EDEVICE = 5, /* no HIP device, or the current device is not gfx950 */
+  SHERRY_ELAUNCH = 6  /* the kernel launch failed (hipGetLastError) */
+} sherry_status;
+
+typedef enum {
+  SHERRY_I8 = 0,
+  SHERRY_I32 = 1,
+  SHERRY_F16 = 2,
+  SHERRY_BF16 = 3,
+  SHERRY_F32 = 4
+} sherry_dtype;
+
+/* Library version, e.g. "0.1.0". */
+const char* sherry_version(void);
+
+/* Human-readable name of a status code (never NULL). */
+const char* sherry_status_str(sherry_status s);
+
+/* Bytes of packed codes for an n x k matrix: n * (k / 128) * 20, i.e. exactly
+ * 5 bits per 4 weights.  Returns 0 if n <= 0, k <= 0, k % 128 != 0 or the size
+ * overflows. */
+size_t sherry_packed_bytes(int64_t n, int64_t k);
+
+/* Pack real weights into codes and per-row scales (Sherry Abstract: ternary
+ * weights under 3:4 sparsity, four weights in five bits).  Rule per block:
+ * the zero goes to the slot of smallest |w| (lowest slot on ties); each other
+ * slot keeps the sign of w (negative iff w < 0, so -0.0 is +1).  Per row,
+ * scale = (sum of kept |w|) / (3k/4), the least-squares scale for that
+ * pattern, accumulated in fp64 (double-double) and rounded once, RNE, to s_dt.
+ *   w      : n x k weights, element (r, c) at w[r * ldw + c]; w_dt F32|F16|BF16
+ *   ldw    : row stride in elements, ldw >= k
+ *   codes  : out, sherry_packed_bytes(n, k) bytes, 4-byte aligned
+ *   scales : out, n elements of s_dt (F32|F16), aligned to its size
+ * Non-finite weights are a caller error (codes and scales then unspecified).
+ * Alignment: w aligned to 4 * element size and ldw a multiple of 4. */
+sherry_status sherry_pack(const void* w, sherry_dtype w_dt, int64_t n, int64_t k, int64_t ldw,
+                          uint32_t* codes, void* scales, sherry_dtype s_dt, hipStream_t stream);
+
+/* Batch-1 product y = diag(s_w) * T * x (the decode-phase GEMV).
+ *   codes    : n x k packed codes (layout above), 4-byte aligned
+ *   w_scales : n scales of s_dt (F32|F16)
+ *   x        : k activations, x_dt I8 (int8) or BF16; 16-byte aligned
+ *   x_scale  : I8 only: pointer to ONE device float s_x, or NULL for 1.0;
+ *              must be NULL for BF16
+ *   acc      : optional out, n int32 exact sums (I8 only, else must be NULL)
+ *   y        : optional out, n values of y_dt: F32 or F16 for I8; F32 for BF16
+ * At least one of acc / y must be non-NULL. */
+sherry_status sherry_gemv(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n,
+                          int64_t k, const void* x, sherry_dtype x_dt, const float* x_scale,
+                          int32_t* acc, void* y, sherry_dtype y_dt, hipStream_t stream);
+
+/* One problem of a grouped GEMV: same meaning as the sherry_gemv arguments. */
+typedef struct {
+  const uint32_t* codes;
+  const void* w_scales;
+  int64_t n;
+  int64_t k;
+  const void* x;
+  const float* x_scale;
+  int32_t* acc;
+  void* y;
+} sherry_gemv_problem;
+
+/* Bytes of the launch plan for these problems (the plan holds one 64-byte
+ * record per problem plus one 8-byte record per workgroup tile).  Returns 0
+ * if probs is NULL, count <= 0 or a problem has an invalid shape. */
+size_t sherry_gemv_plan_bytes(const sherry_gemv_problem* probs /* HOST */, int32_t count);
+
+/* Build the launch plan of a grouped GEMV (many independent batch-1 products,
+ * one kernel launch) into `plan`, a HOST buffer of at least
+ * sherry_gemv_plan_bytes(probs, count) bytes, 8-byte aligned.  Every problem
+ * is validated as in sherry_gemv, with the dtypes shared by all problems.
+ * Pure host code: no HIP call.  The caller then copies the plan bytes
+ * unchanged to a device buffer (8-byte aligned) and launches it. */
+sherry_status sherry_gemv_plan(const sherry_gemv_problem* probs /* HOST */, int32_t count,
+                               sherry_dtype s_dt, sherry_dtype x_dt, sherry_dtype y_dt, void* plan,
+                               size_t plan_bytes);
+
+/* Launch a planned grouped GEMV (a plan from sherry_gemv_plan or
+ * tern2_gemv_plan): `plan_host` is the host plan, `plan_dev` a device copy of
+ * the same bytes.  Returns SHERRY_EINVAL if the host plan header is malformed.
+ * The device copy and every buffer named by the plan must stay alive until
+ * the kernel completes. */
+sherry_status sherry_gemv_grouped(const void* plan_host, const void* plan_dev, hipStream_t stream);
+
+/* Matrix product for M tokens: Y[m, r] = s_x[m] * s_w[r] * sum_k X[m, k] T[r, k].
+ * Small M (<= 16) decodes codes in registers into int8 MFMA operands; larger
+ * M decodes tiles of codes once per tile and feeds int8 MFMA.
+ *   X        : m x k int8, row-major with row stride ldx bytes (ldx >= k,
+ *              ldx % 16 == 0, X 16-byte aligned); x_dt must be I8
+ *   x_scales : m floats (per-token scale), or NULL for 1.0
+ *   acc      : optional out, m x n int32, row stride n
+ *   y        : optional out, m x n of y_dt (F16|F32), row stride ldy >= n
+ * At least one of acc / y must be non-NULL. */
+sherry_status sherry_gemm(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n,
+                          int64_t k, const void* x, sherry_dtype x_dt, int64_t m, int64_t ldx,
+                          const float* x_scales, int32_t* acc, void* y, sherry_dtype y_dt, int64_t ldy,
+                          hipStream_t stream);
+
+/* ---- 2-bit dense-ternary comparator (Sherry Abstract and Figure 2: the
+ * 2-bit aligned packing that keeps alignment by wasting bits) ----
+ * Layout (a reading; the pages give none): 16 weights per little-endian
+ * uint32 word, field value 00 = 0, 01 = +1, 11 = -1 (10 never written);
+ * weight 4q + p of a word (q, p in 0..3) sits at bits [8p + 2q, 8p + 2q + 2),
+ * so one shift and mask put four consecutive weights in the low bits of the
+ * four bytes.  Row-major, k / 16 words per row, k % 128 == 0.  Scales and
+ * epilogues are exactly those of the Sherry entry points. */
+size_t tern2_packed_bytes(int64_t n, int64_t k); /* n * k / 4, 0 if invalid */
+
+/* Encode a dense ternary int8 matrix t (values -1, 0, +1; row stride ldt
+ * elements, ldt >= k, ldt % 16 == 0, t 16-byte aligned) into 2-bit words.
+ * Values outside {-1, 0, +1} are a caller error (output unspecified). */
+sherry_status tern2_encode(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint32_t* codes,
+                           hipStream_t stream);
+
+/* Same contract as sherry_gemv with I8 x, on 2-bit codes. */
+sherry_status tern2_gemv(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n,
+                         int64_t k, const void* x, sherry_dtype x_dt, const float* x_scale,
+                         int32_t* acc, void* y, sherry_dtype y_dt, hipStream_t stream);
+
+/* Same contract as sherry_gemv_plan, on 2-bit codes (x_dt must be I8); the
+ * plan is launched with sherry_gemv_grouped. */
+sherry_status tern2_gemv_plan(const sherry_gemv_problem* probs /* HOST */, int32_t count,
+                              sherry_dtype s_dt, sherry_dtype x_dt, sherry_dtype y_dt, void* plan,
+                              size_t plan_bytes);
+
+/* Same contract as sherry_gemm, on 2-bit codes. */
+sherry_status tern2_gemm(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n,
+                         int64_t k, const void* x, sherry_dtype x_dt, int64_t m, int64_t ldx,
+                         const float* x_scales, int32_t* acc, void* y, sherry_dtype y_dt, int64_t ldy,
+                         hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SHERRY_H */

@@ -1,0 +1,171 @@
+"""libsherry.so on the host: it loads, exports every function include/sherry.h
+declares, and rejects invalid arguments before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sherry.h")
+LIB = os.path.join(ROOT, "ultra_bit_weight_amd", "lib", "libsherry.so")
+
+OK, EINVAL, ESHAPE, EDTYPE, EALIGN, EDEVICE = 0, 1, 2, 3, 4, 5
+I8, I32, F16, BF16, F32 = 0, 1, 2, 3, 4
+A = 0x10000  # a fake, well-aligned non-null "device" address: never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(\w+)\s*\([^;{]*\)\s*;", text)
+    return sorted(set(n for n in names if n.startswith(("sherry_", "tern2_"))))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} missing: build with __graft_entry__.build()")
+    from ultra_bit_weight_amd import sherry
+
+    return sherry.load(LIB)
+
+
+def test_header_declares_the_api():
+    names = declared_functions()
+    for required in ("sherry_pack", "sherry_gemv", "sherry_gemm", "sherry_gemv_grouped", "tern2_gemv"):
+        assert required in names
+    assert len(names) >= 14
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(LIB)
+    for name in declared_functions():
+        assert hasattr(raw, name), f"{name} declared in sherry.h but not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.sherry_version().decode().count(".") == 2
+    for s in range(7):
+        assert lib.sherry_status_str(s).decode().startswith("SHERRY_")
+    assert lib.sherry_status_str(99).decode() == "SHERRY_UNKNOWN_STATUS"
+
+
+def test_packed_bytes(lib):
+    assert lib.sherry_packed_bytes(256, 1024) == 256 * 1024 * 5 // 32
+    assert lib.sherry_packed_bytes(2048, 8192) == 2048 * 8192 * 5 // 32
+    assert lib.sherry_packed_bytes(1, 128) == 20
+    for n, k in [(0, 128), (4, 0), (4, 100), (-1, 128), (4, 129)]:
+        assert lib.sherry_packed_bytes(n, k) == 0
+    assert lib.tern2_packed_bytes(256, 1024) == 256 * 1024 // 4
+    assert lib.tern2_packed_bytes(3, 100) == 0
+
+
+def gemv(lib, codes=A, sw=A, s_dt=F16, n=64, k=1024, x=A, x_dt=I8, xs=None, acc=A, y=A, y_dt=F16, fn="sherry_gemv"):
+    return getattr(lib, fn)(codes, sw, s_dt, n, k, x, x_dt, xs, acc, y, y_dt, None)
+
+
+@pytest.mark.parametrize("fn", ["sherry_gemv", "tern2_gemv"])
+def test_gemv_validation(lib, fn):
+    assert gemv(lib, codes=None, fn=fn) == EINVAL
+    assert gemv(lib, sw=None, fn=fn) == EINVAL
+    assert gemv(lib, x=None, fn=fn) == EINVAL
+    assert gemv(lib, acc=None, y=None, fn=fn) == EINVAL
+    assert gemv(lib, n=0, fn=fn) == EINVAL
+    assert gemv(lib, k=-128, fn=fn) == EINVAL
+    assert gemv(lib, k=1000, fn=fn) == ESHAPE
+    assert gemv(lib, n=2 ** 31, fn=fn) == ESHAPE
+    assert gemv(lib, s_dt=BF16, fn=fn) == EDTYPE
+    assert gemv(lib, x_dt=F32, fn=fn) == EDTYPE
+    assert gemv(lib, y_dt=I8, fn=fn) == EDTYPE
+    assert gemv(lib, codes=A + 2, fn=fn) == EALIGN
+    assert gemv(lib, x=A + 4, fn=fn) == EALIGN
+    assert gemv(lib, sw=A + 1, fn=fn) == EALIGN
+    assert gemv(lib, y=A + 1, fn=fn) == EALIGN
+    assert gemv(lib, acc=A + 2, fn=fn) == EALIGN
+    # valid arguments: the first HIP call finds no gfx950 device here
+    assert gemv(lib, fn=fn) == EDEVICE
+
+
+def test_gemv_bf16_rules(lib):
+    assert gemv(lib, x_dt=BF16, acc=None, y_dt=F32) == EDEVICE  # valid
+    assert gemv(lib, x_dt=BF16, acc=A, y_dt=F32) == EDTYPE       # no int32 sums for bf16
+    assert gemv(lib, x_dt=BF16, acc=None, y_dt=F16) == EDTYPE
+    assert gemv(lib, x_dt=BF16, acc=None, y_dt=F32, xs=A) == EDTYPE
+    assert gemv(lib, x_dt=BF16, acc=None, y=None) == EINVAL
+    assert gemv(lib, x_dt=BF16, acc=None, y_dt=F32, fn="tern2_gemv") == EDTYPE
+
+
+def test_pack_validation(lib):
+    f = lib.sherry_pack
+    assert f(None, F32, 8, 128, 128, A, A, F16, None) == EINVAL
+    assert f(A, F32, 8, 128, 128, None, A, F16, None) == EINVAL
+    assert f(A, F32, 8, 100, 100, A, A, F16, None) == ESHAPE
+    assert f(A, F32, 8, 128, 64, A, A, F16, None) == ESHAPE
+    assert f(A, I8, 8, 128, 128, A, A, F16, None) == EDTYPE
+    assert f(A, F32, 8, 128, 128, A, A, BF16, None) == EDTYPE
+    assert f(A + 4, F32, 8, 128, 128, A, A, F16, None) == EALIGN
+    assert f(A, F32, 8, 128, 130, A, A, F16, None) == EALIGN
+    assert f(A, F32, 8, 128, 128, A, A, F16, None) == EDEVICE
+
+
+def gemm(lib, codes=A, sw=A, s_dt=F16, n=64, k=1024, x=A, x_dt=I8, m=4, ldx=1024, xs=A, acc=A, y=A, y_dt=F16,
+         ldy=64, fn="sherry_gemm"):
+    return getattr(lib, fn)(codes, sw, s_dt, n, k, x, x_dt, m, ldx, xs, acc, y, y_dt, ldy, None)
+
+
+@pytest.mark.parametrize("fn", ["sherry_gemm", "tern2_gemm"])
+def test_gemm_validation(lib, fn):
+    assert gemm(lib, x=None, fn=fn) == EINVAL
+    assert gemm(lib, m=0, fn=fn) == EINVAL
+    assert gemm(lib, acc=None, y=None, fn=fn) == EINVAL
+    assert gemm(lib, k=1000, ldx=1008, fn=fn) == ESHAPE
+    assert gemm(lib, ldx=1000, fn=fn) == ESHAPE
+    assert gemm(lib, ldx=1032, fn=fn) == ESHAPE
+    assert gemm(lib, ldy=32, fn=fn) == ESHAPE
+    assert gemm(lib, x_dt=BF16, fn=fn) == EDTYPE
+    assert gemm(lib, y_dt=I32, fn=fn) == EDTYPE
+    assert gemm(lib, x=A + 8, fn=fn) == EALIGN
+    assert gemm(lib, xs=A + 2, fn=fn) == EALIGN
+    assert gemm(lib, fn=fn) == EDEVICE
+    assert gemm(lib, xs=None, acc=None, fn=fn) == EDEVICE
+
+
+def test_tern2_encode_validation(lib):
+    f = lib.tern2_encode
+    assert f(None, 4, 128, 128, A, None) == EINVAL
+    assert f(A, 4, 96, 96, A, None) == ESHAPE
+    assert f(A, 4, 128, 120, A, None) == ESHAPE
+    assert f(A, 4, 128, 136, A, None) == EALIGN
+    assert f(A + 8, 4, 128, 128, A, None) == EALIGN
+    assert f(A, 4, 128, 128, A, None) == EDEVICE
+
+
+def test_grouped_plan_on_host(lib):
+    from ultra_bit_weight_amd.sherry import GemvProblem
+
+    shapes = [(2048, 2048), (512, 2048), (2048, 8192), (256, 1024), (300, 384)]
+    arr = (GemvProblem * len(shapes))()
+    for i, (n, k) in enumerate(shapes):
+        arr[i] = GemvProblem(A, A, n, k, A, None, None, A)
+    nbytes = lib.sherry_gemv_plan_bytes(arr, len(shapes))
+    # 64-byte header + 64 bytes per problem + 8 bytes per tile; tile rows are
+    # 4 iterations x rows per iteration (4 waves x 64 / lanes per row)
+    tiles = 2048 // 64 + 512 // 64 + 2048 // 16 + 256 // 128 + -(-300 // 16)
+    assert nbytes == 64 + 64 * len(shapes) + 8 * tiles
+    buf = ctypes.create_string_buffer(nbytes + 8)
+    base = (ctypes.addressof(buf) + 7) // 8 * 8
+    assert lib.sherry_gemv_plan(arr, len(shapes), F16, I8, F16, base, nbytes) == OK
+    hdr = ctypes.string_at(base, 16)
+    assert int.from_bytes(hdr[8:12], "little") == len(shapes)
+    assert int.from_bytes(hdr[12:16], "little") == tiles
+    assert lib.sherry_gemv_plan(arr, len(shapes), F16, I8, F16, base, nbytes - 8) == EINVAL
+    assert lib.sherry_gemv_plan(arr, len(shapes), F16, F32, F16, base, nbytes) == EDTYPE
+    assert lib.sherry_gemv_plan(arr, len(shapes), F16, I8, F16, base + 4, nbytes) == EALIGN
+    arr[1].k = 100
+    assert lib.sherry_gemv_plan_bytes(arr, len(shapes)) == 0
+    assert lib.sherry_gemv_plan(arr, len(shapes), F16, I8, F16, base, nbytes) == ESHAPE
+    # a malformed host plan is rejected before any device call
+    bad = ctypes.create_string_buffer(64)
+    assert lib.sherry_gemv_grouped(ctypes.addressof(bad), A, None) == EINVAL
+    assert lib.sherry_gemv_grouped(None, A, None) == EINVAL

@@ -1,0 +1,342 @@
+"""HIP path (libsherry.so via the C ABI) against the CPU oracle, element by element.
+
+Integer results (codes, int32 sums) must match bit for bit; fp16/fp32 outputs of
+the int8 paths too (the epilogue is the same chain of IEEE fp32 products).  The
+bf16 path accumulates in fp32 in a different order from the exact reference,
+so it is held to max|d| <= 1e-3 * max|y_ref| and relative L2 <= 1e-4.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import sherry_ref, tern2_ref
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def words_dev(w):
+    return dev(np.asarray(w, dtype=np.uint32).view(np.int32))
+
+
+def host_words(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# ----------------------------------------------------------------- runtime ---
+
+def test_single_hip_runtime_in_process(gpu_lib):
+    x = torch.zeros(4, device=DEV)
+    gpu_lib.gemv(words_dev(np.zeros(20, np.uint32)), dev(np.ones(1, np.float16)), dev(np.zeros(128, np.int8)))
+    torch.cuda.synchronize()
+    maps = open("/proc/self/maps").read().splitlines()
+    libs = {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
+    assert len(libs) == 1, libs
+    assert x.sum().item() == 0
+
+
+# -------------------------------------------------------------------- pack ---
+
+PACK_SHAPES = [(1, 128), (3, 256), (37, 640), (256, 1024), (64, 2048), (5, 3072), (9, 8192)]
+
+
+@pytest.mark.parametrize("n,k", PACK_SHAPES)
+@pytest.mark.parametrize("w_dtype", [np.float32, np.float16, "bf16"])
+@pytest.mark.parametrize("s_dtype", [np.float32, np.float16])
+def test_pack_matches_oracle(gpu_lib, n, k, w_dtype, s_dtype):
+    say(f"pack n={n} k={k} w={w_dtype} s={s_dtype}")
+    g = synth.rng(1000 + n + k)
+    w32 = g.standard_normal((n, k)).astype(np.float32)
+    w32[0, :12] = [0.5, -0.5, 0.5, 0.5, -0.0, 0.0, 1.0, -1.0, 0.25, 0.25, 0.25, 0.25]  # ties, signed zero
+    if w_dtype == "bf16":
+        bits = synth.f32_to_bf16_bits(w32)
+        w_host = (bits.astype(np.uint32) << 16).view(np.float32)  # exact values the GPU sees
+        w_t = dev(bits.view(np.int16)).view(torch.bfloat16)
+    else:
+        w_host = w32.astype(w_dtype)
+        w_t = dev(w_host)
+    ref_words, ref_scales = sherry_ref.pack(w_host, s_dtype)
+    codes, scales = gpu_lib.pack(w_t, torch.float32 if s_dtype == np.float32 else torch.float16)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_words(codes), ref_words)
+    got = scales.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32 if s_dtype == np.float32 else np.uint16),
+                          ref_scales.view(np.uint32 if s_dtype == np.float32 else np.uint16))
+
+
+def test_pack_exact_ternary_and_row_stride(gpu_lib):
+    g = synth.rng(77)
+    n, k, ld = 50, 1024, 1024 + 64
+    t = synth.ternary_34(n, k, g)
+    s = synth.row_scales(n, g, np.float32)
+    full = np.zeros((n, ld), np.float32)
+    full[:, :k] = t * s[:, None]
+    full[:, k:] = 1e6  # padding past k must be ignored
+    wt = dev(full)[:, :k]
+    codes, scales = gpu_lib.pack(wt, torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(sherry_ref.unpack(host_words(codes), n, k), t)
+    assert np.array_equal(scales.cpu().numpy(), s)
+
+
+# -------------------------------------------------------------- int8 GEMV ---
+
+GEMV_K = [128, 256, 384, 640, 1024, 2048, 3072, 4096, 8192]
+GEMV_N = [1, 7, 64, 257, 1000]
+
+
+@pytest.mark.parametrize("k", GEMV_K)
+@pytest.mark.parametrize("n", GEMV_N)
+def test_gemv_i8_matches_oracle(gpu_lib, n, k):
+    say(f"gemv_i8 n={n} k={k}")
+    g = synth.rng(n * 31 + k)
+    words = synth.random_words(n * (k // 128) * 5, g)
+    s16 = synth.row_scales(n, g, np.float16)
+    x = synth.x_int8_uniform(k, g)
+    x[:3] = [-128, 127, -127]
+    sx = np.float32(g.uniform(0.005, 0.05))
+    ref_acc, ref_y = sherry_ref.gemv_i8(words, s16, n, k, x, sx, np.float16)
+    acc, y = gpu_lib.gemv(words_dev(words), dev(s16), dev(x), dev(np.array([sx], np.float32)), torch.float16,
+                          want_acc=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), ref_acc)
+    assert np.array_equal(y.cpu().numpy().view(np.uint16), ref_y.view(np.uint16))
+
+
+@pytest.mark.parametrize("k", [1024, 2048, 8192])
+def test_gemv_i8_fp32_scales_and_outputs(gpu_lib, k):
+    g = synth.rng(5 + k)
+    n = 256
+    words = synth.random_words(n * (k // 128) * 5, g)
+    s32 = synth.row_scales(n, g, np.float32)
+    x = synth.x_int8_uniform(k, g)
+    ref_acc, ref_y = sherry_ref.gemv_i8(words, s32, n, k, x, None, np.float32)
+    _, y = gpu_lib.gemv(words_dev(words), dev(s32), dev(x), None, torch.float32)
+    acc, y2 = gpu_lib.gemv(words_dev(words), dev(s32), dev(x), None, None, want_acc=True)
+    torch.cuda.synchronize()
+    assert y2 is None
+    assert np.array_equal(acc.cpu().numpy(), ref_acc)
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), ref_y.view(np.uint32))
+
+
+def test_gemv_i8_extreme_accumulators(gpu_lib):
+    """All weights of a row +1 where x = 127 (max positive sum) and a flipped
+    row (max negative sum), at the largest k."""
+    k, n = 8192, 2
+    t = np.zeros((n, k), np.int8)
+    t[0] = np.tile([0, 1, 1, 1], k // 4)
+    t[1] = -t[0]
+    t[1, ::4] = 0
+    words = sherry_ref.pack_codes(sherry_ref.codes_from_dense(t))
+    x = np.full(k, 127, np.int8)
+    acc, _ = gpu_lib.gemv(words_dev(words), dev(np.ones(n, np.float32)), dev(x), None, None, want_acc=True)
+    torch.cuda.synchronize()
+    assert acc.cpu().numpy().tolist() == [127 * 3 * k // 4, -127 * 3 * k // 4]
+
+
+# -------------------------------------------------------------- bf16 GEMV ---
+
+def check_fp_tolerance(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    scale = np.max(np.abs(ref))
+    assert np.max(np.abs(got - ref)) <= 1e-3 * scale, np.max(np.abs(got - ref)) / scale
+    assert np.linalg.norm(got - ref) <= 1e-4 * np.linalg.norm(ref), np.linalg.norm(got - ref) / np.linalg.norm(ref)
+
+
+@pytest.mark.parametrize("k", [128, 640, 1024, 2048, 3072, 4096, 8192])
+@pytest.mark.parametrize("n", [1, 33, 512])
+def test_gemv_bf16_within_tolerance(gpu_lib, n, k):
+    say(f"gemv_bf16 n={n} k={k}")
+    g = synth.rng(n * 7 + k)
+    words = synth.random_words(n * (k // 128) * 5, g)
+    sw = synth.row_scales(n, g, np.float16)
+    xb = synth.x_bf16_normal(k, g)
+    ref = sherry_ref.gemv_bf16(words, sw, n, k, xb)
+    x_t = dev(xb.view(np.int16)).view(torch.bfloat16)
+    _, y = gpu_lib.gemv(words_dev(words), dev(sw), x_t, None, torch.float32)
+    torch.cuda.synchronize()
+    check_fp_tolerance(y.cpu().numpy(), ref)
+
+
+# -------------------------------------------------------------------- GEMM ---
+
+@pytest.mark.parametrize("m", [1, 2, 3, 4, 8, 15, 16, 17, 33])
+@pytest.mark.parametrize("n,k", [(1, 128), (16, 384), (100, 1024), (513, 2048), (64, 8192), (40, 3072)])
+def test_gemm_matches_oracle(gpu_lib, m, n, k):
+    say(f"gemm m={m} n={n} k={k}")
+    g = synth.rng(m * 1000 + n * 3 + k)
+    words = synth.random_words(n * (k // 128) * 5, g)
+    sw = synth.row_scales(n, g, np.float16)
+    xq, sx, _ = synth.act_absmax_int8(m, k, g)
+    ref_acc, ref_y = sherry_ref.gemm_i8(words, sw, n, k, xq, sx, np.float16)
+    acc, y = gpu_lib.gemm(words_dev(words), dev(sw), dev(xq), dev(sx), torch.float16, want_acc=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), ref_acc)
+    assert np.array_equal(y.cpu().numpy().view(np.uint16), ref_y.view(np.uint16))
+
+
+def test_gemm_strided_x_and_fp32_out(gpu_lib):
+    g = synth.rng(99)
+    m, n, k, ldx = 5, 96, 1024, 1024 + 32
+    words = synth.random_words(n * (k // 128) * 5, g)
+    sw = synth.row_scales(n, g, np.float32)
+    big = synth.x_int8_uniform((m, ldx), g)
+    ref_acc, ref_y = sherry_ref.gemm_i8(words, sw, n, k, big[:, :k], None, np.float32)
+    acc, y = gpu_lib.gemm(words_dev(words), dev(sw), dev(big)[:, :k], None, torch.float32, want_acc=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), ref_acc)
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), ref_y.view(np.uint32))
+
+
+# ------------------------------------------------------ 2-bit comparator ---
+
+@pytest.mark.parametrize("n,k", [(1, 128), (37, 640), (256, 2048), (64, 8192)])
+def test_tern2_encode_and_products(gpu_lib, n, k):
+    say(f"tern2 n={n} k={k}")
+    g = synth.rng(n + 3 * k)
+    t = synth.ternary_dense(n, k, g)
+    codes = gpu_lib.tern2_encode(dev(t))
+    torch.cuda.synchronize()
+    ref_words = tern2_ref.pack(t)
+    assert np.array_equal(host_words(codes), ref_words)
+    sw = synth.row_scales(n, g, np.float16)
+    xq, sx, _ = synth.act_absmax_int8(3, k, g)
+    ref_acc, ref_y = tern2_ref.gemv_i8(ref_words, sw, n, k, xq[0], sx[0], np.float16)
+    acc, y = gpu_lib.tern2_gemv(codes, dev(sw), dev(xq[0]), dev(sx[:1]), torch.float16, want_acc=True)
+    ref_acc2, ref_y2 = tern2_ref.gemm_i8(ref_words, sw, n, k, xq, sx, np.float16)
+    acc2, y2 = gpu_lib.tern2_gemm(codes, dev(sw), dev(xq), dev(sx), torch.float16, want_acc=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), ref_acc)
+    assert np.array_equal(y.cpu().numpy().view(np.uint16), ref_y.view(np.uint16))
+    assert np.array_equal(acc2.cpu().numpy(), ref_acc2)
+    assert np.array_equal(y2.cpu().numpy().view(np.uint16), ref_y2.view(np.uint16))
+
+
+def test_sherry_and_tern2_agree_on_gpu(gpu_lib):
+    """Same 3:4 ternary matrix in both encodings: identical sums and outputs."""
+    g = synth.rng(4242)
+    n, k = 512, 2048
+    t = synth.ternary_34(n, k, g)
+    s = synth.row_scales(n, g, np.float32)
+    codes5, scales = gpu_lib.pack(dev((t * s[:, None]).astype(np.float32)), torch.float16)
+    codes2 = gpu_lib.tern2_encode(dev(t))
+    xq, sx, _ = synth.act_absmax_int8(4, k, g)
+    a5, y5 = gpu_lib.gemv(codes5, scales, dev(xq[0]), dev(sx[:1]), torch.float16, want_acc=True)
+    a2, y2 = gpu_lib.tern2_gemv(codes2, scales, dev(xq[0]), dev(sx[:1]), torch.float16, want_acc=True)
+    b5, z5 = gpu_lib.gemm(codes5, scales, dev(xq), dev(sx), torch.float16, want_acc=True)
+    b2, z2 = gpu_lib.tern2_gemm(codes2, scales, dev(xq), dev(sx), torch.float16, want_acc=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a5, a2) and torch.equal(y5, y2)
+    assert torch.equal(b5, b2) and torch.equal(z5, z2)
+    assert torch.equal(b5[0], a5)
+
+
+# ----------------------------------------------------------------- grouped ---
+
+def test_grouped_gemv_matches_single_calls_and_oracle(gpu_lib):
+    g = synth.rng(31337)
+    shapes = [(2048, 2048), (512, 2048), (700, 8192), (256, 1024), (300, 384), (65, 3072), (17, 4096)]
+    probs, refs = [], []
+    for n, k in shapes:
+        words = synth.random_words(n * (k // 128) * 5, g)
+        sw = synth.row_scales(n, g, np.float16)
+        x = synth.x_int8_uniform(k, g)
+        sx = np.array([g.uniform(0.01, 0.03)], np.float32)
+        refs.append(sherry_ref.gemv_i8(words, sw, n, k, x, sx[0], np.float16))
+        probs.append(dict(codes=words_dev(words), scales=dev(sw), x=dev(x), x_scale=dev(sx),
+                          acc=torch.empty(n, dtype=torch.int32, device=DEV),
+                          y=torch.empty(n, dtype=torch.float16, device=DEV)))
+    grouped = gpu_lib.GroupedGemv(probs)
+    grouped()
+    torch.cuda.synchronize()
+    for p, (ra, ry), (n, k) in zip(probs, refs, shapes):
+        assert np.array_equal(p["acc"].cpu().numpy(), ra), (n, k)
+        assert np.array_equal(p["y"].cpu().numpy().view(np.uint16), ry.view(np.uint16)), (n, k)
+    for p in probs:  # run twice: the plan is reusable
+        p["y"].zero_()
+    grouped()
+    torch.cuda.synchronize()
+    for p, (ra, ry) in zip(probs, refs):
+        assert np.array_equal(p["y"].cpu().numpy().view(np.uint16), ry.view(np.uint16))
+
+
+def test_grouped_bf16_and_tern2(gpu_lib):
+    g = synth.rng(2718)
+    shapes = [(1024, 3072), (300, 8192), (64, 2048)]
+    probs, refs = [], []
+    for n, k in shapes:
+        words = synth.random_words(n * (k // 128) * 5, g)
+        sw = synth.row_scales(n, g, np.float16)
+        xb = synth.x_bf16_normal(k, g)
+        refs.append(sherry_ref.gemv_bf16(words, sw, n, k, xb))
+        probs.append(dict(codes=words_dev(words), scales=dev(sw), x=dev(xb.view(np.int16)).view(torch.bfloat16),
+                          y=torch.empty(n, dtype=torch.float32, device=DEV)))
+    gpu_lib.GroupedGemv(probs)()
+    torch.cuda.synchronize()
+    for p, r in zip(probs, refs):
+        check_fp_tolerance(p["y"].cpu().numpy(), r)
+    probs2, refs2 = [], []
+    for n, k in [(512, 2048), (128, 8192)]:
+        t = synth.ternary_dense(n, k, g)
+        sw = synth.row_scales(n, g, np.float16)
+        x = synth.x_int8_uniform(k, g)
+        refs2.append(tern2_ref.gemv_i8(tern2_ref.pack(t), sw, n, k, x, None, np.float16))
+        probs2.append(dict(codes=gpu_lib.tern2_encode(dev(t)), scales=dev(sw), x=dev(x),
+                           acc=torch.empty(n, dtype=torch.int32, device=DEV),
+                           y=torch.empty(n, dtype=torch.float16, device=DEV)))
+    gpu_lib.GroupedGemv(probs2, tern2=True)()
+    torch.cuda.synchronize()
+    for p, (ra, ry) in zip(probs2, refs2):
+        assert np.array_equal(p["acc"].cpu().numpy(), ra)
+        assert np.array_equal(p["y"].cpu().numpy().view(np.uint16), ry.view(np.uint16))
+
+
+# ------------------------------------------------ full-size LLaMA shapes ---
+
+@pytest.mark.parametrize("layer", ["1b", "3b"])
+def test_full_layer_sampled_rows(gpu_lib, layer):
+    """Every matrix of a LLaMA-3.2 decoder layer at full size, through the
+    grouped launch the benchmark times; 64 sampled rows per matrix checked."""
+    g = synth.rng(11 if layer == "1b" else 12)
+    shapes = synth.LLAMA32_1B_LAYER if layer == "1b" else synth.LLAMA32_3B_LAYER
+    probs, keep = [], []
+    for name, n, k in shapes:
+        say(f"full {layer} {name} {n}x{k}")
+        words = synth.random_words(n * (k // 128) * 5, g)
+        sw = synth.row_scales(n, g, np.float16)
+        if layer == "1b":
+            xq, sx, _ = synth.act_absmax_int8(1, k, g)
+            x_t, xs_t = dev(xq[0]), dev(sx)
+            y = torch.empty(n, dtype=torch.float16, device=DEV)
+            acc = torch.empty(n, dtype=torch.int32, device=DEV)
+        else:
+            xb = synth.x_bf16_normal(k, g)
+            x_t, xs_t = dev(xb.view(np.int16)).view(torch.bfloat16), None
+            y = torch.empty(n, dtype=torch.float32, device=DEV)
+            acc = None
+        probs.append(dict(codes=words_dev(words), scales=dev(sw), x=x_t, x_scale=xs_t, acc=acc, y=y))
+        keep.append((words, sw, xq[0] if layer == "1b" else xb, sx if layer == "1b" else None, n, k))
+    gpu_lib.GroupedGemv(probs)()
+    torch.cuda.synchronize()
+    for p, (words, sw, x, sx, n, k) in zip(probs, keep):
+        rows = np.unique(np.concatenate([[0, n - 1], g.integers(0, n, 62)]))
+        g5 = k // 128 * 5
+        sub = np.concatenate([words[r * g5:(r + 1) * g5] for r in rows])
+        if layer == "1b":
+            ra, ry = sherry_ref.gemv_i8(sub, sw[rows], len(rows), k, x, sx[0], np.float16)
+            assert np.array_equal(p["acc"].cpu().numpy()[rows], ra)
+            assert np.array_equal(p["y"].cpu().numpy()[rows].view(np.uint16), ry.view(np.uint16))
+        else:
+            ref = sherry_ref.gemv_bf16(sub, sw[rows], len(rows), k, x)
+            check_fp_tolerance(p["y"].cpu().numpy()[rows], ref)

@@ -1,0 +1,303 @@
+// C ABI of libsherry.so: argument validation, device check and dispatch.
+//
+// Every argument check runs on the host before the first HIP call, so an
+// invalid call returns a status without touching the device (and can be
+// tested without a GPU).  Contracts are documented in include/sherry.h.
+#include <atomic>
+#include <cstring>
+#include <limits>
+
+#include "launch.h"
+#include "sherry.h"
+
+using namespace sherry;
+
+namespace {
+
+constexpr int64_t kMaxDim = std::numeric_limits<int32_t>::max();
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t dt_size(sherry_dtype d) {
+  switch (d) {
+    case SHERRY_I8: return 1;
+    case SHERRY_F16:
+    case SHERRY_BF16: return 2;
+    case SHERRY_I32:
+    case SHERRY_F32: return 4;
+  }
+  return 0;
+}
+
+bool is_scale_dt(sherry_dtype d) { return d == SHERRY_F32 || d == SHERRY_F16; }
+
+// n x k packed matrix shape: positive, k % 128 == 0, every index fits int32
+// rows and int64 words.
+sherry_status check_nk(int64_t n, int64_t k) {
+  if (n <= 0 || k <= 0) return SHERRY_EINVAL;
+  if (k % kGroupWeights != 0) return SHERRY_ESHAPE;
+  if (n > kMaxDim || k > kMaxDim) return SHERRY_ESHAPE;
+  const int64_t g = k / kGroupWeights;
+  if (n > std::numeric_limits<int64_t>::max() / (g * 32)) return SHERRY_ESHAPE;
+  return SHERRY_OK;
+}
+
+std::atomic<int> g_dev_state[256];  // 0 unknown, 1 gfx950, 2 other
+
+sherry_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return SHERRY_EDEVICE;
+  if (dev < 256) {
+    const int s = g_dev_state[dev].load(std::memory_order_relaxed);
+    if (s == 1) return SHERRY_OK;
+    if (s == 2) return SHERRY_EDEVICE;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SHERRY_EDEVICE;
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < 256) g_dev_state[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? SHERRY_OK : SHERRY_EDEVICE;
+}
+
+sherry_status launched(hipError_t e) { return e == hipSuccess ? SHERRY_OK : SHERRY_ELAUNCH; }
+
+// Shared validation of a batch-1 product (both formats).
+sherry_status check_gemv(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,
+                         const void* x, sherry_dtype x_dt, const float* x_scale, const int32_t* acc, const void* y,
+                         sherry_dtype y_dt, bool allow_bf16) {
+  if (!codes || !w_scales || !x || (!acc && !y)) return SHERRY_EINVAL;
+  if (sherry_status s = check_nk(n, k)) return s;
+  if (!is_scale_dt(s_dt)) return SHERRY_EDTYPE;
+  if (x_dt == SHERRY_I8) {
+    if (y && y_dt != SHERRY_F32 && y_dt != SHERRY_F16) return SHERRY_EDTYPE;
+  } else if (x_dt == SHERRY_BF16 && allow_bf16) {
+    if (acc || x_scale || !y || y_dt != SHERRY_F32) return SHERRY_EDTYPE;
+  } else {
+    return SHERRY_EDTYPE;
+  }
+  if (!aligned(codes, 4) || !aligned(x, 16) || !aligned(w_scales, dt_size(s_dt)) || (acc && !aligned(acc, 4)) ||
+      (x_scale && !aligned(x_scale, 4)) || (y && !aligned(y, dt_size(y_dt))))
+    return SHERRY_EALIGN;
+  return SHERRY_OK;
+}
+
+GemvDesc make_desc(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,
+                   const void* x, const float* x_scale, int32_t* acc, void* y, sherry_dtype y_dt) {
+  GemvDesc d;
+  d.codes = codes;
+  d.w_scales = w_scales;
+  d.x = x;
+  d.x_scale = x_scale;
+  d.acc = acc;
+  d.y = y;
+  d.n = static_cast<int32_t>(n);
+  d.k = static_cast<int32_t>(k);
+  d.flags = (s_dt == SHERRY_F16 ? kFlagScaleF16 : 0) | (y && y_dt == SHERRY_F16 ? kFlagYF16 : 0);
+  d.kclass = kclass_of(k);
+  return d;
+}
+
+sherry_status gemv_impl(int32_t format, const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n,
+                        int64_t k, const void* x, sherry_dtype x_dt, const float* x_scale, int32_t* acc, void* y,
+                        sherry_dtype y_dt, hipStream_t stream) {
+  if (sherry_status s = check_gemv(codes, w_scales, s_dt, n, k, x, x_dt, x_scale, acc, y, y_dt,
+                                   format == kFmtSherry))
+    return s;
+  if (sherry_status s = check_device()) return s;
+  const GemvDesc d = make_desc(codes, w_scales, s_dt, n, k, x, x_scale, acc, y, y_dt);
+  return launched(launch_gemv(d, x_dt == SHERRY_BF16, format, stream));
+}
+
+sherry_status gemm_impl(int32_t format, const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n,
+                        int64_t k, const void* x, sherry_dtype x_dt, int64_t m, int64_t ldx, const float* x_scales,
+                        int32_t* acc, void* y, sherry_dtype y_dt, int64_t ldy, hipStream_t stream) {
+  if (!codes || !w_scales || !x || (!acc && !y)) return SHERRY_EINVAL;
+  if (m <= 0) return SHERRY_EINVAL;
+  if (sherry_status s = check_nk(n, k)) return s;
+  if (m > 16 * 65535 || ldx < k || ldx % 16 != 0 || (y && ldy < n)) return SHERRY_ESHAPE;
+  if (ldx > std::numeric_limits<int64_t>::max() / m || (y && ldy > std::numeric_limits<int64_t>::max() / m))
+    return SHERRY_ESHAPE;
+  if (!is_scale_dt(s_dt) || x_dt != SHERRY_I8) return SHERRY_EDTYPE;
+  if (y && y_dt != SHERRY_F32 && y_dt != SHERRY_F16) return SHERRY_EDTYPE;
+  if (!aligned(codes, 4) || !aligned(x, 16) || !aligned(w_scales, dt_size(s_dt)) || (acc && !aligned(acc, 4)) ||
+      (x_scales && !aligned(x_scales, 4)) || (y && !aligned(y, dt_size(y_dt))))
+    return SHERRY_EALIGN;
+  if (sherry_status s = check_device()) return s;
+  GemmDesc d;
+  d.codes = codes;
+  d.w_scales = w_scales;
+  d.x = static_cast<const int8_t*>(x);
+  d.x_scales = x_scales;
+  d.acc = acc;
+  d.y = y;
+  d.ldx = ldx;
+  d.ldy = y ? ldy : n;
+  d.n = static_cast<int32_t>(n);
+  d.k = static_cast<int32_t>(k);
+  d.m = static_cast<int32_t>(m);
+  d.flags = (s_dt == SHERRY_F16 ? kFlagScaleF16 : 0) | (y && y_dt == SHERRY_F16 ? kFlagYF16 : 0);
+  return launched(launch_gemm(d, format, stream));
+}
+
+// Grouped plan: header | GemvDesc[count] | PlanTile[n_tiles].
+int64_t plan_tiles(const sherry_gemv_problem* probs, int32_t count) {
+  int64_t tiles = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const int32_t kc = kclass_of(probs[i].k);
+    const int64_t rows = static_cast<int64_t>(rows_per_iter(kc)) * kGroupedIters;
+    tiles += (probs[i].n + rows - 1) / rows;
+  }
+  return tiles;
+}
+
+size_t plan_bytes_impl(const sherry_gemv_problem* probs, int32_t count) {
+  if (!probs || count <= 0) return 0;
+  for (int32_t i = 0; i < count; ++i)
+    if (check_nk(probs[i].n, probs[i].k) != SHERRY_OK) return 0;
+  const int64_t tiles = plan_tiles(probs, count);
+  if (tiles > kMaxDim) return 0;
+  return sizeof(PlanHeader) + sizeof(GemvDesc) * static_cast<size_t>(count) + sizeof(PlanTile) * tiles;
+}
+
+sherry_status plan_impl(int32_t format, const sherry_gemv_problem* probs, int32_t count, sherry_dtype s_dt,
+                        sherry_dtype x_dt, sherry_dtype y_dt, void* plan, size_t plan_bytes) {
+  if (!probs || count <= 0 || !plan) return SHERRY_EINVAL;
+  for (int32_t i = 0; i < count; ++i) {
+    const sherry_gemv_problem& p = probs[i];
+    if (sherry_status s = check_gemv(p.codes, p.w_scales, s_dt, p.n, p.k, p.x, x_dt, p.x_scale, p.acc, p.y, y_dt,
+                                     format == kFmtSherry))
+      return s;
+  }
+  const size_t need = plan_bytes_impl(probs, count);
+  if (need == 0) return SHERRY_ESHAPE;
+  if (plan_bytes < need) return SHERRY_EINVAL;
+  if (!aligned(plan, 8)) return SHERRY_EALIGN;
+  char* out = static_cast<char*>(plan);
+  PlanHeader h;
+  std::memset(&h, 0, sizeof(h));
+  h.magic = kPlanMagic;
+  h.version = kPlanVersion;
+  h.count = count;
+  h.n_tiles = static_cast<int32_t>(plan_tiles(probs, count));
+  h.s_dt = s_dt;
+  h.x_dt = x_dt;
+  h.y_dt = y_dt;
+  h.format = format;
+  h.bytes = need;
+  for (int32_t i = 0; i < count; ++i)
+    if (kclass_of(probs[i].k) == k3072) h.reserved[0] = 1;
+  std::memcpy(out, &h, sizeof(h));
+  GemvDesc* descs = reinterpret_cast<GemvDesc*>(out + sizeof(PlanHeader));
+  PlanTile* tiles = reinterpret_cast<PlanTile*>(descs + count);
+  int64_t t = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    const sherry_gemv_problem& p = probs[i];
+    descs[i] = make_desc(p.codes, p.w_scales, s_dt, p.n, p.k, p.x, p.x_scale, p.acc, p.y, y_dt);
+    const int64_t rows = static_cast<int64_t>(rows_per_iter(descs[i].kclass)) * kGroupedIters;
+    for (int64_t r0 = 0; r0 < p.n; r0 += rows) tiles[t++] = PlanTile{i, static_cast<int32_t>(r0)};
+  }
+  return SHERRY_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sherry_version(void) { return "0.1.0"; }
+
+const char* sherry_status_str(sherry_status s) {
+  switch (s) {
+    case SHERRY_OK: return "SHERRY_OK";
+    case SHERRY_EINVAL: return "SHERRY_EINVAL: null pointer, non-positive size or bad argument";
+    case SHERRY_ESHAPE: return "SHERRY_ESHAPE: k % 128 != 0, leading dimension too small or size overflow";
+    case SHERRY_EDTYPE: return "SHERRY_EDTYPE: unsupported dtype combination";
+    case SHERRY_EALIGN: return "SHERRY_EALIGN: pointer or leading dimension misaligned";
+    case SHERRY_EDEVICE: return "SHERRY_EDEVICE: no HIP device or the current device is not gfx950";
+    case SHERRY_ELAUNCH: return "SHERRY_ELAUNCH: kernel launch failed";
+  }
+  return "SHERRY_UNKNOWN_STATUS";
+}
+
+size_t sherry_packed_bytes(int64_t n, int64_t k) {
+  if (check_nk(n, k) != SHERRY_OK) return 0;
+  return static_cast<size_t>(n) * static_cast<size_t>(k / kGroupWeights) * kGroupWords * 4;
+}
+
+sherry_status sherry_pack(const void* w, sherry_dtype w_dt, int64_t n, int64_t k, int64_t ldw, uint32_t* codes,
+                          void* scales, sherry_dtype s_dt, hipStream_t stream) {
+  if (!w || !codes || !scales) return SHERRY_EINVAL;
+  if (sherry_status s = check_nk(n, k)) return s;
+  if (ldw < k || ldw > std::numeric_limits<int64_t>::max() / n) return SHERRY_ESHAPE;
+  if (w_dt != SHERRY_F32 && w_dt != SHERRY_F16 && w_dt != SHERRY_BF16) return SHERRY_EDTYPE;
+  if (!is_scale_dt(s_dt)) return SHERRY_EDTYPE;
+  if (!aligned(w, 4 * dt_size(w_dt)) || ldw % 4 != 0 || !aligned(codes, 4) || !aligned(scales, dt_size(s_dt)))
+    return SHERRY_EALIGN;
+  if (sherry_status s = check_device()) return s;
+  return launched(launch_pack(w, w_dt, n, k, ldw, codes, scales, s_dt == SHERRY_F16, stream));
+}
+
+sherry_status sherry_gemv(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,
+                          const void* x, sherry_dtype x_dt, const float* x_scale, int32_t* acc, void* y,
+                          sherry_dtype y_dt, hipStream_t stream) {
+  return gemv_impl(kFmtSherry, codes, w_scales, s_dt, n, k, x, x_dt, x_scale, acc, y, y_dt, stream);
+}
+
+size_t sherry_gemv_plan_bytes(const sherry_gemv_problem* probs, int32_t count) {
+  return plan_bytes_impl(probs, count);
+}
+
+sherry_status sherry_gemv_plan(const sherry_gemv_problem* probs, int32_t count, sherry_dtype s_dt,
+                               sherry_dtype x_dt, sherry_dtype y_dt, void* plan, size_t plan_bytes) {
+  return plan_impl(kFmtSherry, probs, count, s_dt, x_dt, y_dt, plan, plan_bytes);
+}
+
+sherry_status sherry_gemv_grouped(const void* plan_host, const void* plan_dev, hipStream_t stream) {
+  if (!plan_host || !plan_dev) return SHERRY_EINVAL;
+  if (!aligned(plan_host, 8) || !aligned(plan_dev, 8)) return SHERRY_EALIGN;
+  PlanHeader h;
+  std::memcpy(&h, plan_host, sizeof(h));
+  if (h.magic != kPlanMagic || h.version != kPlanVersion || h.count <= 0 || h.n_tiles < 0 ||
+      (h.format != kFmtSherry && h.format != kFmtTern2))
+    return SHERRY_EINVAL;
+  if (sherry_status s = check_device()) return s;
+  return launched(launch_gemv_grouped(&h, plan_dev, stream));
+}
+
+sherry_status sherry_gemm(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,
+                          const void* x, sherry_dtype x_dt, int64_t m, int64_t ldx, const float* x_scales,
+                          int32_t* acc, void* y, sherry_dtype y_dt, int64_t ldy, hipStream_t stream) {
+  return gemm_impl(kFmtSherry, codes, w_scales, s_dt, n, k, x, x_dt, m, ldx, x_scales, acc, y, y_dt, ldy, stream);
+}
+
+size_t tern2_packed_bytes(int64_t n, int64_t k) {
+  if (check_nk(n, k) != SHERRY_OK) return 0;
+  return static_cast<size_t>(n) * static_cast<size_t>(k) / 4;
+}
+
+sherry_status tern2_encode(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint32_t* codes, hipStream_t stream) {
+  if (!t || !codes) return SHERRY_EINVAL;
+  if (sherry_status s = check_nk(n, k)) return s;
+  if (ldt < k || ldt > std::numeric_limits<int64_t>::max() / n) return SHERRY_ESHAPE;
+  if (!aligned(t, 16) || ldt % 16 != 0 || !aligned(codes, 4)) return SHERRY_EALIGN;
+  if (sherry_status s = check_device()) return s;
+  return launched(launch_tern2_encode(t, n, k, ldt, codes, stream));
+}
+
+sherry_status tern2_gemv(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,
+                         const void* x, sherry_dtype x_dt, const float* x_scale, int32_t* acc, void* y,
+                         sherry_dtype y_dt, hipStream_t stream) {
+  return gemv_impl(kFmtTern2, codes, w_scales, s_dt, n, k, x, x_dt, x_scale, acc, y, y_dt, stream);
+}
+
+sherry_status tern2_gemv_plan(const sherry_gemv_problem* probs, int32_t count, sherry_dtype s_dt,
+                              sherry_dtype x_dt, sherry_dtype y_dt, void* plan, size_t plan_bytes) {
+  return plan_impl(kFmtTern2, probs, count, s_dt, x_dt, y_dt, plan, plan_bytes);
+}
+
+sherry_status tern2_gemm(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,
+                         const void* x, sherry_dtype x_dt, int64_t m, int64_t ldx, const float* x_scales,
+                         int32_t* acc, void* y, sherry_dtype y_dt, int64_t ldy, hipStream_t stream) {
+  return gemm_impl(kFmtTern2, codes, w_scales, s_dt, n, k, x, x_dt, m, ldx, x_scales, acc, y, y_dt, ldy, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,471 @@
+// Batch-1 products y = diag(s_w) * T * x on packed ternary weights
+// (decode-phase GEMV; "Sherry: Hardware-Efficient 1.25-Bit Ternary
+// Quantization via Fine-grained Sparsification", Abstract: 3:4 sparse ternary
+// blocks, four weights in five bits).
+//
+// The kernels stream the packed rows once from HBM and never materialise the
+// weights: each lane keeps its slice of x in registers (x-stationary) and
+// walks down the rows; per 4-weight block it expands the code to four int8
+// (or bf16) weights and accumulates with v_dot4_i32_i8 (or two
+// v_dot2_f32_bf16).  L lanes share one row and combine their partial sums
+// with DPP row operations; the lane that owns the row applies the scale.
+//
+// Row-to-lane mapping for L lanes per row and GPL groups per lane: lane
+// (row r, position p) owns groups p, p + L, ..., p + (GPL-1) L, so the L lanes
+// of a row read one contiguous run of 20 * L bytes per step.
+#include "formats.h"
+#include "launch.h"
+
+namespace sherry {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b),
+                                         c, false);
+}
+
+// Streamed once: non-temporal loads.  Callers clamp the row so every load is
+// in bounds and unconditional (a branch around a load would force a wait).
+template <int NW>
+__device__ __forceinline__ void load_words(uint32_t (&dst)[NW], const uint32_t* src) {
+#pragma unroll
+  for (int i = 0; i < NW; ++i) dst[i] = __builtin_nontemporal_load(src + i);
+}
+
+// ---------------------------------------------------------------- int8 x ---
+template <class Fmt, int L, int GPL>
+__device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, int row_end,
+                                             const uint32_t* tab, int32_t* out) {
+  constexpr int RPW = kWave / L;
+  constexpr int RPI = (kGemvThreads / kWave) * RPW;
+  constexpr int NW = Fmt::kWords;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int lp = lane % L;
+  const int rs = lane / L;
+  constexpr int G = GPL * L;
+
+  uint32_t xr[GPL][32];
+  const int8_t* x = static_cast<const int8_t*>(d.x);
+#pragma unroll
+  for (int t = 0; t < GPL; ++t) {
+    const uint4* xp = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(t * L + lp) * kGroupWeights);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint4 v = xp[q];
+      xr[t][4 * q + 0] = v.x;
+      xr[t][4 * q + 1] = v.y;
+      xr[t][4 * q + 2] = v.z;
+      xr[t][4 * q + 3] = v.w;
+    }
+  }
+  // Rows past the tile load the tile's last row instead (results discarded).
+  // Two register buffers alternate (loop unrolled by two): while one row is
+  // decoded, the next row's words are in flight into the other buffer.
+  const int last = row_end - 1;
+  const int r0 = row_begin + wave * RPW + rs;
+  const uint32_t* cbase = d.codes + static_cast<int64_t>(lp) * NW;
+  auto fetch = [&](uint32_t (&buf)[GPL][NW], int row) {
+    const int64_t rr = min(row, last);
+#pragma unroll
+    for (int t = 0; t < GPL; ++t) load_words(buf[t], cbase + (rr * G + t * L) * NW);
+  };
+  auto step = [&](const uint32_t (&buf)[GPL][NW], int row) {
+    int a4[4] = {0, 0, 0, 0};  // independent dot4 chains
+#pragma unroll
+    for (int t = 0; t < GPL; ++t) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j)
+        a4[j & 3] = __builtin_amdgcn_sdot4(static_cast<int>(Fmt::i8x4(buf[t], j, tab)),
+                                           static_cast<int>(xr[t][j]), a4[j & 3], false);
+    }
+    const int acc = reduce_add_i32<L>((a4[0] + a4[1]) + (a4[2] + a4[3]));
+    if (lp == 0 && row < row_end) out[row - row_begin] = acc;
+  };
+  uint32_t bufa[GPL][NW], bufb[GPL][NW];
+  fetch(bufa, r0);
+  int r = r0;
+  for (int base = row_begin; base < row_end; base += 2 * RPI, r += 2 * RPI) {
+    fetch(bufb, r + RPI);
+    step(bufa, r);
+    if (base + RPI >= row_end) break;
+    fetch(bufa, r + 2 * RPI);
+    step(bufb, r + RPI);
+  }
+}
+
+// Any k % 128 == 0: 64 lanes per row, x read per group (not register-resident).
+template <class Fmt>
+__device__ __forceinline__ void gemv_i8_rows_generic(const GemvDesc& d, int row_begin, int row_end,
+                                                     const uint32_t* tab, int32_t* out) {
+  constexpr int NW = Fmt::kWords;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int G = d.k / kGroupWeights;
+  const int8_t* x = static_cast<const int8_t*>(d.x);
+  for (int r = row_begin + wave; r < row_end; r += kGemvThreads / kWave) {
+    int acc = 0;
+    for (int g = lane; g < G; g += kWave) {
+      uint32_t w[NW];
+      load_words(w, d.codes + (static_cast<int64_t>(r) * G + g) * NW);
+      const uint4* xp = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(g) * kGroupWeights);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint4 v = xp[q];
+        acc = __builtin_amdgcn_sdot4(static_cast<int>(Fmt::i8x4(w, 4 * q + 0, tab)), static_cast<int>(v.x), acc, false);
+        acc = __builtin_amdgcn_sdot4(static_cast<int>(Fmt::i8x4(w, 4 * q + 1, tab)), static_cast<int>(v.y), acc, false);
+        acc = __builtin_amdgcn_sdot4(static_cast<int>(Fmt::i8x4(w, 4 * q + 2, tab)), static_cast<int>(v.z), acc, false);
+        acc = __builtin_amdgcn_sdot4(static_cast<int>(Fmt::i8x4(w, 4 * q + 3, tab)), static_cast<int>(v.w), acc, false);
+      }
+    }
+    acc = reduce_add_i32<64>(acc);
+    if (lane == 0) out[r - row_begin] = acc;
+  }
+}
+
+// ---------------------------------------------------------------- bf16 x ---
+// Weights expanded to four bf16 (one 8-byte table entry) per code, two
+// v_dot2_f32_bf16 per block; fp32 accumulation, then y = acc * s_w.
+template <int L, int GPL>
+__device__ __forceinline__ void gemv_bf16_rows(const GemvDesc& d, int row_begin, int row_end, const uint2* tab,
+                                               float* out) {
+  constexpr int RPW = kWave / L;
+  constexpr int RPI = (kGemvThreads / kWave) * RPW;
+  constexpr int NW = kGroupWords;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int lp = lane % L;
+  const int rs = lane / L;
+  constexpr int G = GPL * L;
+
+  uint32_t xr[GPL][64];
+  const uint16_t* x = static_cast<const uint16_t*>(d.x);
+#pragma unroll
+  for (int t = 0; t < GPL; ++t) {
+    const uint4* xp = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(t * L + lp) * kGroupWeights);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const uint4 v = xp[q];
+      xr[t][4 * q + 0] = v.x;
+      xr[t][4 * q + 1] = v.y;
+      xr[t][4 * q + 2] = v.z;
+      xr[t][4 * q + 3] = v.w;
+    }
+  }
+  const int last = row_end - 1;
+  const int r0 = row_begin + wave * RPW + rs;
+  const uint32_t* cbase = d.codes + static_cast<int64_t>(lp) * NW;
+  auto fetch = [&](uint32_t (&buf)[GPL][NW], int row) {
+    const int64_t rr = min(row, last);
+#pragma unroll
+    for (int t = 0; t < GPL; ++t) load_words(buf[t], cbase + (rr * G + t * L) * NW);
+  };
+  auto step = [&](const uint32_t (&buf)[GPL][NW], int row) {
+    float a2[2] = {0.0f, 0.0f};  // two chains: slot pairs (0,1) and (2,3)
+#pragma unroll
+    for (int t = 0; t < GPL; ++t) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const uint2 wv = lds_u64(tab, code_offset<3>(buf[t], j));
+        a2[0] = dot2_bf16(wv.x, xr[t][2 * j], a2[0]);
+        a2[1] = dot2_bf16(wv.y, xr[t][2 * j + 1], a2[1]);
+      }
+    }
+    const float acc = reduce_add_f32<L>(a2[0] + a2[1]);
+    if (lp == 0 && row < row_end) out[row - row_begin] = acc;
+  };
+  uint32_t bufa[GPL][NW], bufb[GPL][NW];
+  fetch(bufa, r0);
+  int r = r0;
+  for (int base = row_begin; base < row_end; base += 2 * RPI, r += 2 * RPI) {
+    fetch(bufb, r + RPI);
+    step(bufa, r);
+    if (base + RPI >= row_end) break;
+    fetch(bufa, r + 2 * RPI);
+    step(bufb, r + RPI);
+  }
+}
+
+__device__ __forceinline__ void gemv_bf16_rows_generic(const GemvDesc& d, int row_begin, int row_end,
+                                                       const uint2* tab, float* out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int G = d.k / kGroupWeights;
+  const uint16_t* x = static_cast<const uint16_t*>(d.x);
+  for (int r = row_begin + wave; r < row_end; r += kGemvThreads / kWave) {
+    float acc = 0.0f;
+    for (int g = lane; g < G; g += kWave) {
+      uint32_t w[kGroupWords];
+      load_words(w, d.codes + (static_cast<int64_t>(r) * G + g) * kGroupWords);
+      const uint4* xp = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(g) * kGroupWeights);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const uint4 v = xp[q];
+        const uint2 w0 = lds_u64(tab, code_offset<3>(w, 2 * q));
+        const uint2 w1 = lds_u64(tab, code_offset<3>(w, 2 * q + 1));
+        acc = dot2_bf16(w0.x, v.x, acc);
+        acc = dot2_bf16(w0.y, v.y, acc);
+        acc = dot2_bf16(w1.x, v.z, acc);
+        acc = dot2_bf16(w1.y, v.w, acc);
+      }
+    }
+    acc = reduce_add_f32<64>(acc);
+    if (lane == 0) out[r - row_begin] = acc;
+  }
+}
+
+// ---------------------------------------------------------------- kernels ---
+// Row results go to LDS during the row loop; after it the workgroup applies
+// the epilogue and writes the tile's outputs in one coalesced pass.  Keeping
+// global stores out of the loop keeps the prefetched loads in flight.
+constexpr int kMaxTileRows = 2048;
+
+__device__ __forceinline__ void finalize_i8(const GemvDesc& d, int row0, int row1, const int32_t* res) {
+  const bool s_f16 = d.flags & kFlagScaleF16;
+  const bool y_f16 = d.flags & kFlagYF16;
+  const bool has_sx = d.x_scale != nullptr;
+  const float sx = has_sx ? *d.x_scale : 1.0f;
+  for (int i = threadIdx.x; i < row1 - row0; i += blockDim.x) {
+    const int r = row0 + i;
+    if (d.acc) d.acc[r] = res[i];
+    if (d.y) store_y(d.y, r, epilogue_i32(res[i], load_scale(d.w_scales, r, s_f16), sx, has_sx), y_f16);
+  }
+}
+
+__device__ __forceinline__ void finalize_bf16(const GemvDesc& d, int row0, int row1, const float* res) {
+  const bool s_f16 = d.flags & kFlagScaleF16;
+  for (int i = threadIdx.x; i < row1 - row0; i += blockDim.x) {
+    const int r = row0 + i;
+    reinterpret_cast<float*>(d.y)[r] = __fmul_rn(res[i], load_scale(d.w_scales, r, s_f16));
+  }
+}
+
+// Single problem: one kernel per class, so each keeps its own register count.
+template <class Fmt, int L, int GPL>
+__global__ __launch_bounds__(kGemvThreads) void gemv_i8_kernel(GemvDesc d, int tile_rows) {
+  __shared__ uint32_t tab[32];
+  __shared__ int32_t res[kMaxTileRows];
+  const int row0 = blockIdx.x * tile_rows;
+  const int row1 = min(row0 + tile_rows, d.n);
+  Fmt::init_table(tab, threadIdx.x);
+  __syncthreads();
+  if (L == 0)
+    gemv_i8_rows_generic<Fmt>(d, row0, row1, tab, res);
+  else
+    gemv_i8_rows<Fmt, (L > 0 ? L : 64), GPL>(d, row0, row1, tab, res);
+  __syncthreads();
+  finalize_i8(d, row0, row1, res);
+}
+
+template <int L, int GPL>
+__global__ __launch_bounds__(kGemvThreads) void gemv_bf16_kernel(GemvDesc d, int tile_rows) {
+  __shared__ uint2 tab[32];
+  __shared__ float res[kMaxTileRows];
+  const int row0 = blockIdx.x * tile_rows;
+  const int row1 = min(row0 + tile_rows, d.n);
+  if (threadIdx.x < 32) tab[threadIdx.x] = decode_bf16x4(threadIdx.x);
+  __syncthreads();
+  if (L == 0)
+    gemv_bf16_rows_generic(d, row0, row1, tab, res);
+  else
+    gemv_bf16_rows<(L > 0 ? L : 64), GPL>(d, row0, row1, tab, res);
+  __syncthreads();
+  finalize_bf16(d, row0, row1, res);
+}
+
+// Grouped: one workgroup per plan tile {problem, first row}; a tile spans
+// kGroupedIters row iterations of its problem's class.  WIDE selects the
+// family that also holds the 3-groups-per-lane class (k = 3072), which needs
+// more registers; plans without k = 3072 use the narrow family.
+__device__ __forceinline__ int tile_rows_of(int32_t kc) {
+  int lanes = 64;
+  switch (kc) {
+    case k1024: lanes = 8; break;
+    case k2048: lanes = 16; break;
+    case k4096: lanes = 32; break;
+    case k8192: lanes = 64; break;
+    case k3072: lanes = 8; break;
+    default: lanes = 64; break;
+  }
+  return (kGemvThreads / kWave) * (kWave / lanes) * kGroupedIters;
+}
+constexpr int kMaxGroupedTileRows = (kGemvThreads / kWave) * (kWave / 8) * kGroupedIters;
+
+template <class Fmt, bool WIDE>
+__global__ __launch_bounds__(kGemvThreads) void gemv_i8_grouped_kernel(const char* plan) {
+  __shared__ uint32_t tab[32];
+  __shared__ int32_t res[kMaxGroupedTileRows];
+  Fmt::init_table(tab, threadIdx.x);
+  const PlanHeader* h = reinterpret_cast<const PlanHeader*>(plan);
+  const GemvDesc* descs = reinterpret_cast<const GemvDesc*>(plan + sizeof(PlanHeader));
+  const PlanTile* tiles = reinterpret_cast<const PlanTile*>(descs + h->count);
+  const PlanTile tl = tiles[blockIdx.x];
+  const GemvDesc d = descs[tl.prob];
+  const int row0 = tl.row0;
+  const int row1 = min(row0 + tile_rows_of(d.kclass), d.n);
+  __syncthreads();
+  switch (d.kclass) {
+    case k1024: gemv_i8_rows<Fmt, 8, 1>(d, row0, row1, tab, res); break;
+    case k2048: gemv_i8_rows<Fmt, 16, 1>(d, row0, row1, tab, res); break;
+    case k4096: gemv_i8_rows<Fmt, 32, 1>(d, row0, row1, tab, res); break;
+    case k8192: gemv_i8_rows<Fmt, 64, 1>(d, row0, row1, tab, res); break;
+    case k3072:
+      if (WIDE) {
+        gemv_i8_rows<Fmt, 8, 3>(d, row0, row1, tab, res);
+        break;
+      }
+      [[fallthrough]];
+    default: gemv_i8_rows_generic<Fmt>(d, row0, row1, tab, res); break;
+  }
+  __syncthreads();
+  finalize_i8(d, row0, row1, res);
+}
+
+template <bool WIDE>
+__global__ __launch_bounds__(kGemvThreads) void gemv_bf16_grouped_kernel(const char* plan) {
+  __shared__ uint2 tab[32];
+  __shared__ float res[kMaxGroupedTileRows];
+  if (threadIdx.x < 32) tab[threadIdx.x] = decode_bf16x4(threadIdx.x);
+  const PlanHeader* h = reinterpret_cast<const PlanHeader*>(plan);
+  const GemvDesc* descs = reinterpret_cast<const GemvDesc*>(plan + sizeof(PlanHeader));
+  const PlanTile* tiles = reinterpret_cast<const PlanTile*>(descs + h->count);
+  const PlanTile tl = tiles[blockIdx.x];
+  const GemvDesc d = descs[tl.prob];
+  const int row0 = tl.row0;
+  const int row1 = min(row0 + tile_rows_of(d.kclass), d.n);
+  __syncthreads();
+  switch (d.kclass) {
+    case k1024: gemv_bf16_rows<8, 1>(d, row0, row1, tab, res); break;
+    case k2048: gemv_bf16_rows<16, 1>(d, row0, row1, tab, res); break;
+    case k4096: gemv_bf16_rows<32, 1>(d, row0, row1, tab, res); break;
+    case k8192: gemv_bf16_rows<64, 1>(d, row0, row1, tab, res); break;
+    case k3072:
+      if (WIDE) {
+        gemv_bf16_rows<8, 3>(d, row0, row1, tab, res);
+        break;
+      }
+      [[fallthrough]];
+    default: gemv_bf16_rows_generic(d, row0, row1, tab, res); break;
+  }
+  __syncthreads();
+  finalize_bf16(d, row0, row1, res);
+}
+
+// ---------------------------------------------------------- tern2 encode ---
+// One thread per output word: 16 int8 weights -> 2-bit fields at 8p + 2q.
+__global__ __launch_bounds__(256) void tern2_encode_kernel(const int8_t* t, int64_t n, int64_t k, int64_t ldt,
+                                                           uint32_t* codes) {
+  const int64_t wpr = k / 16;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= n * wpr) return;
+  const int64_t r = idx / wpr;
+  const int64_t c = idx % wpr;
+  const uint4 v = *reinterpret_cast<const uint4*>(t + r * ldt + c * 16);
+  const uint32_t b[4] = {v.x, v.y, v.z, v.w};
+  uint32_t w = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int8_t val = static_cast<int8_t>((b[i >> 2] >> (8 * (i & 3))) & 0xFF);
+    const uint32_t f = val < 0 ? 3u : static_cast<uint32_t>(val);
+    w |= (f & 3u) << (8 * (i & 3) + 2 * (i >> 2));
+  }
+  codes[idx] = w;
+}
+
+}  // namespace
+
+int tile_iters_for(int64_t n, int rpi) {
+  // Enough workgroups to cover the chip (>= 1024 when the matrix allows it);
+  // a tile never exceeds kMaxTileRows rows (its scales are staged in LDS).
+  const int64_t per = (n + rpi - 1) / rpi;
+  int64_t iters = (per + 1023) / 1024;
+  if (iters < 1) iters = 1;
+  if (iters * rpi > kMaxTileRows) iters = kMaxTileRows / rpi;
+  return static_cast<int>(iters);
+}
+
+namespace {
+
+template <class Fmt, int L, int GPL>
+void launch_i8(const GemvDesc& d, unsigned grid, int tile_rows, hipStream_t stream) {
+  hipLaunchKernelGGL((gemv_i8_kernel<Fmt, L, GPL>), dim3(grid), dim3(kGemvThreads), 0, stream, d, tile_rows);
+}
+
+template <class Fmt>
+void launch_i8_class(const GemvDesc& d, unsigned grid, int tile_rows, hipStream_t stream) {
+  switch (d.kclass) {
+    case k1024: launch_i8<Fmt, 8, 1>(d, grid, tile_rows, stream); break;
+    case k2048: launch_i8<Fmt, 16, 1>(d, grid, tile_rows, stream); break;
+    case k4096: launch_i8<Fmt, 32, 1>(d, grid, tile_rows, stream); break;
+    case k8192: launch_i8<Fmt, 64, 1>(d, grid, tile_rows, stream); break;
+    case k3072: launch_i8<Fmt, 8, 3>(d, grid, tile_rows, stream); break;
+    default: launch_i8<Fmt, 0, 1>(d, grid, tile_rows, stream); break;
+  }
+}
+
+template <int L, int GPL>
+void launch_bf16(const GemvDesc& d, unsigned grid, int tile_rows, hipStream_t stream) {
+  hipLaunchKernelGGL((gemv_bf16_kernel<L, GPL>), dim3(grid), dim3(kGemvThreads), 0, stream, d, tile_rows);
+}
+
+void launch_bf16_class(const GemvDesc& d, unsigned grid, int tile_rows, hipStream_t stream) {
+  switch (d.kclass) {
+    case k1024: launch_bf16<8, 1>(d, grid, tile_rows, stream); break;
+    case k2048: launch_bf16<16, 1>(d, grid, tile_rows, stream); break;
+    case k4096: launch_bf16<32, 1>(d, grid, tile_rows, stream); break;
+    case k8192: launch_bf16<64, 1>(d, grid, tile_rows, stream); break;
+    case k3072: launch_bf16<8, 3>(d, grid, tile_rows, stream); break;
+    default: launch_bf16<0, 1>(d, grid, tile_rows, stream); break;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const GemvDesc& d, bool bf16_x, int32_t format, hipStream_t stream) {
+  const int rpi = rows_per_iter(d.kclass);
+  const int tile_rows = rpi * tile_iters_for(d.n, rpi);
+  const unsigned grid = static_cast<unsigned>((d.n + tile_rows - 1) / tile_rows);
+  if (bf16_x)
+    launch_bf16_class(d, grid, tile_rows, stream);
+  else if (format == kFmtTern2)
+    launch_i8_class<Tern2>(d, grid, tile_rows, stream);
+  else
+    launch_i8_class<Sherry3of4>(d, grid, tile_rows, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_grouped(const PlanHeader* h, const void* dev, hipStream_t stream) {
+  if (h->n_tiles == 0) return hipSuccess;
+  const char* plan = static_cast<const char*>(dev);
+  const dim3 grid(h->n_tiles), block(kGemvThreads);
+  const bool wide = h->reserved[0] != 0;  // some problem has k = 3072
+  if (h->x_dt == SHERRY_BF16) {
+    if (wide)
+      hipLaunchKernelGGL((gemv_bf16_grouped_kernel<true>), grid, block, 0, stream, plan);
+    else
+      hipLaunchKernelGGL((gemv_bf16_grouped_kernel<false>), grid, block, 0, stream, plan);
+  } else if (h->format == kFmtTern2) {
+    if (wide)
+      hipLaunchKernelGGL((gemv_i8_grouped_kernel<Tern2, true>), grid, block, 0, stream, plan);
+    else
+      hipLaunchKernelGGL((gemv_i8_grouped_kernel<Tern2, false>), grid, block, 0, stream, plan);
+  } else {
+    if (wide)
+      hipLaunchKernelGGL((gemv_i8_grouped_kernel<Sherry3of4, true>), grid, block, 0, stream, plan);
+    else
+      hipLaunchKernelGGL((gemv_i8_grouped_kernel<Sherry3of4, false>), grid, block, 0, stream, plan);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_tern2_encode(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint32_t* codes,
+                               hipStream_t stream) {
+  const int64_t words = n * (k / 16);
+  const unsigned grid = static_cast<unsigned>((words + 255) / 256);
+  hipLaunchKernelGGL(tern2_encode_kernel, dim3(grid), dim3(256), 0, stream, t, n, k, ldt, codes);
+  return hipGetLastError();
+}
+
+}  // namespace sherry

@@ -1,0 +1,88 @@
+// Internal launcher interface between the C ABI (abi.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace sherry {
+
+// Reduction-length classes with a register-resident (x-stationary) kernel.
+// L = lanes that share one row, GPL = 128-weight groups per lane (L*GPL*128 = k).
+enum KClass : int32_t { kGeneric = 0, k1024 = 1, k2048 = 2, k4096 = 3, k8192 = 4, k3072 = 5 };
+
+inline int32_t kclass_of(int64_t k) {
+  switch (k) {
+    case 1024: return k1024;
+    case 2048: return k2048;
+    case 4096: return k4096;
+    case 8192: return k8192;
+    case 3072: return k3072;
+    default: return kGeneric;
+  }
+}
+// Lanes per row for a class (64 for the generic kernel).
+inline int lanes_per_row(int32_t kc) {
+  switch (kc) {
+    case k1024: return 8;
+    case k2048: return 16;
+    case k4096: return 32;
+    case k8192: return 64;
+    case k3072: return 8;
+    default: return 64;
+  }
+}
+constexpr int kGemvThreads = 256;  // 4 waves
+// Rows one GEMV workgroup advances per iteration.
+inline int rows_per_iter(int32_t kc) { return (kGemvThreads / kWave) * (kWave / lanes_per_row(kc)); }
+
+enum Format : int32_t { kFmtSherry = 0, kFmtTern2 = 1 };
+
+struct PlanHeader {
+  uint32_t magic;
+  uint32_t version;
+  int32_t count;
+  int32_t n_tiles;
+  int32_t s_dt;
+  int32_t x_dt;
+  int32_t y_dt;
+  int32_t format;
+  uint64_t bytes;
+  uint64_t reserved[3];  // reserved[0]: nonzero if some problem has k = 3072
+};
+static_assert(sizeof(PlanHeader) == 64, "plan header layout");
+constexpr uint32_t kPlanMagic = 0x53485950u;  // "PYHS"
+constexpr uint32_t kPlanVersion = 1;
+constexpr int kGroupedIters = 4;  // row iterations per grouped tile
+
+struct PlanTile {
+  int32_t prob;
+  int32_t row0;
+};
+
+// GEMM (M tokens) problem.
+struct GemmDesc {
+  const uint32_t* codes;
+  const void* w_scales;
+  const int8_t* x;
+  const float* x_scales;
+  int32_t* acc;
+  void* y;
+  int64_t ldx;
+  int64_t ldy;
+  int32_t n;
+  int32_t k;
+  int32_t m;
+  int32_t flags;
+};
+
+hipError_t launch_pack(const void* w, int w_dt, int64_t n, int64_t k, int64_t ldw, uint32_t* codes,
+                       void* scales, bool s_f16, hipStream_t stream);
+hipError_t launch_gemv(const GemvDesc& d, bool bf16_x, int32_t format, hipStream_t stream);
+hipError_t launch_gemv_grouped(const PlanHeader* host, const void* dev, hipStream_t stream);
+hipError_t launch_gemm(const GemmDesc& d, int32_t format, hipStream_t stream);
+hipError_t launch_tern2_encode(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint32_t* codes,
+                               hipStream_t stream);
+
+}  // namespace sherry

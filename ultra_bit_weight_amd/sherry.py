@@ -1,0 +1,231 @@
+"""Thin ctypes binding over libsherry.so (C ABI in include/sherry.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libsherry.so.  Tensors are torch tensors on the current HIP device;
+the binding passes their data pointers and the current stream to the C ABI and
+raises SherryError on any non-OK status.  If the library is missing the binding
+raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libsherry.so")
+
+I8, I32, F16, BF16, F32 = 0, 1, 2, 3, 4
+_DT = {torch.int8: I8, torch.int32: I32, torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+STATUS = {0: "SHERRY_OK", 1: "SHERRY_EINVAL", 2: "SHERRY_ESHAPE", 3: "SHERRY_EDTYPE", 4: "SHERRY_EALIGN",
+          5: "SHERRY_EDEVICE", 6: "SHERRY_ELAUNCH"}
+
+EXPORTS = [
+    "sherry_version", "sherry_status_str", "sherry_packed_bytes", "sherry_pack", "sherry_gemv",
+    "sherry_gemv_plan_bytes", "sherry_gemv_plan", "sherry_gemv_grouped", "sherry_gemm",
+    "tern2_packed_bytes", "tern2_encode", "tern2_gemv", "tern2_gemv_plan", "tern2_gemm",
+]
+
+
+class SherryError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {msg}")
+        self.status = status
+
+
+class GemvProblem(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("w_scales", ctypes.c_void_p), ("n", ctypes.c_int64),
+                ("k", ctypes.c_int64), ("x", ctypes.c_void_p), ("x_scale", ctypes.c_void_p),
+                ("acc", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libsherry.so (after torch, so it binds to torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    vp, i64, i32, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+    sz = ctypes.c_size_t
+    lib.sherry_version.restype = ctypes.c_char_p
+    lib.sherry_status_str.restype = ctypes.c_char_p
+    lib.sherry_status_str.argtypes = [i]
+    lib.sherry_packed_bytes.restype = sz
+    lib.sherry_packed_bytes.argtypes = [i64, i64]
+    lib.tern2_packed_bytes.restype = sz
+    lib.tern2_packed_bytes.argtypes = [i64, i64]
+    lib.sherry_pack.restype = i
+    lib.sherry_pack.argtypes = [vp, i, i64, i64, i64, vp, vp, i, vp]
+    gemv_args = [vp, vp, i, i64, i64, vp, i, vp, vp, vp, i, vp]
+    for f in (lib.sherry_gemv, lib.tern2_gemv):
+        f.restype = i
+        f.argtypes = gemv_args
+    lib.sherry_gemv_plan_bytes.restype = sz
+    lib.sherry_gemv_plan_bytes.argtypes = [ctypes.POINTER(GemvProblem), i32]
+    for f in (lib.sherry_gemv_plan, lib.tern2_gemv_plan):
+        f.restype = i
+        f.argtypes = [ctypes.POINTER(GemvProblem), i32, i, i, i, vp, sz]
+    lib.sherry_gemv_grouped.restype = i
+    lib.sherry_gemv_grouped.argtypes = [vp, vp, vp]
+    gemm_args = [vp, vp, i, i64, i64, vp, i, i64, i64, vp, vp, vp, i, i64, vp]
+    for f in (lib.sherry_gemm, lib.tern2_gemm):
+        f.restype = i
+        f.argtypes = gemm_args
+    lib.tern2_encode.restype = i
+    lib.tern2_encode.argtypes = [vp, i64, i64, i64, vp, vp]
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise SherryError(fn, status, load().sherry_status_str(status).decode())
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+
+
+def packed_bytes(n: int, k: int) -> int:
+    return load().sherry_packed_bytes(n, k)
+
+
+def tern2_packed_bytes(n: int, k: int) -> int:
+    return load().tern2_packed_bytes(n, k)
+
+
+def version() -> str:
+    return load().sherry_version().decode()
+
+
+def empty_codes(n: int, k: int, device=None) -> torch.Tensor:
+    """Uninitialised code buffer for an n x k matrix (int32 view of the words)."""
+    words = packed_bytes(n, k) // 4
+    if words == 0:
+        raise ValueError(f"invalid shape n={n} k={k}")
+    return torch.empty(words, dtype=torch.int32, device=device or "cuda")
+
+
+def pack(w: torch.Tensor, scale_dtype=torch.float16):
+    """Real weights [n, k] (fp32/fp16/bf16, row stride = w.stride(0)) ->
+    (codes int32 [n*k*5/128], scales [n])."""
+    if w.dim() != 2 or w.stride(1) != 1 or not w.is_cuda:
+        raise ValueError("w must be a 2-D GPU tensor with unit column stride")
+    n, k = w.shape
+    codes = empty_codes(n, k, w.device)
+    scales = torch.empty(n, dtype=scale_dtype, device=w.device)
+    _check("sherry_pack", load().sherry_pack(w.data_ptr(), _DT[w.dtype], n, k, w.stride(0), codes.data_ptr(),
+                                             scales.data_ptr(), _DT[scale_dtype], _stream()))
+    return codes, scales
+
+
+def _gemv(fn_name, codes, scales, x, x_scale, acc, y):
+    _dev(codes, scales, x, x_scale, acc, y)
+    n = scales.numel()
+    k = x.numel()
+    f = getattr(load(), fn_name)
+    _check(fn_name, f(codes.data_ptr(), scales.data_ptr(), _DT[scales.dtype], n, k, x.data_ptr(), _DT[x.dtype],
+                      _ptr(x_scale), _ptr(acc), _ptr(y), _DT[y.dtype] if y is not None else F32, _stream()))
+
+
+def gemv(codes, scales, x, x_scale=None, out_dtype=torch.float16, want_acc=False, out=None, acc_out=None):
+    """y = diag(scales) T x for int8 or bf16 x.  Returns (acc or None, y or None)."""
+    n = scales.numel()
+    y = out if out is not None else (torch.empty(n, dtype=out_dtype, device=x.device) if out_dtype else None)
+    acc = acc_out if acc_out is not None else (torch.empty(n, dtype=torch.int32, device=x.device) if want_acc else None)
+    _gemv("sherry_gemv", codes, scales, x, x_scale, acc, y)
+    return acc, y
+
+
+def tern2_gemv(codes, scales, x, x_scale=None, out_dtype=torch.float16, want_acc=False, out=None, acc_out=None):
+    n = scales.numel()
+    y = out if out is not None else (torch.empty(n, dtype=out_dtype, device=x.device) if out_dtype else None)
+    acc = acc_out if acc_out is not None else (torch.empty(n, dtype=torch.int32, device=x.device) if want_acc else None)
+    _gemv("tern2_gemv", codes, scales, x, x_scale, acc, y)
+    return acc, y
+
+
+def _gemm(fn_name, codes, scales, x, x_scales, out_dtype, want_acc, n=None):
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [m, k] with unit column stride")
+    _dev(codes, scales, x_scales)
+    m, k = x.shape
+    n = scales.numel() if n is None else n
+    y = torch.empty(m, n, dtype=out_dtype, device=x.device) if out_dtype else None
+    acc = torch.empty(m, n, dtype=torch.int32, device=x.device) if want_acc else None
+    f = getattr(load(), fn_name)
+    _check(fn_name, f(codes.data_ptr(), scales.data_ptr(), _DT[scales.dtype], n, k, x.data_ptr(), _DT[x.dtype], m,
+                      x.stride(0), _ptr(x_scales), _ptr(acc), _ptr(y), _DT[out_dtype] if out_dtype else F32,
+                      y.stride(0) if y is not None else n, _stream()))
+    return acc, y
+
+
+def gemm(codes, scales, x, x_scales=None, out_dtype=torch.float16, want_acc=False):
+    """Y[m, r] = s_x[m] s_w[r] sum_k X[m, k] T[r, k] for int8 X [m, k]."""
+    return _gemm("sherry_gemm", codes, scales, x, x_scales, out_dtype, want_acc)
+
+
+def tern2_gemm(codes, scales, x, x_scales=None, out_dtype=torch.float16, want_acc=False):
+    return _gemm("tern2_gemm", codes, scales, x, x_scales, out_dtype, want_acc)
+
+
+def tern2_encode(t: torch.Tensor) -> torch.Tensor:
+    """Dense int8 ternary [n, k] -> 2-bit words (int32 view) [n * k / 16]."""
+    if t.dim() != 2 or t.stride(1) != 1 or not t.is_cuda or t.dtype != torch.int8:
+        raise ValueError("t must be a 2-D int8 GPU tensor with unit column stride")
+    n, k = t.shape
+    words = tern2_packed_bytes(n, k) // 4
+    if words == 0:
+        raise ValueError(f"invalid shape n={n} k={k}")
+    codes = torch.empty(words, dtype=torch.int32, device=t.device)
+    _check("tern2_encode", load().tern2_encode(t.data_ptr(), n, k, t.stride(0), codes.data_ptr(), _stream()))
+    return codes
+
+
+class GroupedGemv:
+    """Many batch-1 products in one launch.  `problems` is a list of dicts with
+    keys codes, scales, x, x_scale (or None), acc (or None), y (or None); all
+    share the scale / x / y dtypes.  The plan is built once on the host and
+    copied to the device; call() launches it on the current stream."""
+
+    def __init__(self, problems, tern2: bool = False):
+        lib = load()
+        arr = (GemvProblem * len(problems))()
+        self._keep = []
+        for i, p in enumerate(problems):
+            _dev(p["codes"], p["scales"], p["x"], p.get("x_scale"), p.get("acc"), p.get("y"))
+            arr[i] = GemvProblem(p["codes"].data_ptr(), p["scales"].data_ptr(), p["scales"].numel(), p["x"].numel(),
+                                 p["x"].data_ptr(), _ptr(p.get("x_scale")), _ptr(p.get("acc")), _ptr(p.get("y")))
+            self._keep.append(p)
+        p0 = problems[0]
+        s_dt = _DT[p0["scales"].dtype]
+        x_dt = _DT[p0["x"].dtype]
+        y_dt = _DT[p0["y"].dtype] if p0.get("y") is not None else F32
+        nbytes = lib.sherry_gemv_plan_bytes(arr, len(problems))
+        if nbytes == 0:
+            raise ValueError("invalid grouped GEMV problems")
+        self.host = torch.empty(nbytes, dtype=torch.uint8)
+        fn = lib.tern2_gemv_plan if tern2 else lib.sherry_gemv_plan
+        _check("gemv_plan", fn(arr, len(problems), s_dt, x_dt, y_dt, self.host.data_ptr(), nbytes))
+        self.dev = self.host.to(p0["x"].device, non_blocking=False)
+        self.n_tiles = int.from_bytes(bytes(self.host[12:16].tolist()), "little", signed=True)
+        self.count = len(problems)
+
+    def __call__(self):
+        _check("sherry_gemv_grouped", load().sherry_gemv_grouped(self.host.data_ptr(), self.dev.data_ptr(), _stream()))
