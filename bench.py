@@ -1,0 +1,425 @@
+#!/usr/bin/env python3
+"""Benchmark of the Sherry 1.25-bit ternary GEMV on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one batch-1 decode pass of the GEMV over every matrix of a
+LLaMA-3.2-1B decoder layer (q, k, v, o, gate, up, down; int8 activations with
+a per-token scale, fp16 row scales, fp16 outputs), repeated over R distinct
+replicas of the layer (default 112, 1.06 GB of codes, four times the 256 MB
+last-level cache) in one grouped launch, so the codes stream from HBM.  All
+inputs are seeded synthetic data already resident in device memory.
+
+Prints one JSON line (the metric), with the dominant kernel's roofline and
+the CPU oracle's throughput on a bounded sample; secondary measurements go
+under "extras".
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, 5.0 POP/s
+METRIC = "1.25-bit ternary GEMV weights/s + % of HBM peak (LLaMA-3.2-1B shapes, batch 1)"
+KERNEL_SOURCES = ["ultra_bit_weight_amd/csrc/gemv.hip", "ultra_bit_weight_amd/csrc/formats.h",
+                  "ultra_bit_weight_amd/csrc/common.h", "ultra_bit_weight_amd/csrc/launch.h"]
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "gemv_grouped_llama1b_b1_counters.md")
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--replicas", type=int, default=112)
+    p.add_argument("--seed", type=int, default=2)
+    p.add_argument("--no-extras", action="store_true", help="only the metric line (no secondary measurements)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="also run one plain 1 GiB device copy (calibrates HBM byte counters)")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) and exit")
+    return p.parse_args(argv)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------- workloads ---
+
+def layer_bytes(shapes, x_bytes_per_elem=1, y_bytes=2, scale_bytes=2, with_sx=True):
+    """Algorithmic bytes of one batch-1 pass over a layer: codes (5/32 B per
+    weight), row scales, x, y and the per-token scale, each read/written once."""
+    total = 0
+    for _, n, k in shapes:
+        total += n * k * 5 // 32 + n * scale_bytes + k * x_bytes_per_elem + n * y_bytes + (4 if with_sx else 0)
+    return total
+
+
+def build_layer_replicas(torch, sherry, synth, shapes, replicas, seed, x_kind="i8", tern2=False):
+    """R replicas of a decoder layer, all distinct: codes from a seeded device
+    RNG (uniform words are uniform 3:4 ternary matrices), fp16 row scales
+    U[0.01, 0.1], activations per matrix from the host generator."""
+    import numpy as np
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    words_per_layer = sum(n * (k // 128) * 5 for _, n, k in shapes)
+    codes = torch.randint(-2 ** 31, 2 ** 31, (replicas * words_per_layer,), dtype=torch.int32, device=dev,
+                          generator=gen)
+    rows_per_layer = sum(n for _, n, _ in shapes)
+    scales = (torch.rand(replicas * rows_per_layer, generator=gen, device=dev, dtype=torch.float64) * 0.09
+              + 0.01).to(torch.float16)
+    g = synth.rng(seed)
+    probs = []
+    wo = so = 0
+    for r in range(replicas):
+        for name, n, k in shapes:
+            nw = n * (k // 128) * 5
+            c = codes[wo:wo + nw]
+            s = scales[so:so + n]
+            wo += nw
+            so += n
+            if x_kind == "i8":
+                xq, sx, _ = synth.act_absmax_int8(1, k, g)
+                x = torch.from_numpy(xq[0]).to(dev)
+                xs = torch.from_numpy(sx).to(dev)
+                y = torch.empty(n, dtype=torch.float16, device=dev)
+            else:
+                xb = synth.x_bf16_normal(k, g)
+                x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+                xs = None
+                y = torch.empty(n, dtype=torch.float32, device=dev)
+            probs.append(dict(codes=c, scales=s, x=x, x_scale=xs, acc=None, y=y, n=n, k=k, name=name, replica=r))
+    return codes, probs
+
+
+def time_launches(torch, fn, steps, warmup):
+    """Time `steps` back-to-back calls of fn on the current stream: one HIP event
+    pair brackets the whole timed region (events between launches would add
+    their own overhead to every launch), plus a wall clock around it with a
+    synchronize on both sides.  Returns (mean ms per call from the events,
+    wall ms per call)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    return a.elapsed_time(b) / steps, wall_ms
+
+
+def traffic_from_summary():
+    """HBM bytes per launch of the grouped kernel from the committed counter
+    summary, or None if absent or taken on a different version of the kernel."""
+    if not os.path.exists(COUNTER_SUMMARY):
+        return None
+    vals = {}
+    for line in open(COUNTER_SUMMARY):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_hash") != kernel_hash():
+        return None
+    try:
+        return int(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------ cpu oracle ---
+
+def cpu_baseline(torch, probs, shapes, min_seconds=10.0, max_layers=16):
+    """The oracle as it stands, one thread, on whole 1B layers (7 matrices
+    each, replicas 0, 1, ...) until at least min_seconds of CPU work:
+    unpack + exact product + epilogue, per matrix."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import sherry_ref
+
+    per_layer = sum(n * k for _, n, k in shapes)
+    done = 0
+    dt = 0.0
+    with threadpool_limits(limits=1):
+        for r in range(max_layers):
+            layer = [p for p in probs if p["replica"] == r]
+            if not layer:
+                break
+            host = [(p["codes"].cpu().numpy().view(np.uint32), p["scales"].cpu().numpy(), p["n"], p["k"],
+                     p["x"].cpu().numpy(), p["x_scale"].cpu().numpy()[0]) for p in layer]
+            t0 = time.perf_counter()
+            for words, sw, n, k, x, sx in host:
+                sherry_ref.gemv_i8(words, sw, n, k, x, sx, np.float16)
+            dt += time.perf_counter() - t0
+            done += 1
+            if dt >= min_seconds:
+                break
+    return {"value": done * per_layer / dt, "unit": "weights/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} LLaMA-3.2-1B decoder layer(s) (7 matrices, {per_layer} weights each), batch 1, "
+                      f"numpy oracle limited to 1 thread, {dt:.1f} s"}
+
+
+# ----------------------------------------------------------------- extras ---
+
+def extras(torch, sherry, synth, probs_1b, codes_1b, args):
+    import numpy as np
+
+    out = {}
+    dev = torch.device("cuda:0")
+    shapes_1b = synth.LLAMA32_1B_LAYER
+    R = args.replicas
+
+    # per-call latency of single matrices, rotating over replicas
+    lat = {}
+    for name, n, k in shapes_1b:
+        sel = [p for p in probs_1b if p["name"] == name]
+        it = [0]
+
+        def one():
+            p = sel[it[0] % len(sel)]
+            it[0] += 1
+            sherry.gemv(p["codes"], p["scales"], p["x"], p["x_scale"], out=p["y"])
+        mean_ms, _ = time_launches(torch, one, 200, 20)
+        us = mean_ms * 1e3
+        lat[f"{name}_{n}x{k}"] = {"us_per_call": round(us, 2),
+                                  "GBps": round((n * k * 5 / 32 + 4 * n + k) / (us * 1e-6) / 1e9, 1)}
+    out["per_call_gemv_1b"] = lat
+
+    # 2-bit dense-ternary comparator on the same ternary matrices
+    t2_codes = []
+    probs_t2 = []
+    for p in probs_1b:
+        t = sherry.decode(p["codes"], p["n"], p["k"])
+        c2 = sherry.tern2_encode(t)
+        del t
+        t2_codes.append(c2)
+        q = dict(p)
+        q["codes"] = c2
+        probs_t2.append(q)
+    torch.cuda.synchronize()
+    g2 = sherry.GroupedGemv(probs_t2, tern2=True)
+    mean_ms, wall_ms = time_launches(torch, g2, args.steps, args.warmup)
+    weights = R * sum(n * k for _, n, k in shapes_1b)
+    bytes2 = R * (sum(n * k // 4 + 2 * n + k + 2 * n + 4 for _, n, k in shapes_1b))
+    out["tern2_grouped_1b"] = {"ms_per_launch": round(mean_ms, 4), "weights_per_s": weights / (mean_ms * 1e-3),
+                               "GBps": round(bytes2 / (mean_ms * 1e-3) / 1e9, 1),
+                               "frac_hbm": round(bytes2 / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    # same grouped launch on the 1.25-bit codes, for the ratio
+    del g2, probs_t2, t2_codes
+    torch.cuda.empty_cache()
+
+    # bf16 activations on the 3B layer (fp32 accumulation), 72 replicas
+    shapes_3b = synth.LLAMA32_3B_LAYER
+    R3 = max(1, int(round(R * 72 / 112)))
+    codes_3b, probs_3b = build_layer_replicas(torch, sherry, synth, shapes_3b, R3, args.seed + 1, x_kind="bf16")
+    g3 = sherry.GroupedGemv(probs_3b)
+    mean_ms, _ = time_launches(torch, g3, args.steps, args.warmup)
+    b3 = R3 * layer_bytes(shapes_3b, x_bytes_per_elem=2, y_bytes=4, with_sx=False)
+    w3 = R3 * sum(n * k for _, n, k in shapes_3b)
+    out["bf16_grouped_3b"] = {"replicas": R3, "ms_per_launch": round(mean_ms, 4),
+                              "weights_per_s": w3 / (mean_ms * 1e-3),
+                              "GBps": round(b3 / (mean_ms * 1e-3) / 1e9, 1),
+                              "frac_hbm": round(b3 / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del g3, probs_3b, codes_3b
+    torch.cuda.empty_cache()
+
+    # M-token GEMM on the 1B layer: small batch (HBM-bound) and prefill (MFMA-bound)
+    g = synth.rng(args.seed + 7)
+    gemm = {}
+    layer0 = [p for p in probs_1b if p["replica"] < 16]
+    for m in (2, 4, 8, 16, 2048):
+        xs = {}
+        for _, n, k in shapes_1b:
+            if k not in xs:
+                xq, sx, _ = synth.act_absmax_int8(m, k, g)
+                xs[k] = (torch.from_numpy(xq).to(dev), torch.from_numpy(sx).to(dev))
+        ys = {p["name"]: torch.empty(m, p["n"], dtype=torch.float16, device=dev) for p in layer0[:7]}
+        reps = 16 if m <= 16 else 1
+        sel = [p for p in layer0 if p["replica"] < reps]
+
+        def layer_pass():
+            for p in sel:
+                x, sx = xs[p["k"]]
+                sherry.gemm(p["codes"], p["scales"], x, sx, out=ys[p["name"]])
+        mean_ms, _ = time_launches(torch, layer_pass, 5 if m <= 16 else 3, 2)
+        per_layer_ms = mean_ms / reps
+        ops = 2 * m * sum(n * k for _, n, k in shapes_1b)
+        byts = sum(n * k * 5 // 32 + 2 * n + m * k + 2 * m * n + 4 * m for _, n, k in shapes_1b)
+        gemm[f"M{m}"] = {"us_per_layer": round(per_layer_ms * 1e3, 2),
+                         "TOPS": round(ops / (per_layer_ms * 1e-3) / 1e12, 2),
+                         "frac_int8_peak": round(ops / (per_layer_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+                         "GBps": round(byts / (per_layer_ms * 1e-3) / 1e9, 1)}
+    out["gemm_1b_layer"] = gemm
+
+    # packer: fp16 weights of one 1B layer -> codes + fp16 scales
+    wts = {}
+    for name, n, k in shapes_1b:
+        wts[name] = (torch.randn(n, k, device=dev, dtype=torch.float32) * 0.02).to(torch.float16)
+    def pack_all():
+        for name, _, _ in shapes_1b:
+            sherry.pack(wts[name], torch.float16)
+    mean_ms, _ = time_launches(torch, pack_all, 3, 1)
+    wl = sum(n * k for _, n, k in shapes_1b)
+    out["pack_1b_layer_fp16"] = {"ms": round(mean_ms, 3), "weights_per_s": wl / (mean_ms * 1e-3)}
+    return out
+
+
+# ------------------------------------------------------------ counters ---
+
+def summarize_counters(fetch_dir, write_dir):
+    """rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of `bench.py --copy-probe`:
+    per-dispatch KiB of the grouped GEMV and of the 1 GiB negation (reads
+    1 GiB, writes 1 GiB), the factor bytes / counter that calibrates each
+    counter, and the scaled HBM bytes per grouped launch."""
+    import csv
+
+    def read(d, counter):
+        rows = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for row in csv.DictReader(fh):
+                    if row.get("Counter_Name") != counter:
+                        continue
+                    name = row.get("Kernel_Name", "")
+                    rows.setdefault(name, []).append(float(row["Counter_Value"]))
+        return rows
+
+    fetch, write = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
+
+    def pick(rows, pat):
+        vals = [v for k, vs in rows.items() if pat in k for v in vs]
+        return statistics.median(vals) if vals else None
+
+    g_f, g_w = pick(fetch, "gemv_i8_grouped"), pick(write, "gemv_i8_grouped")
+    c_f, c_w = pick(fetch, "neg_kernel"), pick(write, "neg_kernel")
+    gib = float(1 << 30)
+    f_fac = gib / (c_f * 1024) if c_f else None
+    w_fac = gib / (c_w * 1024) if c_w else None
+    res = {"grouped_fetch_kib": g_f, "grouped_write_kib": g_w, "copy_fetch_kib": c_f, "copy_write_kib": c_w,
+           "fetch_factor": f_fac, "write_factor": w_fac}
+    if g_f and f_fac and g_w is not None and w_fac:
+        res["hbm_bytes_per_launch"] = int(g_f * 1024 * f_fac + g_w * 1024 * w_fac)
+    print(json.dumps(res))
+    return res
+
+
+# ------------------------------------------------------------------- main ---
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return 0
+    if args.gpus != 1:
+        print(f"bench.py: this benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU sharding is described in the design notes but not measured.", file=sys.stderr)
+        return 2
+    import torch
+
+    import synth
+    from ultra_bit_weight_amd import sherry
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    sherry.load()
+    torch.cuda.set_device(0)
+    shapes = synth.LLAMA32_1B_LAYER
+    R = args.replicas
+    codes, probs = build_layer_replicas(torch, sherry, synth, shapes, R, args.seed)
+    grouped = sherry.GroupedGemv(probs)
+    torch.cuda.synchronize()
+    print(f"# built {R} replicas of the 1B layer: {codes.numel() * 4 / 1e9:.3f} GB of codes, "
+          f"{grouped.n_tiles} workgroup tiles", file=sys.stderr, flush=True)
+
+    if args.copy_probe:
+        # plain streaming kernel of known traffic: 1 GiB read + 1 GiB written
+        src = torch.ones(1 << 28, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    mean_ms, wall_ms = time_launches(torch, grouped, args.steps, args.warmup)
+    weights_per_step = R * sum(n * k for _, n, k in shapes)
+    alg_bytes = R * layer_bytes(shapes)
+    value = weights_per_step / (wall_ms * 1e-3)
+    achieved = alg_bytes / (mean_ms * 1e-3) / 1e9
+    print(f"# grouped GEMV: {mean_ms:.4f} ms per launch (events), {wall_ms:.4f} ms per step (wall)",
+          file=sys.stderr, flush=True)
+
+    traffic = traffic_from_summary()
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {
+            "workload": "LLaMA-3.2-1B decoder-layer GEMVs (q 2048x2048, k/v 512x2048, o 2048x2048, "
+                        "gate/up 8192x2048, down 2048x8192), batch 1, int8 activations with per-token scale, "
+                        f"fp16 row scales and outputs; {R} distinct layer replicas per step in one grouped launch",
+            "replicas": R,
+            "weights_per_step": weights_per_step,
+            "code_bytes_per_step": R * sum(n * k * 5 // 32 for _, n, k in shapes),
+            "bits_per_weight": 1.25,
+            "kernel": "gemv_i8_grouped_kernel<Sherry3of4>",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": alg_bytes,
+            "launch_ms": round(mean_ms, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(torch, probs, shapes)
+        print(f"# cpu oracle: {line['cpu_baseline']['value']:.3e} weights/s", file=sys.stderr, flush=True)
+    if not args.no_extras:
+        ex = extras(torch, sherry, synth, probs, codes, args)
+        t2 = ex.get("tern2_grouped_1b")
+        if t2:
+            ex["sherry_over_tern2_speedup"] = round(t2["ms_per_launch"] / mean_ms, 3)
+        line["extras"] = ex
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -17,7 +17,10 @@
  *   group              = 32 codes (128 weights) in 5 little-endian uint32
  *                        words, one LSB-first 160-bit stream: code j at bits
  *                        [5j, 5j+5) of d0 + d1*2^32 + ... + d4*2^128
- *   matrix             = uint32 codes[n][K/128][5], row-major, K % 128 == 0
+ *   row                = 5 * K/128 words: words 0-3 of every group first
+ *                        (group g at word 4g, 16 bytes), then word 4 of
+ *                        every group (group g at word 4*K/128 + g)
+ *   matrix             = n rows one after another, K % 128 == 0
  *   scales             = one per output row (fp32 or fp16)
  *
  * Products (all accumulate exactly in int32 for int8 activations):
@@ -93,6 +96,13 @@ size_t sherry_packed_bytes(int64_t n, int64_t k);
  * Alignment: w aligned to 4 * element size and ldw a multiple of 4. */
 sherry_status sherry_pack(const void* w, sherry_dtype w_dt, int64_t n, int64_t k, int64_t ldw,
                           uint32_t* codes, void* scales, sherry_dtype s_dt, hipStream_t stream);
+
+/* Expand packed codes to the dense ternary matrix: t[r * ldt + c] = T[r, c]
+ * as int8 (-1, 0, +1), the inverse of the layout above (every 5-bit pattern is
+ * a valid block, so any code words decode).
+ *   t : out, n x k int8, row stride ldt >= k, ldt % 16 == 0, 16-byte aligned */
+sherry_status sherry_decode(const uint32_t* codes, int64_t n, int64_t k, int8_t* t, int64_t ldt,
+                            hipStream_t stream);
 
 /* Batch-1 product y = diag(s_w) * T * x (the decode-phase GEMV).
  *   codes    : n x k packed codes (layout above), 4-byte aligned

@@ -26,8 +26,12 @@ justification, in the design notes):
   R3  32 codes (128 weights) form a group stored in five little-endian uint32
       words as one LSB-first bitstream: code j occupies bits [5j, 5j + 5) of
       d0 + d1 * 2^32 + ... + d4 * 2^128 (codes 6, 12, 19, 25 straddle words);
-  R4  matrix layout row-major by groups: word i of group g of row r is at
-      uint32 index (r * G + g) * 5 + i, G = K / 128, and K % 128 == 0;
+  R4  matrix layout row-major, G = K / 128 groups per row, K % 128 == 0; row
+      r occupies the 5G words [5Gr, 5G(r+1)): first words 0-3 of every group
+      (group g at 5Gr + 4g), then word 4 of every group (group g at
+      5Gr + 4G + g).  Each group keeps its five words; splitting them into a
+      16-byte part and a 4-byte part lets a GPU read both parts of a row with
+      aligned, contiguous loads.  A one-group row is simply its five words;
   R5  packer: zero slot = argmin |w| over the block (lowest slot on ties),
       kept weight negative iff w < 0 (so -0.0 is +1);
   R6  one scale per output row, alpha_r = (sum of kept |w|) / (3K / 4), the
@@ -187,31 +191,53 @@ def dense_from_codes(codes: np.ndarray) -> np.ndarray:
 
 def pack_codes(codes: np.ndarray) -> np.ndarray:
     """uint8 codes [n, k/4] -> uint32 words [n * G * 5] (R3, R4): each group's
-    160 bits as an LSB-first stream, 5 bits per code."""
+    160 bits as an LSB-first stream, 5 bits per code, giving words d0..d4;
+    per row the d0..d3 of every group come first, then the d4 of every group."""
     c = np.asarray(codes).astype(np.uint8)
     n, nb = c.shape
     if nb % GROUP_BLOCKS:
         raise ValueError("k/4 must be a multiple of 32")
     if np.any(c >= N_CODES):
         raise ValueError("codes must be in [0, 32)")
+    g = nb // GROUP_BLOCKS
     bits = np.unpackbits(c[:, :, None], axis=2, bitorder="little")[:, :, :5]  # [n, nb, 5]
-    bits = bits.reshape(n, nb // GROUP_BLOCKS, GROUP_BLOCKS * 5)  # 160 bits per group
+    bits = bits.reshape(n, g, GROUP_BLOCKS * 5)  # 160 bits per group
     by = np.packbits(bits, axis=2, bitorder="little")  # [n, G, 20] bytes
-    return np.ascontiguousarray(by).reshape(-1).view("<u4").astype(np.uint32)
+    d = np.ascontiguousarray(by).reshape(-1).view("<u4").astype(np.uint32).reshape(n, g, GROUP_WORDS)
+    return np.concatenate([d[:, :, :4].reshape(n, 4 * g), d[:, :, 4]], axis=1).reshape(-1)
+
+
+def group_words(words: np.ndarray, n: int, k: int) -> np.ndarray:
+    """Packed words (layout R4) -> uint32 [n, G, 5]: d0..d4 of every group."""
+    check_shape(n, k)
+    g = k // GROUP_WEIGHTS
+    w = np.asarray(words, dtype=np.uint32).reshape(-1)
+    if w.size != n * g * GROUP_WORDS:
+        raise ValueError(f"expected {n * g * GROUP_WORDS} words, got {w.size}")
+    w = w.reshape(n, GROUP_WORDS * g)
+    out = np.empty((n, g, GROUP_WORDS), dtype=np.uint32)
+    out[:, :, :4] = w[:, :4 * g].reshape(n, g, 4)
+    out[:, :, 4] = w[:, 4 * g:]
+    return out
 
 
 def unpack_codes(words: np.ndarray, n: int, k: int) -> np.ndarray:
     """uint32 words [n * G * 5] -> uint8 codes [n, k/4] (inverse of pack_codes)."""
-    check_shape(n, k)
-    g = k // GROUP_WEIGHTS
-    w = np.ascontiguousarray(np.asarray(words, dtype=np.uint32).reshape(-1))
-    if w.size != n * g * GROUP_WORDS:
-        raise ValueError(f"expected {n * g * GROUP_WORDS} words, got {w.size}")
-    by = w.astype("<u4").view(np.uint8).reshape(n, g, GROUP_WORDS * 4)
+    d = group_words(words, n, k)
+    g = d.shape[1]
+    by = np.ascontiguousarray(d).astype("<u4").view(np.uint8).reshape(n, g, GROUP_WORDS * 4)
     bits = np.unpackbits(by, axis=2, bitorder="little").reshape(n, g, GROUP_BLOCKS, 5)
     weights = (1 << np.arange(5)).astype(np.uint8)
     codes = (bits * weights).sum(axis=3).astype(np.uint8)
     return codes.reshape(n, g * GROUP_BLOCKS)
+
+
+def row_words(words: np.ndarray, n: int, k: int, rows) -> np.ndarray:
+    """The words of the given rows, in order (rows are contiguous in R4)."""
+    check_shape(n, k)
+    per = (k // GROUP_WEIGHTS) * GROUP_WORDS
+    w = np.asarray(words, dtype=np.uint32).reshape(n, per)
+    return np.ascontiguousarray(w[np.asarray(rows)]).reshape(-1)
 
 
 def unpack(words: np.ndarray, n: int, k: int) -> np.ndarray:

@@ -112,6 +112,20 @@ def pin_packed_groups(ref):
         assert [int(c) for c in u[0]] == codes, f"vectorised unpack {name}"
 
 
+def pin_row_layout(ref):
+    """R4 by hand: a row of two groups, "ramp" then "ramp_down", is the four
+    leading words of each group followed by the fifth word of each group."""
+    ramp, down = HAND_GROUPS["ramp"], HAND_GROUPS["ramp_down"]
+    want = ramp[1][:4] + down[1][:4] + [ramp[1][4], down[1][4]]
+    codes = np.array([ramp[0] + down[0]], dtype=np.uint8)
+    assert [int(w) for w in ref.pack_codes(codes)] == want
+    assert ref.unpack_codes(np.array(want, np.uint32), 1, 256).tolist() == codes.tolist()
+    # two rows: each row is contiguous, the second starts after 10 words
+    two = ref.pack_codes(np.vstack([codes, codes[:, ::-1]]))
+    assert [int(w) for w in two[:10]] == want
+    assert ref.unpack_codes(two, 2, 256)[1].tolist() == codes[0, ::-1].tolist()
+
+
 def pin_straddles(ref):
     """A code straddles two words iff flipping it changes two words."""
     found = []
@@ -158,7 +172,8 @@ def pin_closed_forms(ref):
         e[col] = 1
         acc, _ = ref.gemv_i8(words, sw, n, k, e, None, np.float32)
         for r in range(n):
-            grp = [int(words[(r * (k // 128) + col // 128) * 5 + i]) for i in range(5)]
+            G, gi = k // 128, col // 128  # R4: d0-d3 at 5Gr + 4g + i, d4 at 5Gr + 4G + g
+            grp = [int(words[5 * G * r + 4 * gi + i]) for i in range(4)] + [int(words[5 * G * r + 4 * G + gi])]
             v = 0
             for i, w in enumerate(grp):
                 v |= w << (32 * i)

@@ -131,6 +131,16 @@ def test_gemm_validation(lib, fn):
     assert gemm(lib, xs=None, acc=None, fn=fn) == EDEVICE
 
 
+def test_decode_validation(lib):
+    f = lib.sherry_decode
+    assert f(None, 4, 128, A, 128, None) == EINVAL
+    assert f(A, 4, 100, A, 112, None) == ESHAPE
+    assert f(A, 4, 128, A, 112, None) == ESHAPE
+    assert f(A, 4, 128, A + 8, 128, None) == EALIGN
+    assert f(A, 4, 128, A, 136, None) == EALIGN
+    assert f(A, 4, 128, A, 128, None) == EDEVICE
+
+
 def test_tern2_encode_validation(lib):
     f = lib.tern2_encode
     assert f(None, 4, 128, 128, A, None) == EINVAL
@@ -150,8 +160,10 @@ def test_grouped_plan_on_host(lib):
         arr[i] = GemvProblem(A, A, n, k, A, None, None, A)
     nbytes = lib.sherry_gemv_plan_bytes(arr, len(shapes))
     # 64-byte header + 64 bytes per problem + 8 bytes per tile; tile rows are
-    # 4 iterations x rows per iteration (4 waves x 64 / lanes per row)
-    tiles = 2048 // 64 + 512 // 64 + 2048 // 16 + 256 // 128 + -(-300 // 16)
+    # 16 iterations x rows per iteration (4 waves x 64 / lanes per row):
+    # k=2048 -> 16 lanes -> 256 rows, k=8192 -> 64 lanes -> 64 rows,
+    # k=1024 -> 8 lanes -> 512 rows, other k -> 64 lanes -> 64 rows
+    tiles = 2048 // 256 + 512 // 256 + 2048 // 64 + 1 + -(-300 // 64)
     assert nbytes == 64 + 64 * len(shapes) + 8 * tiles
     buf = ctypes.create_string_buffer(nbytes + 8)
     base = (ctypes.addressof(buf) + 7) // 8 * 8

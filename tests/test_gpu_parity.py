@@ -89,6 +89,15 @@ def test_pack_exact_ternary_and_row_stride(gpu_lib):
     assert np.array_equal(scales.cpu().numpy(), s)
 
 
+@pytest.mark.parametrize("n,k", [(1, 128), (37, 640), (256, 1024), (9, 8192)])
+def test_decode_matches_oracle(gpu_lib, n, k):
+    g = synth.rng(n * 13 + k)
+    words = synth.random_words(n * (k // 128) * 5, g)
+    t = gpu_lib.decode(words_dev(words), n, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(t.cpu().numpy(), sherry_ref.unpack(words, n, k))
+
+
 # -------------------------------------------------------------- int8 GEMV ---
 
 GEMV_K = [128, 256, 384, 640, 1024, 2048, 3072, 4096, 8192]
@@ -331,8 +340,7 @@ def test_full_layer_sampled_rows(gpu_lib, layer):
     torch.cuda.synchronize()
     for p, (words, sw, x, sx, n, k) in zip(probs, keep):
         rows = np.unique(np.concatenate([[0, n - 1], g.integers(0, n, 62)]))
-        g5 = k // 128 * 5
-        sub = np.concatenate([words[r * g5:(r + 1) * g5] for r in rows])
+        sub = sherry_ref.row_words(words, n, k, rows)
         if layer == "1b":
             ra, ry = sherry_ref.gemv_i8(sub, sw[rows], len(rows), k, x, sx[0], np.float16)
             assert np.array_equal(p["acc"].cpu().numpy()[rows], ra)

@@ -13,7 +13,7 @@ import pytest
 from tests import oracle_pins as P
 
 PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "sherry_ref.py")
-ALL_PINS = [P.pin_bijection, P.pin_code_table, P.pin_packed_groups, P.pin_straddles, P.pin_size,
+ALL_PINS = [P.pin_bijection, P.pin_code_table, P.pin_packed_groups, P.pin_row_layout, P.pin_straddles, P.pin_size,
             P.pin_ramp_dot, P.pin_closed_forms, P.pin_brute_force, P.pin_packer, P.pin_epilogue,
             P.pin_bf16_path]
 
@@ -82,6 +82,19 @@ def m_word_order_swapped(ref):
     ref.unpack_codes = bad
 
 
+def m_groups_contiguous(ref):
+    """five words of a group kept together instead of the two-part row layout"""
+    def pack(codes):
+        c = np.asarray(codes).astype(np.uint8)
+        n, nb = c.shape
+        out = []
+        for r in range(n):
+            for gi in range(nb // 32):
+                out += ref.pack_group(c[r, 32 * gi:32 * gi + 32])
+        return np.array(out, dtype=np.uint32)
+    ref.pack_codes = pack
+
+
 def m_transposed_operand(ref):
     def bad(words, s_w, n, k, x, s_x, y_dtype=np.float16):
         t = ref.unpack(words, n, k)
@@ -135,7 +148,7 @@ def m_bf16_scale_dropped(ref):
 
 
 MUTANTS = [m_sign_order_reversed, m_sign_meaning_flipped, m_zero_field_high, m_msb_first_stream,
-           m_word_order_swapped, m_transposed_operand, m_dropped_token_scale, m_fp64_epilogue,
+           m_word_order_swapped, m_groups_contiguous, m_transposed_operand, m_dropped_token_scale, m_fp64_epilogue,
            m_tie_to_highest, m_absmean_scale, m_bf16_scale_dropped]
 
 

@@ -8,7 +8,7 @@ from tests import oracle_pins as P
 
 
 @pytest.mark.parametrize("pin", [
-    P.pin_bijection, P.pin_code_table, P.pin_packed_groups, P.pin_straddles, P.pin_size,
+    P.pin_bijection, P.pin_code_table, P.pin_packed_groups, P.pin_row_layout, P.pin_straddles, P.pin_size,
     P.pin_ramp_dot, P.pin_closed_forms, P.pin_brute_force, P.pin_packer, P.pin_epilogue,
     P.pin_bf16_path,
 ], ids=lambda f: f.__name__)
@@ -21,9 +21,12 @@ def test_vectorised_matches_scalar_routines():
     n, k = 11, 640
     words = synth.random_words(n * (k // 128) * 5, g)
     codes = sherry_ref.unpack_codes(words, n, k)
+    d = sherry_ref.group_words(words, n, k)
+    G = k // 128
     for r in range(n):
-        for grp in range(k // 128):
-            w5 = words[(r * (k // 128) + grp) * 5:(r * (k // 128) + grp + 1) * 5]
+        for grp in range(G):
+            w5 = [words[5 * G * r + 4 * grp + i] for i in range(4)] + [words[5 * G * r + 4 * G + grp]]
+            assert d[r, grp].tolist() == [int(v) for v in w5]
             assert sherry_ref.unpack_group(w5) == codes[r, grp * 32:(grp + 1) * 32].tolist()
     assert np.array_equal(sherry_ref.pack_codes(codes), words)
     dense = sherry_ref.dense_from_codes(codes)

@@ -40,9 +40,9 @@ def common_flags() -> list:
     ]
 
 
-def _compile(src: str, save_temps: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, save_temps: bool, objdir: str, defines) -> str:
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *common_flags(), *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
     if save_temps:
         cmd += ["-save-temps=obj"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,21 +51,25 @@ def _compile(src: str, save_temps: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, save_temps: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    os.makedirs(LIBDIR, exist_ok=True)
+def build(verbose: bool = False, save_temps: bool = False, defines=(), out: str = LIB) -> str:
+    """Compile every source and link `out` (default: the in-tree library).
+    `defines` (NAME=VALUE strings) override the build-time tunables."""
+    tag = "_".join(d.replace("=", "") for d in defines)
+    objdir = os.path.join(BUILD, tag) if tag else BUILD
+    os.makedirs(objdir, exist_ok=True)
+    os.makedirs(os.path.dirname(out), exist_ok=True)
     srcs = list(SOURCES)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, save_temps), srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, save_temps, objdir, defines), srcs))
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":

@@ -140,11 +140,14 @@ sherry_status gemm_impl(int32_t format, const uint32_t* codes, const void* w_sca
 }
 
 // Grouped plan: header | GemvDesc[count] | PlanTile[n_tiles].
+int64_t tile_rows_for(const sherry_gemv_problem& p) {
+  return static_cast<int64_t>(rows_per_iter(kclass_of(p.k))) * kGroupedIters;
+}
+
 int64_t plan_tiles(const sherry_gemv_problem* probs, int32_t count) {
   int64_t tiles = 0;
   for (int32_t i = 0; i < count; ++i) {
-    const int32_t kc = kclass_of(probs[i].k);
-    const int64_t rows = static_cast<int64_t>(rows_per_iter(kc)) * kGroupedIters;
+    const int64_t rows = tile_rows_for(probs[i]);
     tiles += (probs[i].n + rows - 1) / rows;
   }
   return tiles;
@@ -193,7 +196,7 @@ sherry_status plan_impl(int32_t format, const sherry_gemv_problem* probs, int32_
   for (int32_t i = 0; i < count; ++i) {
     const sherry_gemv_problem& p = probs[i];
     descs[i] = make_desc(p.codes, p.w_scales, s_dt, p.n, p.k, p.x, p.x_scale, p.acc, p.y, y_dt);
-    const int64_t rows = static_cast<int64_t>(rows_per_iter(descs[i].kclass)) * kGroupedIters;
+    const int64_t rows = tile_rows_for(p);
     for (int64_t r0 = 0; r0 < p.n; r0 += rows) tiles[t++] = PlanTile{i, static_cast<int32_t>(r0)};
   }
   return SHERRY_OK;
@@ -234,6 +237,16 @@ sherry_status sherry_pack(const void* w, sherry_dtype w_dt, int64_t n, int64_t k
     return SHERRY_EALIGN;
   if (sherry_status s = check_device()) return s;
   return launched(launch_pack(w, w_dt, n, k, ldw, codes, scales, s_dt == SHERRY_F16, stream));
+}
+
+sherry_status sherry_decode(const uint32_t* codes, int64_t n, int64_t k, int8_t* t, int64_t ldt,
+                            hipStream_t stream) {
+  if (!codes || !t) return SHERRY_EINVAL;
+  if (sherry_status s = check_nk(n, k)) return s;
+  if (ldt < k || ldt > std::numeric_limits<int64_t>::max() / n) return SHERRY_ESHAPE;
+  if (!aligned(codes, 4) || !aligned(t, 16) || ldt % 16 != 0) return SHERRY_EALIGN;
+  if (sherry_status s = check_device()) return s;
+  return launched(launch_decode(codes, n, k, t, ldt, stream));
 }
 
 sherry_status sherry_gemv(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,

@@ -83,6 +83,21 @@ __device__ __forceinline__ uint32_t code_offset(const uint32_t* w, int j) {
   return __builtin_amdgcn_alignbit(w[i + 1], w[i], o - SCALE_LOG2) & mask;
 }
 
+// Row layout: a row of G groups is 5G words; words 0-3 of group g sit at
+// 4g (16 bytes, aligned when the row is), word 4 of group g at 4G + g.  So
+// the lanes reading consecutive groups issue one contiguous 16-byte-per-lane
+// load and one contiguous 4-byte-per-lane load.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void load_group(uint32_t* w, const uint32_t* row, int G, int g) {
+  const u32x4_t h = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + 4 * g));
+  w[0] = h.x;
+  w[1] = h.y;
+  w[2] = h.z;
+  w[3] = h.w;
+  w[4] = __builtin_nontemporal_load(row + 4 * G + g);
+}
+
 __device__ __forceinline__ uint32_t lds_u32(const uint32_t* base, uint32_t byte_off) {
   return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(base) + byte_off);
 }

@@ -70,9 +70,12 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmDesc d, int n_tile
       if (!kStationary) load_x(g);
       uint32_t w[NW];
       const bool ok = row < d.n && g < G;
-      const uint32_t* src = d.codes + (static_cast<int64_t>(row) * G + g) * NW;
+      if (ok) {
+        Fmt::load(w, d.codes + static_cast<int64_t>(row) * (G * NW), G, g);
+      } else {
 #pragma unroll
-      for (int t = 0; t < NW; ++t) w[t] = ok ? __builtin_nontemporal_load(src + t) : 0u;
+        for (int t = 0; t < NW; ++t) w[t] = 0u;
+      }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         v4i a, b;

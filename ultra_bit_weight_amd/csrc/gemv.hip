@@ -11,8 +11,10 @@
 // with DPP row operations; the lane that owns the row applies the scale.
 //
 // Row-to-lane mapping for L lanes per row and GPL groups per lane: lane
-// (row r, position p) owns groups p, p + L, ..., p + (GPL-1) L, so the L lanes
-// of a row read one contiguous run of 20 * L bytes per step.
+// (row r, position p) owns groups p, p + L, ..., p + (GPL-1) L.  With the row
+// layout (words 0-3 of every group, then word 4 of every group) the L lanes
+// of a row read 16 L contiguous bytes with one 16-byte load each and 4 L
+// contiguous bytes with one 4-byte load each.
 #include "formats.h"
 #include "launch.h"
 
@@ -26,18 +28,10 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          c, false);
 }
 
-// Streamed once: non-temporal loads.  Callers clamp the row so every load is
-// in bounds and unconditional (a branch around a load would force a wait).
-template <int NW>
-__device__ __forceinline__ void load_words(uint32_t (&dst)[NW], const uint32_t* src) {
-#pragma unroll
-  for (int i = 0; i < NW; ++i) dst[i] = __builtin_nontemporal_load(src + i);
-}
-
 // ---------------------------------------------------------------- int8 x ---
 template <class Fmt, int L, int GPL>
 __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, int row_end,
-                                             const uint32_t* tab, int32_t* out) {
+                                             const uint32_t* tab, const uint4* xs, int32_t* out) {
   constexpr int RPW = kWave / L;
   constexpr int RPI = (kGemvThreads / kWave) * RPW;
   constexpr int NW = Fmt::kWords;
@@ -47,14 +41,15 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
   const int rs = lane / L;
   constexpr int G = GPL * L;
 
+  // x (staged in LDS by the workgroup) -> registers: this lane's groups
+  // (each group's 128-byte slice sits 144 bytes after the previous one in LDS,
+  // so the lanes of a row read different banks)
   uint32_t xr[GPL][32];
-  const int8_t* x = static_cast<const int8_t*>(d.x);
 #pragma unroll
   for (int t = 0; t < GPL; ++t) {
-    const uint4* xp = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(t * L + lp) * kGroupWeights);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const uint4 v = xp[q];
+      const uint4 v = xs[(t * L + lp) * 9 + q];
       xr[t][4 * q + 0] = v.x;
       xr[t][4 * q + 1] = v.y;
       xr[t][4 * q + 2] = v.z;
@@ -62,15 +57,13 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
     }
   }
   // Rows past the tile load the tile's last row instead (results discarded).
-  // Two register buffers alternate (loop unrolled by two): while one row is
-  // decoded, the next row's words are in flight into the other buffer.
+  // A ring of kRing register buffers (the loop is unrolled by kRing): while
+  // one row is decoded, the words of the next kRing - 1 rows are in flight.
   const int last = row_end - 1;
-  const int r0 = row_begin + wave * RPW + rs;
-  const uint32_t* cbase = d.codes + static_cast<int64_t>(lp) * NW;
   auto fetch = [&](uint32_t (&buf)[GPL][NW], int row) {
-    const int64_t rr = min(row, last);
+    const uint32_t* rp = d.codes + static_cast<int64_t>(min(row, last)) * (G * NW);
 #pragma unroll
-    for (int t = 0; t < GPL; ++t) load_words(buf[t], cbase + (rr * G + t * L) * NW);
+    for (int t = 0; t < GPL; ++t) Fmt::load(buf[t], rp, G, t * L + lp);
   };
   auto step = [&](const uint32_t (&buf)[GPL][NW], int row) {
     int a4[4] = {0, 0, 0, 0};  // independent dot4 chains
@@ -84,15 +77,18 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
     const int acc = reduce_add_i32<L>((a4[0] + a4[1]) + (a4[2] + a4[3]));
     if (lp == 0 && row < row_end) out[row - row_begin] = acc;
   };
-  uint32_t bufa[GPL][NW], bufb[GPL][NW];
-  fetch(bufa, r0);
-  int r = r0;
-  for (int base = row_begin; base < row_end; base += 2 * RPI, r += 2 * RPI) {
-    fetch(bufb, r + RPI);
-    step(bufa, r);
-    if (base + RPI >= row_end) break;
-    fetch(bufa, r + 2 * RPI);
-    step(bufb, r + RPI);
+  uint32_t ring[kRing][GPL][NW];
+  const int r0 = row_begin + wave * RPW + rs;
+#pragma unroll
+  for (int b = 0; b + 1 < kRing; ++b) fetch(ring[b], r0 + b * RPI);
+  for (int base = row_begin, r = r0; base < row_end; base += kRing * RPI, r += kRing * RPI) {
+    // all kRing steps run; rows past the tile end are clamped loads whose
+    // results are never stored (no branch inside the ring)
+#pragma unroll
+    for (int b = 0; b < kRing; ++b) {
+      fetch(ring[(b + kRing - 1) % kRing], r + (b + kRing - 1) * RPI);
+      step(ring[b], r + b * RPI);
+    }
   }
 }
 
@@ -109,7 +105,7 @@ __device__ __forceinline__ void gemv_i8_rows_generic(const GemvDesc& d, int row_
     int acc = 0;
     for (int g = lane; g < G; g += kWave) {
       uint32_t w[NW];
-      load_words(w, d.codes + (static_cast<int64_t>(r) * G + g) * NW);
+      Fmt::load(w, d.codes + static_cast<int64_t>(r) * (G * NW), G, g);
       const uint4* xp = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(g) * kGroupWeights);
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -130,7 +126,7 @@ __device__ __forceinline__ void gemv_i8_rows_generic(const GemvDesc& d, int row_
 // v_dot2_f32_bf16 per block; fp32 accumulation, then y = acc * s_w.
 template <int L, int GPL>
 __device__ __forceinline__ void gemv_bf16_rows(const GemvDesc& d, int row_begin, int row_end, const uint2* tab,
-                                               float* out) {
+                                               const uint4* xs, float* out) {
   constexpr int RPW = kWave / L;
   constexpr int RPI = (kGemvThreads / kWave) * RPW;
   constexpr int NW = kGroupWords;
@@ -141,13 +137,11 @@ __device__ __forceinline__ void gemv_bf16_rows(const GemvDesc& d, int row_begin,
   constexpr int G = GPL * L;
 
   uint32_t xr[GPL][64];
-  const uint16_t* x = static_cast<const uint16_t*>(d.x);
 #pragma unroll
   for (int t = 0; t < GPL; ++t) {
-    const uint4* xp = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(t * L + lp) * kGroupWeights);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const uint4 v = xp[q];
+      const uint4 v = xs[(t * L + lp) * 17 + q];
       xr[t][4 * q + 0] = v.x;
       xr[t][4 * q + 1] = v.y;
       xr[t][4 * q + 2] = v.z;
@@ -155,12 +149,10 @@ __device__ __forceinline__ void gemv_bf16_rows(const GemvDesc& d, int row_begin,
     }
   }
   const int last = row_end - 1;
-  const int r0 = row_begin + wave * RPW + rs;
-  const uint32_t* cbase = d.codes + static_cast<int64_t>(lp) * NW;
   auto fetch = [&](uint32_t (&buf)[GPL][NW], int row) {
-    const int64_t rr = min(row, last);
+    const uint32_t* rp = d.codes + static_cast<int64_t>(min(row, last)) * (G * NW);
 #pragma unroll
-    for (int t = 0; t < GPL; ++t) load_words(buf[t], cbase + (rr * G + t * L) * NW);
+    for (int t = 0; t < GPL; ++t) load_group(buf[t], rp, G, t * L + lp);
   };
   auto step = [&](const uint32_t (&buf)[GPL][NW], int row) {
     float a2[2] = {0.0f, 0.0f};  // two chains: slot pairs (0,1) and (2,3)
@@ -176,15 +168,17 @@ __device__ __forceinline__ void gemv_bf16_rows(const GemvDesc& d, int row_begin,
     const float acc = reduce_add_f32<L>(a2[0] + a2[1]);
     if (lp == 0 && row < row_end) out[row - row_begin] = acc;
   };
-  uint32_t bufa[GPL][NW], bufb[GPL][NW];
-  fetch(bufa, r0);
-  int r = r0;
-  for (int base = row_begin; base < row_end; base += 2 * RPI, r += 2 * RPI) {
-    fetch(bufb, r + RPI);
-    step(bufa, r);
-    if (base + RPI >= row_end) break;
-    fetch(bufa, r + 2 * RPI);
-    step(bufb, r + RPI);
+  constexpr int NR = GPL > 1 ? 2 : kRing;  // the 3-groups-per-lane class keeps two buffers
+  uint32_t ring[NR][GPL][NW];
+  const int r0 = row_begin + wave * RPW + rs;
+#pragma unroll
+  for (int b = 0; b + 1 < NR; ++b) fetch(ring[b], r0 + b * RPI);
+  for (int base = row_begin, r = r0; base < row_end; base += NR * RPI, r += NR * RPI) {
+#pragma unroll
+    for (int b = 0; b < NR; ++b) {
+      fetch(ring[(b + NR - 1) % NR], r + (b + NR - 1) * RPI);
+      step(ring[b], r + b * RPI);
+    }
   }
 }
 
@@ -198,7 +192,7 @@ __device__ __forceinline__ void gemv_bf16_rows_generic(const GemvDesc& d, int ro
     float acc = 0.0f;
     for (int g = lane; g < G; g += kWave) {
       uint32_t w[kGroupWords];
-      load_words(w, d.codes + (static_cast<int64_t>(r) * G + g) * kGroupWords);
+      load_group(w, d.codes + static_cast<int64_t>(r) * (G * kGroupWords), G, g);
       const uint4* xp = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(g) * kGroupWeights);
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
@@ -242,19 +236,35 @@ __device__ __forceinline__ void finalize_bf16(const GemvDesc& d, int row0, int r
   }
 }
 
+// x is staged once per workgroup into LDS with contiguous 16-byte loads; the
+// register-resident classes then read their slices from LDS.  One 16-byte pad
+// follows every group slice (8 chunks for int8, 16 for bf16) so that lanes
+// reading different slices hit different banks.
+constexpr int kMaxStagedK = 8192;
+constexpr int kStagedChunksI8 = kMaxStagedK / 16 * 9 / 8;
+constexpr int kStagedChunksBf16 = kMaxStagedK * 2 / 16 * 17 / 16;
+
+template <int PERIOD>
+__device__ __forceinline__ void stage_x(uint4* xs, const void* x, int bytes) {
+  const uint4* src = static_cast<const uint4*>(x);
+  for (int i = threadIdx.x; i < bytes / 16; i += blockDim.x) xs[i + i / PERIOD] = src[i];
+}
+
 // Single problem: one kernel per class, so each keeps its own register count.
 template <class Fmt, int L, int GPL>
 __global__ __launch_bounds__(kGemvThreads) void gemv_i8_kernel(GemvDesc d, int tile_rows) {
   __shared__ uint32_t tab[32];
   __shared__ int32_t res[kMaxTileRows];
+  __shared__ uint4 xs[L == 0 ? 1 : kStagedChunksI8];
   const int row0 = blockIdx.x * tile_rows;
   const int row1 = min(row0 + tile_rows, d.n);
   Fmt::init_table(tab, threadIdx.x);
+  if (L != 0) stage_x<8>(xs, d.x, d.k);
   __syncthreads();
   if (L == 0)
     gemv_i8_rows_generic<Fmt>(d, row0, row1, tab, res);
   else
-    gemv_i8_rows<Fmt, (L > 0 ? L : 64), GPL>(d, row0, row1, tab, res);
+    gemv_i8_rows<Fmt, (L > 0 ? L : 64), GPL>(d, row0, row1, tab, xs, res);
   __syncthreads();
   finalize_i8(d, row0, row1, res);
 }
@@ -263,14 +273,16 @@ template <int L, int GPL>
 __global__ __launch_bounds__(kGemvThreads) void gemv_bf16_kernel(GemvDesc d, int tile_rows) {
   __shared__ uint2 tab[32];
   __shared__ float res[kMaxTileRows];
+  __shared__ uint4 xs[L == 0 ? 1 : kStagedChunksBf16];
   const int row0 = blockIdx.x * tile_rows;
   const int row1 = min(row0 + tile_rows, d.n);
   if (threadIdx.x < 32) tab[threadIdx.x] = decode_bf16x4(threadIdx.x);
+  if (L != 0) stage_x<16>(xs, d.x, 2 * d.k);
   __syncthreads();
   if (L == 0)
     gemv_bf16_rows_generic(d, row0, row1, tab, res);
   else
-    gemv_bf16_rows<(L > 0 ? L : 64), GPL>(d, row0, row1, tab, res);
+    gemv_bf16_rows<(L > 0 ? L : 64), GPL>(d, row0, row1, tab, xs, res);
   __syncthreads();
   finalize_bf16(d, row0, row1, res);
 }
@@ -297,6 +309,7 @@ template <class Fmt, bool WIDE>
 __global__ __launch_bounds__(kGemvThreads) void gemv_i8_grouped_kernel(const char* plan) {
   __shared__ uint32_t tab[32];
   __shared__ int32_t res[kMaxGroupedTileRows];
+  __shared__ uint4 xs[kStagedChunksI8];
   Fmt::init_table(tab, threadIdx.x);
   const PlanHeader* h = reinterpret_cast<const PlanHeader*>(plan);
   const GemvDesc* descs = reinterpret_cast<const GemvDesc*>(plan + sizeof(PlanHeader));
@@ -305,15 +318,17 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_i8_grouped_kernel(const cha
   const GemvDesc d = descs[tl.prob];
   const int row0 = tl.row0;
   const int row1 = min(row0 + tile_rows_of(d.kclass), d.n);
+  const bool staged = d.kclass != kGeneric && (WIDE || d.kclass != k3072);
+  if (staged) stage_x<8>(xs, d.x, d.k);
   __syncthreads();
   switch (d.kclass) {
-    case k1024: gemv_i8_rows<Fmt, 8, 1>(d, row0, row1, tab, res); break;
-    case k2048: gemv_i8_rows<Fmt, 16, 1>(d, row0, row1, tab, res); break;
-    case k4096: gemv_i8_rows<Fmt, 32, 1>(d, row0, row1, tab, res); break;
-    case k8192: gemv_i8_rows<Fmt, 64, 1>(d, row0, row1, tab, res); break;
+    case k1024: gemv_i8_rows<Fmt, 8, 1>(d, row0, row1, tab, xs, res); break;
+    case k2048: gemv_i8_rows<Fmt, 16, 1>(d, row0, row1, tab, xs, res); break;
+    case k4096: gemv_i8_rows<Fmt, 32, 1>(d, row0, row1, tab, xs, res); break;
+    case k8192: gemv_i8_rows<Fmt, 64, 1>(d, row0, row1, tab, xs, res); break;
     case k3072:
       if (WIDE) {
-        gemv_i8_rows<Fmt, 8, 3>(d, row0, row1, tab, res);
+        gemv_i8_rows<Fmt, 8, 3>(d, row0, row1, tab, xs, res);
         break;
       }
       [[fallthrough]];
@@ -327,6 +342,7 @@ template <bool WIDE>
 __global__ __launch_bounds__(kGemvThreads) void gemv_bf16_grouped_kernel(const char* plan) {
   __shared__ uint2 tab[32];
   __shared__ float res[kMaxGroupedTileRows];
+  __shared__ uint4 xs[kStagedChunksBf16];
   if (threadIdx.x < 32) tab[threadIdx.x] = decode_bf16x4(threadIdx.x);
   const PlanHeader* h = reinterpret_cast<const PlanHeader*>(plan);
   const GemvDesc* descs = reinterpret_cast<const GemvDesc*>(plan + sizeof(PlanHeader));
@@ -335,15 +351,17 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_bf16_grouped_kernel(const c
   const GemvDesc d = descs[tl.prob];
   const int row0 = tl.row0;
   const int row1 = min(row0 + tile_rows_of(d.kclass), d.n);
+  const bool staged = d.kclass != kGeneric && (WIDE || d.kclass != k3072);
+  if (staged) stage_x<16>(xs, d.x, 2 * d.k);
   __syncthreads();
   switch (d.kclass) {
-    case k1024: gemv_bf16_rows<8, 1>(d, row0, row1, tab, res); break;
-    case k2048: gemv_bf16_rows<16, 1>(d, row0, row1, tab, res); break;
-    case k4096: gemv_bf16_rows<32, 1>(d, row0, row1, tab, res); break;
-    case k8192: gemv_bf16_rows<64, 1>(d, row0, row1, tab, res); break;
+    case k1024: gemv_bf16_rows<8, 1>(d, row0, row1, tab, xs, res); break;
+    case k2048: gemv_bf16_rows<16, 1>(d, row0, row1, tab, xs, res); break;
+    case k4096: gemv_bf16_rows<32, 1>(d, row0, row1, tab, xs, res); break;
+    case k8192: gemv_bf16_rows<64, 1>(d, row0, row1, tab, xs, res); break;
     case k3072:
       if (WIDE) {
-        gemv_bf16_rows<8, 3>(d, row0, row1, tab, res);
+        gemv_bf16_rows<8, 3>(d, row0, row1, tab, xs, res);
         break;
       }
       [[fallthrough]];

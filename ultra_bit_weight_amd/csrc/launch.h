@@ -54,7 +54,16 @@ struct PlanHeader {
 static_assert(sizeof(PlanHeader) == 64, "plan header layout");
 constexpr uint32_t kPlanMagic = 0x53485950u;  // "PYHS"
 constexpr uint32_t kPlanVersion = 1;
-constexpr int kGroupedIters = 4;  // row iterations per grouped tile
+// Row iterations per grouped-GEMV tile and depth of the GEMV prefetch ring
+// (build-time tunables; the defaults are the measured best on MI355X).
+#ifndef SHERRY_GROUPED_ITERS
+#define SHERRY_GROUPED_ITERS 16
+#endif
+#ifndef SHERRY_RING
+#define SHERRY_RING 4
+#endif
+constexpr int kGroupedIters = SHERRY_GROUPED_ITERS;
+constexpr int kRing = SHERRY_RING;
 
 struct PlanTile {
   int32_t prob;
@@ -82,6 +91,7 @@ hipError_t launch_pack(const void* w, int w_dt, int64_t n, int64_t k, int64_t ld
 hipError_t launch_gemv(const GemvDesc& d, bool bf16_x, int32_t format, hipStream_t stream);
 hipError_t launch_gemv_grouped(const PlanHeader* host, const void* dev, hipStream_t stream);
 hipError_t launch_gemm(const GemmDesc& d, int32_t format, hipStream_t stream);
+hipError_t launch_decode(const uint32_t* codes, int64_t n, int64_t k, int8_t* t, int64_t ldt, hipStream_t stream);
 hipError_t launch_tern2_encode(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint32_t* codes,
                                hipStream_t stream);
 

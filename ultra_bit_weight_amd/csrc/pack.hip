@@ -80,7 +80,6 @@ __device__ __forceinline__ float4 load4(const _Float16* p) {
   return make_float4(static_cast<float>(h[0]), static_cast<float>(h[1]), static_cast<float>(h[2]),
                      static_cast<float>(h[3]));
 }
-struct Bf16Tag {};
 __device__ __forceinline__ float4 load4_bf16(const uint16_t* p) {
   const uint2 v = *reinterpret_cast<const uint2*>(p);
   return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u), __uint_as_float(v.y << 16),
@@ -147,7 +146,10 @@ __global__ __launch_bounds__(256) void pack_kernel(const T* w, int64_t ldw, int 
     out = j == 2 ? word[2] : out;
     out = j == 3 ? word[3] : out;
     out = j == 4 ? word[4] : out;
-    if (j < 5) codes[(static_cast<int64_t>(r) * G + g) * kGroupWords + j] = out;
+    // row layout: words 0-3 of group g at 4g, word 4 at 4G + g
+    uint32_t* rowc = codes + static_cast<int64_t>(r) * G * kGroupWords;
+    if (j < 4) rowc[4 * g + j] = out;
+    if (j == 4) rowc[4 * G + g] = out;
   }
   // row sum of kept magnitudes: wave butterfly, then across the 4 waves
 #pragma unroll
@@ -169,7 +171,35 @@ __global__ __launch_bounds__(256) void pack_kernel(const T* w, int64_t ldw, int 
   }
 }
 
+// Decode: one thread per 128-weight group; the five words are expanded
+// through the same per-block rule as the GEMV table and written as 8 x 16 B.
+__global__ __launch_bounds__(256) void decode_kernel(const uint32_t* codes, int64_t n, int G, int8_t* t,
+                                                     int64_t ldt) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= n * G) return;
+  const int64_t r = idx / G;
+  const int g = static_cast<int>(idx % G);
+  uint32_t w[kGroupWords];
+  load_group(w, codes + r * G * kGroupWords, G, g);
+  uint4* out = reinterpret_cast<uint4*>(t + r * ldt + static_cast<int64_t>(g) * kGroupWeights);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    uint32_t v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = decode_i8x4(code_offset<0>(w, 4 * q + e));
+    out[q] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_decode(const uint32_t* codes, int64_t n, int64_t k, int8_t* t, int64_t ldt, hipStream_t stream) {
+  const int G = static_cast<int>(k / kGroupWeights);
+  const int64_t groups = n * G;
+  const unsigned grid = static_cast<unsigned>((groups + 255) / 256);
+  hipLaunchKernelGGL(decode_kernel, dim3(grid), dim3(256), 0, stream, codes, n, G, t, ldt);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack(const void* w, int w_dt, int64_t n, int64_t k, int64_t ldw, uint32_t* codes, void* scales,
                        bool s_f16, hipStream_t stream) {

@@ -22,7 +22,7 @@ STATUS = {0: "SHERRY_OK", 1: "SHERRY_EINVAL", 2: "SHERRY_ESHAPE", 3: "SHERRY_EDT
           5: "SHERRY_EDEVICE", 6: "SHERRY_ELAUNCH"}
 
 EXPORTS = [
-    "sherry_version", "sherry_status_str", "sherry_packed_bytes", "sherry_pack", "sherry_gemv",
+    "sherry_version", "sherry_status_str", "sherry_packed_bytes", "sherry_pack", "sherry_decode", "sherry_gemv",
     "sherry_gemv_plan_bytes", "sherry_gemv_plan", "sherry_gemv_grouped", "sherry_gemm",
     "tern2_packed_bytes", "tern2_encode", "tern2_gemv", "tern2_gemv_plan", "tern2_gemm",
 ]
@@ -62,6 +62,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tern2_packed_bytes.argtypes = [i64, i64]
     lib.sherry_pack.restype = i
     lib.sherry_pack.argtypes = [vp, i, i64, i64, i64, vp, vp, i, vp]
+    lib.sherry_decode.restype = i
+    lib.sherry_decode.argtypes = [vp, i64, i64, vp, i64, vp]
     gemv_args = [vp, vp, i, i64, i64, vp, i, vp, vp, vp, i, vp]
     for f in (lib.sherry_gemv, lib.tern2_gemv):
         f.restype = i
@@ -135,6 +137,14 @@ def pack(w: torch.Tensor, scale_dtype=torch.float16):
     return codes, scales
 
 
+def decode(codes: torch.Tensor, n: int, k: int) -> torch.Tensor:
+    """Packed codes -> dense int8 ternary matrix [n, k]."""
+    _dev(codes)
+    t = torch.empty(n, k, dtype=torch.int8, device=codes.device)
+    _check("sherry_decode", load().sherry_decode(codes.data_ptr(), n, k, t.data_ptr(), t.stride(0), _stream()))
+    return t
+
+
 def _gemv(fn_name, codes, scales, x, x_scale, acc, y):
     _dev(codes, scales, x, x_scale, acc, y)
     n = scales.numel()
@@ -161,28 +171,31 @@ def tern2_gemv(codes, scales, x, x_scale=None, out_dtype=torch.float16, want_acc
     return acc, y
 
 
-def _gemm(fn_name, codes, scales, x, x_scales, out_dtype, want_acc, n=None):
+def _gemm(fn_name, codes, scales, x, x_scales, out_dtype, want_acc, out=None, acc_out=None):
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be [m, k] with unit column stride")
-    _dev(codes, scales, x_scales)
+    _dev(codes, scales, x_scales, acc_out)
     m, k = x.shape
-    n = scales.numel() if n is None else n
-    y = torch.empty(m, n, dtype=out_dtype, device=x.device) if out_dtype else None
-    acc = torch.empty(m, n, dtype=torch.int32, device=x.device) if want_acc else None
+    n = scales.numel()
+    y = out if out is not None else (torch.empty(m, n, dtype=out_dtype, device=x.device) if out_dtype else None)
+    if y is not None and (y.dim() != 2 or y.stride(1) != 1 or not y.is_cuda):
+        raise ValueError("out must be a [m, n] GPU tensor with unit column stride")
+    acc = acc_out if acc_out is not None else (torch.empty(m, n, dtype=torch.int32, device=x.device) if want_acc
+                                               else None)
     f = getattr(load(), fn_name)
     _check(fn_name, f(codes.data_ptr(), scales.data_ptr(), _DT[scales.dtype], n, k, x.data_ptr(), _DT[x.dtype], m,
-                      x.stride(0), _ptr(x_scales), _ptr(acc), _ptr(y), _DT[out_dtype] if out_dtype else F32,
+                      x.stride(0), _ptr(x_scales), _ptr(acc), _ptr(y), _DT[y.dtype] if y is not None else F32,
                       y.stride(0) if y is not None else n, _stream()))
     return acc, y
 
 
-def gemm(codes, scales, x, x_scales=None, out_dtype=torch.float16, want_acc=False):
+def gemm(codes, scales, x, x_scales=None, out_dtype=torch.float16, want_acc=False, out=None, acc_out=None):
     """Y[m, r] = s_x[m] s_w[r] sum_k X[m, k] T[r, k] for int8 X [m, k]."""
-    return _gemm("sherry_gemm", codes, scales, x, x_scales, out_dtype, want_acc)
+    return _gemm("sherry_gemm", codes, scales, x, x_scales, out_dtype, want_acc, out, acc_out)
 
 
-def tern2_gemm(codes, scales, x, x_scales=None, out_dtype=torch.float16, want_acc=False):
-    return _gemm("tern2_gemm", codes, scales, x, x_scales, out_dtype, want_acc)
+def tern2_gemm(codes, scales, x, x_scales=None, out_dtype=torch.float16, want_acc=False, out=None, acc_out=None):
+    return _gemm("tern2_gemm", codes, scales, x, x_scales, out_dtype, want_acc, out, acc_out)
 
 
 def tern2_encode(t: torch.Tensor) -> torch.Tensor:
