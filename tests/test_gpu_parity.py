@@ -208,6 +208,92 @@ def test_gemm_strided_x_and_fp32_out(gpu_lib):
     assert np.array_equal(y.cpu().numpy().view(np.uint32), ref_y.view(np.uint32))
 
 
+@pytest.mark.parametrize("m", [64, 100, 128, 200, 300])
+@pytest.mark.parametrize("n,k", [(1, 128), (130, 640), (100, 1024), (513, 2048), (64, 8192), (40, 3072)])
+def test_gemm_tiled_matches_oracle(gpu_lib, m, n, k):
+    """Token counts that take the tiled (prefill) kernel: ragged in tokens and rows."""
+    say(f"gemm tiled m={m} n={n} k={k}")
+    g = synth.rng(m * 7919 + n * 3 + k)
+    words = synth.random_words(n * (k // 128) * 5, g)
+    sw = synth.row_scales(n, g, np.float16)
+    xq, sx, _ = synth.act_absmax_int8(m, k, g)
+    ref_acc, ref_y = sherry_ref.gemm_i8(words, sw, n, k, xq, sx, np.float16)
+    acc, y = gpu_lib.gemm(words_dev(words), dev(sw), dev(xq), dev(sx), torch.float16, want_acc=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), ref_acc)
+    assert np.array_equal(y.cpu().numpy().view(np.uint16), ref_y.view(np.uint16))
+
+
+def test_gemm_tiled_strided_x_fp32_scales_and_out(gpu_lib):
+    say("gemm tiled strided")
+    g = synth.rng(1999)
+    m, n, k, ldx = 150, 200, 1024, 1024 + 48
+    words = synth.random_words(n * (k // 128) * 5, g)
+    sw = synth.row_scales(n, g, np.float32)
+    big = synth.x_int8_uniform((m, ldx), g)
+    ref_acc, ref_y = sherry_ref.gemm_i8(words, sw, n, k, big[:, :k], None, np.float32)
+    acc, y = gpu_lib.gemm(words_dev(words), dev(sw), dev(big)[:, :k], None, torch.float32, want_acc=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), ref_acc)
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), ref_y.view(np.uint32))
+
+
+def test_gemm_tiled_extreme_accumulators(gpu_lib):
+    """All weights +1 or all -1 against x = -128 / 127: the largest sums the
+    int32 accumulator sees at K = 8192."""
+    say("gemm tiled extremes")
+    n, k, m = 4, 8192, 64
+    t = np.zeros((n, k), np.int8)
+    t[0] = 1
+    t[1] = -1
+    t[2] = np.where(np.arange(k) % 2 == 0, 1, -1)
+    t[3] = np.where(np.arange(k) % 3 == 0, -1, 1)
+    t[:, 3::4] = 0  # keep every block 3:4
+    words, _ = sherry_ref.pack(t.astype(np.float64))
+    sw = np.ones(n, np.float32)
+    x = np.full((m, k), 127, np.int8)
+    x[1::2] = -128
+    ref_acc, _ = sherry_ref.gemm_i8(words, sw, n, k, x, None, np.float32)
+    acc, _ = gpu_lib.gemm(words_dev(words), dev(sw), dev(x), None, torch.float32, want_acc=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), ref_acc)
+
+
+@pytest.mark.parametrize("name,n,k", [("q", 2048, 2048), ("up", 8192, 2048), ("down", 2048, 8192)])
+def test_gemm_prefill_full_size_sampled(gpu_lib, name, n, k):
+    """LLaMA-3.2-1B prefill at 2048 tokens, the launch the benchmark times;
+    64 sampled weight rows checked against every token."""
+    say(f"gemm prefill {name} {n}x{k} m=2048")
+    g = synth.rng({"q": 77, "up": 78, "down": 79}[name])
+    m = 2048
+    words = synth.random_words(n * (k // 128) * 5, g)
+    sw = synth.row_scales(n, g, np.float16)
+    xq, sx, _ = synth.act_absmax_int8(m, k, g)
+    acc, y = gpu_lib.gemm(words_dev(words), dev(sw), dev(xq), dev(sx), torch.float16, want_acc=True)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, n - 1], g.integers(0, n, 62)]))
+    sub = sherry_ref.row_words(words, n, k, rows)
+    ra, ry = sherry_ref.gemm_i8(sub, sw[rows], len(rows), k, xq, sx, np.float16)
+    assert np.array_equal(acc.cpu().numpy()[:, rows], ra)
+    assert np.array_equal(y.cpu().numpy()[:, rows].view(np.uint16), ry.view(np.uint16))
+
+
+@pytest.mark.parametrize("m", [64, 130])
+@pytest.mark.parametrize("n,k", [(37, 640), (256, 2048)])
+def test_tern2_gemm_tiled(gpu_lib, m, n, k):
+    say(f"tern2 gemm tiled m={m} n={n} k={k}")
+    g = synth.rng(m + 5 * n + k)
+    t = synth.ternary_dense(n, k, g)
+    words = tern2_ref.pack(t)
+    sw = synth.row_scales(n, g, np.float16)
+    xq, sx, _ = synth.act_absmax_int8(m, k, g)
+    ref_acc, ref_y = tern2_ref.gemm_i8(words, sw, n, k, xq, sx, np.float16)
+    acc, y = gpu_lib.tern2_gemm(words_dev(words), dev(sw), dev(xq), dev(sx), torch.float16, want_acc=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), ref_acc)
+    assert np.array_equal(y.cpu().numpy().view(np.uint16), ref_y.view(np.uint16))
+
+
 # ------------------------------------------------------ 2-bit comparator ---
 
 @pytest.mark.parametrize("n,k", [(1, 128), (37, 640), (256, 2048), (64, 8192)])

@@ -33,14 +33,28 @@ struct Sherry3of4 {
   __device__ __forceinline__ static uint32_t i8x4(const uint32_t* w, int j, const uint32_t* tab) {
     return lds_u32(tab, code_offset<2>(w, j));
   }
-  // group g of a row held in LDS (same layout as in memory)
-  __device__ __forceinline__ static void lds_load(uint32_t* w, const uint32_t* row, int G, int g) {
-    const uint4 h = *reinterpret_cast<const uint4*>(row + 4 * g);
-    w[0] = h.x;
-    w[1] = h.y;
-    w[2] = h.z;
-    w[3] = h.w;
-    w[4] = row[4 * G + g];
+  // Tiled GEMM: lane part q (0..3) of a group is blocks 8q .. 8q+7, bits
+  // [40q, 40q + 40) of the 160-bit stream, which lie in words q and q + 1.
+  // part_words returns the word offsets of those two words for group g:
+  // word i < 4 sits at 4g + i, word 4 at 4G + g.
+  __device__ __forceinline__ static void part_load(uint32_t* w, const uint32_t* row, int G, int g, int q) {
+    w[0] = __builtin_nontemporal_load(row + 4 * g + q);
+    w[1] = __builtin_nontemporal_load(row + (q < 3 ? 4 * g + q + 1 : 4 * G + g));
+  }
+  // the 8 codes of part q as table offsets (code * 4)
+  __device__ __forceinline__ static void part_decode(uint32_t (&o)[8], const uint32_t* w, int q) {
+    const uint32_t sh = (8u * static_cast<uint32_t>(q)) & 31u;  // 40q mod 32
+    const uint32_t lo = __builtin_amdgcn_alignbit(w[1], w[0], sh);  // window bits 0..31
+    const uint32_t hi = w[1] >> sh;                                 // window bits 32..
+#pragma unroll
+    for (int e = 0; e < 6; ++e) o[e] = e == 0 ? (lo << 2) & 0x7Cu : (lo >> (5 * e - 2)) & 0x7Cu;
+    o[6] = __builtin_amdgcn_alignbit(hi, lo, 28) & 0x7Cu;  // window bits 30..34
+    o[7] = (hi >> 1) & 0x7Cu;                              // window bits 35..39
+  }
+  __device__ __forceinline__ static uint32_t part_i8x4(const uint32_t (&o)[8], const uint32_t* w, int b,
+                                                       const uint32_t* tab) {
+    (void)w;
+    return lds_u32(tab, o[b]);
   }
 };
 
@@ -64,17 +78,19 @@ struct Tern2 {
     const uint32_t sel = (w[j >> 2] >> (2 * (j & 3))) & 0x03030303u;
     return __builtin_amdgcn_perm(0u, 0xFF000100u, sel);
   }
-  __device__ __forceinline__ static void lds_load(uint32_t* w, const uint32_t* row, int, int g) {
-    const uint4 a = *reinterpret_cast<const uint4*>(row + 8 * g);
-    const uint4 b = *reinterpret_cast<const uint4*>(row + 8 * g + 4);
-    w[0] = a.x;
-    w[1] = a.y;
-    w[2] = a.z;
-    w[3] = a.w;
-    w[4] = b.x;
-    w[5] = b.y;
-    w[6] = b.z;
-    w[7] = b.w;
+  // Tiled GEMM: lane part q of a group is weights 32q .. 32q + 31, words 2q
+  // and 2q + 1 of the group; block b (0..7) of the part is quarter b & 3 of
+  // word 2q + (b >> 2).
+  __device__ __forceinline__ static void part_load(uint32_t* w, const uint32_t* row, int, int g, int q) {
+    const uint2 v = *reinterpret_cast<const uint2*>(row + 8 * g + 2 * q);
+    w[0] = v.x;
+    w[1] = v.y;
+  }
+  __device__ __forceinline__ static void part_decode(uint32_t (&)[8], const uint32_t*, int) {}
+  __device__ __forceinline__ static uint32_t part_i8x4(const uint32_t (&)[8], const uint32_t* w, int b,
+                                                       const uint32_t*) {
+    const uint32_t sel = (w[b >> 2] >> (2 * (b & 3))) & 0x03030303u;
+    return __builtin_amdgcn_perm(0u, 0xFF000100u, sel);
   }
 };
 
