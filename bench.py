@@ -39,10 +39,12 @@ COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "gemv_grouped_llama1b_b1_counte
 def parse_args(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=30)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--replicas", type=int, default=112)
     p.add_argument("--seed", type=int, default=2)
+    p.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                   help="sustained-load time before each timed region (lets the clocks settle)")
     p.add_argument("--no-extras", action="store_true", help="only the metric line (no secondary measurements)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
@@ -110,16 +112,33 @@ def build_layer_replicas(torch, sherry, synth, shapes, replicas, seed, x_kind="i
     return codes, probs
 
 
-def time_launches(torch, fn, steps, warmup):
+SETTLE_MS = 80.0
+
+
+def time_launches(torch, fn, steps, warmup, settle_ms=None):
     """Time `steps` back-to-back calls of fn on the current stream: one HIP event
     pair brackets the whole timed region (events between launches would add
     their own overhead to every launch), plus a wall clock around it with a
     synchronize on both sides.  Returns (mean ms per call from the events,
-    wall ms per call)."""
+    wall ms per call).
+
+    Before timing, fn runs `warmup` times and then keeps running until
+    `settle_ms` of wall time have passed: after an idle period the GPU's power
+    management first lowers the shader clock under this load and needs some
+    tens of milliseconds of sustained work to settle (measured with a clock
+    probe on MI355X: ~1.6 GHz after the first launches, ~2.3 GHz after
+    ~40 ms), so a short warmup would time the transient."""
     stream = torch.cuda.current_stream()
+    if settle_ms is None:
+        settle_ms = SETTLE_MS
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    t_settle = time.perf_counter()
+    while (time.perf_counter() - t_settle) * 1e3 < settle_ms:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -330,7 +349,9 @@ def summarize_counters(fetch_dir, write_dir):
 # ------------------------------------------------------------------- main ---
 
 def main(argv=None):
+    global SETTLE_MS
     args = parse_args(argv)
+    SETTLE_MS = args.settle_ms
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
         return 0

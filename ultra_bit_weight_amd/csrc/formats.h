@@ -5,13 +5,16 @@
 //   init_table(lds)   fill the workgroup's lookup table (call from 32 lanes)
 //   load(w, row, G, g) load group g of a row (row points at the row's words)
 //   i8x4(w, j, tab)   int8x4 dword of weights 4j .. 4j+3 of the group
+//   i8x8(w, p, pairs) the eight weights 8p .. 8p+7 (GEMV; pair table in LDS)
 //
 // Sherry3of4: 3:4-sparse ternary, 5-bit block codes ("Sherry: Hardware-
 //   Efficient 1.25-Bit Ternary Quantization via Fine-grained Sparsification",
 //   Abstract; Figure 2 caption: four weights packed in five bits).  A code is
 //   expanded through a 32-entry table in LDS: one shift-and-mask gives the
 //   table byte offset, one LDS read the four int8 weights.  The 32 entries sit
-//   in 32 distinct banks, so lookups never conflict.
+//   in 32 distinct banks, so lookups never conflict.  The GEMV reads two codes
+//   at once from a 1024-entry table of eight weights (8 KB): one extraction
+//   and one 8-byte LDS read per two blocks.
 // Tern2: the 2-bit aligned comparator (same paper, Figure 2 caption, left).
 //   Weight 4q+p of a word sits at bits 8p+2q, so (w >> 2q) & 0x03030303 holds
 //   four 2-bit fields, one per byte, and v_perm_b32 with the constant
@@ -24,8 +27,29 @@ namespace sherry {
 
 struct Sherry3of4 {
   static constexpr int kWords = kGroupWords;
+  static constexpr int kPairEntries = 1024;  // GEMV table: two codes per entry
   __device__ static void init_table(uint32_t* tab, int t) {
     if (t < 32) tab[t] = decode_i8x4(static_cast<uint32_t>(t));
+  }
+  // Pair table for the GEMV: entry c0 | c1 << 5 holds the eight int8 weights
+  // of codes c0 (low dword) and c1, i.e. of two consecutive blocks.  Built
+  // from the 32-entry table tab32 (filled and synchronised before the call).
+  __device__ static void init_pair_table(uint2* pairs, const uint32_t* tab32, int t, int nthreads) {
+    for (int e = t; e < kPairEntries; e += nthreads) pairs[e] = make_uint2(tab32[e & 31], tab32[e >> 5]);
+  }
+  // Weights of blocks 2p and 2p + 1 of a group: the two codes form the 10-bit
+  // field at bit 10p of the stream, which is the pair-table index.
+  __device__ __forceinline__ static uint2 i8x8(const uint32_t* w, int p, const uint2* pairs) {
+    const int bit = 10 * p;
+    const int i = bit >> 5;
+    const int o = bit & 31;
+    constexpr uint32_t mask = 0x3FFu << 3;  // index * 8 = byte offset
+    uint32_t off;
+    if (o <= 22)
+      off = (o >= 3 ? (w[i] >> (o - 3)) : (w[i] << (3 - o))) & mask;
+    else
+      off = __builtin_amdgcn_alignbit(w[i + 1], w[i], o - 3) & mask;
+    return lds_u64(pairs, off);
   }
   __device__ __forceinline__ static void load(uint32_t* w, const uint32_t* row, int G, int g) {
     load_group(w, row, G, g);
@@ -60,7 +84,9 @@ struct Sherry3of4 {
 
 struct Tern2 {
   static constexpr int kWords = 8;  // 128 weights * 2 bits
+  static constexpr int kPairEntries = 1;
   __device__ static void init_table(uint32_t*, int) {}
+  __device__ static void init_pair_table(uint2*, const uint32_t*, int, int) {}
   __device__ __forceinline__ static void load(uint32_t* w, const uint32_t* row, int, int g) {
     const u32x4_t* p = reinterpret_cast<const u32x4_t*>(row + 8 * g);
     const u32x4_t a = __builtin_nontemporal_load(p);
@@ -77,6 +103,9 @@ struct Tern2 {
   __device__ __forceinline__ static uint32_t i8x4(const uint32_t* w, int j, const uint32_t*) {
     const uint32_t sel = (w[j >> 2] >> (2 * (j & 3))) & 0x03030303u;
     return __builtin_amdgcn_perm(0u, 0xFF000100u, sel);
+  }
+  __device__ __forceinline__ static uint2 i8x8(const uint32_t* w, int p, const uint2*) {
+    return make_uint2(i8x4(w, 2 * p, nullptr), i8x4(w, 2 * p + 1, nullptr));
   }
   // Tiled GEMM: lane part q of a group is weights 32q .. 32q + 31, words 2q
   // and 2q + 1 of the group; block b (0..7) of the part is quarter b & 3 of

@@ -29,9 +29,19 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 
 // ---------------------------------------------------------------- int8 x ---
+// The 32-entry code table, then the pair table built from it.  Ends with a
+// barrier, so the tables are ready to read.
+template <class Fmt>
+__device__ __forceinline__ void init_tables(uint32_t* tab32, uint2* pairs) {
+  Fmt::init_table(tab32, threadIdx.x);
+  __syncthreads();
+  Fmt::init_pair_table(pairs, tab32, threadIdx.x, blockDim.x);
+  __syncthreads();
+}
+
 template <class Fmt, int L, int GPL>
-__device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, int row_end,
-                                             const uint32_t* tab, const uint4* xs, int32_t* out) {
+__device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, int row_end, uint32_t* tab32,
+                                             uint2* tab, int32_t* out) {
   constexpr int RPW = kWave / L;
   constexpr int RPI = (kGemvThreads / kWave) * RPW;
   constexpr int NW = Fmt::kWords;
@@ -41,15 +51,17 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
   const int rs = lane / L;
   constexpr int G = GPL * L;
 
-  // x (staged in LDS by the workgroup) -> registers: this lane's groups
-  // (each group's 128-byte slice sits 144 bytes after the previous one in LDS,
-  // so the lanes of a row read different banks)
+  // Start-up order keeps the memory pipe busy: this lane's x slice (shared
+  // by every row, so cache-resident after the first workgroup), then the
+  // first kRing - 1 ring entries, and only then the LDS tables and barrier.
   uint32_t xr[GPL][32];
 #pragma unroll
   for (int t = 0; t < GPL; ++t) {
+    const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(static_cast<const int8_t*>(d.x) +
+                                                         static_cast<int64_t>(t * L + lp) * kGroupWeights);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const uint4 v = xs[(t * L + lp) * 9 + q];
+      const u32x4_t v = xp[q];
       xr[t][4 * q + 0] = v.x;
       xr[t][4 * q + 1] = v.y;
       xr[t][4 * q + 2] = v.z;
@@ -70,9 +82,17 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
 #pragma unroll
     for (int t = 0; t < GPL; ++t) {
 #pragma unroll
-      for (int j = 0; j < 32; ++j)
-        a4[j & 3] = __builtin_amdgcn_sdot4(static_cast<int>(Fmt::i8x4(buf[t], j, tab)),
-                                           static_cast<int>(xr[t][j]), a4[j & 3], false);
+      for (int p = 0; p < 16; ++p) {
+        // block pairs in kPairMask: one pair-table read; the others: two
+        // reads of the 32-entry table (balances VALU against LDS bank conflicts)
+        const uint2 v = ((kPairMask >> p) & 1) ? Fmt::i8x8(buf[t], p, tab)
+                                               : make_uint2(Fmt::i8x4(buf[t], 2 * p, tab32),
+                                                            Fmt::i8x4(buf[t], 2 * p + 1, tab32));
+        a4[(2 * p) & 3] = __builtin_amdgcn_sdot4(static_cast<int>(v.x), static_cast<int>(xr[t][2 * p]),
+                                                 a4[(2 * p) & 3], false);
+        a4[(2 * p + 1) & 3] = __builtin_amdgcn_sdot4(static_cast<int>(v.y), static_cast<int>(xr[t][2 * p + 1]),
+                                                     a4[(2 * p + 1) & 3], false);
+      }
     }
     const int acc = reduce_add_i32<L>((a4[0] + a4[1]) + (a4[2] + a4[3]));
     if (lp == 0 && row < row_end) out[row - row_begin] = acc;
@@ -81,6 +101,7 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
   const int r0 = row_begin + wave * RPW + rs;
 #pragma unroll
   for (int b = 0; b + 1 < kRing; ++b) fetch(ring[b], r0 + b * RPI);
+  init_tables<Fmt>(tab32, tab);
   for (int base = row_begin, r = r0; base < row_end; base += kRing * RPI, r += kRing * RPI) {
     // all kRing steps run; rows past the tile end are clamped loads whose
     // results are never stored (no branch inside the ring)
@@ -95,8 +116,9 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
 // Any k % 128 == 0: 64 lanes per row, x read per group (not register-resident).
 template <class Fmt>
 __device__ __forceinline__ void gemv_i8_rows_generic(const GemvDesc& d, int row_begin, int row_end,
-                                                     const uint32_t* tab, int32_t* out) {
+                                                     uint32_t* tab32, uint2* tab, int32_t* out) {
   constexpr int NW = Fmt::kWords;
+  init_tables<Fmt>(tab32, tab);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int G = d.k / kGroupWeights;
@@ -110,10 +132,12 @@ __device__ __forceinline__ void gemv_i8_rows_generic(const GemvDesc& d, int row_
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const uint4 v = xp[q];
-        acc = __builtin_amdgcn_sdot4(static_cast<int>(Fmt::i8x4(w, 4 * q + 0, tab)), static_cast<int>(v.x), acc, false);
-        acc = __builtin_amdgcn_sdot4(static_cast<int>(Fmt::i8x4(w, 4 * q + 1, tab)), static_cast<int>(v.y), acc, false);
-        acc = __builtin_amdgcn_sdot4(static_cast<int>(Fmt::i8x4(w, 4 * q + 2, tab)), static_cast<int>(v.z), acc, false);
-        acc = __builtin_amdgcn_sdot4(static_cast<int>(Fmt::i8x4(w, 4 * q + 3, tab)), static_cast<int>(v.w), acc, false);
+        const uint2 w0 = Fmt::i8x8(w, 2 * q, tab);
+        const uint2 w1 = Fmt::i8x8(w, 2 * q + 1, tab);
+        acc = __builtin_amdgcn_sdot4(static_cast<int>(w0.x), static_cast<int>(v.x), acc, false);
+        acc = __builtin_amdgcn_sdot4(static_cast<int>(w0.y), static_cast<int>(v.y), acc, false);
+        acc = __builtin_amdgcn_sdot4(static_cast<int>(w1.x), static_cast<int>(v.z), acc, false);
+        acc = __builtin_amdgcn_sdot4(static_cast<int>(w1.y), static_cast<int>(v.w), acc, false);
       }
     }
     acc = reduce_add_i32<64>(acc);
@@ -236,12 +260,11 @@ __device__ __forceinline__ void finalize_bf16(const GemvDesc& d, int row0, int r
   }
 }
 
-// x is staged once per workgroup into LDS with contiguous 16-byte loads; the
-// register-resident classes then read their slices from LDS.  One 16-byte pad
-// follows every group slice (8 chunks for int8, 16 for bf16) so that lanes
-// reading different slices hit different banks.
+// bf16 x is staged once per workgroup into LDS with contiguous 16-byte
+// loads; the register-resident classes then read their slices from LDS.  One
+// 16-byte pad follows every group slice (16 chunks) so that lanes reading
+// different slices hit different banks.
 constexpr int kMaxStagedK = 8192;
-constexpr int kStagedChunksI8 = kMaxStagedK / 16 * 9 / 8;
 constexpr int kStagedChunksBf16 = kMaxStagedK * 2 / 16 * 17 / 16;
 
 template <int PERIOD>
@@ -251,20 +274,18 @@ __device__ __forceinline__ void stage_x(uint4* xs, const void* x, int bytes) {
 }
 
 // Single problem: one kernel per class, so each keeps its own register count.
+// The row walkers build the LDS tables themselves (after their first loads).
 template <class Fmt, int L, int GPL>
 __global__ __launch_bounds__(kGemvThreads) void gemv_i8_kernel(GemvDesc d, int tile_rows) {
-  __shared__ uint32_t tab[32];
+  __shared__ uint32_t tab32[32];
+  __shared__ uint2 tab[Fmt::kPairEntries];
   __shared__ int32_t res[kMaxTileRows];
-  __shared__ uint4 xs[L == 0 ? 1 : kStagedChunksI8];
   const int row0 = blockIdx.x * tile_rows;
   const int row1 = min(row0 + tile_rows, d.n);
-  Fmt::init_table(tab, threadIdx.x);
-  if (L != 0) stage_x<8>(xs, d.x, d.k);
-  __syncthreads();
   if (L == 0)
-    gemv_i8_rows_generic<Fmt>(d, row0, row1, tab, res);
+    gemv_i8_rows_generic<Fmt>(d, row0, row1, tab32, tab, res);
   else
-    gemv_i8_rows<Fmt, (L > 0 ? L : 64), GPL>(d, row0, row1, tab, xs, res);
+    gemv_i8_rows<Fmt, (L > 0 ? L : 64), GPL>(d, row0, row1, tab32, tab, res);
   __syncthreads();
   finalize_i8(d, row0, row1, res);
 }
@@ -307,10 +328,9 @@ constexpr int kMaxGroupedTileRows = (kGemvThreads / kWave) * (kWave / 8) * kGrou
 
 template <class Fmt, bool WIDE>
 __global__ __launch_bounds__(kGemvThreads) void gemv_i8_grouped_kernel(const char* plan) {
-  __shared__ uint32_t tab[32];
+  __shared__ uint32_t tab32[32];
+  __shared__ uint2 tab[Fmt::kPairEntries];
   __shared__ int32_t res[kMaxGroupedTileRows];
-  __shared__ uint4 xs[kStagedChunksI8];
-  Fmt::init_table(tab, threadIdx.x);
   const PlanHeader* h = reinterpret_cast<const PlanHeader*>(plan);
   const GemvDesc* descs = reinterpret_cast<const GemvDesc*>(plan + sizeof(PlanHeader));
   const PlanTile* tiles = reinterpret_cast<const PlanTile*>(descs + h->count);
@@ -318,21 +338,18 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_i8_grouped_kernel(const cha
   const GemvDesc d = descs[tl.prob];
   const int row0 = tl.row0;
   const int row1 = min(row0 + tile_rows_of(d.kclass), d.n);
-  const bool staged = d.kclass != kGeneric && (WIDE || d.kclass != k3072);
-  if (staged) stage_x<8>(xs, d.x, d.k);
-  __syncthreads();
   switch (d.kclass) {
-    case k1024: gemv_i8_rows<Fmt, 8, 1>(d, row0, row1, tab, xs, res); break;
-    case k2048: gemv_i8_rows<Fmt, 16, 1>(d, row0, row1, tab, xs, res); break;
-    case k4096: gemv_i8_rows<Fmt, 32, 1>(d, row0, row1, tab, xs, res); break;
-    case k8192: gemv_i8_rows<Fmt, 64, 1>(d, row0, row1, tab, xs, res); break;
+    case k1024: gemv_i8_rows<Fmt, 8, 1>(d, row0, row1, tab32, tab, res); break;
+    case k2048: gemv_i8_rows<Fmt, 16, 1>(d, row0, row1, tab32, tab, res); break;
+    case k4096: gemv_i8_rows<Fmt, 32, 1>(d, row0, row1, tab32, tab, res); break;
+    case k8192: gemv_i8_rows<Fmt, 64, 1>(d, row0, row1, tab32, tab, res); break;
     case k3072:
       if (WIDE) {
-        gemv_i8_rows<Fmt, 8, 3>(d, row0, row1, tab, xs, res);
+        gemv_i8_rows<Fmt, 8, 3>(d, row0, row1, tab32, tab, res);
         break;
       }
       [[fallthrough]];
-    default: gemv_i8_rows_generic<Fmt>(d, row0, row1, tab, res); break;
+    default: gemv_i8_rows_generic<Fmt>(d, row0, row1, tab32, tab, res); break;
   }
   __syncthreads();
   finalize_i8(d, row0, row1, res);

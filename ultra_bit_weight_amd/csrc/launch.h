@@ -64,6 +64,12 @@ constexpr uint32_t kPlanVersion = 1;
 #endif
 constexpr int kGroupedIters = SHERRY_GROUPED_ITERS;
 constexpr int kRing = SHERRY_RING;
+// GEMV decode: bit p set = block pair p of a group is read from the pair
+// table, clear = its two blocks from the 32-entry table.
+#ifndef SHERRY_PAIR_MASK
+#define SHERRY_PAIR_MASK 0x5555
+#endif
+constexpr unsigned kPairMask = SHERRY_PAIR_MASK;
 
 struct PlanTile {
   int32_t prob;
