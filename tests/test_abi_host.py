@@ -160,10 +160,10 @@ def test_grouped_plan_on_host(lib):
         arr[i] = GemvProblem(A, A, n, k, A, None, None, A)
     nbytes = lib.sherry_gemv_plan_bytes(arr, len(shapes))
     # 64-byte header + 64 bytes per problem + 8 bytes per tile; tile rows are
-    # 16 iterations x rows per iteration (4 waves x 64 / lanes per row):
-    # k=2048 -> 16 lanes -> 256 rows, k=8192 -> 64 lanes -> 64 rows,
-    # k=1024 -> 8 lanes -> 512 rows, other k -> 64 lanes -> 64 rows
-    tiles = 2048 // 256 + 512 // 256 + 2048 // 64 + 1 + -(-300 // 64)
+    # 32 iterations x rows per iteration (4 waves x 64 / lanes per row):
+    # k=2048 -> 16 lanes -> 512 rows, k=8192 -> 64 lanes -> 128 rows,
+    # k=1024 -> 8 lanes -> 1024 rows, other k -> 64 lanes -> 128 rows
+    tiles = 4 + 1 + 16 + 1 + 3
     assert nbytes == 64 + 64 * len(shapes) + 8 * tiles
     buf = ctypes.create_string_buffer(nbytes + 8)
     base = (ctypes.addressof(buf) + 7) // 8 * 8
@@ -171,6 +171,12 @@ def test_grouped_plan_on_host(lib):
     hdr = ctypes.string_at(base, 16)
     assert int.from_bytes(hdr[8:12], "little") == len(shapes)
     assert int.from_bytes(hdr[12:16], "little") == tiles
+    # tiles of the longest rows come first (k = 8192, then 2048, 1024, 384)
+    raw = ctypes.string_at(base + 64 + 64 * len(shapes), 8 * tiles)
+    order = [(int.from_bytes(raw[8 * t:8 * t + 4], "little"), int.from_bytes(raw[8 * t + 4:8 * t + 8], "little"))
+             for t in range(tiles)]
+    assert order == ([(2, 128 * j) for j in range(16)] + [(0, 0), (0, 512), (0, 1024), (0, 1536), (1, 0)] +
+                     [(3, 0)] + [(4, 0), (4, 128), (4, 256)])
     assert lib.sherry_gemv_plan(arr, len(shapes), F16, I8, F16, base, nbytes - 8) == EINVAL
     assert lib.sherry_gemv_plan(arr, len(shapes), F16, F32, F16, base, nbytes) == EDTYPE
     assert lib.sherry_gemv_plan(arr, len(shapes), F16, I8, F16, base + 4, nbytes) == EALIGN

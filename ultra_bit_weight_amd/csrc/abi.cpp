@@ -3,9 +3,11 @@
 // Every argument check runs on the host before the first HIP call, so an
 // invalid call returns a status without touching the device (and can be
 // tested without a GPU).  Contracts are documented in include/sherry.h.
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 #include <limits>
+#include <vector>
 
 #include "launch.h"
 #include "sherry.h"
@@ -192,10 +194,18 @@ sherry_status plan_impl(int32_t format, const sherry_gemv_problem* probs, int32_
   std::memcpy(out, &h, sizeof(h));
   GemvDesc* descs = reinterpret_cast<GemvDesc*>(out + sizeof(PlanHeader));
   PlanTile* tiles = reinterpret_cast<PlanTile*>(descs + count);
-  int64_t t = 0;
   for (int32_t i = 0; i < count; ++i) {
     const sherry_gemv_problem& p = probs[i];
     descs[i] = make_desc(p.codes, p.w_scales, s_dt, p.n, p.k, p.x, p.x_scale, p.acc, p.y, y_dt);
+  }
+  // Tiles of the longest rows first: the workgroups are dispatched in tile
+  // order, so the large tiles start early and the small ones fill the tail.
+  std::vector<int32_t> order(static_cast<size_t>(count));
+  for (int32_t i = 0; i < count; ++i) order[static_cast<size_t>(i)] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return probs[a].k > probs[b].k; });
+  int64_t t = 0;
+  for (const int32_t i : order) {
+    const sherry_gemv_problem& p = probs[i];
     const int64_t rows = tile_rows_for(p);
     for (int64_t r0 = 0; r0 < p.n; r0 += rows) tiles[t++] = PlanTile{i, static_cast<int32_t>(r0)};
   }

@@ -88,14 +88,30 @@ __device__ __forceinline__ uint32_t code_offset(const uint32_t* w, int j) {
 // the lanes reading consecutive groups issue one contiguous 16-byte-per-lane
 // load and one contiguous 4-byte-per-lane load.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));  // MFMA int8 operands / int32 accumulators
+
+// Pointers read from a grouped plan are generic to the compiler, which then
+// emits FLAT accesses; those also count against the LDS wait counter, so an
+// LDS wait would drain the prefetched loads too.  Every device-memory access
+// goes through gmem(), which states the global address space.
+#define SHERRY_GLOBAL __attribute__((address_space(1)))
+template <class T>
+__device__ __forceinline__ const SHERRY_GLOBAL T* gmem(const T* p) {
+  return (const SHERRY_GLOBAL T*)p;
+}
+template <class T>
+__device__ __forceinline__ SHERRY_GLOBAL T* gmem(T* p) {
+  return (SHERRY_GLOBAL T*)p;
+}
 
 __device__ __forceinline__ void load_group(uint32_t* w, const uint32_t* row, int G, int g) {
-  const u32x4_t h = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + 4 * g));
+  const u32x4_t h = __builtin_nontemporal_load(gmem(reinterpret_cast<const u32x4_t*>(row + 4 * g)));
   w[0] = h.x;
   w[1] = h.y;
   w[2] = h.z;
   w[3] = h.w;
-  w[4] = __builtin_nontemporal_load(row + 4 * G + g);
+  w[4] = __builtin_nontemporal_load(gmem(row + 4 * G + g));
 }
 
 __device__ __forceinline__ uint32_t lds_u32(const uint32_t* base, uint32_t byte_off) {
@@ -136,15 +152,15 @@ __device__ __forceinline__ float reduce_add_f32(float v) {
 
 // ---- epilogue: y = ydt((fp32(acc) * s_w) * s_x), each product IEEE RNE ----
 __device__ __forceinline__ float load_scale(const void* s, int r, bool f16) {
-  return f16 ? static_cast<float>(reinterpret_cast<const _Float16*>(s)[r])
-             : reinterpret_cast<const float*>(s)[r];
+  return f16 ? static_cast<float>(gmem(reinterpret_cast<const _Float16*>(s))[r])
+             : gmem(reinterpret_cast<const float*>(s))[r];
 }
 
 __device__ __forceinline__ void store_y(void* y, int64_t idx, float v, bool f16) {
   if (f16)
-    reinterpret_cast<_Float16*>(y)[idx] = static_cast<_Float16>(v);
+    gmem(reinterpret_cast<_Float16*>(y))[idx] = static_cast<_Float16>(v);
   else
-    reinterpret_cast<float*>(y)[idx] = v;
+    gmem(reinterpret_cast<float*>(y))[idx] = v;
 }
 
 __device__ __forceinline__ float epilogue_i32(int32_t acc, float sw, float sx, bool has_sx) {

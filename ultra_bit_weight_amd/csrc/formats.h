@@ -62,8 +62,8 @@ struct Sherry3of4 {
   // part_words returns the word offsets of those two words for group g:
   // word i < 4 sits at 4g + i, word 4 at 4G + g.
   __device__ __forceinline__ static void part_load(uint32_t* w, const uint32_t* row, int G, int g, int q) {
-    w[0] = __builtin_nontemporal_load(row + 4 * g + q);
-    w[1] = __builtin_nontemporal_load(row + (q < 3 ? 4 * g + q + 1 : 4 * G + g));
+    w[0] = __builtin_nontemporal_load(gmem(row + 4 * g + q));
+    w[1] = __builtin_nontemporal_load(gmem(row + (q < 3 ? 4 * g + q + 1 : 4 * G + g)));
   }
   // the 8 codes of part q as table offsets (code * 4)
   __device__ __forceinline__ static void part_decode(uint32_t (&o)[8], const uint32_t* w, int q) {
@@ -89,8 +89,8 @@ struct Tern2 {
   __device__ static void init_pair_table(uint2*, const uint32_t*, int, int) {}
   __device__ __forceinline__ static void load(uint32_t* w, const uint32_t* row, int, int g) {
     const u32x4_t* p = reinterpret_cast<const u32x4_t*>(row + 8 * g);
-    const u32x4_t a = __builtin_nontemporal_load(p);
-    const u32x4_t b = __builtin_nontemporal_load(p + 1);
+    const u32x4_t a = __builtin_nontemporal_load(gmem(p));
+    const u32x4_t b = __builtin_nontemporal_load(gmem(p + 1));
     w[0] = a.x;
     w[1] = a.y;
     w[2] = a.z;
@@ -111,7 +111,7 @@ struct Tern2 {
   // and 2q + 1 of the group; block b (0..7) of the part is quarter b & 3 of
   // word 2q + (b >> 2).
   __device__ __forceinline__ static void part_load(uint32_t* w, const uint32_t* row, int, int g, int q) {
-    const uint2 v = *reinterpret_cast<const uint2*>(row + 8 * g + 2 * q);
+    const u32x2_t v = *gmem(reinterpret_cast<const u32x2_t*>(row + 8 * g + 2 * q));
     w[0] = v.x;
     w[1] = v.y;
   }

@@ -18,7 +18,6 @@
 namespace sherry {
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxKRanges = 16;  // waves per workgroup (k <= 8192 stays x-stationary)
 

@@ -57,8 +57,8 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
   uint32_t xr[GPL][32];
 #pragma unroll
   for (int t = 0; t < GPL; ++t) {
-    const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(static_cast<const int8_t*>(d.x) +
-                                                         static_cast<int64_t>(t * L + lp) * kGroupWeights);
+    const SHERRY_GLOBAL u32x4_t* xp = gmem(reinterpret_cast<const u32x4_t*>(
+        static_cast<const int8_t*>(d.x) + static_cast<int64_t>(t * L + lp) * kGroupWeights));
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const u32x4_t v = xp[q];
@@ -128,10 +128,11 @@ __device__ __forceinline__ void gemv_i8_rows_generic(const GemvDesc& d, int row_
     for (int g = lane; g < G; g += kWave) {
       uint32_t w[NW];
       Fmt::load(w, d.codes + static_cast<int64_t>(r) * (G * NW), G, g);
-      const uint4* xp = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(g) * kGroupWeights);
+      const SHERRY_GLOBAL u32x4_t* xp =
+          gmem(reinterpret_cast<const u32x4_t*>(x + static_cast<int64_t>(g) * kGroupWeights));
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const uint4 v = xp[q];
+        const u32x4_t v = xp[q];
         const uint2 w0 = Fmt::i8x8(w, 2 * q, tab);
         const uint2 w1 = Fmt::i8x8(w, 2 * q + 1, tab);
         acc = __builtin_amdgcn_sdot4(static_cast<int>(w0.x), static_cast<int>(v.x), acc, false);
@@ -217,10 +218,11 @@ __device__ __forceinline__ void gemv_bf16_rows_generic(const GemvDesc& d, int ro
     for (int g = lane; g < G; g += kWave) {
       uint32_t w[kGroupWords];
       load_group(w, d.codes + static_cast<int64_t>(r) * (G * kGroupWords), G, g);
-      const uint4* xp = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(g) * kGroupWeights);
+      const SHERRY_GLOBAL u32x4_t* xp =
+          gmem(reinterpret_cast<const u32x4_t*>(x + static_cast<int64_t>(g) * kGroupWeights));
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const uint4 v = xp[q];
+        const u32x4_t v = xp[q];
         const uint2 w0 = lds_u64(tab, code_offset<3>(w, 2 * q));
         const uint2 w1 = lds_u64(tab, code_offset<3>(w, 2 * q + 1));
         acc = dot2_bf16(w0.x, v.x, acc);
@@ -244,10 +246,10 @@ __device__ __forceinline__ void finalize_i8(const GemvDesc& d, int row0, int row
   const bool s_f16 = d.flags & kFlagScaleF16;
   const bool y_f16 = d.flags & kFlagYF16;
   const bool has_sx = d.x_scale != nullptr;
-  const float sx = has_sx ? *d.x_scale : 1.0f;
+  const float sx = has_sx ? *gmem(d.x_scale) : 1.0f;
   for (int i = threadIdx.x; i < row1 - row0; i += blockDim.x) {
     const int r = row0 + i;
-    if (d.acc) d.acc[r] = res[i];
+    if (d.acc) gmem(d.acc)[r] = res[i];
     if (d.y) store_y(d.y, r, epilogue_i32(res[i], load_scale(d.w_scales, r, s_f16), sx, has_sx), y_f16);
   }
 }
@@ -256,7 +258,7 @@ __device__ __forceinline__ void finalize_bf16(const GemvDesc& d, int row0, int r
   const bool s_f16 = d.flags & kFlagScaleF16;
   for (int i = threadIdx.x; i < row1 - row0; i += blockDim.x) {
     const int r = row0 + i;
-    reinterpret_cast<float*>(d.y)[r] = __fmul_rn(res[i], load_scale(d.w_scales, r, s_f16));
+    gmem(reinterpret_cast<float*>(d.y))[r] = __fmul_rn(res[i], load_scale(d.w_scales, r, s_f16));
   }
 }
 
@@ -269,8 +271,8 @@ constexpr int kStagedChunksBf16 = kMaxStagedK * 2 / 16 * 17 / 16;
 
 template <int PERIOD>
 __device__ __forceinline__ void stage_x(uint4* xs, const void* x, int bytes) {
-  const uint4* src = static_cast<const uint4*>(x);
-  for (int i = threadIdx.x; i < bytes / 16; i += blockDim.x) xs[i + i / PERIOD] = src[i];
+  const SHERRY_GLOBAL u32x4_t* src = gmem(static_cast<const u32x4_t*>(x));
+  for (int i = threadIdx.x; i < bytes / 16; i += blockDim.x) reinterpret_cast<u32x4_t*>(xs)[i + i / PERIOD] = src[i];
 }
 
 // Single problem: one kernel per class, so each keeps its own register count.

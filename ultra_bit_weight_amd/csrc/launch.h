@@ -33,11 +33,15 @@ inline int lanes_per_row(int32_t kc) {
     default: return 64;
   }
 }
-constexpr int kGemvThreads = 256;  // 4 waves
+#ifndef SHERRY_GEMV_THREADS
+#define SHERRY_GEMV_THREADS 256
+#endif
+constexpr int kGemvThreads = SHERRY_GEMV_THREADS;  // GEMV workgroup size (4 waves by default)
 // Rows one GEMV workgroup advances per iteration.
 inline int rows_per_iter(int32_t kc) { return (kGemvThreads / kWave) * (kWave / lanes_per_row(kc)); }
 
 enum Format : int32_t { kFmtSherry = 0, kFmtTern2 = 1 };
+
 
 struct PlanHeader {
   uint32_t magic;
@@ -57,7 +61,7 @@ constexpr uint32_t kPlanVersion = 1;
 // Row iterations per grouped-GEMV tile and depth of the GEMV prefetch ring
 // (build-time tunables; the defaults are the measured best on MI355X).
 #ifndef SHERRY_GROUPED_ITERS
-#define SHERRY_GROUPED_ITERS 16
+#define SHERRY_GROUPED_ITERS 32
 #endif
 #ifndef SHERRY_RING
 #define SHERRY_RING 4
