@@ -78,7 +78,8 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
     for (int t = 0; t < GPL; ++t) Fmt::load(buf[t], rp, G, t * L + lp);
   };
   auto step = [&](const uint32_t (&buf)[GPL][NW], int row) {
-    int a4[4] = {0, 0, 0, 0};  // independent dot4 chains
+    constexpr int C = kDotChains;  // independent dot4 accumulation chains
+    int a4[C] = {};
 #pragma unroll
     for (int t = 0; t < GPL; ++t) {
 #pragma unroll
@@ -88,13 +89,16 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
         const uint2 v = ((kPairMask >> p) & 1) ? Fmt::i8x8(buf[t], p, tab)
                                                : make_uint2(Fmt::i8x4(buf[t], 2 * p, tab32),
                                                             Fmt::i8x4(buf[t], 2 * p + 1, tab32));
-        a4[(2 * p) & 3] = __builtin_amdgcn_sdot4(static_cast<int>(v.x), static_cast<int>(xr[t][2 * p]),
-                                                 a4[(2 * p) & 3], false);
-        a4[(2 * p + 1) & 3] = __builtin_amdgcn_sdot4(static_cast<int>(v.y), static_cast<int>(xr[t][2 * p + 1]),
-                                                     a4[(2 * p + 1) & 3], false);
+        a4[(2 * p) % C] = __builtin_amdgcn_sdot4(static_cast<int>(v.x), static_cast<int>(xr[t][2 * p]),
+                                                 a4[(2 * p) % C], false);
+        a4[(2 * p + 1) % C] = __builtin_amdgcn_sdot4(static_cast<int>(v.y), static_cast<int>(xr[t][2 * p + 1]),
+                                                     a4[(2 * p + 1) % C], false);
       }
     }
-    const int acc = reduce_add_i32<L>((a4[0] + a4[1]) + (a4[2] + a4[3]));
+    int sum = a4[0];
+#pragma unroll
+    for (int c = 1; c < C; ++c) sum += a4[c];
+    const int acc = reduce_add_i32<L>(sum);
     if (lp == 0 && row < row_end) out[row - row_begin] = acc;
   };
   uint32_t ring[kRing][GPL][NW];

@@ -74,6 +74,11 @@ constexpr int kRing = SHERRY_RING;
 #define SHERRY_PAIR_MASK 0x5555
 #endif
 constexpr unsigned kPairMask = SHERRY_PAIR_MASK;
+// Independent v_dot4 accumulation chains per row step.
+#ifndef SHERRY_DOT_CHAINS
+#define SHERRY_DOT_CHAINS 1
+#endif
+constexpr int kDotChains = SHERRY_DOT_CHAINS;
 
 struct PlanTile {
   int32_t prob;
