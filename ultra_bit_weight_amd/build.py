@@ -40,9 +40,16 @@ def common_flags() -> list:
     ]
 
 
+# Per-source flags.  gemm.hip: MFMA accumulators in ordinary VGPRs (the
+# default AGPR form made the compiler copy the tiled kernel's accumulators
+# between the two register files on every k step).
+FILE_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str, save_temps: bool, objdir: str, defines) -> str:
     obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *common_flags(), *FILE_FLAGS.get(src, []), *[f"-D{d}" for d in defines], "-c",
+           os.path.join(CSRC, src), "-o", obj]
     if save_temps:
         cmd += ["-save-temps=obj"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -80,6 +80,21 @@ struct Sherry3of4 {
     (void)w;
     return lds_u32(tab, o[b]);
   }
+  // Tiled GEMM copies a step's words of a row into LDS as kTileChunks 16-byte
+  // chunks (chunk-major, rows contiguous) and, with kTileTail, one 4-byte word:
+  // here words 0-3 of group g (at 4g) and word 4 (at 4G + g).
+  static constexpr int kTileChunks = 1;
+  static constexpr bool kTileTail = true;
+  __device__ __forceinline__ static const uint32_t* tile_src(const uint32_t* row, int G, int g, int kind) {
+    return kind < kTileChunks ? row + 4 * g : row + 4 * G + g;
+  }
+  // the two words of part q of row r from those LDS copies (R rows per chunk)
+  __device__ __forceinline__ static void tile_words(uint32_t* w, const uint32_t* chunks, const uint32_t* tail, int R,
+                                                    int r, int q) {
+    (void)R;
+    w[0] = chunks[4 * r + q];
+    w[1] = q < 3 ? chunks[4 * r + q + 1] : tail[r];
+  }
 };
 
 struct Tern2 {
@@ -120,6 +135,18 @@ struct Tern2 {
                                                        const uint32_t*) {
     const uint32_t sel = (w[b >> 2] >> (2 * (b & 3))) & 0x03030303u;
     return __builtin_amdgcn_perm(0u, 0xFF000100u, sel);
+  }
+  // Tiled GEMM copies: the group's 8 words as two 16-byte chunks, no tail.
+  static constexpr int kTileChunks = 2;
+  static constexpr bool kTileTail = false;
+  __device__ __forceinline__ static const uint32_t* tile_src(const uint32_t* row, int, int g, int kind) {
+    return row + 8 * g + 4 * kind;
+  }
+  __device__ __forceinline__ static void tile_words(uint32_t* w, const uint32_t* chunks, const uint32_t*, int R,
+                                                    int r, int q) {
+    const uint32_t* h = chunks + 4 * ((q >> 1) * R + r) + 2 * (q & 1);
+    w[0] = h[0];
+    w[1] = h[1];
   }
 };
 
