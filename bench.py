@@ -270,28 +270,65 @@ def extras(torch, sherry, synth, probs_1b, codes_1b, args):
     g = synth.rng(args.seed + 7)
     gemm = {}
     layer0 = [p for p in probs_1b if p["replica"] < 16]
-    for m in (2, 4, 8, 16, 2048):
+
+    # prefill, 2048 tokens: the layer's seven matrices in one grouped launch,
+    # and the 2-bit comparator on the same ternary matrices
+    m = 2048
+    xs = {}
+    for _, n, k in shapes_1b:
+        if k not in xs:
+            xq, sx, _ = synth.act_absmax_int8(m, k, g)
+            xs[k] = (torch.from_numpy(xq).to(dev), torch.from_numpy(sx).to(dev))
+    rep0 = [p for p in probs_1b if p["replica"] == 0]
+    ops = 2 * m * sum(n * k for _, n, k in shapes_1b)
+    for label, tern2 in (("M2048_grouped", False), ("M2048_grouped_tern2", True)):
+        gp = []
+        for p in rep0:
+            codes = p["codes"]
+            if tern2:
+                codes = sherry.tern2_encode(sherry.decode(p["codes"], p["n"], p["k"]))
+            x, sx = xs[p["k"]]
+            gp.append(dict(codes=codes, scales=p["scales"], x=x, x_scales=sx,
+                           y=torch.empty(m, p["n"], dtype=torch.float16, device=dev)))
+        grouped = sherry.GroupedGemm(gp, tern2=tern2)
+        mean_ms, _ = time_launches(torch, grouped, 20, 3)
+        gemm[label] = {"us_per_layer": round(mean_ms * 1e3, 2), "workgroups": grouped.n_tiles,
+                       "TOPS": round(ops / (mean_ms * 1e-3) / 1e12, 2),
+                       "frac_int8_peak": round(ops / (mean_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4)}
+        del gp, grouped
+    gemm["M2048_sherry_over_tern2"] = round(gemm["M2048_grouped_tern2"]["us_per_layer"] /
+                                            gemm["M2048_grouped"]["us_per_layer"], 3)
+    torch.cuda.empty_cache()
+
+    # a few tokens (small-batch decode): every matrix of all R replicas in one
+    # grouped launch (256 x 16 tiles, HBM-bound), and, for latency, one layer's
+    # seven matrices as separate calls
+    for m in (2, 4, 8, 16):
         xs = {}
         for _, n, k in shapes_1b:
             if k not in xs:
                 xq, sx, _ = synth.act_absmax_int8(m, k, g)
                 xs[k] = (torch.from_numpy(xq).to(dev), torch.from_numpy(sx).to(dev))
-        ys = {p["name"]: torch.empty(m, p["n"], dtype=torch.float16, device=dev) for p in layer0[:7]}
-        reps = 16 if m <= 16 else 1
-        sel = [p for p in layer0 if p["replica"] < reps]
-
-        def layer_pass():
-            for p in sel:
-                x, sx = xs[p["k"]]
-                sherry.gemm(p["codes"], p["scales"], x, sx, out=ys[p["name"]])
-        mean_ms, _ = time_launches(torch, layer_pass, 5 if m <= 16 else 3, 2)
-        per_layer_ms = mean_ms / reps
+        ys = {p["name"]: torch.empty(m, p["n"], dtype=torch.float16, device=dev) for p in rep0}
+        gp = [dict(codes=p["codes"], scales=p["scales"], x=xs[p["k"]][0], x_scales=xs[p["k"]][1], y=ys[p["name"]])
+              for p in probs_1b]
+        grouped = sherry.GroupedGemm(gp)
+        mean_ms, _ = time_launches(torch, grouped, 50, 5)
+        per_layer_ms = mean_ms / R
         ops = 2 * m * sum(n * k for _, n, k in shapes_1b)
         byts = sum(n * k * 5 // 32 + 2 * n + m * k + 2 * m * n + 4 * m for _, n, k in shapes_1b)
-        gemm[f"M{m}"] = {"us_per_layer": round(per_layer_ms * 1e3, 2),
+
+        def layer_pass():
+            for p in rep0:
+                x, sx = xs[p["k"]]
+                sherry.gemm(p["codes"], p["scales"], x, sx, out=ys[p["name"]])
+        call_ms, _ = time_launches(torch, layer_pass, 20, 2)
+        gemm[f"M{m}"] = {"grouped_us_per_layer": round(per_layer_ms * 1e3, 3), "replicas": R,
+                         "GBps": round(byts / (per_layer_ms * 1e-3) / 1e9, 1),
+                         "frac_hbm": round(byts / (per_layer_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                          "TOPS": round(ops / (per_layer_ms * 1e-3) / 1e12, 2),
-                         "frac_int8_peak": round(ops / (per_layer_ms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
-                         "GBps": round(byts / (per_layer_ms * 1e-3) / 1e9, 1)}
+                         "us_per_layer_7_calls": round(call_ms * 1e3, 2)}
+        del gp, grouped
     out["gemm_1b_layer"] = gemm
 
     # packer: fp16 weights of one 1B layer -> codes + fp16 scales

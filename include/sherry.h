@@ -165,6 +165,43 @@ sherry_status sherry_gemm(const uint32_t* codes, const void* w_scales, sherry_dt
                           const float* x_scales, int32_t* acc, void* y, sherry_dtype y_dt, int64_t ldy,
                           hipStream_t stream);
 
+/* One product of a grouped GEMM (HOST struct; the pointers are device
+ * pointers with the meaning, layout and alignment of sherry_gemm's arguments). */
+typedef struct sherry_gemm_problem {
+  const uint32_t* codes;
+  const void* w_scales;
+  int64_t n;
+  int64_t k;
+  const void* x;
+  int64_t m;
+  int64_t ldx;
+  const float* x_scales; /* may be NULL */
+  int32_t* acc;          /* may be NULL */
+  void* y;               /* may be NULL (not both acc and y) */
+  int64_t ldy;
+} sherry_gemm_problem;
+
+/* Bytes of the launch plan of a grouped GEMM (a 64-byte header, one 80-byte
+ * record per problem, one 16-byte record per workgroup tile).  Returns 0 if
+ * probs is NULL, count <= 0 or a problem has an invalid shape. */
+size_t sherry_gemm_plan_bytes(const sherry_gemm_problem* probs /* HOST */, int32_t count);
+
+/* Build the plan of a grouped GEMM: many independent products for M tokens
+ * (each as in sherry_gemm, dtypes shared by all problems) in one kernel
+ * launch, e.g. the seven matrices of a decoder layer during prefill.  The
+ * tiles of the problems with the longest rows come first.  Pure host code, no
+ * HIP call; `plan` is a HOST buffer of at least sherry_gemm_plan_bytes bytes,
+ * 8-byte aligned.  The caller copies the bytes unchanged to a device buffer
+ * (8-byte aligned) and passes both to sherry_gemm_grouped. */
+sherry_status sherry_gemm_plan(const sherry_gemm_problem* probs /* HOST */, int32_t count, sherry_dtype s_dt,
+                               sherry_dtype x_dt, sherry_dtype y_dt, void* plan, size_t plan_bytes);
+
+/* Launch a planned grouped GEMM (from sherry_gemm_plan or tern2_gemm_plan).
+ * Returns SHERRY_EINVAL if the host plan header is malformed.  The device copy
+ * and every buffer named by the plan must stay alive until the kernel
+ * completes. */
+sherry_status sherry_gemm_grouped(const void* plan_host, const void* plan_dev, hipStream_t stream);
+
 /* ---- 2-bit dense-ternary comparator (Sherry Abstract and Figure 2: the
  * 2-bit aligned packing that keeps alignment by wasting bits) ----
  * Layout (a reading; the pages give none): 16 weights per little-endian
@@ -191,6 +228,10 @@ sherry_status tern2_gemv(const uint32_t* codes, const void* w_scales, sherry_dty
 sherry_status tern2_gemv_plan(const sherry_gemv_problem* probs /* HOST */, int32_t count,
                               sherry_dtype s_dt, sherry_dtype x_dt, sherry_dtype y_dt, void* plan,
                               size_t plan_bytes);
+
+/* Same contract as sherry_gemm_plan, on 2-bit codes. */
+sherry_status tern2_gemm_plan(const sherry_gemm_problem* probs /* HOST */, int32_t count, sherry_dtype s_dt,
+                              sherry_dtype x_dt, sherry_dtype y_dt, void* plan, size_t plan_bytes);
 
 /* Same contract as sherry_gemm, on 2-bit codes. */
 sherry_status tern2_gemm(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n,

@@ -187,3 +187,71 @@ def test_grouped_plan_on_host(lib):
     bad = ctypes.create_string_buffer(64)
     assert lib.sherry_gemv_grouped(ctypes.addressof(bad), A, None) == EINVAL
     assert lib.sherry_gemv_grouped(None, A, None) == EINVAL
+
+
+def test_grouped_gemm_plan_on_host(lib):
+    from ultra_bit_weight_amd.sherry import GemmProblem
+
+    def problems(shapes):
+        arr = (GemmProblem * len(shapes))()
+        for i, (n, k, m) in enumerate(shapes):
+            arr[i] = GemmProblem(A, A, n, k, A, m, k, None, None, A, n)
+        return arr
+
+    def tiles_of(base, count, n_tiles):
+        raw = ctypes.string_at(base + 64 + 80 * count, 16 * n_tiles)
+        return [tuple(int.from_bytes(raw[16 * t + 4 * f:16 * t + 4 * f + 4], "little") for f in range(3))
+                for t in range(n_tiles)]
+
+    # a prefill layer (LLaMA-3.2-1B, 2048 tokens): 256 x 192 tiles (11 token
+    # tiles, the last one ragged), longest rows first
+    layer = [(2048, 2048, 2048), (512, 2048, 2048), (512, 2048, 2048), (2048, 2048, 2048), (8192, 2048, 2048),
+             (8192, 2048, 2048), (2048, 8192, 2048)]
+    arr = problems(layer)
+    n_tiles = (8 + 2 + 2 + 8 + 32 + 32 + 8) * 11
+    nbytes = lib.sherry_gemm_plan_bytes(arr, len(layer))
+    assert nbytes == 64 + 80 * len(layer) + 16 * n_tiles
+    buf = ctypes.create_string_buffer(nbytes + 8)
+    base = (ctypes.addressof(buf) + 7) // 8 * 8
+    assert lib.sherry_gemm_plan(arr, len(layer), F16, I8, F16, base, nbytes) == OK
+    hdr = ctypes.string_at(base, 64)
+    assert int.from_bytes(hdr[8:12], "little") == len(layer)
+    assert int.from_bytes(hdr[12:16], "little") == n_tiles
+    assert int.from_bytes(hdr[40:48], "little") == 1  # 256 x 192 tiling
+    t = tiles_of(base, len(layer), n_tiles)
+    assert t[:88] == [(6, a, b) for a in range(8) for b in range(11)]  # down (k = 8192) first
+    assert t[88] == (0, 0, 0) and t[-1] == (5, 31, 10)
+    assert lib.tern2_gemm_plan(arr, len(layer), F16, I8, F16, base, nbytes) == OK
+    # a small set of problems: 128 x 128 tiles (ragged in rows and tokens)
+    small = [(300, 1024, 200), (64, 128, 64)]
+    arr2 = problems(small)
+    n2 = 3 * 2 + 1 * 1
+    nb2 = lib.sherry_gemm_plan_bytes(arr2, len(small))
+    assert nb2 == 64 + 80 * 2 + 16 * n2
+    assert lib.sherry_gemm_plan(arr2, 2, F16, I8, F16, base, nb2) == OK
+    assert int.from_bytes(ctypes.string_at(base + 40, 8), "little") == 0
+    assert tiles_of(base, 2, n2) == [(0, a, b) for a in range(3) for b in range(2)] + [(1, 0, 0)]
+    # validation: buffer too small, bad dtype, misaligned, bad shape, bad m
+    assert lib.sherry_gemm_plan(arr2, 2, F16, I8, F16, base, nb2 - 8) == EINVAL
+    assert lib.sherry_gemm_plan(arr2, 2, F16, BF16, F16, base, nb2) == EDTYPE
+    assert lib.sherry_gemm_plan(arr2, 2, F16, I8, F16, base + 4, nb2) == EALIGN
+    arr2[1].k = 100
+    assert lib.sherry_gemm_plan_bytes(arr2, 2) == 0
+    assert lib.sherry_gemm_plan(arr2, 2, F16, I8, F16, base, nb2) == ESHAPE
+    arr2[1].k = 128
+    arr2[1].m = 0
+    assert lib.sherry_gemm_plan(arr2, 2, F16, I8, F16, base, nb2) == EINVAL
+    # every problem with m <= 16: the 256 x 16 tiling
+    few = [(2048, 2048, 16), (300, 1024, 3)]
+    arr3 = problems(few)
+    n3 = 8 + 2
+    nb3 = lib.sherry_gemm_plan_bytes(arr3, 2)
+    assert nb3 == 64 + 80 * 2 + 16 * n3
+    assert lib.sherry_gemm_plan(arr3, 2, F16, I8, F16, base, nb3) == OK
+    assert int.from_bytes(ctypes.string_at(base + 40, 8), "little") == 2
+    assert tiles_of(base, 2, n3) == [(0, a, 0) for a in range(8)] + [(1, 0, 0), (1, 1, 0)]
+    # a malformed or foreign host plan is rejected before any device call
+    bad = ctypes.create_string_buffer(64)
+    assert lib.sherry_gemm_grouped(ctypes.addressof(bad), A, None) == EINVAL
+    assert lib.sherry_gemm_plan(arr, len(layer), F16, I8, F16, base, nbytes) == OK
+    assert lib.sherry_gemv_grouped(base, A, None) == EINVAL  # a GEMM plan is not a GEMV plan

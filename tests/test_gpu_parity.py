@@ -294,6 +294,103 @@ def test_tern2_gemm_tiled(gpu_lib, m, n, k):
     assert np.array_equal(y.cpu().numpy().view(np.uint16), ref_y.view(np.uint16))
 
 
+@pytest.mark.parametrize("tern2", [False, True])
+def test_grouped_gemm_small_tiling(gpu_lib, tern2):
+    """Several ragged products in one launch (128 x 128 tiles)."""
+    say(f"grouped gemm small tern2={tern2}")
+    g = synth.rng(515 + tern2)
+    shapes = [(300, 1024, 200), (64, 128, 64), (130, 640, 100), (17, 384, 300)]
+    probs, refs = [], []
+    for n, k, m in shapes:
+        sw = synth.row_scales(n, g, np.float16)
+        xq, sx, _ = synth.act_absmax_int8(m, k, g)
+        if tern2:
+            words = tern2_ref.pack(synth.ternary_dense(n, k, g))
+            refs.append(tern2_ref.gemm_i8(words, sw, n, k, xq, sx, np.float16))
+        else:
+            words = synth.random_words(n * (k // 128) * 5, g)
+            refs.append(sherry_ref.gemm_i8(words, sw, n, k, xq, sx, np.float16))
+        probs.append(dict(codes=words_dev(words), scales=dev(sw), x=dev(xq), x_scales=dev(sx),
+                          acc=torch.empty(m, n, dtype=torch.int32, device=DEV),
+                          y=torch.empty(m, n, dtype=torch.float16, device=DEV)))
+    grouped = gpu_lib.GroupedGemm(probs, tern2=tern2)
+    assert grouped.n_tiles == 3 * 2 + 1 + 2 * 1 + 1 * 3
+    grouped()
+    torch.cuda.synchronize()
+    for p, (ra, ry) in zip(probs, refs):
+        assert np.array_equal(p["acc"].cpu().numpy(), ra)
+        assert np.array_equal(p["y"].cpu().numpy().view(np.uint16), ry.view(np.uint16))
+
+
+@pytest.mark.parametrize("tern2", [False, True])
+def test_grouped_gemm_few_tokens(gpu_lib, tern2):
+    """Problems with m <= 16 in one launch (256 x 16 tiles): ragged rows,
+    every m from 1 to 16 somewhere, k from 128 to 8192."""
+    say(f"grouped gemm few tokens tern2={tern2}")
+    g = synth.rng(717 + tern2)
+    shapes = [(300, 1024, 1), (64, 128, 16), (513, 2048, 7), (17, 8192, 3), (1000, 640, 12), (2048, 3072, 16)]
+    probs, refs = [], []
+    for n, k, m in shapes:
+        sw = synth.row_scales(n, g, np.float16)
+        xq, sx, _ = synth.act_absmax_int8(m, k, g)
+        if tern2:
+            words = tern2_ref.pack(synth.ternary_dense(n, k, g))
+            refs.append(tern2_ref.gemm_i8(words, sw, n, k, xq, sx, np.float16))
+        else:
+            words = synth.random_words(n * (k // 128) * 5, g)
+            refs.append(sherry_ref.gemm_i8(words, sw, n, k, xq, sx, np.float16))
+        probs.append(dict(codes=words_dev(words), scales=dev(sw), x=dev(xq), x_scales=dev(sx),
+                          acc=torch.empty(m, n, dtype=torch.int32, device=DEV),
+                          y=torch.empty(m, n, dtype=torch.float16, device=DEV)))
+    grouped = gpu_lib.GroupedGemm(probs, tern2=tern2)
+    assert grouped.n_tiles == 2 + 1 + 3 + 1 + 4 + 8
+    grouped()
+    torch.cuda.synchronize()
+    for p, (ra, ry) in zip(probs, refs):
+        assert np.array_equal(p["acc"].cpu().numpy(), ra)
+        assert np.array_equal(p["y"].cpu().numpy().view(np.uint16), ry.view(np.uint16))
+
+
+@pytest.mark.parametrize("tern2", [False, True])
+def test_grouped_gemm_prefill_layer_sampled(gpu_lib, tern2):
+    """The seven matrices of a LLaMA-3.2-1B layer at 2048 tokens in one launch
+    (256 x 256 tiles, the benchmark's launch); 48 sampled rows of every
+    matrix checked against every token."""
+    say(f"grouped gemm prefill layer tern2={tern2}")
+    g = synth.rng(616 + tern2)
+    m = 2048
+    xs = {}
+    probs, keep = [], []
+    for name, n, k in synth.LLAMA32_1B_LAYER:
+        if k not in xs:
+            xq, sx, _ = synth.act_absmax_int8(m, k, g)
+            xs[k] = (xq, sx, dev(xq), dev(sx))
+        sw = synth.row_scales(n, g, np.float16)
+        if tern2:
+            t = synth.ternary_dense(n, k, g)
+            words = tern2_ref.pack(t)
+        else:
+            t = None
+            words = synth.random_words(n * (k // 128) * 5, g)
+        probs.append(dict(codes=words_dev(words), scales=dev(sw), x=xs[k][2], x_scales=xs[k][3],
+                          acc=torch.empty(m, n, dtype=torch.int32, device=DEV),
+                          y=torch.empty(m, n, dtype=torch.float16, device=DEV)))
+        keep.append((name, n, k, words, t, sw))
+    grouped = gpu_lib.GroupedGemm(probs, tern2=tern2)
+    grouped()
+    torch.cuda.synchronize()
+    for p, (name, n, k, words, t, sw) in zip(probs, keep):
+        rows = np.unique(np.concatenate([[0, n - 1], g.integers(0, n, 46)]))
+        xq, sx = xs[k][0], xs[k][1]
+        if tern2:
+            ra, ry = tern2_ref.gemm_i8(tern2_ref.pack(t[rows]), sw[rows], len(rows), k, xq, sx, np.float16)
+        else:
+            ra, ry = sherry_ref.gemm_i8(sherry_ref.row_words(words, n, k, rows), sw[rows], len(rows), k, xq, sx,
+                                        np.float16)
+        assert np.array_equal(p["acc"].cpu().numpy()[:, rows], ra), name
+        assert np.array_equal(p["y"].cpu().numpy()[:, rows].view(np.uint16), ry.view(np.uint16)), name
+
+
 # ------------------------------------------------------ 2-bit comparator ---
 
 @pytest.mark.parametrize("n,k", [(1, 128), (37, 640), (256, 2048), (64, 8192)])

@@ -110,22 +110,26 @@ sherry_status gemv_impl(int32_t format, const uint32_t* codes, const void* w_sca
   return launched(launch_gemv(d, x_dt == SHERRY_BF16, format, stream));
 }
 
-sherry_status gemm_impl(int32_t format, const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n,
-                        int64_t k, const void* x, sherry_dtype x_dt, int64_t m, int64_t ldx, const float* x_scales,
-                        int32_t* acc, void* y, sherry_dtype y_dt, int64_t ldy, hipStream_t stream) {
+// Validation of one product for M tokens; fills the kernel record.
+sherry_status check_gemm(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,
+                         const void* x, sherry_dtype x_dt, int64_t m, int64_t ldx, const float* x_scales, int32_t* acc,
+                         void* y, sherry_dtype y_dt, int64_t ldy, GemmDesc* out) {
   if (!codes || !w_scales || !x || (!acc && !y)) return SHERRY_EINVAL;
   if (m <= 0) return SHERRY_EINVAL;
   if (sherry_status s = check_nk(n, k)) return s;
   if (m > 16 * 65535 || ldx < k || ldx % 16 != 0 || (y && ldy < n)) return SHERRY_ESHAPE;
   if (ldx > std::numeric_limits<int64_t>::max() / m || (y && ldy > std::numeric_limits<int64_t>::max() / m))
     return SHERRY_ESHAPE;
+  // the tiled kernel addresses one matrix's codes and x with 32-bit offsets
+  if (static_cast<uint64_t>(n) * static_cast<uint64_t>(k / kGroupWeights) * kGroupWords * 4 > 0xFFFFFFFFull ||
+      static_cast<uint64_t>(m) * static_cast<uint64_t>(ldx) > 0xFFFFFFFFull)
+    return SHERRY_ESHAPE;
   if (!is_scale_dt(s_dt) || x_dt != SHERRY_I8) return SHERRY_EDTYPE;
   if (y && y_dt != SHERRY_F32 && y_dt != SHERRY_F16) return SHERRY_EDTYPE;
   if (!aligned(codes, 4) || !aligned(x, 16) || !aligned(w_scales, dt_size(s_dt)) || (acc && !aligned(acc, 4)) ||
       (x_scales && !aligned(x_scales, 4)) || (y && !aligned(y, dt_size(y_dt))))
     return SHERRY_EALIGN;
-  if (sherry_status s = check_device()) return s;
-  GemmDesc d;
+  GemmDesc& d = *out;
   d.codes = codes;
   d.w_scales = w_scales;
   d.x = static_cast<const int8_t*>(x);
@@ -138,7 +142,103 @@ sherry_status gemm_impl(int32_t format, const uint32_t* codes, const void* w_sca
   d.k = static_cast<int32_t>(k);
   d.m = static_cast<int32_t>(m);
   d.flags = (s_dt == SHERRY_F16 ? kFlagScaleF16 : 0) | (y && y_dt == SHERRY_F16 ? kFlagYF16 : 0);
+  return SHERRY_OK;
+}
+
+sherry_status gemm_impl(int32_t format, const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n,
+                        int64_t k, const void* x, sherry_dtype x_dt, int64_t m, int64_t ldx, const float* x_scales,
+                        int32_t* acc, void* y, sherry_dtype y_dt, int64_t ldy, hipStream_t stream) {
+  GemmDesc d;
+  if (sherry_status s = check_gemm(codes, w_scales, s_dt, n, k, x, x_dt, m, ldx, x_scales, acc, y, y_dt, ldy, &d))
+    return s;
+  if (sherry_status s = check_device()) return s;
   return launched(launch_gemm(d, format, stream));
+}
+
+// Grouped GEMM plan: header | GemmDesc[count] | GemmTile[n_tiles].  Tiling:
+// 256 x 16 when every problem has m <= 16; else 256 x 256 when that gives at
+// least kLargeTileMinGroups tiles; else 128 x 128.
+int64_t gemm_tiles(const sherry_gemm_problem* probs, int32_t count, int rows, int tok) {
+  int64_t tiles = 0;
+  for (int32_t i = 0; i < count; ++i) tiles += ((probs[i].n + rows - 1) / rows) * ((probs[i].m + tok - 1) / tok);
+  return tiles;
+}
+
+int64_t gemm_tiling(const sherry_gemm_problem* probs, int32_t count, int* rows, int* tok) {
+  bool skinny = true;
+  for (int32_t i = 0; i < count; ++i) skinny = skinny && probs[i].m <= kGemmSkinnyTok;
+  if (skinny) {
+    *rows = kGemmSkinnyRows;
+    *tok = kGemmSkinnyTok;
+    return kGemmTilingSkinny;
+  }
+  if (gemm_tiles(probs, count, kGemmLargeRows, kGemmLargeTok) >= kLargeTileMinGroups) {
+    *rows = kGemmLargeRows;
+    *tok = kGemmLargeTok;
+    return kGemmTilingLarge;
+  }
+  *rows = kGemmSmallRows;
+  *tok = kGemmSmallTok;
+  return kGemmTilingSmall;
+}
+
+size_t gemm_plan_bytes_impl(const sherry_gemm_problem* probs, int32_t count) {
+  if (!probs || count <= 0) return 0;
+  for (int32_t i = 0; i < count; ++i) {
+    if (check_nk(probs[i].n, probs[i].k) != SHERRY_OK) return 0;
+    if (probs[i].m <= 0 || probs[i].m > 16 * 65535) return 0;
+  }
+  int rows = 0, tok = 0;
+  gemm_tiling(probs, count, &rows, &tok);
+  const int64_t tiles = gemm_tiles(probs, count, rows, tok);
+  if (tiles > kMaxDim) return 0;
+  return sizeof(PlanHeader) + sizeof(GemmDesc) * static_cast<size_t>(count) + sizeof(GemmTile) * tiles;
+}
+
+sherry_status gemm_plan_impl(int32_t format, const sherry_gemm_problem* probs, int32_t count, sherry_dtype s_dt,
+                             sherry_dtype x_dt, sherry_dtype y_dt, void* plan, size_t plan_bytes) {
+  if (!probs || count <= 0 || !plan) return SHERRY_EINVAL;
+  std::vector<GemmDesc> descs(static_cast<size_t>(count));
+  for (int32_t i = 0; i < count; ++i) {
+    const sherry_gemm_problem& p = probs[i];
+    if (sherry_status s = check_gemm(p.codes, p.w_scales, s_dt, p.n, p.k, p.x, x_dt, p.m, p.ldx, p.x_scales, p.acc,
+                                     p.y, y_dt, p.ldy, &descs[static_cast<size_t>(i)]))
+      return s;
+  }
+  const size_t need = gemm_plan_bytes_impl(probs, count);
+  if (need == 0) return SHERRY_ESHAPE;
+  if (plan_bytes < need) return SHERRY_EINVAL;
+  if (!aligned(plan, 8)) return SHERRY_EALIGN;
+  int rows = 0, tok = 0;
+  const int64_t tiling = gemm_tiling(probs, count, &rows, &tok);
+  char* out = static_cast<char*>(plan);
+  PlanHeader h;
+  std::memset(&h, 0, sizeof(h));
+  h.magic = kGemmPlanMagic;
+  h.version = kPlanVersion;
+  h.count = count;
+  h.n_tiles = static_cast<int32_t>(gemm_tiles(probs, count, rows, tok));
+  h.s_dt = s_dt;
+  h.x_dt = x_dt;
+  h.y_dt = y_dt;
+  h.format = format;
+  h.bytes = need;
+  h.reserved[0] = static_cast<uint64_t>(tiling);
+  std::memcpy(out, &h, sizeof(h));
+  std::memcpy(out + sizeof(PlanHeader), descs.data(), sizeof(GemmDesc) * descs.size());
+  GemmTile* tiles = reinterpret_cast<GemmTile*>(out + sizeof(PlanHeader) + sizeof(GemmDesc) * descs.size());
+  // longest rows (most k steps) first
+  std::vector<int32_t> order(static_cast<size_t>(count));
+  for (int32_t i = 0; i < count; ++i) order[static_cast<size_t>(i)] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return probs[a].k > probs[b].k; });
+  int64_t t = 0;
+  for (const int32_t i : order) {
+    const int64_t tn = (probs[i].n + rows - 1) / rows, tm = (probs[i].m + tok - 1) / tok;
+    for (int64_t a = 0; a < tn; ++a)
+      for (int64_t b = 0; b < tm; ++b)
+        tiles[t++] = GemmTile{i, static_cast<int32_t>(a), static_cast<int32_t>(b), 0};
+  }
+  return SHERRY_OK;
 }
 
 // Grouped plan: header | GemvDesc[count] | PlanTile[n_tiles].
@@ -284,6 +384,32 @@ sherry_status sherry_gemv_grouped(const void* plan_host, const void* plan_dev, h
     return SHERRY_EINVAL;
   if (sherry_status s = check_device()) return s;
   return launched(launch_gemv_grouped(&h, plan_dev, stream));
+}
+
+size_t sherry_gemm_plan_bytes(const sherry_gemm_problem* probs, int32_t count) {
+  return gemm_plan_bytes_impl(probs, count);
+}
+
+sherry_status sherry_gemm_plan(const sherry_gemm_problem* probs, int32_t count, sherry_dtype s_dt, sherry_dtype x_dt,
+                               sherry_dtype y_dt, void* plan, size_t plan_bytes) {
+  return gemm_plan_impl(kFmtSherry, probs, count, s_dt, x_dt, y_dt, plan, plan_bytes);
+}
+
+sherry_status tern2_gemm_plan(const sherry_gemm_problem* probs, int32_t count, sherry_dtype s_dt, sherry_dtype x_dt,
+                              sherry_dtype y_dt, void* plan, size_t plan_bytes) {
+  return gemm_plan_impl(kFmtTern2, probs, count, s_dt, x_dt, y_dt, plan, plan_bytes);
+}
+
+sherry_status sherry_gemm_grouped(const void* plan_host, const void* plan_dev, hipStream_t stream) {
+  if (!plan_host || !plan_dev) return SHERRY_EINVAL;
+  if (!aligned(plan_host, 8) || !aligned(plan_dev, 8)) return SHERRY_EALIGN;
+  PlanHeader h;
+  std::memcpy(&h, plan_host, sizeof(h));
+  if (h.magic != kGemmPlanMagic || h.version != kPlanVersion || h.count <= 0 || h.n_tiles < 0 ||
+      (h.format != kFmtSherry && h.format != kFmtTern2))
+    return SHERRY_EINVAL;
+  if (sherry_status s = check_device()) return s;
+  return launched(launch_gemm_grouped(&h, plan_dev, stream));
 }
 
 sherry_status sherry_gemm(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,

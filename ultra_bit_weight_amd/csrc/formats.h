@@ -58,42 +58,46 @@ struct Sherry3of4 {
     return lds_u32(tab, code_offset<2>(w, j));
   }
   // Tiled GEMM: lane part q (0..3) of a group is blocks 8q .. 8q+7, bits
-  // [40q, 40q + 40) of the 160-bit stream, which lie in words q and q + 1.
-  // part_words returns the word offsets of those two words for group g:
-  // word i < 4 sits at 4g + i, word 4 at 4G + g.
-  __device__ __forceinline__ static void part_load(uint32_t* w, const uint32_t* row, int G, int g, int q) {
-    w[0] = __builtin_nontemporal_load(gmem(row + 4 * g + q));
-    w[1] = __builtin_nontemporal_load(gmem(row + (q < 3 ? 4 * g + q + 1 : 4 * G + g)));
-  }
-  // the 8 codes of part q as table offsets (code * 4)
-  __device__ __forceinline__ static void part_decode(uint32_t (&o)[8], const uint32_t* w, int q) {
-    const uint32_t sh = (8u * static_cast<uint32_t>(q)) & 31u;  // 40q mod 32
+  // [40q, 40q + 40) of the 160-bit stream, which lie in words q and q + 1
+  // (w[0], w[1]).  frag returns half s of the part (blocks 8q + 4s .. + 4) as
+  // an MFMA int8 fragment: four table lookups.
+  __device__ __forceinline__ static v4i frag(const uint32_t* w, int q, int s, const uint32_t* tab) {
+    const uint32_t sh = (8u * static_cast<uint32_t>(q)) & 31u;     // 40q mod 32
     const uint32_t lo = __builtin_amdgcn_alignbit(w[1], w[0], sh);  // window bits 0..31
-    const uint32_t hi = w[1] >> sh;                                 // window bits 32..
-#pragma unroll
-    for (int e = 0; e < 6; ++e) o[e] = e == 0 ? (lo << 2) & 0x7Cu : (lo >> (5 * e - 2)) & 0x7Cu;
-    o[6] = __builtin_amdgcn_alignbit(hi, lo, 28) & 0x7Cu;  // window bits 30..34
-    o[7] = (hi >> 1) & 0x7Cu;                              // window bits 35..39
+    uint32_t o[4];
+    if (s == 0) {
+      o[0] = (lo << 2) & 0x7Cu;
+      o[1] = (lo >> 3) & 0x7Cu;
+      o[2] = (lo >> 8) & 0x7Cu;
+      o[3] = (lo >> 13) & 0x7Cu;
+    } else {
+      const uint32_t hi = w[1] >> sh;  // window bits 32..
+      o[0] = (lo >> 18) & 0x7Cu;
+      o[1] = (lo >> 23) & 0x7Cu;
+      o[2] = __builtin_amdgcn_alignbit(hi, lo, 28) & 0x7Cu;  // window bits 30..34
+      o[3] = (hi >> 1) & 0x7Cu;                              // window bits 35..39
+    }
+    return v4i{static_cast<int>(lds_u32(tab, o[0])), static_cast<int>(lds_u32(tab, o[1])),
+               static_cast<int>(lds_u32(tab, o[2])), static_cast<int>(lds_u32(tab, o[3]))};
   }
-  __device__ __forceinline__ static uint32_t part_i8x4(const uint32_t (&o)[8], const uint32_t* w, int b,
-                                                       const uint32_t* tab) {
-    (void)w;
-    return lds_u32(tab, o[b]);
-  }
-  // Tiled GEMM copies a step's words of a row into LDS as kTileChunks 16-byte
-  // chunks (chunk-major, rows contiguous) and, with kTileTail, one 4-byte word:
-  // here words 0-3 of group g (at 4g) and word 4 (at 4G + g).
-  static constexpr int kTileChunks = 1;
+  // Tiled GEMM: codes reach LDS in stages of kTileP groups per row, as
+  // kTileHC 16-byte head chunks (words 0-3 of each group, contiguous in the
+  // row) and, with kTileTail, kTileP tail words (word 4 of each group).
+  // Word offsets from the row start (groups past the row end clamp to the
+  // last group: such words are copied but never used):
+  static constexpr int kTileP = 4;
+  static constexpr int kTileHC = 4;
   static constexpr bool kTileTail = true;
-  __device__ __forceinline__ static const uint32_t* tile_src(const uint32_t* row, int G, int g, int kind) {
-    return kind < kTileChunks ? row + 4 * g : row + 4 * G + g;
-  }
-  // the two words of part q of row r from those LDS copies (R rows per chunk)
-  __device__ __forceinline__ static void tile_words(uint32_t* w, const uint32_t* chunks, const uint32_t* tail, int R,
-                                                    int r, int q) {
-    (void)R;
-    w[0] = chunks[4 * r + q];
-    w[1] = q < 3 ? chunks[4 * r + q + 1] : tail[r];
+  __device__ __forceinline__ static int head_word(int G, int g0, int c) { return 4 * min(g0 + c, G - 1); }
+  __device__ __forceinline__ static int tail_word(int G, int g0, int j) { return 4 * G + min(g0 + j, G - 1); }
+  // part q of group j of a stage from a row's LDS copy: chunk c of the row
+  // sits at position c ^ swz
+  __device__ __forceinline__ static void stage_words(uint32_t* w, const uint32_t* heads, int swz,
+                                                     const uint32_t* tails, int j, int q) {
+    const uint32_t* c = heads + 4 * (j ^ swz);
+    w[0] = c[q];
+    const uint32_t nxt = c[min(q + 1, 3)];
+    w[1] = q < 3 ? nxt : tails[j];
   }
 };
 
@@ -123,30 +127,28 @@ struct Tern2 {
     return make_uint2(i8x4(w, 2 * p, nullptr), i8x4(w, 2 * p + 1, nullptr));
   }
   // Tiled GEMM: lane part q of a group is weights 32q .. 32q + 31, words 2q
-  // and 2q + 1 of the group; block b (0..7) of the part is quarter b & 3 of
-  // word 2q + (b >> 2).
-  __device__ __forceinline__ static void part_load(uint32_t* w, const uint32_t* row, int, int g, int q) {
-    const u32x2_t v = *gmem(reinterpret_cast<const u32x2_t*>(row + 8 * g + 2 * q));
-    w[0] = v.x;
-    w[1] = v.y;
+  // and 2q + 1 of the group (w[0], w[1]); block b (0..7) of the part is
+  // quarter b & 3 of word b >> 2.  frag returns half s (blocks 4s .. 4s + 3).
+  __device__ __forceinline__ static v4i frag(const uint32_t* w, int, int s, const uint32_t*) {
+    const uint32_t x = w[s];
+    return v4i{static_cast<int>(__builtin_amdgcn_perm(0u, 0xFF000100u, x & 0x03030303u)),
+               static_cast<int>(__builtin_amdgcn_perm(0u, 0xFF000100u, (x >> 2) & 0x03030303u)),
+               static_cast<int>(__builtin_amdgcn_perm(0u, 0xFF000100u, (x >> 4) & 0x03030303u)),
+               static_cast<int>(__builtin_amdgcn_perm(0u, 0xFF000100u, (x >> 6) & 0x03030303u))};
   }
-  __device__ __forceinline__ static void part_decode(uint32_t (&)[8], const uint32_t*, int) {}
-  __device__ __forceinline__ static uint32_t part_i8x4(const uint32_t (&)[8], const uint32_t* w, int b,
-                                                       const uint32_t*) {
-    const uint32_t sel = (w[b >> 2] >> (2 * (b & 3))) & 0x03030303u;
-    return __builtin_amdgcn_perm(0u, 0xFF000100u, sel);
-  }
-  // Tiled GEMM copies: the group's 8 words as two 16-byte chunks, no tail.
-  static constexpr int kTileChunks = 2;
+  // Tiled GEMM stages: 2 groups per row (4 chunks of 16 bytes), no tail.
+  static constexpr int kTileP = 2;
+  static constexpr int kTileHC = 4;
   static constexpr bool kTileTail = false;
-  __device__ __forceinline__ static const uint32_t* tile_src(const uint32_t* row, int, int g, int kind) {
-    return row + 8 * g + 4 * kind;
+  __device__ __forceinline__ static int head_word(int G, int g0, int c) {
+    return 8 * min(g0 + (c >> 1), G - 1) + 4 * (c & 1);
   }
-  __device__ __forceinline__ static void tile_words(uint32_t* w, const uint32_t* chunks, const uint32_t*, int R,
-                                                    int r, int q) {
-    const uint32_t* h = chunks + 4 * ((q >> 1) * R + r) + 2 * (q & 1);
-    w[0] = h[0];
-    w[1] = h[1];
+  __device__ __forceinline__ static int tail_word(int, int, int) { return 0; }
+  __device__ __forceinline__ static void stage_words(uint32_t* w, const uint32_t* heads, int swz, const uint32_t*,
+                                                     int j, int q) {
+    const uint32_t* c = heads + 4 * ((2 * j + (q >> 1)) ^ swz) + 2 * (q & 1);
+    w[0] = c[0];
+    w[1] = c[1];
   }
 };
 

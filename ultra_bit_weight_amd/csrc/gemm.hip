@@ -26,11 +26,7 @@ constexpr int kMaxKRanges = 16;  // waves per workgroup (k <= 8192 stays x-stati
 #endif
 constexpr int kTileDepth = SHERRY_TILE_DEPTH;
 static_assert(kTileDepth >= 2 && kTileDepth <= 4, "tile pipeline depth");
-// Workgroups the 256 x 256 tiling must give before it is used.
-#ifndef SHERRY_LARGE_TILE_MIN_GROUPS
-#define SHERRY_LARGE_TILE_MIN_GROUPS 256
-#endif
-constexpr int64_t kLargeTileMinGroups = SHERRY_LARGE_TILE_MIN_GROUPS;
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
 // lgkmcnt 11:8; a field at its maximum means "do not wait").
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -131,26 +127,64 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmDesc d, int n_tile
   }
 }
 
-// Tiled kernel for many tokens (prefill).  A workgroup of WR x WC waves
-// computes a (64 WR weight rows) x (16 UT WC tokens) tile of Y, stepping k by
-// one 128-weight group.  Wave w owns rows 64 (w % WR) .. + 64 and tokens
+// Tiled kernel for many tokens.  A workgroup of WR x WC waves computes a
+// (64 WR weight rows) x (16 UT WC tokens) tile of Y, stepping k by one
+// 128-weight group.  Wave w owns rows 64 (w % WR) .. + 64 and tokens
 // 16 UT (w / WR) .. + 16 UT as 4 x UT MFMA tiles.
-//   * Everything a step reads from memory is copied by the memory system
-//     straight into LDS (global_load_lds, no staging registers), kTileDepth
-//     steps ahead, into a ring of LDS buffers: the tokens' int8 tile, and per
-//     weight row of the tile the group's 16-byte head (words 0-3) and 4-byte
-//     tail (word 4).  Within a token's 128 bytes the 16-byte chunk c sits at
-//     position c ^ ((token >> 1) & 7), so the B-fragment reads of 16
-//     consecutive tokens hit 16 different bank groups.
+//   * Everything the loop reads from memory is copied by the memory system
+//     straight into LDS (global_load_lds, no staging registers):
+//       - the tokens' int8 tile of a step, D steps ahead, into a ring of D
+//         buffers.  Within a token's 128 bytes the 16-byte chunk c sits at
+//         position c ^ ((token >> 1) & 7), so the B-fragment reads of 16
+//         consecutive tokens hit 16 different bank groups;
+//       - the codes in stages of P groups, two stages ahead, into a ring of 3
+//         buffers: per row the P groups' head words (contiguous in the row,
+//         so four lanes read 64 contiguous bytes) and tail words.  Chunk c of
+//         a row sits at position c ^ ((row >> 2) & 3): the word reads of 16
+//         consecutive rows then hit 64 different banks.  A stage's copies
+//         are spread evenly over the P steps of the stage two earlier.
 //   * Lane (i, q) decodes, for each of its 4 row tiles t (row 16 t + i), part q
 //     of the group (blocks 8q .. 8q+7, two code words) straight into two A
 //     fragments: half s takes blocks 8q + 4s .. 8q + 4s + 3, i.e. k bytes
 //     32q + 16s .. + 16, which is the B fragment it reads from LDS.
 //   * One barrier per step.  Every vector-memory operation in the loop is one
 //     of these copies, a fixed number per wave and step, so before the
-//     barrier each wave waits (vmcnt) for exactly its copies of the next
-//     step; after it the whole step is in LDS and the buffers of the finished
-//     step are free for the copies issued next.
+//     barrier each wave waits (vmcnt) for its copies of the step's x tile;
+//     the copies of the step's code stage are older, so they have landed
+//     too.  After the barrier the whole step is in LDS, and the buffers of
+//     the finished step (and, at a stage start, stage) are free for the
+//     copies issued next.
+// Direct global->LDS copies (global_load_lds_dword{,x4}, saddr form): lane l
+// copies 4 or 16 bytes from base + voff to LDS byte address lds + l * size.
+// Written as asm so that the compiler does not track them: its wait-count
+// pass cannot tell which LDS buffer such a copy writes and would wait for all
+// of them before every LDS read.  The kernel waits for them explicitly.  The
+// instructions write no register (the address VGPR is read at issue); the
+// s_nop covers the M0-write-to-LDS-DMA hazard.
+__device__ __forceinline__ void lds_copy16(const SHERRY_GLOBAL void* base, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(lds), "v"(voff), "s"(base)
+      : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copy4(const SHERRY_GLOBAL void* base, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, %2"
+      :
+      : "s"(lds), "v"(voff), "s"(base)
+      : "memory", "m0");
+}
+template <class T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+  return __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) T*)p)));
+}
+
 template <int WR_, int WC_, int UT_>
 struct TileCfg {
   static constexpr int WR = WR_, WC = WC_, UT = UT_;
@@ -158,102 +192,138 @@ struct TileCfg {
   static constexpr int kThreads = kWaves * kWave;
   static constexpr int kRows = 64 * WR;
   static constexpr int kTok = 16 * UT * WC;
-  static constexpr int kXBytes = kTok * kGroupWeights;            // one step's x tile
-  static constexpr int kCopies = kXBytes / (16 * kWave) / kWaves;  // 1 KB x copies per wave per step
-  static_assert(kCopies * 16 * kWave * kWaves == kXBytes, "x tile split");
-  static constexpr int kRowGroups = kRows / 64;  // 64-row blocks (one copy each per kind)
-  static constexpr int kWgPerCu = kWaves <= 4 ? 2 : 1;  // workgroups one CU is sized to hold
+  static constexpr int kXBytes = kTok * kGroupWeights;  // one step's x tile
+  static constexpr int kXCopies = kXBytes / (16 * kWave);  // 1 KB copies of it per step
+  static_assert(kXCopies * 16 * kWave == kXBytes, "x tile split");
+  // workgroups one CU is sized to hold (sets the x ring depth)
+  static constexpr int kWgPerCu = kWaves > 4 ? 1 : 2;
 };
-using TileSmall = TileCfg<2, 2, 4>;  // 128 x 128, 4 waves
-using TileLarge = TileCfg<4, 2, 8>;  // 256 x 256, 8 waves
+using TileSmall = TileCfg<2, 2, 4>;   // 128 x 128, 4 waves
+using TileLarge = TileCfg<4, 2, 6>;   // 256 x 192, 8 waves
+using TileSkinny = TileCfg<4, 1, 1>;  // 256 x 16, 4 waves (a few tokens: HBM-bound)
+static_assert(TileSmall::kRows == kGemmSmallRows && TileSmall::kTok == kGemmSmallTok, "small tiling");
+static_assert(TileLarge::kRows == kGemmLargeRows && TileLarge::kTok == kGemmLargeTok, "large tiling");
+static_assert(TileSkinny::kRows == kGemmSkinnyRows && TileSkinny::kTok == kGemmSkinnyTok, "skinny tiling");
 
-// Ring depth: kTileDepth, or fewer steps if a CU's share of the 160 KB of LDS
-// cannot hold them (x tile + code chunks + tail words per step, plus 1 KB).
+constexpr int kCodeSlots = 3;  // code stages in LDS: in use, next, in flight
+constexpr int kTileUnroll = 12;  // steps per loop iteration: a multiple of D and of 3 P
+
+// Code bytes of one stage and x-ring depth: kTileDepth, or fewer steps if the
+// CU's share of the 160 KB of LDS cannot hold them next to the code ring.
+template <class Fmt, class C>
+constexpr int code_stage_bytes() {
+  return C::kRows * (16 * Fmt::kTileHC + (Fmt::kTileTail ? 4 * Fmt::kTileP : 0));
+}
+// The depth is also at most P + 1: a stage's last copies are then issued
+// before the x copies of its first step, so waiting for those covers them.
 template <class Fmt, class C>
 constexpr int tile_depth() {
-  constexpr int slot = C::kXBytes + C::kRows * (16 * Fmt::kTileChunks + (Fmt::kTileTail ? 4 : 0));
-  constexpr int fit = (160 * 1024 / C::kWgPerCu - 1024) / slot;
-  return fit < kTileDepth ? fit : kTileDepth;
+  constexpr int fit = (160 * 1024 / C::kWgPerCu - 1024 - kCodeSlots * code_stage_bytes<Fmt, C>()) / C::kXBytes;
+  constexpr int cap = kTileDepth < Fmt::kTileP + 1 ? kTileDepth : Fmt::kTileP + 1;
+  return fit < cap ? fit : cap;
 }
 
 template <class Fmt, class C>
-__global__ __launch_bounds__(C::kThreads) void gemm_tile_kernel(GemmDesc d) {
-  // code copies per step: one per 64-row block and kind (16-byte chunks of
-  // the format, then its 4-byte tail word), exactly one per wave
-  constexpr int kKinds = Fmt::kTileChunks + (Fmt::kTileTail ? 1 : 0);
-  static_assert(kKinds * C::kRowGroups == C::kWaves, "one code copy per wave");
+__device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int tile_m) {
   constexpr int D = tile_depth<Fmt, C>();
-  static_assert(D >= 2, "tile ring depth");
+  static_assert(D >= 2 && kTileUnroll % D == 0, "x ring depth");
+  constexpr int P = Fmt::kTileP;
+  constexpr int HC = Fmt::kTileHC;
+  static_assert(kTileUnroll % (kCodeSlots * P) == 0 && D <= P + 1, "code stage cadence");
   constexpr int UT = C::UT;
-  constexpr int NC = C::kCopies;
-  constexpr int kOpsPerStep = NC + 1;  // copies per wave and step
-  constexpr int XV = C::kXBytes / 16;
+  constexpr int W = C::kWaves;
   constexpr int R = C::kRows;
+  // x copies per step: TX, wave w issues NX w .. (those that exist)
+  constexpr int TX = C::kXCopies;
+  constexpr int NX = (TX + W - 1) / W;
+  // code copies per stage: head copies (64 chunk slots each) then tail copies
+  // (64 words each); every wave issues CPW of them in every step
+  constexpr int TH = R * HC / 64;
+  constexpr int TT = Fmt::kTileTail ? R * P / 64 : 0;
+  constexpr int CPW = (TH + TT) / (P * W);
+  static_assert(CPW * P * W == TH + TT && CPW >= 1, "code copies per wave and step");
+  constexpr int kOpsPerStep = TX / W + CPW;  // vector-memory operations per wave and step, at least
+  constexpr int XV = C::kXBytes / 16;
+  constexpr int HV = R * HC;
+  constexpr int TV = Fmt::kTileTail ? R * P : 1;
   // the code table first in LDS (largest alignment): its address then fits
   // the 16-bit offset field of the lookups
   __shared__ __attribute__((aligned(1024))) uint32_t tab[32];
   // one LDS array per ring slot and kind: distinct objects let the compiler
   // see that reading one slot does not depend on the copies to the others
   __shared__ u32x4_t xt0[XV], xt1[XV], xt2[D > 2 ? XV : 1], xt3[D > 3 ? XV : 1];
-  constexpr int HV = R * Fmt::kTileChunks;
-  constexpr int TV = Fmt::kTileTail ? R : 1;
-  __shared__ u32x4_t hd0[HV], hd1[HV], hd2[D > 2 ? HV : 1], hd3[D > 3 ? HV : 1];
-  __shared__ uint32_t tl0[TV], tl1[TV], tl2[D > 2 ? TV : 1], tl3[D > 3 ? TV : 1];
+  __shared__ u32x4_t hd0[HV], hd1[HV], hd2[HV];
+  __shared__ uint32_t tl0[TV], tl1[TV], tl2[TV];
   auto xbuf = [&](int slot) -> u32x4_t* {
     return slot == 0 ? xt0 : slot == 1 ? xt1 : slot == 2 ? xt2 : xt3;
   };
-  auto hbuf = [&](int slot) -> u32x4_t* {
-    return slot == 0 ? hd0 : slot == 1 ? hd1 : slot == 2 ? hd2 : hd3;
-  };
-  auto tbuf = [&](int slot) -> uint32_t* {
-    return slot == 0 ? tl0 : slot == 1 ? tl1 : slot == 2 ? tl2 : tl3;
-  };
+  auto hbuf = [&](int slot) -> u32x4_t* { return slot == 0 ? hd0 : slot == 1 ? hd1 : hd2; };
+  auto tbuf = [&](int slot) -> uint32_t* { return slot == 0 ? tl0 : slot == 1 ? tl1 : tl2; };
   Fmt::init_table(tab, threadIdx.x);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int i = lane & 15;
   const int q = lane >> 4;
   const int wn = wave % C::WR;
   const int wm = wave / C::WR;
-  const int n0 = blockIdx.x * R;
-  const int m0 = blockIdx.y * C::kTok;
+  const int n0 = tile_n * R;
+  const int m0 = tile_m * C::kTok;
   const int G = d.k / kGroupWeights;
   const int lastn = d.n - 1;
   const int lastm = d.m - 1;
-  typedef __attribute__((address_space(3))) void* lds_ptr;
+  // Copy sources are a uniform base plus a 32-bit per-lane byte offset (the
+  // caller keeps each matrix's codes and x below 4 GiB).
+  const uint32_t row_words = static_cast<uint32_t>(G) * Fmt::kWords;
+  const SHERRY_GLOBAL char* cbase = gmem(reinterpret_cast<const char*>(d.codes));
+  const SHERRY_GLOBAL char* xbase = gmem(reinterpret_cast<const char*>(d.x));
 
-  // x copies: copy j of wave w fills 16-byte slots 64 (NC w + j) + lane of
-  // the buffer; slot s holds chunk (s % 8) ^ ((token >> 1) & 7) of token s / 8.
-  const SHERRY_GLOBAL int8_t* xsrc[NC];
+  // x copy c fills 16-byte slots 64 c + lane of the buffer; slot s holds
+  // chunk (s % 8) ^ ((token >> 1) & 7) of token s / 8.
+  uint32_t xoff[NX];
 #pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    const int slot = 64 * (NC * wave + j) + lane;
+  for (int j = 0; j < NX; ++j) {
+    const int slot = 64 * min(NX * wave + j, TX - 1) + lane;
     const int tok = slot >> 3;
     const int chunk = (slot & 7) ^ ((tok >> 1) & 7);
-    xsrc[j] = gmem(d.x + static_cast<int64_t>(min(m0 + tok, lastm)) * d.ldx + 16 * chunk);
+    xoff[j] = static_cast<uint32_t>(min(m0 + tok, lastm)) * static_cast<uint32_t>(d.ldx) + 16u * chunk;
   }
-  // code copy of this wave: kind wave / (R / 64) (a 16-byte chunk, or the
-  // tail word) of rows 64 c + lane, c = wave % (R / 64); rows past n read row
-  // n - 1
-  const int cblk = wave % C::kRowGroups;
-  const int kind = wave / C::kRowGroups;
-  const bool is_chunk = kind < Fmt::kTileChunks;
-  const uint32_t* crow = d.codes + static_cast<int64_t>(min(n0 + 64 * cblk + lane, lastn)) * (G * Fmt::kWords);
-  auto fetch = [&](int step, int slot) {
-    const int g = min(step, G - 1);  // past the end: a valid group, never used
+  // Per-lane copy offsets are recomputed in every step from values passed
+  // through an empty asm statement: otherwise the compiler keeps the offsets
+  // of all unrolled steps live at once.
+  auto opaque = [](uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+  };
+  auto copy_x = [&](int step, int slot) {
+    const uint32_t g = static_cast<uint32_t>(min(step, G - 1));  // past the end: a valid group, never used
 #pragma unroll
-    for (int j = 0; j < NC; ++j)
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const SHERRY_GLOBAL void*>(xsrc[j] + static_cast<int64_t>(g) * kGroupWeights),
-          (lds_ptr)(xbuf(slot) + 64 * (NC * wave + j)), 16, 0, 0);
-    const SHERRY_GLOBAL uint32_t* src = gmem(Fmt::tile_src(crow, G, g, kind));
-    if (is_chunk)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const SHERRY_GLOBAL void*>(src),
-                                       (lds_ptr)(hbuf(slot) + R * kind + 64 * cblk), 16, 0, 0);
-    else
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const SHERRY_GLOBAL void*>(src),
-                                       (lds_ptr)(tbuf(slot) + 64 * cblk), 4, 0, 0);
+    for (int j = 0; j < NX; ++j) {
+      const int c = NX * wave + j;
+      if (c < TX) lds_copy16(xbase, opaque(xoff[j]) + g * kGroupWeights, lds_addr(xbuf(slot) + 64 * c));
+    }
+  };
+  // code copy c of stage `stage` (groups P stage ..), into code slot `slot`
+  auto copy_code = [&](int stage, int slot, int c) {
+    const int g0 = P * stage;
+    const int ln = static_cast<int>(opaque(static_cast<uint32_t>(lane)));
+    if (c < TH) {
+      const int sl = 64 * c + ln;  // chunk slot of the stage buffer
+      const int r = sl / HC;
+      const int chunk = (sl % HC) ^ ((r >> 2) & 3);
+      const uint32_t w = static_cast<uint32_t>(min(n0 + r, lastn)) * row_words + Fmt::head_word(G, g0, chunk);
+      lds_copy16(cbase, 4u * w, lds_addr(hbuf(slot) + 64 * c));
+    } else {
+      const int sl = 64 * (c - TH) + ln;  // word slot of the stage's tails
+      const uint32_t w = static_cast<uint32_t>(min(n0 + sl / P, lastn)) * row_words + Fmt::tail_word(G, g0, sl % P);
+      lds_copy4(cbase, 4u * w, lds_addr(tbuf(slot) + 64 * (c - TH)));
+    }
+  };
+  // in step s: this wave's share (part s % P) of the copies of stage s / P + 2
+  auto copy_code_part = [&](int s, int b) {
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+      copy_code(s / P + 2, (b / P + 2) % kCodeSlots, (b % P) * (CPW * W) + CPW * wave + j);
   };
 
   v4i acc[4][UT];
@@ -262,26 +332,22 @@ __global__ __launch_bounds__(C::kThreads) void gemm_tile_kernel(GemmDesc d) {
 #pragma unroll
     for (int u = 0; u < UT; ++u) acc[t][u] = v4i{0, 0, 0, 0};
 
-  auto compute = [&](int slot) {
-    const u32x4_t* xb = xbuf(slot);
-    const uint32_t* hb = reinterpret_cast<const uint32_t*>(hbuf(slot));
-    const uint32_t* tb = tbuf(slot);
-    // this lane's two code words of each row tile
+  // step with x in x slot xs, codes in code slot cs, group j of its stage
+  auto compute = [&](int xs, int cs, int j) {
+    const u32x4_t* xb = xbuf(xs);
+    const uint32_t* hb = reinterpret_cast<const uint32_t*>(hbuf(cs));
+    const uint32_t* tb = tbuf(cs);
     uint32_t w[4][2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) Fmt::tile_words(w[t], hb, tb, R, 64 * wn + 16 * t + i, q);
+    for (int t = 0; t < 4; ++t) {
+      const int r = 64 * wn + 16 * t + i;
+      Fmt::stage_words(w[t], hb + 4 * HC * r, (r >> 2) & 3, tb + P * r, j, q);
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       v4i a[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        uint32_t off[8];
-        Fmt::part_decode(off, w[t], q);
-        a[t] = v4i{static_cast<int>(Fmt::part_i8x4(off, w[t], 4 * s + 0, tab)),
-                   static_cast<int>(Fmt::part_i8x4(off, w[t], 4 * s + 1, tab)),
-                   static_cast<int>(Fmt::part_i8x4(off, w[t], 4 * s + 2, tab)),
-                   static_cast<int>(Fmt::part_i8x4(off, w[t], 4 * s + 3, tab))};
-      }
+      for (int t = 0; t < 4; ++t) a[t] = Fmt::frag(w[t], q, s, tab);
 #pragma unroll
       for (int u = 0; u < UT; ++u) {
         const int tok = 16 * UT * wm + 16 * u + i;
@@ -292,7 +358,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_tile_kernel(GemmDesc d) {
       }
     }
   };
-  // Wait until this wave's copies of step k landed (the copies of the D - 2
+  // Wait until this wave's x copies of step k landed (the copies of the D - 2
   // younger steps may still be in flight), then the barrier.  The empty asm
   // statements keep the compiler from moving memory accesses across.
   auto step_barrier = [&]() {
@@ -303,17 +369,36 @@ __global__ __launch_bounds__(C::kThreads) void gemm_tile_kernel(GemmDesc d) {
     asm volatile("" ::: "memory");
   };
 
+  // prologue: code stages 0 and 1, x steps 0 .. D - 2.  As in the loop, CPW
+  // code copies follow the x copies of each step, so that the wait count of
+  // the barriers holds from step 0 on: after a step's x copies every wave has
+  // issued at least kOpsPerStep * (D - 2) + CPW more operations by the
+  // barrier that needs them.  A wave's copies of one stage are copies
+  // wave + W t, t < P CPW.
+  constexpr int PC = P * CPW;
+  constexpr int late = (D - 1) * CPW;  // stage-1 copies after the x copies
+  static_assert(late <= PC, "prologue code copies");
 #pragma unroll
-  for (int b = 0; b + 1 < D; ++b) fetch(b, b);
-  __syncthreads();  // code table
-  for (int g = 0; g < G; g += D) {
+  for (int t = 0; t < PC; ++t) copy_code(0, 0, wave + W * t);
 #pragma unroll
-    for (int b = 0; b < D; ++b) {
-      // step g + b: its data sits in slot b; the slot of the previous step
-      // ((b + D - 1) % D) is refilled with step g + b + D - 1 after the barrier
+  for (int t = 0; t < PC - late; ++t) copy_code(1, 1, wave + W * t);
+#pragma unroll
+  for (int b = 0; b + 1 < D; ++b) {
+    copy_x(b, b);
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) copy_code(1, 1, wave + W * (PC - late + CPW * b + j));
+  }
+  __syncthreads();  // code table, and all of the above
+  for (int g = 0; g < G; g += kTileUnroll) {
+#pragma unroll
+    for (int b = 0; b < kTileUnroll; ++b) {
+      // step g + b: x in slot b % D, codes of stage (g + b) / P in code slot
+      // (b / P) % 3; after the barrier the finished step's x slot is refilled
+      // with step g + b + D - 1, and part of stage (g + b) / P + 2 is copied
       step_barrier();
-      fetch(g + b + D - 1, (b + D - 1) % D);
-      if (g + b < G) compute(b);
+      copy_x(g + b + D - 1, (b + D - 1) % D);
+      copy_code_part(g + b, b);
+      if (g + b < G) compute(b % D, (b / P) % kCodeSlots, b % P);
     }
   }
   asm volatile("" ::: "memory");
@@ -377,6 +462,21 @@ __global__ __launch_bounds__(C::kThreads) void gemm_tile_kernel(GemmDesc d) {
   }
 }
 
+template <class Fmt, class C>
+__global__ __launch_bounds__(C::kThreads) void gemm_tile_kernel(GemmDesc d) {
+  gemm_tile<Fmt, C>(d, blockIdx.x, blockIdx.y);
+}
+
+// Grouped: one workgroup per plan tile {problem, row tile, token tile}.
+template <class Fmt, class C>
+__global__ __launch_bounds__(C::kThreads) void gemm_tile_grouped_kernel(const char* plan) {
+  const PlanHeader* h = reinterpret_cast<const PlanHeader*>(plan);
+  const GemmDesc* descs = reinterpret_cast<const GemmDesc*>(plan + sizeof(PlanHeader));
+  const GemmTile tl = reinterpret_cast<const GemmTile*>(descs + h->count)[blockIdx.x];
+  const GemmDesc d = descs[tl.prob];
+  gemm_tile<Fmt, C>(d, tl.tile_n, tl.tile_m);
+}
+
 // The 256 x 256 tiles when they still give every CU a workgroup, else the
 // 128 x 128 tiles.
 template <class Fmt>
@@ -418,6 +518,37 @@ hipError_t launch_small(const GemmDesc& d, hipStream_t stream) {
 
 // Tokens per launch above which the tiled kernel is used.
 constexpr int kTiledMinM = 64;
+
+hipError_t launch_gemm_grouped(const PlanHeader* h, const void* dev, hipStream_t stream) {
+  if (h->n_tiles == 0) return hipSuccess;
+  const char* plan = static_cast<const char*>(dev);
+  const int64_t tiling = h->reserved[0];
+  const dim3 grid(h->n_tiles);
+  const bool t2 = h->format == kFmtTern2;
+  if (tiling == kGemmTilingLarge) {
+    if (t2)
+      hipLaunchKernelGGL((gemm_tile_grouped_kernel<Tern2, TileLarge>), grid, dim3(TileLarge::kThreads), 0, stream,
+                         plan);
+    else
+      hipLaunchKernelGGL((gemm_tile_grouped_kernel<Sherry3of4, TileLarge>), grid, dim3(TileLarge::kThreads), 0,
+                         stream, plan);
+  } else if (tiling == kGemmTilingSkinny) {
+    if (t2)
+      hipLaunchKernelGGL((gemm_tile_grouped_kernel<Tern2, TileSkinny>), grid, dim3(TileSkinny::kThreads), 0, stream,
+                         plan);
+    else
+      hipLaunchKernelGGL((gemm_tile_grouped_kernel<Sherry3of4, TileSkinny>), grid, dim3(TileSkinny::kThreads), 0,
+                         stream, plan);
+  } else {
+    if (t2)
+      hipLaunchKernelGGL((gemm_tile_grouped_kernel<Tern2, TileSmall>), grid, dim3(TileSmall::kThreads), 0, stream,
+                         plan);
+    else
+      hipLaunchKernelGGL((gemm_tile_grouped_kernel<Sherry3of4, TileSmall>), grid, dim3(TileSmall::kThreads), 0,
+                         stream, plan);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(const GemmDesc& d, int32_t format, hipStream_t stream) {
   if (d.m >= kTiledMinM)

@@ -85,7 +85,7 @@ struct PlanTile {
   int32_t row0;
 };
 
-// GEMM (M tokens) problem.
+// GEMM (M tokens) problem; the grouped plan stores these verbatim.
 struct GemmDesc {
   const uint32_t* codes;
   const void* w_scales;
@@ -100,12 +100,36 @@ struct GemmDesc {
   int32_t m;
   int32_t flags;
 };
+static_assert(sizeof(GemmDesc) == 80, "grouped GEMM plan record layout");
+
+// Grouped GEMM plan: PlanHeader (magic kGemmPlanMagic; reserved[0] = the
+// tiling, kGemmTiling*) | GemmDesc[count] | GemmTile[n_tiles].
+constexpr uint32_t kGemmPlanMagic = 0x53484750u;  // "PGHS"
+struct GemmTile {
+  int32_t prob;
+  int32_t tile_n;  // row tile index
+  int32_t tile_m;  // token tile index
+  int32_t pad;
+};
+static_assert(sizeof(GemmTile) == 16, "grouped GEMM tile record layout");
+// Rows x tokens of the tilings of the tiled kernel: 128 x 128, 256 x 256,
+// and 256 x 16 for plans whose problems all have m <= 16.
+constexpr int64_t kGemmTilingSmall = 0, kGemmTilingLarge = 1, kGemmTilingSkinny = 2;
+constexpr int kGemmLargeRows = 256, kGemmLargeTok = 192;
+constexpr int kGemmSmallRows = 128, kGemmSmallTok = 128;
+constexpr int kGemmSkinnyRows = 256, kGemmSkinnyTok = 16;
+// Large tiles are used when they give at least this many workgroups.
+#ifndef SHERRY_LARGE_TILE_MIN_GROUPS
+#define SHERRY_LARGE_TILE_MIN_GROUPS 256
+#endif
+constexpr int64_t kLargeTileMinGroups = SHERRY_LARGE_TILE_MIN_GROUPS;
 
 hipError_t launch_pack(const void* w, int w_dt, int64_t n, int64_t k, int64_t ldw, uint32_t* codes,
                        void* scales, bool s_f16, hipStream_t stream);
 hipError_t launch_gemv(const GemvDesc& d, bool bf16_x, int32_t format, hipStream_t stream);
 hipError_t launch_gemv_grouped(const PlanHeader* host, const void* dev, hipStream_t stream);
 hipError_t launch_gemm(const GemmDesc& d, int32_t format, hipStream_t stream);
+hipError_t launch_gemm_grouped(const PlanHeader* host, const void* dev, hipStream_t stream);
 hipError_t launch_decode(const uint32_t* codes, int64_t n, int64_t k, int8_t* t, int64_t ldt, hipStream_t stream);
 hipError_t launch_tern2_encode(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint32_t* codes,
                                hipStream_t stream);

@@ -24,7 +24,8 @@ STATUS = {0: "SHERRY_OK", 1: "SHERRY_EINVAL", 2: "SHERRY_ESHAPE", 3: "SHERRY_EDT
 EXPORTS = [
     "sherry_version", "sherry_status_str", "sherry_packed_bytes", "sherry_pack", "sherry_decode", "sherry_gemv",
     "sherry_gemv_plan_bytes", "sherry_gemv_plan", "sherry_gemv_grouped", "sherry_gemm",
-    "tern2_packed_bytes", "tern2_encode", "tern2_gemv", "tern2_gemv_plan", "tern2_gemm",
+    "sherry_gemm_plan_bytes", "sherry_gemm_plan", "sherry_gemm_grouped",
+    "tern2_packed_bytes", "tern2_encode", "tern2_gemv", "tern2_gemv_plan", "tern2_gemm", "tern2_gemm_plan",
 ]
 
 
@@ -38,6 +39,13 @@ class GemvProblem(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("w_scales", ctypes.c_void_p), ("n", ctypes.c_int64),
                 ("k", ctypes.c_int64), ("x", ctypes.c_void_p), ("x_scale", ctypes.c_void_p),
                 ("acc", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
+class GemmProblem(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("w_scales", ctypes.c_void_p), ("n", ctypes.c_int64),
+                ("k", ctypes.c_int64), ("x", ctypes.c_void_p), ("m", ctypes.c_int64), ("ldx", ctypes.c_int64),
+                ("x_scales", ctypes.c_void_p), ("acc", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("ldy", ctypes.c_int64)]
 
 
 _lib = None
@@ -81,6 +89,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         f.argtypes = gemm_args
     lib.tern2_encode.restype = i
     lib.tern2_encode.argtypes = [vp, i64, i64, i64, vp, vp]
+    lib.sherry_gemm_plan_bytes.restype = sz
+    lib.sherry_gemm_plan_bytes.argtypes = [ctypes.POINTER(GemmProblem), i32]
+    for f in (lib.sherry_gemm_plan, lib.tern2_gemm_plan):
+        f.restype = i
+        f.argtypes = [ctypes.POINTER(GemmProblem), i32, i, i, i, vp, sz]
+    lib.sherry_gemm_grouped.restype = i
+    lib.sherry_gemm_grouped.argtypes = [vp, vp, vp]
     _lib = lib
     return lib
 
@@ -242,3 +257,44 @@ class GroupedGemv:
 
     def __call__(self):
         _check("sherry_gemv_grouped", load().sherry_gemv_grouped(self.host.data_ptr(), self.dev.data_ptr(), _stream()))
+
+
+class GroupedGemm:
+    """Many products for M tokens in one launch.  `problems` is a list of dicts
+    with keys codes, scales, x ([m, k] int8, unit column stride), x_scales (or
+    None), acc (or None, [m, n] int32 contiguous), y (or None, [m, n] with unit
+    column stride); all share the scale / y dtypes.  The plan is built once on
+    the host and copied to the device; call() launches it on the current
+    stream."""
+
+    def __init__(self, problems, tern2: bool = False):
+        lib = load()
+        arr = (GemmProblem * len(problems))()
+        self._keep = []
+        for i, p in enumerate(problems):
+            x, y, acc = p["x"], p.get("y"), p.get("acc")
+            _dev(p["codes"], p["scales"], x, p.get("x_scales"), acc, y)
+            if x.dim() != 2 or x.stride(1) != 1:
+                raise ValueError("x must be [m, k] with unit column stride")
+            if y is not None and (y.dim() != 2 or y.stride(1) != 1):
+                raise ValueError("y must be [m, n] with unit column stride")
+            m, k = x.shape
+            n = p["scales"].numel()
+            arr[i] = GemmProblem(p["codes"].data_ptr(), p["scales"].data_ptr(), n, k, x.data_ptr(), m, x.stride(0),
+                                 _ptr(p.get("x_scales")), _ptr(acc), _ptr(y), y.stride(0) if y is not None else n)
+            self._keep.append(p)
+        p0 = problems[0]
+        s_dt = _DT[p0["scales"].dtype]
+        y_dt = _DT[p0["y"].dtype] if p0.get("y") is not None else F32
+        nbytes = lib.sherry_gemm_plan_bytes(arr, len(problems))
+        if nbytes == 0:
+            raise ValueError("invalid grouped GEMM problems")
+        self.host = torch.empty(nbytes, dtype=torch.uint8)
+        fn = lib.tern2_gemm_plan if tern2 else lib.sherry_gemm_plan
+        _check("gemm_plan", fn(arr, len(problems), s_dt, I8, y_dt, self.host.data_ptr(), nbytes))
+        self.dev = self.host.to(p0["x"].device, non_blocking=False)
+        self.n_tiles = int.from_bytes(bytes(self.host[12:16].tolist()), "little", signed=True)
+        self.count = len(problems)
+
+    def __call__(self):
+        _check("sherry_gemm_grouped", load().sherry_gemm_grouped(self.host.data_ptr(), self.dev.data_ptr(), _stream()))
