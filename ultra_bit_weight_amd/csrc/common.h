@@ -114,6 +114,42 @@ __device__ __forceinline__ void load_group(uint32_t* w, const uint32_t* row, int
   w[4] = __builtin_nontemporal_load(gmem(row + 4 * G + g));
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+// lgkmcnt 11:8; a field at its maximum means "do not wait").
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+
+// Direct global->LDS copies (global_load_lds_dword{,x4}, saddr form): lane l
+// copies 4 or 16 bytes from base + voff to LDS byte address lds + l * size.
+// Written as asm so that the compiler does not track them: its wait-count
+// pass cannot tell which LDS buffer such a copy writes and would wait for all
+// of them before every LDS read.  The kernel waits for them explicitly.  The
+// instructions write no register (the address VGPR is read at issue); the
+// s_nop covers the M0-write-to-LDS-DMA hazard.
+__device__ __forceinline__ void lds_copy16(const SHERRY_GLOBAL void* base, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(lds), "v"(voff), "s"(base)
+      : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copy4(const SHERRY_GLOBAL void* base, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, %2"
+      :
+      : "s"(lds), "v"(voff), "s"(base)
+      : "memory", "m0");
+}
+template <class T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+  return __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) T*)p)));
+}
+
 __device__ __forceinline__ uint32_t lds_u32(const uint32_t* base, uint32_t byte_off) {
   return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(base) + byte_off);
 }

@@ -90,14 +90,18 @@ struct Sherry3of4 {
   static constexpr bool kTileTail = true;
   __device__ __forceinline__ static int head_word(int G, int g0, int c) { return 4 * min(g0 + c, G - 1); }
   __device__ __forceinline__ static int tail_word(int G, int g0, int j) { return 4 * G + min(g0 + j, G - 1); }
-  // part q of group j of a stage from a row's LDS copy: chunk c of the row
-  // sits at position c ^ swz
-  __device__ __forceinline__ static void stage_words(uint32_t* w, const uint32_t* heads, int swz,
-                                                     const uint32_t* tails, int j, int q) {
-    const uint32_t* c = heads + 4 * (j ^ swz);
-    w[0] = c[q];
-    const uint32_t nxt = c[min(q + 1, 3)];
-    w[1] = q < 3 ? nxt : tails[j];
+  // Part q of group j of a stage from the LDS copy.  heads / tails point at
+  // the first row of the lane's row tile; lh / lt are the lane's byte
+  // offsets from there (its row), and chunk c of a row sits at position
+  // c ^ swz.  The next head word, or for part 3 the group's tail word,
+  // completes the part.
+  __device__ __forceinline__ static void stage_words(uint32_t* w, const char* heads, const char* tails,
+                                                     uint32_t lh, uint32_t lt, int swz, int j, int q) {
+    const char* c = heads + lh + 16 * (j ^ swz);
+    w[0] = *reinterpret_cast<const uint32_t*>(c + 4 * q);
+    const uint32_t nxt = *reinterpret_cast<const uint32_t*>(c + 4 * min(q + 1, 3));
+    const uint32_t tail = *reinterpret_cast<const uint32_t*>(tails + lt + 4 * j);
+    w[1] = q < 3 ? nxt : tail;
   }
 };
 
@@ -144,9 +148,10 @@ struct Tern2 {
     return 8 * min(g0 + (c >> 1), G - 1) + 4 * (c & 1);
   }
   __device__ __forceinline__ static int tail_word(int, int, int) { return 0; }
-  __device__ __forceinline__ static void stage_words(uint32_t* w, const uint32_t* heads, int swz, const uint32_t*,
-                                                     int j, int q) {
-    const uint32_t* c = heads + 4 * ((2 * j + (q >> 1)) ^ swz) + 2 * (q & 1);
+  __device__ __forceinline__ static void stage_words(uint32_t* w, const char* heads, const char*, uint32_t lh,
+                                                     uint32_t, int swz, int j, int q) {
+    const uint32_t* c =
+        reinterpret_cast<const uint32_t*>(heads + lh + 16 * ((2 * j + (q >> 1)) ^ swz) + 8 * (q & 1));
     w[0] = c[0];
     w[1] = c[1];
   }

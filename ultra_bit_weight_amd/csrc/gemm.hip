@@ -27,11 +27,6 @@ constexpr int kMaxKRanges = 16;  // waves per workgroup (k <= 8192 stays x-stati
 constexpr int kTileDepth = SHERRY_TILE_DEPTH;
 static_assert(kTileDepth >= 2 && kTileDepth <= 4, "tile pipeline depth");
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
-// lgkmcnt 11:8; a field at its maximum means "do not wait").
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
-
 template <class Fmt, bool kStationary>
 __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmDesc d, int n_tiles) {
   constexpr int NW = Fmt::kWords;
@@ -154,37 +149,6 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmDesc d, int n_tile
 //     too.  After the barrier the whole step is in LDS, and the buffers of
 //     the finished step (and, at a stage start, stage) are free for the
 //     copies issued next.
-// Direct global->LDS copies (global_load_lds_dword{,x4}, saddr form): lane l
-// copies 4 or 16 bytes from base + voff to LDS byte address lds + l * size.
-// Written as asm so that the compiler does not track them: its wait-count
-// pass cannot tell which LDS buffer such a copy writes and would wait for all
-// of them before every LDS read.  The kernel waits for them explicitly.  The
-// instructions write no register (the address VGPR is read at issue); the
-// s_nop covers the M0-write-to-LDS-DMA hazard.
-__device__ __forceinline__ void lds_copy16(const SHERRY_GLOBAL void* base, uint32_t voff, uint32_t lds) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2"
-      :
-      : "s"(lds), "v"(voff), "s"(base)
-      : "memory", "m0");
-}
-__device__ __forceinline__ void lds_copy4(const SHERRY_GLOBAL void* base, uint32_t voff, uint32_t lds) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dword %1, %2"
-      :
-      : "s"(lds), "v"(voff), "s"(base)
-      : "memory", "m0");
-}
-template <class T>
-__device__ __forceinline__ uint32_t lds_addr(const T* p) {
-  return __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) T*)p)));
-}
-
 template <int WR_, int WC_, int UT_>
 struct TileCfg {
   static constexpr int WR = WR_, WC = WC_, UT = UT_;
@@ -333,16 +297,23 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int til
     for (int u = 0; u < UT; ++u) acc[t][u] = v4i{0, 0, 0, 0};
 
   // step with x in x slot xs, codes in code slot cs, group j of its stage
+  // The lane's code byte offsets pass through opaque() in every step, so the
+  // addresses are rebuilt from them there (the slot and row-tile parts are
+  // constants the LDS reads take as offsets); otherwise the compiler keeps an
+  // address register for every slot, row tile and group of the unrolled loop.
+  const uint32_t lane_h = static_cast<uint32_t>(16 * HC * (64 * wn + i));
+  const uint32_t lane_t = static_cast<uint32_t>(4 * P * (64 * wn + i));
+  const int swz = (i >> 2) & 3;  // = (row >> 2) & 3 for the lane's rows
   auto compute = [&](int xs, int cs, int j) {
     const u32x4_t* xb = xbuf(xs);
-    const uint32_t* hb = reinterpret_cast<const uint32_t*>(hbuf(cs));
-    const uint32_t* tb = tbuf(cs);
+    const char* hb = reinterpret_cast<const char*>(hbuf(cs));
+    const char* tb = reinterpret_cast<const char*>(tbuf(cs));
+    const uint32_t lh = opaque(lane_h);
+    const uint32_t lt = opaque(lane_t);
     uint32_t w[4][2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int r = 64 * wn + 16 * t + i;
-      Fmt::stage_words(w[t], hb + 4 * HC * r, (r >> 2) & 3, tb + P * r, j, q);
-    }
+    for (int t = 0; t < 4; ++t)
+      Fmt::stage_words(w[t], hb + 16 * HC * 16 * t, tb + 4 * P * 16 * t, lh, lt, swz, j, q);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       v4i a[4];
