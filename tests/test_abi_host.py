@@ -241,15 +241,26 @@ def test_grouped_gemm_plan_on_host(lib):
     arr2[1].k = 128
     arr2[1].m = 0
     assert lib.sherry_gemm_plan(arr2, 2, F16, I8, F16, base, nb2) == EINVAL
-    # every problem with m <= 16: the 256 x 16 tiling
-    few = [(2048, 2048, 16), (300, 1024, 3)]
+    # every problem with m <= 16 and k <= 8192: the few-token kernel, row
+    # tiles of min(512, 2048 / slices) rows (slices = k / 512 rounded up to a
+    # power of two): 512 rows at k = 2048 and 1024, 128 at 8192
+    few = [(2048, 2048, 16), (300, 1024, 3), (300, 8192, 1)]
     arr3 = problems(few)
-    n3 = 8 + 2
-    nb3 = lib.sherry_gemm_plan_bytes(arr3, 2)
-    assert nb3 == 64 + 80 * 2 + 16 * n3
-    assert lib.sherry_gemm_plan(arr3, 2, F16, I8, F16, base, nb3) == OK
+    n3 = 4 + 1 + 3
+    nb3 = lib.sherry_gemm_plan_bytes(arr3, 3)
+    assert nb3 == 64 + 80 * 3 + 16 * n3
+    assert lib.sherry_gemm_plan(arr3, 3, F16, I8, F16, base, nb3) == OK
+    assert int.from_bytes(ctypes.string_at(base + 40, 8), "little") == 3
+    assert tiles_of(base, 3, n3) == [(2, a, 0) for a in range(3)] + [(0, a, 0) for a in range(4)] + [(1, 0, 0)]
+    # m <= 16 with a k above 8192: the 256 x 16 tiling
+    skinny = [(2048, 2048, 16), (300, 9216, 3)]
+    arr4 = problems(skinny)
+    n4 = 8 + 2
+    nb4 = lib.sherry_gemm_plan_bytes(arr4, 2)
+    assert nb4 == 64 + 80 * 2 + 16 * n4
+    assert lib.sherry_gemm_plan(arr4, 2, F16, I8, F16, base, nb4) == OK
     assert int.from_bytes(ctypes.string_at(base + 40, 8), "little") == 2
-    assert tiles_of(base, 2, n3) == [(0, a, 0) for a in range(8)] + [(1, 0, 0), (1, 1, 0)]
+    assert tiles_of(base, 2, n4) == [(1, 0, 0), (1, 1, 0)] + [(0, a, 0) for a in range(8)]
     # a malformed or foreign host plan is rejected before any device call
     bad = ctypes.create_string_buffer(64)
     assert lib.sherry_gemm_grouped(ctypes.addressof(bad), A, None) == EINVAL

@@ -322,13 +322,8 @@ def test_grouped_gemm_small_tiling(gpu_lib, tern2):
         assert np.array_equal(p["y"].cpu().numpy().view(np.uint16), ry.view(np.uint16))
 
 
-@pytest.mark.parametrize("tern2", [False, True])
-def test_grouped_gemm_few_tokens(gpu_lib, tern2):
-    """Problems with m <= 16 in one launch (256 x 16 tiles): ragged rows,
-    every m from 1 to 16 somewhere, k from 128 to 8192."""
-    say(f"grouped gemm few tokens tern2={tern2}")
-    g = synth.rng(717 + tern2)
-    shapes = [(300, 1024, 1), (64, 128, 16), (513, 2048, 7), (17, 8192, 3), (1000, 640, 12), (2048, 3072, 16)]
+def run_grouped_gemm(gpu_lib, tern2, shapes, seed, n_tiles):
+    g = synth.rng(seed)
     probs, refs = [], []
     for n, k, m in shapes:
         sw = synth.row_scales(n, g, np.float16)
@@ -343,12 +338,56 @@ def test_grouped_gemm_few_tokens(gpu_lib, tern2):
                           acc=torch.empty(m, n, dtype=torch.int32, device=DEV),
                           y=torch.empty(m, n, dtype=torch.float16, device=DEV)))
     grouped = gpu_lib.GroupedGemm(probs, tern2=tern2)
-    assert grouped.n_tiles == 2 + 1 + 3 + 1 + 4 + 8
+    assert grouped.n_tiles == n_tiles
     grouped()
     torch.cuda.synchronize()
     for p, (ra, ry) in zip(probs, refs):
         assert np.array_equal(p["acc"].cpu().numpy(), ra)
         assert np.array_equal(p["y"].cpu().numpy().view(np.uint16), ry.view(np.uint16))
+
+
+@pytest.mark.parametrize("tern2", [False, True])
+def test_grouped_gemm_few_tokens(gpu_lib, tern2):
+    """Problems with m <= 16 and k <= 8192 in one launch (few-token kernel):
+    ragged rows, m from 1 to 16, and every k-slice class (k / 512 rounded up
+    to 1, 2, 4, 8, 16).  Row tiles: min(512, 2048 / slices) rows."""
+    say(f"grouped gemm few tokens tern2={tern2}")
+    shapes = [(300, 1024, 1), (64, 128, 16), (513, 2048, 7), (17, 8192, 3), (1000, 640, 12), (2048, 3072, 16)]
+    run_grouped_gemm(gpu_lib, tern2, shapes, 717 + tern2, 1 + 1 + 2 + 1 + 2 + 8)
+
+
+@pytest.mark.parametrize("tern2", [False, True])
+def test_grouped_gemm_few_tokens_long_rows(gpu_lib, tern2):
+    """m <= 16 with a k above 8192: the 256 x 16 tiles of the tiled kernel."""
+    say(f"grouped gemm few tokens, k > 8192, tern2={tern2}")
+    shapes = [(300, 9216, 5), (40, 256, 16)]
+    run_grouped_gemm(gpu_lib, tern2, shapes, 718 + tern2, 2 + 1)
+
+
+@pytest.mark.parametrize("m", [16, 2])
+def test_grouped_gemm_few_tokens_layer(gpu_lib, m):
+    """The seven LLaMA-3.2-1B matrices at m tokens in one launch (the
+    benchmark's small-batch launch), every output checked."""
+    say(f"grouped gemm few tokens 1B layer m={m}")
+    g = synth.rng(919 + m)
+    xs = {}
+    probs, refs = [], []
+    for name, n, k in synth.LLAMA32_1B_LAYER:
+        if k not in xs:
+            xq, sx, _ = synth.act_absmax_int8(m, k, g)
+            xs[k] = (xq, sx, dev(xq), dev(sx))
+        sw = synth.row_scales(n, g, np.float16)
+        words = synth.random_words(n * (k // 128) * 5, g)
+        refs.append(sherry_ref.gemm_i8(words, sw, n, k, xs[k][0], xs[k][1], np.float16))
+        probs.append(dict(codes=words_dev(words), scales=dev(sw), x=xs[k][2], x_scales=xs[k][3],
+                          acc=torch.empty(m, n, dtype=torch.int32, device=DEV),
+                          y=torch.empty(m, n, dtype=torch.float16, device=DEV)))
+    grouped = gpu_lib.GroupedGemm(probs)
+    grouped()
+    torch.cuda.synchronize()
+    for p, (ra, ry), (name, _, _) in zip(probs, refs, synth.LLAMA32_1B_LAYER):
+        assert np.array_equal(p["acc"].cpu().numpy(), ra), name
+        assert np.array_equal(p["y"].cpu().numpy().view(np.uint16), ry.view(np.uint16)), name
 
 
 @pytest.mark.parametrize("tern2", [False, True])

@@ -156,30 +156,38 @@ sherry_status gemm_impl(int32_t format, const uint32_t* codes, const void* w_sca
 }
 
 // Grouped GEMM plan: header | GemmDesc[count] | GemmTile[n_tiles].  Tiling:
-// 256 x 16 when every problem has m <= 16; else 256 x 256 when that gives at
-// least kLargeTileMinGroups tiles; else 128 x 128.
-int64_t gemm_tiles(const sherry_gemm_problem* probs, int32_t count, int rows, int tok) {
+// the few-token kernel when every problem has m <= 16 and k <= 8192 (row
+// tiles of few_tile_rows(k / 128) rows, all tokens); else 256 x 16 when every
+// problem has m <= 16; else 256 x 192 when that gives at least
+// kLargeTileMinGroups tiles; else 128 x 128.
+struct GemmTiling {
+  int64_t kind;
+  int rows, tok;
+  int64_t rows_of(const sherry_gemm_problem& p) const {
+    return kind == kGemmTilingFew ? few_tile_rows(static_cast<int>(p.k / kGroupWeights)) : rows;
+  }
+};
+
+int64_t gemm_tiles(const sherry_gemm_problem* probs, int32_t count, const GemmTiling& t) {
   int64_t tiles = 0;
-  for (int32_t i = 0; i < count; ++i) tiles += ((probs[i].n + rows - 1) / rows) * ((probs[i].m + tok - 1) / tok);
+  for (int32_t i = 0; i < count; ++i) {
+    const int64_t rows = t.rows_of(probs[i]);
+    tiles += ((probs[i].n + rows - 1) / rows) * ((probs[i].m + t.tok - 1) / t.tok);
+  }
   return tiles;
 }
 
-int64_t gemm_tiling(const sherry_gemm_problem* probs, int32_t count, int* rows, int* tok) {
-  bool skinny = true;
-  for (int32_t i = 0; i < count; ++i) skinny = skinny && probs[i].m <= kGemmSkinnyTok;
-  if (skinny) {
-    *rows = kGemmSkinnyRows;
-    *tok = kGemmSkinnyTok;
-    return kGemmTilingSkinny;
+GemmTiling gemm_tiling(const sherry_gemm_problem* probs, int32_t count) {
+  bool few = true, skinny = true;
+  for (int32_t i = 0; i < count; ++i) {
+    skinny = skinny && probs[i].m <= kGemmSkinnyTok;
+    few = few && probs[i].m <= kFewMaxTok && probs[i].k <= kFewMaxGroups * kGroupWeights;
   }
-  if (gemm_tiles(probs, count, kGemmLargeRows, kGemmLargeTok) >= kLargeTileMinGroups) {
-    *rows = kGemmLargeRows;
-    *tok = kGemmLargeTok;
-    return kGemmTilingLarge;
-  }
-  *rows = kGemmSmallRows;
-  *tok = kGemmSmallTok;
-  return kGemmTilingSmall;
+  if (few) return GemmTiling{kGemmTilingFew, 0, kFewMaxTok};
+  if (skinny) return GemmTiling{kGemmTilingSkinny, kGemmSkinnyRows, kGemmSkinnyTok};
+  const GemmTiling large{kGemmTilingLarge, kGemmLargeRows, kGemmLargeTok};
+  if (gemm_tiles(probs, count, large) >= kLargeTileMinGroups) return large;
+  return GemmTiling{kGemmTilingSmall, kGemmSmallRows, kGemmSmallTok};
 }
 
 size_t gemm_plan_bytes_impl(const sherry_gemm_problem* probs, int32_t count) {
@@ -188,9 +196,7 @@ size_t gemm_plan_bytes_impl(const sherry_gemm_problem* probs, int32_t count) {
     if (check_nk(probs[i].n, probs[i].k) != SHERRY_OK) return 0;
     if (probs[i].m <= 0 || probs[i].m > 16 * 65535) return 0;
   }
-  int rows = 0, tok = 0;
-  gemm_tiling(probs, count, &rows, &tok);
-  const int64_t tiles = gemm_tiles(probs, count, rows, tok);
+  const int64_t tiles = gemm_tiles(probs, count, gemm_tiling(probs, count));
   if (tiles > kMaxDim) return 0;
   return sizeof(PlanHeader) + sizeof(GemmDesc) * static_cast<size_t>(count) + sizeof(GemmTile) * tiles;
 }
@@ -209,21 +215,20 @@ sherry_status gemm_plan_impl(int32_t format, const sherry_gemm_problem* probs, i
   if (need == 0) return SHERRY_ESHAPE;
   if (plan_bytes < need) return SHERRY_EINVAL;
   if (!aligned(plan, 8)) return SHERRY_EALIGN;
-  int rows = 0, tok = 0;
-  const int64_t tiling = gemm_tiling(probs, count, &rows, &tok);
+  const GemmTiling tiling = gemm_tiling(probs, count);
   char* out = static_cast<char*>(plan);
   PlanHeader h;
   std::memset(&h, 0, sizeof(h));
   h.magic = kGemmPlanMagic;
   h.version = kPlanVersion;
   h.count = count;
-  h.n_tiles = static_cast<int32_t>(gemm_tiles(probs, count, rows, tok));
+  h.n_tiles = static_cast<int32_t>(gemm_tiles(probs, count, tiling));
   h.s_dt = s_dt;
   h.x_dt = x_dt;
   h.y_dt = y_dt;
   h.format = format;
   h.bytes = need;
-  h.reserved[0] = static_cast<uint64_t>(tiling);
+  h.reserved[0] = static_cast<uint64_t>(tiling.kind);
   std::memcpy(out, &h, sizeof(h));
   std::memcpy(out + sizeof(PlanHeader), descs.data(), sizeof(GemmDesc) * descs.size());
   GemmTile* tiles = reinterpret_cast<GemmTile*>(out + sizeof(PlanHeader) + sizeof(GemmDesc) * descs.size());
@@ -233,7 +238,8 @@ sherry_status gemm_plan_impl(int32_t format, const sherry_gemm_problem* probs, i
   std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return probs[a].k > probs[b].k; });
   int64_t t = 0;
   for (const int32_t i : order) {
-    const int64_t tn = (probs[i].n + rows - 1) / rows, tm = (probs[i].m + tok - 1) / tok;
+    const int64_t rows = tiling.rows_of(probs[i]);
+    const int64_t tn = (probs[i].n + rows - 1) / rows, tm = (probs[i].m + tiling.tok - 1) / tiling.tok;
     for (int64_t a = 0; a < tn; ++a)
       for (int64_t b = 0; b < tm; ++b)
         tiles[t++] = GemmTile{i, static_cast<int32_t>(a), static_cast<int32_t>(b), 0};

@@ -27,6 +27,7 @@ namespace sherry {
 
 struct Sherry3of4 {
   static constexpr int kWords = kGroupWords;
+  static constexpr bool kTableDecode = true;  // decoding reads LDS
   static constexpr int kPairEntries = 1024;  // GEMV table: two codes per entry
   __device__ static void init_table(uint32_t* tab, int t) {
     if (t < 32) tab[t] = decode_i8x4(static_cast<uint32_t>(t));
@@ -53,6 +54,16 @@ struct Sherry3of4 {
   }
   __device__ __forceinline__ static void load(uint32_t* w, const uint32_t* row, int G, int g) {
     load_group(w, row, G, g);
+  }
+  // Same words with ordinary (cached) loads, for kernels whose waves share
+  // the cache lines of a row.
+  __device__ __forceinline__ static void load_cached(uint32_t* w, const uint32_t* row, int G, int g) {
+    const u32x4_t h = *gmem(reinterpret_cast<const u32x4_t*>(row + 4 * g));
+    w[0] = h.x;
+    w[1] = h.y;
+    w[2] = h.z;
+    w[3] = h.w;
+    w[4] = *gmem(row + 4 * G + g);
   }
   __device__ __forceinline__ static uint32_t i8x4(const uint32_t* w, int j, const uint32_t* tab) {
     return lds_u32(tab, code_offset<2>(w, j));
@@ -107,6 +118,7 @@ struct Sherry3of4 {
 
 struct Tern2 {
   static constexpr int kWords = 8;  // 128 weights * 2 bits
+  static constexpr bool kTableDecode = false;
   static constexpr int kPairEntries = 1;
   __device__ static void init_table(uint32_t*, int) {}
   __device__ static void init_pair_table(uint2*, const uint32_t*, int, int) {}
@@ -114,6 +126,19 @@ struct Tern2 {
     const u32x4_t* p = reinterpret_cast<const u32x4_t*>(row + 8 * g);
     const u32x4_t a = __builtin_nontemporal_load(gmem(p));
     const u32x4_t b = __builtin_nontemporal_load(gmem(p + 1));
+    w[0] = a.x;
+    w[1] = a.y;
+    w[2] = a.z;
+    w[3] = a.w;
+    w[4] = b.x;
+    w[5] = b.y;
+    w[6] = b.z;
+    w[7] = b.w;
+  }
+  __device__ __forceinline__ static void load_cached(uint32_t* w, const uint32_t* row, int, int g) {
+    const u32x4_t* p = reinterpret_cast<const u32x4_t*>(row + 8 * g);
+    const u32x4_t a = *gmem(p);
+    const u32x4_t b = *gmem(p + 1);
     w[0] = a.x;
     w[1] = a.y;
     w[2] = a.z;

@@ -448,6 +448,208 @@ __global__ __launch_bounds__(C::kThreads) void gemm_tile_grouped_kernel(const ch
   gemm_tile<Fmt, C>(d, tl.tile_n, tl.tile_m);
 }
 
+// ------------------------------------------------------- few tokens ---
+// m <= 16 (decode with a handful of sequences): HBM-bound, so the codes
+// stream once through registers, GEMV-like, and only the products use the
+// matrix cores.  v_mfma_i32_16x16x64_i8 contracts over the four quarter-
+// waves and 16 bytes per lane, so lane (q, i) = (lane / 16, lane % 16) takes
+// weight row i and group 4 c + q of a k slice c of 512 weights: one slice of
+// 16 rows is eight instructions with the decoded group as A and the 16
+// tokens' x for the same group as B (token i in lane (q, i)).
+//
+// A workgroup of kFewWaves waves owns a tile of rows with all of k.  The S
+// slices of k (a power of two) are split over KW = min(S, 8) waves (SPW
+// slices each), so each wave keeps its x in registers; the 8 / KW row groups
+// of KW waves walk NBLK blocks of 16 rows each, with a ring of code
+// registers kept D blocks ahead.  Each wave adds its 16 x 16 partial sums of
+// a block into the tile's int32 sums in LDS (exact, so the order of the
+// additions does not matter); one barrier at the end, then the epilogue
+// writes the tile.
+//
+// Sums of block row (4 q + e) and token t sit at LDS word 256 blk +
+// 16 (4 e + q) + t: the four quarter-waves' adds then hit distinct banks.
+#ifndef SHERRY_FEW_RING
+#define SHERRY_FEW_RING 4
+#endif
+constexpr int kFewRing = SHERRY_FEW_RING;  // blocks of codes in flight per wave (5-word groups)
+
+template <class Fmt, int S>
+struct FewShape {
+  static constexpr int KW = S < kFewWaves ? S : kFewWaves;  // waves per row group
+  static constexpr int SPW = S / KW;                         // slices per wave
+  static constexpr int RG = kFewWaves / KW;                  // row groups
+  static constexpr int RT = few_tile_rows(4 * S);
+  static constexpr int NBLK = RT / (16 * RG);                // blocks per row group
+  // ring depth (blocks): kFewRing words-of-a-5-word-group budget
+  static constexpr int DW = kFewRing * 5 / (SPW * Fmt::kWords);
+  static constexpr int D = DW < 2 ? 2 : (DW > NBLK ? NBLK : DW);
+  static_assert(NBLK * 16 * RG == RT, "few-token tile shape");
+};
+
+template <class Fmt, int S>
+__device__ __forceinline__ void gemm_few(const GemmDesc& d, int tile, const uint32_t* tab32, const uint2* pairs,
+                                         int32_t* sums) {
+  using Sh = FewShape<Fmt, S>;
+  constexpr int NW = Fmt::kWords;
+  constexpr int KW = Sh::KW, SPW = Sh::SPW, NBLK = Sh::NBLK, D = Sh::D;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int kw = wave % KW;
+  const int rg = wave / KW;
+  const int i = lane & 15;
+  const int q = lane >> 4;
+  const int G = d.k / kGroupWeights;
+  const int row0 = tile * Sh::RT + rg * (NBLK * 16);
+  const int64_t row_words = static_cast<int64_t>(G) * NW;
+
+  // x of token i for this lane's groups (zero past m and past k)
+  uint32_t xr[SPW][32];
+#pragma unroll
+  for (int sp = 0; sp < SPW; ++sp) {
+    const int g = 4 * (kw + KW * sp) + q;
+    const bool ok = i < d.m && g < G;
+    const SHERRY_GLOBAL u32x4_t* xp = gmem(reinterpret_cast<const u32x4_t*>(
+        d.x + static_cast<int64_t>(ok ? i : 0) * d.ldx + static_cast<int64_t>(ok ? g : 0) * kGroupWeights));
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const u32x4_t v = xp[u];
+      xr[sp][4 * u + 0] = ok ? v.x : 0u;
+      xr[sp][4 * u + 1] = ok ? v.y : 0u;
+      xr[sp][4 * u + 2] = ok ? v.z : 0u;
+      xr[sp][4 * u + 3] = ok ? v.w : 0u;
+    }
+  }
+  // rows past n and groups past k load valid words (clamped) whose products
+  // are never stored or meet zero x
+  auto fetch = [&](uint32_t (&buf)[SPW][NW], int blk) {
+    const int row = min(row0 + 16 * blk + i, d.n - 1);
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp)
+      Fmt::load_cached(buf[sp], d.codes + row * row_words, G, min(4 * (kw + KW * sp) + q, G - 1));
+  };
+  // With table decoding, the lookups of half a group are issued before its
+  // four products, so the products wait on one LDS round trip per half, not
+  // one each (decoding in registers needs no batching).
+  constexpr int HB = Fmt::kTableDecode ? 2 : 8;  // batches per group
+  auto step = [&](const uint32_t (&buf)[SPW][NW], int blk) {
+    v4i c = {0, 0, 0, 0};
+#pragma unroll
+    for (int sp = 0; sp < SPW; ++sp) {
+#pragma unroll
+      for (int hf = 0; hf < HB; ++hf) {
+        uint32_t a[32 / HB];
+#pragma unroll
+        for (int pp = 0; pp < 16 / HB; ++pp) {
+          const int p = (16 / HB) * hf + pp;
+          const uint2 v = ((kPairMask >> p) & 1)
+                              ? Fmt::i8x8(buf[sp], p, pairs)
+                              : make_uint2(Fmt::i8x4(buf[sp], 2 * p, tab32), Fmt::i8x4(buf[sp], 2 * p + 1, tab32));
+          a[2 * pp] = v.x;
+          a[2 * pp + 1] = v.y;
+        }
+#pragma unroll
+        for (int uu = 0; uu < 8 / HB; ++uu) {
+          const int u = (8 / HB) * hf + uu;
+          const v4i av = {static_cast<int>(a[4 * uu]), static_cast<int>(a[4 * uu + 1]),
+                          static_cast<int>(a[4 * uu + 2]), static_cast<int>(a[4 * uu + 3])};
+          const v4i bv = {static_cast<int>(xr[sp][4 * u]), static_cast<int>(xr[sp][4 * u + 1]),
+                          static_cast<int>(xr[sp][4 * u + 2]), static_cast<int>(xr[sp][4 * u + 3])};
+          c = __builtin_amdgcn_mfma_i32_16x16x64_i8(av, bv, c, 0, 0, 0);
+        }
+      }
+    }
+    int32_t* dst = sums + 256 * (rg * NBLK + blk) + 16 * q + i;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) atomicAdd(dst + 64 * e, c[e]);
+  };
+  uint32_t ring[D][SPW][NW];
+#pragma unroll
+  for (int b = 0; b + 1 < D; ++b) fetch(ring[b], b);
+  for (int b0 = 0; b0 < NBLK; b0 += D) {
+#pragma unroll
+    for (int b = 0; b < D; ++b) {
+      fetch(ring[(b + D - 1) % D], min(b0 + b + D - 1, NBLK - 1));
+      if (NBLK % D == 0 || b0 + b < NBLK) step(ring[b], b0 + b);
+    }
+  }
+}
+
+// Zero the tile's sums, build the tables, run the row groups, write the tile.
+// Thread t writes rows t % rt + j * 512 (j < RPT) of the tile for tokens
+// t / rt, t / rt + 512 / rt, ... (all tokens when rt >= 512): its weight
+// scales are loaded before the main loop and the token scales are staged in
+// LDS, so the epilogue waits on no global load.
+template <class Fmt>
+__device__ __forceinline__ void gemm_few_tile(const GemmDesc& d, int tile) {
+  constexpr int kThreads = kFewWaves * kWave;
+  constexpr int RPT = kFewMaxTileRows > kThreads ? kFewMaxTileRows / kThreads : 1;  // rows per thread
+  static_assert(kThreads % kFewMaxTileRows == 0 || kFewMaxTileRows % kThreads == 0, "epilogue mapping");
+  __shared__ uint32_t tab32[32];
+  __shared__ uint2 pairs[kPairMask != 0 ? Fmt::kPairEntries : 1];
+  __shared__ __attribute__((aligned(16))) int32_t sums[kFewMaxTileRows * kFewMaxTok];
+  __shared__ float sxs[kFewMaxTok];
+  const int G = d.k / kGroupWeights;
+  const int rt = few_tile_rows(G);
+  const int tid = static_cast<int>(threadIdx.x);
+  const int r0 = rt >= kThreads ? tid : tid % rt;  // first row; then + kThreads
+  const int m0 = rt >= kThreads ? 0 : tid / rt;
+  const int mstep = rt >= kThreads ? 1 : kThreads / rt;
+  const int nrows = rt >= kThreads ? rt / kThreads : 1;
+  const bool s_f16 = d.flags & kFlagScaleF16;
+  float sw[RPT];
+#pragma unroll
+  for (int j = 0; j < RPT; ++j)
+    sw[j] = d.y && j < nrows ? load_scale(d.w_scales, min(tile * rt + r0 + j * kThreads, d.n - 1), s_f16) : 0.0f;
+  const bool has_sx = d.x_scales != nullptr;
+  if (tid < kFewMaxTok) sxs[tid] = has_sx && tid < d.m ? gmem(d.x_scales)[tid] : 1.0f;
+  for (int t = tid; t < kFewMaxTileRows * kFewMaxTok / 4; t += kThreads)
+    reinterpret_cast<v4i*>(sums)[t] = v4i{0, 0, 0, 0};
+  Fmt::init_table(tab32, threadIdx.x);
+  __syncthreads();
+  if constexpr (kPairMask != 0) {
+    Fmt::init_pair_table(pairs, tab32, threadIdx.x, kThreads);
+    __syncthreads();
+  }
+  switch (few_slices(G)) {
+    case 1: gemm_few<Fmt, 1>(d, tile, tab32, pairs, sums); break;
+    case 2: gemm_few<Fmt, 2>(d, tile, tab32, pairs, sums); break;
+    case 4: gemm_few<Fmt, 4>(d, tile, tab32, pairs, sums); break;
+    case 8: gemm_few<Fmt, 8>(d, tile, tab32, pairs, sums); break;
+    default: gemm_few<Fmt, 16>(d, tile, tab32, pairs, sums); break;
+  }
+  __syncthreads();
+  const bool y_f16 = d.flags & kFlagYF16;
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int r = r0 + j * kThreads;
+    const int n = tile * rt + r;
+    if (j >= nrows || n >= d.n) break;
+    const int32_t* col = sums + 256 * (r >> 4) + 16 * (4 * (r & 3) + ((r >> 2) & 3));
+    for (int m = m0; m < d.m; m += mstep) {
+      const int32_t v = col[m];
+      if (d.acc) gmem(d.acc)[static_cast<int64_t>(m) * d.n + n] = v;
+      if (d.y) store_y(d.y, static_cast<int64_t>(m) * d.ldy + n, epilogue_i32(v, sw[j], sxs[m], has_sx), y_f16);
+    }
+  }
+}
+
+// Two workgroups per CU (four waves per SIMD) is the occupancy aimed at: the
+// compiler may then use up to 128 VGPRs for overlapping the lookups.
+template <class Fmt>
+__global__ __launch_bounds__(kFewWaves * kWave) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemm_few_kernel(
+    GemmDesc d) {
+  gemm_few_tile<Fmt>(d, blockIdx.x);
+}
+
+template <class Fmt>
+__global__ __launch_bounds__(kFewWaves * kWave) __attribute__((amdgpu_waves_per_eu(4, 4))) void
+gemm_few_grouped_kernel(const char* plan) {
+  const PlanHeader* h = reinterpret_cast<const PlanHeader*>(plan);
+  const GemmDesc* descs = reinterpret_cast<const GemmDesc*>(plan + sizeof(PlanHeader));
+  const GemmTile tl = reinterpret_cast<const GemmTile*>(descs + h->count)[blockIdx.x];
+  gemm_few_tile<Fmt>(descs[tl.prob], tl.tile_n);
+}
+
 // The 256 x 256 tiles when they still give every CU a workgroup, else the
 // 128 x 128 tiles.
 template <class Fmt>
@@ -496,7 +698,12 @@ hipError_t launch_gemm_grouped(const PlanHeader* h, const void* dev, hipStream_t
   const int64_t tiling = h->reserved[0];
   const dim3 grid(h->n_tiles);
   const bool t2 = h->format == kFmtTern2;
-  if (tiling == kGemmTilingLarge) {
+  if (tiling == kGemmTilingFew) {
+    if (t2)
+      hipLaunchKernelGGL((gemm_few_grouped_kernel<Tern2>), grid, dim3(kFewWaves * kWave), 0, stream, plan);
+    else
+      hipLaunchKernelGGL((gemm_few_grouped_kernel<Sherry3of4>), grid, dim3(kFewWaves * kWave), 0, stream, plan);
+  } else if (tiling == kGemmTilingLarge) {
     if (t2)
       hipLaunchKernelGGL((gemm_tile_grouped_kernel<Tern2, TileLarge>), grid, dim3(TileLarge::kThreads), 0, stream,
                          plan);
@@ -522,6 +729,16 @@ hipError_t launch_gemm_grouped(const PlanHeader* h, const void* dev, hipStream_t
 }
 
 hipError_t launch_gemm(const GemmDesc& d, int32_t format, hipStream_t stream) {
+  const int G = d.k / kGroupWeights;
+  if (d.m <= kFewMaxTok && G <= kFewMaxGroups) {
+    const int rt = few_tile_rows(G);
+    const dim3 grid((d.n + rt - 1) / rt);
+    if (format == kFmtTern2)
+      hipLaunchKernelGGL((gemm_few_kernel<Tern2>), grid, dim3(kFewWaves * kWave), 0, stream, d);
+    else
+      hipLaunchKernelGGL((gemm_few_kernel<Sherry3of4>), grid, dim3(kFewWaves * kWave), 0, stream, d);
+    return hipGetLastError();
+  }
   if (d.m >= kTiledMinM)
     return format == kFmtTern2 ? launch_tile<Tern2>(d, stream) : launch_tile<Sherry3of4>(d, stream);
   return format == kFmtTern2 ? launch_small<Tern2>(d, stream) : launch_small<Sherry3of4>(d, stream);

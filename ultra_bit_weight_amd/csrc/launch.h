@@ -114,10 +114,29 @@ struct GemmTile {
 static_assert(sizeof(GemmTile) == 16, "grouped GEMM tile record layout");
 // Rows x tokens of the tilings of the tiled kernel: 128 x 128, 256 x 256,
 // and 256 x 16 for plans whose problems all have m <= 16.
-constexpr int64_t kGemmTilingSmall = 0, kGemmTilingLarge = 1, kGemmTilingSkinny = 2;
+constexpr int64_t kGemmTilingSmall = 0, kGemmTilingLarge = 1, kGemmTilingSkinny = 2, kGemmTilingFew = 3;
 constexpr int kGemmLargeRows = 256, kGemmLargeTok = 192;
 constexpr int kGemmSmallRows = 128, kGemmSmallTok = 128;
 constexpr int kGemmSkinnyRows = 256, kGemmSkinnyTok = 16;
+// Few-token kernel (every problem m <= 16, k <= 8192): a row tile of
+// min(R, 4 R / S) rows with all of k (R = kFewMaxTileRows), S = k slices of
+// 512 weights rounded up to a power of two.
+constexpr int kFewMaxTok = 16;
+constexpr int kFewMaxGroups = 64;
+constexpr int kFewWaves = 8;
+inline constexpr int few_slices(int groups) {
+  int s = 1;
+  while (4 * s < groups) s *= 2;
+  return s;
+}
+#ifndef SHERRY_FEW_TILE_ROWS
+#define SHERRY_FEW_TILE_ROWS 512
+#endif
+constexpr int kFewMaxTileRows = SHERRY_FEW_TILE_ROWS;
+inline constexpr int few_tile_rows(int groups) {
+  return 4 * kFewMaxTileRows / few_slices(groups) < kFewMaxTileRows ? 4 * kFewMaxTileRows / few_slices(groups)
+                                                                     : kFewMaxTileRows;
+}
 // Large tiles are used when they give at least this many workgroups.
 #ifndef SHERRY_LARGE_TILE_MIN_GROUPS
 #define SHERRY_LARGE_TILE_MIN_GROUPS 256
