@@ -6,6 +6,7 @@ and this package imports nothing from the GPU library.
 
 Plain, slow, obviously correct: numpy in fp64 (exact integers) with pure-Python
 loops kept to the small reference routines.  See ``sherry_ref`` for the 3:4
-format and ``tern2_ref`` for the 2-bit dense-ternary comparator.
+format, ``tern2_ref`` for the 2-bit dense-ternary comparator and ``act_ref``
+for the per-token int8 activation quantization.
 """
-from . import sherry_ref, tern2_ref  # noqa: F401
+from . import act_ref, sherry_ref, tern2_ref  # noqa: F401

@@ -332,3 +332,95 @@ def pin_bf16_path(ref):
         exact = sum(int(t[r, c]) * xv[c] for c in range(k))
         # one rounding of the exact sum to fp64, one for the scale product
         assert y[r] == float(exact) * float(sw[r]), r
+
+
+# ------------------------------------------- activation quantization ---
+# Pins for oracle.act_ref (per-token absmax int8, readings A1-A3): hand
+# values, exact rational arithmetic, invariants, and the generator's own
+# independent quantizer.
+
+def _rint_half_even(q: Fraction) -> int:
+    fl = q.numerator // q.denominator
+    rem = q - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return fl
+
+
+def pin_act_hand(act):
+    # s = 127 / 127 = 1 exactly; quotients are the values: ties go to even
+    q, s = act.quantize(np.array([[127.0, 63.5, -62.5, 0.5, -1.5, 2.5, -126.5]], np.float32))
+    assert s.tolist() == [1.0]
+    assert q.tolist() == [[127, 64, -62, 0, -2, 2, -126]]
+    # amax 190.5 -> s = 190.5 / 127 = 1.5 exactly; 0.75 / 1.5 = 0.5,
+    # 3.75 / 1.5 = 2.5, -6.75 / 1.5 = -4.5, 2.25 / 1.5 = 1.5 exactly (ties);
+    # a product with fp32(1 / 1.5) would push 0.75 over 0.5
+    q, s = act.quantize(np.array([[190.5, 0.75, 3.75, -6.75, 2.25]], np.float32))
+    assert s.tolist() == [1.5]
+    assert q.tolist() == [[127, 0, 2, -4, 2]]
+    # amax 222.25 -> s = 1.75 exactly; 11.375 / 1.75 = 6.5 exactly, a tie
+    # that goes to 6, while 11.375 * fp32(1 / 1.75) rounds to 6.5000005
+    q, s = act.quantize(np.array([[222.25, 11.375, -11.375, 4.375]], np.float32))
+    assert s.tolist() == [1.75]
+    assert q.tolist() == [[127, 6, -6, 2]]
+
+
+def pin_act_zero_and_signs(act):
+    q, s = act.quantize(np.zeros((2, 64), np.float32))
+    assert s.tolist() == [1.0, 1.0] and not q.any()
+    g = synth.rng(51)
+    x = g.standard_normal((5, 256)).astype(np.float32)
+    q, s = act.quantize(x)
+    qn, sn = act.quantize(-x)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)  # round-half-even is odd-symmetric
+    am = np.argmax(np.abs(x), axis=1)
+    for t in range(5):
+        assert q[t, am[t]] == (127 if x[t, am[t]] > 0 else -127)
+    assert np.abs(q.astype(np.int32)).max() <= 127
+    # power-of-two scaling is exact in fp32: same codes, scale times 2^e
+    for e in (-7, 5):
+        q2, s2 = act.quantize(x * np.float32(2.0 ** e))
+        assert np.array_equal(q2, q) and np.array_equal(s2, s * np.float32(2.0 ** e))
+    # error bound: |q s - x| <= s / 2 up to the quotient's rounding
+    err = np.abs(q.astype(np.float64) * s[:, None].astype(np.float64) - x.astype(np.float64))
+    assert np.all(err <= s[:, None].astype(np.float64) * (0.5 + 2.0 ** -16))
+
+
+def pin_act_exact(act):
+    """Every element against exact rationals: s = RN32(amax / 127), then
+    rint_even(RN32(x / s)) clipped."""
+    g = synth.rng(52)
+    x = (g.standard_normal((4, 96)) * np.array([[1.0], [1e-3], [37.0], [0.25]])).astype(np.float32)
+    x[3, :8] = [0.0, -0.0, 1.0, -1.0, 0.5, 0.25, -0.125, 0.0]
+    q, s = act.quantize(x)
+    for t in range(x.shape[0]):
+        amax = max(abs(Fraction(float(v))) for v in x[t])
+        st = f32_exact(amax / 127)
+        assert Fraction(float(s[t])) == st, t
+        for j in range(x.shape[1]):
+            want = max(-127, min(127, _rint_half_even(f32_exact(Fraction(float(x[t, j])) / st))))
+            assert int(q[t, j]) == want, (t, j)
+
+
+def pin_act_generator(act):
+    """The input generator quantizes by the same rule with its own code."""
+    g = synth.rng(53)
+    xq, sx, x = synth.act_absmax_int8(7, 640, g)
+    q, s = act.quantize(x)
+    assert np.array_equal(q, xq) and np.array_equal(s, sx)
+
+
+def pin_act_dtypes(act):
+    """fp16 and bf16 inputs quantize as their (exact) fp32 values."""
+    g = synth.rng(54)
+    x = g.standard_normal((3, 128)).astype(np.float32)
+    h = x.astype(np.float16)
+    assert all(np.array_equal(a, b) for a, b in zip(act.quantize(h, "f16"), act.quantize(h.astype(np.float32))))
+    bits = synth.f32_to_bf16_bits(x)
+    # bf16 value by the definition sign * (1 + m / 128) * 2^(e - 127)
+    vals = np.array([[(-1.0 if b >> 15 else 1.0) * (1 + (b & 0x7F) / 128.0) * 2.0 ** (((b >> 7) & 0xFF) - 127)
+                      for b in row] for row in bits.tolist()], np.float32)
+    assert all(np.array_equal(a, b) for a, b in zip(act.quantize(bits, "bf16"), act.quantize(vals)))
+
+
+ACT_PINS = [pin_act_hand, pin_act_zero_and_signs, pin_act_exact, pin_act_generator, pin_act_dtypes]

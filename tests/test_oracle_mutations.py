@@ -5,6 +5,7 @@ a plausibly wrong variant (a dropped term, a wrong sign or bit order, a
 transposed operand, a different tie rule), and checks that the pins reject it.
 The real oracle module is never modified."""
 import importlib.util
+import types
 import os
 
 import numpy as np
@@ -165,3 +166,44 @@ def test_planted_mistake_is_caught(mutant):
         except (AssertionError, ValueError, OverflowError):
             caught.append(pin.__name__)
     assert caught, f"{mutant.__name__} passed every pin"
+
+
+# ------------------------------------------- activation quantization ---
+# Planted in the source text of a private copy of oracle/act_ref.py.
+ACT_PATH = os.path.join(os.path.dirname(PATH), "act_ref.py")
+ACT_MUTANTS = {
+    "reciprocal_product": ("quot = (row / st).astype(np.float32)",
+                           "quot = (row * np.float32(np.float32(1) / st)).astype(np.float32)"),
+    "half_away_from_zero": ("np.rint(quot)", "np.trunc(quot + np.copysign(np.float32(0.5), quot))"),
+    "divide_by_128": ("amax / np.float32(127)", "amax / np.float32(128)"),
+    "zero_token_scale_0": ("continue  # s = 1, x_q = 0", "s[t] = 0\n            continue"),
+    "mean_not_max": ("np.max(np.abs(row))", "np.mean(np.abs(row))"),
+}
+
+
+def fresh_act(patch=None):
+    src = open(ACT_PATH).read()
+    if patch:
+        assert patch[0] in src, patch[0]
+        src = src.replace(patch[0], patch[1])
+    mod = types.ModuleType("act_ref_planted")
+    exec(compile(src, ACT_PATH, "exec"), mod.__dict__)
+    return mod
+
+
+def test_act_copy_passes_every_pin():
+    act = fresh_act()
+    for pin in P.ACT_PINS:
+        pin(act)
+
+
+@pytest.mark.parametrize("name", sorted(ACT_MUTANTS))
+def test_act_planted_mistake_is_caught(name):
+    act = fresh_act(ACT_MUTANTS[name])
+    caught = []
+    for pin in P.ACT_PINS:
+        try:
+            pin(act)
+        except (AssertionError, ValueError, OverflowError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, f"{name} passed every pin"

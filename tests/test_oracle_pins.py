@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import sherry_ref, tern2_ref
+from oracle import act_ref, sherry_ref, tern2_ref
 from tests import oracle_pins as P
 
 
@@ -116,3 +116,8 @@ def test_accumulator_bound_at_largest_shape():
     words = sherry_ref.pack_codes(sherry_ref.codes_from_dense(t))
     acc, _ = sherry_ref.gemv_i8(words, np.ones(1, np.float32), 1, k, np.full(k, 127, np.int8), None, np.float32)
     assert int(acc[0]) == 127 * 3 * k // 4
+
+
+@pytest.mark.parametrize("pin", P.ACT_PINS, ids=lambda f: f.__name__)
+def test_act_pin(pin):
+    pin(act_ref)
