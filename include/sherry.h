@@ -104,6 +104,23 @@ sherry_status sherry_pack(const void* w, sherry_dtype w_dt, int64_t n, int64_t k
 sherry_status sherry_decode(const uint32_t* codes, int64_t n, int64_t k, int8_t* t, int64_t ldt,
                             hipStream_t stream);
 
+/* Per-token int8 quantization of activations, the input of the int8
+ * products (x_scale / x_scales arguments).  The Sherry paper quantizes the
+ * weights only; the activations follow the symmetric absmax rule, in fp32:
+ *   scales[t] = max_j |x[t, j]| / 127  (one IEEE division; 1.0 for an
+ *               all-zero token)
+ *   xq[t, j]  = clip(rint(x[t, j] / scales[t]), -127, 127)  (one IEEE
+ *               division per element, then round half to even)
+ *   x      : m x k values of x_dt (F32|F16|BF16), row stride ldx >= k
+ *            elements, aligned to its element size; DEVICE
+ *   xq     : out, m x k int8, row stride ldq >= k bytes; DEVICE
+ *   scales : out, m fp32, 4-byte aligned; DEVICE
+ * Non-finite inputs are a caller error (outputs then unspecified).
+ * Errors: EINVAL null pointer or m, k <= 0; EDTYPE other x_dt; ESHAPE
+ * ld < k or m above 2^31 - 1; EALIGN misaligned x or scales. */
+sherry_status sherry_act_quant(const void* x, sherry_dtype x_dt, int64_t m, int64_t k, int64_t ldx, int8_t* xq,
+                               int64_t ldq, float* scales, hipStream_t stream);
+
 /* Batch-1 product y = diag(s_w) * T * x (the decode-phase GEMV).
  *   codes    : n x k packed codes (layout above), 4-byte aligned
  *   w_scales : n scales of s_dt (F32|F16)

@@ -131,6 +131,25 @@ def test_gemm_validation(lib, fn):
     assert gemm(lib, xs=None, acc=None, fn=fn) == EDEVICE
 
 
+def test_act_quant_validation(lib):
+    f = lib.sherry_act_quant
+    assert f(None, F32, 2, 128, 128, A, 128, A, None) == EINVAL
+    assert f(A, F32, 2, 128, 128, None, 128, A, None) == EINVAL
+    assert f(A, F32, 2, 128, 128, A, 128, None, None) == EINVAL
+    assert f(A, F32, 0, 128, 128, A, 128, A, None) == EINVAL
+    assert f(A, F32, 2, 0, 128, A, 128, A, None) == EINVAL
+    assert f(A, I8, 2, 128, 128, A, 128, A, None) == EDTYPE
+    assert f(A, I32, 2, 128, 128, A, 128, A, None) == EDTYPE
+    assert f(A, F32, 2, 128, 100, A, 128, A, None) == ESHAPE
+    assert f(A, F32, 2, 128, 128, A, 127, A, None) == ESHAPE
+    assert f(A, F32, 2 ** 31, 128, 128, A, 128, A, None) == ESHAPE
+    assert f(A + 2, F32, 2, 128, 128, A, 128, A, None) == EALIGN
+    assert f(A + 1, BF16, 2, 128, 128, A, 128, A, None) == EALIGN
+    assert f(A, F32, 2, 128, 128, A, 128, A + 2, None) == EALIGN
+    assert f(A + 2, F16, 2, 100, 100, A + 1, 100, A, None) == EDEVICE  # valid: odd k, ld, 2-byte x
+    assert f(A, BF16, 1, 8192, 8192, A, 8192, A, None) == EDEVICE
+
+
 def test_decode_validation(lib):
     f = lib.sherry_decode
     assert f(None, 4, 128, A, 128, None) == EINVAL

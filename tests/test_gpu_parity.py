@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import synth
-from oracle import sherry_ref, tern2_ref
+from oracle import act_ref, sherry_ref, tern2_ref
 
 pytestmark = pytest.mark.gpu
 
@@ -570,3 +570,71 @@ def test_full_layer_sampled_rows(gpu_lib, layer):
         else:
             ref = sherry_ref.gemv_bf16(sub, sw[rows], len(rows), k, x)
             check_fp_tolerance(p["y"].cpu().numpy()[rows], ref)
+
+
+# ------------------------------------------- activation quantization ---
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("m,k", [(1, 2048), (5, 8192), (3, 100), (2048, 2048)])
+def test_act_quant(gpu_lib, dt, m, k):
+    """Per-token absmax int8 on the GPU equals the oracle bit for bit (codes
+    and scales); rows include an all-zero token and exact ties."""
+    say(f"act quant {dt} m={m} k={k}")
+    g = synth.rng(61 + m + k)
+    x = g.standard_normal((m, k)).astype(np.float32) * np.float32(g.uniform(0.01, 30.0))
+    if m >= 3:
+        x[1] = 0.0
+        x[2, :5] = [222.25, 11.375, -11.375, 4.375, 0.0]  # s = 1.75, exact ties
+        x[2, 5:] = np.clip(x[2, 5:], -200.0, 200.0)
+    if dt == "f32":
+        host, tx = x, torch.from_numpy(x)
+    elif dt == "f16":
+        host = x.astype(np.float16)
+        tx = torch.from_numpy(host)
+    else:
+        host = synth.f32_to_bf16_bits(x)
+        tx = torch.from_numpy(host.view(np.int16)).view(torch.bfloat16)
+    q, s = gpu_lib.act_quant(tx.to(DEV))
+    torch.cuda.synchronize()
+    rq, rs = act_ref.quantize(host, dt)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), rq)
+
+
+def test_act_quant_strided_rows(gpu_lib):
+    """Rows of a wider buffer (ldx > k) and a 1-D token."""
+    g = synth.rng(66)
+    full = torch.from_numpy(g.standard_normal((4, 3072)).astype(np.float32)).to(DEV)
+    q, s = gpu_lib.act_quant(full[:, :2048])
+    q1, s1 = gpu_lib.act_quant(full[2, 1024:3072])
+    torch.cuda.synchronize()
+    host = full.cpu().numpy()
+    rq, rs = act_ref.quantize(host[:, :2048])
+    assert np.array_equal(q.cpu().numpy(), rq) and np.array_equal(s.cpu().numpy(), rs)
+    rq1, rs1 = act_ref.quantize(host[2:3, 1024:3072])
+    assert np.array_equal(q1.cpu().numpy(), rq1[0]) and np.array_equal(s1.cpu().numpy(), rs1)
+
+
+@pytest.mark.parametrize("m", [1, 16])
+def test_quantized_fused_projections(gpu_lib, m):
+    """bf16 activations -> int8 on the GPU -> one product over the
+    concatenated q | k | v rows (3072 x 2048, shared x) and one over gate | up
+    (16384 x 2048), as a decode step runs them; every output checked against
+    the oracle chain (quantization, then the int8 product)."""
+    say(f"fused qkv / gate-up after activation quant m={m}")
+    g = synth.rng(67 + m)
+    xb = synth.x_bf16_normal((m, 2048), g)
+    xq, sx = gpu_lib.act_quant(torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(DEV))
+    rq, rs = act_ref.quantize(xb, "bf16")
+    for n in (2048 + 512 + 512, 8192 + 8192):
+        words = synth.random_words(n * 16 * 5, g)
+        sw = synth.row_scales(n, g, np.float16)
+        if m == 1:
+            acc, y = gpu_lib.gemv(words_dev(words), dev(sw), xq[0], sx, torch.float16, want_acc=True)
+            ra, ry = sherry_ref.gemv_i8(words, sw, n, 2048, rq[0], rs[0], np.float16)
+        else:
+            acc, y = gpu_lib.gemm(words_dev(words), dev(sw), xq, sx, torch.float16, want_acc=True)
+            ra, ry = sherry_ref.gemm_i8(words, sw, n, 2048, rq, rs, np.float16)
+        torch.cuda.synchronize()
+        assert np.array_equal(acc.cpu().numpy(), ra)
+        assert np.array_equal(y.cpu().numpy().view(np.uint16), ry.view(np.uint16))

@@ -355,6 +355,25 @@ sherry_status sherry_pack(const void* w, sherry_dtype w_dt, int64_t n, int64_t k
   return launched(launch_pack(w, w_dt, n, k, ldw, codes, scales, s_dt == SHERRY_F16, stream));
 }
 
+sherry_status sherry_act_quant(const void* x, sherry_dtype x_dt, int64_t m, int64_t k, int64_t ldx, int8_t* xq,
+                               int64_t ldq, float* scales, hipStream_t stream) {
+  if (!x || !xq || !scales) return SHERRY_EINVAL;
+  if (m <= 0 || k <= 0) return SHERRY_EINVAL;
+  int dt = 0;
+  switch (x_dt) {
+    case SHERRY_F32: dt = kActF32; break;
+    case SHERRY_F16: dt = kActF16; break;
+    case SHERRY_BF16: dt = kActBf16; break;
+    default: return SHERRY_EDTYPE;
+  }
+  if (m > kMaxDim || ldx < k || ldq < k) return SHERRY_ESHAPE;
+  if (ldx > std::numeric_limits<int64_t>::max() / m || ldq > std::numeric_limits<int64_t>::max() / m)
+    return SHERRY_ESHAPE;
+  if (!aligned(x, dt_size(x_dt)) || !aligned(scales, 4)) return SHERRY_EALIGN;
+  if (sherry_status s = check_device()) return s;
+  return launched(launch_act_quant(x, dt, m, k, ldx, xq, ldq, scales, stream));
+}
+
 sherry_status sherry_decode(const uint32_t* codes, int64_t n, int64_t k, int8_t* t, int64_t ldt,
                             hipStream_t stream) {
   if (!codes || !t) return SHERRY_EINVAL;

@@ -149,6 +149,10 @@ hipError_t launch_gemv(const GemvDesc& d, bool bf16_x, int32_t format, hipStream
 hipError_t launch_gemv_grouped(const PlanHeader* host, const void* dev, hipStream_t stream);
 hipError_t launch_gemm(const GemmDesc& d, int32_t format, hipStream_t stream);
 hipError_t launch_gemm_grouped(const PlanHeader* host, const void* dev, hipStream_t stream);
+// Activation quantization: input element types.
+constexpr int kActF32 = 0, kActF16 = 1, kActBf16 = 2;
+hipError_t launch_act_quant(const void* x, int dt, int64_t m, int64_t k, int64_t ldx, int8_t* q, int64_t ldq,
+                            float* scales, hipStream_t stream);
 hipError_t launch_decode(const uint32_t* codes, int64_t n, int64_t k, int8_t* t, int64_t ldt, hipStream_t stream);
 hipError_t launch_tern2_encode(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint32_t* codes,
                                hipStream_t stream);

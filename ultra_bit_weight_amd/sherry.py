@@ -23,6 +23,7 @@ STATUS = {0: "SHERRY_OK", 1: "SHERRY_EINVAL", 2: "SHERRY_ESHAPE", 3: "SHERRY_EDT
 
 EXPORTS = [
     "sherry_version", "sherry_status_str", "sherry_packed_bytes", "sherry_pack", "sherry_decode", "sherry_gemv",
+    "sherry_act_quant",
     "sherry_gemv_plan_bytes", "sherry_gemv_plan", "sherry_gemv_grouped", "sherry_gemm",
     "sherry_gemm_plan_bytes", "sherry_gemm_plan", "sherry_gemm_grouped",
     "tern2_packed_bytes", "tern2_encode", "tern2_gemv", "tern2_gemv_plan", "tern2_gemm", "tern2_gemm_plan",
@@ -72,6 +73,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sherry_pack.argtypes = [vp, i, i64, i64, i64, vp, vp, i, vp]
     lib.sherry_decode.restype = i
     lib.sherry_decode.argtypes = [vp, i64, i64, vp, i64, vp]
+    lib.sherry_act_quant.restype = i
+    lib.sherry_act_quant.argtypes = [vp, i, i64, i64, i64, vp, i64, vp, vp]
     gemv_args = [vp, vp, i, i64, i64, vp, i, vp, vp, vp, i, vp]
     for f in (lib.sherry_gemv, lib.tern2_gemv):
         f.restype = i
@@ -158,6 +161,22 @@ def decode(codes: torch.Tensor, n: int, k: int) -> torch.Tensor:
     t = torch.empty(n, k, dtype=torch.int8, device=codes.device)
     _check("sherry_decode", load().sherry_decode(codes.data_ptr(), n, k, t.data_ptr(), t.stride(0), _stream()))
     return t
+
+
+def act_quant(x: torch.Tensor):
+    """Per-token int8 quantization of activations x [m, k] (fp32, fp16 or
+    bf16; a 1-D x is one token) -> (x_q int8 [m, k], scales fp32 [m])."""
+    x2 = x.unsqueeze(0) if x.dim() == 1 else x
+    if not x.is_cuda or x2.dim() != 2 or x2.stride(1) != 1:
+        raise ValueError("x must be a GPU tensor [m, k] with unit stride along k")
+    m, k = x2.shape
+    q = torch.empty(m, k, dtype=torch.int8, device=x.device)
+    s = torch.empty(m, dtype=torch.float32, device=x.device)
+    _check("sherry_act_quant", load().sherry_act_quant(x2.data_ptr(), _DT.get(x2.dtype, -1), m, k, x2.stride(0),
+                                                       q.data_ptr(), q.stride(0), s.data_ptr(), _stream()))
+    if x.dim() == 1:
+        return q[0], s
+    return q, s
 
 
 def _gemv(fn_name, codes, scales, x, x_scale, acc, y):
