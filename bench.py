@@ -204,6 +204,35 @@ def cpu_baseline(torch, probs, shapes, min_seconds=10.0, max_layers=16):
 
 # ----------------------------------------------------------------- extras ---
 
+def graph_time(torch, fn, outs, replays=200):
+    """Mean us per replay of fn captured in a HIP graph, after checking three
+    replays (outputs cleared before each) against one eager run; a string
+    when capture or the check fails."""
+    fn()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    try:
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(graph):
+            fn()
+        for _ in range(3):
+            for o in outs:
+                o.zero_()
+            graph.replay()
+            torch.cuda.synchronize()
+            if not all(torch.equal(o, r) for o, r in zip(outs, ref)):
+                return "replay mismatch"
+        mean_ms, _ = time_launches(torch, graph.replay, replays, 20)
+        return round(mean_ms * 1e3, 2)
+    except RuntimeError as e:  # capture not available: report, do not fail the run
+        return f"capture failed: {e}"[:120]
+
+
 def extras(torch, sherry, synth, probs_1b, codes_1b, args):
     import numpy as np
 
@@ -301,8 +330,8 @@ def extras(torch, sherry, synth, probs_1b, codes_1b, args):
     torch.cuda.empty_cache()
 
     # a few tokens (small-batch decode): every matrix of all R replicas in one
-    # grouped launch (256 x 16 tiles, HBM-bound), and, for latency, one layer's
-    # seven matrices as separate calls
+    # grouped launch (few-token kernel, HBM-bound), and, for latency, one
+    # layer's seven matrices as separate calls
     for m in (2, 4, 8, 16):
         xs = {}
         for _, n, k in shapes_1b:
@@ -330,6 +359,43 @@ def extras(torch, sherry, synth, probs_1b, codes_1b, args):
                          "us_per_layer_7_calls": round(call_ms * 1e3, 2)}
         del gp, grouped
     out["gemm_1b_layer"] = gemm
+
+    # activation quantization, and the decode step it feeds for one 1B layer:
+    # bf16 x -> int8 on the GPU, one product over the concatenated q | k | v
+    # rows (shared x), then again for gate | up -- as four launches
+    # (quantize, product, quantize, product) and as two products that
+    # quantize x themselves; eager, and replayed from a HIP graph (checked
+    # against eager first)
+    act = {}
+    for label, m in (("x_1x2048_bf16", 1), ("x_2048x2048_bf16", 2048), ("x_1x8192_bf16", 1)):
+        k = 8192 if "8192" in label else 2048
+        xb = torch.randn(m, k, device=dev).to(torch.bfloat16)
+        mean_ms, _ = time_launches(torch, lambda: sherry.act_quant(xb), 100, 10)
+        act[label] = {"us": round(mean_ms * 1e3, 2), "GBps": round(3 * m * k / (mean_ms * 1e-3) / 1e9, 1)}
+    by = {p["name"]: p for p in rep0}
+    qkv = (torch.cat([by[nm]["codes"] for nm in ("q", "k", "v")]), torch.cat([by[nm]["scales"] for nm in ("q", "k", "v")]))
+    gu = (torch.cat([by[nm]["codes"] for nm in ("gate", "up")]), torch.cat([by[nm]["scales"] for nm in ("gate", "up")]))
+    x1 = torch.randn(2048, device=dev).to(torch.bfloat16)
+    x2 = torch.randn(2048, device=dev).to(torch.bfloat16)
+    y_qkv = torch.empty(qkv[1].numel(), dtype=torch.float16, device=dev)
+    y_gu = torch.empty(gu[1].numel(), dtype=torch.float16, device=dev)
+
+    def decode_step():
+        q1, s1 = sherry.act_quant(x1)
+        sherry.gemv(qkv[0], qkv[1], q1, s1, out=y_qkv)
+        q2, s2 = sherry.act_quant(x2)
+        sherry.gemv(gu[0], gu[1], q2, s2, out=y_gu)
+
+    def decode_step_fused():  # x quantized inside the products: two launches
+        sherry.gemv_quant(qkv[0], qkv[1], x1, out=y_qkv)
+        sherry.gemv_quant(gu[0], gu[1], x2, out=y_gu)
+
+    for label, fn in (("decode_step", decode_step), ("decode_step_fused_quant", decode_step_fused)):
+        mean_ms, _ = time_launches(torch, fn, 200, 20)
+        act[f"{label}_us"] = round(mean_ms * 1e3, 2)
+        act[f"{label}_graph_us"] = graph_time(torch, fn, (y_qkv, y_gu))
+    act["decode_step_code_bytes"] = int(qkv[0].numel() * 4 + gu[0].numel() * 4)
+    out["act_quant_and_fused_projections"] = act
 
     # packer: fp16 weights of one 1B layer -> codes + fp16 scales
     wts = {}

@@ -121,6 +121,19 @@ sherry_status sherry_decode(const uint32_t* codes, int64_t n, int64_t k, int8_t*
 sherry_status sherry_act_quant(const void* x, sherry_dtype x_dt, int64_t m, int64_t k, int64_t ldx, int8_t* xq,
                                int64_t ldq, float* scales, hipStream_t stream);
 
+/* Batch-1 product of fp activations: x is quantized per token inside the
+ * kernel (the rule of sherry_act_quant, bit for bit), then the int8 product
+ * and epilogue of sherry_gemv with that scale -- one launch instead of
+ * sherry_act_quant followed by sherry_gemv, for decode steps.
+ *   x           : k values of x_dt (F32|F16|BF16), aligned to its size; DEVICE
+ *   x_scale_out : nullable; receives the token's scale (4-byte aligned)
+ *   k           : at most 8192 (the quantized x is held in LDS)
+ * Everything else as sherry_gemv with int8 x.  Errors: as sherry_gemv, plus
+ * ESHAPE for k > 8192 and EDTYPE for another x_dt. */
+sherry_status sherry_gemv_quant(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,
+                                const void* x, sherry_dtype x_dt, float* x_scale_out, int32_t* acc, void* y,
+                                sherry_dtype y_dt, hipStream_t stream);
+
 /* Batch-1 product y = diag(s_w) * T * x (the decode-phase GEMV).
  *   codes    : n x k packed codes (layout above), 4-byte aligned
  *   w_scales : n scales of s_dt (F32|F16)

@@ -150,6 +150,24 @@ def test_act_quant_validation(lib):
     assert f(A, BF16, 1, 8192, 8192, A, 8192, A, None) == EDEVICE
 
 
+def test_gemv_quant_validation(lib):
+    def call(codes=A, sw=A, s_dt=F16, n=64, k=1024, x=A, x_dt=BF16, xs=None, acc=A, y=A, y_dt=F16):
+        return lib.sherry_gemv_quant(codes, sw, s_dt, n, k, x, x_dt, xs, acc, y, y_dt, None)
+    assert call(codes=None) == EINVAL
+    assert call(x=None) == EINVAL
+    assert call(acc=None, y=None) == EINVAL
+    assert call(k=1000) == ESHAPE
+    assert call(k=8192 + 128) == ESHAPE
+    assert call(x_dt=I8) == EDTYPE
+    assert call(s_dt=BF16) == EDTYPE
+    assert call(y_dt=I8) == EDTYPE
+    assert call(x=A + 1) == EALIGN
+    assert call(x=A + 2, x_dt=F32) == EALIGN
+    assert call(xs=A + 2) == EALIGN
+    assert call(x=A + 2, x_dt=F16, xs=A) == EDEVICE  # valid
+    assert call(k=8192, x_dt=F32, acc=None) == EDEVICE
+
+
 def test_decode_validation(lib):
     f = lib.sherry_decode
     assert f(None, 4, 128, A, 128, None) == EINVAL

@@ -575,7 +575,7 @@ def test_full_layer_sampled_rows(gpu_lib, layer):
 # ------------------------------------------- activation quantization ---
 
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("m,k", [(1, 2048), (5, 8192), (3, 100), (2048, 2048)])
+@pytest.mark.parametrize("m,k", [(1, 2048), (5, 8192), (3, 100), (2048, 2048), (2, 10000)])
 def test_act_quant(gpu_lib, dt, m, k):
     """Per-token absmax int8 on the GPU equals the oracle bit for bit (codes
     and scales); rows include an all-zero token and exact ties."""
@@ -638,3 +638,44 @@ def test_quantized_fused_projections(gpu_lib, m):
         torch.cuda.synchronize()
         assert np.array_equal(acc.cpu().numpy(), ra)
         assert np.array_equal(y.cpu().numpy().view(np.uint16), ry.view(np.uint16))
+
+
+@pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("n,k", [(256, 1024), (3072, 2048), (300, 384), (2048, 8192), (8192, 2048), (40, 3072)])
+def test_gemv_quant(gpu_lib, dt, n, k):
+    """fp x quantized inside the GEMV: sums, outputs and the scale equal the
+    oracle chain (quantize, then the int8 product) bit for bit."""
+    say(f"gemv with in-kernel x quantization {dt} n={n} k={k}")
+    g = synth.rng(71 + n + k)
+    x = (g.standard_normal(k) * g.uniform(0.01, 20.0)).astype(np.float32)
+    x[:5] = [0.0, 222.25 / 8, 11.375 / 8, -11.375 / 8, 4.375 / 8]  # exact ties when 222.25 / 8 is the max
+    if dt == "f32":
+        host, tx = x, torch.from_numpy(x)
+    elif dt == "f16":
+        host = x.astype(np.float16)
+        tx = torch.from_numpy(host)
+    else:
+        host = synth.f32_to_bf16_bits(x)
+        tx = torch.from_numpy(host.view(np.int16)).view(torch.bfloat16)
+    words = synth.random_words(n * (k // 128) * 5, g)
+    sw = synth.row_scales(n, g, np.float16)
+    acc, y, sx = gpu_lib.gemv_quant(words_dev(words), dev(sw), tx.to(DEV), torch.float16, want_acc=True,
+                                    want_scale=True)
+    torch.cuda.synchronize()
+    rq, rs = act_ref.quantize(host.reshape(1, k), dt)
+    ra, ry = sherry_ref.gemv_i8(words, sw, n, k, rq[0], rs[0], np.float16)
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(acc.cpu().numpy(), ra)
+    assert np.array_equal(y.cpu().numpy().view(np.uint16), ry.view(np.uint16))
+
+
+def test_gemv_quant_zero_token(gpu_lib):
+    """An all-zero x: scale 1, every sum 0."""
+    g = synth.rng(72)
+    n, k = 130, 2048
+    words = synth.random_words(n * (k // 128) * 5, g)
+    sw = synth.row_scales(n, g, np.float16)
+    acc, y, sx = gpu_lib.gemv_quant(words_dev(words), dev(sw), torch.zeros(k, dtype=torch.bfloat16, device=DEV),
+                                    torch.float32, want_acc=True, want_scale=True)
+    torch.cuda.synchronize()
+    assert sx.item() == 1.0 and not acc.any().item() and not y.any().item()

@@ -110,6 +110,29 @@ sherry_status gemv_impl(int32_t format, const uint32_t* codes, const void* w_sca
   return launched(launch_gemv(d, x_dt == SHERRY_BF16, format, stream));
 }
 
+// Batch-1 product of fp activations quantized per token inside the kernel.
+sherry_status gemv_quant_impl(int32_t format, const uint32_t* codes, const void* w_scales, sherry_dtype s_dt,
+                              int64_t n, int64_t k, const void* x, sherry_dtype x_dt, float* x_scale_out,
+                              int32_t* acc, void* y, sherry_dtype y_dt, hipStream_t stream) {
+  if (!codes || !w_scales || !x || (!acc && !y)) return SHERRY_EINVAL;
+  if (sherry_status s = check_nk(n, k)) return s;
+  if (k > kActMaxK) return SHERRY_ESHAPE;
+  int dt = 0;
+  switch (x_dt) {
+    case SHERRY_F32: dt = kActF32; break;
+    case SHERRY_F16: dt = kActF16; break;
+    case SHERRY_BF16: dt = kActBf16; break;
+    default: return SHERRY_EDTYPE;
+  }
+  if (!is_scale_dt(s_dt) || (y && y_dt != SHERRY_F32 && y_dt != SHERRY_F16)) return SHERRY_EDTYPE;
+  if (!aligned(codes, 4) || !aligned(x, dt_size(x_dt)) || !aligned(w_scales, dt_size(s_dt)) ||
+      (acc && !aligned(acc, 4)) || (x_scale_out && !aligned(x_scale_out, 4)) || (y && !aligned(y, dt_size(y_dt))))
+    return SHERRY_EALIGN;
+  if (sherry_status s = check_device()) return s;
+  const GemvDesc d = make_desc(codes, w_scales, s_dt, n, k, x, nullptr, acc, y, y_dt);
+  return launched(launch_gemv_xq(d, dt, x_scale_out, format, stream));
+}
+
 // Validation of one product for M tokens; fills the kernel record.
 sherry_status check_gemm(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,
                          const void* x, sherry_dtype x_dt, int64_t m, int64_t ldx, const float* x_scales, int32_t* acc,
@@ -382,6 +405,12 @@ sherry_status sherry_decode(const uint32_t* codes, int64_t n, int64_t k, int8_t*
   if (!aligned(codes, 4) || !aligned(t, 16) || ldt % 16 != 0) return SHERRY_EALIGN;
   if (sherry_status s = check_device()) return s;
   return launched(launch_decode(codes, n, k, t, ldt, stream));
+}
+
+sherry_status sherry_gemv_quant(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,
+                                const void* x, sherry_dtype x_dt, float* x_scale_out, int32_t* acc, void* y,
+                                sherry_dtype y_dt, hipStream_t stream) {
+  return gemv_quant_impl(kFmtSherry, codes, w_scales, s_dt, n, k, x, x_dt, x_scale_out, acc, y, y_dt, stream);
 }
 
 sherry_status sherry_gemv(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,

@@ -9,23 +9,11 @@
 // absmax / 127 by one IEEE division (1 for an all-zero token), and every
 // element is x / s by one IEEE division, rounded to an integer with ties to
 // even (v_rndne_f32) and clipped to [-127, 127].
+#include "actq.h"
 #include "launch.h"
 
 namespace sherry {
 namespace {
-
-constexpr int kActThreads = 256;
-
-template <int DT>
-__device__ __forceinline__ float act_value(const void* x, int64_t i) {
-  if constexpr (DT == kActF32) {
-    return gmem(static_cast<const float*>(x))[i];
-  } else if constexpr (DT == kActF16) {
-    return static_cast<float>(gmem(static_cast<const _Float16*>(x))[i]);
-  } else {
-    return __uint_as_float(static_cast<uint32_t>(gmem(static_cast<const uint16_t*>(x))[i]) << 16);
-  }
-}
 
 template <int DT>
 __global__ __launch_bounds__(kActThreads) void act_quant_kernel(const void* x, int64_t k, int64_t ldx, int8_t* q,
@@ -33,22 +21,23 @@ __global__ __launch_bounds__(kActThreads) void act_quant_kernel(const void* x, i
   __shared__ float wmax[kActThreads / kWave];
   const int64_t row = blockIdx.x;
   const int64_t base = row * ldx;
-  float amax = 0.0f;
-  for (int64_t j = threadIdx.x; j < k; j += kActThreads) amax = fmaxf(amax, fabsf(act_value<DT>(x, base + j)));
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  if ((threadIdx.x & (kWave - 1)) == 0) wmax[threadIdx.x / kWave] = amax;
-  __syncthreads();
-  amax = wmax[0];
-#pragma unroll
-  for (int w = 1; w < kActThreads / kWave; ++w) amax = fmaxf(amax, wmax[w]);
-  const float s = amax == 0.0f ? 1.0f : __fdiv_rn(amax, 127.0f);
-  if (threadIdx.x == 0) gmem(scales)[row] = s;
   int8_t* out = q + row * ldq;
-  for (int64_t j = threadIdx.x; j < k; j += kActThreads) {
-    const float v = __builtin_rintf(__fdiv_rn(act_value<DT>(x, base + j), s));
-    gmem(out)[j] = static_cast<int8_t>(static_cast<int>(fminf(fmaxf(v, -127.0f), 127.0f)));
+  if (k <= kActMaxRegK) {
+    float v[kActRegs];
+    const float s = act_scale(block_max(act_load_token(x, DT, base, k, v), wmax));
+    if (threadIdx.x == 0) gmem(scales)[row] = s;
+#pragma unroll
+    for (int i = 0; i < kActRegs; ++i) {
+      const int64_t j = threadIdx.x + static_cast<int64_t>(i) * kActThreads;
+      if (j < k) gmem(out)[j] = act_code(v[i], s);
+    }
+    return;
   }
+  float amax = 0.0f;
+  for (int64_t j = threadIdx.x; j < k; j += kActThreads) amax = fmaxf(amax, fabsf(act_value(x, DT, base + j)));
+  const float s = act_scale(block_max(amax, wmax));
+  if (threadIdx.x == 0) gmem(scales)[row] = s;
+  for (int64_t j = threadIdx.x; j < k; j += kActThreads) gmem(out)[j] = act_code(act_value(x, DT, base + j), s);
 }
 
 }  // namespace

@@ -1,0 +1,57 @@
+// Device helpers of the per-token absmax int8 activation quantization (the
+// symmetric rule the int8 products take: scale = absmax / 127 by one IEEE
+// division, 1 for an all-zero token; each value one IEEE division, round
+// half to even, clip to 127), shared by the stand-alone kernel and the
+// GEMV that quantizes its x itself.
+#pragma once
+
+#include "launch.h"  // kActF32, kActF16, kActBf16
+
+namespace sherry {
+
+constexpr int kActThreads = 256;  // workgroup size of both users
+
+__device__ __forceinline__ float act_value(const void* x, int dt, int64_t i) {
+  if (dt == kActF32) return gmem(static_cast<const float*>(x))[i];
+  if (dt == kActF16) return static_cast<float>(gmem(static_cast<const _Float16*>(x))[i]);
+  return __uint_as_float(static_cast<uint32_t>(gmem(static_cast<const uint16_t*>(x))[i]) << 16);
+}
+
+// Max over the workgroup (kActThreads threads; every thread gets it).
+__device__ __forceinline__ float block_max(float v, float* wmax) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  if ((threadIdx.x & (kWave - 1)) == 0) wmax[threadIdx.x / kWave] = v;
+  __syncthreads();
+  v = wmax[0];
+#pragma unroll
+  for (int w = 1; w < kActThreads / kWave; ++w) v = fmaxf(v, wmax[w]);
+  return v;
+}
+
+__device__ __forceinline__ float act_scale(float amax) { return amax == 0.0f ? 1.0f : __fdiv_rn(amax, 127.0f); }
+
+__device__ __forceinline__ int8_t act_code(float v, float s) {
+  const float r = __builtin_rintf(__fdiv_rn(v, s));
+  return static_cast<int8_t>(static_cast<int>(fminf(fmaxf(r, -127.0f), 127.0f)));
+}
+
+// Tokens of up to kActRegs * kActThreads values: every thread loads its
+// values (j = thread + kActThreads i) at once into registers.
+constexpr int kActRegs = 32;
+constexpr int kActMaxRegK = kActRegs * kActThreads;
+static_assert(kActMaxRegK == kActMaxK, "the in-kernel quantization covers every k it accepts");
+
+__device__ __forceinline__ float act_load_token(const void* x, int dt, int64_t base, int64_t k, float (&v)[kActRegs]) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kActRegs; ++i) {
+    const int64_t j = threadIdx.x + static_cast<int64_t>(i) * kActThreads;
+    v[i] = j < k ? act_value(x, dt, base + j) : 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < kActRegs; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  return amax;
+}
+
+}  // namespace sherry

@@ -15,6 +15,7 @@
 // layout (words 0-3 of every group, then word 4 of every group) the L lanes
 // of a row read 16 L contiguous bytes with one 16-byte load each and 4 L
 // contiguous bytes with one 4-byte load each.
+#include "actq.h"
 #include "formats.h"
 #include "launch.h"
 
@@ -39,9 +40,34 @@ __device__ __forceinline__ void init_tables(uint32_t* tab32, uint2* pairs) {
   __syncthreads();
 }
 
-template <class Fmt, int L, int GPL>
+// x quantized by the workgroup itself (XQ): all threads load the token's fp
+// values (kActRegs each), take the absmax over the workgroup, and write the
+// int8 codes to xl in LDS; the scale goes to *sx.  Ends with a barrier.
+__device__ __forceinline__ void quantize_x_lds(const GemvDesc& d, int dt, int8_t* xl, float* sx, float* wmax) {
+  float v[kActRegs];
+  const float s = act_scale(block_max(act_load_token(d.x, dt, 0, d.k, v), wmax));
+#pragma unroll
+  for (int i = 0; i < kActRegs; ++i) {
+    const int j = threadIdx.x + i * kActThreads;
+    if (j < d.k) xl[j] = act_code(v[i], s);
+  }
+  if (threadIdx.x == 0) *sx = s;
+  __syncthreads();
+}
+
+// XQ: d.x holds fp values of type xdt; the workgroup quantizes them into xl
+// (LDS, scale to *sx) right after issuing its first code loads, and the
+// lanes take their x from there.
+struct XQuant {
+  int dt;
+  int8_t* xl;
+  float* sx;
+  float* wmax;
+};
+
+template <class Fmt, int L, int GPL, bool XQ = false>
 __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, int row_end, uint32_t* tab32,
-                                             uint2* tab, int32_t* out) {
+                                             uint2* tab, int32_t* out, XQuant xq = XQuant{}) {
   constexpr int RPW = kWave / L;
   constexpr int RPI = (kGemvThreads / kWave) * RPW;
   constexpr int NW = Fmt::kWords;
@@ -55,19 +81,25 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
   // by every row, so cache-resident after the first workgroup), then the
   // first kRing - 1 ring entries, and only then the LDS tables and barrier.
   uint32_t xr[GPL][32];
+  auto load_x = [&]() {
 #pragma unroll
-  for (int t = 0; t < GPL; ++t) {
-    const SHERRY_GLOBAL u32x4_t* xp = gmem(reinterpret_cast<const u32x4_t*>(
-        static_cast<const int8_t*>(d.x) + static_cast<int64_t>(t * L + lp) * kGroupWeights));
+    for (int t = 0; t < GPL; ++t) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const u32x4_t v = xp[q];
-      xr[t][4 * q + 0] = v.x;
-      xr[t][4 * q + 1] = v.y;
-      xr[t][4 * q + 2] = v.z;
-      xr[t][4 * q + 3] = v.w;
+      for (int q = 0; q < 8; ++q) {
+        u32x4_t v;
+        if constexpr (XQ)
+          v = reinterpret_cast<const u32x4_t*>(xq.xl + (t * L + lp) * kGroupWeights)[q];
+        else
+          v = gmem(reinterpret_cast<const u32x4_t*>(static_cast<const int8_t*>(d.x) +
+                                                    static_cast<int64_t>(t * L + lp) * kGroupWeights))[q];
+        xr[t][4 * q + 0] = v.x;
+        xr[t][4 * q + 1] = v.y;
+        xr[t][4 * q + 2] = v.z;
+        xr[t][4 * q + 3] = v.w;
+      }
     }
-  }
+  };
+  if constexpr (!XQ) load_x();
   // Rows past the tile load the tile's last row instead (results discarded).
   // A ring of kRing register buffers (the loop is unrolled by kRing): while
   // one row is decoded, the words of the next kRing - 1 rows are in flight.
@@ -105,6 +137,10 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
   const int r0 = row_begin + wave * RPW + rs;
 #pragma unroll
   for (int b = 0; b + 1 < kRing; ++b) fetch(ring[b], r0 + b * RPI);
+  if constexpr (XQ) {
+    quantize_x_lds(d, xq.dt, xq.xl, xq.sx, xq.wmax);
+    load_x();
+  }
   init_tables<Fmt>(tab32, tab);
   for (int base = row_begin, r = r0; base < row_end; base += kRing * RPI, r += kRing * RPI) {
     // all kRing steps run; rows past the tile end are clamped loads whose
@@ -120,8 +156,10 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
 // Any k % 128 == 0: 64 lanes per row, x read per group (not register-resident).
 template <class Fmt>
 __device__ __forceinline__ void gemv_i8_rows_generic(const GemvDesc& d, int row_begin, int row_end,
-                                                     uint32_t* tab32, uint2* tab, int32_t* out) {
+                                                     uint32_t* tab32, uint2* tab, int32_t* out,
+                                                     XQuant xq = XQuant{}) {
   constexpr int NW = Fmt::kWords;
+  if (xq.xl) quantize_x_lds(d, xq.dt, xq.xl, xq.sx, xq.wmax);
   init_tables<Fmt>(tab32, tab);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -132,13 +170,14 @@ __device__ __forceinline__ void gemv_i8_rows_generic(const GemvDesc& d, int row_
     for (int g = lane; g < G; g += kWave) {
       uint32_t w[NW];
       Fmt::load(w, d.codes + static_cast<int64_t>(r) * (G * NW), G, g);
-      const SHERRY_GLOBAL u32x4_t* xp =
-          gmem(reinterpret_cast<const u32x4_t*>(x + static_cast<int64_t>(g) * kGroupWeights));
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const u32x4_t v = xp[q];
-        const uint2 w0 = Fmt::i8x8(w, 2 * q, tab);
-        const uint2 w1 = Fmt::i8x8(w, 2 * q + 1, tab);
+        const u32x4_t v = xq.xl ? reinterpret_cast<const u32x4_t*>(xq.xl + g * kGroupWeights)[q]
+                                : gmem(reinterpret_cast<const u32x4_t*>(x + static_cast<int64_t>(g) * kGroupWeights))[q];
+        const uint2 w0 = kPairMask != 0 ? Fmt::i8x8(w, 2 * q, tab)
+                                        : make_uint2(Fmt::i8x4(w, 4 * q, tab32), Fmt::i8x4(w, 4 * q + 1, tab32));
+        const uint2 w1 = kPairMask != 0 ? Fmt::i8x8(w, 2 * q + 1, tab)
+                                        : make_uint2(Fmt::i8x4(w, 4 * q + 2, tab32), Fmt::i8x4(w, 4 * q + 3, tab32));
         acc = __builtin_amdgcn_sdot4(static_cast<int>(w0.x), static_cast<int>(v.x), acc, false);
         acc = __builtin_amdgcn_sdot4(static_cast<int>(w0.y), static_cast<int>(v.y), acc, false);
         acc = __builtin_amdgcn_sdot4(static_cast<int>(w1.x), static_cast<int>(v.z), acc, false);
@@ -246,11 +285,10 @@ __device__ __forceinline__ void gemv_bf16_rows_generic(const GemvDesc& d, int ro
 // global stores out of the loop keeps the prefetched loads in flight.
 constexpr int kMaxTileRows = 2048;
 
-__device__ __forceinline__ void finalize_i8(const GemvDesc& d, int row0, int row1, const int32_t* res) {
+__device__ __forceinline__ void finalize_i8(const GemvDesc& d, int row0, int row1, const int32_t* res,
+                                            bool has_sx, float sx) {
   const bool s_f16 = d.flags & kFlagScaleF16;
   const bool y_f16 = d.flags & kFlagYF16;
-  const bool has_sx = d.x_scale != nullptr;
-  const float sx = has_sx ? *gmem(d.x_scale) : 1.0f;
   for (int i = threadIdx.x; i < row1 - row0; i += blockDim.x) {
     const int r = row0 + i;
     if (d.acc) gmem(d.acc)[r] = res[i];
@@ -293,7 +331,31 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_i8_kernel(GemvDesc d, int t
   else
     gemv_i8_rows<Fmt, (L > 0 ? L : 64), GPL>(d, row0, row1, tab32, tab, res);
   __syncthreads();
-  finalize_i8(d, row0, row1, res);
+  finalize_i8(d, row0, row1, res, d.x_scale != nullptr, d.x_scale ? *gmem(d.x_scale) : 1.0f);
+}
+
+// fp x quantized per token inside the workgroup (k <= kActMaxRegK), then
+// the int8 product; block 0 writes the scale to sx_out if given.
+static_assert(kGemvThreads == kActThreads, "the workgroup quantizes x with every thread");
+template <class Fmt, int L, int GPL>
+__global__ __launch_bounds__(kGemvThreads) void gemv_i8_xq_kernel(GemvDesc d, int tile_rows, int xdt,
+                                                                  float* sx_out) {
+  __shared__ uint32_t tab32[32];
+  __shared__ uint2 tab[kPairMask != 0 ? Fmt::kPairEntries : 1];
+  __shared__ int32_t res[kMaxTileRows];
+  __shared__ __attribute__((aligned(16))) int8_t xl[kActMaxRegK];
+  __shared__ float sx;
+  __shared__ float wmax[kGemvThreads / kWave];
+  const XQuant xq{xdt, xl, &sx, wmax};
+  const int row0 = blockIdx.x * tile_rows;
+  const int row1 = min(row0 + tile_rows, d.n);
+  if constexpr (L == 0)
+    gemv_i8_rows_generic<Fmt>(d, row0, row1, tab32, tab, res, xq);
+  else
+    gemv_i8_rows<Fmt, L, GPL, true>(d, row0, row1, tab32, tab, res, xq);
+  __syncthreads();
+  finalize_i8(d, row0, row1, res, true, sx);
+  if (sx_out && blockIdx.x == 0 && threadIdx.x == 0) *gmem(sx_out) = sx;
 }
 
 template <int L, int GPL>
@@ -358,7 +420,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_i8_grouped_kernel(const cha
     default: gemv_i8_rows_generic<Fmt>(d, row0, row1, tab32, tab, res); break;
   }
   __syncthreads();
-  finalize_i8(d, row0, row1, res);
+  finalize_i8(d, row0, row1, res, d.x_scale != nullptr, d.x_scale ? *gmem(d.x_scale) : 1.0f);
 }
 
 template <bool WIDE>
@@ -446,6 +508,24 @@ void launch_i8_class(const GemvDesc& d, unsigned grid, int tile_rows, hipStream_
   }
 }
 
+template <class Fmt, int L, int GPL>
+void launch_xq(const GemvDesc& d, unsigned grid, int tile_rows, int xdt, float* sx_out, hipStream_t stream) {
+  hipLaunchKernelGGL((gemv_i8_xq_kernel<Fmt, L, GPL>), dim3(grid), dim3(kGemvThreads), 0, stream, d, tile_rows, xdt,
+                     sx_out);
+}
+
+template <class Fmt>
+void launch_xq_class(const GemvDesc& d, unsigned grid, int tile_rows, int xdt, float* sx_out, hipStream_t stream) {
+  switch (d.kclass) {
+    case k1024: launch_xq<Fmt, 8, 1>(d, grid, tile_rows, xdt, sx_out, stream); break;
+    case k2048: launch_xq<Fmt, 16, 1>(d, grid, tile_rows, xdt, sx_out, stream); break;
+    case k4096: launch_xq<Fmt, 32, 1>(d, grid, tile_rows, xdt, sx_out, stream); break;
+    case k8192: launch_xq<Fmt, 64, 1>(d, grid, tile_rows, xdt, sx_out, stream); break;
+    case k3072: launch_xq<Fmt, 8, 3>(d, grid, tile_rows, xdt, sx_out, stream); break;
+    default: launch_xq<Fmt, 0, 1>(d, grid, tile_rows, xdt, sx_out, stream); break;
+  }
+}
+
 template <int L, int GPL>
 void launch_bf16(const GemvDesc& d, unsigned grid, int tile_rows, hipStream_t stream) {
   hipLaunchKernelGGL((gemv_bf16_kernel<L, GPL>), dim3(grid), dim3(kGemvThreads), 0, stream, d, tile_rows);
@@ -474,6 +554,17 @@ hipError_t launch_gemv(const GemvDesc& d, bool bf16_x, int32_t format, hipStream
     launch_i8_class<Tern2>(d, grid, tile_rows, stream);
   else
     launch_i8_class<Sherry3of4>(d, grid, tile_rows, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemv_xq(const GemvDesc& d, int xdt, float* sx_out, int32_t format, hipStream_t stream) {
+  const int rpi = rows_per_iter(d.kclass);
+  const int tile_rows = rpi * tile_iters_for(d.n, rpi);
+  const unsigned grid = static_cast<unsigned>((d.n + tile_rows - 1) / tile_rows);
+  if (format == kFmtTern2)
+    launch_xq_class<Tern2>(d, grid, tile_rows, xdt, sx_out, stream);
+  else
+    launch_xq_class<Sherry3of4>(d, grid, tile_rows, xdt, sx_out, stream);
   return hipGetLastError();
 }
 

@@ -147,10 +147,13 @@ hipError_t launch_pack(const void* w, int w_dt, int64_t n, int64_t k, int64_t ld
                        void* scales, bool s_f16, hipStream_t stream);
 hipError_t launch_gemv(const GemvDesc& d, bool bf16_x, int32_t format, hipStream_t stream);
 hipError_t launch_gemv_grouped(const PlanHeader* host, const void* dev, hipStream_t stream);
+hipError_t launch_gemv_xq(const GemvDesc& d, int xdt, float* sx_out, int32_t format, hipStream_t stream);
 hipError_t launch_gemm(const GemmDesc& d, int32_t format, hipStream_t stream);
 hipError_t launch_gemm_grouped(const PlanHeader* host, const void* dev, hipStream_t stream);
-// Activation quantization: input element types.
+// Activation quantization: input element types; the GEMV that quantizes its
+// own x holds it in LDS, k <= kActMaxK.
 constexpr int kActF32 = 0, kActF16 = 1, kActBf16 = 2;
+constexpr int64_t kActMaxK = 8192;
 hipError_t launch_act_quant(const void* x, int dt, int64_t m, int64_t k, int64_t ldx, int8_t* q, int64_t ldq,
                             float* scales, hipStream_t stream);
 hipError_t launch_decode(const uint32_t* codes, int64_t n, int64_t k, int8_t* t, int64_t ldt, hipStream_t stream);

@@ -23,7 +23,7 @@ STATUS = {0: "SHERRY_OK", 1: "SHERRY_EINVAL", 2: "SHERRY_ESHAPE", 3: "SHERRY_EDT
 
 EXPORTS = [
     "sherry_version", "sherry_status_str", "sherry_packed_bytes", "sherry_pack", "sherry_decode", "sherry_gemv",
-    "sherry_act_quant",
+    "sherry_act_quant", "sherry_gemv_quant",
     "sherry_gemv_plan_bytes", "sherry_gemv_plan", "sherry_gemv_grouped", "sherry_gemm",
     "sherry_gemm_plan_bytes", "sherry_gemm_plan", "sherry_gemm_grouped",
     "tern2_packed_bytes", "tern2_encode", "tern2_gemv", "tern2_gemv_plan", "tern2_gemm", "tern2_gemm_plan",
@@ -73,6 +73,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sherry_pack.argtypes = [vp, i, i64, i64, i64, vp, vp, i, vp]
     lib.sherry_decode.restype = i
     lib.sherry_decode.argtypes = [vp, i64, i64, vp, i64, vp]
+    lib.sherry_gemv_quant.restype = i
+    lib.sherry_gemv_quant.argtypes = [vp, vp, i, i64, i64, vp, i, vp, vp, vp, i, vp]
     lib.sherry_act_quant.restype = i
     lib.sherry_act_quant.argtypes = [vp, i, i64, i64, i64, vp, i64, vp, vp]
     gemv_args = [vp, vp, i, i64, i64, vp, i, vp, vp, vp, i, vp]
@@ -177,6 +179,21 @@ def act_quant(x: torch.Tensor):
     if x.dim() == 1:
         return q[0], s
     return q, s
+
+
+def gemv_quant(codes, scales, x, out_dtype=torch.float16, want_acc=False, want_scale=False, out=None):
+    """y = diag(scales) T q(x) for fp x [k] (fp32, fp16 or bf16), x quantized
+    per token inside the kernel.  Returns (acc or None, y or None, scale or
+    None)."""
+    _dev(codes, scales, x, out)
+    n, k = scales.numel(), x.numel()
+    y = out if out is not None else (torch.empty(n, dtype=out_dtype, device=x.device) if out_dtype else None)
+    acc = torch.empty(n, dtype=torch.int32, device=x.device) if want_acc else None
+    sx = torch.empty(1, dtype=torch.float32, device=x.device) if want_scale else None
+    _check("sherry_gemv_quant", load().sherry_gemv_quant(
+        codes.data_ptr(), scales.data_ptr(), _DT[scales.dtype], n, k, x.data_ptr(), _DT.get(x.dtype, -1), _ptr(sx),
+        _ptr(acc), _ptr(y), _DT[y.dtype] if y is not None else F32, _stream()))
+    return acc, y, sx
 
 
 def _gemv(fn_name, codes, scales, x, x_scale, acc, y):
