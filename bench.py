@@ -49,6 +49,9 @@ def parse_args(argv=None):
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run one plain 1 GiB device copy (calibrates HBM byte counters)")
+    p.add_argument("--gemm-profile", action="store_true",
+                   help="only the grouped GEMM launches on the 1B layer (M = 2048 prefill and M = 16 few-token), "
+                        "a few of each, for a profiler; prints their timing and exits")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) and exit")
     return p.parse_args(argv)
@@ -203,6 +206,36 @@ def cpu_baseline(torch, probs, shapes, min_seconds=10.0, max_layers=16):
 
 
 # ----------------------------------------------------------------- extras ---
+
+def gemm_profile(torch, sherry, synth, probs, args):
+    """The grouped GEMM launches alone: one 1B layer at M = 2048 (tiled int8
+    MFMA kernel) and every replica at M = 16 (few-token kernel), a few
+    launches of each after the clocks settle; one JSON line of their mean
+    times."""
+    dev = torch.device("cuda:0")
+    g = synth.rng(args.seed + 7)
+    shapes = synth.LLAMA32_1B_LAYER
+    res = {}
+    for m, sel, steps in ((2048, [p for p in probs if p["replica"] == 0], 10), (16, probs, 20)):
+        xs = {}
+        for _, n, k in shapes:
+            if k not in xs:
+                xq, sx, _ = synth.act_absmax_int8(m, k, g)
+                xs[k] = (torch.from_numpy(xq).to(dev), torch.from_numpy(sx).to(dev))
+        gp = [dict(codes=p["codes"], scales=p["scales"], x=xs[p["k"]][0], x_scales=xs[p["k"]][1],
+                   y=torch.empty(m, p["n"], dtype=torch.float16, device=dev)) for p in sel]
+        grouped = sherry.GroupedGemm(gp)
+        mean_ms, _ = time_launches(torch, grouped, steps, 3)
+        layers = len(sel) // len(shapes)
+        ops = 2 * m * layers * sum(n * k for _, n, k in shapes)
+        code_bytes = layers * sum(n * k * 5 // 32 for _, n, k in shapes)
+        res[f"M{m}"] = {"us_per_launch": round(mean_ms * 1e3, 2), "layers": layers, "tiles": grouped.n_tiles,
+                        "TOPS": round(ops / (mean_ms * 1e-3) / 1e12, 1),
+                        "code_TBps": round(code_bytes / (mean_ms * 1e-3) / 1e12, 3)}
+        del gp, grouped
+    print(json.dumps(res), flush=True)
+    return 0
+
 
 def graph_time(torch, fn, outs, replays=200):
     """Mean us per replay of fn captured in a HIP graph, after checking three
@@ -475,6 +508,8 @@ def main(argv=None):
     shapes = synth.LLAMA32_1B_LAYER
     R = args.replicas
     codes, probs = build_layer_replicas(torch, sherry, synth, shapes, R, args.seed)
+    if args.gemm_profile:
+        return gemm_profile(torch, sherry, synth, probs, args)
     grouped = sherry.GroupedGemv(probs)
     torch.cuda.synchronize()
     print(f"# built {R} replicas of the 1B layer: {codes.numel() * 4 / 1e9:.3f} GB of codes, "
