@@ -226,6 +226,34 @@ def test_grouped_plan_on_host(lib):
     assert lib.sherry_gemv_grouped(None, A, None) == EINVAL
 
 
+def test_grouped_plan_k3072_tiles_by_x_type(lib):
+    """k = 3072 rows: int8 x puts one group in each of 24 of 32 lanes (8 rows
+    per iteration, 256-row tiles); bf16 x keeps 3 groups in each of 8 lanes
+    (32 rows per iteration, 1024-row tiles) and flags the plan for that
+    kernel family.  The plan size covers the int8 tiling, the larger one."""
+    from ultra_bit_weight_amd.sherry import GemvProblem
+
+    arr = (GemvProblem * 2)()
+    arr[0] = GemvProblem(A, A, 1024, 3072, A, None, None, A)
+    arr[1] = GemvProblem(A, A, 300, 2048, A, None, None, A)
+    nbytes = lib.sherry_gemv_plan_bytes(arr, 2)
+    assert nbytes == 64 + 64 * 2 + 8 * (4 + 1)
+    buf = ctypes.create_string_buffer(nbytes + 8)
+    base = (ctypes.addressof(buf) + 7) // 8 * 8
+    assert lib.sherry_gemv_plan(arr, 2, F16, I8, F16, base, nbytes) == OK
+    hdr = ctypes.string_at(base, 64)
+    assert int.from_bytes(hdr[12:16], "little") == 5
+    assert int.from_bytes(hdr[40:48], "little") == 0
+    arr[0].x_scale = None
+    arr[1].x_scale = None
+    arr[0].acc = None
+    arr[1].acc = None
+    assert lib.sherry_gemv_plan(arr, 2, F16, BF16, F32, base, nbytes) == OK
+    hdr = ctypes.string_at(base, 64)
+    assert int.from_bytes(hdr[12:16], "little") == 2
+    assert int.from_bytes(hdr[40:48], "little") == 1
+
+
 def test_grouped_gemm_plan_on_host(lib):
     from ultra_bit_weight_amd.sherry import GemmProblem
 

@@ -270,15 +270,17 @@ sherry_status gemm_plan_impl(int32_t format, const sherry_gemm_problem* probs, i
   return SHERRY_OK;
 }
 
-// Grouped plan: header | GemvDesc[count] | PlanTile[n_tiles].
-int64_t tile_rows_for(const sherry_gemv_problem& p) {
-  return static_cast<int64_t>(rows_per_iter(kclass_of(p.k))) * kGroupedIters;
+// Grouped plan: header | GemvDesc[count] | PlanTile[n_tiles].  Tile rows
+// depend on the k class and, at k = 3072, on the x type; the int8 tiling
+// has at least as many tiles, so plan sizes are computed for it.
+int64_t tile_rows_for(const sherry_gemv_problem& p, bool bf16) {
+  return static_cast<int64_t>(rows_per_iter(kclass_of(p.k), bf16)) * kGroupedIters;
 }
 
-int64_t plan_tiles(const sherry_gemv_problem* probs, int32_t count) {
+int64_t plan_tiles(const sherry_gemv_problem* probs, int32_t count, bool bf16) {
   int64_t tiles = 0;
   for (int32_t i = 0; i < count; ++i) {
-    const int64_t rows = tile_rows_for(probs[i]);
+    const int64_t rows = tile_rows_for(probs[i], bf16);
     tiles += (probs[i].n + rows - 1) / rows;
   }
   return tiles;
@@ -288,7 +290,7 @@ size_t plan_bytes_impl(const sherry_gemv_problem* probs, int32_t count) {
   if (!probs || count <= 0) return 0;
   for (int32_t i = 0; i < count; ++i)
     if (check_nk(probs[i].n, probs[i].k) != SHERRY_OK) return 0;
-  const int64_t tiles = plan_tiles(probs, count);
+  const int64_t tiles = plan_tiles(probs, count, false);
   if (tiles > kMaxDim) return 0;
   return sizeof(PlanHeader) + sizeof(GemvDesc) * static_cast<size_t>(count) + sizeof(PlanTile) * tiles;
 }
@@ -312,14 +314,15 @@ sherry_status plan_impl(int32_t format, const sherry_gemv_problem* probs, int32_
   h.magic = kPlanMagic;
   h.version = kPlanVersion;
   h.count = count;
-  h.n_tiles = static_cast<int32_t>(plan_tiles(probs, count));
+  const bool bf16 = x_dt == SHERRY_BF16;
+  h.n_tiles = static_cast<int32_t>(plan_tiles(probs, count, bf16));
   h.s_dt = s_dt;
   h.x_dt = x_dt;
   h.y_dt = y_dt;
   h.format = format;
   h.bytes = need;
   for (int32_t i = 0; i < count; ++i)
-    if (kclass_of(probs[i].k) == k3072) h.reserved[0] = 1;
+    if (bf16 && kclass_of(probs[i].k) == k3072) h.reserved[0] = 1;  // the bf16 kernel family with 3 groups per lane
   std::memcpy(out, &h, sizeof(h));
   GemvDesc* descs = reinterpret_cast<GemvDesc*>(out + sizeof(PlanHeader));
   PlanTile* tiles = reinterpret_cast<PlanTile*>(descs + count);
@@ -335,7 +338,7 @@ sherry_status plan_impl(int32_t format, const sherry_gemv_problem* probs, int32_
   int64_t t = 0;
   for (const int32_t i : order) {
     const sherry_gemv_problem& p = probs[i];
-    const int64_t rows = tile_rows_for(p);
+    const int64_t rows = tile_rows_for(p, bf16);
     for (int64_t r0 = 0; r0 < p.n; r0 += rows) tiles[t++] = PlanTile{i, static_cast<int32_t>(r0)};
   }
   return SHERRY_OK;

@@ -65,7 +65,7 @@ struct XQuant {
   float* wmax;
 };
 
-template <class Fmt, int L, int GPL, bool XQ = false>
+template <class Fmt, int L, int GPL, int GR = GPL * L, bool XQ = false>
 __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, int row_end, uint32_t* tab32,
                                              uint2* tab, int32_t* out, XQuant xq = XQuant{}) {
   constexpr int RPW = kWave / L;
@@ -75,7 +75,7 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
   const int wave = threadIdx.x / kWave;
   const int lp = lane % L;
   const int rs = lane / L;
-  constexpr int G = GPL * L;
+  constexpr int G = GR;  // groups per row (lanes t L + lp >= G hold none: x = 0)
 
   // Start-up order keeps the memory pipe busy: this lane's x slice (shared
   // by every row, so cache-resident after the first workgroup), then the
@@ -88,10 +88,11 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
       for (int q = 0; q < 8; ++q) {
         u32x4_t v;
         if constexpr (XQ)
-          v = reinterpret_cast<const u32x4_t*>(xq.xl + (t * L + lp) * kGroupWeights)[q];
+          v = reinterpret_cast<const u32x4_t*>(xq.xl + min(t * L + lp, G - 1) * kGroupWeights)[q];
         else
           v = gmem(reinterpret_cast<const u32x4_t*>(static_cast<const int8_t*>(d.x) +
-                                                    static_cast<int64_t>(t * L + lp) * kGroupWeights))[q];
+                                                    static_cast<int64_t>(min(t * L + lp, G - 1)) * kGroupWeights))[q];
+        if (G < GPL * L && t * L + lp >= G) v = u32x4_t{0u, 0u, 0u, 0u};
         xr[t][4 * q + 0] = v.x;
         xr[t][4 * q + 1] = v.y;
         xr[t][4 * q + 2] = v.z;
@@ -107,7 +108,7 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
   auto fetch = [&](uint32_t (&buf)[GPL][NW], int row) {
     const uint32_t* rp = d.codes + static_cast<int64_t>(min(row, last)) * (G * NW);
 #pragma unroll
-    for (int t = 0; t < GPL; ++t) Fmt::load(buf[t], rp, G, t * L + lp);
+    for (int t = 0; t < GPL; ++t) Fmt::load(buf[t], rp, G, min(t * L + lp, G - 1));
   };
   auto step = [&](const uint32_t (&buf)[GPL][NW], int row) {
     constexpr int C = kDotChains;  // independent dot4 accumulation chains
@@ -192,7 +193,7 @@ __device__ __forceinline__ void gemv_i8_rows_generic(const GemvDesc& d, int row_
 // ---------------------------------------------------------------- bf16 x ---
 // Weights expanded to four bf16 (one 8-byte table entry) per code, two
 // v_dot2_f32_bf16 per block; fp32 accumulation, then y = acc * s_w.
-template <int L, int GPL>
+template <int L, int GPL, int GR = GPL * L>
 __device__ __forceinline__ void gemv_bf16_rows(const GemvDesc& d, int row_begin, int row_end, const uint2* tab,
                                                const uint4* xs, float* out) {
   constexpr int RPW = kWave / L;
@@ -202,14 +203,15 @@ __device__ __forceinline__ void gemv_bf16_rows(const GemvDesc& d, int row_begin,
   const int wave = threadIdx.x / kWave;
   const int lp = lane % L;
   const int rs = lane / L;
-  constexpr int G = GPL * L;
+  constexpr int G = GR;  // groups per row (lanes t L + lp >= G hold none: x = 0)
 
   uint32_t xr[GPL][64];
 #pragma unroll
   for (int t = 0; t < GPL; ++t) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const uint4 v = xs[(t * L + lp) * 17 + q];
+      uint4 v = xs[min(t * L + lp, G - 1) * 17 + q];
+      if (G < GPL * L && t * L + lp >= G) v = make_uint4(0u, 0u, 0u, 0u);
       xr[t][4 * q + 0] = v.x;
       xr[t][4 * q + 1] = v.y;
       xr[t][4 * q + 2] = v.z;
@@ -220,7 +222,7 @@ __device__ __forceinline__ void gemv_bf16_rows(const GemvDesc& d, int row_begin,
   auto fetch = [&](uint32_t (&buf)[GPL][NW], int row) {
     const uint32_t* rp = d.codes + static_cast<int64_t>(min(row, last)) * (G * NW);
 #pragma unroll
-    for (int t = 0; t < GPL; ++t) load_group(buf[t], rp, G, t * L + lp);
+    for (int t = 0; t < GPL; ++t) load_group(buf[t], rp, G, min(t * L + lp, G - 1));
   };
   auto step = [&](const uint32_t (&buf)[GPL][NW], int row) {
     float a2[2] = {0.0f, 0.0f};  // two chains: slot pairs (0,1) and (2,3)
@@ -236,7 +238,7 @@ __device__ __forceinline__ void gemv_bf16_rows(const GemvDesc& d, int row_begin,
     const float acc = reduce_add_f32<L>(a2[0] + a2[1]);
     if (lp == 0 && row < row_end) out[row - row_begin] = acc;
   };
-  constexpr int NR = GPL > 1 ? 2 : kRing;  // the 3-groups-per-lane class keeps two buffers
+  constexpr int NR = GPL > 1 ? 2 : kRing;  // several groups per lane: two buffers (registers)
   uint32_t ring[NR][GPL][NW];
   const int r0 = row_begin + wave * RPW + rs;
 #pragma unroll
@@ -319,7 +321,7 @@ __device__ __forceinline__ void stage_x(uint4* xs, const void* x, int bytes) {
 
 // Single problem: one kernel per class, so each keeps its own register count.
 // The row walkers build the LDS tables themselves (after their first loads).
-template <class Fmt, int L, int GPL>
+template <class Fmt, int L, int GPL, int GR>
 __global__ __launch_bounds__(kGemvThreads) void gemv_i8_kernel(GemvDesc d, int tile_rows) {
   __shared__ uint32_t tab32[32];
   __shared__ uint2 tab[Fmt::kPairEntries];
@@ -329,7 +331,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_i8_kernel(GemvDesc d, int t
   if (L == 0)
     gemv_i8_rows_generic<Fmt>(d, row0, row1, tab32, tab, res);
   else
-    gemv_i8_rows<Fmt, (L > 0 ? L : 64), GPL>(d, row0, row1, tab32, tab, res);
+    gemv_i8_rows<Fmt, (L > 0 ? L : 64), GPL, (L > 0 ? GR : 64)>(d, row0, row1, tab32, tab, res);
   __syncthreads();
   finalize_i8(d, row0, row1, res, d.x_scale != nullptr, d.x_scale ? *gmem(d.x_scale) : 1.0f);
 }
@@ -337,7 +339,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_i8_kernel(GemvDesc d, int t
 // fp x quantized per token inside the workgroup (k <= kActMaxRegK), then
 // the int8 product; block 0 writes the scale to sx_out if given.
 static_assert(kGemvThreads == kActThreads, "the workgroup quantizes x with every thread");
-template <class Fmt, int L, int GPL>
+template <class Fmt, int L, int GPL, int GR>
 __global__ __launch_bounds__(kGemvThreads) void gemv_i8_xq_kernel(GemvDesc d, int tile_rows, int xdt,
                                                                   float* sx_out) {
   __shared__ uint32_t tab32[32];
@@ -352,13 +354,13 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_i8_xq_kernel(GemvDesc d, in
   if constexpr (L == 0)
     gemv_i8_rows_generic<Fmt>(d, row0, row1, tab32, tab, res, xq);
   else
-    gemv_i8_rows<Fmt, L, GPL, true>(d, row0, row1, tab32, tab, res, xq);
+    gemv_i8_rows<Fmt, L, GPL, GR, true>(d, row0, row1, tab32, tab, res, xq);
   __syncthreads();
   finalize_i8(d, row0, row1, res, true, sx);
   if (sx_out && blockIdx.x == 0 && threadIdx.x == 0) *gmem(sx_out) = sx;
 }
 
-template <int L, int GPL>
+template <int L, int GPL, int GR>
 __global__ __launch_bounds__(kGemvThreads) void gemv_bf16_kernel(GemvDesc d, int tile_rows) {
   __shared__ uint2 tab[32];
   __shared__ float res[kMaxTileRows];
@@ -371,30 +373,33 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_bf16_kernel(GemvDesc d, int
   if (L == 0)
     gemv_bf16_rows_generic(d, row0, row1, tab, res);
   else
-    gemv_bf16_rows<(L > 0 ? L : 64), GPL>(d, row0, row1, tab, xs, res);
+    gemv_bf16_rows<(L > 0 ? L : 64), GPL, (L > 0 ? GR : 64)>(d, row0, row1, tab, xs, res);
   __syncthreads();
   finalize_bf16(d, row0, row1, res);
 }
 
 // Grouped: one workgroup per plan tile {problem, first row}; a tile spans
-// kGroupedIters row iterations of its problem's class.  WIDE selects the
-// family that also holds the 3-groups-per-lane class (k = 3072), which needs
-// more registers; plans without k = 3072 use the narrow family.
-__device__ __forceinline__ int tile_rows_of(int32_t kc) {
+// kGroupedIters row iterations of its problem's class.  The int8 classes
+// keep one group per lane (k = 3072: 24 of 32 lanes), so one register
+// budget serves all of them.  The bf16 path is bound by its VALU work, where
+// idle lanes cost more than occupancy gains: its k = 3072 class keeps 3
+// groups in each of 8 lanes, in the WIDE kernel family (more registers),
+// used only by plans that hold such a problem.
+__device__ __forceinline__ int tile_rows_of(int32_t kc, bool bf16) {
   int lanes = 64;
   switch (kc) {
     case k1024: lanes = 8; break;
     case k2048: lanes = 16; break;
     case k4096: lanes = 32; break;
     case k8192: lanes = 64; break;
-    case k3072: lanes = 8; break;
+    case k3072: lanes = bf16 ? 8 : 32; break;
     default: lanes = 64; break;
   }
   return (kGemvThreads / kWave) * (kWave / lanes) * kGroupedIters;
 }
 constexpr int kMaxGroupedTileRows = (kGemvThreads / kWave) * (kWave / 8) * kGroupedIters;
 
-template <class Fmt, bool WIDE>
+template <class Fmt>
 __global__ __launch_bounds__(kGemvThreads) void gemv_i8_grouped_kernel(const char* plan) {
   __shared__ uint32_t tab32[32];
   __shared__ uint2 tab[Fmt::kPairEntries];
@@ -405,18 +410,13 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_i8_grouped_kernel(const cha
   const PlanTile tl = tiles[blockIdx.x];
   const GemvDesc d = descs[tl.prob];
   const int row0 = tl.row0;
-  const int row1 = min(row0 + tile_rows_of(d.kclass), d.n);
+  const int row1 = min(row0 + tile_rows_of(d.kclass, false), d.n);
   switch (d.kclass) {
     case k1024: gemv_i8_rows<Fmt, 8, 1>(d, row0, row1, tab32, tab, res); break;
     case k2048: gemv_i8_rows<Fmt, 16, 1>(d, row0, row1, tab32, tab, res); break;
     case k4096: gemv_i8_rows<Fmt, 32, 1>(d, row0, row1, tab32, tab, res); break;
     case k8192: gemv_i8_rows<Fmt, 64, 1>(d, row0, row1, tab32, tab, res); break;
-    case k3072:
-      if (WIDE) {
-        gemv_i8_rows<Fmt, 8, 3>(d, row0, row1, tab32, tab, res);
-        break;
-      }
-      [[fallthrough]];
+    case k3072: gemv_i8_rows<Fmt, 32, 1, 24>(d, row0, row1, tab32, tab, res); break;
     default: gemv_i8_rows_generic<Fmt>(d, row0, row1, tab32, tab, res); break;
   }
   __syncthreads();
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_bf16_grouped_kernel(const c
   const PlanTile tl = tiles[blockIdx.x];
   const GemvDesc d = descs[tl.prob];
   const int row0 = tl.row0;
-  const int row1 = min(row0 + tile_rows_of(d.kclass), d.n);
+  const int row1 = min(row0 + tile_rows_of(d.kclass, true), d.n);
   const bool staged = d.kclass != kGeneric && (WIDE || d.kclass != k3072);
   if (staged) stage_x<16>(xs, d.x, 2 * d.k);
   __syncthreads();
@@ -491,9 +491,9 @@ int tile_iters_for(int64_t n, int rpi) {
 
 namespace {
 
-template <class Fmt, int L, int GPL>
+template <class Fmt, int L, int GPL, int GR = GPL * L>
 void launch_i8(const GemvDesc& d, unsigned grid, int tile_rows, hipStream_t stream) {
-  hipLaunchKernelGGL((gemv_i8_kernel<Fmt, L, GPL>), dim3(grid), dim3(kGemvThreads), 0, stream, d, tile_rows);
+  hipLaunchKernelGGL((gemv_i8_kernel<Fmt, L, GPL, GR>), dim3(grid), dim3(kGemvThreads), 0, stream, d, tile_rows);
 }
 
 template <class Fmt>
@@ -503,14 +503,14 @@ void launch_i8_class(const GemvDesc& d, unsigned grid, int tile_rows, hipStream_
     case k2048: launch_i8<Fmt, 16, 1>(d, grid, tile_rows, stream); break;
     case k4096: launch_i8<Fmt, 32, 1>(d, grid, tile_rows, stream); break;
     case k8192: launch_i8<Fmt, 64, 1>(d, grid, tile_rows, stream); break;
-    case k3072: launch_i8<Fmt, 8, 3>(d, grid, tile_rows, stream); break;
+    case k3072: launch_i8<Fmt, 32, 1, 24>(d, grid, tile_rows, stream); break;
     default: launch_i8<Fmt, 0, 1>(d, grid, tile_rows, stream); break;
   }
 }
 
-template <class Fmt, int L, int GPL>
+template <class Fmt, int L, int GPL, int GR = GPL * L>
 void launch_xq(const GemvDesc& d, unsigned grid, int tile_rows, int xdt, float* sx_out, hipStream_t stream) {
-  hipLaunchKernelGGL((gemv_i8_xq_kernel<Fmt, L, GPL>), dim3(grid), dim3(kGemvThreads), 0, stream, d, tile_rows, xdt,
+  hipLaunchKernelGGL((gemv_i8_xq_kernel<Fmt, L, GPL, GR>), dim3(grid), dim3(kGemvThreads), 0, stream, d, tile_rows, xdt,
                      sx_out);
 }
 
@@ -521,14 +521,14 @@ void launch_xq_class(const GemvDesc& d, unsigned grid, int tile_rows, int xdt, f
     case k2048: launch_xq<Fmt, 16, 1>(d, grid, tile_rows, xdt, sx_out, stream); break;
     case k4096: launch_xq<Fmt, 32, 1>(d, grid, tile_rows, xdt, sx_out, stream); break;
     case k8192: launch_xq<Fmt, 64, 1>(d, grid, tile_rows, xdt, sx_out, stream); break;
-    case k3072: launch_xq<Fmt, 8, 3>(d, grid, tile_rows, xdt, sx_out, stream); break;
+    case k3072: launch_xq<Fmt, 32, 1, 24>(d, grid, tile_rows, xdt, sx_out, stream); break;
     default: launch_xq<Fmt, 0, 1>(d, grid, tile_rows, xdt, sx_out, stream); break;
   }
 }
 
-template <int L, int GPL>
+template <int L, int GPL, int GR = GPL * L>
 void launch_bf16(const GemvDesc& d, unsigned grid, int tile_rows, hipStream_t stream) {
-  hipLaunchKernelGGL((gemv_bf16_kernel<L, GPL>), dim3(grid), dim3(kGemvThreads), 0, stream, d, tile_rows);
+  hipLaunchKernelGGL((gemv_bf16_kernel<L, GPL, GR>), dim3(grid), dim3(kGemvThreads), 0, stream, d, tile_rows);
 }
 
 void launch_bf16_class(const GemvDesc& d, unsigned grid, int tile_rows, hipStream_t stream) {
@@ -545,7 +545,7 @@ void launch_bf16_class(const GemvDesc& d, unsigned grid, int tile_rows, hipStrea
 }  // namespace
 
 hipError_t launch_gemv(const GemvDesc& d, bool bf16_x, int32_t format, hipStream_t stream) {
-  const int rpi = rows_per_iter(d.kclass);
+  const int rpi = rows_per_iter(d.kclass, bf16_x);
   const int tile_rows = rpi * tile_iters_for(d.n, rpi);
   const unsigned grid = static_cast<unsigned>((d.n + tile_rows - 1) / tile_rows);
   if (bf16_x)
@@ -572,23 +572,14 @@ hipError_t launch_gemv_grouped(const PlanHeader* h, const void* dev, hipStream_t
   if (h->n_tiles == 0) return hipSuccess;
   const char* plan = static_cast<const char*>(dev);
   const dim3 grid(h->n_tiles), block(kGemvThreads);
-  const bool wide = h->reserved[0] != 0;  // some problem has k = 3072
-  if (h->x_dt == SHERRY_BF16) {
-    if (wide)
-      hipLaunchKernelGGL((gemv_bf16_grouped_kernel<true>), grid, block, 0, stream, plan);
-    else
-      hipLaunchKernelGGL((gemv_bf16_grouped_kernel<false>), grid, block, 0, stream, plan);
-  } else if (h->format == kFmtTern2) {
-    if (wide)
-      hipLaunchKernelGGL((gemv_i8_grouped_kernel<Tern2, true>), grid, block, 0, stream, plan);
-    else
-      hipLaunchKernelGGL((gemv_i8_grouped_kernel<Tern2, false>), grid, block, 0, stream, plan);
-  } else {
-    if (wide)
-      hipLaunchKernelGGL((gemv_i8_grouped_kernel<Sherry3of4, true>), grid, block, 0, stream, plan);
-    else
-      hipLaunchKernelGGL((gemv_i8_grouped_kernel<Sherry3of4, false>), grid, block, 0, stream, plan);
-  }
+  if (h->x_dt == SHERRY_BF16 && h->reserved[0] != 0)  // some problem has k = 3072
+    hipLaunchKernelGGL((gemv_bf16_grouped_kernel<true>), grid, block, 0, stream, plan);
+  else if (h->x_dt == SHERRY_BF16)
+    hipLaunchKernelGGL((gemv_bf16_grouped_kernel<false>), grid, block, 0, stream, plan);
+  else if (h->format == kFmtTern2)
+    hipLaunchKernelGGL((gemv_i8_grouped_kernel<Tern2>), grid, block, 0, stream, plan);
+  else
+    hipLaunchKernelGGL((gemv_i8_grouped_kernel<Sherry3of4>), grid, block, 0, stream, plan);
   return hipGetLastError();
 }
 

@@ -23,13 +23,15 @@ inline int32_t kclass_of(int64_t k) {
   }
 }
 // Lanes per row for a class (64 for the generic kernel).
-inline int lanes_per_row(int32_t kc) {
+// Lanes per row of a k class: one group per lane (k = 3072: 24 of 32 lanes
+// hold one), except bf16 x at k = 3072, which keeps 3 groups in each of 8.
+inline int lanes_per_row(int32_t kc, bool bf16 = false) {
   switch (kc) {
     case k1024: return 8;
     case k2048: return 16;
     case k4096: return 32;
     case k8192: return 64;
-    case k3072: return 8;
+    case k3072: return bf16 ? 8 : 32;
     default: return 64;
   }
 }
@@ -38,7 +40,9 @@ inline int lanes_per_row(int32_t kc) {
 #endif
 constexpr int kGemvThreads = SHERRY_GEMV_THREADS;  // GEMV workgroup size (4 waves by default)
 // Rows one GEMV workgroup advances per iteration.
-inline int rows_per_iter(int32_t kc) { return (kGemvThreads / kWave) * (kWave / lanes_per_row(kc)); }
+inline int rows_per_iter(int32_t kc, bool bf16 = false) {
+  return (kGemvThreads / kWave) * (kWave / lanes_per_row(kc, bf16));
+}
 
 enum Format : int32_t { kFmtSherry = 0, kFmtTern2 = 1 };
 
@@ -53,7 +57,7 @@ struct PlanHeader {
   int32_t y_dt;
   int32_t format;
   uint64_t bytes;
-  uint64_t reserved[3];  // reserved[0]: nonzero if some problem has k = 3072
+  uint64_t reserved[3];  // GEMV plans: reserved[0] nonzero if some problem has k = 3072; GEMM plans: the tiling
 };
 static_assert(sizeof(PlanHeader) == 64, "plan header layout");
 constexpr uint32_t kPlanMagic = 0x53485950u;  // "PYHS"
