@@ -207,6 +207,60 @@ def cpu_baseline(torch, probs, shapes, min_seconds=10.0, max_layers=16):
 
 # ----------------------------------------------------------------- extras ---
 
+def oracle_beside(synth, max_seconds=2.0):
+    """The oracle of each measured row as it stands, one thread, on a bounded
+    synthetic sample of that row's workload (a few seconds in all): the CPU
+    rate beside each GPU figure.  Rates are per unit of the row's work."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import act_ref, sherry_ref, tern2_ref
+
+    g = synth.rng(97)
+    out = {}
+
+    def timed(fn, reps_max=50):
+        t0 = time.perf_counter()
+        reps = 0
+        while reps < reps_max:
+            fn()
+            reps += 1
+            if time.perf_counter() - t0 >= max_seconds:
+                break
+        return (time.perf_counter() - t0) / reps
+
+    with threadpool_limits(limits=1):
+        words = {k: (synth.random_words(n * k // 128 * 5, g), synth.row_scales(n, g, np.float16), n)
+                 for name, n, k in synth.LLAMA32_1B_LAYER if name in ("q", "down")}
+        n, k = 2048, 2048
+        w, sw, _ = words[2048]
+        xq, sx, _ = synth.act_absmax_int8(16, k, g)
+        s16 = timed(lambda: sherry_ref.gemm_i8(w, sw, n, k, xq, sx, np.float16))
+        out["a7_gemm_m16_q_2048x2048"] = {"s": round(s16, 4), "weights_per_s": n * k / s16}
+        xp, sxp, _ = synth.act_absmax_int8(2048, k, g)
+        s2048 = timed(lambda: sherry_ref.gemm_i8(w, sw, n, k, xp, sxp, np.float16), reps_max=2)
+        out["a8_gemm_m2048_q_2048x2048"] = {"s": round(s2048, 3), "TOPS": 2 * 2048 * n * k / s2048 / 1e12}
+        t = synth.ternary_dense(n, k, g)
+        w2 = tern2_ref.pack(t)
+        x1, s1, _ = synth.act_absmax_int8(1, k, g)
+        st = timed(lambda: tern2_ref.gemv_i8(w2, sw, n, k, x1[0], s1[0], np.float16))
+        out["a9_tern2_gemv_q_2048x2048"] = {"s": round(st, 4), "weights_per_s": n * k / st}
+        n3 = k3 = 3072
+        w3 = synth.random_words(n3 * k3 // 128 * 5, g)
+        sw3 = synth.row_scales(n3, g, np.float32)
+        xb = synth.x_bf16_normal(k3, g)
+        sb = timed(lambda: sherry_ref.gemv_bf16(w3, sw3, n3, k3, xb))
+        out["a2_a6_bf16_gemv_q_3072x3072"] = {"s": round(sb, 4), "weights_per_s": n3 * k3 / sb}
+        xa = synth.x_bf16_normal((16, 2048), g)
+        sa = timed(lambda: act_ref.quantize(xa, "bf16"))
+        out["f1_act_quant_16x2048_bf16"] = {"s": round(sa, 5), "values_per_s": 16 * 2048 / sa}
+        wp = (g.standard_normal((512, 2048)) * 0.02).astype(np.float16)
+        spk = timed(lambda: sherry_ref.pack(wp, np.float16), reps_max=2)
+        out["a1_pack_512x2048_fp16"] = {"s": round(spk, 3), "weights_per_s": 512 * 2048 / spk}
+    out["cores"] = 1
+    return out
+
+
 def gemm_profile(torch, sherry, synth, probs, args):
     """The grouped GEMM launches alone: one 1B layer at M = 2048 (tiled int8
     MFMA kernel) and every replica at M = 16 (few-token kernel), a few
@@ -429,6 +483,29 @@ def extras(torch, sherry, synth, probs_1b, codes_1b, args):
         act[f"{label}_graph_us"] = graph_time(torch, fn, (y_qkv, y_gu))
     act["decode_step_code_bytes"] = int(qkv[0].numel() * 4 + gu[0].numel() * 4)
     out["act_quant_and_fused_projections"] = act
+
+    # a whole 1B decoder layer's products in dependency order, x quantized
+    # inside each: q|k|v, (attention not run) o, gate|up, down -- four
+    # launches per layer; 16 layers make a LLaMA-3.2-1B token's weight pass
+    xo = torch.randn(2048, device=dev).to(torch.bfloat16)
+    xd = torch.randn(8192, device=dev).to(torch.bfloat16)
+    y_o = torch.empty(2048, dtype=torch.float16, device=dev)
+    y_d = torch.empty(2048, dtype=torch.float16, device=dev)
+
+    def layer_step():
+        sherry.gemv_quant(qkv[0], qkv[1], x1, out=y_qkv)
+        sherry.gemv_quant(by["o"]["codes"], by["o"]["scales"], xo, out=y_o)
+        sherry.gemv_quant(gu[0], gu[1], x2, out=y_gu)
+        sherry.gemv_quant(by["down"]["codes"], by["down"]["scales"], xd, out=y_d)
+    mean_ms, _ = time_launches(torch, layer_step, 200, 20)
+    lay = {"eager_us_per_layer": round(mean_ms * 1e3, 2)}
+    gus = graph_time(torch, layer_step, (y_qkv, y_o, y_gu, y_d))
+    lay["graph_us_per_layer"] = gus
+    lay["code_bytes_per_layer"] = int(sum(n * k * 5 // 32 for _, n, k in shapes_1b))
+    if isinstance(gus, float):
+        lay["graph_us_per_token_16_layers"] = round(16 * gus, 1)
+    out["f4_decode_layer_1b"] = lay
+    out["oracle_beside"] = oracle_beside(synth)
 
     # packer: fp16 weights of one 1B layer -> codes + fp16 scales
     wts = {}
