@@ -424,3 +424,76 @@ def pin_act_dtypes(act):
 
 
 ACT_PINS = [pin_act_hand, pin_act_zero_and_signs, pin_act_exact, pin_act_generator, pin_act_dtypes]
+
+
+# ------------------------------------------------ 1.67-bit comparator ---
+# Pins for oracle.tern3_ref (three ternary weights in five bits, readings
+# F1-F4): base-3 digits written out by hand, the all-zero row from the bit
+# pattern of its code, one changed weight located by hand, sizes, and
+# brute-force products over the generator's dense matrix.
+
+def pin_t3_codes(t3):
+    # c = (t0 + 1) + 3 (t1 + 1) + 9 (t2 + 1), digits written out by hand
+    hand = {0: (-1, -1, -1), 13: (0, 0, 0), 26: (1, 1, 1), 5: (1, 0, -1), 21: (-1, 0, 1), 1: (0, -1, -1),
+            9: (-1, -1, 0), 14: (1, 0, 0)}
+    for c, blk in hand.items():
+        assert t3.decode_block(c) == blk, c
+        assert t3.encode_block(blk) == c, c
+    seen = {t3.encode_block(b) for b in itertools.product((-1, 0, 1), repeat=3)}
+    assert seen == set(range(27))
+    for c in range(27, 32):
+        try:
+            t3.decode_block(c)
+        except ValueError:
+            continue
+        raise AssertionError(f"code {c} is not a block")
+
+
+def pin_t3_layout(t3):
+    assert t3.packed_words(1, 128) == 10 and t3.packed_words(1, 2048) == 110 and t3.packed_words(3, 8192) == 3 * 430
+    # an all-zero row: every code is 13 = 0b01101, so stream bit b is set iff
+    # b mod 5 is 0, 2 or 3; the words are the stream's 32-bit slices
+    k, G = 2048, 22
+    bits = [1 if b % 5 in (0, 2, 3) else 0 for b in range(160)]
+    slices = [sum(bits[32 * i + j] << j for j in range(32)) for i in range(5)]
+    w = t3.pack(np.zeros((1, k), np.int8))
+    for g in range(G):
+        assert [int(v) for v in w[4 * g:4 * g + 4]] == slices[:4], g
+        assert int(w[4 * G + g]) == slices[4], g
+    # weight 189 = 96 + 3 * 31 is t0 of code 31 of group 1 (stream bits
+    # 155..159, word 4 of the group, bits 27..31, stored at word 4 G + 1);
+    # setting it to +1 turns that code from 13 into 14 (0b01110)
+    t = np.zeros((1, k), np.int8)
+    t[0, 189] = 1
+    w2 = t3.pack(t)
+    diff = np.nonzero(w2 != w)[0].tolist()
+    assert diff == [4 * G + 1]
+    assert int(w2[4 * G + 1]) ^ int(w[4 * G + 1]) == (13 ^ 14) << 27
+
+
+def pin_t3_products(t3):
+    g = synth.rng(57)
+    n, k = 5, 256
+    t = synth.ternary_dense(n, k, g)
+    words = t3.pack(t)
+    assert np.array_equal(t3.unpack(words, n, k), t)
+    codes_ok = True
+    G = t3.groups(k)
+    for r in range(n):
+        for grp in range(G):
+            parts = [int(words[5 * G * r + 4 * grp + i]) for i in range(4)] + [int(words[5 * G * r + 4 * G + grp])]
+            stream = sum(p << (32 * i) for i, p in enumerate(parts))
+            codes_ok &= all(((stream >> (5 * j)) & 31) < 27 for j in range(32))
+    assert codes_ok
+    x = synth.x_int8_uniform(k, g)
+    sw = synth.row_scales(n, g, np.float32)
+    acc, y = t3.gemv_i8(words, sw, n, k, x, None, np.float32)
+    for r in range(n):  # brute force over the generator's dense matrix
+        want = 0
+        for c in range(k):
+            want += int(t[r, c]) * int(x[c])
+        assert int(acc[r]) == want, r
+        assert Fraction(float(y[r])) == f32_exact(Fraction(want) * Fraction(float(sw[r]))), r
+
+
+T3_PINS = [pin_t3_codes, pin_t3_layout, pin_t3_products]

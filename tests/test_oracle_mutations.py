@@ -207,3 +207,44 @@ def test_act_planted_mistake_is_caught(name):
         except (AssertionError, ValueError, OverflowError, FloatingPointError):
             caught.append(pin.__name__)
     assert caught, f"{name} passed every pin"
+
+
+# ------------------------------------------------ 1.67-bit comparator ---
+T3_PATH = os.path.join(os.path.dirname(PATH), "tern3_ref.py")
+T3_MUTANTS = {
+    "digit_order_reversed": ("return (t0 + 1) + 3 * (t1 + 1) + 9 * (t2 + 1)",
+                             "return (t2 + 1) + 3 * (t1 + 1) + 9 * (t0 + 1)"),
+    "signs_swapped": ("return (c % 3 - 1, (c // 3) % 3 - 1, c // 9 - 1)",
+                      "return (1 - c % 3, 1 - (c // 3) % 3, 1 - c // 9)"),
+    "groups_contiguous": ("out[r, 4 * g + i if i < 4 else 4 * G + g] = word", "out[r, 5 * g + i] = word"),
+    "msb_first_stream": ("stream |= encode_block(padded[r, w0:w0 + 3]) << (5 * j)",
+                         "stream |= encode_block(padded[r, w0:w0 + 3]) << (5 * (31 - j))"),
+}
+
+
+def fresh_module(path, name, patch=None):
+    src = open(path).read()
+    if patch:
+        assert patch[0] in src, patch[0]
+        src = src.replace(patch[0], patch[1])
+    mod = types.ModuleType(name)
+    exec(compile(src, path, "exec"), mod.__dict__)
+    return mod
+
+
+def test_t3_copy_passes_every_pin():
+    t3 = fresh_module(T3_PATH, "tern3_ref_copy")
+    for pin in P.T3_PINS:
+        pin(t3)
+
+
+@pytest.mark.parametrize("name", sorted(T3_MUTANTS))
+def test_t3_planted_mistake_is_caught(name):
+    t3 = fresh_module(T3_PATH, "tern3_ref_planted", T3_MUTANTS[name])
+    caught = []
+    for pin in P.T3_PINS:
+        try:
+            pin(t3)
+        except (AssertionError, ValueError, OverflowError):
+            caught.append(pin.__name__)
+    assert caught, f"{name} passed every pin"

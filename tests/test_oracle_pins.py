@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import act_ref, sherry_ref, tern2_ref
+from oracle import act_ref, sherry_ref, tern2_ref, tern3_ref
 from tests import oracle_pins as P
 
 
@@ -121,3 +121,8 @@ def test_accumulator_bound_at_largest_shape():
 @pytest.mark.parametrize("pin", P.ACT_PINS, ids=lambda f: f.__name__)
 def test_act_pin(pin):
     pin(act_ref)
+
+
+@pytest.mark.parametrize("pin", P.T3_PINS, ids=lambda f: f.__name__)
+def test_t3_pin(pin):
+    pin(tern3_ref)
