@@ -175,7 +175,7 @@ sherry_status sherry_gemv_plan(const sherry_gemv_problem* probs /* HOST */, int3
                                size_t plan_bytes);
 
 /* Launch a planned grouped GEMV (a plan from sherry_gemv_plan or
- * tern2_gemv_plan): `plan_host` is the host plan, `plan_dev` a device copy of
+ * tern2_gemv_plan or tern3_gemv_plan): `plan_host` is the host plan, `plan_dev` a device copy of
  * the same bytes.  Returns SHERRY_EINVAL if the host plan header is malformed.
  * The device copy and every buffer named by the plan must stay alive until
  * the kernel completes. */
@@ -268,6 +268,35 @@ sherry_status tern2_gemm(const uint32_t* codes, const void* w_scales, sherry_dty
                          int64_t k, const void* x, sherry_dtype x_dt, int64_t m, int64_t ldx,
                          const float* x_scales, int32_t* acc, void* y, sherry_dtype y_dt, int64_t ldy,
                          hipStream_t stream);
+
+/* ---- 1.67-bit comparator (same paper, Figure 2 caption, middle: three
+ * ternary weights packed into five bits, "3-way patterns"; Abstract: the
+ * irregular 1.67-bit packing) ----
+ * Layout (a reading; the pages give none): a code holds three consecutive
+ * weights of a row, c = (t0 + 1) + 3 (t1 + 1) + 9 (t2 + 1) (0..26); 32 codes
+ * (96 weights) form a group of 5 words in the LSB-first stream of the Sherry
+ * layout above, rows are zero-padded to G3 = ceil(k / 96) groups and stored
+ * in its two-part row layout (words 0-3 of group g at 4g, word 4 at
+ * 4 G3 + g).  k % 128 == 0.  Scales and epilogues as the Sherry entry points. */
+size_t tern3_packed_bytes(int64_t n, int64_t k); /* n * ceil(k / 96) * 20, 0 if invalid */
+
+/* Encode a dense int8 matrix t into 1.67-bit codes (values taken by sign:
+ * negative -1, zero 0, positive +1).  Same argument rules as tern2_encode. */
+sherry_status tern3_encode(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint32_t* codes,
+                           hipStream_t stream);
+
+/* Same contract as sherry_gemv with I8 x, on 1.67-bit codes. */
+sherry_status tern3_gemv(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n,
+                         int64_t k, const void* x, sherry_dtype x_dt, const float* x_scale,
+                         int32_t* acc, void* y, sherry_dtype y_dt, hipStream_t stream);
+
+/* Plan size and plan for a grouped 1.67-bit GEMV (x_dt I8), launched with
+ * sherry_gemv_grouped; same contract as sherry_gemv_plan_bytes /
+ * sherry_gemv_plan (tile rows follow this format's row length). */
+size_t tern3_gemv_plan_bytes(const sherry_gemv_problem* probs /* HOST */, int32_t count);
+sherry_status tern3_gemv_plan(const sherry_gemv_problem* probs /* HOST */, int32_t count,
+                              sherry_dtype s_dt, sherry_dtype x_dt, sherry_dtype y_dt, void* plan,
+                              size_t plan_bytes);
 
 #ifdef __cplusplus
 }

@@ -168,6 +168,31 @@ def test_gemv_quant_validation(lib):
     assert call(k=8192, x_dt=F32, acc=None) == EDEVICE
 
 
+def test_tern3_sizes_and_validation(lib):
+    assert lib.tern3_packed_bytes(1, 2048) == 22 * 20
+    assert lib.tern3_packed_bytes(3, 8192) == 3 * 86 * 20
+    assert lib.tern3_packed_bytes(2, 128) == 2 * 2 * 20
+    assert lib.tern3_packed_bytes(2, 100) == 0
+    f = lib.tern3_encode
+    assert f(None, 4, 128, 128, A, None) == EINVAL
+    assert f(A, 4, 96, 96, A, None) == ESHAPE
+    assert f(A, 4, 128, 120, A, None) == ESHAPE
+    assert f(A + 8, 4, 128, 128, A, None) == EALIGN
+    assert f(A, 4, 128, 128, A, None) == EDEVICE
+    assert gemv(lib, fn="tern3_gemv", x_dt=BF16, acc=None, y_dt=F32) == EDTYPE
+    assert gemv(lib, fn="tern3_gemv") == EDEVICE
+    from ultra_bit_weight_amd.sherry import GemvProblem
+    arr = (GemvProblem * 2)()
+    arr[0] = GemvProblem(A, A, 1024, 2048, A, None, None, A)  # 22 groups: 32 lanes, 8 rows per iteration
+    arr[1] = GemvProblem(A, A, 300, 8192, A, None, None, A)   # 86 groups: 64 lanes, 4 rows per iteration
+    nbytes = lib.tern3_gemv_plan_bytes(arr, 2)
+    assert nbytes == 64 + 64 * 2 + 8 * (4 + 3)
+    buf = ctypes.create_string_buffer(nbytes + 8)
+    base = (ctypes.addressof(buf) + 7) // 8 * 8
+    assert lib.tern3_gemv_plan(arr, 2, F16, I8, F16, base, nbytes) == OK
+    assert int.from_bytes(ctypes.string_at(base + 12, 4), "little") == 7
+
+
 def test_decode_validation(lib):
     f = lib.sherry_decode
     assert f(None, 4, 128, A, 128, None) == EINVAL

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import synth
-from oracle import act_ref, sherry_ref, tern2_ref
+from oracle import act_ref, sherry_ref, tern2_ref, tern3_ref
 
 pytestmark = pytest.mark.gpu
 
@@ -679,3 +679,51 @@ def test_gemv_quant_zero_token(gpu_lib):
                                     torch.float32, want_acc=True, want_scale=True)
     torch.cuda.synchronize()
     assert sx.item() == 1.0 and not acc.any().item() and not y.any().item()
+
+
+# --------------------------------------------------- 1.67-bit comparator ---
+
+@pytest.mark.parametrize("n,k", [(1, 128), (37, 640), (256, 2048), (64, 8192), (40, 3072), (300, 2048)])
+def test_tern3_encode_and_gemv(gpu_lib, n, k):
+    """GPU encode equals the oracle's words; the batch-1 product equals the
+    oracle's sums and outputs bit for bit (22- and 86-group classes and the
+    generic walk)."""
+    say(f"tern3 n={n} k={k}")
+    g = synth.rng(5 * n + k)
+    t = synth.ternary_dense(n, k, g)
+    codes = gpu_lib.tern3_encode(dev(t))
+    torch.cuda.synchronize()
+    ref_words = tern3_ref.pack(t)
+    assert np.array_equal(host_words(codes), ref_words)
+    sw = synth.row_scales(n, g, np.float16)
+    xq, sx, _ = synth.act_absmax_int8(1, k, g)
+    acc, y = gpu_lib.tern3_gemv(codes, dev(sw), dev(xq[0]), dev(sx), torch.float16, want_acc=True)
+    torch.cuda.synchronize()
+    ra, ry = tern3_ref.gemv_i8(ref_words, sw, n, k, xq[0], sx[0], np.float16)
+    assert np.array_equal(acc.cpu().numpy(), ra)
+    assert np.array_equal(y.cpu().numpy().view(np.uint16), ry.view(np.uint16))
+
+
+def test_tern3_grouped(gpu_lib):
+    """Grouped 1.67-bit products over ragged problems of every class (22 and
+    86 groups, generic), every output checked against the oracle."""
+    say("tern3 grouped")
+    g = synth.rng(7373)
+    shapes = [(2048, 2048), (512, 2048), (300, 8192), (65, 1024), (17, 2048)]
+    probs, refs = [], []
+    for n, k in shapes:
+        t = synth.ternary_dense(n, k, g)
+        sw = synth.row_scales(n, g, np.float16)
+        xq, sx, _ = synth.act_absmax_int8(1, k, g)
+        words = tern3_ref.pack(t)
+        refs.append(tern3_ref.gemv_i8(words, sw, n, k, xq[0], sx[0], np.float16))
+        probs.append(dict(codes=words_dev(words), scales=dev(sw), x=dev(xq[0]), x_scale=dev(sx),
+                          acc=torch.empty(n, dtype=torch.int32, device=DEV),
+                          y=torch.empty(n, dtype=torch.float16, device=DEV)))
+    grouped = gpu_lib.GroupedGemv(probs, tern3=True)
+    assert grouped.n_tiles == 8 + 2 + 3 + 1 + 1
+    grouped()
+    torch.cuda.synchronize()
+    for p, (ra, ry) in zip(probs, refs):
+        assert np.array_equal(p["acc"].cpu().numpy(), ra)
+        assert np.array_equal(p["y"].cpu().numpy().view(np.uint16), ry.view(np.uint16))

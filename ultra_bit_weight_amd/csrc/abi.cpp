@@ -63,7 +63,7 @@ sherry_status check_device() {
 
 sherry_status launched(hipError_t e) { return e == hipSuccess ? SHERRY_OK : SHERRY_ELAUNCH; }
 
-// Shared validation of a batch-1 product (both formats).
+// Shared validation of a batch-1 product (every format).
 sherry_status check_gemv(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,
                          const void* x, sherry_dtype x_dt, const float* x_scale, const int32_t* acc, const void* y,
                          sherry_dtype y_dt, bool allow_bf16) {
@@ -83,8 +83,8 @@ sherry_status check_gemv(const uint32_t* codes, const void* w_scales, sherry_dty
   return SHERRY_OK;
 }
 
-GemvDesc make_desc(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,
-                   const void* x, const float* x_scale, int32_t* acc, void* y, sherry_dtype y_dt) {
+GemvDesc make_desc(int32_t format, const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n,
+                   int64_t k, const void* x, const float* x_scale, int32_t* acc, void* y, sherry_dtype y_dt) {
   GemvDesc d;
   d.codes = codes;
   d.w_scales = w_scales;
@@ -95,7 +95,7 @@ GemvDesc make_desc(const uint32_t* codes, const void* w_scales, sherry_dtype s_d
   d.n = static_cast<int32_t>(n);
   d.k = static_cast<int32_t>(k);
   d.flags = (s_dt == SHERRY_F16 ? kFlagScaleF16 : 0) | (y && y_dt == SHERRY_F16 ? kFlagYF16 : 0);
-  d.kclass = kclass_of(k);
+  d.kclass = format == kFmtTern3 ? kclass_of_t3(k) : kclass_of(k);
   return d;
 }
 
@@ -106,7 +106,7 @@ sherry_status gemv_impl(int32_t format, const uint32_t* codes, const void* w_sca
                                    format == kFmtSherry))
     return s;
   if (sherry_status s = check_device()) return s;
-  const GemvDesc d = make_desc(codes, w_scales, s_dt, n, k, x, x_scale, acc, y, y_dt);
+  const GemvDesc d = make_desc(format, codes, w_scales, s_dt, n, k, x, x_scale, acc, y, y_dt);
   return launched(launch_gemv(d, x_dt == SHERRY_BF16, format, stream));
 }
 
@@ -129,7 +129,7 @@ sherry_status gemv_quant_impl(int32_t format, const uint32_t* codes, const void*
       (acc && !aligned(acc, 4)) || (x_scale_out && !aligned(x_scale_out, 4)) || (y && !aligned(y, dt_size(y_dt))))
     return SHERRY_EALIGN;
   if (sherry_status s = check_device()) return s;
-  const GemvDesc d = make_desc(codes, w_scales, s_dt, n, k, x, nullptr, acc, y, y_dt);
+  const GemvDesc d = make_desc(format, codes, w_scales, s_dt, n, k, x, nullptr, acc, y, y_dt);
   return launched(launch_gemv_xq(d, dt, x_scale_out, format, stream));
 }
 
@@ -273,24 +273,25 @@ sherry_status gemm_plan_impl(int32_t format, const sherry_gemm_problem* probs, i
 // Grouped plan: header | GemvDesc[count] | PlanTile[n_tiles].  Tile rows
 // depend on the k class and, at k = 3072, on the x type; the int8 tiling
 // has at least as many tiles, so plan sizes are computed for it.
-int64_t tile_rows_for(const sherry_gemv_problem& p, bool bf16) {
-  return static_cast<int64_t>(rows_per_iter(kclass_of(p.k), bf16)) * kGroupedIters;
+int64_t tile_rows_for(const sherry_gemv_problem& p, bool bf16, int32_t format) {
+  const int32_t kc = format == kFmtTern3 ? kclass_of_t3(p.k) : kclass_of(p.k);
+  return static_cast<int64_t>(rows_per_iter(kc, bf16)) * kGroupedIters;
 }
 
-int64_t plan_tiles(const sherry_gemv_problem* probs, int32_t count, bool bf16) {
+int64_t plan_tiles(const sherry_gemv_problem* probs, int32_t count, bool bf16, int32_t format) {
   int64_t tiles = 0;
   for (int32_t i = 0; i < count; ++i) {
-    const int64_t rows = tile_rows_for(probs[i], bf16);
+    const int64_t rows = tile_rows_for(probs[i], bf16, format);
     tiles += (probs[i].n + rows - 1) / rows;
   }
   return tiles;
 }
 
-size_t plan_bytes_impl(const sherry_gemv_problem* probs, int32_t count) {
+size_t plan_bytes_impl(const sherry_gemv_problem* probs, int32_t count, int32_t format) {
   if (!probs || count <= 0) return 0;
   for (int32_t i = 0; i < count; ++i)
     if (check_nk(probs[i].n, probs[i].k) != SHERRY_OK) return 0;
-  const int64_t tiles = plan_tiles(probs, count, false);
+  const int64_t tiles = plan_tiles(probs, count, false, format);
   if (tiles > kMaxDim) return 0;
   return sizeof(PlanHeader) + sizeof(GemvDesc) * static_cast<size_t>(count) + sizeof(PlanTile) * tiles;
 }
@@ -304,7 +305,7 @@ sherry_status plan_impl(int32_t format, const sherry_gemv_problem* probs, int32_
                                      format == kFmtSherry))
       return s;
   }
-  const size_t need = plan_bytes_impl(probs, count);
+  const size_t need = plan_bytes_impl(probs, count, format);
   if (need == 0) return SHERRY_ESHAPE;
   if (plan_bytes < need) return SHERRY_EINVAL;
   if (!aligned(plan, 8)) return SHERRY_EALIGN;
@@ -315,7 +316,7 @@ sherry_status plan_impl(int32_t format, const sherry_gemv_problem* probs, int32_
   h.version = kPlanVersion;
   h.count = count;
   const bool bf16 = x_dt == SHERRY_BF16;
-  h.n_tiles = static_cast<int32_t>(plan_tiles(probs, count, bf16));
+  h.n_tiles = static_cast<int32_t>(plan_tiles(probs, count, bf16, format));
   h.s_dt = s_dt;
   h.x_dt = x_dt;
   h.y_dt = y_dt;
@@ -328,7 +329,7 @@ sherry_status plan_impl(int32_t format, const sherry_gemv_problem* probs, int32_
   PlanTile* tiles = reinterpret_cast<PlanTile*>(descs + count);
   for (int32_t i = 0; i < count; ++i) {
     const sherry_gemv_problem& p = probs[i];
-    descs[i] = make_desc(p.codes, p.w_scales, s_dt, p.n, p.k, p.x, p.x_scale, p.acc, p.y, y_dt);
+    descs[i] = make_desc(format, p.codes, p.w_scales, s_dt, p.n, p.k, p.x, p.x_scale, p.acc, p.y, y_dt);
   }
   // Tiles of the longest rows first: the workgroups are dispatched in tile
   // order, so the large tiles start early and the small ones fill the tail.
@@ -338,7 +339,7 @@ sherry_status plan_impl(int32_t format, const sherry_gemv_problem* probs, int32_
   int64_t t = 0;
   for (const int32_t i : order) {
     const sherry_gemv_problem& p = probs[i];
-    const int64_t rows = tile_rows_for(p, bf16);
+    const int64_t rows = tile_rows_for(p, bf16, format);
     for (int64_t r0 = 0; r0 < p.n; r0 += rows) tiles[t++] = PlanTile{i, static_cast<int32_t>(r0)};
   }
   return SHERRY_OK;
@@ -423,7 +424,7 @@ sherry_status sherry_gemv(const uint32_t* codes, const void* w_scales, sherry_dt
 }
 
 size_t sherry_gemv_plan_bytes(const sherry_gemv_problem* probs, int32_t count) {
-  return plan_bytes_impl(probs, count);
+  return plan_bytes_impl(probs, count, kFmtSherry);
 }
 
 sherry_status sherry_gemv_plan(const sherry_gemv_problem* probs, int32_t count, sherry_dtype s_dt,
@@ -437,7 +438,7 @@ sherry_status sherry_gemv_grouped(const void* plan_host, const void* plan_dev, h
   PlanHeader h;
   std::memcpy(&h, plan_host, sizeof(h));
   if (h.magic != kPlanMagic || h.version != kPlanVersion || h.count <= 0 || h.n_tiles < 0 ||
-      (h.format != kFmtSherry && h.format != kFmtTern2))
+      (h.format != kFmtSherry && h.format != kFmtTern2 && h.format != kFmtTern3))
     return SHERRY_EINVAL;
   if (sherry_status s = check_device()) return s;
   return launched(launch_gemv_grouped(&h, plan_dev, stream));
@@ -498,6 +499,35 @@ sherry_status tern2_gemv(const uint32_t* codes, const void* w_scales, sherry_dty
 sherry_status tern2_gemv_plan(const sherry_gemv_problem* probs, int32_t count, sherry_dtype s_dt,
                               sherry_dtype x_dt, sherry_dtype y_dt, void* plan, size_t plan_bytes) {
   return plan_impl(kFmtTern2, probs, count, s_dt, x_dt, y_dt, plan, plan_bytes);
+}
+
+size_t tern3_packed_bytes(int64_t n, int64_t k) {
+  if (check_nk(n, k) != SHERRY_OK) return 0;
+  return static_cast<size_t>(n) * static_cast<size_t>((k + 95) / 96) * 20;
+}
+
+sherry_status tern3_encode(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint32_t* codes, hipStream_t stream) {
+  if (!t || !codes) return SHERRY_EINVAL;
+  if (sherry_status s = check_nk(n, k)) return s;
+  if (ldt < k || ldt > std::numeric_limits<int64_t>::max() / n) return SHERRY_ESHAPE;
+  if (!aligned(t, 16) || ldt % 16 != 0 || !aligned(codes, 4)) return SHERRY_EALIGN;
+  if (sherry_status s = check_device()) return s;
+  return launched(launch_tern3_encode(t, n, k, ldt, codes, stream));
+}
+
+sherry_status tern3_gemv(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,
+                         const void* x, sherry_dtype x_dt, const float* x_scale, int32_t* acc, void* y,
+                         sherry_dtype y_dt, hipStream_t stream) {
+  return gemv_impl(kFmtTern3, codes, w_scales, s_dt, n, k, x, x_dt, x_scale, acc, y, y_dt, stream);
+}
+
+size_t tern3_gemv_plan_bytes(const sherry_gemv_problem* probs, int32_t count) {
+  return plan_bytes_impl(probs, count, kFmtTern3);
+}
+
+sherry_status tern3_gemv_plan(const sherry_gemv_problem* probs, int32_t count, sherry_dtype s_dt,
+                              sherry_dtype x_dt, sherry_dtype y_dt, void* plan, size_t plan_bytes) {
+  return plan_impl(kFmtTern3, probs, count, s_dt, x_dt, y_dt, plan, plan_bytes);
 }
 
 sherry_status tern2_gemm(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,

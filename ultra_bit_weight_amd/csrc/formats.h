@@ -27,6 +27,7 @@ namespace sherry {
 
 struct Sherry3of4 {
   static constexpr int kWords = kGroupWords;
+  static constexpr int kGroupW = kGroupWeights;  // weights per group
   static constexpr bool kTableDecode = true;  // decoding reads LDS
   static constexpr int kPairEntries = 1024;  // GEMV table: two codes per entry
   __device__ static void init_table(uint32_t* tab, int t) {
@@ -118,6 +119,7 @@ struct Sherry3of4 {
 
 struct Tern2 {
   static constexpr int kWords = 8;  // 128 weights * 2 bits
+  static constexpr int kGroupW = kGroupWeights;
   static constexpr bool kTableDecode = false;
   static constexpr int kPairEntries = 1;
   __device__ static void init_table(uint32_t*, int) {}
@@ -181,5 +183,32 @@ struct Tern2 {
     w[1] = c[1];
   }
 };
+
+// Tern3: the 1.67-bit comparator, three ternary weights per 5-bit code
+// (base 3: c = (t0 + 1) + 3 (t1 + 1) + 9 (t2 + 1); same paper, Figure 2
+// caption, middle), 32 codes per group of 96 weights in the stream and
+// two-part row layout of Sherry3of4, rows zero-padded to whole groups.  A
+// code expands to a dword of three int8 weights and a zero byte, so the
+// code extraction, tables and GEMV of Sherry3of4 serve it unchanged; only the
+// table differs, and x is taken 3 bytes per code (repacked per lane).
+__device__ __forceinline__ uint32_t decode_t3_i8x3(uint32_t c) {
+  if (c >= 27) return 0u;  // not a code
+  const uint32_t t0 = c % 3u, t1 = (c / 3u) % 3u, t2 = c / 9u;  // digit 0, 1, 2 = weight -1, 0, +1
+  auto b = [](uint32_t d) { return d == 0u ? 0xFFu : (d == 1u ? 0x00u : 0x01u); };
+  return b(t0) | (b(t1) << 8) | (b(t2) << 16);
+}
+
+struct Tern3 : Sherry3of4 {
+  static constexpr int kGroupW = 96;
+  __device__ static void init_table(uint32_t* tab, int t) {
+    if (t < 32) tab[t] = decode_t3_i8x3(static_cast<uint32_t>(t));
+  }
+};
+
+// Groups per row of a format (Tern3 pads rows to whole groups).
+template <class Fmt>
+__host__ __device__ constexpr int groups_of(int64_t k) {
+  return static_cast<int>((k + Fmt::kGroupW - 1) / Fmt::kGroupW);
+}
 
 }  // namespace sherry

@@ -65,6 +65,44 @@ struct XQuant {
   float* wmax;
 };
 
+// The 32 x dwords a lane multiplies with group g's 32 decoded dwords: for
+// 128-weight groups the group's 128 bytes as they are; for 96-weight groups
+// (three weights per code) bytes 3j .. 3j + 2 in dword j, top byte zero.
+// Bytes at or past k read as zero.
+template <class Fmt>
+__device__ __forceinline__ void load_x_group(const void* x, int k, int g, uint32_t* xr) {
+  const int8_t* xb = static_cast<const int8_t*>(x);
+  if constexpr (Fmt::kGroupW == 128) {
+    const SHERRY_GLOBAL u32x4_t* xp = gmem(reinterpret_cast<const u32x4_t*>(xb + static_cast<int64_t>(g) * 128));
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const u32x4_t v = xp[q];
+      xr[4 * q + 0] = v.x;
+      xr[4 * q + 1] = v.y;
+      xr[4 * q + 2] = v.z;
+      xr[4 * q + 3] = v.w;
+    }
+  } else {
+    static_assert(Fmt::kGroupW == 96, "x layout of the format");
+    const int base = 96 * g;
+    const SHERRY_GLOBAL u32x4_t* xp = gmem(reinterpret_cast<const u32x4_t*>(xb + base));
+    uint32_t raw[24];
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {
+      const u32x4_t v = base + 16 * q < k ? xp[q] : u32x4_t{0u, 0u, 0u, 0u};
+      raw[4 * q + 0] = v.x;
+      raw[4 * q + 1] = v.y;
+      raw[4 * q + 2] = v.z;
+      raw[4 * q + 3] = v.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const int i = (3 * j) >> 2;
+      xr[j] = __builtin_amdgcn_alignbyte(raw[i + 1 < 24 ? i + 1 : 23], raw[i], (3 * j) & 3) & 0x00FFFFFFu;
+    }
+  }
+}
+
 template <class Fmt, int L, int GPL, int GR = GPL * L, bool XQ = false>
 __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, int row_end, uint32_t* tab32,
                                              uint2* tab, int32_t* out, XQuant xq = XQuant{}) {
@@ -84,19 +122,22 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
   auto load_x = [&]() {
 #pragma unroll
     for (int t = 0; t < GPL; ++t) {
+      if constexpr (XQ) {
+        static_assert(Fmt::kGroupW == 128, "in-kernel quantization: 128-weight groups");
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        u32x4_t v;
-        if constexpr (XQ)
-          v = reinterpret_cast<const u32x4_t*>(xq.xl + min(t * L + lp, G - 1) * kGroupWeights)[q];
-        else
-          v = gmem(reinterpret_cast<const u32x4_t*>(static_cast<const int8_t*>(d.x) +
-                                                    static_cast<int64_t>(min(t * L + lp, G - 1)) * kGroupWeights))[q];
-        if (G < GPL * L && t * L + lp >= G) v = u32x4_t{0u, 0u, 0u, 0u};
-        xr[t][4 * q + 0] = v.x;
-        xr[t][4 * q + 1] = v.y;
-        xr[t][4 * q + 2] = v.z;
-        xr[t][4 * q + 3] = v.w;
+        for (int q = 0; q < 8; ++q) {
+          const u32x4_t v = reinterpret_cast<const u32x4_t*>(xq.xl + min(t * L + lp, G - 1) * kGroupWeights)[q];
+          xr[t][4 * q + 0] = v.x;
+          xr[t][4 * q + 1] = v.y;
+          xr[t][4 * q + 2] = v.z;
+          xr[t][4 * q + 3] = v.w;
+        }
+      } else {
+        load_x_group<Fmt>(d.x, d.k, min(t * L + lp, G - 1), xr[t]);
+      }
+      if (G < GPL * L && t * L + lp >= G) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) xr[t][j] = 0u;
       }
     }
   };
@@ -134,21 +175,22 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
     const int acc = reduce_add_i32<L>(sum);
     if (lp == 0 && row < row_end) out[row - row_begin] = acc;
   };
-  uint32_t ring[kRing][GPL][NW];
+  constexpr int NR = GPL > 1 ? 2 : kRing;  // several groups per lane: two buffers (registers)
+  uint32_t ring[NR][GPL][NW];
   const int r0 = row_begin + wave * RPW + rs;
 #pragma unroll
-  for (int b = 0; b + 1 < kRing; ++b) fetch(ring[b], r0 + b * RPI);
+  for (int b = 0; b + 1 < NR; ++b) fetch(ring[b], r0 + b * RPI);
   if constexpr (XQ) {
     quantize_x_lds(d, xq.dt, xq.xl, xq.sx, xq.wmax);
     load_x();
   }
   init_tables<Fmt>(tab32, tab);
-  for (int base = row_begin, r = r0; base < row_end; base += kRing * RPI, r += kRing * RPI) {
-    // all kRing steps run; rows past the tile end are clamped loads whose
+  for (int base = row_begin, r = r0; base < row_end; base += NR * RPI, r += NR * RPI) {
+    // all NR steps run; rows past the tile end are clamped loads whose
     // results are never stored (no branch inside the ring)
 #pragma unroll
-    for (int b = 0; b < kRing; ++b) {
-      fetch(ring[(b + kRing - 1) % kRing], r + (b + kRing - 1) * RPI);
+    for (int b = 0; b < NR; ++b) {
+      fetch(ring[(b + NR - 1) % NR], r + (b + NR - 1) * RPI);
       step(ring[b], r + b * RPI);
     }
   }
@@ -164,13 +206,25 @@ __device__ __forceinline__ void gemv_i8_rows_generic(const GemvDesc& d, int row_
   init_tables<Fmt>(tab32, tab);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  const int G = d.k / kGroupWeights;
+  const int G = groups_of<Fmt>(d.k);
   const int8_t* x = static_cast<const int8_t*>(d.x);
   for (int r = row_begin + wave; r < row_end; r += kGemvThreads / kWave) {
     int acc = 0;
     for (int g = lane; g < G; g += kWave) {
       uint32_t w[NW];
       Fmt::load(w, d.codes + static_cast<int64_t>(r) * (G * NW), G, g);
+      if constexpr (Fmt::kGroupW != 128) {  // three weights per code
+        uint32_t xv[32];
+        load_x_group<Fmt>(d.x, d.k, g, xv);
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+          const uint2 v = kPairMask != 0 ? Fmt::i8x8(w, p, tab)
+                                         : make_uint2(Fmt::i8x4(w, 2 * p, tab32), Fmt::i8x4(w, 2 * p + 1, tab32));
+          acc = __builtin_amdgcn_sdot4(static_cast<int>(v.x), static_cast<int>(xv[2 * p]), acc, false);
+          acc = __builtin_amdgcn_sdot4(static_cast<int>(v.y), static_cast<int>(xv[2 * p + 1]), acc, false);
+        }
+        continue;
+      }
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const u32x4_t v = xq.xl ? reinterpret_cast<const u32x4_t*>(xq.xl + g * kGroupWeights)[q]
@@ -430,6 +484,8 @@ __device__ __forceinline__ int tile_rows_of(int32_t kc, bool bf16) {
     case k4096: lanes = 32; break;
     case k8192: lanes = 64; break;
     case k3072: lanes = bf16 ? 8 : 32; break;
+    case kT3k2048: lanes = 32; break;
+    case kT3k8192: lanes = 64; break;
     default: lanes = 64; break;
   }
   return (kGemvThreads / kWave) * (kWave / lanes) * kGroupedIters;
@@ -448,7 +504,13 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_i8_grouped_kernel(const cha
   const GemvDesc d = descs[tl.prob];
   const int row0 = tl.row0;
   const int row1 = min(row0 + tile_rows_of(d.kclass, false), d.n);
-  switch (d.kclass) {
+  if constexpr (Fmt::kGroupW != 128) {
+    switch (d.kclass) {
+      case kT3k2048: gemv_i8_rows<Fmt, 32, 1, 22>(d, row0, row1, tab32, tab, res); break;
+      case kT3k8192: gemv_i8_rows<Fmt, 64, 2, 86>(d, row0, row1, tab32, tab, res); break;
+      default: gemv_i8_rows_generic<Fmt>(d, row0, row1, tab32, tab, res); break;
+    }
+  } else switch (d.kclass) {
     case k1024: gemv_i8_rows<Fmt, 8, 1>(d, row0, row1, tab32, tab, res); break;
     case k2048: gemv_i8_rows<Fmt, 16, 1>(d, row0, row1, tab32, tab, res); break;
     case k4096: gemv_i8_rows<Fmt, 32, 1>(d, row0, row1, tab32, tab, res); break;
@@ -493,6 +555,48 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_bf16_grouped_kernel(const c
   finalize_bf16(d, row0, row1, res);
 }
 
+// ---------------------------------------------------------- tern3 encode ---
+// One thread per (row, group): the group's 96 weights (zero past k; values
+// taken by sign) -> 32 base-3 codes -> the 5-word stream, words 0-3 at 4g and
+// word 4 at 4G + g of the row.
+__global__ __launch_bounds__(256) void tern3_encode_kernel(const int8_t* t, int64_t n, int64_t k, int64_t ldt,
+                                                           uint32_t* codes) {
+  const int64_t G = (k + 95) / 96;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= n * G) return;
+  const int64_t r = idx / G;
+  const int64_t g = idx % G;
+  uint32_t raw[24];
+  const int64_t base = 96 * g;
+#pragma unroll
+  for (int q = 0; q < 6; ++q) {
+    const u32x4_t v = base + 16 * q < k ? *gmem(reinterpret_cast<const u32x4_t*>(t + r * ldt + base + 16 * q))
+                                        : u32x4_t{0u, 0u, 0u, 0u};
+    raw[4 * q + 0] = v.x;
+    raw[4 * q + 1] = v.y;
+    raw[4 * q + 2] = v.z;
+    raw[4 * q + 3] = v.w;
+  }
+  uint32_t w[5] = {0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 2; i >= 0; --i) {
+      const int b = 3 * j + i;
+      const int8_t v = static_cast<int8_t>((raw[b >> 2] >> (8 * (b & 3))) & 0xFFu);
+      c = 3u * c + (v < 0 ? 0u : (v == 0 ? 1u : 2u));
+    }
+    const int bit = 5 * j;
+    w[bit >> 5] |= c << (bit & 31);
+    if ((bit & 31) > 27) w[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
+  }
+  uint32_t* row = codes + r * 5 * G;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) gmem(row)[4 * g + i] = w[i];
+  gmem(row)[4 * G + g] = w[4];
+}
+
 // ---------------------------------------------------------- tern2 encode ---
 // One thread per output word: 16 int8 weights -> 2-bit fields at 8p + 2q.
 __global__ __launch_bounds__(256) void tern2_encode_kernel(const int8_t* t, int64_t n, int64_t k, int64_t ldt,
@@ -535,13 +639,21 @@ void launch_i8(const GemvDesc& d, unsigned grid, int tile_rows, hipStream_t stre
 
 template <class Fmt>
 void launch_i8_class(const GemvDesc& d, unsigned grid, int tile_rows, hipStream_t stream) {
-  switch (d.kclass) {
-    case k1024: launch_i8<Fmt, 8, 1>(d, grid, tile_rows, stream); break;
-    case k2048: launch_i8<Fmt, 16, 1>(d, grid, tile_rows, stream); break;
-    case k4096: launch_i8<Fmt, 32, 1>(d, grid, tile_rows, stream); break;
-    case k8192: launch_i8<Fmt, 64, 1>(d, grid, tile_rows, stream); break;
-    case k3072: launch_i8<Fmt, 32, 1, 24>(d, grid, tile_rows, stream); break;
-    default: launch_i8<Fmt, 0, 1>(d, grid, tile_rows, stream); break;
+  if constexpr (Fmt::kGroupW != 128) {  // 1.67-bit rows: 22 or 86 groups, else the generic walk
+    switch (d.kclass) {
+      case kT3k2048: launch_i8<Fmt, 32, 1, 22>(d, grid, tile_rows, stream); break;
+      case kT3k8192: launch_i8<Fmt, 64, 2, 86>(d, grid, tile_rows, stream); break;
+      default: launch_i8<Fmt, 0, 1>(d, grid, tile_rows, stream); break;
+    }
+  } else {
+    switch (d.kclass) {
+      case k1024: launch_i8<Fmt, 8, 1>(d, grid, tile_rows, stream); break;
+      case k2048: launch_i8<Fmt, 16, 1>(d, grid, tile_rows, stream); break;
+      case k4096: launch_i8<Fmt, 32, 1>(d, grid, tile_rows, stream); break;
+      case k8192: launch_i8<Fmt, 64, 1>(d, grid, tile_rows, stream); break;
+      case k3072: launch_i8<Fmt, 32, 1, 24>(d, grid, tile_rows, stream); break;
+      default: launch_i8<Fmt, 0, 1>(d, grid, tile_rows, stream); break;
+    }
   }
 }
 
@@ -589,6 +701,8 @@ hipError_t launch_gemv(const GemvDesc& d, bool bf16_x, int32_t format, hipStream
     launch_bf16_class(d, grid, tile_rows, stream);
   else if (format == kFmtTern2)
     launch_i8_class<Tern2>(d, grid, tile_rows, stream);
+  else if (format == kFmtTern3)
+    launch_i8_class<Tern3>(d, grid, tile_rows, stream);
   else
     launch_i8_class<Sherry3of4>(d, grid, tile_rows, stream);
   return hipGetLastError();
@@ -615,8 +729,18 @@ hipError_t launch_gemv_grouped(const PlanHeader* h, const void* dev, hipStream_t
     hipLaunchKernelGGL((gemv_bf16_grouped_kernel<false>), grid, block, 0, stream, plan);
   else if (h->format == kFmtTern2)
     hipLaunchKernelGGL((gemv_i8_grouped_kernel<Tern2>), grid, block, 0, stream, plan);
+  else if (h->format == kFmtTern3)
+    hipLaunchKernelGGL((gemv_i8_grouped_kernel<Tern3>), grid, block, 0, stream, plan);
   else
     hipLaunchKernelGGL((gemv_i8_grouped_kernel<Sherry3of4>), grid, block, 0, stream, plan);
+  return hipGetLastError();
+}
+
+hipError_t launch_tern3_encode(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint32_t* codes,
+                               hipStream_t stream) {
+  const int64_t items = n * ((k + 95) / 96);
+  const unsigned grid = static_cast<unsigned>((items + 255) / 256);
+  hipLaunchKernelGGL(tern3_encode_kernel, dim3(grid), dim3(256), 0, stream, t, n, k, ldt, codes);
   return hipGetLastError();
 }
 

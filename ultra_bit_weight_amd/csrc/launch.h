@@ -10,7 +10,7 @@ namespace sherry {
 
 // Reduction-length classes with a register-resident (x-stationary) kernel.
 // L = lanes that share one row, GPL = 128-weight groups per lane (L*GPL*128 = k).
-enum KClass : int32_t { kGeneric = 0, k1024 = 1, k2048 = 2, k4096 = 3, k8192 = 4, k3072 = 5 };
+enum KClass : int32_t { kGeneric = 0, k1024 = 1, k2048 = 2, k4096 = 3, k8192 = 4, k3072 = 5, kT3k2048 = 6, kT3k8192 = 7 };
 
 inline int32_t kclass_of(int64_t k) {
   switch (k) {
@@ -22,6 +22,8 @@ inline int32_t kclass_of(int64_t k) {
     default: return kGeneric;
   }
 }
+// 1.67-bit rows (96-weight groups): 22 groups at k = 2048, 86 at k = 8192.
+inline int32_t kclass_of_t3(int64_t k) { return k == 2048 ? kT3k2048 : (k == 8192 ? kT3k8192 : kGeneric); }
 // Lanes per row for a class (64 for the generic kernel).
 // Lanes per row of a k class: one group per lane (k = 3072: 24 of 32 lanes
 // hold one), except bf16 x at k = 3072, which keeps 3 groups in each of 8.
@@ -32,6 +34,8 @@ inline int lanes_per_row(int32_t kc, bool bf16 = false) {
     case k4096: return 32;
     case k8192: return 64;
     case k3072: return bf16 ? 8 : 32;
+    case kT3k2048: return 32;
+    case kT3k8192: return 64;
     default: return 64;
   }
 }
@@ -44,7 +48,7 @@ inline int rows_per_iter(int32_t kc, bool bf16 = false) {
   return (kGemvThreads / kWave) * (kWave / lanes_per_row(kc, bf16));
 }
 
-enum Format : int32_t { kFmtSherry = 0, kFmtTern2 = 1 };
+enum Format : int32_t { kFmtSherry = 0, kFmtTern2 = 1, kFmtTern3 = 2 };
 
 
 struct PlanHeader {
@@ -161,6 +165,8 @@ constexpr int64_t kActMaxK = 8192;
 hipError_t launch_act_quant(const void* x, int dt, int64_t m, int64_t k, int64_t ldx, int8_t* q, int64_t ldq,
                             float* scales, hipStream_t stream);
 hipError_t launch_decode(const uint32_t* codes, int64_t n, int64_t k, int8_t* t, int64_t ldt, hipStream_t stream);
+hipError_t launch_tern3_encode(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint32_t* codes,
+                               hipStream_t stream);
 hipError_t launch_tern2_encode(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint32_t* codes,
                                hipStream_t stream);
 

@@ -27,6 +27,7 @@ EXPORTS = [
     "sherry_gemv_plan_bytes", "sherry_gemv_plan", "sherry_gemv_grouped", "sherry_gemm",
     "sherry_gemm_plan_bytes", "sherry_gemm_plan", "sherry_gemm_grouped",
     "tern2_packed_bytes", "tern2_encode", "tern2_gemv", "tern2_gemv_plan", "tern2_gemm", "tern2_gemm_plan",
+    "tern3_packed_bytes", "tern3_encode", "tern3_gemv", "tern3_gemv_plan_bytes", "tern3_gemv_plan",
 ]
 
 
@@ -69,6 +70,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sherry_packed_bytes.argtypes = [i64, i64]
     lib.tern2_packed_bytes.restype = sz
     lib.tern2_packed_bytes.argtypes = [i64, i64]
+    lib.tern3_packed_bytes.restype = sz
+    lib.tern3_packed_bytes.argtypes = [i64, i64]
     lib.sherry_pack.restype = i
     lib.sherry_pack.argtypes = [vp, i, i64, i64, i64, vp, vp, i, vp]
     lib.sherry_decode.restype = i
@@ -78,12 +81,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sherry_act_quant.restype = i
     lib.sherry_act_quant.argtypes = [vp, i, i64, i64, i64, vp, i64, vp, vp]
     gemv_args = [vp, vp, i, i64, i64, vp, i, vp, vp, vp, i, vp]
-    for f in (lib.sherry_gemv, lib.tern2_gemv):
+    for f in (lib.sherry_gemv, lib.tern2_gemv, lib.tern3_gemv):
         f.restype = i
         f.argtypes = gemv_args
     lib.sherry_gemv_plan_bytes.restype = sz
     lib.sherry_gemv_plan_bytes.argtypes = [ctypes.POINTER(GemvProblem), i32]
-    for f in (lib.sherry_gemv_plan, lib.tern2_gemv_plan):
+    lib.tern3_gemv_plan_bytes.restype = sz
+    lib.tern3_gemv_plan_bytes.argtypes = [ctypes.POINTER(GemvProblem), i32]
+    for f in (lib.sherry_gemv_plan, lib.tern2_gemv_plan, lib.tern3_gemv_plan):
         f.restype = i
         f.argtypes = [ctypes.POINTER(GemvProblem), i32, i, i, i, vp, sz]
     lib.sherry_gemv_grouped.restype = i
@@ -94,6 +99,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         f.argtypes = gemm_args
     lib.tern2_encode.restype = i
     lib.tern2_encode.argtypes = [vp, i64, i64, i64, vp, vp]
+    lib.tern3_encode.restype = i
+    lib.tern3_encode.argtypes = [vp, i64, i64, i64, vp, vp]
     lib.sherry_gemm_plan_bytes.restype = sz
     lib.sherry_gemm_plan_bytes.argtypes = [ctypes.POINTER(GemmProblem), i32]
     for f in (lib.sherry_gemm_plan, lib.tern2_gemm_plan):
@@ -249,6 +256,31 @@ def tern2_gemm(codes, scales, x, x_scales=None, out_dtype=torch.float16, want_ac
     return _gemm("tern2_gemm", codes, scales, x, x_scales, out_dtype, want_acc, out, acc_out)
 
 
+def tern3_packed_bytes(n: int, k: int) -> int:
+    return load().tern3_packed_bytes(n, k)
+
+
+def tern3_encode(t: torch.Tensor) -> torch.Tensor:
+    """Dense int8 ternary [n, k] -> 1.67-bit words (int32 view)."""
+    if t.dim() != 2 or t.stride(1) != 1 or not t.is_cuda or t.dtype != torch.int8:
+        raise ValueError("t must be a 2-D int8 GPU tensor with unit column stride")
+    n, k = t.shape
+    words = tern3_packed_bytes(n, k) // 4
+    if words == 0:
+        raise ValueError(f"invalid shape n={n} k={k}")
+    codes = torch.empty(words, dtype=torch.int32, device=t.device)
+    _check("tern3_encode", load().tern3_encode(t.data_ptr(), n, k, t.stride(0), codes.data_ptr(), _stream()))
+    return codes
+
+
+def tern3_gemv(codes, scales, x, x_scale=None, out_dtype=torch.float16, want_acc=False, out=None, acc_out=None):
+    n = scales.numel()
+    y = out if out is not None else (torch.empty(n, dtype=out_dtype, device=x.device) if out_dtype else None)
+    acc = acc_out if acc_out is not None else (torch.empty(n, dtype=torch.int32, device=x.device) if want_acc else None)
+    _gemv("tern3_gemv", codes, scales, x, x_scale, acc, y)
+    return acc, y
+
+
 def tern2_encode(t: torch.Tensor) -> torch.Tensor:
     """Dense int8 ternary [n, k] -> 2-bit words (int32 view) [n * k / 16]."""
     if t.dim() != 2 or t.stride(1) != 1 or not t.is_cuda or t.dtype != torch.int8:
@@ -268,7 +300,7 @@ class GroupedGemv:
     share the scale / x / y dtypes.  The plan is built once on the host and
     copied to the device; call() launches it on the current stream."""
 
-    def __init__(self, problems, tern2: bool = False):
+    def __init__(self, problems, tern2: bool = False, tern3: bool = False):
         lib = load()
         arr = (GemvProblem * len(problems))()
         self._keep = []
@@ -281,11 +313,11 @@ class GroupedGemv:
         s_dt = _DT[p0["scales"].dtype]
         x_dt = _DT[p0["x"].dtype]
         y_dt = _DT[p0["y"].dtype] if p0.get("y") is not None else F32
-        nbytes = lib.sherry_gemv_plan_bytes(arr, len(problems))
+        nbytes = (lib.tern3_gemv_plan_bytes if tern3 else lib.sherry_gemv_plan_bytes)(arr, len(problems))
         if nbytes == 0:
             raise ValueError("invalid grouped GEMV problems")
         self.host = torch.empty(nbytes, dtype=torch.uint8)
-        fn = lib.tern2_gemv_plan if tern2 else lib.sherry_gemv_plan
+        fn = lib.tern3_gemv_plan if tern3 else (lib.tern2_gemv_plan if tern2 else lib.sherry_gemv_plan)
         _check("gemv_plan", fn(arr, len(problems), s_dt, x_dt, y_dt, self.host.data_ptr(), nbytes))
         self.dev = self.host.to(p0["x"].device, non_blocking=False)
         self.n_tiles = int.from_bytes(bytes(self.host[12:16].tolist()), "little", signed=True)
