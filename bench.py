@@ -214,7 +214,7 @@ def oracle_beside(synth, max_seconds=2.0):
     import numpy as np
     from threadpoolctl import threadpool_limits
 
-    from oracle import act_ref, sherry_ref, tern2_ref
+    from oracle import act_ref, sherry_ref, tern2_ref, tern3_ref
 
     g = synth.rng(97)
     out = {}
@@ -245,6 +245,10 @@ def oracle_beside(synth, max_seconds=2.0):
         x1, s1, _ = synth.act_absmax_int8(1, k, g)
         st = timed(lambda: tern2_ref.gemv_i8(w2, sw, n, k, x1[0], s1[0], np.float16))
         out["a9_tern2_gemv_q_2048x2048"] = {"s": round(st, 4), "weights_per_s": n * k / st}
+        t3 = t[:256]
+        w3t = tern3_ref.pack(t3)
+        st3 = timed(lambda: tern3_ref.gemv_i8(w3t, sw[:256], 256, k, x1[0], s1[0], np.float16), reps_max=5)
+        out["f2_tern3_gemv_q_256x2048"] = {"s": round(st3, 4), "weights_per_s": 256 * k / st3}
         n3 = k3 = 3072
         w3 = synth.random_words(n3 * k3 // 128 * 5, g)
         sw3 = synth.row_scales(n3, g, np.float32)
@@ -365,6 +369,27 @@ def extras(torch, sherry, synth, probs_1b, codes_1b, args):
                                "frac_hbm": round(bytes2 / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     # same grouped launch on the 1.25-bit codes, for the ratio
     del g2, probs_t2, t2_codes
+    torch.cuda.empty_cache()
+
+    # 1.67-bit comparator (three weights in five bits) on the same matrices
+    t3_codes = []
+    probs_t3 = []
+    for p in probs_1b:
+        t = sherry.decode(p["codes"], p["n"], p["k"])
+        c3 = sherry.tern3_encode(t)
+        del t
+        t3_codes.append(c3)
+        q = dict(p)
+        q["codes"] = c3
+        probs_t3.append(q)
+    torch.cuda.synchronize()
+    g3 = sherry.GroupedGemv(probs_t3, tern3=True)
+    mean_ms, wall_ms = time_launches(torch, g3, args.steps, args.warmup)
+    bytes3 = R * (sum(sherry.tern3_packed_bytes(n, k) + 2 * n + k + 2 * n + 4 for _, n, k in shapes_1b))
+    out["tern3_grouped_1b"] = {"ms_per_launch": round(mean_ms, 4), "weights_per_s": weights / (mean_ms * 1e-3),
+                               "GBps": round(bytes3 / (mean_ms * 1e-3) / 1e9, 1),
+                               "frac_hbm": round(bytes3 / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del g3, probs_t3, t3_codes
     torch.cuda.empty_cache()
 
     # bf16 activations on the 3B layer (fp32 accumulation), 72 replicas
@@ -652,6 +677,9 @@ def main(argv=None):
         t2 = ex.get("tern2_grouped_1b")
         if t2:
             ex["sherry_over_tern2_speedup"] = round(t2["ms_per_launch"] / mean_ms, 3)
+        t3 = ex.get("tern3_grouped_1b")
+        if t3:
+            ex["sherry_over_tern3_speedup"] = round(t3["ms_per_launch"] / mean_ms, 3)
         line["extras"] = ex
     print(json.dumps(line), flush=True)
     return 0
