@@ -469,6 +469,24 @@ def pin_t3_layout(t3):
     diff = np.nonzero(w2 != w)[0].tolist()
     assert diff == [4 * G + 1]
     assert int(w2[4 * G + 1]) ^ int(w[4 * G + 1]) == (13 ^ 14) << 27
+    # weight 20 is t2 of code 6 of group 0, which straddles words 0 and 1
+    # (stream bits 30..34): 13 -> 22, 13 ^ 22 = 0b11011, so word 0 flips its
+    # bits 30, 31 and word 1 its bits 1, 2
+    t = np.zeros((1, k), np.int8)
+    t[0, 20] = 1
+    w3 = t3.pack(t)
+    assert np.nonzero(w3 != w)[0].tolist() == [0, 1]
+    assert int(w3[0]) ^ int(w[0]) == 3 << 30 and int(w3[1]) ^ int(w[1]) == 6
+    # K = 128: two groups, weights 128..191 padding (zeros, code 13); weight
+    # 127 is t1 of code 10 of group 1 (stream bits 50..54: word 1 of the group,
+    # stored at 4 + 1, bits 18..22), 13 -> 16
+    t = np.zeros((1, 128), np.int8)
+    w0 = t3.pack(t)
+    assert len(w0) == 10 and int(w0[8]) == int(w0[9]) == slices[4]
+    t[0, 127] = 1
+    w4 = t3.pack(t)
+    assert np.nonzero(w4 != w0)[0].tolist() == [5]
+    assert int(w4[5]) ^ int(w0[5]) == (13 ^ 16) << 18
 
 
 def pin_t3_products(t3):
