@@ -404,7 +404,14 @@ def extras(torch, sherry, synth, probs_1b, codes_1b, args):
                               "weights_per_s": w3 / (mean_ms * 1e-3),
                               "GBps": round(b3 / (mean_ms * 1e-3) / 1e9, 1),
                               "frac_hbm": round(b3 / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    del g3, probs_3b, codes_3b
+    # the same launch on the matrix cores (sherry_gemv_plan_mfma)
+    g3m = sherry.GroupedGemv(probs_3b, mfma=True)
+    mean_ms, _ = time_launches(torch, g3m, args.steps, args.warmup)
+    out["bf16_grouped_3b_mfma"] = {"replicas": R3, "ms_per_launch": round(mean_ms, 4),
+                                   "weights_per_s": w3 / (mean_ms * 1e-3),
+                                   "GBps": round(b3 / (mean_ms * 1e-3) / 1e9, 1),
+                                   "frac_hbm": round(b3 / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del g3, g3m, probs_3b, codes_3b
     torch.cuda.empty_cache()
 
     # M-token GEMM on the 1B layer: small batch (HBM-bound) and prefill (MFMA-bound)

@@ -174,6 +174,21 @@ sherry_status sherry_gemv_plan(const sherry_gemv_problem* probs /* HOST */, int3
                                sherry_dtype s_dt, sherry_dtype x_dt, sherry_dtype y_dt, void* plan,
                                size_t plan_bytes);
 
+/* The same plan for bf16 x, run on the matrix cores (v_mfma_f32_16x16x32_bf16)
+ * instead of v_dot2_f32_bf16: each lane's 8 weights and 8 x values per
+ * product sit on the diagonal of the 16 x 16 result, and the four lanes of a
+ * column (one row) add there.  At batch 1 only 16 of a product's 256 results
+ * are distinct, so its useful rate equals v_dot2's; it is an alternative
+ * kernel, not the faster default (sherry_gemv_plan is).  Same arguments,
+ * buffer size and launch as sherry_gemv_plan; x_dt must be BF16
+ * (SHERRY_EDTYPE) and every k <= 8192 (SHERRY_ESHAPE).  fp32 outputs within
+ * the bf16 tolerance of sherry_gemv; the per-row sum order is fixed, so
+ * results repeat bit for bit.  (The Sherry paper's kernel is a CPU LUT
+ * design, TL;DR and Abstract; this is a GPU counterpart.) */
+sherry_status sherry_gemv_plan_mfma(const sherry_gemv_problem* probs /* HOST */, int32_t count,
+                                    sherry_dtype s_dt, sherry_dtype x_dt, sherry_dtype y_dt, void* plan,
+                                    size_t plan_bytes);
+
 /* Launch a planned grouped GEMV (a plan from sherry_gemv_plan or
  * tern2_gemv_plan or tern3_gemv_plan): `plan_host` is the host plan, `plan_dev` a device copy of
  * the same bytes.  Returns SHERRY_EINVAL if the host plan header is malformed.

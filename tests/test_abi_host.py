@@ -251,32 +251,41 @@ def test_grouped_plan_on_host(lib):
     assert lib.sherry_gemv_grouped(None, A, None) == EINVAL
 
 
-def test_grouped_plan_k3072_tiles_by_x_type(lib):
-    """k = 3072 rows: int8 x puts one group in each of 24 of 32 lanes (8 rows
-    per iteration, 256-row tiles); bf16 x keeps 3 groups in each of 8 lanes
-    (32 rows per iteration, 1024-row tiles) and flags the plan for that
-    kernel family.  The plan size covers the int8 tiling, the larger one."""
+def test_grouped_plan_tiles_by_x_type(lib):
+    """int8 x at k = 3072 puts one group in each of 24 of 32 lanes (8 rows per
+    iteration, 256-row tiles; k = 2048: 512-row tiles); bf16 x keeps 3 groups
+    in each of 8 lanes at k = 3072 (1024-row tiles, reserved[0] set).  The
+    matrix-core plan (bf16 x, every k <= 8192) takes tiles of max(256, the
+    int8 tile) rows and sets reserved[1].  The plan size covers the int8
+    tiling, the largest."""
     from ultra_bit_weight_amd.sherry import GemvProblem
 
-    arr = (GemvProblem * 2)()
+    def header(arr, count, x_dt, y_dt, fn=lib.sherry_gemv_plan):
+        nbytes = lib.sherry_gemv_plan_bytes(arr, count)
+        buf = ctypes.create_string_buffer(nbytes + 8)
+        base = (ctypes.addressof(buf) + 7) // 8 * 8
+        st = fn(arr, count, F16, x_dt, y_dt, base, nbytes)
+        if st != OK:
+            return st
+        hdr = ctypes.string_at(base, 64)
+        return (int.from_bytes(hdr[12:16], "little"), int.from_bytes(hdr[40:48], "little"),
+                int.from_bytes(hdr[48:56], "little"))
+
+    arr = (GemvProblem * 3)()
     arr[0] = GemvProblem(A, A, 1024, 3072, A, None, None, A)
     arr[1] = GemvProblem(A, A, 300, 2048, A, None, None, A)
-    nbytes = lib.sherry_gemv_plan_bytes(arr, 2)
-    assert nbytes == 64 + 64 * 2 + 8 * (4 + 1)
-    buf = ctypes.create_string_buffer(nbytes + 8)
-    base = (ctypes.addressof(buf) + 7) // 8 * 8
-    assert lib.sherry_gemv_plan(arr, 2, F16, I8, F16, base, nbytes) == OK
-    hdr = ctypes.string_at(base, 64)
-    assert int.from_bytes(hdr[12:16], "little") == 5
-    assert int.from_bytes(hdr[40:48], "little") == 0
-    arr[0].x_scale = None
-    arr[1].x_scale = None
-    arr[0].acc = None
-    arr[1].acc = None
-    assert lib.sherry_gemv_plan(arr, 2, F16, BF16, F32, base, nbytes) == OK
-    hdr = ctypes.string_at(base, 64)
-    assert int.from_bytes(hdr[12:16], "little") == 2
-    assert int.from_bytes(hdr[40:48], "little") == 1
+    arr[2] = GemvProblem(A, A, 300, 16384, A, None, None, A)
+    assert lib.sherry_gemv_plan_bytes(arr, 2) == 64 + 64 * 2 + 8 * (4 + 1)
+    assert header(arr, 2, I8, F16) == (5, 0, 0)
+    assert header(arr, 2, I8, F16, lib.sherry_gemv_plan_mfma) == EDTYPE
+    for a in arr:
+        a.x_scale = None
+        a.acc = None
+    assert header(arr, 2, BF16, F32) == (1 + 1, 1, 0)
+    assert header(arr, 2, BF16, F32, lib.sherry_gemv_plan_mfma) == (4 + 1, 1, 1)
+    # k = 16384 (generic class, 128-row tiles): beyond the matrix-core kernel
+    assert header(arr, 3, BF16, F32) == (1 + 1 + 3, 1, 0)
+    assert header(arr, 3, BF16, F32, lib.sherry_gemv_plan_mfma) == ESHAPE
 
 
 def test_grouped_gemm_plan_on_host(lib):

@@ -163,9 +163,11 @@ def check_fp_tolerance(got, ref):
     assert np.linalg.norm(got - ref) <= 1e-4 * np.linalg.norm(ref), np.linalg.norm(got - ref) / np.linalg.norm(ref)
 
 
-@pytest.mark.parametrize("k", [128, 640, 1024, 2048, 3072, 4096, 8192])
+@pytest.mark.parametrize("k", [128, 640, 1024, 1152, 2048, 3072, 4096, 8192, 16384])
 @pytest.mark.parametrize("n", [1, 33, 512])
 def test_gemv_bf16_within_tolerance(gpu_lib, n, k):
+    """Every k class and the generic walk (k = 640, 1152, 16384); a second
+    call gives the same bits."""
     say(f"gemv_bf16 n={n} k={k}")
     g = synth.rng(n * 7 + k)
     words = synth.random_words(n * (k // 128) * 5, g)
@@ -174,8 +176,10 @@ def test_gemv_bf16_within_tolerance(gpu_lib, n, k):
     ref = sherry_ref.gemv_bf16(words, sw, n, k, xb)
     x_t = dev(xb.view(np.int16)).view(torch.bfloat16)
     _, y = gpu_lib.gemv(words_dev(words), dev(sw), x_t, None, torch.float32)
+    _, y2 = gpu_lib.gemv(words_dev(words), dev(sw), x_t, None, torch.float32)
     torch.cuda.synchronize()
     check_fp_tolerance(y.cpu().numpy(), ref)
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
 
 
 # -------------------------------------------------------------------- GEMM ---
@@ -502,9 +506,18 @@ def test_grouped_gemv_matches_single_calls_and_oracle(gpu_lib):
         assert np.array_equal(p["y"].cpu().numpy().view(np.uint16), ry.view(np.uint16))
 
 
-def test_grouped_bf16_and_tern2(gpu_lib):
-    g = synth.rng(2718)
-    shapes = [(1024, 3072), (300, 8192), (64, 2048)]
+@pytest.mark.parametrize("shapes,mfma", [
+    ([(1024, 3072), (300, 8192), (64, 2048), (1500, 1024), (77, 640), (520, 4096)], False),
+    ([(1024, 3072), (200, 16384), (64, 2048)], False),
+    ([(1024, 3072), (300, 8192), (64, 2048), (1500, 1024), (77, 640), (520, 4096), (33, 128), (300, 1152)], True),
+])
+def test_grouped_bf16(gpu_lib, shapes, mfma):
+    """VALU kernels (with and without the k = 3072 family) and the
+    matrix-core plan: one 16-row column per group of 4 lanes, P = ceil(G / 4)
+    columns per row (k = 640, 1152, 128: groups past k; 1500 and 520 rows:
+    partial tiles).  The matrix-core results repeat bit for bit."""
+    say(f"grouped bf16 mfma={mfma} {shapes}")
+    g = synth.rng(2718 + len(shapes))
     probs, refs = [], []
     for n, k in shapes:
         words = synth.random_words(n * (k // 128) * 5, g)
@@ -513,10 +526,21 @@ def test_grouped_bf16_and_tern2(gpu_lib):
         refs.append(sherry_ref.gemv_bf16(words, sw, n, k, xb))
         probs.append(dict(codes=words_dev(words), scales=dev(sw), x=dev(xb.view(np.int16)).view(torch.bfloat16),
                           y=torch.empty(n, dtype=torch.float32, device=DEV)))
-    gpu_lib.GroupedGemv(probs)()
+    grouped = gpu_lib.GroupedGemv(probs, mfma=mfma)
+    grouped()
     torch.cuda.synchronize()
+    first = [p["y"].clone() for p in probs]
     for p, r in zip(probs, refs):
         check_fp_tolerance(p["y"].cpu().numpy(), r)
+    if mfma:
+        grouped()
+        torch.cuda.synchronize()
+        for p, y0 in zip(probs, first):
+            assert torch.equal(p["y"].view(torch.int32), y0.view(torch.int32))
+
+
+def test_grouped_tern2(gpu_lib):
+    g = synth.rng(2718)
     probs2, refs2 = [], []
     for n, k in [(512, 2048), (128, 8192)]:
         t = synth.ternary_dense(n, k, g)

@@ -271,17 +271,19 @@ sherry_status gemm_plan_impl(int32_t format, const sherry_gemm_problem* probs, i
 }
 
 // Grouped plan: header | GemvDesc[count] | PlanTile[n_tiles].  Tile rows
-// depend on the k class and, at k = 3072, on the x type; the int8 tiling
-// has at least as many tiles, so plan sizes are computed for it.
-int64_t tile_rows_for(const sherry_gemv_problem& p, bool bf16, int32_t format) {
+// depend on the k class and the x type (bf16 x on the matrix cores: at
+// least 256 rows); the int8 tiling has at least as many tiles, so plan sizes
+// are computed for it.
+int64_t tile_rows_for(const sherry_gemv_problem& p, bool bf16, int32_t format, bool mfma = false) {
   const int32_t kc = format == kFmtTern3 ? kclass_of_t3(p.k) : kclass_of(p.k);
+  if (mfma) return bf16_mfma_tile_rows(kc);
   return static_cast<int64_t>(rows_per_iter(kc, bf16)) * kGroupedIters;
 }
 
-int64_t plan_tiles(const sherry_gemv_problem* probs, int32_t count, bool bf16, int32_t format) {
+int64_t plan_tiles(const sherry_gemv_problem* probs, int32_t count, bool bf16, int32_t format, bool mfma = false) {
   int64_t tiles = 0;
   for (int32_t i = 0; i < count; ++i) {
-    const int64_t rows = tile_rows_for(probs[i], bf16, format);
+    const int64_t rows = tile_rows_for(probs[i], bf16, format, mfma);
     tiles += (probs[i].n + rows - 1) / rows;
   }
   return tiles;
@@ -297,13 +299,18 @@ size_t plan_bytes_impl(const sherry_gemv_problem* probs, int32_t count, int32_t 
 }
 
 sherry_status plan_impl(int32_t format, const sherry_gemv_problem* probs, int32_t count, sherry_dtype s_dt,
-                        sherry_dtype x_dt, sherry_dtype y_dt, void* plan, size_t plan_bytes) {
+                        sherry_dtype x_dt, sherry_dtype y_dt, void* plan, size_t plan_bytes, bool mfma = false) {
   if (!probs || count <= 0 || !plan) return SHERRY_EINVAL;
   for (int32_t i = 0; i < count; ++i) {
     const sherry_gemv_problem& p = probs[i];
     if (sherry_status s = check_gemv(p.codes, p.w_scales, s_dt, p.n, p.k, p.x, x_dt, p.x_scale, p.acc, p.y, y_dt,
                                      format == kFmtSherry))
       return s;
+  }
+  if (mfma) {
+    if (x_dt != SHERRY_BF16) return SHERRY_EDTYPE;
+    for (int32_t i = 0; i < count; ++i)
+      if (probs[i].k > kBf16MfmaMaxK) return SHERRY_ESHAPE;
   }
   const size_t need = plan_bytes_impl(probs, count, format);
   if (need == 0) return SHERRY_ESHAPE;
@@ -316,7 +323,7 @@ sherry_status plan_impl(int32_t format, const sherry_gemv_problem* probs, int32_
   h.version = kPlanVersion;
   h.count = count;
   const bool bf16 = x_dt == SHERRY_BF16;
-  h.n_tiles = static_cast<int32_t>(plan_tiles(probs, count, bf16, format));
+  h.n_tiles = static_cast<int32_t>(plan_tiles(probs, count, bf16, format, mfma));
   h.s_dt = s_dt;
   h.x_dt = x_dt;
   h.y_dt = y_dt;
@@ -324,6 +331,7 @@ sherry_status plan_impl(int32_t format, const sherry_gemv_problem* probs, int32_
   h.bytes = need;
   for (int32_t i = 0; i < count; ++i)
     if (bf16 && kclass_of(probs[i].k) == k3072) h.reserved[0] = 1;  // the bf16 kernel family with 3 groups per lane
+  h.reserved[1] = mfma ? 1 : 0;
   std::memcpy(out, &h, sizeof(h));
   GemvDesc* descs = reinterpret_cast<GemvDesc*>(out + sizeof(PlanHeader));
   PlanTile* tiles = reinterpret_cast<PlanTile*>(descs + count);
@@ -339,7 +347,7 @@ sherry_status plan_impl(int32_t format, const sherry_gemv_problem* probs, int32_
   int64_t t = 0;
   for (const int32_t i : order) {
     const sherry_gemv_problem& p = probs[i];
-    const int64_t rows = tile_rows_for(p, bf16, format);
+    const int64_t rows = tile_rows_for(p, bf16, format, mfma);
     for (int64_t r0 = 0; r0 < p.n; r0 += rows) tiles[t++] = PlanTile{i, static_cast<int32_t>(r0)};
   }
   return SHERRY_OK;
@@ -430,6 +438,11 @@ size_t sherry_gemv_plan_bytes(const sherry_gemv_problem* probs, int32_t count) {
 sherry_status sherry_gemv_plan(const sherry_gemv_problem* probs, int32_t count, sherry_dtype s_dt,
                                sherry_dtype x_dt, sherry_dtype y_dt, void* plan, size_t plan_bytes) {
   return plan_impl(kFmtSherry, probs, count, s_dt, x_dt, y_dt, plan, plan_bytes);
+}
+
+sherry_status sherry_gemv_plan_mfma(const sherry_gemv_problem* probs, int32_t count, sherry_dtype s_dt,
+                                    sherry_dtype x_dt, sherry_dtype y_dt, void* plan, size_t plan_bytes) {
+  return plan_impl(kFmtSherry, probs, count, s_dt, x_dt, y_dt, plan, plan_bytes, true);
 }
 
 sherry_status sherry_gemv_grouped(const void* plan_host, const void* plan_dev, hipStream_t stream) {

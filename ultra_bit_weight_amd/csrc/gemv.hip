@@ -555,6 +555,171 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_bf16_grouped_kernel(const c
   finalize_bf16(d, row0, row1, res);
 }
 
+// ----------------------------------------------- bf16 x on the matrix cores ---
+// v_mfma_f32_16x16x32_bf16 multiplies A (16 x 32) by B (32 x 16): lane
+// (q, i) = (lane / 16, lane % 16) holds 8 bf16 of row i of A and the same 8 k
+// of column i of B, and C[4q + e][i] lands in register e.  Only the diagonal
+// is used: C[i][i] = sum over q of lane (q, i)'s 8 weights times its own 8 x
+// values, so each lane may take any k positions as long as its A and B
+// agree, and the four lanes of column i add up.  Here lane (q, i) owns one
+// 128-weight group of one row (its 32 codes feed 16 products, two blocks
+// each, and the group's 128 x values stay in 64 registers), and the four
+// lanes of a column belong to the same row: a row of G groups takes
+// P = ceil(G / 4) columns (group 4p + q in column p of the row), and a wave
+// walks R = 16 / P rows at a time.  A row's codes are therefore read by
+// consecutive lanes as in the VALU kernel, whole lines per instruction; the
+// multiply-adds and the 4-lane sum run on the matrix cores, and the VALU
+// keeps only the code extraction.  The P diagonal values of a row go to LDS
+// and are added in column order after the walk, so the result does not
+// depend on timing.  Columns past R P, and groups past G, repeat the loads
+// of an active lane (same addresses) with x = 0.
+// x is staged in LDS once per tile (a 16-byte pad after every group); the
+// first code loads are issued before the staging barrier and the epilogue's
+// scales are loaded with them.
+typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+constexpr int kBfThreads = kBf16MfmaWaves * kWave;
+constexpr int kBfResFloats = 4096;  // tile rows * P: 256 * 16 (k = 8192), 1024 * 2 (k = 1024)
+constexpr int kBfMaxTileRows = 1024;
+constexpr int kBfRowsPerThread = (kBfMaxTileRows + kBfThreads - 1) / kBfThreads;
+constexpr int kBfStagedChunks = kBf16MfmaMaxK / 8 * 17 / 16;  // 16-byte chunks of x with one pad per group
+// Codes whose table reads are issued before their products; independent
+// accumulators (back-to-back products into one accumulator wait for each
+// other's results); depth of the code prefetch ring.
+#ifndef SHERRY_BF_BATCH
+#define SHERRY_BF_BATCH 8
+#endif
+#ifndef SHERRY_BF_ACC
+#define SHERRY_BF_ACC 1
+#endif
+#ifndef SHERRY_BF_RING
+#define SHERRY_BF_RING 4
+#endif
+constexpr int kBfBatch = SHERRY_BF_BATCH;
+constexpr int kBfAcc = SHERRY_BF_ACC;
+constexpr int kBfRing = SHERRY_BF_RING;
+
+struct BfShared {
+  uint2 tab[32];
+  float res[kBfResFloats];
+  u32x4_t xs[kBfStagedChunks];
+};
+
+__device__ __forceinline__ void gemv_bf16_mfma_tile(const GemvDesc& d, int row0, int rt, BfShared& sh) {
+  constexpr int D = kBfRing;
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int i = lane & 15;
+  const int q = lane >> 4;
+  const int G = d.k / kGroupWeights;
+  const int P = (G + 3) / 4;  // columns per row
+  const int R = 16 / P;       // rows per step
+  const int RW = rt / kBf16MfmaWaves;
+  const int steps = (RW + R - 1) / R;
+  const int wrow0 = wave * RW;  // the wave's first row in the tile
+  const int nrows = min(rt, d.n - row0);
+  const int ie = i % (R * P);  // idle columns load what column ie loads
+  const int rho = ie / P;
+  const int g = 4 * (ie % P) + q;
+  const bool active = i < R * P && g < G;
+  const int gc = min(g, G - 1);
+  const int64_t row_words = static_cast<int64_t>(G) * kGroupWords;
+  auto fetch = [&](uint32_t (&w)[kGroupWords], int t) {
+    const int row = min(row0 + wrow0 + min(t, steps - 1) * R + rho, d.n - 1);
+    Sherry3of4::load(w, d.codes + row * row_words, G, gc);
+  };
+  uint32_t ring[D][kGroupWords];
+#pragma unroll
+  for (int r = 0; r + 1 < D; ++r) fetch(ring[r], r);
+  // epilogue scales, x staged in LDS, the table
+  const bool s_f16 = d.flags & kFlagScaleF16;
+  float sw[kBfRowsPerThread];
+#pragma unroll
+  for (int u = 0; u < kBfRowsPerThread; ++u) {
+    const int t = tid + u * kBfThreads;
+    sw[u] = t < nrows ? load_scale(d.w_scales, row0 + t, s_f16) : 0.0f;
+  }
+  const SHERRY_GLOBAL u32x4_t* xg = gmem(static_cast<const u32x4_t*>(d.x));
+  for (int c = tid; c < d.k / 8; c += kBfThreads) sh.xs[c + c / 16] = xg[c];
+  if (tid < 32) sh.tab[tid] = decode_bf16x4(tid);
+  __syncthreads();
+  uint32_t xr[64];
+  {
+    const u32x4_t* xp = sh.xs + 17 * gc;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const u32x4_t v = xp[u];
+      xr[4 * u + 0] = active ? v.x : 0u;
+      xr[4 * u + 1] = active ? v.y : 0u;
+      xr[4 * u + 2] = active ? v.z : 0u;
+      xr[4 * u + 3] = active ? v.w : 0u;
+    }
+  }
+  // C[i][i] sits in lane (i / 4, i), register i % 4
+  const bool diag = q == (i >> 2) && i < R * P;
+  auto step = [&](const uint32_t (&w)[kGroupWords], int t) {
+    uint32_t m[10];
+    masked_words8(w, m);
+    v4f_t c[kBfAcc];
+#pragma unroll
+    for (int r = 0; r < kBfAcc; ++r) c[r] = v4f_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int h = 0; h < 32 / kBfBatch; ++h) {
+      uint2 a[kBfBatch];
+#pragma unroll
+      for (int u = 0; u < kBfBatch; ++u) a[u] = lds_u64(sh.tab, code_offset8(w, m, kBfBatch * h + u));
+      // the batch's table reads all go out before its products (left to
+      // itself the scheduler pairs each product with its own two reads, and
+      // every product waits on an LDS round trip)
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kBfBatch / 2; ++u) {
+        const int p = (kBfBatch / 2) * h + u;  // blocks 2p, 2p + 1: x values 8p .. 8p + 7
+        const v4u_t av = {a[2 * u].x, a[2 * u].y, a[2 * u + 1].x, a[2 * u + 1].y};
+        const v4u_t bv = {xr[4 * p], xr[4 * p + 1], xr[4 * p + 2], xr[4 * p + 3]};
+        c[p % kBfAcc] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(v8bf_t, av), __builtin_bit_cast(v8bf_t, bv), c[p % kBfAcc], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int r = 1; r < kBfAcc; ++r) c[0] += c[r];
+    const int e = i & 3;
+    const float v = e == 0 ? c[0][0] : (e == 1 ? c[0][1] : (e == 2 ? c[0][2] : c[0][3]));
+    const int rl = t * R + rho;
+    if (diag && rl < RW) sh.res[(wrow0 + rl) * P + ie % P] = v;
+  };
+  for (int t0 = 0; t0 < steps; t0 += D) {
+#pragma unroll
+    for (int r = 0; r < D; ++r) {
+      fetch(ring[(r + D - 1) % D], t0 + r + D - 1);
+      if (t0 + r < steps) step(ring[r], t0 + r);
+    }
+  }
+  __syncthreads();
+  // y[row] = (sum over the row's columns, in order) * s_w[row], fp32
+#pragma unroll
+  for (int u = 0; u < kBfRowsPerThread; ++u) {
+    const int t = tid + u * kBfThreads;
+    if (t < nrows) {
+      float acc = sh.res[t * P];
+      for (int p = 1; p < P; ++p) acc = __fadd_rn(acc, sh.res[t * P + p]);
+      gmem(reinterpret_cast<float*>(d.y))[row0 + t] = __fmul_rn(acc, sw[u]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBfThreads) void gemv_bf16_mfma_grouped_kernel(const char* plan) {
+  __shared__ BfShared sh;
+  const PlanHeader* h = reinterpret_cast<const PlanHeader*>(plan);
+  const GemvDesc* descs = reinterpret_cast<const GemvDesc*>(plan + sizeof(PlanHeader));
+  const PlanTile tl = reinterpret_cast<const PlanTile*>(descs + h->count)[blockIdx.x];
+  const GemvDesc d = descs[tl.prob];
+  gemv_bf16_mfma_tile(d, tl.row0, bf16_mfma_tile_rows(d.kclass), sh);
+}
+
 // ---------------------------------------------------------- tern3 encode ---
 // One thread per (row, group): the group's 96 weights (zero past k; values
 // taken by sign) -> 32 base-3 codes -> the 5-word stream, words 0-3 at 4g and
@@ -723,7 +888,9 @@ hipError_t launch_gemv_grouped(const PlanHeader* h, const void* dev, hipStream_t
   if (h->n_tiles == 0) return hipSuccess;
   const char* plan = static_cast<const char*>(dev);
   const dim3 grid(h->n_tiles), block(kGemvThreads);
-  if (h->x_dt == SHERRY_BF16 && h->reserved[0] != 0)  // some problem has k = 3072
+  if (h->x_dt == SHERRY_BF16 && h->reserved[1] != 0)  // matrix-core tiling
+    hipLaunchKernelGGL(gemv_bf16_mfma_grouped_kernel, grid, dim3(kBfThreads), 0, stream, plan);
+  else if (h->x_dt == SHERRY_BF16 && h->reserved[0] != 0)  // some problem has k = 3072
     hipLaunchKernelGGL((gemv_bf16_grouped_kernel<true>), grid, block, 0, stream, plan);
   else if (h->x_dt == SHERRY_BF16)
     hipLaunchKernelGGL((gemv_bf16_grouped_kernel<false>), grid, block, 0, stream, plan);

@@ -39,6 +39,9 @@ inline int lanes_per_row(int32_t kc, bool bf16 = false) {
     default: return 64;
   }
 }
+#ifndef SHERRY_GROUPED_ITERS
+#define SHERRY_GROUPED_ITERS 32
+#endif
 #ifndef SHERRY_GEMV_THREADS
 #define SHERRY_GEMV_THREADS 256
 #endif
@@ -49,6 +52,21 @@ inline int rows_per_iter(int32_t kc, bool bf16 = false) {
 }
 
 enum Format : int32_t { kFmtSherry = 0, kFmtTern2 = 1, kFmtTern3 = 2 };
+
+// bf16 x on the matrix cores (3:4 codes, every problem k <= kBf16MfmaMaxK),
+// chosen by sherry_gemv_plan_mfma: 8-wave workgroups over tiles of
+// max(256, the int8 grouped tile) rows, so a plan sized for the int8 tiling
+// also holds this one.
+constexpr int kBf16MfmaMaxK = 8192;
+#ifndef SHERRY_BF16_MFMA_WAVES
+#define SHERRY_BF16_MFMA_WAVES 8
+#endif
+constexpr int kBf16MfmaWaves = SHERRY_BF16_MFMA_WAVES;
+__host__ __device__ constexpr int bf16_mfma_tile_rows(int32_t kc) {
+  const int lanes = kc == k1024 ? 8 : (kc == k2048 ? 16 : (kc == k3072 || kc == k4096 ? 32 : 64));
+  const int r = (kGemvThreads / kWave) * (kWave / lanes) * SHERRY_GROUPED_ITERS;
+  return r > 256 ? r : 256;
+}
 
 
 struct PlanHeader {
@@ -61,16 +79,14 @@ struct PlanHeader {
   int32_t y_dt;
   int32_t format;
   uint64_t bytes;
-  uint64_t reserved[3];  // GEMV plans: reserved[0] nonzero if some problem has k = 3072; GEMM plans: the tiling
+  uint64_t reserved[3];  // GEMV plans: reserved[0] nonzero if some problem has k = 3072, reserved[1] nonzero
+                         // for bf16 x on the matrix cores; GEMM plans: reserved[0] = the tiling
 };
 static_assert(sizeof(PlanHeader) == 64, "plan header layout");
 constexpr uint32_t kPlanMagic = 0x53485950u;  // "PYHS"
 constexpr uint32_t kPlanVersion = 1;
 // Row iterations per grouped-GEMV tile and depth of the GEMV prefetch ring
 // (build-time tunables; the defaults are the measured best on MI355X).
-#ifndef SHERRY_GROUPED_ITERS
-#define SHERRY_GROUPED_ITERS 32
-#endif
 #ifndef SHERRY_RING
 #define SHERRY_RING 4
 #endif

@@ -24,7 +24,7 @@ STATUS = {0: "SHERRY_OK", 1: "SHERRY_EINVAL", 2: "SHERRY_ESHAPE", 3: "SHERRY_EDT
 EXPORTS = [
     "sherry_version", "sherry_status_str", "sherry_packed_bytes", "sherry_pack", "sherry_decode", "sherry_gemv",
     "sherry_act_quant", "sherry_gemv_quant",
-    "sherry_gemv_plan_bytes", "sherry_gemv_plan", "sherry_gemv_grouped", "sherry_gemm",
+    "sherry_gemv_plan_bytes", "sherry_gemv_plan", "sherry_gemv_plan_mfma", "sherry_gemv_grouped", "sherry_gemm",
     "sherry_gemm_plan_bytes", "sherry_gemm_plan", "sherry_gemm_grouped",
     "tern2_packed_bytes", "tern2_encode", "tern2_gemv", "tern2_gemv_plan", "tern2_gemm", "tern2_gemm_plan",
     "tern3_packed_bytes", "tern3_encode", "tern3_gemv", "tern3_gemv_plan_bytes", "tern3_gemv_plan",
@@ -88,7 +88,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sherry_gemv_plan_bytes.argtypes = [ctypes.POINTER(GemvProblem), i32]
     lib.tern3_gemv_plan_bytes.restype = sz
     lib.tern3_gemv_plan_bytes.argtypes = [ctypes.POINTER(GemvProblem), i32]
-    for f in (lib.sherry_gemv_plan, lib.tern2_gemv_plan, lib.tern3_gemv_plan):
+    for f in (lib.sherry_gemv_plan, lib.sherry_gemv_plan_mfma, lib.tern2_gemv_plan, lib.tern3_gemv_plan):
         f.restype = i
         f.argtypes = [ctypes.POINTER(GemvProblem), i32, i, i, i, vp, sz]
     lib.sherry_gemv_grouped.restype = i
@@ -298,9 +298,11 @@ class GroupedGemv:
     """Many batch-1 products in one launch.  `problems` is a list of dicts with
     keys codes, scales, x, x_scale (or None), acc (or None), y (or None); all
     share the scale / x / y dtypes.  The plan is built once on the host and
-    copied to the device; call() launches it on the current stream."""
+    copied to the device; call() launches it on the current stream.  With
+    mfma=True (bf16 x, k <= 8192) the plan runs on the matrix cores
+    (sherry_gemv_plan_mfma)."""
 
-    def __init__(self, problems, tern2: bool = False, tern3: bool = False):
+    def __init__(self, problems, tern2: bool = False, tern3: bool = False, mfma: bool = False):
         lib = load()
         arr = (GemvProblem * len(problems))()
         self._keep = []
@@ -317,7 +319,10 @@ class GroupedGemv:
         if nbytes == 0:
             raise ValueError("invalid grouped GEMV problems")
         self.host = torch.empty(nbytes, dtype=torch.uint8)
-        fn = lib.tern3_gemv_plan if tern3 else (lib.tern2_gemv_plan if tern2 else lib.sherry_gemv_plan)
+        if mfma:
+            fn = lib.sherry_gemv_plan_mfma
+        else:
+            fn = lib.tern3_gemv_plan if tern3 else (lib.tern2_gemv_plan if tern2 else lib.sherry_gemv_plan)
         _check("gemv_plan", fn(arr, len(problems), s_dt, x_dt, y_dt, self.host.data_ptr(), nbytes))
         self.dev = self.host.to(p0["x"].device, non_blocking=False)
         self.n_tiles = int.from_bytes(bytes(self.host[12:16].tolist()), "little", signed=True)
