@@ -265,6 +265,53 @@ def oracle_beside(synth, max_seconds=2.0):
     return out
 
 
+def library_beside(torch, synth, args):
+    """Dense products of the installed libraries (through torch) on the same
+    shapes, as context: batch 1 with fp16 weights over the 112 replicas
+    (seven batched products per step, one per matrix shape, operands
+    contiguous), and M = 2048 with int8 (torch._int_mm) and bf16 weights,
+    seven calls per layer.  Random data; nothing here is checked."""
+    dev = torch.device("cuda:0")
+    shapes = synth.LLAMA32_1B_LAYER
+    R = args.replicas
+    out = {}
+    ws = {name: torch.randn(R, n, k, device=dev, dtype=torch.float16) for name, n, k in shapes}
+    xs = {name: torch.randn(R, k, 1, device=dev, dtype=torch.float16) for name, n, k in shapes}
+
+    def gemv_step():
+        for name, _, _ in shapes:
+            torch.bmm(ws[name], xs[name])
+    mean_ms, _ = time_launches(torch, gemv_step, 20, 3)
+    wbytes = R * sum(2 * n * k for _, n, k in shapes)
+    out["dense_fp16_gemv_1b_x%d" % R] = {"ms_per_step": round(mean_ms, 4),
+                                         "weights_per_s": R * sum(n * k for _, n, k in shapes) / (mean_ms * 1e-3),
+                                         "weight_GBps": round(wbytes / (mean_ms * 1e-3) / 1e9, 1)}
+    del ws, xs
+    torch.cuda.empty_cache()
+    M = 2048
+    ops = 2 * M * sum(n * k for _, n, k in shapes)
+    for dt in ("int8", "bf16"):
+        calls = []
+        for name, n, k in shapes:
+            if dt == "int8":
+                a = torch.randint(-127, 128, (M, k), dtype=torch.int8, device=dev)
+                b = torch.randint(-1, 2, (n, k), dtype=torch.int8, device=dev).t()
+                calls.append(lambda a=a, b=b: torch._int_mm(a, b))
+            else:
+                a = torch.randn(M, k, device=dev).to(torch.bfloat16)
+                b = torch.randn(k, n, device=dev).to(torch.bfloat16)
+                calls.append(lambda a=a, b=b: torch.matmul(a, b))
+        try:
+            mean_ms, _ = time_launches(torch, lambda: [c() for c in calls], 20, 3)
+        except RuntimeError as ex:
+            out[f"dense_{dt}_gemm_1b_M2048"] = {"error": str(ex)[:200]}
+            continue
+        out[f"dense_{dt}_gemm_1b_M2048"] = {"us_per_layer": round(mean_ms * 1e3, 1),
+                                            "TOPS": round(ops / (mean_ms * 1e-3) / 1e12, 1)}
+        del calls
+    return out
+
+
 def gemm_profile(torch, sherry, synth, probs, args):
     """The grouped GEMM launches alone: one 1B layer at M = 2048 (tiled int8
     MFMA kernel) and every replica at M = 16 (few-token kernel), a few
@@ -538,6 +585,7 @@ def extras(torch, sherry, synth, probs_1b, codes_1b, args):
         lay["graph_us_per_token_16_layers"] = round(16 * gus, 1)
     out["f4_decode_layer_1b"] = lay
     out["oracle_beside"] = oracle_beside(synth)
+    out["library_beside"] = library_beside(torch, synth, args)
 
     # packer: fp16 weights of one 1B layer -> codes + fp16 scales
     wts = {}
@@ -687,6 +735,9 @@ def main(argv=None):
         t3 = ex.get("tern3_grouped_1b")
         if t3:
             ex["sherry_over_tern3_speedup"] = round(t3["ms_per_launch"] / mean_ms, 3)
+        dense = ex.get("library_beside", {}).get("dense_fp16_gemv_1b_x%d" % args.replicas)
+        if dense:
+            ex["sherry_over_dense_fp16_gemv_speedup"] = round(dense["ms_per_step"] / mean_ms, 2)
         line["extras"] = ex
     print(json.dumps(line), flush=True)
     return 0
