@@ -257,6 +257,16 @@ sherry_status sherry_gemm_grouped(const void* plan_host, const void* plan_dev, h
  * epilogues are exactly those of the Sherry entry points. */
 size_t tern2_packed_bytes(int64_t n, int64_t k); /* n * k / 4, 0 if invalid */
 
+/* Pack real weights into 2-bit words with the decisions and scales of
+ * sherry_pack: per block of four the zero at the smallest |w|, the other
+ * three by sign, one least-squares scale per row.  The two formats then hold
+ * the same ternary matrix (a reading: the pages compare packings of ternary
+ * weights, Abstract and Figure 2, and give no separate quantizer for the
+ * 2-bit one).  Arguments, alignment and errors as in sherry_pack; codes
+ * receives tern2_packed_bytes(n, k) bytes (4-byte aligned). */
+sherry_status tern2_pack(const void* w, sherry_dtype w_dt, int64_t n, int64_t k, int64_t ldw, uint32_t* codes,
+                         void* scales, sherry_dtype s_dt, hipStream_t stream);
+
 /* Encode a dense ternary int8 matrix t (values -1, 0, +1; row stride ldt
  * elements, ldt >= k, ldt % 16 == 0, t 16-byte aligned) into 2-bit words.
  * Values outside {-1, 0, +1} are a caller error (output unspecified). */

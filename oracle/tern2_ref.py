@@ -71,6 +71,16 @@ def pack(t: np.ndarray) -> np.ndarray:
     return words.astype(np.uint32).reshape(-1)
 
 
+def pack_weights(w: np.ndarray, scale_dtype=np.float16):
+    """Real matrix [n, k] -> (2-bit words, per-row scales).  Reading R8b: the
+    ternary matrix and scales are those of the 3:4 quantizer (sherry_ref
+    quantize, readings R5/R6), stored in the 2-bit layout R8, so the two
+    formats hold the same matrix (the pages compare packings of ternary
+    weights and give no separate quantizer for the 2-bit one)."""
+    codes, alpha = sherry_ref.quantize(w)
+    return pack(sherry_ref.dense_from_codes(codes)), alpha.astype(scale_dtype)
+
+
 def unpack(words: np.ndarray, n: int, k: int) -> np.ndarray:
     sherry_ref.check_shape(n, k)
     w = np.asarray(words, dtype=np.uint32).reshape(n, k // WEIGHTS_PER_WORD).astype(np.uint64)

@@ -96,8 +96,9 @@ def test_gemv_bf16_rules(lib):
     assert gemv(lib, x_dt=BF16, acc=None, y_dt=F32, fn="tern2_gemv") == EDTYPE
 
 
-def test_pack_validation(lib):
-    f = lib.sherry_pack
+@pytest.mark.parametrize("fn", ["sherry_pack", "tern2_pack"])
+def test_pack_validation(lib, fn):
+    f = getattr(lib, fn)
     assert f(None, F32, 8, 128, 128, A, A, F16, None) == EINVAL
     assert f(A, F32, 8, 128, 128, None, A, F16, None) == EINVAL
     assert f(A, F32, 8, 100, 100, A, A, F16, None) == ESHAPE

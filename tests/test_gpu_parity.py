@@ -74,6 +74,33 @@ def test_pack_matches_oracle(gpu_lib, n, k, w_dtype, s_dtype):
                           ref_scales.view(np.uint32 if s_dtype == np.float32 else np.uint16))
 
 
+@pytest.mark.parametrize("n,k", [(1, 128), (37, 640), (256, 2048)])
+@pytest.mark.parametrize("w_dtype", [np.float32, np.float16, "bf16"])
+def test_tern2_pack_matches_oracle(gpu_lib, n, k, w_dtype):
+    """The 2-bit packer keeps the 3:4 decisions and scales (reading R8b):
+    words and scales equal the oracle's, and equal tern2_encode of the 3:4
+    packer's decoded matrix."""
+    say(f"tern2_pack n={n} k={k} {w_dtype}")
+    g = synth.rng(11 * n + k)
+    w32 = (g.standard_normal((n, k)) * 0.05).astype(np.float32)
+    w32[0, :12] = [0.5, -0.5, 0.5, 0.5, -0.0, 0.0, 1.0, -1.0, 0.25, 0.25, 0.25, 0.25]  # ties, signed zero
+    if w_dtype == "bf16":
+        bits = synth.f32_to_bf16_bits(w32)
+        w_ref = (bits.astype(np.uint32) << 16).view(np.float32)
+        w_dev = dev(bits.view(np.int16)).view(torch.bfloat16)
+    else:
+        w_ref = w32.astype(w_dtype)
+        w_dev = dev(w_ref)
+    words, sc = gpu_lib.tern2_pack(w_dev, torch.float16)
+    c5, s5 = gpu_lib.pack(w_dev, torch.float16)
+    via = gpu_lib.tern2_encode(gpu_lib.decode(c5, n, k))
+    torch.cuda.synchronize()
+    ref_words, ref_s = tern2_ref.pack_weights(w_ref, np.float16)
+    assert np.array_equal(host_words(words), ref_words)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint16), ref_s.view(np.uint16))
+    assert torch.equal(words, via) and torch.equal(sc.view(torch.int16), s5.view(torch.int16))
+
+
 def test_pack_exact_ternary_and_row_stride(gpu_lib):
     g = synth.rng(77)
     n, k, ld = 50, 1024, 1024 + 64

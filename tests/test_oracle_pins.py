@@ -88,6 +88,28 @@ def test_tern2_hand_words():
             assert tern2_ref.decode_word(words[r * 16 + i]) == t[r, 16 * i:16 * i + 16].tolist()
 
 
+def test_tern2_pack_weights():
+    """Reading R8b: the 2-bit packer keeps the 3:4 quantizer's decisions and
+    scales.  Hand row: block 0 = (0.5, -0.1, 2.0, -3.0) -> zero at slot 1,
+    (+1, 0, +1, -1); every other block is all zeros -> zero at slot 0 (lowest
+    slot on ties), (0, +1, +1, +1).  Word 0 holds blocks 0-3, block q's weight
+    p at bits 8p + 2q: 0x03010001 | 0x04040400 | 0x10101000 | 0x40404000;
+    words of four zero blocks: 0x01010100 | 0x04040400 | 0x10101000 |
+    0x40404000.  Scale: kept magnitudes 0.5 + 2 + 3 over 3 * 128 / 4 = 96."""
+    w = np.zeros((1, 128), np.float32)
+    w[0, :4] = [0.5, -0.1, 2.0, -3.0]
+    words, s = tern2_ref.pack_weights(w, np.float32)
+    assert int(words[0]) == 0x57555401
+    assert all(int(v) == 0x55555500 for v in words[1:])
+    assert s[0] == np.float32(5.5 / 96)
+    # W = s T with T 3:4 ternary: the words of T and the scale s exactly
+    g = synth.rng(31)
+    t = synth.ternary_34(6, 256, g)
+    sc = synth.row_scales(6, g, np.float32)
+    words, s2 = tern2_ref.pack_weights(t.astype(np.float32) * sc[:, None], np.float32)
+    assert np.array_equal(words, tern2_ref.pack(t)) and np.array_equal(s2, sc)
+
+
 def test_sherry_and_tern2_agree_on_the_same_matrix():
     """Two encodings of one ternary matrix give one product, bit for bit."""
     g = synth.rng(13)

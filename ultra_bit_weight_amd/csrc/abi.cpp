@@ -353,6 +353,19 @@ sherry_status plan_impl(int32_t format, const sherry_gemv_problem* probs, int32_
   return SHERRY_OK;
 }
 
+sherry_status pack_impl(const void* w, sherry_dtype w_dt, int64_t n, int64_t k, int64_t ldw, uint32_t* codes,
+                        void* scales, sherry_dtype s_dt, bool tern2, hipStream_t stream) {
+  if (!w || !codes || !scales) return SHERRY_EINVAL;
+  if (sherry_status s = check_nk(n, k)) return s;
+  if (ldw < k || ldw > std::numeric_limits<int64_t>::max() / n) return SHERRY_ESHAPE;
+  if (w_dt != SHERRY_F32 && w_dt != SHERRY_F16 && w_dt != SHERRY_BF16) return SHERRY_EDTYPE;
+  if (!is_scale_dt(s_dt)) return SHERRY_EDTYPE;
+  if (!aligned(w, 4 * dt_size(w_dt)) || ldw % 4 != 0 || !aligned(codes, 4) || !aligned(scales, dt_size(s_dt)))
+    return SHERRY_EALIGN;
+  if (sherry_status s = check_device()) return s;
+  return launched(launch_pack(w, w_dt, n, k, ldw, codes, scales, s_dt == SHERRY_F16, tern2, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -379,15 +392,12 @@ size_t sherry_packed_bytes(int64_t n, int64_t k) {
 
 sherry_status sherry_pack(const void* w, sherry_dtype w_dt, int64_t n, int64_t k, int64_t ldw, uint32_t* codes,
                           void* scales, sherry_dtype s_dt, hipStream_t stream) {
-  if (!w || !codes || !scales) return SHERRY_EINVAL;
-  if (sherry_status s = check_nk(n, k)) return s;
-  if (ldw < k || ldw > std::numeric_limits<int64_t>::max() / n) return SHERRY_ESHAPE;
-  if (w_dt != SHERRY_F32 && w_dt != SHERRY_F16 && w_dt != SHERRY_BF16) return SHERRY_EDTYPE;
-  if (!is_scale_dt(s_dt)) return SHERRY_EDTYPE;
-  if (!aligned(w, 4 * dt_size(w_dt)) || ldw % 4 != 0 || !aligned(codes, 4) || !aligned(scales, dt_size(s_dt)))
-    return SHERRY_EALIGN;
-  if (sherry_status s = check_device()) return s;
-  return launched(launch_pack(w, w_dt, n, k, ldw, codes, scales, s_dt == SHERRY_F16, stream));
+  return pack_impl(w, w_dt, n, k, ldw, codes, scales, s_dt, false, stream);
+}
+
+sherry_status tern2_pack(const void* w, sherry_dtype w_dt, int64_t n, int64_t k, int64_t ldw, uint32_t* codes,
+                         void* scales, sherry_dtype s_dt, hipStream_t stream) {
+  return pack_impl(w, w_dt, n, k, ldw, codes, scales, s_dt, true, stream);
 }
 
 sherry_status sherry_act_quant(const void* x, sherry_dtype x_dt, int64_t m, int64_t k, int64_t ldx, int8_t* xq,

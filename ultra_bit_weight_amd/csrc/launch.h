@@ -168,7 +168,7 @@ inline constexpr int few_tile_rows(int groups) {
 constexpr int64_t kLargeTileMinGroups = SHERRY_LARGE_TILE_MIN_GROUPS;
 
 hipError_t launch_pack(const void* w, int w_dt, int64_t n, int64_t k, int64_t ldw, uint32_t* codes,
-                       void* scales, bool s_f16, hipStream_t stream);
+                       void* scales, bool s_f16, bool tern2, hipStream_t stream);
 hipError_t launch_gemv(const GemvDesc& d, bool bf16_x, int32_t format, hipStream_t stream);
 hipError_t launch_gemv_grouped(const PlanHeader* host, const void* dev, hipStream_t stream);
 hipError_t launch_gemv_xq(const GemvDesc& d, int xdt, float* sx_out, int32_t format, hipStream_t stream);

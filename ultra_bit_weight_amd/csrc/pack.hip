@@ -13,7 +13,10 @@
 //
 // One workgroup per row; a half-wave (32 lanes) owns one 128-weight group,
 // lane j encodes block j and the group's five words are assembled with an
-// OR-butterfly across the half-wave.
+// OR-butterfly across the half-wave.  The same decisions can instead be
+// stored as 2-bit fields (the dense-ternary comparator: 00 = 0, 01 = +1,
+// 11 = -1, weight 4q + p of each 16-weight word at bits 8p + 2q), so both
+// formats hold one matrix with the same scales.
 #include "launch.h"
 
 namespace sherry {
@@ -94,7 +97,7 @@ __device__ __forceinline__ float4 load_block(const T* p) {
     return load4(p);
 }
 
-template <typename T>
+template <typename T, bool TERN2>
 __global__ __launch_bounds__(256) void pack_kernel(const T* w, int64_t ldw, int k, uint32_t* codes, void* scales,
                                                    int s_f16) {
   __shared__ double red_hi[4], red_lo[4];
@@ -127,6 +130,18 @@ __global__ __launch_bounds__(256) void pack_kernel(const T* w, int64_t ldw, int 
       if (val[s] < 0.0f) code |= 1u << sb;
       sum = dd_add(sum, DD{static_cast<double>(mag[s]), 0.0});
       ++sb;
+    }
+    if constexpr (TERN2) {
+      // block j = weights 4j .. 4j + 3 of the group: word j / 4 of the
+      // group's eight, weight 4 (j % 4) + p of it at bits 8p + 2 (j % 4)
+      uint32_t f = 0;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (s != z) f |= (val[s] < 0.0f ? 3u : 1u) << (8 * s + 2 * (j & 3));
+      f |= __shfl_xor(f, 1);
+      f |= __shfl_xor(f, 2);
+      if ((j & 3) == 0) codes[static_cast<int64_t>(r) * (k / 16) + 8 * g + (j >> 2)] = f;
+      continue;
     }
     // contributions of code j to the group's five words
     const int bit = 5 * j;
@@ -201,24 +216,33 @@ hipError_t launch_decode(const uint32_t* codes, int64_t n, int64_t k, int8_t* t,
   return hipGetLastError();
 }
 
-hipError_t launch_pack(const void* w, int w_dt, int64_t n, int64_t k, int64_t ldw, uint32_t* codes, void* scales,
-                       bool s_f16, hipStream_t stream) {
+template <bool TERN2>
+void launch_pack_fmt(const void* w, int w_dt, int64_t n, int64_t k, int64_t ldw, uint32_t* codes, void* scales,
+                     bool s_f16, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(n)), block(256);
   const int kk = static_cast<int>(k);
   switch (w_dt) {
     case SHERRY_F32:
-      hipLaunchKernelGGL(pack_kernel<float>, grid, block, 0, stream, static_cast<const float*>(w), ldw, kk, codes,
+      hipLaunchKernelGGL((pack_kernel<float, TERN2>), grid, block, 0, stream, static_cast<const float*>(w), ldw, kk, codes,
                          scales, s_f16 ? 1 : 0);
       break;
     case SHERRY_F16:
-      hipLaunchKernelGGL(pack_kernel<_Float16>, grid, block, 0, stream, static_cast<const _Float16*>(w), ldw, kk,
+      hipLaunchKernelGGL((pack_kernel<_Float16, TERN2>), grid, block, 0, stream, static_cast<const _Float16*>(w), ldw, kk,
                          codes, scales, s_f16 ? 1 : 0);
       break;
     default:
-      hipLaunchKernelGGL(pack_kernel<uint16_t>, grid, block, 0, stream, static_cast<const uint16_t*>(w), ldw, kk,
+      hipLaunchKernelGGL((pack_kernel<uint16_t, TERN2>), grid, block, 0, stream, static_cast<const uint16_t*>(w), ldw, kk,
                          codes, scales, s_f16 ? 1 : 0);
       break;
   }
+}
+
+hipError_t launch_pack(const void* w, int w_dt, int64_t n, int64_t k, int64_t ldw, uint32_t* codes, void* scales,
+                       bool s_f16, bool tern2, hipStream_t stream) {
+  if (tern2)
+    launch_pack_fmt<true>(w, w_dt, n, k, ldw, codes, scales, s_f16, stream);
+  else
+    launch_pack_fmt<false>(w, w_dt, n, k, ldw, codes, scales, s_f16, stream);
   return hipGetLastError();
 }
 

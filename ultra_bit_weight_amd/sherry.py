@@ -26,7 +26,7 @@ EXPORTS = [
     "sherry_act_quant", "sherry_gemv_quant",
     "sherry_gemv_plan_bytes", "sherry_gemv_plan", "sherry_gemv_plan_mfma", "sherry_gemv_grouped", "sherry_gemm",
     "sherry_gemm_plan_bytes", "sherry_gemm_plan", "sherry_gemm_grouped",
-    "tern2_packed_bytes", "tern2_encode", "tern2_gemv", "tern2_gemv_plan", "tern2_gemm", "tern2_gemm_plan",
+    "tern2_packed_bytes", "tern2_pack", "tern2_encode", "tern2_gemv", "tern2_gemv_plan", "tern2_gemm", "tern2_gemm_plan",
     "tern3_packed_bytes", "tern3_encode", "tern3_gemv", "tern3_gemv_plan_bytes", "tern3_gemv_plan",
 ]
 
@@ -72,8 +72,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tern2_packed_bytes.argtypes = [i64, i64]
     lib.tern3_packed_bytes.restype = sz
     lib.tern3_packed_bytes.argtypes = [i64, i64]
-    lib.sherry_pack.restype = i
-    lib.sherry_pack.argtypes = [vp, i, i64, i64, i64, vp, vp, i, vp]
+    for f in (lib.sherry_pack, lib.tern2_pack):
+        f.restype = i
+        f.argtypes = [vp, i, i64, i64, i64, vp, vp, i, vp]
     lib.sherry_decode.restype = i
     lib.sherry_decode.argtypes = [vp, i64, i64, vp, i64, vp]
     lib.sherry_gemv_quant.restype = i
@@ -161,6 +162,19 @@ def pack(w: torch.Tensor, scale_dtype=torch.float16):
     scales = torch.empty(n, dtype=scale_dtype, device=w.device)
     _check("sherry_pack", load().sherry_pack(w.data_ptr(), _DT[w.dtype], n, k, w.stride(0), codes.data_ptr(),
                                              scales.data_ptr(), _DT[scale_dtype], _stream()))
+    return codes, scales
+
+
+def tern2_pack(w: torch.Tensor, scale_dtype=torch.float16):
+    """Real weights [n, k] -> (2-bit words int32 [n*k/16], scales [n]) with
+    the decisions and scales of pack(): the same ternary matrix."""
+    if w.dim() != 2 or w.stride(1) != 1 or not w.is_cuda:
+        raise ValueError("w must be a 2-D GPU tensor with unit column stride")
+    n, k = w.shape
+    codes = torch.empty(max(tern2_packed_bytes(n, k) // 4, 1), dtype=torch.int32, device=w.device)
+    scales = torch.empty(n, dtype=scale_dtype, device=w.device)
+    _check("tern2_pack", load().tern2_pack(w.data_ptr(), _DT[w.dtype], n, k, w.stride(0), codes.data_ptr(),
+                                           scales.data_ptr(), _DT[scale_dtype], _stream()))
     return codes, scales
 
 
