@@ -47,6 +47,8 @@ def parse_args(argv=None):
                    help="sustained-load time before each timed region (lets the clocks settle)")
     p.add_argument("--no-extras", action="store_true", help="only the metric line (no secondary measurements)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--probes", action="store_true",
+                   help="only the ceiling probes (streaming read, matrix-core and v_dot4 rates): one JSON line")
     p.add_argument("--copy-probe", action="store_true",
                    help="also run one plain 1 GiB device copy (calibrates HBM byte counters)")
     p.add_argument("--gemm-profile", action="store_true",
@@ -262,6 +264,33 @@ def oracle_beside(synth, max_seconds=2.0):
         spk = timed(lambda: sherry_ref.pack(wp, np.float16), reps_max=2)
         out["a1_pack_512x2048_fp16"] = {"s": round(spk, 3), "weights_per_s": 512 * 2048 / spk}
     out["cores"] = 1
+    return out
+
+
+def peak_probes(torch, sherry):
+    """Measured ceilings beside the published peaks: a 1 GiB streaming read
+    (HBM), the int8 matrix-core and v_dot4 rates, and both kinds of work in
+    the same wave and in alternate waves.  overlap = t(both) / (t(mfma) +
+    t(dot4)): 1.0 when they do not overlap, max / sum when they fully do."""
+    dev = torch.device("cuda:0")
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    buf = torch.empty(1 << 28, dtype=torch.int32, device=dev)
+    buf.fill_(1)
+    mean_ms, _ = time_launches(torch, lambda: sherry.probe_read(buf, sink), 20, 3)
+    out = {"read_1GiB_TBps": round((1 << 30) / (mean_ms * 1e-3) / 1e12, 3)}
+    del buf
+    blocks, iters = 1024, 8192
+    t = {}
+    for name, mode in (("mfma", sherry.PROBE_MFMA), ("dot4", sherry.PROBE_DOT4), ("same_wave", sherry.PROBE_SAME_WAVE),
+                       ("alt_waves", sherry.PROBE_ALT_WAVES)):
+        mean_ms, _ = time_launches(torch, lambda: sherry.probe_rates(mode, iters, blocks, sink), 10, 2, settle_ms=20)
+        t[name] = mean_ms
+    waves = 4 * blocks * iters
+    out["mfma_i8_TOPS"] = round(waves * sherry.PROBE_MFMA_OPS / (t["mfma"] * 1e-3) / 1e12, 1)
+    out["dot4_i8_TOPS"] = round(waves * sherry.PROBE_DOT4_OPS / (t["dot4"] * 1e-3) / 1e12, 1)
+    out["ms"] = {k: round(v, 4) for k, v in t.items()}
+    out["overlap_same_wave"] = round(t["same_wave"] / (t["mfma"] + t["dot4"]), 3)
+    out["overlap_alt_waves"] = round(2 * t["alt_waves"] / (t["mfma"] + t["dot4"]), 3)
     return out
 
 
@@ -586,6 +615,7 @@ def extras(torch, sherry, synth, probs_1b, codes_1b, args):
     out["f4_decode_layer_1b"] = lay
     out["oracle_beside"] = oracle_beside(synth)
     out["library_beside"] = library_beside(torch, synth, args)
+    out["peak_probes"] = peak_probes(torch, sherry)
 
     # packer: fp16 weights of one 1B layer -> codes + fp16 scales
     wts = {}
@@ -662,6 +692,9 @@ def main(argv=None):
         return 1
     sherry.load()
     torch.cuda.set_device(0)
+    if args.probes:
+        print(json.dumps(peak_probes(torch, sherry)), flush=True)
+        return 0
     shapes = synth.LLAMA32_1B_LAYER
     R = args.replicas
     codes, probs = build_layer_replicas(torch, sherry, synth, shapes, R, args.seed)

@@ -1,0 +1,42 @@
+/* sherry_probes.h -- measured ceilings for the rooflines of the products in
+ * sherry.h (streaming HBM reads, the int8 matrix-core and v_dot4 rates, and
+ * whether the two overlap).  Same conventions as sherry.h: extern "C",
+ * device pointers owned by the caller, host-side validation (a status and
+ * nothing enqueued on error), asynchronous on `stream`.  Measurement aids
+ * beside the published peaks; the products do not use them. */
+#ifndef SHERRY_PROBES_H
+#define SHERRY_PROBES_H
+
+#include "sherry.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Read `bytes` (> 0, a multiple of 16) from `src` (16-byte aligned device
+ * memory) once, with 16-byte non-temporal loads: up to 64 workgroups per CU,
+ * each streaming one contiguous chunk.  `sink`: device buffer of 256
+ * uint32 (4-byte aligned), written only in the practically impossible case
+ * that the XOR of a thread's data equals a fixed constant (the store keeps
+ * the loads).  Time it with events: the
+ * achieved read bandwidth is bytes / time. */
+sherry_status sherry_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
+/* Rate probe: `blocks` workgroups of 4 waves each run `iters` iterations
+ * (1 .. 2^24; blocks 1 .. 2^20).  Per iteration a working wave issues
+ *   matrix-core work: 4 independent v_mfma_i32_16x16x64_i8 (4 x 32768 ops),
+ *   VALU work:        16 independent v_dot4_i32_i8 (16 x 512 ops),
+ * by mode: SHERRY_PROBE_MFMA (every wave, matrix cores only),
+ * SHERRY_PROBE_DOT4 (every wave, VALU only), SHERRY_PROBE_SAME_WAVE (every
+ * wave does both, interleaved), SHERRY_PROBE_ALT_WAVES (even waves of a
+ * workgroup the matrix-core work, odd waves the VALU work).  `sink` as in
+ * sherry_probe_read.  If the two kinds of work overlap, the SAME_WAVE time
+ * is close to the larger of the MFMA and DOT4 times; if not, to their sum. */
+enum { SHERRY_PROBE_MFMA = 0, SHERRY_PROBE_DOT4 = 1, SHERRY_PROBE_SAME_WAVE = 2, SHERRY_PROBE_ALT_WAVES = 3 };
+sherry_status sherry_probe_rates(int32_t mode, int32_t iters, int32_t blocks, uint32_t* sink, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SHERRY_PROBES_H */

@@ -1,6 +1,8 @@
-"""libsherry.so on the host: it loads, exports every function include/sherry.h
-declares, and rejects invalid arguments before any HIP call (no GPU needed)."""
+"""libsherry.so on the host: it loads, exports every function the headers in
+include/ declare, and rejects invalid arguments before any HIP call (no GPU
+needed)."""
 import ctypes
+import glob
 import os
 import re
 
@@ -15,11 +17,12 @@ I8, I32, F16, BF16, F32 = 0, 1, 2, 3, 4
 A = 0x10000  # a fake, well-aligned non-null "device" address: never dereferenced
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"\b(\w+)\s*\([^;{]*\)\s*;", text)
-    return sorted(set(n for n in names if n.startswith(("sherry_", "tern2_"))))
+def declared_functions(paths=None):
+    names = set()
+    for path in paths or sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names.update(re.findall(r"\b(\w+)\s*\([^;{]*\)\s*;", text))
+    return sorted(n for n in names if n.startswith(("sherry_", "tern2_", "tern3_")))
 
 
 @pytest.fixture(scope="module")
@@ -32,7 +35,7 @@ def lib():
 
 
 def test_header_declares_the_api():
-    names = declared_functions()
+    names = declared_functions([HEADER])
     for required in ("sherry_pack", "sherry_gemv", "sherry_gemm", "sherry_gemv_grouped", "tern2_gemv"):
         assert required in names
     assert len(names) >= 14
@@ -41,7 +44,7 @@ def test_header_declares_the_api():
 def test_every_declared_symbol_is_exported(lib):
     raw = ctypes.CDLL(LIB)
     for name in declared_functions():
-        assert hasattr(raw, name), f"{name} declared in sherry.h but not exported"
+        assert hasattr(raw, name), f"{name} declared in include/ but not exported"
 
 
 def test_version_and_status_strings(lib):
@@ -366,3 +369,23 @@ def test_grouped_gemm_plan_on_host(lib):
     assert lib.sherry_gemm_grouped(ctypes.addressof(bad), A, None) == EINVAL
     assert lib.sherry_gemm_plan(arr, len(layer), F16, I8, F16, base, nbytes) == OK
     assert lib.sherry_gemv_grouped(base, A, None) == EINVAL  # a GEMM plan is not a GEMV plan
+
+
+def test_probe_validation(lib):
+    """Ceiling probes (include/sherry_probes.h): argument checks before any
+    HIP call; EDEVICE without a GPU."""
+    raw = ctypes.CDLL(LIB)
+    rd, rt = raw.sherry_probe_read, raw.sherry_probe_rates
+    rd.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    rt.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    assert rd(None, 1024, A, None) == EINVAL
+    assert rd(A, 0, A, None) == EINVAL
+    assert rd(A, 1000, A, None) == ESHAPE
+    assert rd(A + 4, 1024, A, None) == EALIGN
+    assert rd(A, 1024, A, None) == EDEVICE
+    assert rt(4, 10, 10, A, None) == EINVAL
+    assert rt(0, 0, 10, A, None) == EINVAL
+    assert rt(0, 10, 0, A, None) == EINVAL
+    assert rt(0, 10, 10, None, None) == EINVAL
+    assert rt(0, 10, 10, A + 2, None) == EALIGN
+    assert rt(0, 10, 10, A, None) == EDEVICE

@@ -5,6 +5,8 @@ the int8 paths too (the epilogue is the same chain of IEEE fp32 products).  The
 bf16 path accumulates in fp32 in a different order from the exact reference,
 so it is held to max|d| <= 1e-3 * max|y_ref| and relative L2 <= 1e-4.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -778,3 +780,41 @@ def test_tern3_grouped(gpu_lib):
     for p, (ra, ry) in zip(probs, refs):
         assert np.array_equal(p["acc"].cpu().numpy(), ra)
         assert np.array_equal(p["y"].cpu().numpy().view(np.uint16), ry.view(np.uint16))
+
+
+# ------------------------------------------------------------------ probes ---
+
+def test_probes_and_bench_line(gpu_lib):
+    """The ceiling probes run and give rates below the published peaks (a
+    figure above them would mean cache hits or dropped work), and the
+    benchmark's JSON line holds the fields its contract names."""
+    import json
+    import subprocess
+    import sys
+    say("probes")
+    sink = torch.zeros(256, dtype=torch.int32, device=DEV)
+    buf = torch.ones(1 << 26, dtype=torch.int32, device=DEV)
+    gpu_lib.probe_read(buf, sink)
+    for mode in range(4):
+        gpu_lib.probe_rates(mode, 64, 256, sink)
+    torch.cuda.synchronize()
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--probes"], capture_output=True, text=True,
+                       timeout=110)
+    assert r.returncode == 0, r.stderr[-2000:]
+    pk = json.loads(r.stdout.strip().splitlines()[-1])
+    assert 0.5 < pk["read_1GiB_TBps"] < 8.0
+    assert 10 < pk["mfma_i8_TOPS"] < 5000
+    assert 1 < pk["dot4_i8_TOPS"] < 2 * 314.6  # 314.6: 1024 SIMDs x 64 lanes x 8 ops / 4 cycles x 2.4 GHz
+    say("bench line")
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--steps", "5", "--warmup", "2", "--replicas",
+                        "8", "--no-extras", "--no-cpu-baseline"], capture_output=True, text=True, timeout=110)
+    assert r.returncode == 0, r.stderr[-2000:]
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
+                "vs_baseline", "dtype", "data", "config", "roofline"):
+        assert key in line, key
+    assert line["n_gpus"] == 1 and line["steps"] == 5 and line["value"] > 0
+    assert "workload" in line["config"]
+    rf = line["roofline"]
+    assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and 0 < rf["frac"] < 1 and rf["peak"] == 8000.0

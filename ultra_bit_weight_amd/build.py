@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libsherry.so")
-SOURCES = ["abi.cpp", "pack.hip", "gemv.hip", "gemm.hip", "act.hip"]
+SOURCES = ["abi.cpp", "pack.hip", "gemv.hip", "gemm.hip", "act.hip", "probes.hip"]
 ARCH = "gfx950"
 
 

@@ -28,6 +28,7 @@ EXPORTS = [
     "sherry_gemm_plan_bytes", "sherry_gemm_plan", "sherry_gemm_grouped",
     "tern2_packed_bytes", "tern2_pack", "tern2_encode", "tern2_gemv", "tern2_gemv_plan", "tern2_gemm", "tern2_gemm_plan",
     "tern3_packed_bytes", "tern3_encode", "tern3_gemv", "tern3_gemv_plan_bytes", "tern3_gemv_plan",
+    "sherry_probe_read", "sherry_probe_rates",
 ]
 
 
@@ -63,6 +64,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     vp, i64, i32, i = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int
     sz = ctypes.c_size_t
+    lib.sherry_probe_read.restype = i
+    lib.sherry_probe_read.argtypes = [vp, sz, vp, vp]
+    lib.sherry_probe_rates.restype = i
+    lib.sherry_probe_rates.argtypes = [i32, i32, i32, vp, vp]
     lib.sherry_version.restype = ctypes.c_char_p
     lib.sherry_status_str.restype = ctypes.c_char_p
     lib.sherry_status_str.argtypes = [i]
@@ -176,6 +181,25 @@ def tern2_pack(w: torch.Tensor, scale_dtype=torch.float16):
     _check("tern2_pack", load().tern2_pack(w.data_ptr(), _DT[w.dtype], n, k, w.stride(0), codes.data_ptr(),
                                            scales.data_ptr(), _DT[scale_dtype], _stream()))
     return codes, scales
+
+
+PROBE_MFMA, PROBE_DOT4, PROBE_SAME_WAVE, PROBE_ALT_WAVES = 0, 1, 2, 3
+# int8 ops per wave and iteration of the rate probe: 4 matrix-core products
+# of 16 x 16 x 64, 16 v_dot4 over 64 lanes
+PROBE_MFMA_OPS, PROBE_DOT4_OPS = 4 * 2 * 16 * 16 * 64, 16 * 2 * 4 * 64
+
+
+def probe_read(buf: torch.Tensor, sink: torch.Tensor):
+    """Read all of buf (GPU, bytes a multiple of 16) once (sherry_probe_read)."""
+    _dev(buf, sink)
+    _check("sherry_probe_read", load().sherry_probe_read(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                                         sink.data_ptr(), _stream()))
+
+
+def probe_rates(mode: int, iters: int, blocks: int, sink: torch.Tensor):
+    """Rate probe (sherry_probe_rates): `blocks` workgroups of 4 waves."""
+    _dev(sink)
+    _check("sherry_probe_rates", load().sherry_probe_rates(mode, iters, blocks, sink.data_ptr(), _stream()))
 
 
 def decode(codes: torch.Tensor, n: int, k: int) -> torch.Tensor:
