@@ -486,6 +486,17 @@ struct FewShape {
   static_assert(NBLK * 16 * RG == RT, "few-token tile shape");
 };
 
+// LDS word of the sum for row 16 b + 4 q + e of a tile and token i.  Blocks
+// are 257 words apart, so the bank is (b + 16 q + i) mod 64: the MFMA lanes
+// (q, i) of one block and e, and the epilogue's 64 consecutive quads (b, q)
+// of one token, each fall in 64 different banks.
+constexpr int kFewSumStride = 257;
+constexpr int kFewSumWords = kFewMaxTileRows / 16 * kFewSumStride;
+static_assert(kFewSumWords % 4 == 0, "sums are cleared as int4");
+__device__ __forceinline__ int few_sum_word(int b, int q, int e, int i) {
+  return kFewSumStride * b + 64 * e + 16 * q + i;
+}
+
 template <class Fmt, int S>
 __device__ __forceinline__ void gemm_few(const GemmDesc& d, int tile, const uint32_t* tab32, const uint2* pairs,
                                          int32_t* sums) {
@@ -558,7 +569,8 @@ __device__ __forceinline__ void gemm_few(const GemmDesc& d, int tile, const uint
         }
       }
     }
-    int32_t* dst = sums + 256 * (rg * NBLK + blk) + 16 * q + i;
+    const int b = rg * NBLK + blk;
+    int32_t* dst = sums + few_sum_word(b, q, 0, i);
 #pragma unroll
     for (int e = 0; e < 4; ++e) atomicAdd(dst + 64 * e, c[e]);
   };
@@ -575,35 +587,30 @@ __device__ __forceinline__ void gemm_few(const GemmDesc& d, int tile, const uint
 }
 
 // Zero the tile's sums, build the tables, run the row groups, write the tile.
-// Thread t writes rows t % rt + j * 512 (j < RPT) of the tile for tokens
-// t / rt, t / rt + 512 / rt, ... (all tokens when rt >= 512): its weight
-// scales are loaded before the main loop and the token scales are staged in
-// LDS, so the epilogue waits on no global load.
+// Thread t writes the four rows 4Q .. 4Q + 3 of quad Q = t % (rt / 4) for
+// tokens t / (rt / 4), + 2048 / rt, ...: consecutive threads hold consecutive
+// quads of one token, so a wave stores 64 x 4 consecutive outputs at once
+// (8 bytes per lane in fp16), and its LDS reads of the sums hit 64 banks
+// (few_sum_word).  The tile's weight scales and the token scales are staged
+// in LDS before the main loop, so the epilogue waits on no global load.
 template <class Fmt>
 __device__ __forceinline__ void gemm_few_tile(const GemmDesc& d, int tile) {
   constexpr int kThreads = kFewWaves * kWave;
-  constexpr int RPT = kFewMaxTileRows > kThreads ? kFewMaxTileRows / kThreads : 1;  // rows per thread
-  static_assert(kThreads % kFewMaxTileRows == 0 || kFewMaxTileRows % kThreads == 0, "epilogue mapping");
+  static_assert(kThreads % (kFewMaxTileRows / 4) == 0 && kFewMaxTileRows % 64 == 0, "epilogue mapping");
   __shared__ uint32_t tab32[32];
   __shared__ uint2 pairs[kPairMask != 0 ? Fmt::kPairEntries : 1];
-  __shared__ __attribute__((aligned(16))) int32_t sums[kFewMaxTileRows * kFewMaxTok];
+  __shared__ __attribute__((aligned(16))) int32_t sums[kFewSumWords];
   __shared__ float sxs[kFewMaxTok];
+  __shared__ float sws[kFewMaxTileRows];
   const int G = d.k / kGroupWeights;
   const int rt = few_tile_rows(G);
   const int tid = static_cast<int>(threadIdx.x);
-  const int r0 = rt >= kThreads ? tid : tid % rt;  // first row; then + kThreads
-  const int m0 = rt >= kThreads ? 0 : tid / rt;
-  const int mstep = rt >= kThreads ? 1 : kThreads / rt;
-  const int nrows = rt >= kThreads ? rt / kThreads : 1;
   const bool s_f16 = d.flags & kFlagScaleF16;
-  float sw[RPT];
-#pragma unroll
-  for (int j = 0; j < RPT; ++j)
-    sw[j] = d.y && j < nrows ? load_scale(d.w_scales, min(tile * rt + r0 + j * kThreads, d.n - 1), s_f16) : 0.0f;
+  for (int t = tid; t < rt; t += kThreads)
+    sws[t] = d.y ? load_scale(d.w_scales, min(tile * rt + t, d.n - 1), s_f16) : 0.0f;
   const bool has_sx = d.x_scales != nullptr;
   if (tid < kFewMaxTok) sxs[tid] = has_sx && tid < d.m ? gmem(d.x_scales)[tid] : 1.0f;
-  for (int t = tid; t < kFewMaxTileRows * kFewMaxTok / 4; t += kThreads)
-    reinterpret_cast<v4i*>(sums)[t] = v4i{0, 0, 0, 0};
+  for (int t = tid; t < kFewSumWords / 4; t += kThreads) reinterpret_cast<v4i*>(sums)[t] = v4i{0, 0, 0, 0};
   Fmt::init_table(tab32, threadIdx.x);
   __syncthreads();
   if constexpr (kPairMask != 0) {
@@ -618,17 +625,56 @@ __device__ __forceinline__ void gemm_few_tile(const GemmDesc& d, int tile) {
     default: gemm_few<Fmt, 16>(d, tile, tab32, pairs, sums); break;
   }
   __syncthreads();
+  const int nq = rt / 4;                // quads of the tile (32, 64 or 128)
+  const int quad = tid % nq;
+  const int m0 = tid / nq;              // first token; then + kThreads / nq
+  const int mstep = kThreads / nq;
+  const int n4 = tile * rt + 4 * quad;  // the quad's first row
+  if (n4 >= d.n) return;
   const bool y_f16 = d.flags & kFlagYF16;
+  const bool full = n4 + 3 < d.n;
+  const int b = quad >> 2;
+  const int q = quad & 3;
+  // whole quads go out as one 8- (fp16) or 16-byte (fp32, int32) store
+  const bool vec_acc = d.acc && full && d.n % 4 == 0 && (reinterpret_cast<uintptr_t>(d.acc) & 15) == 0;
+  const bool vec_y = d.y && full && d.ldy % 4 == 0 &&
+                     (reinterpret_cast<uintptr_t>(d.y) & (y_f16 ? 7 : 15)) == 0;
+  float sw[4];
 #pragma unroll
-  for (int j = 0; j < RPT; ++j) {
-    const int r = r0 + j * kThreads;
-    const int n = tile * rt + r;
-    if (j >= nrows || n >= d.n) break;
-    const int32_t* col = sums + 256 * (r >> 4) + 16 * (4 * (r & 3) + ((r >> 2) & 3));
-    for (int m = m0; m < d.m; m += mstep) {
-      const int32_t v = col[m];
-      if (d.acc) gmem(d.acc)[static_cast<int64_t>(m) * d.n + n] = v;
-      if (d.y) store_y(d.y, static_cast<int64_t>(m) * d.ldy + n, epilogue_i32(v, sw[j], sxs[m], has_sx), y_f16);
+  for (int e = 0; e < 4; ++e) sw[e] = sws[4 * quad + e];
+  for (int m = m0; m < d.m; m += mstep) {
+    const int32_t* col = sums + few_sum_word(b, q, 0, m);
+    v4i v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = col[64 * e];
+    if (d.acc) {
+      const int64_t o = static_cast<int64_t>(m) * d.n + n4;
+      if (vec_acc) {
+        *gmem(reinterpret_cast<v4i*>(d.acc + o)) = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n4 + e < d.n) gmem(d.acc)[o + e] = v[e];
+      }
+    }
+    if (d.y) {
+      const int64_t o = static_cast<int64_t>(m) * d.ldy + n4;
+      float f[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] = epilogue_i32(v[e], sw[e], sxs[m], has_sx);
+      if (vec_y && y_f16) {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        const h4 hv = {static_cast<_Float16>(f[0]), static_cast<_Float16>(f[1]), static_cast<_Float16>(f[2]),
+                       static_cast<_Float16>(f[3])};
+        *gmem(reinterpret_cast<h4*>(static_cast<_Float16*>(d.y) + o)) = hv;
+      } else if (vec_y) {
+        typedef float f4 __attribute__((ext_vector_type(4)));
+        *gmem(reinterpret_cast<f4*>(static_cast<float*>(d.y) + o)) = f4{f[0], f[1], f[2], f[3]};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n4 + e < d.n) store_y(d.y, o + e, f[e], y_f16);
+      }
     }
   }
 }
