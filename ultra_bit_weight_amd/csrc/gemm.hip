@@ -497,9 +497,13 @@ __device__ __forceinline__ int few_sum_word(int b, int q, int e, int i) {
   return kFewSumStride * b + 64 * e + 16 * q + i;
 }
 
-template <class Fmt, int S>
+// `setup` builds the tile's LDS state (tables, zeroed sums, staged scales)
+// and meets the barriers; it runs after this wave's x loads and first code
+// loads are issued, which stay in flight across the barriers (they wait for
+// LDS operations only).
+template <class Fmt, int S, class Setup>
 __device__ __forceinline__ void gemm_few(const GemmDesc& d, int tile, const uint32_t* tab32, const uint2* pairs,
-                                         int32_t* sums) {
+                                         int32_t* sums, const Setup& setup) {
   using Sh = FewShape<Fmt, S>;
   constexpr int NW = Fmt::kWords;
   constexpr int KW = Sh::KW, SPW = Sh::SPW, NBLK = Sh::NBLK, D = Sh::D;
@@ -577,6 +581,7 @@ __device__ __forceinline__ void gemm_few(const GemmDesc& d, int tile, const uint
   uint32_t ring[D][SPW][NW];
 #pragma unroll
   for (int b = 0; b + 1 < D; ++b) fetch(ring[b], b);
+  setup();
   for (int b0 = 0; b0 < NBLK; b0 += D) {
 #pragma unroll
     for (int b = 0; b < D; ++b) {
@@ -606,23 +611,25 @@ __device__ __forceinline__ void gemm_few_tile(const GemmDesc& d, int tile) {
   const int rt = few_tile_rows(G);
   const int tid = static_cast<int>(threadIdx.x);
   const bool s_f16 = d.flags & kFlagScaleF16;
-  for (int t = tid; t < rt; t += kThreads)
-    sws[t] = d.y ? load_scale(d.w_scales, min(tile * rt + t, d.n - 1), s_f16) : 0.0f;
   const bool has_sx = d.x_scales != nullptr;
-  if (tid < kFewMaxTok) sxs[tid] = has_sx && tid < d.m ? gmem(d.x_scales)[tid] : 1.0f;
-  for (int t = tid; t < kFewSumWords / 4; t += kThreads) reinterpret_cast<v4i*>(sums)[t] = v4i{0, 0, 0, 0};
-  Fmt::init_table(tab32, threadIdx.x);
-  __syncthreads();
-  if constexpr (kPairMask != 0) {
-    Fmt::init_pair_table(pairs, tab32, threadIdx.x, kThreads);
+  auto setup = [&]() {
+    for (int t = tid; t < rt; t += kThreads)
+      sws[t] = d.y ? load_scale(d.w_scales, min(tile * rt + t, d.n - 1), s_f16) : 0.0f;
+    if (tid < kFewMaxTok) sxs[tid] = has_sx && tid < d.m ? gmem(d.x_scales)[tid] : 1.0f;
+    for (int t = tid; t < kFewSumWords / 4; t += kThreads) reinterpret_cast<v4i*>(sums)[t] = v4i{0, 0, 0, 0};
+    Fmt::init_table(tab32, threadIdx.x);
     __syncthreads();
-  }
+    if constexpr (kPairMask != 0) {
+      Fmt::init_pair_table(pairs, tab32, threadIdx.x, kThreads);
+      __syncthreads();
+    }
+  };
   switch (few_slices(G)) {
-    case 1: gemm_few<Fmt, 1>(d, tile, tab32, pairs, sums); break;
-    case 2: gemm_few<Fmt, 2>(d, tile, tab32, pairs, sums); break;
-    case 4: gemm_few<Fmt, 4>(d, tile, tab32, pairs, sums); break;
-    case 8: gemm_few<Fmt, 8>(d, tile, tab32, pairs, sums); break;
-    default: gemm_few<Fmt, 16>(d, tile, tab32, pairs, sums); break;
+    case 1: gemm_few<Fmt, 1>(d, tile, tab32, pairs, sums, setup); break;
+    case 2: gemm_few<Fmt, 2>(d, tile, tab32, pairs, sums, setup); break;
+    case 4: gemm_few<Fmt, 4>(d, tile, tab32, pairs, sums, setup); break;
+    case 8: gemm_few<Fmt, 8>(d, tile, tab32, pairs, sums, setup); break;
+    default: gemm_few<Fmt, 16>(d, tile, tab32, pairs, sums, setup); break;
   }
   __syncthreads();
   const int nq = rt / 4;                // quads of the tile (32, 64 or 128)
