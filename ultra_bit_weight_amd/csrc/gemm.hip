@@ -501,9 +501,18 @@ __device__ __forceinline__ int few_sum_word(int b, int q, int e, int i) {
 // and meets the barriers; it runs after this wave's x loads and first code
 // loads are issued, which stay in flight across the barriers (they wait for
 // LDS operations only).
+// x staged in LDS (tiles with several row groups, k <= 2048): token rows of
+// k / 16 + 1 chunks of 16 bytes (one pad chunk, so that the four quarters'
+// reads of one group fall in different banks).
+constexpr int kFewXChunks = kFewMaxTok * (4 * kGroupWeights * 4 / 16 + 1);
+#ifndef SHERRY_FEW_STAGE_MIN_TOK
+#define SHERRY_FEW_STAGE_MIN_TOK 8
+#endif
+constexpr int kFewStageMinTok = SHERRY_FEW_STAGE_MIN_TOK;
+
 template <class Fmt, int S, class Setup>
 __device__ __forceinline__ void gemm_few(const GemmDesc& d, int tile, const uint32_t* tab32, const uint2* pairs,
-                                         int32_t* sums, const Setup& setup) {
+                                         int32_t* sums, u32x4_t* xst, const Setup& setup) {
   using Sh = FewShape<Fmt, S>;
   constexpr int NW = Fmt::kWords;
   constexpr int KW = Sh::KW, SPW = Sh::SPW, NBLK = Sh::NBLK, D = Sh::D;
@@ -517,21 +526,45 @@ __device__ __forceinline__ void gemm_few(const GemmDesc& d, int tile, const uint
   const int row0 = tile * Sh::RT + rg * (NBLK * 16);
   const int64_t row_words = static_cast<int64_t>(G) * NW;
 
-  // x of token i for this lane's groups (zero past m and past k)
+  // x of token i for this lane's groups (zero past m and past k).  With
+  // several row groups every one of them needs all of x: the workgroup then
+  // copies x once into LDS with contiguous loads (issued first, written
+  // before the set-up's barrier) and the lanes read their slices there.
+  constexpr bool kCanStage = Sh::RG > 1;
+  static_assert(!kCanStage || (S <= 4 && SPW == 1), "staged x: k <= 2048, one slice per wave");
+  // only worth its extra LDS round trip with several tokens
+  const bool stage = kCanStage && d.m >= kFewStageMinTok;
+  constexpr int kThreads = kFewWaves * kWave;
+  constexpr int kStageLoads = kFewXChunks / kThreads + 1;  // 16-byte loads per thread, upper bound
+  const int cpt = d.k / 16;  // chunks per token
   uint32_t xr[SPW][32];
+  u32x4_t xsv[kCanStage ? kStageLoads : 1];
+  auto set_xr = [&](int sp, int u, const u32x4_t& v, bool ok) {
+    xr[sp][4 * u + 0] = ok ? v.x : 0u;
+    xr[sp][4 * u + 1] = ok ? v.y : 0u;
+    xr[sp][4 * u + 2] = ok ? v.z : 0u;
+    xr[sp][4 * u + 3] = ok ? v.w : 0u;
+  };
+  if (stage) {
 #pragma unroll
-  for (int sp = 0; sp < SPW; ++sp) {
-    const int g = 4 * (kw + KW * sp) + q;
-    const bool ok = i < d.m && g < G;
-    const SHERRY_GLOBAL u32x4_t* xp = gmem(reinterpret_cast<const u32x4_t*>(
-        d.x + static_cast<int64_t>(ok ? i : 0) * d.ldx + static_cast<int64_t>(ok ? g : 0) * kGroupWeights));
+    for (int j = 0; j < (kCanStage ? kStageLoads : 0); ++j) {
+      const int c = static_cast<int>(threadIdx.x) + kThreads * j;
+      const int tok = c / cpt;
+      if (tok < d.m)
+        xsv[j] = *gmem(reinterpret_cast<const u32x4_t*>(d.x + static_cast<int64_t>(tok) * d.ldx + 16 * (c % cpt)));
+    }
+  } else {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const u32x4_t v = xp[u];
-      xr[sp][4 * u + 0] = ok ? v.x : 0u;
-      xr[sp][4 * u + 1] = ok ? v.y : 0u;
-      xr[sp][4 * u + 2] = ok ? v.z : 0u;
-      xr[sp][4 * u + 3] = ok ? v.w : 0u;
+    for (int sp = 0; sp < SPW; ++sp) {
+      const int g = 4 * (kw + KW * sp) + q;
+      const bool ok = i < d.m && g < G;
+      const SHERRY_GLOBAL u32x4_t* xp = gmem(reinterpret_cast<const u32x4_t*>(
+          d.x + static_cast<int64_t>(ok ? i : 0) * d.ldx + static_cast<int64_t>(ok ? g : 0) * kGroupWeights));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const u32x4_t v = xp[u];
+        set_xr(sp, u, v, ok);
+      }
     }
   }
   // rows past n and groups past k load valid words (clamped) whose products
@@ -581,7 +614,22 @@ __device__ __forceinline__ void gemm_few(const GemmDesc& d, int tile, const uint
   uint32_t ring[D][SPW][NW];
 #pragma unroll
   for (int b = 0; b + 1 < D; ++b) fetch(ring[b], b);
+  if (stage) {
+#pragma unroll
+    for (int j = 0; j < (kCanStage ? kStageLoads : 0); ++j) {
+      const int c = static_cast<int>(threadIdx.x) + kThreads * j;
+      const int tok = c / cpt;
+      if (tok < d.m) xst[tok * (cpt + 1) + c % cpt] = xsv[j];
+    }
+  }
   setup();
+  if (stage) {
+    const int g = 4 * kw + q;
+    const bool ok = i < d.m && g < G;
+    const u32x4_t* xp = xst + (ok ? i * (cpt + 1) + 8 * g : 0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) set_xr(0, u, xp[u], ok);
+  }
   for (int b0 = 0; b0 < NBLK; b0 += D) {
 #pragma unroll
     for (int b = 0; b < D; ++b) {
@@ -607,6 +655,7 @@ __device__ __forceinline__ void gemm_few_tile(const GemmDesc& d, int tile) {
   __shared__ __attribute__((aligned(16))) int32_t sums[kFewSumWords];
   __shared__ float sxs[kFewMaxTok];
   __shared__ float sws[kFewMaxTileRows];
+  __shared__ u32x4_t xst[kFewXChunks];
   const int G = d.k / kGroupWeights;
   const int rt = few_tile_rows(G);
   const int tid = static_cast<int>(threadIdx.x);
@@ -625,11 +674,11 @@ __device__ __forceinline__ void gemm_few_tile(const GemmDesc& d, int tile) {
     }
   };
   switch (few_slices(G)) {
-    case 1: gemm_few<Fmt, 1>(d, tile, tab32, pairs, sums, setup); break;
-    case 2: gemm_few<Fmt, 2>(d, tile, tab32, pairs, sums, setup); break;
-    case 4: gemm_few<Fmt, 4>(d, tile, tab32, pairs, sums, setup); break;
-    case 8: gemm_few<Fmt, 8>(d, tile, tab32, pairs, sums, setup); break;
-    default: gemm_few<Fmt, 16>(d, tile, tab32, pairs, sums, setup); break;
+    case 1: gemm_few<Fmt, 1>(d, tile, tab32, pairs, sums, xst, setup); break;
+    case 2: gemm_few<Fmt, 2>(d, tile, tab32, pairs, sums, xst, setup); break;
+    case 4: gemm_few<Fmt, 4>(d, tile, tab32, pairs, sums, xst, setup); break;
+    case 8: gemm_few<Fmt, 8>(d, tile, tab32, pairs, sums, xst, setup); break;
+    default: gemm_few<Fmt, 16>(d, tile, tab32, pairs, sums, xst, setup); break;
   }
   __syncthreads();
   const int nq = rt / 4;                // quads of the tile (32, 64 or 128)
