@@ -424,6 +424,19 @@ def extras(torch, sherry, synth, probs_1b, codes_1b, args):
                                   "GBps": round((n * k * 5 / 32 + 4 * n + k) / (us * 1e-6) / 1e9, 1)}
     out["per_call_gemv_1b"] = lat
 
+    # the same grouped launch over 4x the replicas: time per launch grows by
+    # the marginal cost per replica, so the fixed per-launch cost (start-up
+    # and drain, a few microseconds) weighs 4x less
+    R4 = 4 * R
+    codes4, probs4 = build_layer_replicas(torch, sherry, synth, shapes_1b, R4, args.seed + 11)
+    g4 = sherry.GroupedGemv(probs4)
+    mean_ms, _ = time_launches(torch, g4, max(20, args.steps // 4), args.warmup)
+    b4 = R4 * layer_bytes(shapes_1b)
+    out[f"gemv_grouped_1b_x{R4}"] = {"ms_per_launch": round(mean_ms, 4), "GBps": round(b4 / (mean_ms * 1e-3) / 1e9, 1),
+                                     "frac_hbm": round(b4 / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del g4, probs4, codes4
+    torch.cuda.empty_cache()
+
     # 2-bit dense-ternary comparator on the same ternary matrices
     t2_codes = []
     probs_t2 = []
