@@ -295,7 +295,7 @@ sherry_status tern2_gemm(const uint32_t* codes, const void* w_scales, sherry_dty
                          hipStream_t stream);
 
 /* ---- 1.67-bit comparator (same paper, Figure 2 caption, middle: three
- * ternary weights packed into five bits, "3-way patterns"; Abstract: the
+ * ternary weights packed into five bits, in patterns of three; Abstract: the
  * irregular 1.67-bit packing) ----
  * Layout (a reading; the pages give none): a code holds three consecutive
  * weights of a row, c = (t0 + 1) + 3 (t1 + 1) + 9 (t2 + 1) (0..26); 32 codes
