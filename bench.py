@@ -207,9 +207,7 @@ def cpu_baseline(torch, probs, shapes, min_seconds=10.0, max_layers=16):
                       f"numpy oracle limited to 1 thread, {dt:.1f} s"}
 
 
-# ----------------------------------------------------------------- extras ---
-
-def oracle_beside(synth, max_seconds=2.0):
+def cpu_baseline_per_row(synth, max_seconds=2.0):
     """The oracle of each measured row as it stands, one thread, on a bounded
     synthetic sample of that row's workload (a few seconds in all): the CPU
     rate beside each GPU figure.  Rates are per unit of the row's work."""
@@ -266,6 +264,8 @@ def oracle_beside(synth, max_seconds=2.0):
     out["cores"] = 1
     return out
 
+
+# ----------------------------------------------------------------- extras ---
 
 def peak_probes(torch, sherry):
     """Measured ceilings beside the published peaks: a 1 GiB streaming read
@@ -626,7 +626,6 @@ def extras(torch, sherry, synth, probs_1b, codes_1b, args):
     if isinstance(gus, float):
         lay["graph_us_per_token_16_layers"] = round(16 * gus, 1)
     out["f4_decode_layer_1b"] = lay
-    out["oracle_beside"] = oracle_beside(synth)
     out["library_beside"] = library_beside(torch, synth, args)
     out["peak_probes"] = peak_probes(torch, sherry)
 
@@ -772,6 +771,8 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(torch, probs, shapes)
+        if not args.no_extras:
+            line["cpu_baseline"]["per_row"] = cpu_baseline_per_row(synth)
         print(f"# cpu oracle: {line['cpu_baseline']['value']:.3e} weights/s", file=sys.stderr, flush=True)
     if not args.no_extras:
         ex = extras(torch, sherry, synth, probs, codes, args)
