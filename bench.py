@@ -156,6 +156,45 @@ def time_launches(torch, fn, steps, warmup, settle_ms=None):
     return a.elapsed_time(b) / steps, wall_ms
 
 
+def per_launch_us(torch, fn, steps=200):
+    """Each of `steps` calls of fn between its own HIP event pair on the
+    current stream (call right after time_launches, so the clock has
+    settled): p10 / median / p90 of the per-call times in microseconds.  The
+    events add a little to each call, so these are upper bounds beside the
+    mean that time_launches gives."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    return {"p10": round(t[steps // 10], 2), "median": round(t[steps // 2], 2), "p90": round(t[(9 * steps) // 10], 2)}
+
+
+def per_call_table(torch, probs, shapes, call, x_bytes=1, y_bytes=2, with_sx=True):
+    """Per-call latency of each matrix of a layer, rotating over the layer
+    replicas in `probs` so that the codes come from HBM, not the last-level
+    cache: the mean over 200 back-to-back calls and the per-call
+    percentiles."""
+    lat = {}
+    for name, n, k in shapes:
+        sel = [p for p in probs if p["name"] == name]
+        it = [0]
+
+        def one():
+            p = sel[it[0] % len(sel)]
+            it[0] += 1
+            call(p)
+        mean_ms, _ = time_launches(torch, one, 200, 20)
+        us = mean_ms * 1e3
+        byts = n * k * 5 / 32 + 2 * n + x_bytes * k + y_bytes * n + (4 if with_sx else 0)
+        lat[f"{name}_{n}x{k}"] = {"us_per_call": round(us, 2), "GBps": round(byts / (us * 1e-6) / 1e9, 1),
+                                  "per_call_us": per_launch_us(torch, one)}
+    return lat
+
+
 def traffic_from_summary():
     """HBM bytes per launch of the grouped kernel from the committed counter
     summary, or None if absent or taken on a different version of the kernel."""
@@ -181,7 +220,7 @@ def cpu_baseline(torch, probs, shapes, min_seconds=10.0, max_layers=16):
     each, replicas 0, 1, ...) until at least min_seconds of CPU work:
     unpack + exact product + epilogue, per matrix."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import sherry_ref
 
@@ -202,9 +241,41 @@ def cpu_baseline(torch, probs, shapes, min_seconds=10.0, max_layers=16):
             done += 1
             if dt >= min_seconds:
                 break
-    return {"value": done * per_layer / dt, "unit": "weights/s", "cores": 1, "kind": "oracle",
+    line = {"value": done * per_layer / dt, "unit": "weights/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} LLaMA-3.2-1B decoder layer(s) (7 matrices, {per_layer} weights each), batch 1, "
                       f"numpy oracle limited to 1 thread, {dt:.1f} s"}
+    # the same oracle with the BLAS pool at its default size, on fewer layers
+    with threadpool_limits(limits=None):
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        done_all, dt_all = 0, 0.0
+        for r in range(max_layers):
+            layer = [p for p in probs if p["replica"] == r]
+            if not layer:
+                break
+            host = [(p["codes"].cpu().numpy().view(np.uint32), p["scales"].cpu().numpy(), p["n"], p["k"],
+                     p["x"].cpu().numpy(), p["x_scale"].cpu().numpy()[0]) for p in layer]
+            t0 = time.perf_counter()
+            for words, sw, n, k, x, sx in host:
+                sherry_ref.gemv_i8(words, sw, n, k, x, sx, np.float16)
+            dt_all += time.perf_counter() - t0
+            done_all += 1
+            if dt_all >= min_seconds / 4:
+                break
+    line["all_threads"] = {"value": done_all * per_layer / dt_all, "blas_threads": threads,
+                           "sample": f"{done_all} layer(s), {dt_all:.1f} s"}
+    line["host"] = {"cpus_in_affinity": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
+    return line
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline_per_row(synth, max_seconds=2.0):
@@ -409,20 +480,8 @@ def extras(torch, sherry, synth, probs_1b, codes_1b, args):
     R = args.replicas
 
     # per-call latency of single matrices, rotating over replicas
-    lat = {}
-    for name, n, k in shapes_1b:
-        sel = [p for p in probs_1b if p["name"] == name]
-        it = [0]
-
-        def one():
-            p = sel[it[0] % len(sel)]
-            it[0] += 1
-            sherry.gemv(p["codes"], p["scales"], p["x"], p["x_scale"], out=p["y"])
-        mean_ms, _ = time_launches(torch, one, 200, 20)
-        us = mean_ms * 1e3
-        lat[f"{name}_{n}x{k}"] = {"us_per_call": round(us, 2),
-                                  "GBps": round((n * k * 5 / 32 + 4 * n + k) / (us * 1e-6) / 1e9, 1)}
-    out["per_call_gemv_1b"] = lat
+    out["per_call_gemv_1b"] = per_call_table(
+        torch, probs_1b, shapes_1b, lambda p: sherry.gemv(p["codes"], p["scales"], p["x"], p["x_scale"], out=p["y"]))
 
     # the same grouped launch over 4x the replicas: time per launch grows by
     # the marginal cost per replica, so the fixed per-launch cost (start-up
@@ -456,6 +515,12 @@ def extras(torch, sherry, synth, probs_1b, codes_1b, args):
     out["tern2_grouped_1b"] = {"ms_per_launch": round(mean_ms, 4), "weights_per_s": weights / (mean_ms * 1e-3),
                                "GBps": round(bytes2 / (mean_ms * 1e-3) / 1e9, 1),
                                "frac_hbm": round(bytes2 / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    # per call; GBps on the 2-bit bytes (8/5 of the 3:4 codes)
+    t2lat = per_call_table(
+        torch, probs_t2, shapes_1b, lambda p: sherry.tern2_gemv(p["codes"], p["scales"], p["x"], p["x_scale"], out=p["y"]))
+    for (name, n, k), v in zip(shapes_1b, t2lat.values()):
+        v["GBps"] = round((n * k / 4 + 2 * n + k + 2 * n + 4) / (v["us_per_call"] * 1e-6) / 1e9, 1)
+    out["per_call_tern2_gemv_1b"] = t2lat
     # same grouped launch on the 1.25-bit codes, for the ratio
     del g2, probs_t2, t2_codes
     torch.cuda.empty_cache()
@@ -493,6 +558,10 @@ def extras(torch, sherry, synth, probs_1b, codes_1b, args):
                               "weights_per_s": w3 / (mean_ms * 1e-3),
                               "GBps": round(b3 / (mean_ms * 1e-3) / 1e9, 1),
                               "frac_hbm": round(b3 / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    out["per_call_gemv_bf16_3b"] = per_call_table(
+        torch, probs_3b, shapes_3b, lambda p: sherry.gemv(p["codes"], p["scales"], p["x"], None, out_dtype=torch.float32,
+                                                          out=p["y"]),
+        x_bytes=2, y_bytes=4, with_sx=False)
     # the same launch on the matrix cores (sherry_gemv_plan_mfma)
     g3m = sherry.GroupedGemv(probs_3b, mfma=True)
     mean_ms, _ = time_launches(torch, g3m, args.steps, args.warmup)

@@ -185,15 +185,20 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
     load_x();
   }
   init_tables<Fmt>(tab32, tab);
-  for (int base = row_begin, r = r0; base < row_end; base += NR * RPI, r += NR * RPI) {
-    // all NR steps run; rows past the tile end are clamped loads whose
-    // results are never stored (no branch inside the ring)
+  // Every round runs all NR steps; rows past the tile end are clamped loads
+  // whose results are never stored (no branch inside the ring).  The last
+  // round fetches only its own last row: nothing follows it.
+  int base = row_begin, r = r0;
+  for (; base + NR * RPI < row_end; base += NR * RPI, r += NR * RPI) {
 #pragma unroll
     for (int b = 0; b < NR; ++b) {
       fetch(ring[(b + NR - 1) % NR], r + (b + NR - 1) * RPI);
       step(ring[b], r + b * RPI);
     }
   }
+  fetch(ring[NR - 1], r + (NR - 1) * RPI);
+#pragma unroll
+  for (int b = 0; b < NR; ++b) step(ring[b], r + b * RPI);
 }
 
 // Any k % 128 == 0: 64 lanes per row, x read per group (not register-resident).
@@ -334,6 +339,9 @@ __device__ __forceinline__ void gemv_bf16_rows(const GemvDesc& d, int row_begin,
   const int r0 = row_begin + wave * RPW + rs;
 #pragma unroll
   for (int b = 0; b + 1 < NR; ++b) fetch(ring[b], r0 + b * RPI);
+  // All NR steps of every round run (rows past the tile end are clamped
+  // loads).  Peeling the last round's surplus fetches, as the int8 walk
+  // does, measured 6 % slower here.
   for (int base = row_begin, r = r0; base < row_end; base += NR * RPI, r += NR * RPI) {
 #pragma unroll
     for (int b = 0; b < NR; ++b) {
