@@ -103,9 +103,20 @@ __device__ __forceinline__ void load_x_group(const void* x, int k, int g, uint32
   }
 }
 
+// int8 x staged once per workgroup in LDS: 16-byte chunk c at slot c + c / 8
+// (one pad chunk after each group's 128 bytes, so that the 16 lanes reading
+// 16 group slices hit 16 disjoint sets of four banks).
+constexpr int kMaxStagedKI8 = 8192;  // largest k of the register-resident classes
+#ifndef SHERRY_GEMV_XLDS
+#define SHERRY_GEMV_XLDS 1
+#endif
+constexpr int kXsChunks = kMaxStagedKI8 / 16 * 9 / 8;
+constexpr int kXsPerThread = kMaxStagedKI8 / 16 / kGemvThreads;
+static_assert(kXsPerThread * 16 * kGemvThreads == kMaxStagedKI8, "x staging split");
+
 template <class Fmt, int L, int GPL, int GR = GPL * L, bool XQ = false>
 __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, int row_end, uint32_t* tab32,
-                                             uint2* tab, int32_t* out, XQuant xq = XQuant{}) {
+                                             uint2* tab, int32_t* out, u32x4_t* xs, XQuant xq = XQuant{}) {
   constexpr int RPW = kWave / L;
   constexpr int RPI = (kGemvThreads / kWave) * RPW;
   constexpr int NW = Fmt::kWords;
@@ -115,10 +126,24 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
   const int rs = lane / L;
   constexpr int G = GR;  // groups per row (lanes t L + lp >= G hold none: x = 0)
 
-  // Start-up order keeps the memory pipe busy: this lane's x slice (shared
-  // by every row, so cache-resident after the first workgroup), then the
-  // first kRing - 1 ring entries, and only then the LDS tables and barrier.
+  // Start-up order keeps the memory pipe busy: x (shared by every row, so
+  // cache-resident after the first workgroup), then the first kRing - 1 ring
+  // entries, and only then the LDS writes, tables and barriers.  x comes
+  // either as the lane's own 128-byte slice straight from global memory, or
+  // (XS) as one or two 16-byte chunks per thread staged through LDS, which
+  // replaces eight loads per lane with at most two per thread.
+  constexpr bool XS = SHERRY_GEMV_XLDS && !XQ && Fmt::kGroupW == 128;
   uint32_t xr[GPL][32];
+  u32x4_t xv[XS ? kXsPerThread : 1];
+  const int nchunks = d.k / 16;
+  if constexpr (XS) {
+    const SHERRY_GLOBAL u32x4_t* xg = gmem(static_cast<const u32x4_t*>(d.x));
+#pragma unroll
+    for (int j = 0; j < kXsPerThread; ++j) {
+      const int c = static_cast<int>(threadIdx.x) + kGemvThreads * j;
+      if (c < nchunks) xv[j] = xg[c];
+    }
+  }
   auto load_x = [&]() {
 #pragma unroll
     for (int t = 0; t < GPL; ++t) {
@@ -141,7 +166,7 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
       }
     }
   };
-  if constexpr (!XQ) load_x();
+  if constexpr (!XQ && !XS) load_x();
   // Rows past the tile load the tile's last row instead (results discarded).
   // A ring of kRing register buffers (the loop is unrolled by kRing): while
   // one row is decoded, the words of the next kRing - 1 rows are in flight.
@@ -184,7 +209,29 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
     quantize_x_lds(d, xq.dt, xq.xl, xq.sx, xq.wmax);
     load_x();
   }
-  init_tables<Fmt>(tab32, tab);
+  if constexpr (XS) {
+#pragma unroll
+    for (int j = 0; j < kXsPerThread; ++j) {
+      const int c = static_cast<int>(threadIdx.x) + kGemvThreads * j;
+      if (c < nchunks) xs[c + c / 8] = xv[j];
+    }
+  }
+  init_tables<Fmt>(tab32, tab);  // its barriers also publish the staged x
+  if constexpr (XS) {
+#pragma unroll
+    for (int t = 0; t < GPL; ++t) {
+      const bool has = t * L + lp < G;
+      const u32x4_t* xp = xs + 9 * min(t * L + lp, G - 1);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const u32x4_t v = xp[q];
+        xr[t][4 * q + 0] = has ? v.x : 0u;
+        xr[t][4 * q + 1] = has ? v.y : 0u;
+        xr[t][4 * q + 2] = has ? v.z : 0u;
+        xr[t][4 * q + 3] = has ? v.w : 0u;
+      }
+    }
+  }
   // Every round runs all NR steps; rows past the tile end are clamped loads
   // whose results are never stored (no branch inside the ring).  The last
   // round fetches only its own last row: nothing follows it.
@@ -425,12 +472,13 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_i8_kernel(GemvDesc d, int t
   __shared__ uint32_t tab32[32];
   __shared__ uint2 tab[Fmt::kPairEntries];
   __shared__ int32_t res[kMaxTileRows];
+  __shared__ u32x4_t xs[SHERRY_GEMV_XLDS && L > 0 && Fmt::kGroupW == 128 ? kXsChunks : 1];
   const int row0 = blockIdx.x * tile_rows;
   const int row1 = min(row0 + tile_rows, d.n);
   if (L == 0)
     gemv_i8_rows_generic<Fmt>(d, row0, row1, tab32, tab, res);
   else
-    gemv_i8_rows<Fmt, (L > 0 ? L : 64), GPL, (L > 0 ? GR : 64)>(d, row0, row1, tab32, tab, res);
+    gemv_i8_rows<Fmt, (L > 0 ? L : 64), GPL, (L > 0 ? GR : 64)>(d, row0, row1, tab32, tab, res, xs);
   __syncthreads();
   finalize_i8(d, row0, row1, res, d.x_scale != nullptr, d.x_scale ? *gmem(d.x_scale) : 1.0f);
 }
@@ -453,7 +501,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_i8_xq_kernel(GemvDesc d, in
   if constexpr (L == 0)
     gemv_i8_rows_generic<Fmt>(d, row0, row1, tab32, tab, res, xq);
   else
-    gemv_i8_rows<Fmt, L, GPL, GR, true>(d, row0, row1, tab32, tab, res, xq);
+    gemv_i8_rows<Fmt, L, GPL, GR, true>(d, row0, row1, tab32, tab, res, nullptr, xq);
   __syncthreads();
   finalize_i8(d, row0, row1, res, true, sx);
   if (sx_out && blockIdx.x == 0 && threadIdx.x == 0) *gmem(sx_out) = sx;
@@ -505,6 +553,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_i8_grouped_kernel(const cha
   __shared__ uint32_t tab32[32];
   __shared__ uint2 tab[Fmt::kPairEntries];
   __shared__ int32_t res[kMaxGroupedTileRows];
+  __shared__ u32x4_t xs[SHERRY_GEMV_XLDS && Fmt::kGroupW == 128 ? kXsChunks : 1];
   const PlanHeader* h = reinterpret_cast<const PlanHeader*>(plan);
   const GemvDesc* descs = reinterpret_cast<const GemvDesc*>(plan + sizeof(PlanHeader));
   const PlanTile* tiles = reinterpret_cast<const PlanTile*>(descs + h->count);
@@ -514,16 +563,16 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_i8_grouped_kernel(const cha
   const int row1 = min(row0 + tile_rows_of(d.kclass, false), d.n);
   if constexpr (Fmt::kGroupW != 128) {
     switch (d.kclass) {
-      case kT3k2048: gemv_i8_rows<Fmt, 32, 1, 22>(d, row0, row1, tab32, tab, res); break;
-      case kT3k8192: gemv_i8_rows<Fmt, 64, 2, 86>(d, row0, row1, tab32, tab, res); break;
+      case kT3k2048: gemv_i8_rows<Fmt, 32, 1, 22>(d, row0, row1, tab32, tab, res, nullptr); break;
+      case kT3k8192: gemv_i8_rows<Fmt, 64, 2, 86>(d, row0, row1, tab32, tab, res, nullptr); break;
       default: gemv_i8_rows_generic<Fmt>(d, row0, row1, tab32, tab, res); break;
     }
   } else switch (d.kclass) {
-    case k1024: gemv_i8_rows<Fmt, 8, 1>(d, row0, row1, tab32, tab, res); break;
-    case k2048: gemv_i8_rows<Fmt, 16, 1>(d, row0, row1, tab32, tab, res); break;
-    case k4096: gemv_i8_rows<Fmt, 32, 1>(d, row0, row1, tab32, tab, res); break;
-    case k8192: gemv_i8_rows<Fmt, 64, 1>(d, row0, row1, tab32, tab, res); break;
-    case k3072: gemv_i8_rows<Fmt, 32, 1, 24>(d, row0, row1, tab32, tab, res); break;
+    case k1024: gemv_i8_rows<Fmt, 8, 1>(d, row0, row1, tab32, tab, res, xs); break;
+    case k2048: gemv_i8_rows<Fmt, 16, 1>(d, row0, row1, tab32, tab, res, xs); break;
+    case k4096: gemv_i8_rows<Fmt, 32, 1>(d, row0, row1, tab32, tab, res, xs); break;
+    case k8192: gemv_i8_rows<Fmt, 64, 1>(d, row0, row1, tab32, tab, res, xs); break;
+    case k3072: gemv_i8_rows<Fmt, 32, 1, 24>(d, row0, row1, tab32, tab, res, xs); break;
     default: gemv_i8_rows_generic<Fmt>(d, row0, row1, tab32, tab, res); break;
   }
   __syncthreads();
