@@ -56,7 +56,9 @@ extern "C" {
 typedef enum {
   SHERRY_OK = 0,
   SHERRY_EINVAL = 1,  /* null pointer where one is required, n/k/m <= 0, bad enum */
-  SHERRY_ESHAPE = 2,  /* k % 128 != 0, leading dimension too small, size overflow */
+  SHERRY_ESHAPE = 2,  /* k % 128 != 0, leading dimension too small, size overflow; for the
+                         products also one matrix's codes (or a GEMM's x, m * ldx bytes)
+                         above 4 GiB - 1 bytes, the reach of the kernels' 32-bit offsets */
   SHERRY_EDTYPE = 3,  /* unsupported dtype combination */
   SHERRY_EALIGN = 4,  /* a pointer or leading dimension breaks the stated alignment */
   SHERRY_EDEVICE = 5, /* no HIP device, or the current device is not gfx950 */

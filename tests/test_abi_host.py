@@ -90,6 +90,27 @@ def test_gemv_validation(lib, fn):
     assert gemv(lib, fn=fn) == EDEVICE
 
 
+@pytest.mark.parametrize("fn, row_bytes", [("sherry_gemv", 64 * 20), ("tern2_gemv", 64 * 32),
+                                           ("tern3_gemv", 86 * 20), ("sherry_gemm", 64 * 20),
+                                           ("tern2_gemm", 64 * 32)])
+def test_codes_below_4gib(lib, fn, row_bytes):
+    """The kernels address one matrix's codes with 32-bit byte offsets: the
+    largest accepted n at k = 8192 is the last whose codes fit 2^32 - 1 bytes
+    in that format (5 words per 128 weights, 8 for the 2-bit codes, 5 per 96
+    weights for the 1.67-bit codes)."""
+    n_max = (2 ** 32 - 1) // row_bytes
+    call = gemm if fn.endswith("gemm") else gemv
+    extra = {"ldx": 8192, "ldy": n_max + 1} if fn.endswith("gemm") else {}
+    assert call(lib, n=n_max, k=8192, fn=fn, **extra) == EDEVICE
+    assert call(lib, n=n_max + 1, k=8192, fn=fn, **extra) == ESHAPE
+
+
+def test_gemm_x_below_4gib(lib):
+    m_max = (2 ** 32 - 1) // 8192
+    assert gemm(lib, m=m_max, k=8192, ldx=8192) == EDEVICE
+    assert gemm(lib, m=m_max + 1, k=8192, ldx=8192) == ESHAPE
+
+
 def test_gemv_bf16_rules(lib):
     assert gemv(lib, x_dt=BF16, acc=None, y_dt=F32) == EDEVICE  # valid
     assert gemv(lib, x_dt=BF16, acc=A, y_dt=F32) == EDTYPE       # no int32 sums for bf16

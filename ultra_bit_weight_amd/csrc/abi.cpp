@@ -44,6 +44,15 @@ sherry_status check_nk(int64_t n, int64_t k) {
   return SHERRY_OK;
 }
 
+// The kernels address one matrix's codes with 32-bit byte offsets from its
+// base pointer, so the codes of every matrix stay below 4 GiB.
+bool codes_fit_32(int32_t format, int64_t n, int64_t k) {
+  const uint64_t groups = format == kFmtTern3 ? static_cast<uint64_t>((k + 95) / 96)
+                                              : static_cast<uint64_t>(k / kGroupWeights);
+  const uint64_t words = format == kFmtTern2 ? 8 : kGroupWords;
+  return static_cast<uint64_t>(n) * groups * words * 4 <= 0xFFFFFFFFull;
+}
+
 std::atomic<int> g_dev_state[256];  // 0 unknown, 1 gfx950, 2 other
 
 sherry_status check_device() {
@@ -64,11 +73,13 @@ sherry_status check_device() {
 sherry_status launched(hipError_t e) { return e == hipSuccess ? SHERRY_OK : SHERRY_ELAUNCH; }
 
 // Shared validation of a batch-1 product (every format).
-sherry_status check_gemv(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,
-                         const void* x, sherry_dtype x_dt, const float* x_scale, const int32_t* acc, const void* y,
-                         sherry_dtype y_dt, bool allow_bf16) {
+sherry_status check_gemv(int32_t format, const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n,
+                         int64_t k, const void* x, sherry_dtype x_dt, const float* x_scale, const int32_t* acc,
+                         const void* y, sherry_dtype y_dt) {
+  const bool allow_bf16 = format == kFmtSherry;
   if (!codes || !w_scales || !x || (!acc && !y)) return SHERRY_EINVAL;
   if (sherry_status s = check_nk(n, k)) return s;
+  if (!codes_fit_32(format, n, k)) return SHERRY_ESHAPE;
   if (!is_scale_dt(s_dt)) return SHERRY_EDTYPE;
   if (x_dt == SHERRY_I8) {
     if (y && y_dt != SHERRY_F32 && y_dt != SHERRY_F16) return SHERRY_EDTYPE;
@@ -102,8 +113,7 @@ GemvDesc make_desc(int32_t format, const uint32_t* codes, const void* w_scales, 
 sherry_status gemv_impl(int32_t format, const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n,
                         int64_t k, const void* x, sherry_dtype x_dt, const float* x_scale, int32_t* acc, void* y,
                         sherry_dtype y_dt, hipStream_t stream) {
-  if (sherry_status s = check_gemv(codes, w_scales, s_dt, n, k, x, x_dt, x_scale, acc, y, y_dt,
-                                   format == kFmtSherry))
+  if (sherry_status s = check_gemv(format, codes, w_scales, s_dt, n, k, x, x_dt, x_scale, acc, y, y_dt))
     return s;
   if (sherry_status s = check_device()) return s;
   const GemvDesc d = make_desc(format, codes, w_scales, s_dt, n, k, x, x_scale, acc, y, y_dt);
@@ -116,7 +126,7 @@ sherry_status gemv_quant_impl(int32_t format, const uint32_t* codes, const void*
                               int32_t* acc, void* y, sherry_dtype y_dt, hipStream_t stream) {
   if (!codes || !w_scales || !x || (!acc && !y)) return SHERRY_EINVAL;
   if (sherry_status s = check_nk(n, k)) return s;
-  if (k > kActMaxK) return SHERRY_ESHAPE;
+  if (k > kActMaxK || !codes_fit_32(format, n, k)) return SHERRY_ESHAPE;
   int dt = 0;
   switch (x_dt) {
     case SHERRY_F32: dt = kActF32; break;
@@ -134,7 +144,8 @@ sherry_status gemv_quant_impl(int32_t format, const uint32_t* codes, const void*
 }
 
 // Validation of one product for M tokens; fills the kernel record.
-sherry_status check_gemm(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,
+sherry_status check_gemm(int32_t format, const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n,
+                         int64_t k,
                          const void* x, sherry_dtype x_dt, int64_t m, int64_t ldx, const float* x_scales, int32_t* acc,
                          void* y, sherry_dtype y_dt, int64_t ldy, GemmDesc* out) {
   if (!codes || !w_scales || !x || (!acc && !y)) return SHERRY_EINVAL;
@@ -144,8 +155,7 @@ sherry_status check_gemm(const uint32_t* codes, const void* w_scales, sherry_dty
   if (ldx > std::numeric_limits<int64_t>::max() / m || (y && ldy > std::numeric_limits<int64_t>::max() / m))
     return SHERRY_ESHAPE;
   // the tiled kernel addresses one matrix's codes and x with 32-bit offsets
-  if (static_cast<uint64_t>(n) * static_cast<uint64_t>(k / kGroupWeights) * kGroupWords * 4 > 0xFFFFFFFFull ||
-      static_cast<uint64_t>(m) * static_cast<uint64_t>(ldx) > 0xFFFFFFFFull)
+  if (!codes_fit_32(format, n, k) || static_cast<uint64_t>(m) * static_cast<uint64_t>(ldx) > 0xFFFFFFFFull)
     return SHERRY_ESHAPE;
   if (!is_scale_dt(s_dt) || x_dt != SHERRY_I8) return SHERRY_EDTYPE;
   if (y && y_dt != SHERRY_F32 && y_dt != SHERRY_F16) return SHERRY_EDTYPE;
@@ -172,7 +182,8 @@ sherry_status gemm_impl(int32_t format, const uint32_t* codes, const void* w_sca
                         int64_t k, const void* x, sherry_dtype x_dt, int64_t m, int64_t ldx, const float* x_scales,
                         int32_t* acc, void* y, sherry_dtype y_dt, int64_t ldy, hipStream_t stream) {
   GemmDesc d;
-  if (sherry_status s = check_gemm(codes, w_scales, s_dt, n, k, x, x_dt, m, ldx, x_scales, acc, y, y_dt, ldy, &d))
+  if (sherry_status s =
+          check_gemm(format, codes, w_scales, s_dt, n, k, x, x_dt, m, ldx, x_scales, acc, y, y_dt, ldy, &d))
     return s;
   if (sherry_status s = check_device()) return s;
   return launched(launch_gemm(d, format, stream));
@@ -230,7 +241,7 @@ sherry_status gemm_plan_impl(int32_t format, const sherry_gemm_problem* probs, i
   std::vector<GemmDesc> descs(static_cast<size_t>(count));
   for (int32_t i = 0; i < count; ++i) {
     const sherry_gemm_problem& p = probs[i];
-    if (sherry_status s = check_gemm(p.codes, p.w_scales, s_dt, p.n, p.k, p.x, x_dt, p.m, p.ldx, p.x_scales, p.acc,
+    if (sherry_status s = check_gemm(format, p.codes, p.w_scales, s_dt, p.n, p.k, p.x, x_dt, p.m, p.ldx, p.x_scales, p.acc,
                                      p.y, y_dt, p.ldy, &descs[static_cast<size_t>(i)]))
       return s;
   }
@@ -303,8 +314,8 @@ sherry_status plan_impl(int32_t format, const sherry_gemv_problem* probs, int32_
   if (!probs || count <= 0 || !plan) return SHERRY_EINVAL;
   for (int32_t i = 0; i < count; ++i) {
     const sherry_gemv_problem& p = probs[i];
-    if (sherry_status s = check_gemv(p.codes, p.w_scales, s_dt, p.n, p.k, p.x, x_dt, p.x_scale, p.acc, p.y, y_dt,
-                                     format == kFmtSherry))
+    if (sherry_status s = check_gemv(format, p.codes, p.w_scales, s_dt, p.n, p.k, p.x, x_dt, p.x_scale, p.acc, p.y,
+                                     y_dt))
       return s;
   }
   if (mfma) {
