@@ -56,6 +56,20 @@ struct Sherry3of4 {
   __device__ __forceinline__ static void load(uint32_t* w, const uint32_t* row, int G, int g) {
     load_group(w, row, G, g);
   }
+  // The same words of the row at byte offset ro from a uniform base: 32-bit
+  // lane offsets (one matrix's codes stay below 4 GiB), so the loads take the
+  // base from scalar registers and need no 64-bit address arithmetic.
+  __device__ __forceinline__ static void load_at(uint32_t* w, const SHERRY_GLOBAL char* base, uint32_t ro, int G,
+                                                 int g) {
+    const u32x4_t h = __builtin_nontemporal_load(
+        reinterpret_cast<const SHERRY_GLOBAL u32x4_t*>(base + (ro + 16u * static_cast<uint32_t>(g))));
+    w[0] = h.x;
+    w[1] = h.y;
+    w[2] = h.z;
+    w[3] = h.w;
+    w[4] = __builtin_nontemporal_load(
+        reinterpret_cast<const SHERRY_GLOBAL uint32_t*>(base + (ro + 4u * static_cast<uint32_t>(4 * G + g))));
+  }
   // Same words with ordinary (cached) loads, for kernels whose waves share
   // the cache lines of a row.
   __device__ __forceinline__ static void load_cached(uint32_t* w, const uint32_t* row, int G, int g) {
@@ -128,6 +142,21 @@ struct Tern2 {
     const u32x4_t* p = reinterpret_cast<const u32x4_t*>(row + 8 * g);
     const u32x4_t a = __builtin_nontemporal_load(gmem(p));
     const u32x4_t b = __builtin_nontemporal_load(gmem(p + 1));
+    w[0] = a.x;
+    w[1] = a.y;
+    w[2] = a.z;
+    w[3] = a.w;
+    w[4] = b.x;
+    w[5] = b.y;
+    w[6] = b.z;
+    w[7] = b.w;
+  }
+  __device__ __forceinline__ static void load_at(uint32_t* w, const SHERRY_GLOBAL char* base, uint32_t ro, int,
+                                                 int g) {
+    const SHERRY_GLOBAL u32x4_t* p =
+        reinterpret_cast<const SHERRY_GLOBAL u32x4_t*>(base + (ro + 32u * static_cast<uint32_t>(g)));
+    const u32x4_t a = __builtin_nontemporal_load(p);
+    const u32x4_t b = __builtin_nontemporal_load(p + 1);
     w[0] = a.x;
     w[1] = a.y;
     w[2] = a.z;

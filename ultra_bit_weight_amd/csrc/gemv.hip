@@ -171,10 +171,17 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
   // A ring of kRing register buffers (the loop is unrolled by kRing): while
   // one row is decoded, the words of the next kRing - 1 rows are in flight.
   const int last = row_end - 1;
-  auto fetch = [&](uint32_t (&buf)[GPL][NW], int row) {
-    const uint32_t* rp = d.codes + static_cast<int64_t>(min(row, last)) * (G * NW);
+  // Rows are addressed by 32-bit byte offsets from the matrix base (the host
+  // keeps one matrix's codes below 4 GiB).  A fetch takes the unclamped
+  // offset of its row, advanced by additions, and clamps it to the tile's
+  // last row: no multiply per row.
+  constexpr uint32_t kRowBytes = G * NW * 4;
+  const SHERRY_GLOBAL char* cbase = gmem(reinterpret_cast<const char*>(d.codes));
+  const uint32_t ro_last = static_cast<uint32_t>(last) * kRowBytes;
+  auto fetch = [&](uint32_t (&buf)[GPL][NW], uint32_t ro_unclamped) {
+    const uint32_t ro = min(ro_unclamped, ro_last);
 #pragma unroll
-    for (int t = 0; t < GPL; ++t) Fmt::load(buf[t], rp, G, min(t * L + lp, G - 1));
+    for (int t = 0; t < GPL; ++t) Fmt::load_at(buf[t], cbase, ro, G, min(t * L + lp, G - 1));
   };
   auto step = [&](const uint32_t (&buf)[GPL][NW], int row) {
     constexpr int C = kDotChains;  // independent dot4 accumulation chains
@@ -204,7 +211,7 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
   uint32_t ring[NR][GPL][NW];
   const int r0 = row_begin + wave * RPW + rs;
 #pragma unroll
-  for (int b = 0; b + 1 < NR; ++b) fetch(ring[b], r0 + b * RPI);
+  for (int b = 0; b + 1 < NR; ++b) fetch(ring[b], static_cast<uint32_t>(r0 + b * RPI) * kRowBytes);
   if constexpr (XQ) {
     quantize_x_lds(d, xq.dt, xq.xl, xq.sx, xq.wmax);
     load_x();
@@ -236,14 +243,15 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
   // whose results are never stored (no branch inside the ring).  The last
   // round fetches only its own last row: nothing follows it.
   int base = row_begin, r = r0;
-  for (; base + NR * RPI < row_end; base += NR * RPI, r += NR * RPI) {
+  uint32_t ro_r = static_cast<uint32_t>(r0) * kRowBytes;  // offset of row r
+  for (; base + NR * RPI < row_end; base += NR * RPI, r += NR * RPI, ro_r += NR * RPI * kRowBytes) {
 #pragma unroll
     for (int b = 0; b < NR; ++b) {
-      fetch(ring[(b + NR - 1) % NR], r + (b + NR - 1) * RPI);
+      fetch(ring[(b + NR - 1) % NR], ro_r + (b + NR - 1) * RPI * kRowBytes);
       step(ring[b], r + b * RPI);
     }
   }
-  fetch(ring[NR - 1], r + (NR - 1) * RPI);
+  fetch(ring[NR - 1], ro_r + (NR - 1) * RPI * kRowBytes);
 #pragma unroll
   for (int b = 0; b < NR; ++b) step(ring[b], r + b * RPI);
 }
