@@ -158,15 +158,19 @@ __device__ __forceinline__ uint2 lds_u64(const uint2* base, uint32_t byte_off) {
 }
 
 // ---- wave reductions over aligned lane groups of width W (power of two) ----
-// DPP quad_perm / row mirrors inside 16-lane rows, then LDS-crossbar swaps.
+
+// Sum over the group, valid in its LAST lane (in every lane for W <= 16):
+// DPP quad_perm and row mirrors inside 16-lane rows, then DPP row broadcasts
+// across rows (row_bcast:15 into rows 1 and 3, then row_bcast:31 into rows 2
+// and 3), so no LDS round trip.
 template <int W>
-__device__ __forceinline__ int reduce_add_i32(int v) {
+__device__ __forceinline__ int reduce_add_i32_last(int v) {
   if (W >= 2) v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
   if (W >= 4) v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
   if (W >= 8) v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
   if (W >= 16) v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false); // row_mirror
-  if (W >= 32) v += __shfl_xor(v, 16);
-  if (W >= 64) v += __shfl_xor(v, 32);
+  if (W >= 32) v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false); // row_bcast:15, rows 1 and 3
+  if (W >= 64) v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false); // row_bcast:31, rows 2 and 3
   return v;
 }
 
@@ -175,14 +179,16 @@ __device__ __forceinline__ float dpp_f32(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
+// fp32 sum valid in the last lane of each group of W lanes, as
+// reduce_add_i32_last (a fixed order, so results repeat bit for bit).
 template <int W>
-__device__ __forceinline__ float reduce_add_f32(float v) {
+__device__ __forceinline__ float reduce_add_f32_last(float v) {
   if (W >= 2) v += dpp_f32<0xB1>(v);
   if (W >= 4) v += dpp_f32<0x4E>(v);
   if (W >= 8) v += dpp_f32<0x141>(v);
   if (W >= 16) v += dpp_f32<0x140>(v);
-  if (W >= 32) v += __shfl_xor(v, 16);
-  if (W >= 64) v += __shfl_xor(v, 32);
+  if (W >= 32) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+  if (W >= 64) v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
   return v;
 }
 

@@ -204,8 +204,8 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
     int sum = a4[0];
 #pragma unroll
     for (int c = 1; c < C; ++c) sum += a4[c];
-    const int acc = reduce_add_i32<L>(sum);
-    if (lp == 0 && row < row_end) out[row - row_begin] = acc;
+    const int acc = reduce_add_i32_last<L>(sum);  // valid in lane L - 1 of the row
+    if (lp == L - 1 && row < row_end) out[row - row_begin] = acc;
   };
   constexpr int NR = GPL > 1 ? 2 : kRing;  // several groups per lane: two buffers (registers)
   uint32_t ring[NR][GPL][NW];
@@ -299,8 +299,8 @@ __device__ __forceinline__ void gemv_i8_rows_generic(const GemvDesc& d, int row_
         acc = __builtin_amdgcn_sdot4(static_cast<int>(w1.y), static_cast<int>(v.w), acc, false);
       }
     }
-    acc = reduce_add_i32<64>(acc);
-    if (lane == 0) out[r - row_begin] = acc;
+    acc = reduce_add_i32_last<64>(acc);
+    if (lane == kWave - 1) out[r - row_begin] = acc;
   }
 }
 
@@ -386,8 +386,8 @@ __device__ __forceinline__ void gemv_bf16_rows(const GemvDesc& d, int row_begin,
         a2[1] = dot2_bf16(wv.y, xr[t][2 * j + 1], a2[1]);
       }
     }
-    const float acc = reduce_add_f32<L>(a2[0] + a2[1]);
-    if (lp == 0 && row < row_end) out[row - row_begin] = acc;
+    const float acc = reduce_add_f32_last<L>(a2[0] + a2[1]);  // valid in lane L - 1 of the row
+    if (lp == L - 1 && row < row_end) out[row - row_begin] = acc;
   };
   constexpr int NR = GPL > 1 ? 2 : kRing;  // several groups per lane: two buffers (registers)
   uint32_t ring[NR][GPL][NW];
@@ -430,8 +430,8 @@ __device__ __forceinline__ void gemv_bf16_rows_generic(const GemvDesc& d, int ro
         acc = dot2_bf16(w1.y, v.w, acc);
       }
     }
-    acc = reduce_add_f32<64>(acc);
-    if (lane == 0) out[r - row_begin] = acc;
+    acc = reduce_add_f32_last<64>(acc);
+    if (lane == kWave - 1) out[r - row_begin] = acc;
   }
 }
 
