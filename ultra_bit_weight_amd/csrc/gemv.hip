@@ -368,10 +368,14 @@ __device__ __forceinline__ void gemv_bf16_rows(const GemvDesc& d, int row_begin,
     }
   }
   const int last = row_end - 1;
-  auto fetch = [&](uint32_t (&buf)[GPL][NW], int row) {
-    const uint32_t* rp = d.codes + static_cast<int64_t>(min(row, last)) * (G * NW);
+  // row offsets as in the int8 walk: 32-bit, advanced by additions, clamped
+  constexpr uint32_t kRowBytes = G * NW * 4;
+  const SHERRY_GLOBAL char* cbase = gmem(reinterpret_cast<const char*>(d.codes));
+  const uint32_t ro_last = static_cast<uint32_t>(last) * kRowBytes;
+  auto fetch = [&](uint32_t (&buf)[GPL][NW], uint32_t ro_unclamped) {
+    const uint32_t ro = min(ro_unclamped, ro_last);
 #pragma unroll
-    for (int t = 0; t < GPL; ++t) load_group(buf[t], rp, G, min(t * L + lp, G - 1));
+    for (int t = 0; t < GPL; ++t) Sherry3of4::load_at(buf[t], cbase, ro, G, min(t * L + lp, G - 1));
   };
   auto step = [&](const uint32_t (&buf)[GPL][NW], int row) {
     float a2[2] = {0.0f, 0.0f};  // two chains: slot pairs (0,1) and (2,3)
@@ -393,14 +397,16 @@ __device__ __forceinline__ void gemv_bf16_rows(const GemvDesc& d, int row_begin,
   uint32_t ring[NR][GPL][NW];
   const int r0 = row_begin + wave * RPW + rs;
 #pragma unroll
-  for (int b = 0; b + 1 < NR; ++b) fetch(ring[b], r0 + b * RPI);
+  for (int b = 0; b + 1 < NR; ++b) fetch(ring[b], static_cast<uint32_t>(r0 + b * RPI) * kRowBytes);
   // All NR steps of every round run (rows past the tile end are clamped
   // loads).  Peeling the last round's surplus fetches, as the int8 walk
   // does, measured 6 % slower here.
-  for (int base = row_begin, r = r0; base < row_end; base += NR * RPI, r += NR * RPI) {
+  uint32_t ro_r = static_cast<uint32_t>(r0) * kRowBytes;  // offset of row r
+  for (int base = row_begin, r = r0; base < row_end;
+       base += NR * RPI, r += NR * RPI, ro_r += NR * RPI * kRowBytes) {
 #pragma unroll
     for (int b = 0; b < NR; ++b) {
-      fetch(ring[(b + NR - 1) % NR], r + (b + NR - 1) * RPI);
+      fetch(ring[(b + NR - 1) % NR], ro_r + (b + NR - 1) * RPI * kRowBytes);
       step(ring[b], r + b * RPI);
     }
   }
