@@ -199,8 +199,11 @@ sherry_status sherry_gemv_plan_mfma(const sherry_gemv_problem* probs /* HOST */,
 sherry_status sherry_gemv_grouped(const void* plan_host, const void* plan_dev, hipStream_t stream);
 
 /* Matrix product for M tokens: Y[m, r] = s_x[m] * s_w[r] * sum_k X[m, k] T[r, k].
- * Small M (<= 16) decodes codes in registers into int8 MFMA operands; larger
- * M decodes tiles of codes once per tile and feeds int8 MFMA.
+ * M <= 2 with k in {1024, 2048, 3072, 4096, 8192} runs the batch-1 walk with
+ * both tokens' x in registers (each decoded code feeds one v_dot4 per token);
+ * other small M (<= 16) decode codes in registers into int8 MFMA operands;
+ * larger M decode tiles of codes once per tile and feed int8 MFMA.  All give
+ * the same bits.
  *   X        : m x k int8, row-major with row stride ldx bytes (ldx >= k,
  *              ldx % 16 == 0, X 16-byte aligned); x_dt must be I8
  *   x_scales : m floats (per-token scale), or NULL for 1.0
@@ -236,7 +239,9 @@ size_t sherry_gemm_plan_bytes(const sherry_gemm_problem* probs /* HOST */, int32
 /* Build the plan of a grouped GEMM: many independent products for M tokens
  * (each as in sherry_gemm, dtypes shared by all problems) in one kernel
  * launch, e.g. the seven matrices of a decoder layer during prefill.  The
- * tiles of the problems with the longest rows come first.  Pure host code, no
+ * kernel is chosen for the whole plan as in sherry_gemm (the two-token walk
+ * only if every problem qualifies).  The tiles of the problems with the
+ * longest rows come first.  Pure host code, no
  * HIP call; `plan` is a HOST buffer of at least sherry_gemm_plan_bytes bytes,
  * 8-byte aligned.  The caller copies the bytes unchanged to a device buffer
  * (8-byte aligned) and passes both to sherry_gemm_grouped. */

@@ -376,6 +376,22 @@ def test_grouped_gemm_plan_on_host(lib):
     assert lib.sherry_gemm_plan(arr3, 3, F16, I8, F16, base, nb3) == OK
     assert int.from_bytes(ctypes.string_at(base + 40, 8), "little") == 3
     assert tiles_of(base, 3, n3) == [(2, a, 0) for a in range(3)] + [(0, a, 0) for a in range(4)] + [(1, 0, 0)]
+    # every problem with m <= 2 and a register-class k: the two-token walk
+    # (tiling 4), row tiles of the grouped GEMV: 512 rows at k = 2048, 1024 at
+    # 1024, 256 at 3072, 128 at 8192; longest rows first
+    two = [(2048, 2048, 2), (300, 1024, 1), (300, 8192, 2), (100, 3072, 1)]
+    arr5 = problems(two)
+    n5 = 4 + 1 + 3 + 1
+    nb5 = lib.sherry_gemm_plan_bytes(arr5, 4)
+    assert nb5 == 64 + 80 * 4 + 16 * n5
+    assert lib.sherry_gemm_plan(arr5, 4, F16, I8, F16, base, nb5) == OK
+    assert int.from_bytes(ctypes.string_at(base + 40, 8), "little") == 4
+    assert tiles_of(base, 4, n5) == ([(2, a, 0) for a in range(3)] + [(3, 0, 0)] + [(0, a, 0) for a in range(4)]
+                                     + [(1, 0, 0)])
+    # one problem outside the register classes (k = 640) keeps the few-token kernel
+    arr5[3].k = 640
+    assert lib.sherry_gemm_plan(arr5, 4, F16, I8, F16, base, lib.sherry_gemm_plan_bytes(arr5, 4)) == OK
+    assert int.from_bytes(ctypes.string_at(base + 40, 8), "little") == 3
     # m <= 16 with a k above 8192: the 256 x 16 tiling
     skinny = [(2048, 2048, 16), (300, 9216, 3)]
     arr4 = problems(skinny)

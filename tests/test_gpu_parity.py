@@ -241,6 +241,24 @@ def test_gemm_strided_x_and_fp32_out(gpu_lib):
     assert np.array_equal(y.cpu().numpy().view(np.uint32), ref_y.view(np.uint32))
 
 
+@pytest.mark.parametrize("m", [1, 2])
+@pytest.mark.parametrize("k", [1024, 2048, 3072, 4096, 8192])
+def test_gemm_two_tokens_strided(gpu_lib, m, k):
+    """m <= 2 with a register-class k (the two-token walk): strided x, no
+    token scales, fp32 scales and outputs, ragged rows."""
+    say(f"gemm two tokens m={m} k={k}")
+    g = synth.rng(4100 + 7 * m + k)
+    n, ldx = 1029, k + 32
+    words = synth.random_words(n * (k // 128) * 5, g)
+    sw = synth.row_scales(n, g, np.float32)
+    big = synth.x_int8_uniform((m, ldx), g)
+    ref_acc, ref_y = sherry_ref.gemm_i8(words, sw, n, k, big[:, :k], None, np.float32)
+    acc, y = gpu_lib.gemm(words_dev(words), dev(sw), dev(big)[:, :k], None, torch.float32, want_acc=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), ref_acc)
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), ref_y.view(np.uint32))
+
+
 @pytest.mark.parametrize("m", [64, 100, 128, 200, 300])
 @pytest.mark.parametrize("n,k", [(1, 128), (130, 640), (100, 1024), (513, 2048), (64, 8192), (40, 3072)])
 def test_gemm_tiled_matches_oracle(gpu_lib, m, n, k):
@@ -387,6 +405,17 @@ def test_grouped_gemm_few_tokens(gpu_lib, tern2):
     say(f"grouped gemm few tokens tern2={tern2}")
     shapes = [(300, 1024, 1), (64, 128, 16), (513, 2048, 7), (17, 8192, 3), (1000, 640, 12), (2048, 3072, 16)]
     run_grouped_gemm(gpu_lib, tern2, shapes, 717 + tern2, 1 + 1 + 2 + 1 + 2 + 8)
+
+
+@pytest.mark.parametrize("tern2", [False, True])
+def test_grouped_gemm_two_tokens(gpu_lib, tern2):
+    """Every problem with m <= 2 and a register-class k in one launch (the
+    two-token walk): m = 1 and 2, ragged rows, every class.  Row tiles as in
+    the grouped GEMV: 1024 rows at k = 1024, 512 at 2048, 256 at 3072 and
+    4096, 128 at 8192."""
+    say(f"grouped gemm two tokens tern2={tern2}")
+    shapes = [(300, 1024, 1), (513, 2048, 2), (17, 8192, 2), (1000, 4096, 1), (257, 3072, 2)]
+    run_grouped_gemm(gpu_lib, tern2, shapes, 727 + tern2, 1 + 2 + 1 + 4 + 2)
 
 
 @pytest.mark.parametrize("tern2", [False, True])

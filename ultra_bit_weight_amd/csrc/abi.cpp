@@ -198,6 +198,7 @@ struct GemmTiling {
   int64_t kind;
   int rows, tok;
   int64_t rows_of(const sherry_gemm_problem& p) const {
+    if (kind == kGemmTilingTwo) return gemm2_tile_rows(p.k);
     return kind == kGemmTilingFew ? few_tile_rows(static_cast<int>(p.k / kGroupWeights)) : rows;
   }
 };
@@ -212,11 +213,13 @@ int64_t gemm_tiles(const sherry_gemm_problem* probs, int32_t count, const GemmTi
 }
 
 GemmTiling gemm_tiling(const sherry_gemm_problem* probs, int32_t count) {
-  bool few = true, skinny = true;
+  bool two = true, few = true, skinny = true;
   for (int32_t i = 0; i < count; ++i) {
+    two = two && gemm2_fits(probs[i].m, probs[i].k);
     skinny = skinny && probs[i].m <= kGemmSkinnyTok;
     few = few && probs[i].m <= kFewMaxTok && probs[i].k <= kFewMaxGroups * kGroupWeights;
   }
+  if (two) return GemmTiling{kGemmTilingTwo, 0, 2};
   if (few) return GemmTiling{kGemmTilingFew, 0, kFewMaxTok};
   if (skinny) return GemmTiling{kGemmTilingSkinny, kGemmSkinnyRows, kGemmSkinnyTok};
   const GemmTiling large{kGemmTilingLarge, kGemmLargeRows, kGemmLargeTok};

@@ -800,6 +800,7 @@ hipError_t launch_gemm_grouped(const PlanHeader* h, const void* dev, hipStream_t
   const int64_t tiling = h->reserved[0];
   const dim3 grid(h->n_tiles);
   const bool t2 = h->format == kFmtTern2;
+  if (tiling == kGemmTilingTwo) return launch_gemm2_grouped(plan, h->n_tiles, h->format, stream);
   if (tiling == kGemmTilingFew) {
     if (t2)
       hipLaunchKernelGGL((gemm_few_grouped_kernel<Tern2>), grid, dim3(kFewWaves * kWave), 0, stream, plan);
@@ -831,6 +832,7 @@ hipError_t launch_gemm_grouped(const PlanHeader* h, const void* dev, hipStream_t
 }
 
 hipError_t launch_gemm(const GemmDesc& d, int32_t format, hipStream_t stream) {
+  if (gemm2_fits(d.m, d.k)) return launch_gemm2(d, format, stream);
   const int G = d.k / kGroupWeights;
   if (d.m <= kFewMaxTok && G <= kFewMaxGroups) {
     const int rt = few_tile_rows(G);

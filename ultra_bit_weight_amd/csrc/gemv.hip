@@ -114,9 +114,13 @@ constexpr int kXsChunks = kMaxStagedKI8 / 16 * 9 / 8;
 constexpr int kXsPerThread = kMaxStagedKI8 / 16 / kGemvThreads;
 static_assert(kXsPerThread * 16 * kGemvThreads == kMaxStagedKI8, "x staging split");
 
-template <class Fmt, int L, int GPL, int GR = GPL * L, bool XQ = false>
+// XM tokens per walk (1, or 2 for two-token products): token t's x row is
+// d.x + min(t, m - 1) * ldx, and its row results go to out[t * out_stride + ..];
+// the decoded codes serve every token.
+template <class Fmt, int L, int GPL, int GR = GPL * L, bool XQ = false, int XM = 1>
 __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, int row_end, uint32_t* tab32,
-                                             uint2* tab, int32_t* out, u32x4_t* xs, XQuant xq = XQuant{}) {
+                                             uint2* tab, int32_t* out, u32x4_t* xs, XQuant xq = XQuant{},
+                                             int64_t ldx = 0, int m = 1, int out_stride = 0) {
   constexpr int RPW = kWave / L;
   constexpr int RPI = (kGemvThreads / kWave) * RPW;
   constexpr int NW = Fmt::kWords;
@@ -133,15 +137,20 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
   // (XS) as one or two 16-byte chunks per thread staged through LDS, which
   // replaces eight loads per lane with at most two per thread.
   constexpr bool XS = SHERRY_GEMV_XLDS && !XQ && Fmt::kGroupW == 128;
-  uint32_t xr[GPL][32];
-  u32x4_t xv[XS ? kXsPerThread : 1];
+  static_assert(XM == 1 || XS, "several tokens: x staged in LDS");
+  uint32_t xr[XM][GPL][32];
+  u32x4_t xv[XS ? XM * kXsPerThread : 1];
   const int nchunks = d.k / 16;
   if constexpr (XS) {
-    const SHERRY_GLOBAL u32x4_t* xg = gmem(static_cast<const u32x4_t*>(d.x));
 #pragma unroll
-    for (int j = 0; j < kXsPerThread; ++j) {
-      const int c = static_cast<int>(threadIdx.x) + kGemvThreads * j;
-      if (c < nchunks) xv[j] = xg[c];
+    for (int tk = 0; tk < XM; ++tk) {
+      const SHERRY_GLOBAL u32x4_t* xg = gmem(reinterpret_cast<const u32x4_t*>(
+          static_cast<const int8_t*>(d.x) + static_cast<int64_t>(min(tk, m - 1)) * ldx));
+#pragma unroll
+      for (int j = 0; j < kXsPerThread; ++j) {
+        const int c = static_cast<int>(threadIdx.x) + kGemvThreads * j;
+        if (c < nchunks) xv[tk * kXsPerThread + j] = xg[c];
+      }
     }
   }
   auto load_x = [&]() {
@@ -152,17 +161,17 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           const u32x4_t v = reinterpret_cast<const u32x4_t*>(xq.xl + min(t * L + lp, G - 1) * kGroupWeights)[q];
-          xr[t][4 * q + 0] = v.x;
-          xr[t][4 * q + 1] = v.y;
-          xr[t][4 * q + 2] = v.z;
-          xr[t][4 * q + 3] = v.w;
+          xr[0][t][4 * q + 0] = v.x;
+          xr[0][t][4 * q + 1] = v.y;
+          xr[0][t][4 * q + 2] = v.z;
+          xr[0][t][4 * q + 3] = v.w;
         }
       } else {
-        load_x_group<Fmt>(d.x, d.k, min(t * L + lp, G - 1), xr[t]);
+        load_x_group<Fmt>(d.x, d.k, min(t * L + lp, G - 1), xr[0][t]);
       }
       if (G < GPL * L && t * L + lp >= G) {
 #pragma unroll
-        for (int j = 0; j < 32; ++j) xr[t][j] = 0u;
+        for (int j = 0; j < 32; ++j) xr[0][t][j] = 0u;
       }
     }
   };
@@ -185,27 +194,35 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
   };
   auto step = [&](const uint32_t (&buf)[GPL][NW], int row) {
     constexpr int C = kDotChains;  // independent dot4 accumulation chains
-    int a4[C] = {};
+    int a4[XM][C] = {};
 #pragma unroll
     for (int t = 0; t < GPL; ++t) {
 #pragma unroll
       for (int p = 0; p < 16; ++p) {
-        // block pairs in kPairMask: one pair-table read; the others: two
-        // reads of the 32-entry table (balances VALU against LDS bank conflicts)
-        const uint2 v = ((kPairMask >> p) & 1) ? Fmt::i8x8(buf[t], p, tab)
-                                               : make_uint2(Fmt::i8x4(buf[t], 2 * p, tab32),
-                                                            Fmt::i8x4(buf[t], 2 * p + 1, tab32));
-        a4[(2 * p) % C] = __builtin_amdgcn_sdot4(static_cast<int>(v.x), static_cast<int>(xr[t][2 * p]),
-                                                 a4[(2 * p) % C], false);
-        a4[(2 * p + 1) % C] = __builtin_amdgcn_sdot4(static_cast<int>(v.y), static_cast<int>(xr[t][2 * p + 1]),
-                                                     a4[(2 * p + 1) % C], false);
+        // block pairs in the mask (kPairMask, kPairMaskTwo for two tokens):
+        // one pair-table read; the others: two reads of the 32-entry table
+        // (balances VALU against LDS bank conflicts)
+        constexpr unsigned PM = XM > 1 ? kPairMaskTwo : kPairMask;
+        const uint2 v = ((PM >> p) & 1) ? Fmt::i8x8(buf[t], p, tab)
+                                        : make_uint2(Fmt::i8x4(buf[t], 2 * p, tab32),
+                                                     Fmt::i8x4(buf[t], 2 * p + 1, tab32));
+#pragma unroll
+        for (int tk = 0; tk < XM; ++tk) {
+          a4[tk][(2 * p) % C] = __builtin_amdgcn_sdot4(static_cast<int>(v.x), static_cast<int>(xr[tk][t][2 * p]),
+                                                       a4[tk][(2 * p) % C], false);
+          a4[tk][(2 * p + 1) % C] = __builtin_amdgcn_sdot4(
+              static_cast<int>(v.y), static_cast<int>(xr[tk][t][2 * p + 1]), a4[tk][(2 * p + 1) % C], false);
+        }
       }
     }
-    int sum = a4[0];
 #pragma unroll
-    for (int c = 1; c < C; ++c) sum += a4[c];
-    const int acc = reduce_add_i32_last<L>(sum);  // valid in lane L - 1 of the row
-    if (lp == L - 1 && row < row_end) out[row - row_begin] = acc;
+    for (int tk = 0; tk < XM; ++tk) {
+      int sum = a4[tk][0];
+#pragma unroll
+      for (int c = 1; c < C; ++c) sum += a4[tk][c];
+      const int acc = reduce_add_i32_last<L>(sum);  // valid in lane L - 1 of the row
+      if (lp == L - 1 && row < row_end) out[tk * out_stride + row - row_begin] = acc;
+    }
   };
   constexpr int NR = GPL > 1 ? 2 : kRing;  // several groups per lane: two buffers (registers)
   uint32_t ring[NR][GPL][NW];
@@ -218,26 +235,30 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
   }
   if constexpr (XS) {
 #pragma unroll
-    for (int j = 0; j < kXsPerThread; ++j) {
-      const int c = static_cast<int>(threadIdx.x) + kGemvThreads * j;
-      if (c < nchunks) xs[c + c / 8] = xv[j];
-    }
+    for (int tk = 0; tk < XM; ++tk)
+#pragma unroll
+      for (int j = 0; j < kXsPerThread; ++j) {
+        const int c = static_cast<int>(threadIdx.x) + kGemvThreads * j;
+        if (c < nchunks) xs[tk * kXsChunks + c + c / 8] = xv[tk * kXsPerThread + j];
+      }
   }
   init_tables<Fmt>(tab32, tab);  // its barriers also publish the staged x
   if constexpr (XS) {
 #pragma unroll
-    for (int t = 0; t < GPL; ++t) {
-      const bool has = t * L + lp < G;
-      const u32x4_t* xp = xs + 9 * min(t * L + lp, G - 1);
+    for (int tk = 0; tk < XM; ++tk)
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const u32x4_t v = xp[q];
-        xr[t][4 * q + 0] = has ? v.x : 0u;
-        xr[t][4 * q + 1] = has ? v.y : 0u;
-        xr[t][4 * q + 2] = has ? v.z : 0u;
-        xr[t][4 * q + 3] = has ? v.w : 0u;
+      for (int t = 0; t < GPL; ++t) {
+        const bool has = t * L + lp < G;
+        const u32x4_t* xp = xs + tk * kXsChunks + 9 * min(t * L + lp, G - 1);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const u32x4_t v = xp[q];
+          xr[tk][t][4 * q + 0] = has ? v.x : 0u;
+          xr[tk][t][4 * q + 1] = has ? v.y : 0u;
+          xr[tk][t][4 * q + 2] = has ? v.z : 0u;
+          xr[tk][t][4 * q + 3] = has ? v.w : 0u;
+        }
       }
-    }
   }
   // Every round runs all NR steps; rows past the tile end are clamped loads
   // whose results are never stored (no branch inside the ring).  The last
@@ -591,6 +612,79 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_i8_grouped_kernel(const cha
   }
   __syncthreads();
   finalize_i8(d, row0, row1, res, d.x_scale != nullptr, d.x_scale ? *gmem(d.x_scale) : 1.0f);
+}
+
+// Two-token products (GEMM with m <= 2 and a register-class k): the batch-1
+// walk with both tokens' x in registers, so each decoded code feeds two
+// v_dot4; tiles as in the grouped GEMV.  m = 1 walks token 0 twice and
+// stores it once.
+__device__ __forceinline__ int32_t kclass_dev(int k) {
+  return k == 1024 ? k1024 : k == 2048 ? k2048 : k == 4096 ? k4096 : k == 8192 ? k8192 : k == 3072 ? k3072 : kGeneric;
+}
+
+// rows: the tile's row count (a whole number of row iterations, at most
+// kMaxGroupedTileRows); 0 = the grouped GEMV tile of the class.
+template <class Fmt>
+__device__ __forceinline__ void gemm2_tile(const GemmDesc& g, int tile_n, int rows, uint32_t* tab32, uint2* tab,
+                                           int32_t* res, u32x4_t* xs) {
+  const int32_t kc = kclass_dev(g.k);
+  if (kc == kGeneric) return;  // the host routes only the register classes here
+  if (rows == 0) rows = tile_rows_of(kc, false);
+  const int row0 = tile_n * rows;
+  const int row1 = min(row0 + rows, g.n);
+  GemvDesc d{};
+  d.codes = g.codes;
+  d.x = g.x;
+  d.n = g.n;
+  d.k = g.k;
+  d.kclass = kc;
+  constexpr int S = kMaxGroupedTileRows;  // res stride between the two tokens
+  const XQuant none{};
+  switch (kc) {
+    case k1024: gemv_i8_rows<Fmt, 8, 1, 8, false, 2>(d, row0, row1, tab32, tab, res, xs, none, g.ldx, g.m, S); break;
+    case k2048: gemv_i8_rows<Fmt, 16, 1, 16, false, 2>(d, row0, row1, tab32, tab, res, xs, none, g.ldx, g.m, S); break;
+    case k4096: gemv_i8_rows<Fmt, 32, 1, 32, false, 2>(d, row0, row1, tab32, tab, res, xs, none, g.ldx, g.m, S); break;
+    case k8192: gemv_i8_rows<Fmt, 64, 1, 64, false, 2>(d, row0, row1, tab32, tab, res, xs, none, g.ldx, g.m, S); break;
+    default: gemv_i8_rows<Fmt, 32, 1, 24, false, 2>(d, row0, row1, tab32, tab, res, xs, none, g.ldx, g.m, S); break;
+  }
+  __syncthreads();
+  const bool s_f16 = g.flags & kFlagScaleF16;
+  const bool y_f16 = g.flags & kFlagYF16;
+  const bool has_sx = g.x_scales != nullptr;
+  const int nr = row1 - row0;
+  for (int i = threadIdx.x; i < g.m * nr; i += kGemvThreads) {
+    const int tk = i / nr;
+    const int r = row0 + (i - tk * nr);
+    const int32_t v = res[tk * S + (r - row0)];
+    if (g.acc) gmem(g.acc)[static_cast<int64_t>(tk) * g.n + r] = v;
+    if (g.y) {
+      const float sx = has_sx ? gmem(g.x_scales)[tk] : 1.0f;
+      store_y(g.y, static_cast<int64_t>(tk) * g.ldy + r, epilogue_i32(v, load_scale(g.w_scales, r, s_f16), sx, has_sx),
+              y_f16);
+    }
+  }
+}
+
+template <class Fmt>
+__global__ __launch_bounds__(kGemvThreads) void gemm2_kernel(GemmDesc d, int tile_rows) {
+  __shared__ uint32_t tab32[32];
+  __shared__ uint2 tab[Fmt::kPairEntries];
+  __shared__ int32_t res[2 * kMaxGroupedTileRows];
+  __shared__ u32x4_t xs[2 * kXsChunks];
+  gemm2_tile<Fmt>(d, blockIdx.x, tile_rows, tab32, tab, res, xs);
+}
+
+template <class Fmt>
+__global__ __launch_bounds__(kGemvThreads) void gemm2_grouped_kernel(const char* plan) {
+  __shared__ uint32_t tab32[32];
+  __shared__ uint2 tab[Fmt::kPairEntries];
+  __shared__ int32_t res[2 * kMaxGroupedTileRows];
+  __shared__ u32x4_t xs[2 * kXsChunks];
+  const PlanHeader* h = reinterpret_cast<const PlanHeader*>(plan);
+  const GemmDesc* descs = reinterpret_cast<const GemmDesc*>(plan + sizeof(PlanHeader));
+  const GemmTile* tiles = reinterpret_cast<const GemmTile*>(descs + h->count);
+  const GemmTile tl = tiles[blockIdx.x];
+  gemm2_tile<Fmt>(descs[tl.prob], tl.tile_n, 0, tab32, tab, res, xs);
 }
 
 template <bool WIDE>
@@ -952,6 +1046,28 @@ hipError_t launch_gemv_xq(const GemvDesc& d, int xdt, float* sx_out, int32_t for
     launch_xq_class<Tern2>(d, grid, tile_rows, xdt, sx_out, stream);
   else
     launch_xq_class<Sherry3of4>(d, grid, tile_rows, xdt, sx_out, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm2(const GemmDesc& d, int32_t format, hipStream_t stream) {
+  // a single call: tiles as for a single GEMV call (enough workgroups to
+  // cover the chip), not the grouped ones, at most kMaxGroupedTileRows rows (the LDS results)
+  const int rpi = rows_per_iter(kclass_of(d.k));
+  const int iters = tile_iters_for(d.n, rpi);
+  const int rows = rpi * (iters * rpi > kMaxGroupedTileRows ? kMaxGroupedTileRows / rpi : iters);
+  const dim3 grid(static_cast<unsigned>((d.n + rows - 1) / rows));
+  if (format == kFmtTern2)
+    hipLaunchKernelGGL((gemm2_kernel<Tern2>), grid, dim3(kGemvThreads), 0, stream, d, rows);
+  else
+    hipLaunchKernelGGL((gemm2_kernel<Sherry3of4>), grid, dim3(kGemvThreads), 0, stream, d, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm2_grouped(const char* plan, int32_t n_tiles, int32_t format, hipStream_t stream) {
+  if (format == kFmtTern2)
+    hipLaunchKernelGGL((gemm2_grouped_kernel<Tern2>), dim3(n_tiles), dim3(kGemvThreads), 0, stream, plan);
+  else
+    hipLaunchKernelGGL((gemm2_grouped_kernel<Sherry3of4>), dim3(n_tiles), dim3(kGemvThreads), 0, stream, plan);
   return hipGetLastError();
 }
 

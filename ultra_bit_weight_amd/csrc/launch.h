@@ -98,6 +98,12 @@ constexpr int kRing = SHERRY_RING;
 #define SHERRY_PAIR_MASK 0x5555
 #endif
 constexpr unsigned kPairMask = SHERRY_PAIR_MASK;
+// The two-token walk does twice the dot products per decoded code, so there
+// the VALU-saving pair reads pay for every block pair.
+#ifndef SHERRY_PAIR_MASK_TWO
+#define SHERRY_PAIR_MASK_TWO 0xFFFF
+#endif
+constexpr unsigned kPairMaskTwo = SHERRY_PAIR_MASK_TWO;
 // Independent v_dot4 accumulation chains per row step.
 #ifndef SHERRY_DOT_CHAINS
 #define SHERRY_DOT_CHAINS 1
@@ -138,7 +144,8 @@ struct GemmTile {
 static_assert(sizeof(GemmTile) == 16, "grouped GEMM tile record layout");
 // Rows x tokens of the tilings of the tiled kernel: 128 x 128, 256 x 256,
 // and 256 x 16 for plans whose problems all have m <= 16.
-constexpr int64_t kGemmTilingSmall = 0, kGemmTilingLarge = 1, kGemmTilingSkinny = 2, kGemmTilingFew = 3;
+constexpr int64_t kGemmTilingSmall = 0, kGemmTilingLarge = 1, kGemmTilingSkinny = 2, kGemmTilingFew = 3,
+                  kGemmTilingTwo = 4;
 constexpr int kGemmLargeRows = 256, kGemmLargeTok = 192;
 constexpr int kGemmSmallRows = 128, kGemmSmallTok = 128;
 constexpr int kGemmSkinnyRows = 256, kGemmSkinnyTok = 16;
@@ -173,6 +180,13 @@ hipError_t launch_gemv(const GemvDesc& d, bool bf16_x, int32_t format, hipStream
 hipError_t launch_gemv_grouped(const PlanHeader* host, const void* dev, hipStream_t stream);
 hipError_t launch_gemv_xq(const GemvDesc& d, int xdt, float* sx_out, int32_t format, hipStream_t stream);
 hipError_t launch_gemm(const GemmDesc& d, int32_t format, hipStream_t stream);
+// Two-token products: m <= 2 and a register-class k run the batch-1 walk with
+// both tokens' x in registers (kGemmTilingTwo), row tiles as in the grouped
+// GEMV.
+inline bool gemm2_fits(int64_t m, int64_t k) { return m <= 2 && kclass_of(k) != kGeneric; }
+inline int gemm2_tile_rows(int64_t k) { return rows_per_iter(kclass_of(k)) * kGroupedIters; }
+hipError_t launch_gemm2(const GemmDesc& d, int32_t format, hipStream_t stream);
+hipError_t launch_gemm2_grouped(const char* plan, int32_t n_tiles, int32_t format, hipStream_t stream);
 hipError_t launch_gemm_grouped(const PlanHeader* host, const void* dev, hipStream_t stream);
 // Activation quantization: input element types; the GEMV that quantizes its
 // own x holds it in LDS, k <= kActMaxK.
