@@ -107,9 +107,6 @@ __device__ __forceinline__ void load_x_group(const void* x, int k, int g, uint32
 // (one pad chunk after each group's 128 bytes, so that the 16 lanes reading
 // 16 group slices hit 16 disjoint sets of four banks).
 constexpr int kMaxStagedKI8 = 8192;  // largest k of the register-resident classes
-#ifndef SHERRY_GEMV_XLDS
-#define SHERRY_GEMV_XLDS 1
-#endif
 constexpr int kXsChunks = kMaxStagedKI8 / 16 * 9 / 8;
 constexpr int kXsPerThread = kMaxStagedKI8 / 16 / kGemvThreads;
 static_assert(kXsPerThread * 16 * kGemvThreads == kMaxStagedKI8, "x staging split");
@@ -136,7 +133,7 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
   // either as the lane's own 128-byte slice straight from global memory, or
   // (XS) as one or two 16-byte chunks per thread staged through LDS, which
   // replaces eight loads per lane with at most two per thread.
-  constexpr bool XS = SHERRY_GEMV_XLDS && !XQ && Fmt::kGroupW == 128;
+  constexpr bool XS = !XQ && Fmt::kGroupW == 128;
   static_assert(XM == 1 || XS, "several tokens: x staged in LDS");
   uint32_t xr[XM][GPL][32];
   u32x4_t xv[XS ? XM * kXsPerThread : 1];
@@ -507,7 +504,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_i8_kernel(GemvDesc d, int t
   __shared__ uint32_t tab32[32];
   __shared__ uint2 tab[Fmt::kPairEntries];
   __shared__ int32_t res[kMaxTileRows];
-  __shared__ u32x4_t xs[SHERRY_GEMV_XLDS && L > 0 && Fmt::kGroupW == 128 ? kXsChunks : 1];
+  __shared__ u32x4_t xs[L > 0 && Fmt::kGroupW == 128 ? kXsChunks : 1];
   const int row0 = blockIdx.x * tile_rows;
   const int row1 = min(row0 + tile_rows, d.n);
   if (L == 0)
@@ -588,7 +585,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_i8_grouped_kernel(const cha
   __shared__ uint32_t tab32[32];
   __shared__ uint2 tab[Fmt::kPairEntries];
   __shared__ int32_t res[kMaxGroupedTileRows];
-  __shared__ u32x4_t xs[SHERRY_GEMV_XLDS && Fmt::kGroupW == 128 ? kXsChunks : 1];
+  __shared__ u32x4_t xs[Fmt::kGroupW == 128 ? kXsChunks : 1];
   const PlanHeader* h = reinterpret_cast<const PlanHeader*>(plan);
   const GemvDesc* descs = reinterpret_cast<const GemvDesc*>(plan + sizeof(PlanHeader));
   const PlanTile* tiles = reinterpret_cast<const PlanTile*>(descs + h->count);
