@@ -17,11 +17,24 @@ __device__ __forceinline__ float act_value(const void* x, int dt, int64_t i) {
   return __uint_as_float(static_cast<uint32_t>(gmem(static_cast<const uint16_t*>(x))[i]) << 16);
 }
 
-// Max over the workgroup (kActThreads threads; every thread gets it).
+// v combined with the DPP move CTRL of v (rows outside ROWS keep v).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_max(float v) {
+  const int b = __float_as_int(v);
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(b, b, CTRL, ROWS, 0xF, false)));
+}
+
+// Max over the workgroup (kActThreads threads; every thread gets it).  The
+// wave max uses DPP only (no LDS round trips): quad_perm and row mirrors
+// inside 16-lane rows, then row broadcasts, so lane 63 holds it.
 __device__ __forceinline__ float block_max(float v, float* wmax) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  if ((threadIdx.x & (kWave - 1)) == 0) wmax[threadIdx.x / kWave] = v;
+  v = dpp_max<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_max<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_max<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_max<0x140, 0xF>(v);  // row_mirror
+  v = dpp_max<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_max<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  if ((threadIdx.x & (kWave - 1)) == kWave - 1) wmax[threadIdx.x / kWave] = v;
   __syncthreads();
   v = wmax[0];
 #pragma unroll
