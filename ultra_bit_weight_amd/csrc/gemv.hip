@@ -43,9 +43,24 @@ __device__ __forceinline__ void init_tables(uint32_t* tab32, uint2* pairs) {
 // x quantized by the workgroup itself (XQ): all threads load the token's fp
 // values (kActRegs each), take the absmax over the workgroup, and write the
 // int8 codes to xl in LDS; the scale goes to *sx.  Ends with a barrier.
-__device__ __forceinline__ void quantize_x_lds(const GemvDesc& d, int dt, int8_t* xl, float* sx, float* wmax) {
-  float v[kActRegs];
-  const float s = act_scale(block_max(act_load_token(d.x, dt, 0, d.k, v), wmax));
+// In two phases, so that other start-up work can run while the loads of x
+// are in flight: xq_issue loads the token (kActRegs values per thread),
+// xq_finish takes the absmax over the workgroup, writes the int8 codes to xl
+// and the scale to *sx, and ends with a barrier.
+__device__ __forceinline__ void xq_issue(const GemvDesc& d, int dt, float (&v)[kActRegs]) {
+#pragma unroll
+  for (int i = 0; i < kActRegs; ++i) {
+    const int j = threadIdx.x + i * kActThreads;
+    v[i] = j < d.k ? act_value(d.x, dt, j) : 0.0f;
+  }
+}
+
+__device__ __forceinline__ void xq_finish(const GemvDesc& d, const float (&v)[kActRegs], int8_t* xl, float* sx,
+                                          float* wmax) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kActRegs; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  const float s = act_scale(block_max(amax, wmax));
 #pragma unroll
   for (int i = 0; i < kActRegs; ++i) {
     const int j = threadIdx.x + i * kActThreads;
@@ -53,6 +68,12 @@ __device__ __forceinline__ void quantize_x_lds(const GemvDesc& d, int dt, int8_t
   }
   if (threadIdx.x == 0) *sx = s;
   __syncthreads();
+}
+
+__device__ __forceinline__ void quantize_x_lds(const GemvDesc& d, int dt, int8_t* xl, float* sx, float* wmax) {
+  float v[kActRegs];
+  xq_issue(d, dt, v);
+  xq_finish(d, v, xl, sx, wmax);
 }
 
 // XQ: d.x holds fp values of type xdt; the workgroup quantizes them into xl
@@ -226,10 +247,10 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
   const int r0 = row_begin + wave * RPW + rs;
 #pragma unroll
   for (int b = 0; b + 1 < NR; ++b) fetch(ring[b], static_cast<uint32_t>(r0 + b * RPI) * kRowBytes);
-  if constexpr (XQ) {
-    quantize_x_lds(d, xq.dt, xq.xl, xq.sx, xq.wmax);
-    load_x();
-  }
+  // XQ: the token's loads are issued before the tables are built, and
+  // quantized after them
+  float xqv[XQ ? kActRegs : 1];
+  if constexpr (XQ) xq_issue(d, xq.dt, xqv);
   if constexpr (XS) {
 #pragma unroll
     for (int tk = 0; tk < XM; ++tk)
@@ -240,6 +261,10 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
       }
   }
   init_tables<Fmt>(tab32, tab);  // its barriers also publish the staged x
+  if constexpr (XQ) {
+    xq_finish(d, xqv, xq.xl, xq.sx, xq.wmax);
+    load_x();
+  }
   if constexpr (XS) {
 #pragma unroll
     for (int tk = 0; tk < XM; ++tk)
