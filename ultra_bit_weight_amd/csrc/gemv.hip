@@ -385,9 +385,16 @@ __device__ __forceinline__ uint32_t code_offset8(const uint32_t* w, const uint32
   return __builtin_amdgcn_alignbit(w[i + 1], c[i], o - 3) & 0xFFu;  // j = 6, 12, 19, 25
 }
 
+// bf16 x is staged once per workgroup into LDS with contiguous 16-byte
+// loads; the register-resident classes then read their slices from LDS.  One
+// 16-byte pad follows every group slice (16 chunks) so that lanes reading
+// different slices hit different banks.
+constexpr int kMaxStagedK = 8192;
+constexpr int kStagedChunksBf16 = kMaxStagedK * 2 / 16 * 17 / 16;
+
 template <int L, int GPL, int GR = GPL * L>
 __device__ __forceinline__ void gemv_bf16_rows(const GemvDesc& d, int row_begin, int row_end, const uint2* tab,
-                                               const uint4* xs, float* out) {
+                                               uint4* xs, float* out) {
   constexpr int RPW = kWave / L;
   constexpr int RPI = (kGemvThreads / kWave) * RPW;
   constexpr int NW = kGroupWords;
@@ -397,19 +404,22 @@ __device__ __forceinline__ void gemv_bf16_rows(const GemvDesc& d, int row_begin,
   const int rs = lane / L;
   constexpr int G = GR;  // groups per row (lanes t L + lp >= G hold none: x = 0)
 
-  uint32_t xr[GPL][64];
+  // Start-up order as in the int8 walk: x's 16-byte chunks into registers,
+  // then the first ring fetches, then the LDS copy of x (one pad chunk per
+  // 256 bytes) and one barrier (which also publishes the code table), then
+  // the lane's slices into registers.
+  constexpr int kXsPer = (kMaxStagedK * 2 / 16 + kGemvThreads - 1) / kGemvThreads;
+  const int nx = 2 * d.k / 16;
+  u32x4_t xv[kXsPer];
+  {
+    const SHERRY_GLOBAL u32x4_t* src = gmem(static_cast<const u32x4_t*>(d.x));
 #pragma unroll
-  for (int t = 0; t < GPL; ++t) {
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      uint4 v = xs[min(t * L + lp, G - 1) * 17 + q];
-      if (G < GPL * L && t * L + lp >= G) v = make_uint4(0u, 0u, 0u, 0u);
-      xr[t][4 * q + 0] = v.x;
-      xr[t][4 * q + 1] = v.y;
-      xr[t][4 * q + 2] = v.z;
-      xr[t][4 * q + 3] = v.w;
+    for (int j = 0; j < kXsPer; ++j) {
+      const int c = static_cast<int>(threadIdx.x) + kGemvThreads * j;
+      if (c < nx) xv[j] = src[c];
     }
   }
+  uint32_t xr[GPL][64];
   const int last = row_end - 1;
   // row offsets as in the int8 walk: 32-bit, advanced by additions, clamped
   constexpr uint32_t kRowBytes = G * NW * 4;
@@ -441,6 +451,24 @@ __device__ __forceinline__ void gemv_bf16_rows(const GemvDesc& d, int row_begin,
   const int r0 = row_begin + wave * RPW + rs;
 #pragma unroll
   for (int b = 0; b + 1 < NR; ++b) fetch(ring[b], static_cast<uint32_t>(r0 + b * RPI) * kRowBytes);
+#pragma unroll
+  for (int j = 0; j < kXsPer; ++j) {
+    const int c = static_cast<int>(threadIdx.x) + kGemvThreads * j;
+    if (c < nx) reinterpret_cast<u32x4_t*>(xs)[c + c / 16] = xv[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < GPL; ++t) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      uint4 v = xs[min(t * L + lp, G - 1) * 17 + q];
+      if (G < GPL * L && t * L + lp >= G) v = make_uint4(0u, 0u, 0u, 0u);
+      xr[t][4 * q + 0] = v.x;
+      xr[t][4 * q + 1] = v.y;
+      xr[t][4 * q + 2] = v.z;
+      xr[t][4 * q + 3] = v.w;
+    }
+  }
   // All NR steps of every round run (rows past the tile end are clamped
   // loads).  Peeling the last round's surplus fetches, as the int8 walk
   // does, measured 6 % slower here.
@@ -457,6 +485,7 @@ __device__ __forceinline__ void gemv_bf16_rows(const GemvDesc& d, int row_begin,
 
 __device__ __forceinline__ void gemv_bf16_rows_generic(const GemvDesc& d, int row_begin, int row_end,
                                                        const uint2* tab, float* out) {
+  __syncthreads();  // the code table
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int G = d.k / kGroupWeights;
@@ -509,19 +538,6 @@ __device__ __forceinline__ void finalize_bf16(const GemvDesc& d, int row0, int r
   }
 }
 
-// bf16 x is staged once per workgroup into LDS with contiguous 16-byte
-// loads; the register-resident classes then read their slices from LDS.  One
-// 16-byte pad follows every group slice (16 chunks) so that lanes reading
-// different slices hit different banks.
-constexpr int kMaxStagedK = 8192;
-constexpr int kStagedChunksBf16 = kMaxStagedK * 2 / 16 * 17 / 16;
-
-template <int PERIOD>
-__device__ __forceinline__ void stage_x(uint4* xs, const void* x, int bytes) {
-  const SHERRY_GLOBAL u32x4_t* src = gmem(static_cast<const u32x4_t*>(x));
-  for (int i = threadIdx.x; i < bytes / 16; i += blockDim.x) reinterpret_cast<u32x4_t*>(xs)[i + i / PERIOD] = src[i];
-}
-
 // Single problem: one kernel per class, so each keeps its own register count.
 // The row walkers build the LDS tables themselves (after their first loads).
 template <class Fmt, int L, int GPL, int GR>
@@ -572,8 +588,6 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_bf16_kernel(GemvDesc d, int
   const int row0 = blockIdx.x * tile_rows;
   const int row1 = min(row0 + tile_rows, d.n);
   if (threadIdx.x < 32) tab[threadIdx.x] = decode_bf16x4(threadIdx.x);
-  if (L != 0) stage_x<16>(xs, d.x, 2 * d.k);
-  __syncthreads();
   if (L == 0)
     gemv_bf16_rows_generic(d, row0, row1, tab, res);
   else
@@ -722,9 +736,6 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_bf16_grouped_kernel(const c
   const GemvDesc d = descs[tl.prob];
   const int row0 = tl.row0;
   const int row1 = min(row0 + tile_rows_of(d.kclass, true), d.n);
-  const bool staged = d.kclass != kGeneric && (WIDE || d.kclass != k3072);
-  if (staged) stage_x<16>(xs, d.x, 2 * d.k);
-  __syncthreads();
   switch (d.kclass) {
     case k1024: gemv_bf16_rows<8, 1>(d, row0, row1, tab, xs, res); break;
     case k2048: gemv_bf16_rows<16, 1>(d, row0, row1, tab, xs, res); break;
