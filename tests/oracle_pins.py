@@ -334,6 +334,54 @@ def pin_bf16_path(ref):
         assert y[r] == float(exact) * float(sw[r]), r
 
 
+def _bf16_value(b: int) -> Fraction:
+    """bf16 bit pattern -> exact value by the definition
+    sign * (1 + m / 128) * 2^(e - 127) (normal numbers and zero only)."""
+    sgn = -1 if b >> 15 else 1
+    e = (b >> 7) & 0xFF
+    m = b & 0x7F
+    if e == 0 and m == 0:
+        return Fraction(0)
+    assert 0 < e < 255, "normal bf16 only"
+    return sgn * (1 + Fraction(m, 128)) * Fraction(2) ** (e - 127)
+
+
+def pin_bf16_wide_range(ref):
+    """bf16 x whose exponents span far more than fp64's 53 bits, so that no
+    fp64 summation order is exact: every block is (a, a, 0, b) against x =
+    (B, -B, u, s) with B huge (2^60 .. 2^120) and s tiny (2^-120 .. 2^-60).
+    The huge terms cancel exactly inside each block, so the exact row sum is
+    sum_j b_j s_j, which any fp64 running sum that meets a huge partial sum
+    loses.  Each row must equal that exact sum rounded once to fp64, times
+    the row scale."""
+    g = synth.rng(44)
+    n, k = 5, 256
+    nb = k // 4
+    a = g.choice([-1, 1], size=(n, nb))
+    b = g.choice([-1, 1], size=(n, nb))
+    t = np.zeros((n, nb, 4), np.int8)
+    t[:, :, 0] = a
+    t[:, :, 1] = a
+    t[:, :, 3] = b
+    t = t.reshape(n, k)
+    bits = np.zeros(k, np.int64)
+    for j in range(nb):
+        big = (int(g.integers(127 + 60, 127 + 121)) << 7) | int(g.integers(0, 128))
+        tiny = (int(g.integers(127 - 120, 127 - 59)) << 7) | int(g.integers(0, 128))
+        mid = (int(g.integers(127 - 20, 127 + 21)) << 7) | int(g.integers(0, 128))
+        bits[4 * j:4 * j + 4] = [big, big | 0x8000, mid | (int(g.integers(0, 2)) << 15),
+                                 tiny | (int(g.integers(0, 2)) << 15)]
+    xb = bits.astype(np.uint16)
+    words = ref.pack_codes(ref.codes_from_dense(t))
+    sw = synth.row_scales(n, g, np.float32)
+    y = ref.gemv_bf16(words, sw, n, k, xb)
+    xv = [_bf16_value(int(v)) for v in xb.tolist()]
+    for r in range(n):
+        exact = sum(int(t[r, c]) * xv[c] for c in range(k))
+        assert exact != 0 and abs(exact) < Fraction(2) ** -50, r  # only the tiny terms survive
+        assert y[r] == float(exact) * float(sw[r]), r
+
+
 # ------------------------------------------- activation quantization ---
 # Pins for oracle.act_ref (per-token absmax int8, readings A1-A3): hand
 # values, exact rational arithmetic, invariants, and the generator's own
@@ -512,6 +560,16 @@ def pin_t3_products(t3):
             want += int(t[r, c]) * int(x[c])
         assert int(acc[r]) == want, r
         assert Fraction(float(y[r])) == f32_exact(Fraction(want) * Fraction(float(sw[r]))), r
+    # with a token scale and fp16 output: ((acc * s_w) * s_x) rounded to fp32
+    # after each product, then once to fp16, against exact rationals
+    sx = np.float32(g.uniform(0.005, 0.05))
+    sw16 = synth.row_scales(n, g, np.float16)
+    acc2, y2 = t3.gemv_i8(words, sw16, n, k, x, sx, np.float16)
+    assert np.array_equal(acc2, acc)
+    for r in range(n):
+        t1 = f32_exact(Fraction(int(acc[r])) * Fraction(float(sw16[r])))
+        want = f16_exact(f32_exact(t1 * Fraction(float(sx))))
+        assert Fraction(float(y2[r])) == want, r
 
 
 T3_PINS = [pin_t3_codes, pin_t3_layout, pin_t3_products]

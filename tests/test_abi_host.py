@@ -10,7 +10,9 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sherry.h")
-LIB = os.path.join(ROOT, "ultra_bit_weight_amd", "lib", "libsherry.so")
+# SHERRY_TEST_LIB selects another build of the library (the sanitized one of
+# tests/test_abi_sanitized.py); default: the in-tree library
+LIB = os.environ.get("SHERRY_TEST_LIB") or os.path.join(ROOT, "ultra_bit_weight_amd", "lib", "libsherry.so")
 
 OK, EINVAL, ESHAPE, EDTYPE, EALIGN, EDEVICE = 0, 1, 2, 3, 4, 5
 I8, I32, F16, BF16, F32 = 0, 1, 2, 3, 4
@@ -426,3 +428,87 @@ def test_probe_validation(lib):
     assert rt(0, 10, 10, None, None) == EINVAL
     assert rt(0, 10, 10, A + 2, None) == EALIGN
     assert rt(0, 10, 10, A, None) == EDEVICE
+
+
+# ------------------------------------------------- binding size checks ---
+# The C ABI takes bare pointers, so the binding checks every tensor's size,
+# type and device against the problem before it calls the library.  These
+# checks read tensor metadata only, so CPU tensors exercise them here; a
+# call that passes them still stops at the device check.
+
+def _t(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+def test_binding_rejects_mismatched_gemv_buffers(lib):
+    import torch
+
+    from ultra_bit_weight_amd import sherry
+
+    n, k = 64, 1024
+    words = n * (k // 128) * 5
+    ok = dict(codes=_t(words, torch.int32), scales=_t(n, torch.float16), x=_t(k, torch.int8),
+              x_scale=_t(1, torch.float32), acc_out=_t(n, torch.int32), out=_t(n, torch.float16))
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return sherry.gemv(a["codes"], a["scales"], a["x"], a["x_scale"], out=a["out"], acc_out=a["acc_out"])
+
+    bad = [dict(codes=_t(words - 1, torch.int32)), dict(codes=_t(words + 5, torch.int32)),
+           dict(scales=_t(n + 1, torch.float16)),  # codes now too short for n + 1 rows
+           dict(x=_t((1, k), torch.int8)), dict(x=_t(k + 128, torch.int8)),
+           dict(x_scale=_t(2, torch.float32)), dict(x_scale=_t(1, torch.float16)),
+           dict(acc_out=_t(n - 1, torch.int32)), dict(acc_out=_t(n, torch.float32)),
+           dict(out=_t(n + 1, torch.float16)), dict(out=_t(n, torch.int32)),
+           dict(scales=_t(n, torch.int32))]
+    for kw in bad:
+        with pytest.raises(ValueError) as e:
+            call(**kw)
+        assert "GPU" not in str(e.value), (kw, str(e.value))  # caught by the size check, not the device check
+    with pytest.raises(ValueError, match="GPU"):  # well-formed but on the CPU
+        call()
+    with pytest.raises(ValueError):
+        sherry.tern2_gemv(_t(words, torch.int32), ok["scales"], ok["x"], None, out=ok["out"])  # 2-bit: n k / 16 words
+    with pytest.raises(ValueError):
+        sherry.tern3_gemv(_t(words, torch.int32), ok["scales"], ok["x"], None, out=ok["out"])
+    with pytest.raises(ValueError, match="elements|bytes"):
+        sherry.gemv_quant(ok["codes"], ok["scales"], _t(k, torch.float32), out=_t(n - 1, torch.float16))
+    with pytest.raises(ValueError, match="bytes"):
+        sherry.decode(_t(words - 1, torch.int32), n, k)
+
+
+def test_binding_rejects_mismatched_gemm_buffers(lib):
+    import torch
+
+    from ultra_bit_weight_amd import sherry
+
+    n, k, m = 48, 640, 5
+    words = n * (k // 128) * 5
+    ok = dict(codes=_t(words, torch.int32), scales=_t(n, torch.float32), x=_t((m, k), torch.int8),
+              x_scales=_t(m, torch.float32), acc_out=_t((m, n), torch.int32), out=_t((m, n), torch.float16))
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return sherry.gemm(a["codes"], a["scales"], a["x"], a["x_scales"], out=a["out"], acc_out=a["acc_out"])
+
+    bad = [dict(codes=_t(words - 5, torch.int32)), dict(x=_t(m * k, torch.int8)),
+           dict(x=_t((m, 2 * k), torch.int8)[:, ::2]), dict(x_scales=_t(m + 1, torch.float32)),
+           dict(acc_out=_t((m, n - 1), torch.int32)), dict(out=_t((m + 1, n), torch.float16)),
+           dict(out=_t((m, n + 1), torch.float16)), dict(out=_t((n, m), torch.float16).t())]
+    for kw in bad:
+        with pytest.raises(ValueError) as e:
+            call(**kw)
+        assert "GPU" not in str(e.value), (kw, str(e.value))
+    with pytest.raises(ValueError, match="GPU"):
+        call()
+    # grouped launches validate each problem the same way
+    p = dict(codes=ok["codes"], scales=ok["scales"], x=ok["x"], x_scales=ok["x_scales"], y=_t((m, n + 1), torch.float16))
+    with pytest.raises(ValueError, match="y must be"):
+        sherry.GroupedGemm([p])
+    q = dict(codes=_t(words, torch.int32), scales=ok["scales"], x=_t(k, torch.int8), x_scale=None, acc=None,
+             y=_t(n - 1, torch.float16))
+    with pytest.raises(ValueError, match="elements"):
+        sherry.GroupedGemv([q])

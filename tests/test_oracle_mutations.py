@@ -16,7 +16,7 @@ from tests import oracle_pins as P
 PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "sherry_ref.py")
 ALL_PINS = [P.pin_bijection, P.pin_code_table, P.pin_packed_groups, P.pin_row_layout, P.pin_straddles, P.pin_size,
             P.pin_ramp_dot, P.pin_closed_forms, P.pin_brute_force, P.pin_packer, P.pin_epilogue,
-            P.pin_bf16_path]
+            P.pin_bf16_path, P.pin_bf16_wide_range]
 
 
 def fresh():
@@ -83,8 +83,10 @@ def m_word_order_swapped(ref):
     ref.unpack_codes = bad
 
 
-def m_groups_contiguous(ref):
-    """five words of a group kept together instead of the two-part row layout"""
+def m_layout_groups_contiguous(ref):
+    """Checks that the row layout R4 is pinned: the five words of every group
+    stored together (another plausible layout, not the one this oracle takes)
+    must be told apart from R4 by the pins."""
     def pack(codes):
         c = np.asarray(codes).astype(np.uint8)
         n, nb = c.shape
@@ -149,8 +151,30 @@ def m_bf16_scale_dropped(ref):
 
 
 MUTANTS = [m_sign_order_reversed, m_sign_meaning_flipped, m_zero_field_high, m_msb_first_stream,
-           m_word_order_swapped, m_groups_contiguous, m_transposed_operand, m_dropped_token_scale, m_fp64_epilogue,
+           m_word_order_swapped, m_layout_groups_contiguous, m_transposed_operand, m_dropped_token_scale, m_fp64_epilogue,
            m_tie_to_highest, m_absmean_scale, m_bf16_scale_dropped]
+
+
+# Planted in the source text of a private copy of oracle/sherry_ref.py: the
+# exact-sum fallback of the bf16 product, taken when x spans too many binades
+# for an exact fp64 BLAS sum.
+SHERRY_SRC_MUTANTS = {
+    "fsum_fallback_doubled": ("return np.array([math.fsum((t[r] * x64).tolist()) for r in range(t.shape[0])])",
+                              "return 2 * np.array([math.fsum((t[r] * x64).tolist()) for r in range(t.shape[0])])"),
+    "fsum_fallback_never_taken": ("if bound * 2.0 ** (-e_min) < 2.0 ** 52:", "if True:"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SHERRY_SRC_MUTANTS))
+def test_sherry_source_planted_mistake_is_caught(name):
+    ref = fresh_module(PATH, "sherry_ref_src_planted", SHERRY_SRC_MUTANTS[name])
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(ref)
+        except (AssertionError, ValueError, OverflowError):
+            caught.append(pin.__name__)
+    assert caught, f"{name} passed every pin"
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=lambda f: f.__name__)
@@ -219,6 +243,8 @@ T3_MUTANTS = {
     "groups_contiguous": ("out[r, 4 * g + i if i < 4 else 4 * G + g] = word", "out[r, 5 * g + i] = word"),
     "msb_first_stream": ("stream |= encode_block(padded[r, w0:w0 + 3]) << (5 * j)",
                          "stream |= encode_block(padded[r, w0:w0 + 3]) << (5 * (31 - j))"),
+    "token_scale_divides": ("a = a * np.float32(s_x)", "a = a / np.float32(s_x)"),
+    "token_scale_dropped": ("a = a * np.float32(s_x)", "a = a * np.float32(1)"),
 }
 
 

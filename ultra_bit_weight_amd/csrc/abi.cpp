@@ -18,9 +18,22 @@ namespace {
 
 constexpr int64_t kMaxDim = std::numeric_limits<int32_t>::max();
 
+// Enum arguments arrive from C callers as plain integers, which may lie
+// outside the enumerators (a C enum is an int).  They are read through their
+// bytes into int32 and validated as integers: loading an out-of-range value
+// as the C++ enum type would itself be undefined.
+using dt_t = int32_t;
+template <class E>
+int32_t raw(const E& e) {  // by reference: no load of the enum value
+  static_assert(sizeof(E) == sizeof(int32_t), "enum arguments are 32-bit");
+  int32_t v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-size_t dt_size(sherry_dtype d) {
+size_t dt_size(dt_t d) {
   switch (d) {
     case SHERRY_I8: return 1;
     case SHERRY_F16:
@@ -31,7 +44,7 @@ size_t dt_size(sherry_dtype d) {
   return 0;
 }
 
-bool is_scale_dt(sherry_dtype d) { return d == SHERRY_F32 || d == SHERRY_F16; }
+bool is_scale_dt(dt_t d) { return d == SHERRY_F32 || d == SHERRY_F16; }
 
 // n x k packed matrix shape: positive, k % 128 == 0, every index fits int32
 // rows and int64 words.
@@ -73,9 +86,9 @@ sherry_status check_device() {
 sherry_status launched(hipError_t e) { return e == hipSuccess ? SHERRY_OK : SHERRY_ELAUNCH; }
 
 // Shared validation of a batch-1 product (every format).
-sherry_status check_gemv(int32_t format, const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n,
-                         int64_t k, const void* x, sherry_dtype x_dt, const float* x_scale, const int32_t* acc,
-                         const void* y, sherry_dtype y_dt) {
+sherry_status check_gemv(int32_t format, const uint32_t* codes, const void* w_scales, dt_t s_dt, int64_t n,
+                         int64_t k, const void* x, dt_t x_dt, const float* x_scale, const int32_t* acc,
+                         const void* y, dt_t y_dt) {
   const bool allow_bf16 = format == kFmtSherry;
   if (!codes || !w_scales || !x || (!acc && !y)) return SHERRY_EINVAL;
   if (sherry_status s = check_nk(n, k)) return s;
@@ -94,8 +107,8 @@ sherry_status check_gemv(int32_t format, const uint32_t* codes, const void* w_sc
   return SHERRY_OK;
 }
 
-GemvDesc make_desc(int32_t format, const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n,
-                   int64_t k, const void* x, const float* x_scale, int32_t* acc, void* y, sherry_dtype y_dt) {
+GemvDesc make_desc(int32_t format, const uint32_t* codes, const void* w_scales, dt_t s_dt, int64_t n,
+                   int64_t k, const void* x, const float* x_scale, int32_t* acc, void* y, dt_t y_dt) {
   GemvDesc d;
   d.codes = codes;
   d.w_scales = w_scales;
@@ -110,9 +123,9 @@ GemvDesc make_desc(int32_t format, const uint32_t* codes, const void* w_scales, 
   return d;
 }
 
-sherry_status gemv_impl(int32_t format, const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n,
-                        int64_t k, const void* x, sherry_dtype x_dt, const float* x_scale, int32_t* acc, void* y,
-                        sherry_dtype y_dt, hipStream_t stream) {
+sherry_status gemv_impl(int32_t format, const uint32_t* codes, const void* w_scales, dt_t s_dt, int64_t n,
+                        int64_t k, const void* x, dt_t x_dt, const float* x_scale, int32_t* acc, void* y,
+                        dt_t y_dt, hipStream_t stream) {
   if (sherry_status s = check_gemv(format, codes, w_scales, s_dt, n, k, x, x_dt, x_scale, acc, y, y_dt))
     return s;
   if (sherry_status s = check_device()) return s;
@@ -121,9 +134,9 @@ sherry_status gemv_impl(int32_t format, const uint32_t* codes, const void* w_sca
 }
 
 // Batch-1 product of fp activations quantized per token inside the kernel.
-sherry_status gemv_quant_impl(int32_t format, const uint32_t* codes, const void* w_scales, sherry_dtype s_dt,
-                              int64_t n, int64_t k, const void* x, sherry_dtype x_dt, float* x_scale_out,
-                              int32_t* acc, void* y, sherry_dtype y_dt, hipStream_t stream) {
+sherry_status gemv_quant_impl(int32_t format, const uint32_t* codes, const void* w_scales, dt_t s_dt,
+                              int64_t n, int64_t k, const void* x, dt_t x_dt, float* x_scale_out,
+                              int32_t* acc, void* y, dt_t y_dt, hipStream_t stream) {
   if (!codes || !w_scales || !x || (!acc && !y)) return SHERRY_EINVAL;
   if (sherry_status s = check_nk(n, k)) return s;
   if (k > kActMaxK || !codes_fit_32(format, n, k)) return SHERRY_ESHAPE;
@@ -144,10 +157,10 @@ sherry_status gemv_quant_impl(int32_t format, const uint32_t* codes, const void*
 }
 
 // Validation of one product for M tokens; fills the kernel record.
-sherry_status check_gemm(int32_t format, const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n,
+sherry_status check_gemm(int32_t format, const uint32_t* codes, const void* w_scales, dt_t s_dt, int64_t n,
                          int64_t k,
-                         const void* x, sherry_dtype x_dt, int64_t m, int64_t ldx, const float* x_scales, int32_t* acc,
-                         void* y, sherry_dtype y_dt, int64_t ldy, GemmDesc* out) {
+                         const void* x, dt_t x_dt, int64_t m, int64_t ldx, const float* x_scales, int32_t* acc,
+                         void* y, dt_t y_dt, int64_t ldy, GemmDesc* out) {
   if (!codes || !w_scales || !x || (!acc && !y)) return SHERRY_EINVAL;
   if (m <= 0) return SHERRY_EINVAL;
   if (sherry_status s = check_nk(n, k)) return s;
@@ -178,9 +191,9 @@ sherry_status check_gemm(int32_t format, const uint32_t* codes, const void* w_sc
   return SHERRY_OK;
 }
 
-sherry_status gemm_impl(int32_t format, const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n,
-                        int64_t k, const void* x, sherry_dtype x_dt, int64_t m, int64_t ldx, const float* x_scales,
-                        int32_t* acc, void* y, sherry_dtype y_dt, int64_t ldy, hipStream_t stream) {
+sherry_status gemm_impl(int32_t format, const uint32_t* codes, const void* w_scales, dt_t s_dt, int64_t n,
+                        int64_t k, const void* x, dt_t x_dt, int64_t m, int64_t ldx, const float* x_scales,
+                        int32_t* acc, void* y, dt_t y_dt, int64_t ldy, hipStream_t stream) {
   GemmDesc d;
   if (sherry_status s =
           check_gemm(format, codes, w_scales, s_dt, n, k, x, x_dt, m, ldx, x_scales, acc, y, y_dt, ldy, &d))
@@ -238,8 +251,8 @@ size_t gemm_plan_bytes_impl(const sherry_gemm_problem* probs, int32_t count) {
   return sizeof(PlanHeader) + sizeof(GemmDesc) * static_cast<size_t>(count) + sizeof(GemmTile) * tiles;
 }
 
-sherry_status gemm_plan_impl(int32_t format, const sherry_gemm_problem* probs, int32_t count, sherry_dtype s_dt,
-                             sherry_dtype x_dt, sherry_dtype y_dt, void* plan, size_t plan_bytes) {
+sherry_status gemm_plan_impl(int32_t format, const sherry_gemm_problem* probs, int32_t count, dt_t s_dt,
+                             dt_t x_dt, dt_t y_dt, void* plan, size_t plan_bytes) {
   if (!probs || count <= 0 || !plan) return SHERRY_EINVAL;
   std::vector<GemmDesc> descs(static_cast<size_t>(count));
   for (int32_t i = 0; i < count; ++i) {
@@ -312,8 +325,8 @@ size_t plan_bytes_impl(const sherry_gemv_problem* probs, int32_t count, int32_t 
   return sizeof(PlanHeader) + sizeof(GemvDesc) * static_cast<size_t>(count) + sizeof(PlanTile) * tiles;
 }
 
-sherry_status plan_impl(int32_t format, const sherry_gemv_problem* probs, int32_t count, sherry_dtype s_dt,
-                        sherry_dtype x_dt, sherry_dtype y_dt, void* plan, size_t plan_bytes, bool mfma = false) {
+sherry_status plan_impl(int32_t format, const sherry_gemv_problem* probs, int32_t count, dt_t s_dt,
+                        dt_t x_dt, dt_t y_dt, void* plan, size_t plan_bytes, bool mfma = false) {
   if (!probs || count <= 0 || !plan) return SHERRY_EINVAL;
   for (int32_t i = 0; i < count; ++i) {
     const sherry_gemv_problem& p = probs[i];
@@ -367,8 +380,8 @@ sherry_status plan_impl(int32_t format, const sherry_gemv_problem* probs, int32_
   return SHERRY_OK;
 }
 
-sherry_status pack_impl(const void* w, sherry_dtype w_dt, int64_t n, int64_t k, int64_t ldw, uint32_t* codes,
-                        void* scales, sherry_dtype s_dt, bool tern2, hipStream_t stream) {
+sherry_status pack_impl(const void* w, dt_t w_dt, int64_t n, int64_t k, int64_t ldw, uint32_t* codes,
+                        void* scales, dt_t s_dt, bool tern2, hipStream_t stream) {
   if (!w || !codes || !scales) return SHERRY_EINVAL;
   if (sherry_status s = check_nk(n, k)) return s;
   if (ldw < k || ldw > std::numeric_limits<int64_t>::max() / n) return SHERRY_ESHAPE;
@@ -387,7 +400,7 @@ extern "C" {
 const char* sherry_version(void) { return "0.1.0"; }
 
 const char* sherry_status_str(sherry_status s) {
-  switch (s) {
+  switch (raw(s)) {
     case SHERRY_OK: return "SHERRY_OK";
     case SHERRY_EINVAL: return "SHERRY_EINVAL: null pointer, non-positive size or bad argument";
     case SHERRY_ESHAPE: return "SHERRY_ESHAPE: k % 128 != 0, leading dimension too small or size overflow";
@@ -406,12 +419,12 @@ size_t sherry_packed_bytes(int64_t n, int64_t k) {
 
 sherry_status sherry_pack(const void* w, sherry_dtype w_dt, int64_t n, int64_t k, int64_t ldw, uint32_t* codes,
                           void* scales, sherry_dtype s_dt, hipStream_t stream) {
-  return pack_impl(w, w_dt, n, k, ldw, codes, scales, s_dt, false, stream);
+  return pack_impl(w, raw(w_dt), n, k, ldw, codes, scales, raw(s_dt), false, stream);
 }
 
 sherry_status tern2_pack(const void* w, sherry_dtype w_dt, int64_t n, int64_t k, int64_t ldw, uint32_t* codes,
                          void* scales, sherry_dtype s_dt, hipStream_t stream) {
-  return pack_impl(w, w_dt, n, k, ldw, codes, scales, s_dt, true, stream);
+  return pack_impl(w, raw(w_dt), n, k, ldw, codes, scales, raw(s_dt), true, stream);
 }
 
 sherry_status sherry_act_quant(const void* x, sherry_dtype x_dt, int64_t m, int64_t k, int64_t ldx, int8_t* xq,
@@ -419,7 +432,8 @@ sherry_status sherry_act_quant(const void* x, sherry_dtype x_dt, int64_t m, int6
   if (!x || !xq || !scales) return SHERRY_EINVAL;
   if (m <= 0 || k <= 0) return SHERRY_EINVAL;
   int dt = 0;
-  switch (x_dt) {
+  const dt_t xd = raw(x_dt);
+  switch (xd) {
     case SHERRY_F32: dt = kActF32; break;
     case SHERRY_F16: dt = kActF16; break;
     case SHERRY_BF16: dt = kActBf16; break;
@@ -428,7 +442,7 @@ sherry_status sherry_act_quant(const void* x, sherry_dtype x_dt, int64_t m, int6
   if (m > kMaxDim || ldx < k || ldq < k) return SHERRY_ESHAPE;
   if (ldx > std::numeric_limits<int64_t>::max() / m || ldq > std::numeric_limits<int64_t>::max() / m)
     return SHERRY_ESHAPE;
-  if (!aligned(x, dt_size(x_dt)) || !aligned(scales, 4)) return SHERRY_EALIGN;
+  if (!aligned(x, dt_size(xd)) || !aligned(scales, 4)) return SHERRY_EALIGN;
   if (sherry_status s = check_device()) return s;
   return launched(launch_act_quant(x, dt, m, k, ldx, xq, ldq, scales, stream));
 }
@@ -446,13 +460,14 @@ sherry_status sherry_decode(const uint32_t* codes, int64_t n, int64_t k, int8_t*
 sherry_status sherry_gemv_quant(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,
                                 const void* x, sherry_dtype x_dt, float* x_scale_out, int32_t* acc, void* y,
                                 sherry_dtype y_dt, hipStream_t stream) {
-  return gemv_quant_impl(kFmtSherry, codes, w_scales, s_dt, n, k, x, x_dt, x_scale_out, acc, y, y_dt, stream);
+  return gemv_quant_impl(kFmtSherry, codes, w_scales, raw(s_dt), n, k, x, raw(x_dt),
+                         x_scale_out, acc, y, raw(y_dt), stream);
 }
 
 sherry_status sherry_gemv(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,
                           const void* x, sherry_dtype x_dt, const float* x_scale, int32_t* acc, void* y,
                           sherry_dtype y_dt, hipStream_t stream) {
-  return gemv_impl(kFmtSherry, codes, w_scales, s_dt, n, k, x, x_dt, x_scale, acc, y, y_dt, stream);
+  return gemv_impl(kFmtSherry, codes, w_scales, raw(s_dt), n, k, x, raw(x_dt), x_scale, acc, y, raw(y_dt), stream);
 }
 
 size_t sherry_gemv_plan_bytes(const sherry_gemv_problem* probs, int32_t count) {
@@ -461,12 +476,12 @@ size_t sherry_gemv_plan_bytes(const sherry_gemv_problem* probs, int32_t count) {
 
 sherry_status sherry_gemv_plan(const sherry_gemv_problem* probs, int32_t count, sherry_dtype s_dt,
                                sherry_dtype x_dt, sherry_dtype y_dt, void* plan, size_t plan_bytes) {
-  return plan_impl(kFmtSherry, probs, count, s_dt, x_dt, y_dt, plan, plan_bytes);
+  return plan_impl(kFmtSherry, probs, count, raw(s_dt), raw(x_dt), raw(y_dt), plan, plan_bytes);
 }
 
 sherry_status sherry_gemv_plan_mfma(const sherry_gemv_problem* probs, int32_t count, sherry_dtype s_dt,
                                     sherry_dtype x_dt, sherry_dtype y_dt, void* plan, size_t plan_bytes) {
-  return plan_impl(kFmtSherry, probs, count, s_dt, x_dt, y_dt, plan, plan_bytes, true);
+  return plan_impl(kFmtSherry, probs, count, raw(s_dt), raw(x_dt), raw(y_dt), plan, plan_bytes, true);
 }
 
 sherry_status sherry_gemv_grouped(const void* plan_host, const void* plan_dev, hipStream_t stream) {
@@ -487,12 +502,12 @@ size_t sherry_gemm_plan_bytes(const sherry_gemm_problem* probs, int32_t count) {
 
 sherry_status sherry_gemm_plan(const sherry_gemm_problem* probs, int32_t count, sherry_dtype s_dt, sherry_dtype x_dt,
                                sherry_dtype y_dt, void* plan, size_t plan_bytes) {
-  return gemm_plan_impl(kFmtSherry, probs, count, s_dt, x_dt, y_dt, plan, plan_bytes);
+  return gemm_plan_impl(kFmtSherry, probs, count, raw(s_dt), raw(x_dt), raw(y_dt), plan, plan_bytes);
 }
 
 sherry_status tern2_gemm_plan(const sherry_gemm_problem* probs, int32_t count, sherry_dtype s_dt, sherry_dtype x_dt,
                               sherry_dtype y_dt, void* plan, size_t plan_bytes) {
-  return gemm_plan_impl(kFmtTern2, probs, count, s_dt, x_dt, y_dt, plan, plan_bytes);
+  return gemm_plan_impl(kFmtTern2, probs, count, raw(s_dt), raw(x_dt), raw(y_dt), plan, plan_bytes);
 }
 
 sherry_status sherry_gemm_grouped(const void* plan_host, const void* plan_dev, hipStream_t stream) {
@@ -510,7 +525,8 @@ sherry_status sherry_gemm_grouped(const void* plan_host, const void* plan_dev, h
 sherry_status sherry_gemm(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,
                           const void* x, sherry_dtype x_dt, int64_t m, int64_t ldx, const float* x_scales,
                           int32_t* acc, void* y, sherry_dtype y_dt, int64_t ldy, hipStream_t stream) {
-  return gemm_impl(kFmtSherry, codes, w_scales, s_dt, n, k, x, x_dt, m, ldx, x_scales, acc, y, y_dt, ldy, stream);
+  return gemm_impl(kFmtSherry, codes, w_scales, raw(s_dt), n, k, x, raw(x_dt),
+                   m, ldx, x_scales, acc, y, raw(y_dt), ldy, stream);
 }
 
 size_t tern2_packed_bytes(int64_t n, int64_t k) {
@@ -530,12 +546,12 @@ sherry_status tern2_encode(const int8_t* t, int64_t n, int64_t k, int64_t ldt, u
 sherry_status tern2_gemv(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,
                          const void* x, sherry_dtype x_dt, const float* x_scale, int32_t* acc, void* y,
                          sherry_dtype y_dt, hipStream_t stream) {
-  return gemv_impl(kFmtTern2, codes, w_scales, s_dt, n, k, x, x_dt, x_scale, acc, y, y_dt, stream);
+  return gemv_impl(kFmtTern2, codes, w_scales, raw(s_dt), n, k, x, raw(x_dt), x_scale, acc, y, raw(y_dt), stream);
 }
 
 sherry_status tern2_gemv_plan(const sherry_gemv_problem* probs, int32_t count, sherry_dtype s_dt,
                               sherry_dtype x_dt, sherry_dtype y_dt, void* plan, size_t plan_bytes) {
-  return plan_impl(kFmtTern2, probs, count, s_dt, x_dt, y_dt, plan, plan_bytes);
+  return plan_impl(kFmtTern2, probs, count, raw(s_dt), raw(x_dt), raw(y_dt), plan, plan_bytes);
 }
 
 size_t tern3_packed_bytes(int64_t n, int64_t k) {
@@ -555,7 +571,7 @@ sherry_status tern3_encode(const int8_t* t, int64_t n, int64_t k, int64_t ldt, u
 sherry_status tern3_gemv(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,
                          const void* x, sherry_dtype x_dt, const float* x_scale, int32_t* acc, void* y,
                          sherry_dtype y_dt, hipStream_t stream) {
-  return gemv_impl(kFmtTern3, codes, w_scales, s_dt, n, k, x, x_dt, x_scale, acc, y, y_dt, stream);
+  return gemv_impl(kFmtTern3, codes, w_scales, raw(s_dt), n, k, x, raw(x_dt), x_scale, acc, y, raw(y_dt), stream);
 }
 
 size_t tern3_gemv_plan_bytes(const sherry_gemv_problem* probs, int32_t count) {
@@ -564,13 +580,14 @@ size_t tern3_gemv_plan_bytes(const sherry_gemv_problem* probs, int32_t count) {
 
 sherry_status tern3_gemv_plan(const sherry_gemv_problem* probs, int32_t count, sherry_dtype s_dt,
                               sherry_dtype x_dt, sherry_dtype y_dt, void* plan, size_t plan_bytes) {
-  return plan_impl(kFmtTern3, probs, count, s_dt, x_dt, y_dt, plan, plan_bytes);
+  return plan_impl(kFmtTern3, probs, count, raw(s_dt), raw(x_dt), raw(y_dt), plan, plan_bytes);
 }
 
 sherry_status tern2_gemm(const uint32_t* codes, const void* w_scales, sherry_dtype s_dt, int64_t n, int64_t k,
                          const void* x, sherry_dtype x_dt, int64_t m, int64_t ldx, const float* x_scales,
                          int32_t* acc, void* y, sherry_dtype y_dt, int64_t ldy, hipStream_t stream) {
-  return gemm_impl(kFmtTern2, codes, w_scales, s_dt, n, k, x, x_dt, m, ldx, x_scales, acc, y, y_dt, ldy, stream);
+  return gemm_impl(kFmtTern2, codes, w_scales, raw(s_dt), n, k, x, raw(x_dt),
+                   m, ldx, x_scales, acc, y, raw(y_dt), ldy, stream);
 }
 
 }  // extern "C"

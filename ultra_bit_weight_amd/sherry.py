@@ -132,9 +132,82 @@ def _ptr(t):
 
 
 def _dev(*ts):
+    """Every given tensor contiguous, on the GPU, and all on one device."""
+    devs = set()
     for t in ts:
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous():
             raise ValueError("tensors must be contiguous and on the GPU")
+        devs.add(t.device)
+    if len(devs) > 1:
+        raise ValueError(f"tensors are on different devices: {sorted(str(d) for d in devs)}")
+
+
+def _need(t, name, numel=None, nbytes=None, dtypes=None, dim=None):
+    """Size and type checks the C ABI cannot make (it takes bare pointers):
+    a wrong size here would let a kernel read or write past a buffer.  Runs on
+    tensor metadata only, before any device check."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must be {dim}-D, got shape {tuple(t.shape)}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    if nbytes is not None and t.numel() * t.element_size() != nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, expected {nbytes}")
+
+
+_SCALE_DT = (torch.float32, torch.float16)
+_Y_DT = (torch.float32, torch.float16)
+
+
+def _codes_bytes(fmt: str, n: int, k: int) -> int:
+    nb = {"sherry": packed_bytes, "tern2": tern2_packed_bytes, "tern3": tern3_packed_bytes}[fmt](n, k)
+    if nb == 0:
+        raise ValueError(f"invalid shape n={n} k={k} (k must be a positive multiple of 128)")
+    return nb
+
+
+def _check_gemv_args(fmt, codes, scales, x, x_scale, acc, y):
+    """Batch-1 product: n from the scales, k from x (1-D)."""
+    _need(scales, "scales", dim=1, dtypes=_SCALE_DT)
+    _need(x, "x", dim=1)
+    n, k = scales.numel(), x.numel()
+    _need(codes, "codes", nbytes=_codes_bytes(fmt, n, k))
+    _need(x_scale, "x_scale", numel=1, dtypes=(torch.float32,))
+    _need(acc, "acc", numel=n, dtypes=(torch.int32,))
+    _need(y, "y", numel=n, dtypes=_Y_DT)
+    _dev(codes, scales, x, x_scale, acc, y)
+    return n, k
+
+
+def _check_gemm_args(fmt, codes, scales, x, x_scales, acc, y):
+    """M-token product: x [m, k] with unit column stride, y [m, n] likewise,
+    acc [m, n] contiguous."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [m, k] with unit column stride")
+    _need(scales, "scales", dim=1, dtypes=_SCALE_DT)
+    m, k = x.shape
+    n = scales.numel()
+    _need(codes, "codes", nbytes=_codes_bytes(fmt, n, k))
+    _need(x_scales, "x_scales", numel=m, dtypes=(torch.float32,))
+    _need(acc, "acc", numel=m * n, dtypes=(torch.int32,))
+    if y is not None:
+        if y.dim() != 2 or tuple(y.shape) != (m, n) or y.stride(1) != 1:
+            raise ValueError(f"y must be [{m}, {n}] with unit column stride, got shape {tuple(y.shape)}")
+        _need(y, "y", dtypes=_Y_DT)
+    _dev(codes, scales, x_scales, acc)  # x and y may have a row stride
+    for name, t in (("x", x), ("y", y)):
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
+    if len({t.device for t in (codes, scales, x, x_scales, acc, y) if t is not None}) > 1:
+        raise ValueError("tensors are on different devices")
+    return m, n, k
 
 
 def packed_bytes(n: int, k: int) -> int:
@@ -204,6 +277,7 @@ def probe_rates(mode: int, iters: int, blocks: int, sink: torch.Tensor):
 
 def decode(codes: torch.Tensor, n: int, k: int) -> torch.Tensor:
     """Packed codes -> dense int8 ternary matrix [n, k]."""
+    _need(codes, "codes", nbytes=_codes_bytes("sherry", n, k))
     _dev(codes)
     t = torch.empty(n, k, dtype=torch.int8, device=codes.device)
     _check("sherry_decode", load().sherry_decode(codes.data_ptr(), n, k, t.data_ptr(), t.stride(0), _stream()))
@@ -230,8 +304,8 @@ def gemv_quant(codes, scales, x, out_dtype=torch.float16, want_acc=False, want_s
     """y = diag(scales) T q(x) for fp x [k] (fp32, fp16 or bf16), x quantized
     per token inside the kernel.  Returns (acc or None, y or None, scale or
     None)."""
-    _dev(codes, scales, x, out)
-    n, k = scales.numel(), x.numel()
+    _need(x, "x", dim=1, dtypes=(torch.float32, torch.float16, torch.bfloat16))
+    n, k = _check_gemv_args("sherry", codes, scales, x, None, None, out)
     y = out if out is not None else (torch.empty(n, dtype=out_dtype, device=x.device) if out_dtype else None)
     acc = torch.empty(n, dtype=torch.int32, device=x.device) if want_acc else None
     sx = torch.empty(1, dtype=torch.float32, device=x.device) if want_scale else None
@@ -241,10 +315,12 @@ def gemv_quant(codes, scales, x, out_dtype=torch.float16, want_acc=False, want_s
     return acc, y, sx
 
 
+_FMT = {"sherry_gemv": "sherry", "tern2_gemv": "tern2", "tern3_gemv": "tern3", "sherry_gemm": "sherry",
+        "tern2_gemm": "tern2"}
+
+
 def _gemv(fn_name, codes, scales, x, x_scale, acc, y):
-    _dev(codes, scales, x, x_scale, acc, y)
-    n = scales.numel()
-    k = x.numel()
+    n, k = _check_gemv_args(_FMT[fn_name], codes, scales, x, x_scale, acc, y)
     f = getattr(load(), fn_name)
     _check(fn_name, f(codes.data_ptr(), scales.data_ptr(), _DT[scales.dtype], n, k, x.data_ptr(), _DT[x.dtype],
                       _ptr(x_scale), _ptr(acc), _ptr(y), _DT[y.dtype] if y is not None else F32, _stream()))
@@ -268,14 +344,8 @@ def tern2_gemv(codes, scales, x, x_scale=None, out_dtype=torch.float16, want_acc
 
 
 def _gemm(fn_name, codes, scales, x, x_scales, out_dtype, want_acc, out=None, acc_out=None):
-    if x.dim() != 2 or x.stride(1) != 1:
-        raise ValueError("x must be [m, k] with unit column stride")
-    _dev(codes, scales, x_scales, acc_out)
-    m, k = x.shape
-    n = scales.numel()
+    m, n, k = _check_gemm_args(_FMT[fn_name], codes, scales, x, x_scales, acc_out, out)
     y = out if out is not None else (torch.empty(m, n, dtype=out_dtype, device=x.device) if out_dtype else None)
-    if y is not None and (y.dim() != 2 or y.stride(1) != 1 or not y.is_cuda):
-        raise ValueError("out must be a [m, n] GPU tensor with unit column stride")
     acc = acc_out if acc_out is not None else (torch.empty(m, n, dtype=torch.int32, device=x.device) if want_acc
                                                else None)
     f = getattr(load(), fn_name)
@@ -344,8 +414,9 @@ class GroupedGemv:
         lib = load()
         arr = (GemvProblem * len(problems))()
         self._keep = []
+        fmt = "tern3" if tern3 else ("tern2" if tern2 else "sherry")
         for i, p in enumerate(problems):
-            _dev(p["codes"], p["scales"], p["x"], p.get("x_scale"), p.get("acc"), p.get("y"))
+            _check_gemv_args(fmt, p["codes"], p["scales"], p["x"], p.get("x_scale"), p.get("acc"), p.get("y"))
             arr[i] = GemvProblem(p["codes"].data_ptr(), p["scales"].data_ptr(), p["scales"].numel(), p["x"].numel(),
                                  p["x"].data_ptr(), _ptr(p.get("x_scale")), _ptr(p.get("acc")), _ptr(p.get("y")))
             self._keep.append(p)
@@ -384,13 +455,8 @@ class GroupedGemm:
         self._keep = []
         for i, p in enumerate(problems):
             x, y, acc = p["x"], p.get("y"), p.get("acc")
-            _dev(p["codes"], p["scales"], x, p.get("x_scales"), acc, y)
-            if x.dim() != 2 or x.stride(1) != 1:
-                raise ValueError("x must be [m, k] with unit column stride")
-            if y is not None and (y.dim() != 2 or y.stride(1) != 1):
-                raise ValueError("y must be [m, n] with unit column stride")
-            m, k = x.shape
-            n = p["scales"].numel()
+            m, n, k = _check_gemm_args("tern2" if tern2 else "sherry", p["codes"], p["scales"], x, p.get("x_scales"),
+                                       acc, y)
             arr[i] = GemmProblem(p["codes"].data_ptr(), p["scales"].data_ptr(), n, k, x.data_ptr(), m, x.stride(0),
                                  _ptr(p.get("x_scales")), _ptr(acc), _ptr(y), y.stride(0) if y is not None else n)
             self._keep.append(p)
