@@ -56,6 +56,9 @@ def parse_args(argv=None):
                         "a few of each, for a profiler; prints their timing and exits")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) and exit")
+    p.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                   help="summarise a rocprofv3 --kernel-trace run of `bench.py --no-extras` (the last --steps "
+                        "dispatches of the grouped GEMV are its timed launches) and exit")
     return p.parse_args(argv)
 
 
@@ -218,7 +221,9 @@ def traffic_from_summary():
 def cpu_baseline(torch, probs, shapes, min_seconds=10.0, max_layers=16):
     """The oracle as it stands, one thread, on whole 1B layers (7 matrices
     each, replicas 0, 1, ...) until at least min_seconds of CPU work:
-    unpack + exact product + epilogue, per matrix."""
+    unpack + exact product + epilogue, per matrix.  The oracle's outputs are
+    then compared, bit for bit, with what the timed grouped launch wrote for
+    the same problems (`checked`)."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
 
@@ -227,6 +232,7 @@ def cpu_baseline(torch, probs, shapes, min_seconds=10.0, max_layers=16):
     per_layer = sum(n * k for _, n, k in shapes)
     done = 0
     dt = 0.0
+    checked = {"problems": 0, "rows": 0, "mismatched_rows": 0}
     with threadpool_limits(limits=1):
         for r in range(max_layers):
             layer = [p for p in probs if p["replica"] == r]
@@ -235,15 +241,20 @@ def cpu_baseline(torch, probs, shapes, min_seconds=10.0, max_layers=16):
             host = [(p["codes"].cpu().numpy().view(np.uint32), p["scales"].cpu().numpy(), p["n"], p["k"],
                      p["x"].cpu().numpy(), p["x_scale"].cpu().numpy()[0]) for p in layer]
             t0 = time.perf_counter()
-            for words, sw, n, k, x, sx in host:
-                sherry_ref.gemv_i8(words, sw, n, k, x, sx, np.float16)
+            outs = [sherry_ref.gemv_i8(words, sw, n, k, x, sx, np.float16) for words, sw, n, k, x, sx in host]
             dt += time.perf_counter() - t0
+            for p, (_, y_ref) in zip(layer, outs):
+                y_gpu = p["y"].cpu().numpy()
+                checked["problems"] += 1
+                checked["rows"] += p["n"]
+                checked["mismatched_rows"] += int(np.count_nonzero(y_gpu.view(np.uint16) != y_ref.view(np.uint16)))
             done += 1
             if dt >= min_seconds:
                 break
     line = {"value": done * per_layer / dt, "unit": "weights/s", "cores": 1, "kind": "oracle",
             "sample": f"{done} LLaMA-3.2-1B decoder layer(s) (7 matrices, {per_layer} weights each), batch 1, "
                       f"numpy oracle limited to 1 thread, {dt:.1f} s"}
+    line["checked"] = dict(checked, what="fp16 outputs of the timed grouped launch against the oracle, bit for bit")
     # the same oracle with the BLAS pool at its default size, on fewer layers
     with threadpool_limits(limits=None):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -737,7 +748,7 @@ def summarize_counters(fetch_dir, write_dir):
         vals = [v for k, vs in rows.items() if pat in k for v in vs]
         return statistics.median(vals) if vals else None
 
-    g_f, g_w = pick(fetch, "gemv_i8_grouped"), pick(write, "gemv_i8_grouped")
+    g_f, g_w = pick(fetch, GEMV_KERNEL_PATTERNS[0]), pick(write, GEMV_KERNEL_PATTERNS[0])
     c_f, c_w = pick(fetch, "neg_kernel"), pick(write, "neg_kernel")
     gib = float(1 << 30)
     f_fac = gib / (c_f * 1024) if c_f else None
@@ -750,6 +761,40 @@ def summarize_counters(fetch_dir, write_dir):
     return res
 
 
+# the grouped GEMV's kernel
+GEMV_KERNEL_PATTERNS = ("gemv_i8_grouped_kernel",)
+
+
+def summarize_trace(trace_dir, timed):
+    """A rocprofv3 --kernel-trace run of the default benchmark: the grouped
+    GEMV's duration over all its dispatches (warm-up and clock settling
+    included) and over the last `timed` dispatches, which are the timed
+    launches when the run had no extras (--no-extras)."""
+    import csv
+
+    rows = []
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                name = row.get("Kernel_Name", "")
+                if any(p in name for p in GEMV_KERNEL_PATTERNS):
+                    rows.append((int(row["Start_Timestamp"]), int(row["End_Timestamp"]) - int(row["Start_Timestamp"]),
+                                 name))
+    rows.sort()
+    durs = [d / 1e3 for _, d, _ in rows]
+    tail = durs[-timed:]
+    res = {"kernel": rows[-1][2] if rows else None, "dispatches": len(durs),
+           "all_mean_us": round(statistics.mean(durs), 2) if durs else None,
+           "timed": len(tail), "timed_mean_us": round(statistics.mean(tail), 2) if tail else None,
+           "timed_min_us": round(min(tail), 2) if tail else None, "timed_max_us": round(max(tail), 2) if tail else None}
+    if tail:
+        layer = sum(n * k * 5 // 32 + 2 * n + k + 2 * n + 4 for n, k in
+                    ((2048, 2048), (512, 2048), (512, 2048), (2048, 2048), (8192, 2048), (8192, 2048), (2048, 8192)))
+        res["timed_frac_hbm_112_layers"] = round(112 * layer / (res["timed_mean_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+    print(json.dumps(res))
+    return res
+
+
 # ------------------------------------------------------------------- main ---
 
 def main(argv=None):
@@ -758,6 +803,9 @@ def main(argv=None):
     SETTLE_MS = args.settle_ms
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
+        return 0
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.steps)
         return 0
     if args.gpus != 1:
         print(f"bench.py: this benchmark runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -784,7 +832,8 @@ def main(argv=None):
     grouped = sherry.GroupedGemv(probs)
     torch.cuda.synchronize()
     print(f"# built {R} replicas of the 1B layer: {codes.numel() * 4 / 1e9:.3f} GB of codes, "
-          f"{grouped.n_tiles} workgroup tiles", file=sys.stderr, flush=True)
+          f"{grouped.n_tiles} workgroup tiles",
+          file=sys.stderr, flush=True)
 
     if args.copy_probe:
         # plain streaming kernel of known traffic: 1 GiB read + 1 GiB written
@@ -826,6 +875,7 @@ def main(argv=None):
             "code_bytes_per_step": R * sum(n * k * 5 // 32 for _, n, k in shapes),
             "bits_per_weight": 1.25,
             "kernel": "gemv_i8_grouped_kernel<Sherry3of4>",
+            "workgroups": grouped.n_tiles,
         },
         "roofline": {
             "bound": "hbm",
@@ -838,11 +888,17 @@ def main(argv=None):
             "launch_ms": round(mean_ms, 4),
         },
     }
+    mismatch = False
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(torch, probs, shapes)
+        chk = line["cpu_baseline"]["checked"]
+        line["checked"] = {k: chk[k] for k in ("problems", "rows", "mismatched_rows")}
+        mismatch = chk["mismatched_rows"] != 0
         if not args.no_extras:
             line["cpu_baseline"]["per_row"] = cpu_baseline_per_row(synth)
-        print(f"# cpu oracle: {line['cpu_baseline']['value']:.3e} weights/s", file=sys.stderr, flush=True)
+        print(f"# cpu oracle: {line['cpu_baseline']['value']:.3e} weights/s; timed launch vs oracle: "
+              f"{chk['problems']} problems, {chk['rows']} rows, {chk['mismatched_rows']} mismatched",
+              file=sys.stderr, flush=True)
     if not args.no_extras:
         ex = extras(torch, sherry, synth, probs, codes, args)
         t2 = ex.get("tern2_grouped_1b")
@@ -856,6 +912,9 @@ def main(argv=None):
             ex["sherry_over_dense_fp16_gemv_speedup"] = round(dense["ms_per_step"] / mean_ms, 2)
         line["extras"] = ex
     print(json.dumps(line), flush=True)
+    if mismatch:
+        print("bench.py: the timed launch's outputs differ from the oracle", file=sys.stderr, flush=True)
+        return 3
     return 0
 
 

@@ -456,7 +456,7 @@ def test_binding_rejects_mismatched_gemv_buffers(lib):
         a.update(kw)
         return sherry.gemv(a["codes"], a["scales"], a["x"], a["x_scale"], out=a["out"], acc_out=a["acc_out"])
 
-    bad = [dict(codes=_t(words - 1, torch.int32)), dict(codes=_t(words + 5, torch.int32)),
+    bad = [dict(codes=_t(words - 1, torch.int32)), dict(codes=_t(words // 2, torch.int8)),
            dict(scales=_t(n + 1, torch.float16)),  # codes now too short for n + 1 rows
            dict(x=_t((1, k), torch.int8)), dict(x=_t(k + 128, torch.int8)),
            dict(x_scale=_t(2, torch.float32)), dict(x_scale=_t(1, torch.float16)),
@@ -469,6 +469,8 @@ def test_binding_rejects_mismatched_gemv_buffers(lib):
         assert "GPU" not in str(e.value), (kw, str(e.value))  # caught by the size check, not the device check
     with pytest.raises(ValueError, match="GPU"):  # well-formed but on the CPU
         call()
+    with pytest.raises(ValueError, match="GPU"):  # codes at the start of a larger buffer are accepted
+        call(codes=_t(words + 5, torch.int32))
     with pytest.raises(ValueError):
         sherry.tern2_gemv(_t(words, torch.int32), ok["scales"], ok["x"], None, out=ok["out"])  # 2-bit: n k / 16 words
     with pytest.raises(ValueError):

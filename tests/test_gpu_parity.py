@@ -564,6 +564,35 @@ def test_grouped_gemv_matches_single_calls_and_oracle(gpu_lib):
         assert np.array_equal(p["y"].cpu().numpy().view(np.uint16), ry.view(np.uint16))
 
 
+@pytest.mark.parametrize("generic", [False, True])
+def test_grouped_gemv_many_problems_every_output(gpu_lib, generic):
+    """A plan of 800 problems (more than a benchmark launch over 112 layers
+    holds) with ragged row counts over every register class, optionally one
+    problem of a generic k; every output of every problem against the
+    oracle."""
+    say(f"800-problem plan generic={generic}")
+    g = synth.rng(800 + generic)
+    ks = [1024, 2048, 3072, 4096, 8192]
+    shapes = [(int(g.integers(1, 160)), ks[i % 5]) for i in range(800)]
+    if generic:
+        shapes[17] = (333, 640)
+    probs, refs = [], []
+    for n, k in shapes:
+        words = synth.random_words(n * (k // 128) * 5, g)
+        sw = synth.row_scales(n, g, np.float16)
+        xq, sx, _ = synth.act_absmax_int8(1, k, g)
+        refs.append(sherry_ref.gemv_i8(words, sw, n, k, xq[0], sx[0], np.float16))
+        probs.append(dict(codes=words_dev(words), scales=dev(sw), x=dev(xq[0]), x_scale=dev(sx),
+                          acc=torch.empty(n, dtype=torch.int32, device=DEV),
+                          y=torch.empty(n, dtype=torch.float16, device=DEV)))
+    grouped = gpu_lib.GroupedGemv(probs)
+    grouped()
+    torch.cuda.synchronize()
+    for i, (p, (ra, ry)) in enumerate(zip(probs, refs)):
+        assert np.array_equal(p["acc"].cpu().numpy(), ra), (i, shapes[i])
+        assert np.array_equal(p["y"].cpu().numpy().view(np.uint16), ry.view(np.uint16)), (i, shapes[i])
+
+
 @pytest.mark.parametrize("shapes,mfma", [
     ([(1024, 3072), (300, 8192), (64, 2048), (1500, 1024), (77, 640), (520, 4096)], False),
     ([(1024, 3072), (200, 16384), (64, 2048)], False),

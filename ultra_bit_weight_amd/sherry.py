@@ -14,7 +14,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "lib", "libsherry.so")
+# SHERRY_LIB names another build of the library (for comparing build-time
+# variants); by default the in-tree one
+LIB_PATH = os.environ.get("SHERRY_LIB") or os.path.join(_HERE, "lib", "libsherry.so")
 
 I8, I32, F16, BF16, F32 = 0, 1, 2, 3, 4
 _DT = {torch.int8: I8, torch.int32: I32, torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
@@ -144,7 +146,7 @@ def _dev(*ts):
         raise ValueError(f"tensors are on different devices: {sorted(str(d) for d in devs)}")
 
 
-def _need(t, name, numel=None, nbytes=None, dtypes=None, dim=None):
+def _need(t, name, numel=None, nbytes=None, dtypes=None, dim=None, min_nbytes=None):
     """Size and type checks the C ABI cannot make (it takes bare pointers):
     a wrong size here would let a kernel read or write past a buffer.  Runs on
     tensor metadata only, before any device check."""
@@ -160,6 +162,8 @@ def _need(t, name, numel=None, nbytes=None, dtypes=None, dim=None):
         raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
     if nbytes is not None and t.numel() * t.element_size() != nbytes:
         raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, expected {nbytes}")
+    if min_nbytes is not None and t.numel() * t.element_size() < min_nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs at least {min_nbytes}")
 
 
 _SCALE_DT = (torch.float32, torch.float16)
@@ -178,7 +182,7 @@ def _check_gemv_args(fmt, codes, scales, x, x_scale, acc, y):
     _need(scales, "scales", dim=1, dtypes=_SCALE_DT)
     _need(x, "x", dim=1)
     n, k = scales.numel(), x.numel()
-    _need(codes, "codes", nbytes=_codes_bytes(fmt, n, k))
+    _need(codes, "codes", min_nbytes=_codes_bytes(fmt, n, k))
     _need(x_scale, "x_scale", numel=1, dtypes=(torch.float32,))
     _need(acc, "acc", numel=n, dtypes=(torch.int32,))
     _need(y, "y", numel=n, dtypes=_Y_DT)
@@ -194,7 +198,7 @@ def _check_gemm_args(fmt, codes, scales, x, x_scales, acc, y):
     _need(scales, "scales", dim=1, dtypes=_SCALE_DT)
     m, k = x.shape
     n = scales.numel()
-    _need(codes, "codes", nbytes=_codes_bytes(fmt, n, k))
+    _need(codes, "codes", min_nbytes=_codes_bytes(fmt, n, k))
     _need(x_scales, "x_scales", numel=m, dtypes=(torch.float32,))
     _need(acc, "acc", numel=m * n, dtypes=(torch.int32,))
     if y is not None:
@@ -277,7 +281,7 @@ def probe_rates(mode: int, iters: int, blocks: int, sink: torch.Tensor):
 
 def decode(codes: torch.Tensor, n: int, k: int) -> torch.Tensor:
     """Packed codes -> dense int8 ternary matrix [n, k]."""
-    _need(codes, "codes", nbytes=_codes_bytes("sherry", n, k))
+    _need(codes, "codes", min_nbytes=_codes_bytes("sherry", n, k))
     _dev(codes)
     t = torch.empty(n, k, dtype=torch.int8, device=codes.device)
     _check("sherry_decode", load().sherry_decode(codes.data_ptr(), n, k, t.data_ptr(), t.stride(0), _stream()))
