@@ -353,3 +353,16 @@ def gemv_bf16(words, s_w, n: int, k: int, x_bits: np.ndarray) -> np.ndarray:
     if x64.shape != (k,):
         raise ValueError("x must have shape (k,)")
     return _exact_rows_dot(t, x64) * np.asarray(s_w).astype(np.float64)
+
+
+def gemm_bf16(words, s_w, n: int, k: int, x_bits: np.ndarray) -> np.ndarray:
+    """Product for M tokens with bf16 X [m, k]: Y[m, r] = s_w[r] * sum_k
+    T[r, k] X[m, k], each token's sums exact and rounded once to fp64, then
+    one rounding for the scale product (the batch-1 rule, token by token).
+    Returns fp64 [m, n]."""
+    t = unpack(words, n, k)
+    xb = np.asarray(x_bits)
+    if xb.ndim != 2 or xb.shape[1] != k:
+        raise ValueError("x must be [m, k]")
+    sw = np.asarray(s_w).astype(np.float64)
+    return np.stack([_exact_rows_dot(t, bf16_bits_to_f64(xb[i])) * sw for i in range(xb.shape[0])])

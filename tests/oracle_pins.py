@@ -382,6 +382,31 @@ def pin_bf16_wide_range(ref):
         assert y[r] == float(exact) * float(sw[r]), r
 
 
+def pin_gemm_bf16(ref):
+    """M tokens of bf16 x against exact rationals, on the generator's dense
+    matrix (never decoded by the oracle): one token of N(0, 1) values, one
+    spanning 2^-120 .. 2^120 (the exact-sum fallback), one of zeros, and
+    ragged sizes.  Each Y[m, r] is the exact sum rounded once to fp64, times
+    the row scale."""
+    g = synth.rng(45)
+    for n, k, m in [(3, 128, 3), (7, 256, 2)]:
+        t = synth.ternary_34(n, k, g)
+        words = ref.pack_codes(ref.codes_from_dense(t))
+        xb = np.zeros((m, k), np.uint16)
+        xb[0] = synth.x_bf16_normal(k, g)
+        if m > 2:
+            e = g.integers(127 - 120, 127 + 121, size=k)
+            xb[1] = ((g.integers(0, 2, size=k) << 15) | (e << 7) | g.integers(0, 128, size=k)).astype(np.uint16)
+        sw = synth.row_scales(n, g, np.float32)
+        y = ref.gemm_bf16(words, sw, n, k, xb)
+        assert y.shape == (m, n)
+        for i in range(m):
+            xv = [_bf16_value(int(v)) for v in xb[i].tolist()]
+            for r in range(n):
+                exact = sum(int(t[r, c]) * xv[c] for c in range(k))
+                assert y[i, r] == float(exact) * float(sw[r]), (n, k, i, r)
+
+
 # ------------------------------------------- activation quantization ---
 # Pins for oracle.act_ref (per-token absmax int8, readings A1-A3): hand
 # values, exact rational arithmetic, invariants, and the generator's own

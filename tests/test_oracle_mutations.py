@@ -16,7 +16,7 @@ from tests import oracle_pins as P
 PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "sherry_ref.py")
 ALL_PINS = [P.pin_bijection, P.pin_code_table, P.pin_packed_groups, P.pin_row_layout, P.pin_straddles, P.pin_size,
             P.pin_ramp_dot, P.pin_closed_forms, P.pin_brute_force, P.pin_packer, P.pin_epilogue,
-            P.pin_bf16_path, P.pin_bf16_wide_range]
+            P.pin_bf16_path, P.pin_bf16_wide_range, P.pin_gemm_bf16]
 
 
 def fresh():
@@ -150,9 +150,36 @@ def m_bf16_scale_dropped(ref):
     ref.gemv_bf16 = bad
 
 
+def m_gemm_bf16_token_order(ref):
+    """tokens taken in reverse order"""
+    orig = ref.gemm_bf16
+    ref.gemm_bf16 = lambda words, s_w, n, k, x_bits: orig(words, s_w, n, k, np.asarray(x_bits)[::-1])
+
+
+def m_gemm_bf16_scale_per_token(ref):
+    """the row scales applied along the token axis"""
+    def bad(words, s_w, n, k, x_bits):
+        t = ref.unpack(words, n, k)
+        xb = np.asarray(x_bits)
+        sw = np.asarray(s_w).astype(np.float64)
+        return np.stack([ref._exact_rows_dot(t, ref.bf16_bits_to_f64(xb[i])) * sw[i % len(sw)]
+                         for i in range(xb.shape[0])])
+    ref.gemm_bf16 = bad
+
+
+def m_gemm_bf16_fp32_sum(ref):
+    """the sums accumulated in fp32"""
+    def bad(words, s_w, n, k, x_bits):
+        t = ref.unpack(words, n, k).astype(np.float32)
+        x = np.stack([ref.bf16_bits_to_f64(r) for r in np.asarray(x_bits)]).astype(np.float32)
+        return (x @ t.T).astype(np.float64) * np.asarray(s_w).astype(np.float64)
+    ref.gemm_bf16 = bad
+
+
 MUTANTS = [m_sign_order_reversed, m_sign_meaning_flipped, m_zero_field_high, m_msb_first_stream,
            m_word_order_swapped, m_layout_groups_contiguous, m_transposed_operand, m_dropped_token_scale, m_fp64_epilogue,
-           m_tie_to_highest, m_absmean_scale, m_bf16_scale_dropped]
+           m_tie_to_highest, m_absmean_scale, m_bf16_scale_dropped, m_gemm_bf16_token_order,
+           m_gemm_bf16_scale_per_token, m_gemm_bf16_fp32_sum]
 
 
 # Planted in the source text of a private copy of oracle/sherry_ref.py: the

@@ -10,7 +10,7 @@ from tests import oracle_pins as P
 @pytest.mark.parametrize("pin", [
     P.pin_bijection, P.pin_code_table, P.pin_packed_groups, P.pin_row_layout, P.pin_straddles, P.pin_size,
     P.pin_ramp_dot, P.pin_closed_forms, P.pin_brute_force, P.pin_packer, P.pin_epilogue,
-    P.pin_bf16_path, P.pin_bf16_wide_range,
+    P.pin_bf16_path, P.pin_bf16_wide_range, P.pin_gemm_bf16,
 ], ids=lambda f: f.__name__)
 def test_pin(pin):
     pin(sherry_ref)
