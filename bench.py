@@ -54,6 +54,9 @@ def parse_args(argv=None):
     p.add_argument("--gemm-profile", action="store_true",
                    help="only the grouped GEMM launches on the 1B layer (M = 2048 prefill and M = 16 few-token), "
                         "a few of each, for a profiler; prints their timing and exits")
+    p.add_argument("--bf16-gemm-profile", action="store_true",
+                   help="only the grouped bf16 few-token GEMM on the 3B layer (M = 2, 4, 8, 16) over 72 replicas; "
+                        "prints their rates and exits")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) and exit")
     p.add_argument("--summarize-trace", metavar="TRACE_DIR",
@@ -453,6 +456,38 @@ def gemm_profile(torch, sherry, synth, probs, args):
     return 0
 
 
+def bf16_gemm_rates(torch, sherry, synth, probs_3b, replicas, seed, ms=(2, 4, 8, 16), steps=20):
+    """The bf16 few-token GEMM (matrix cores, fp32 outputs) over every matrix
+    of the 3B-layer replicas in `probs_3b`, one grouped launch per token
+    count; algorithmic bytes per layer = codes + fp16 row scales + X (2 m k)
+    + Y (4 m n)."""
+    import numpy as np
+
+    dev = torch.device("cuda:0")
+    g = synth.rng(seed)
+    shapes = synth.LLAMA32_3B_LAYER
+    res = {}
+    for m in ms:
+        xs = {}
+        for _, n, k in shapes:
+            if k not in xs:
+                xb = synth.x_bf16_normal((m, k), g)
+                xs[k] = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+        ys = {p["name"]: torch.empty(m, p["n"], dtype=torch.float32, device=dev) for p in probs_3b if p["replica"] == 0}
+        gp = [dict(codes=p["codes"], scales=p["scales"], x=xs[p["k"]], y=ys[p["name"]]) for p in probs_3b]
+        grouped = sherry.GroupedGemm(gp)
+        mean_ms, _ = time_launches(torch, grouped, steps, 3)
+        per_layer_ms = mean_ms / replicas
+        byts = sum(n * k * 5 // 32 + 2 * n + 2 * m * k + 4 * m * n for _, n, k in shapes)
+        flops = 2 * m * sum(n * k for _, n, k in shapes)
+        res[f"M{m}"] = {"grouped_us_per_layer": round(per_layer_ms * 1e3, 3), "replicas": replicas,
+                        "workgroups": grouped.n_tiles, "GBps": round(byts / (per_layer_ms * 1e-3) / 1e9, 1),
+                        "frac_hbm": round(byts / (per_layer_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "TFLOPs": round(flops / (per_layer_ms * 1e-3) / 1e12, 1)}
+        del gp, grouped
+    return res
+
+
 def graph_time(torch, fn, outs, replays=200):
     """Mean us per replay of fn captured in a HIP graph, after checking three
     replays (outputs cleared before each) against one eager run; a string
@@ -580,6 +615,9 @@ def extras(torch, sherry, synth, probs_1b, codes_1b, args):
                                    "weights_per_s": w3 / (mean_ms * 1e-3),
                                    "GBps": round(b3 / (mean_ms * 1e-3) / 1e9, 1),
                                    "frac_hbm": round(b3 / (mean_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    # bf16 x for a few tokens on the matrix cores: every matrix of the 72
+    # replicas in one grouped launch per token count
+    out["gemm_bf16_3b_layer"] = bf16_gemm_rates(torch, sherry, synth, probs_3b, R3, args.seed + 5)
     del g3, g3m, probs_3b, codes_3b
     torch.cuda.empty_cache()
 
@@ -823,6 +861,12 @@ def main(argv=None):
     torch.cuda.set_device(0)
     if args.probes:
         print(json.dumps(peak_probes(torch, sherry)), flush=True)
+        return 0
+    if args.bf16_gemm_profile:
+        R3 = max(1, int(round(args.replicas * 72 / 112)))
+        _, probs_3b = build_layer_replicas(torch, sherry, synth, synth.LLAMA32_3B_LAYER, R3, args.seed + 1,
+                                           x_kind="bf16")
+        print(json.dumps(bf16_gemm_rates(torch, sherry, synth, probs_3b, R3, args.seed + 5)), flush=True)
         return 0
     shapes = synth.LLAMA32_1B_LAYER
     R = args.replicas

@@ -158,6 +158,24 @@ def test_gemm_validation(lib, fn):
     assert gemm(lib, xs=None, acc=None, fn=fn) == EDEVICE
 
 
+def test_gemm_bf16_validation(lib):
+    """bf16 X: 3:4 codes only, m <= 16, k <= 8192, fp32 Y, no token scales
+    and no int32 sums; ldx counts elements (a multiple of 8: 16-byte rows)."""
+    ok = dict(x_dt=BF16, xs=None, acc=None, y_dt=F32)
+    assert gemm(lib, **ok) == EDEVICE
+    assert gemm(lib, **dict(ok, ldx=1032)) == EDEVICE        # 8-element multiple
+    assert gemm(lib, **dict(ok, ldx=1028)) == ESHAPE
+    assert gemm(lib, **dict(ok, m=16)) == EDEVICE
+    assert gemm(lib, **dict(ok, m=17)) == ESHAPE
+    assert gemm(lib, **dict(ok, k=8192, ldx=8192)) == EDEVICE
+    assert gemm(lib, **dict(ok, k=8320, ldx=8320)) == ESHAPE
+    assert gemm(lib, **dict(ok, y_dt=F16)) == EDTYPE
+    assert gemm(lib, **dict(ok, xs=A)) == EDTYPE
+    assert gemm(lib, **dict(ok, acc=A)) == EDTYPE
+    assert gemm(lib, **dict(ok, y=None)) == EINVAL          # neither acc nor y
+    assert gemm(lib, **dict(ok, fn="tern2_gemm")) == EDTYPE
+
+
 def test_act_quant_validation(lib):
     f = lib.sherry_act_quant
     assert f(None, F32, 2, 128, 128, A, 128, A, None) == EINVAL
@@ -360,6 +378,7 @@ def test_grouped_gemm_plan_on_host(lib):
     # validation: buffer too small, bad dtype, misaligned, bad shape, bad m
     assert lib.sherry_gemm_plan(arr2, 2, F16, I8, F16, base, nb2 - 8) == EINVAL
     assert lib.sherry_gemm_plan(arr2, 2, F16, BF16, F16, base, nb2) == EDTYPE
+    assert lib.sherry_gemm_plan(arr2, 2, F16, BF16, F32, base, nb2) == ESHAPE  # bf16 x: at most 16 tokens
     assert lib.sherry_gemm_plan(arr2, 2, F16, I8, F16, base + 4, nb2) == EALIGN
     arr2[1].k = 100
     assert lib.sherry_gemm_plan_bytes(arr2, 2) == 0
@@ -374,10 +393,24 @@ def test_grouped_gemm_plan_on_host(lib):
     arr3 = problems(few)
     n3 = 4 + 1 + 3
     nb3 = lib.sherry_gemm_plan_bytes(arr3, 3)
-    assert nb3 == 64 + 80 * 3 + 16 * n3
+    # room for the bf16 tiling too (every m <= 16, k <= 8192): 256-row tiles
+    n3_bf16 = 8 + 2 + 2
+    assert nb3 == 64 + 80 * 3 + 16 * max(n3, n3_bf16)
     assert lib.sherry_gemm_plan(arr3, 3, F16, I8, F16, base, nb3) == OK
     assert int.from_bytes(ctypes.string_at(base + 40, 8), "little") == 3
     assert tiles_of(base, 3, n3) == [(2, a, 0) for a in range(3)] + [(0, a, 0) for a in range(4)] + [(1, 0, 0)]
+    # the same problems with bf16 x (fp32 y, no token scales): tiling 5,
+    # 256-row tiles, longest rows first
+    assert lib.sherry_gemm_plan(arr3, 3, F16, BF16, F32, base, nb3) == OK
+    hdr = ctypes.string_at(base, 64)
+    assert int.from_bytes(hdr[12:16], "little") == n3_bf16 and int.from_bytes(hdr[40:48], "little") == 5
+    assert tiles_of(base, 3, n3_bf16) == [(2, 0, 0), (2, 1, 0)] + [(0, a, 0) for a in range(8)] + [(1, 0, 0),
+                                                                                                     (1, 1, 0)]
+    assert lib.sherry_gemm_plan(arr3, 3, F16, BF16, F16, base, nb3) == EDTYPE
+    assert lib.tern2_gemm_plan(arr3, 3, F16, BF16, F32, base, nb3) == EDTYPE
+    arr3[0].m = 17
+    assert lib.sherry_gemm_plan(arr3, 3, F16, BF16, F32, base, nb3) == ESHAPE
+    arr3[0].m = 16
     # every problem with m <= 2 and a register-class k: the two-token walk
     # (tiling 4), row tiles of the grouped GEMV: 512 rows at k = 2048, 1024 at
     # 1024, 256 at 3072, 128 at 8192; longest rows first
@@ -385,7 +418,7 @@ def test_grouped_gemm_plan_on_host(lib):
     arr5 = problems(two)
     n5 = 4 + 1 + 3 + 1
     nb5 = lib.sherry_gemm_plan_bytes(arr5, 4)
-    assert nb5 == 64 + 80 * 4 + 16 * n5
+    assert nb5 == 64 + 80 * 4 + 16 * max(n5, 8 + 2 + 2 + 1)  # the bf16 tiling needs more
     assert lib.sherry_gemm_plan(arr5, 4, F16, I8, F16, base, nb5) == OK
     assert int.from_bytes(ctypes.string_at(base + 40, 8), "little") == 4
     assert tiles_of(base, 4, n5) == ([(2, a, 0) for a in range(3)] + [(3, 0, 0)] + [(0, a, 0) for a in range(4)]

@@ -211,6 +211,83 @@ def test_gemv_bf16_within_tolerance(gpu_lib, n, k):
     assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
 
 
+# ------------------------------------------------ bf16 GEMM (few tokens) ---
+
+def bf16_dev(xb):
+    return dev(np.ascontiguousarray(xb).view(np.int16)).view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("m", [2, 3, 4, 8, 16])
+@pytest.mark.parametrize("n,k", [(1, 128), (37, 384), (100, 1024), (513, 2048), (3072, 3072), (64, 8192),
+                                 (300, 4096), (1024, 3072)])
+def test_gemm_bf16_within_tolerance(gpu_lib, m, n, k):
+    """bf16 X for a few tokens on the matrix cores: every k slice count
+    (1 .. 16 slices of 512), ragged rows and tokens; each token's outputs
+    within the bf16 tolerance of the exact reference, and a second call
+    gives the same bits."""
+    say(f"gemm_bf16 m={m} n={n} k={k}")
+    g = synth.rng(m * 1000 + n * 7 + k)
+    words = synth.random_words(n * (k // 128) * 5, g)
+    sw = synth.row_scales(n, g, np.float16 if n % 2 else np.float32)
+    xb = synth.x_bf16_normal((m, k), g)
+    ref = sherry_ref.gemm_bf16(words, sw, n, k, xb)
+    _, y = gpu_lib.gemm(words_dev(words), dev(sw), bf16_dev(xb))
+    _, y2 = gpu_lib.gemm(words_dev(words), dev(sw), bf16_dev(xb))
+    torch.cuda.synchronize()
+    assert y.dtype == torch.float32 and tuple(y.shape) == (m, n)
+    got = y.cpu().numpy()
+    for t in range(m):
+        check_fp_tolerance(got[t], ref[t])
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+
+
+def test_gemm_bf16_strided_x_and_y(gpu_lib):
+    """X rows ldx > k elements apart, Y rows ldy > n apart."""
+    say("gemm_bf16 strided")
+    g = synth.rng(515)
+    m, n, k = 5, 700, 3072
+    words = synth.random_words(n * (k // 128) * 5, g)
+    sw = synth.row_scales(n, g, np.float16)
+    big = synth.x_bf16_normal((m, k + 64), g)
+    ref = sherry_ref.gemm_bf16(words, sw, n, k, big[:, :k])
+    ybig = torch.full((m, n + 40), -7.0, dtype=torch.float32, device=DEV)
+    gpu_lib.gemm(words_dev(words), dev(sw), bf16_dev(big)[:, :k], out=ybig[:, :n])
+    torch.cuda.synchronize()
+    got = ybig.cpu().numpy()
+    for t in range(m):
+        check_fp_tolerance(got[t, :n], ref[t])
+    assert np.all(got[:, n:] == -7.0)
+
+
+@pytest.mark.parametrize("m", [2, 16])
+def test_grouped_gemm_bf16_3b_layer(gpu_lib, m):
+    """The seven matrices of a LLaMA-3.2-3B decoder layer at full size with
+    bf16 X for m tokens, one grouped launch; every output of every token
+    within the bf16 tolerance, and a second launch repeats the bits."""
+    say(f"grouped gemm_bf16 3B layer m={m}")
+    g = synth.rng(300 + m)
+    probs, refs = [], []
+    xs = {k: synth.x_bf16_normal((m, k), g) for k in (3072, 8192)}
+    for name, n, k in synth.LLAMA32_3B_LAYER:
+        words = synth.random_words(n * (k // 128) * 5, g)
+        sw = synth.row_scales(n, g, np.float16)
+        refs.append(sherry_ref.gemm_bf16(words, sw, n, k, xs[k]))
+        probs.append(dict(codes=words_dev(words), scales=dev(sw), x=bf16_dev(xs[k]),
+                          y=torch.empty(m, n, dtype=torch.float32, device=DEV)))
+    grouped = gpu_lib.GroupedGemm(probs)
+    grouped()
+    torch.cuda.synchronize()
+    first = [p["y"].clone() for p in probs]
+    for p, r, (name, n, k) in zip(probs, refs, synth.LLAMA32_3B_LAYER):
+        got = p["y"].cpu().numpy()
+        for t in range(m):
+            check_fp_tolerance(got[t], r[t])
+    grouped()
+    torch.cuda.synchronize()
+    for p, y0 in zip(probs, first):
+        assert torch.equal(p["y"].view(torch.int32), y0.view(torch.int32))
+
+
 # -------------------------------------------------------------------- GEMM ---
 
 @pytest.mark.parametrize("m", [1, 2, 3, 4, 8, 15, 16, 17, 33])

@@ -164,13 +164,21 @@ sherry_status check_gemm(int32_t format, const uint32_t* codes, const void* w_sc
   if (!codes || !w_scales || !x || (!acc && !y)) return SHERRY_EINVAL;
   if (m <= 0) return SHERRY_EINVAL;
   if (sherry_status s = check_nk(n, k)) return s;
-  if (m > 16 * 65535 || ldx < k || ldx % 16 != 0 || (y && ldy < n)) return SHERRY_ESHAPE;
-  if (ldx > std::numeric_limits<int64_t>::max() / m || (y && ldy > std::numeric_limits<int64_t>::max() / m))
+  // bf16 X (3:4 codes only): a few tokens on the matrix cores, fp32 Y only;
+  // row stride ldx in elements, 16-byte rows
+  const bool bf16 = x_dt == SHERRY_BF16;
+  if (bf16 && format != kFmtSherry) return SHERRY_EDTYPE;
+  if (bf16 && (acc || x_scales || !y || y_dt != SHERRY_F32)) return SHERRY_EDTYPE;
+  if (bf16 && (m > kBfFewMaxTok || k > kBfFewMaxK)) return SHERRY_ESHAPE;
+  const int64_t row_align = bf16 ? 8 : 16;  // elements per 16 bytes
+  if (m > 16 * 65535 || ldx < k || ldx % row_align != 0 || (y && ldy < n)) return SHERRY_ESHAPE;
+  if (ldx > std::numeric_limits<int64_t>::max() / (2 * m) || (y && ldy > std::numeric_limits<int64_t>::max() / m))
     return SHERRY_ESHAPE;
   // the tiled kernel addresses one matrix's codes and x with 32-bit offsets
-  if (!codes_fit_32(format, n, k) || static_cast<uint64_t>(m) * static_cast<uint64_t>(ldx) > 0xFFFFFFFFull)
+  if (!codes_fit_32(format, n, k) ||
+      static_cast<uint64_t>(m) * static_cast<uint64_t>(ldx) * (bf16 ? 2u : 1u) > 0xFFFFFFFFull)
     return SHERRY_ESHAPE;
-  if (!is_scale_dt(s_dt) || x_dt != SHERRY_I8) return SHERRY_EDTYPE;
+  if (!is_scale_dt(s_dt) || (x_dt != SHERRY_I8 && !bf16)) return SHERRY_EDTYPE;
   if (y && y_dt != SHERRY_F32 && y_dt != SHERRY_F16) return SHERRY_EDTYPE;
   if (!aligned(codes, 4) || !aligned(x, 16) || !aligned(w_scales, dt_size(s_dt)) || (acc && !aligned(acc, 4)) ||
       (x_scales && !aligned(x_scales, 4)) || (y && !aligned(y, dt_size(y_dt))))
@@ -199,6 +207,7 @@ sherry_status gemm_impl(int32_t format, const uint32_t* codes, const void* w_sca
           check_gemm(format, codes, w_scales, s_dt, n, k, x, x_dt, m, ldx, x_scales, acc, y, y_dt, ldy, &d))
     return s;
   if (sherry_status s = check_device()) return s;
+  if (x_dt == SHERRY_BF16) return launched(launch_gemm_bf16(d, stream));
   return launched(launch_gemm(d, format, stream));
 }
 
@@ -211,6 +220,7 @@ struct GemmTiling {
   int64_t kind;
   int rows, tok;
   int64_t rows_of(const sherry_gemm_problem& p) const {
+    if (kind == kGemmTilingBf16) return kBfFewMaxTileRows;
     if (kind == kGemmTilingTwo) return gemm2_tile_rows(p.k);
     return kind == kGemmTilingFew ? few_tile_rows(static_cast<int>(p.k / kGroupWeights)) : rows;
   }
@@ -225,7 +235,8 @@ int64_t gemm_tiles(const sherry_gemm_problem* probs, int32_t count, const GemmTi
   return tiles;
 }
 
-GemmTiling gemm_tiling(const sherry_gemm_problem* probs, int32_t count) {
+GemmTiling gemm_tiling(const sherry_gemm_problem* probs, int32_t count, dt_t x_dt = SHERRY_I8) {
+  if (x_dt == SHERRY_BF16) return GemmTiling{kGemmTilingBf16, kBfFewMaxTileRows, kBfFewMaxTok};
   bool two = true, few = true, skinny = true;
   for (int32_t i = 0; i < count; ++i) {
     two = two && gemm2_fits(probs[i].m, probs[i].k);
@@ -246,7 +257,13 @@ size_t gemm_plan_bytes_impl(const sherry_gemm_problem* probs, int32_t count) {
     if (check_nk(probs[i].n, probs[i].k) != SHERRY_OK) return 0;
     if (probs[i].m <= 0 || probs[i].m > 16 * 65535) return 0;
   }
-  const int64_t tiles = gemm_tiles(probs, count, gemm_tiling(probs, count));
+  // the plan holds the tiles of the int8 tiling or, if every problem allows
+  // bf16 x, of the bf16 one (the caller's x type decides): room for the larger
+  bool bf16_fits = true;
+  for (int32_t i = 0; i < count; ++i)
+    bf16_fits = bf16_fits && probs[i].m <= kBfFewMaxTok && probs[i].k <= kBfFewMaxK;
+  int64_t tiles = gemm_tiles(probs, count, gemm_tiling(probs, count));
+  if (bf16_fits) tiles = std::max(tiles, gemm_tiles(probs, count, gemm_tiling(probs, count, SHERRY_BF16)));
   if (tiles > kMaxDim) return 0;
   return sizeof(PlanHeader) + sizeof(GemmDesc) * static_cast<size_t>(count) + sizeof(GemmTile) * tiles;
 }
@@ -265,7 +282,7 @@ sherry_status gemm_plan_impl(int32_t format, const sherry_gemm_problem* probs, i
   if (need == 0) return SHERRY_ESHAPE;
   if (plan_bytes < need) return SHERRY_EINVAL;
   if (!aligned(plan, 8)) return SHERRY_EALIGN;
-  const GemmTiling tiling = gemm_tiling(probs, count);
+  const GemmTiling tiling = gemm_tiling(probs, count, x_dt);
   char* out = static_cast<char*>(plan);
   PlanHeader h;
   std::memset(&h, 0, sizeof(h));
@@ -273,6 +290,7 @@ sherry_status gemm_plan_impl(int32_t format, const sherry_gemm_problem* probs, i
   h.version = kPlanVersion;
   h.count = count;
   h.n_tiles = static_cast<int32_t>(gemm_tiles(probs, count, tiling));
+  if (gemm_tiles(probs, count, tiling) > kMaxDim) return SHERRY_ESHAPE;
   h.s_dt = s_dt;
   h.x_dt = x_dt;
   h.y_dt = y_dt;

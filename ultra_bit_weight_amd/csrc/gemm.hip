@@ -801,6 +801,7 @@ hipError_t launch_gemm_grouped(const PlanHeader* h, const void* dev, hipStream_t
   const dim3 grid(h->n_tiles);
   const bool t2 = h->format == kFmtTern2;
   if (tiling == kGemmTilingTwo) return launch_gemm2_grouped(plan, h->n_tiles, h->format, stream);
+  if (tiling == kGemmTilingBf16) return launch_gemm_bf16_grouped(plan, h->n_tiles, stream);
   if (tiling == kGemmTilingFew) {
     if (t2)
       hipLaunchKernelGGL((gemm_few_grouped_kernel<Tern2>), grid, dim3(kFewWaves * kWave), 0, stream, plan);

@@ -350,41 +350,6 @@ __device__ __forceinline__ void gemv_i8_rows_generic(const GemvDesc& d, int row_
 // ---------------------------------------------------------------- bf16 x ---
 // Weights expanded to four bf16 (one 8-byte table entry) per code, two
 // v_dot2_f32_bf16 per block; fp32 accumulation, then y = acc * s_w.
-// Byte offsets code * 8 of the 32 codes of a group (8-byte table entries)
-// with one bit-field extraction for most codes.  Code j sits at bit
-// o = 5j mod 32 of word 5j / 32; its offset is the 8-bit field
-// [o - 3, o + 5) once the three bits under the code -- the top three bits of
-// code j - 1 -- are zero.  Two masked copies of the words provide that: m[0..4]
-// with bits 2-4 of every odd code cleared (for even j), m[5..9] with those of
-// every even code (odd j).  The copies pass through an empty asm statement,
-// or the compiler folds the cleared bits back into a shift and a mask.
-constexpr uint32_t top3_bits(int word, int parity) {
-  uint32_t m = 0;
-  for (int j = parity; j < 32; j += 2)
-    for (int b = 5 * j + 2; b <= 5 * j + 4; ++b)
-      if (b >= 32 * word && b < 32 * word + 32) m |= 1u << (b - 32 * word);
-  return m;
-}
-
-__device__ __forceinline__ void masked_words8(const uint32_t* w, uint32_t* m) {
-#pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    m[i] = w[i] & ~top3_bits(i, 1);
-    m[5 + i] = w[i] & ~top3_bits(i, 0);
-    asm volatile("" : "+v"(m[i]), "+v"(m[5 + i]));
-  }
-}
-
-__device__ __forceinline__ uint32_t code_offset8(const uint32_t* w, const uint32_t* m, int j) {
-  const int bit = 5 * j;
-  const int i = bit >> 5;
-  const int o = bit & 31;
-  const uint32_t* c = m + 5 * (j & 1);
-  if (o < 3) return (w[i] << (3 - o)) & 0xF8u;                       // j = 0, 13, 26
-  if (o <= 27) return (c[i] >> (o - 3)) & 0xFFu;                    // one v_bfe_u32
-  return __builtin_amdgcn_alignbit(w[i + 1], c[i], o - 3) & 0xFFu;  // j = 6, 12, 19, 25
-}
-
 // bf16 x is staged once per workgroup into LDS with contiguous 16-byte
 // loads; the register-resident classes then read their slices from LDS.  One
 // 16-byte pad follows every group slice (16 chunks) so that lanes reading

@@ -145,7 +145,7 @@ static_assert(sizeof(GemmTile) == 16, "grouped GEMM tile record layout");
 // Rows x tokens of the tilings of the tiled kernel: 128 x 128, 256 x 256,
 // and 256 x 16 for plans whose problems all have m <= 16.
 constexpr int64_t kGemmTilingSmall = 0, kGemmTilingLarge = 1, kGemmTilingSkinny = 2, kGemmTilingFew = 3,
-                  kGemmTilingTwo = 4;
+                  kGemmTilingTwo = 4, kGemmTilingBf16 = 5;
 constexpr int kGemmLargeRows = 256, kGemmLargeTok = 192;
 constexpr int kGemmSmallRows = 128, kGemmSmallTok = 128;
 constexpr int kGemmSkinnyRows = 256, kGemmSkinnyTok = 16;
@@ -188,6 +188,21 @@ inline int gemm2_tile_rows(int64_t k) { return rows_per_iter(kclass_of(k)) * kGr
 hipError_t launch_gemm2(const GemmDesc& d, int32_t format, hipStream_t stream);
 hipError_t launch_gemm2_grouped(const char* plan, int32_t n_tiles, int32_t format, hipStream_t stream);
 hipError_t launch_gemm_grouped(const PlanHeader* host, const void* dev, hipStream_t stream);
+// bf16 x for a few tokens (m <= kBfFewMaxTok, k <= kBfFewMaxK) on the matrix
+// cores, fp32 outputs: 16-wave workgroups, k split into S slices of 512
+// weights (S = bf_few_slices, a power of two) and the rows into 16 / S row
+// groups; grouped tiles of kBfFewMaxTileRows rows.
+constexpr int kBfFewWaves = 16;
+constexpr int kBfFewMaxTok = 16;
+constexpr int64_t kBfFewMaxK = 8192;
+constexpr int kBfFewMaxTileRows = 256;
+__host__ __device__ constexpr int bf_few_slices(int groups) {
+  int s = 1;
+  while (4 * s < groups) s *= 2;
+  return s;
+}
+hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t stream);
+hipError_t launch_gemm_bf16_grouped(const char* plan, int32_t n_tiles, hipStream_t stream);
 // Activation quantization: input element types; the GEMV that quantizes its
 // own x holds it in LDS, k <= kActMaxK.
 constexpr int kActF32 = 0, kActF16 = 1, kActBf16 = 2;

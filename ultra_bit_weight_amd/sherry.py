@@ -195,6 +195,7 @@ def _check_gemm_args(fmt, codes, scales, x, x_scales, acc, y):
     acc [m, n] contiguous."""
     if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be [m, k] with unit column stride")
+    _need(x, "x", dtypes=(torch.int8, torch.bfloat16))
     _need(scales, "scales", dim=1, dtypes=_SCALE_DT)
     m, k = x.shape
     n = scales.numel()
@@ -360,7 +361,11 @@ def _gemm(fn_name, codes, scales, x, x_scales, out_dtype, want_acc, out=None, ac
 
 
 def gemm(codes, scales, x, x_scales=None, out_dtype=torch.float16, want_acc=False, out=None, acc_out=None):
-    """Y[m, r] = s_x[m] s_w[r] sum_k X[m, k] T[r, k] for int8 X [m, k]."""
+    """Y[m, r] = s_x[m] s_w[r] sum_k X[m, k] T[r, k] for int8 X [m, k]; for
+    bf16 X (m <= 16, k <= 8192) Y[m, r] = s_w[r] sum_k X[m, k] T[r, k] in fp32
+    (no token scales, no int32 sums, fp32 outputs)."""
+    if x.dtype == torch.bfloat16 and out is None:
+        out_dtype = torch.float32
     return _gemm("sherry_gemm", codes, scales, x, x_scales, out_dtype, want_acc, out, acc_out)
 
 
@@ -447,7 +452,8 @@ class GroupedGemv:
 
 class GroupedGemm:
     """Many products for M tokens in one launch.  `problems` is a list of dicts
-    with keys codes, scales, x ([m, k] int8, unit column stride), x_scales (or
+    with keys codes, scales, x ([m, k] int8 or bf16, unit column stride; one
+    type for all), x_scales (or
     None), acc (or None, [m, n] int32 contiguous), y (or None, [m, n] with unit
     column stride); all share the scale / y dtypes.  The plan is built once on
     the host and copied to the device; call() launches it on the current
@@ -466,13 +472,14 @@ class GroupedGemm:
             self._keep.append(p)
         p0 = problems[0]
         s_dt = _DT[p0["scales"].dtype]
+        x_dt = _DT[p0["x"].dtype]
         y_dt = _DT[p0["y"].dtype] if p0.get("y") is not None else F32
         nbytes = lib.sherry_gemm_plan_bytes(arr, len(problems))
         if nbytes == 0:
             raise ValueError("invalid grouped GEMM problems")
         self.host = torch.empty(nbytes, dtype=torch.uint8)
         fn = lib.tern2_gemm_plan if tern2 else lib.sherry_gemm_plan
-        _check("gemm_plan", fn(arr, len(problems), s_dt, I8, y_dt, self.host.data_ptr(), nbytes))
+        _check("gemm_plan", fn(arr, len(problems), s_dt, x_dt, y_dt, self.host.data_ptr(), nbytes))
         self.dev = self.host.to(p0["x"].device, non_blocking=False)
         self.n_tiles = int.from_bytes(bytes(self.host[12:16].tolist()), "little", signed=True)
         self.count = len(problems)
