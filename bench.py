@@ -59,6 +59,9 @@ def parse_args(argv=None):
                         "prints their rates and exits")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) and exit")
+    p.add_argument("--summarize-pmc", nargs="+", metavar="PMC_DIR",
+                   help="summarise rocprofv3 --pmc runs of `bench.py --no-extras` (grouped GEMV counters per "
+                        "dispatch and per 128-weight group) and exit")
     p.add_argument("--summarize-trace", metavar="TRACE_DIR",
                    help="summarise a rocprofv3 --kernel-trace run of `bench.py --no-extras` (the last --steps "
                         "dispatches of the grouped GEMV are its timed launches) and exit")
@@ -803,6 +806,35 @@ def summarize_counters(fetch_dir, write_dir):
 GEMV_KERNEL_PATTERNS = ("gemv_i8_grouped_kernel",)
 
 
+def summarize_pmc(dirs, replicas):
+    """rocprofv3 --pmc runs of `bench.py --no-extras` (one counter set per
+    directory): the median per dispatch of every counter the grouped GEMV
+    dispatches carry, and the instruction counters per 128-weight group per
+    lane (wave instructions x 64 lanes / groups of the launch: each lane walks
+    one group per row)."""
+    import csv
+
+    layer_groups = sum(n * k // 128 for n, k in
+                       ((2048, 2048), (512, 2048), (512, 2048), (2048, 2048), (8192, 2048), (8192, 2048), (2048, 8192)))
+    groups = replicas * layer_groups
+    vals = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for row in csv.DictReader(fh):
+                    if not any(p in row.get("Kernel_Name", "") for p in GEMV_KERNEL_PATTERNS):
+                        continue
+                    vals.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+    res = {"groups_per_launch": groups, "per_dispatch_median": {}, "per_group_lane": {}}
+    for name, v in sorted(vals.items()):
+        med = statistics.median(v)
+        res["per_dispatch_median"][name] = med
+        if name.startswith("SQ_INSTS") or name in ("SQ_WAIT_INST_ANY", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_VALU"):
+            res["per_group_lane"][name] = round(med * 64 / groups, 2)
+    print(json.dumps(res))
+    return res
+
+
 def summarize_trace(trace_dir, timed):
     """A rocprofv3 --kernel-trace run of the default benchmark: the grouped
     GEMV's duration over all its dispatches (warm-up and clock settling
@@ -841,6 +873,9 @@ def main(argv=None):
     SETTLE_MS = args.settle_ms
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
+        return 0
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc, args.replicas)
         return 0
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.steps)

@@ -393,19 +393,18 @@ def test_grouped_gemm_plan_on_host(lib):
     arr3 = problems(few)
     n3 = 4 + 1 + 3
     nb3 = lib.sherry_gemm_plan_bytes(arr3, 3)
-    # room for the bf16 tiling too (every m <= 16, k <= 8192): 256-row tiles
-    n3_bf16 = 8 + 2 + 2
+    # room for the bf16 tiling too (every m <= 16, k <= 8192): 1024-row tiles
+    n3_bf16 = 2 + 1 + 1
     assert nb3 == 64 + 80 * 3 + 16 * max(n3, n3_bf16)
     assert lib.sherry_gemm_plan(arr3, 3, F16, I8, F16, base, nb3) == OK
     assert int.from_bytes(ctypes.string_at(base + 40, 8), "little") == 3
     assert tiles_of(base, 3, n3) == [(2, a, 0) for a in range(3)] + [(0, a, 0) for a in range(4)] + [(1, 0, 0)]
     # the same problems with bf16 x (fp32 y, no token scales): tiling 5,
-    # 256-row tiles, longest rows first
+    # 1024-row tiles, longest rows first
     assert lib.sherry_gemm_plan(arr3, 3, F16, BF16, F32, base, nb3) == OK
     hdr = ctypes.string_at(base, 64)
     assert int.from_bytes(hdr[12:16], "little") == n3_bf16 and int.from_bytes(hdr[40:48], "little") == 5
-    assert tiles_of(base, 3, n3_bf16) == [(2, 0, 0), (2, 1, 0)] + [(0, a, 0) for a in range(8)] + [(1, 0, 0),
-                                                                                                     (1, 1, 0)]
+    assert tiles_of(base, 3, n3_bf16) == [(2, 0, 0), (0, 0, 0), (0, 1, 0), (1, 0, 0)]
     assert lib.sherry_gemm_plan(arr3, 3, F16, BF16, F16, base, nb3) == EDTYPE
     assert lib.tern2_gemm_plan(arr3, 3, F16, BF16, F32, base, nb3) == EDTYPE
     arr3[0].m = 17
@@ -418,7 +417,7 @@ def test_grouped_gemm_plan_on_host(lib):
     arr5 = problems(two)
     n5 = 4 + 1 + 3 + 1
     nb5 = lib.sherry_gemm_plan_bytes(arr5, 4)
-    assert nb5 == 64 + 80 * 4 + 16 * max(n5, 8 + 2 + 2 + 1)  # the bf16 tiling needs more
+    assert nb5 == 64 + 80 * 4 + 16 * max(n5, 2 + 1 + 1 + 1)  # room for the bf16 tiling too
     assert lib.sherry_gemm_plan(arr5, 4, F16, I8, F16, base, nb5) == OK
     assert int.from_bytes(ctypes.string_at(base + 40, 8), "little") == 4
     assert tiles_of(base, 4, n5) == ([(2, a, 0) for a in range(3)] + [(3, 0, 0)] + [(0, a, 0) for a in range(4)]

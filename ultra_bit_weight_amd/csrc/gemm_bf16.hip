@@ -36,7 +36,8 @@ constexpr int kBfThreads = kBfFewWaves * kWave;
 constexpr int kBfRing = 4;  // blocks of code words in flight per wave
 // table reads issued ahead of their products (in MFMAs): each product then
 // waits on one LDS round trip per batch, not one each
-constexpr int kBfBatch = 4;
+constexpr int kBfBatch = 2;  // (4 made the compiler spill inside the block loop)
+static_assert(16 % kBfBatch == 0, "whole batches per group");
 
 struct BfFewShared {
   uint2 tab[32];                                   // code -> four bf16 weights
@@ -153,26 +154,40 @@ __device__ __forceinline__ void gemm_bf16_few_tile(const GemmDesc& d, int row0, 
   }
 }
 
-// Full tiles (kBfFewMaxTileRows rows: NB = S blocks per row group) or, with
-// `one`, tiles of one block per row group (16 RG rows).
-__device__ __forceinline__ void gemm_bf16_few_dispatch(const GemmDesc& d, int tile, bool one, BfFewShared& sh) {
-  const int S = bf_few_slices(d.k / kGroupWeights);
-  const int rows = one ? 16 * (kBfFewWaves / S) : kBfFewMaxTileRows;
-  const int row0 = tile * rows;
-  switch (S) {
-    case 1: gemm_bf16_few_tile<1, 1>(d, row0, sh); break;
-    case 2: one ? gemm_bf16_few_tile<2, 1>(d, row0, sh) : gemm_bf16_few_tile<2, 2>(d, row0, sh); break;
-    case 4: one ? gemm_bf16_few_tile<4, 1>(d, row0, sh) : gemm_bf16_few_tile<4, 4>(d, row0, sh); break;
-    case 8: one ? gemm_bf16_few_tile<8, 1>(d, row0, sh) : gemm_bf16_few_tile<8, 8>(d, row0, sh); break;
-    default: one ? gemm_bf16_few_tile<16, 1>(d, row0, sh) : gemm_bf16_few_tile<16, 16>(d, row0, sh); break;
+// Row tiles of three sizes, by `size`: 2 = full (kBfFewMaxTileRows rows,
+// NB = F S blocks per row group), 1 = 256 rows (NB = S), 0 = one block per
+// row group (16 RG rows).  NB stays a compile-time constant.
+__host__ __device__ inline int bf_tile_rows(int k, int size) {
+  const int S = bf_few_slices(k / kGroupWeights);
+  return size == 2 ? kBfFewMaxTileRows : (size == 1 ? 256 : 16 * (kBfFewWaves / S));
+}
+
+template <int S>
+__device__ __forceinline__ void gemm_bf16_few_sized(const GemmDesc& d, int row0, int size, BfFewShared& sh) {
+  constexpr int F = kBfFewMaxTileRows / 256;
+  if (size == 2)
+    gemm_bf16_few_tile<S, F * S>(d, row0, sh);
+  else if (size == 1 && F > 1)
+    gemm_bf16_few_tile<S, S>(d, row0, sh);
+  else
+    gemm_bf16_few_tile<S, 1>(d, row0, sh);
+}
+
+__device__ __forceinline__ void gemm_bf16_few_dispatch(const GemmDesc& d, int tile, int size, BfFewShared& sh) {
+  const int row0 = tile * bf_tile_rows(d.k, size);
+  switch (bf_few_slices(d.k / kGroupWeights)) {
+    case 1: gemm_bf16_few_sized<1>(d, row0, size, sh); break;
+    case 2: gemm_bf16_few_sized<2>(d, row0, size, sh); break;
+    case 4: gemm_bf16_few_sized<4>(d, row0, size, sh); break;
+    case 8: gemm_bf16_few_sized<8>(d, row0, size, sh); break;
+    default: gemm_bf16_few_sized<16>(d, row0, size, sh); break;
   }
 }
 
-// Single product: full tiles, or one-block tiles when full ones would leave
-// most of the chip idle.
-__global__ __launch_bounds__(kBfThreads) void gemm_bf16_few_kernel(GemmDesc d, int one) {
+// Single product: the largest tiles that still give every CU a workgroup.
+__global__ __launch_bounds__(kBfThreads) void gemm_bf16_few_kernel(GemmDesc d, int size) {
   __shared__ BfFewShared sh;
-  gemm_bf16_few_dispatch(d, static_cast<int>(blockIdx.x), one != 0, sh);
+  gemm_bf16_few_dispatch(d, static_cast<int>(blockIdx.x), size, sh);
 }
 
 // Grouped: one workgroup per plan tile {problem, row tile}; a tile is
@@ -182,18 +197,17 @@ __global__ __launch_bounds__(kBfThreads) void gemm_bf16_few_grouped_kernel(const
   const PlanHeader* h = reinterpret_cast<const PlanHeader*>(plan);
   const GemmDesc* descs = reinterpret_cast<const GemmDesc*>(plan + sizeof(PlanHeader));
   const GemmTile tl = reinterpret_cast<const GemmTile*>(descs + h->count)[blockIdx.x];
-  gemm_bf16_few_dispatch(descs[tl.prob], tl.tile_n, false, sh);
+  gemm_bf16_few_dispatch(descs[tl.prob], tl.tile_n, 2, sh);
 }
 
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t stream) {
-  // full tiles when they still give every CU a workgroup
-  const int full = (d.n + kBfFewMaxTileRows - 1) / kBfFewMaxTileRows;
-  const bool one = full < 256;
-  const int rows = one ? 16 * (kBfFewWaves / bf_few_slices(d.k / kGroupWeights)) : kBfFewMaxTileRows;
+  int size = 2;
+  while (size > 0 && (d.n + bf_tile_rows(d.k, size) - 1) / bf_tile_rows(d.k, size) < 256) --size;
+  const int rows = bf_tile_rows(d.k, size);
   const dim3 grid(static_cast<unsigned>((d.n + rows - 1) / rows));
-  hipLaunchKernelGGL(gemm_bf16_few_kernel, grid, dim3(kBfThreads), 0, stream, d, one ? 1 : 0);
+  hipLaunchKernelGGL(gemm_bf16_few_kernel, grid, dim3(kBfThreads), 0, stream, d, size);
   return hipGetLastError();
 }
 

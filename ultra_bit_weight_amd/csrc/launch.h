@@ -195,7 +195,10 @@ hipError_t launch_gemm_grouped(const PlanHeader* host, const void* dev, hipStrea
 constexpr int kBfFewWaves = 16;
 constexpr int kBfFewMaxTok = 16;
 constexpr int64_t kBfFewMaxK = 8192;
-constexpr int kBfFewMaxTileRows = 256;
+#ifndef SHERRY_BF_FEW_TILE_ROWS
+#define SHERRY_BF_FEW_TILE_ROWS 1024
+#endif
+constexpr int kBfFewMaxTileRows = SHERRY_BF_FEW_TILE_ROWS;  // a multiple of 256
 __host__ __device__ constexpr int bf_few_slices(int groups) {
   int s = 1;
   while (4 * s < groups) s *= 2;
