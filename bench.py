@@ -54,6 +54,9 @@ def parse_args(argv=None):
     p.add_argument("--gemm-profile", action="store_true",
                    help="only the grouped GEMM launches on the 1B layer (M = 2048 prefill and M = 16 few-token), "
                         "a few of each, for a profiler; prints their timing and exits")
+    p.add_argument("--f4-profile", action="store_true",
+                   help="only the decode pipeline (a 1B token's fused products over min(16, replicas) layers, "
+                        "eager and graph replay); prints its timing and exits")
     p.add_argument("--bf16-gemm-profile", action="store_true",
                    help="only the grouped bf16 few-token GEMM on the 3B layer (M = 2, 4, 8, 16) over 72 replicas; "
                         "prints their rates and exits")
@@ -491,6 +494,58 @@ def bf16_gemm_rates(torch, sherry, synth, probs_3b, replicas, seed, ms=(2, 4, 8,
     return res
 
 
+def f4_decode_token(torch, sherry, probs, layers):
+    """A 1B token's weight pass as decode runs it: per decoder layer the four
+    products in dependency order, x quantized inside each -- q|k|v,
+    (attention not run) o, gate|up, down -- over `layers` layers with weights
+    of their own (replica l is layer l).  Timed eager as prepared calls, eager
+    as plain binding calls (argument checks every call), and replayed from
+    one HIP graph holding the whole token (checked against eager first)."""
+    dev = torch.device("cuda:0")
+    steps, outs, plain = [], [], []
+    code_bytes = 0
+    for l in range(layers):
+        by = {p["name"]: p for p in probs if p["replica"] == l}
+        code_bytes += sum(p["n"] * p["k"] * 5 // 32 for p in by.values())
+        qkv = (torch.cat([by[nm]["codes"] for nm in ("q", "k", "v")]),
+               torch.cat([by[nm]["scales"] for nm in ("q", "k", "v")]))
+        gu = (torch.cat([by[nm]["codes"] for nm in ("gate", "up")]),
+              torch.cat([by[nm]["scales"] for nm in ("gate", "up")]))
+        mats = [qkv, (by["o"]["codes"], by["o"]["scales"]), gu, (by["down"]["codes"], by["down"]["scales"])]
+        for (c, sc), k in zip(mats, (2048, 2048, 2048, 8192)):
+            x = torch.randn(k, device=dev).to(torch.bfloat16)
+            y = torch.empty(sc.numel(), dtype=torch.float16, device=dev)
+            steps.append(sherry.PreparedGemvQuant(c, sc, x, out=y))
+            plain.append((c, sc, x, y))
+            outs.append(y)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def token_prepared():
+        for c in steps:
+            c(stream)
+
+    def token_prepared_current():  # torch's current stream, for capture
+        for c in steps:
+            c()
+
+    def token_plain():
+        for c, sc, x, y in plain:
+            sherry.gemv_quant(c, sc, x, out=y)
+    res = {"layers": layers, "launches_per_token": len(steps), "code_bytes_per_token": code_bytes}
+    mean_ms, _ = time_launches(torch, token_prepared, 50, 5)
+    res["eager_us_per_token"] = round(mean_ms * 1e3, 1)
+    mean_ms, _ = time_launches(torch, token_plain, 50, 5)
+    res["eager_unprepared_us_per_token"] = round(mean_ms * 1e3, 1)
+    gus = graph_time(torch, token_prepared_current, outs, replays=50)
+    res["graph_us_per_token"] = gus
+    for key in ("eager_us_per_token", "eager_unprepared_us_per_token", "graph_us_per_token"):
+        if isinstance(res[key], float):
+            res[key.replace("per_token", "per_layer")] = round(res[key] / layers, 2)
+    if isinstance(gus, float):
+        res["graph_GBps"] = round(code_bytes / (gus * 1e-6) / 1e9, 1)
+    return res
+
+
 def graph_time(torch, fn, outs, replays=200):
     """Mean us per replay of fn captured in a HIP graph, after checking three
     replays (outputs cleared before each) against one eager run; a string
@@ -726,27 +781,7 @@ def extras(torch, sherry, synth, probs_1b, codes_1b, args):
     act["decode_step_code_bytes"] = int(qkv[0].numel() * 4 + gu[0].numel() * 4)
     out["act_quant_and_fused_projections"] = act
 
-    # a whole 1B decoder layer's products in dependency order, x quantized
-    # inside each: q|k|v, (attention not run) o, gate|up, down -- four
-    # launches per layer; 16 layers make a LLaMA-3.2-1B token's weight pass
-    xo = torch.randn(2048, device=dev).to(torch.bfloat16)
-    xd = torch.randn(8192, device=dev).to(torch.bfloat16)
-    y_o = torch.empty(2048, dtype=torch.float16, device=dev)
-    y_d = torch.empty(2048, dtype=torch.float16, device=dev)
-
-    def layer_step():
-        sherry.gemv_quant(qkv[0], qkv[1], x1, out=y_qkv)
-        sherry.gemv_quant(by["o"]["codes"], by["o"]["scales"], xo, out=y_o)
-        sherry.gemv_quant(gu[0], gu[1], x2, out=y_gu)
-        sherry.gemv_quant(by["down"]["codes"], by["down"]["scales"], xd, out=y_d)
-    mean_ms, _ = time_launches(torch, layer_step, 200, 20)
-    lay = {"eager_us_per_layer": round(mean_ms * 1e3, 2)}
-    gus = graph_time(torch, layer_step, (y_qkv, y_o, y_gu, y_d))
-    lay["graph_us_per_layer"] = gus
-    lay["code_bytes_per_layer"] = int(sum(n * k * 5 // 32 for _, n, k in shapes_1b))
-    if isinstance(gus, float):
-        lay["graph_us_per_token_16_layers"] = round(16 * gus, 1)
-    out["f4_decode_layer_1b"] = lay
+    out["f4_decode_token_1b"] = f4_decode_token(torch, sherry, probs_1b, min(16, R))
     out["library_beside"] = library_beside(torch, synth, args)
     out["peak_probes"] = peak_probes(torch, sherry)
 
@@ -908,6 +943,9 @@ def main(argv=None):
     codes, probs = build_layer_replicas(torch, sherry, synth, shapes, R, args.seed)
     if args.gemm_profile:
         return gemm_profile(torch, sherry, synth, probs, args)
+    if args.f4_profile:
+        print(json.dumps(f4_decode_token(torch, sherry, probs, min(16, R))), flush=True)
+        return 0
     grouped = sherry.GroupedGemv(probs)
     torch.cuda.synchronize()
     print(f"# built {R} replicas of the 1B layer: {codes.numel() * 4 / 1e9:.3f} GB of codes, "

@@ -240,6 +240,15 @@ def pin_packer(ref):
         err = lambda s: float(np.sum((w[r] - s * t[r]) ** 2))  # noqa: E731
         assert err(alpha[r]) < err(alpha[r] * (1 + 1e-3)) and err(alpha[r]) < err(alpha[r] * (1 - 1e-3))
         assert math.isclose(alpha[r], float(np.sum(np.abs(w[r]) * (t[r] != 0))) / (3 * k // 4), rel_tol=1e-14)
+    # fp16 scales below 2^-14 round to subnormals, ties to even: W = s T with s
+    # halfway between two subnormals (multiples of 2^-24), the smallest
+    # subnormal, and values that round to zero or up to 2^-24
+    t8 = synth.ternary_34(8, 128, g)
+    for r, s16 in enumerate([(2 * mm + 1) * 2.0 ** -25 for mm in (0, 1, 2, 500)] +
+                            [2.0 ** -24, 2.0 ** -26, 3 * 2.0 ** -26, 0.3e-6]):
+        _, sc = ref.pack((t8[r:r + 1] * s16).astype(np.float32), np.float16)
+        exact = Fraction(float(np.float32(s16)))
+        assert Fraction(float(sc[0])) == f16_exact(exact), (r, s16)
     # pack(s * T) recovers T and s exactly (fp32 s; fp64 sums of equal values are exact)
     t34 = synth.ternary_34(9, 512, g)
     s = synth.row_scales(9, g, np.float32)

@@ -511,6 +511,15 @@ def test_binding_rejects_mismatched_gemv_buffers(lib):
         sherry.gemv_quant(ok["codes"], ok["scales"], _t(k, torch.float32), out=_t(n - 1, torch.float16))
     with pytest.raises(ValueError, match="bytes"):
         sherry.decode(_t(words - 1, torch.int32), n, k)
+    # the prepared call makes the same checks once, at construction
+    with pytest.raises(ValueError, match="elements|bytes"):
+        sherry.PreparedGemvQuant(ok["codes"], ok["scales"], _t(k, torch.bfloat16), out=_t(n + 1, torch.float16))
+    with pytest.raises(ValueError, match="bytes"):
+        sherry.PreparedGemvQuant(_t(words - 1, torch.int32), ok["scales"], _t(k, torch.bfloat16))
+    with pytest.raises(ValueError, match="dtype"):
+        sherry.PreparedGemvQuant(ok["codes"], ok["scales"], _t(k, torch.int8))
+    with pytest.raises(ValueError, match="GPU"):
+        sherry.PreparedGemvQuant(ok["codes"], ok["scales"], _t(k, torch.bfloat16), out=ok["out"])
 
 
 def test_binding_rejects_mismatched_gemm_buffers(lib):

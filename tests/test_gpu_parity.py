@@ -103,6 +103,35 @@ def test_tern2_pack_matches_oracle(gpu_lib, n, k, w_dtype):
     assert torch.equal(words, via) and torch.equal(sc.view(torch.int16), s5.view(torch.int16))
 
 
+@pytest.mark.parametrize("w_dtype", [np.float32, "bf16"])
+def test_pack_subnormal_fp16_scales(gpu_lib, w_dtype):
+    """Row scales in fp16's subnormal range (below 2^-14): weights of about
+    1e-6, rows whose exact scale lies halfway between two subnormals (ties go
+    to the even one), the smallest subnormal 2^-24, and a scale that rounds
+    to zero (2^-26).  Codes and fp16 scale bits against the oracle."""
+    say(f"pack subnormal fp16 scales w={w_dtype}")
+    g = synth.rng(4711)
+    n, k = 16, 256
+    w32 = (g.standard_normal((n, k)) * 1e-6).astype(np.float32)
+    t = synth.ternary_34(8, k, g)
+    halves = [(2 * mm + 1) * 2.0 ** -25 for mm in (0, 1, 2, 3, 500)] + [2.0 ** -24, 2.0 ** -26, 3 * 2.0 ** -26]
+    for r, s in enumerate(halves):  # W = s T: the exact scale is s
+        w32[8 + r] = (t[r] * s).astype(np.float32)
+    if w_dtype == "bf16":
+        bits = synth.f32_to_bf16_bits(w32)
+        w_host = (bits.astype(np.uint32) << 16).view(np.float32)
+        w_t = dev(bits.view(np.int16)).view(torch.bfloat16)
+    else:
+        w_host = w32
+        w_t = dev(w32)
+    ref_words, ref_scales = sherry_ref.pack(w_host, np.float16)
+    assert np.all(np.abs(ref_scales.astype(np.float32)) < 2.0 ** -14)  # every scale subnormal (or zero)
+    codes, scales = gpu_lib.pack(w_t, torch.float16)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_words(codes), ref_words)
+    assert np.array_equal(scales.cpu().numpy().view(np.uint16), ref_scales.view(np.uint16))
+
+
 def test_pack_exact_ternary_and_row_stride(gpu_lib):
     g = synth.rng(77)
     n, k, ld = 50, 1024, 1024 + 64
@@ -855,6 +884,34 @@ def test_gemv_quant(gpu_lib, dt, n, k):
     assert np.array_equal(sx.cpu().numpy().view(np.uint32), rs.view(np.uint32))
     assert np.array_equal(acc.cpu().numpy(), ra)
     assert np.array_equal(y.cpu().numpy().view(np.uint16), ry.view(np.uint16))
+
+
+def test_prepared_gemv_quant_follows_x(gpu_lib):
+    """The prepared call reads x's current contents on every call: two calls
+    with x rewritten between them (bf16, the 2048 class, then the 8192 class
+    with fp32 x) each equal the oracle chain bit for bit."""
+    for n, k, tdt, dt in ((3072, 2048, torch.bfloat16, "bf16"), (512, 8192, torch.float32, "f32")):
+        say(f"prepared gemv_quant n={n} k={k} {dt}")
+        g = synth.rng(73 + k)
+        words = synth.random_words(n * (k // 128) * 5, g)
+        sw = synth.row_scales(n, g, np.float16)
+        x = torch.empty(k, dtype=tdt, device=DEV)
+        call = gpu_lib.PreparedGemvQuant(words_dev(words), dev(sw), x, torch.float16, want_acc=True, want_scale=True)
+        for rep in range(2):
+            xs = (g.standard_normal(k) * (1.0 + 4.0 * rep)).astype(np.float32)
+            if dt == "f32":
+                host = xs
+                x.copy_(torch.from_numpy(xs))
+            else:
+                host = synth.f32_to_bf16_bits(xs)
+                x.copy_(torch.from_numpy(host.view(np.int16)).view(torch.bfloat16))
+            y = call()
+            torch.cuda.synchronize()
+            rq, rs = act_ref.quantize(host.reshape(1, k), dt)
+            ra, ry = sherry_ref.gemv_i8(words, sw, n, k, rq[0], rs[0], np.float16)
+            assert np.array_equal(call.scale.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+            assert np.array_equal(call.acc.cpu().numpy(), ra)
+            assert np.array_equal(y.cpu().numpy().view(np.uint16), ry.view(np.uint16))
 
 
 def test_gemv_quant_zero_token(gpu_lib):

@@ -55,15 +55,50 @@ constexpr int kActRegs = 32;
 constexpr int kActMaxRegK = kActRegs * kActThreads;
 static_assert(kActMaxRegK == kActMaxK, "the in-kernel quantization covers every k it accepts");
 
+// The token's values as raw bits, every load issued before any is used:
+// indices past k are clamped to the last value (an unconditional load; a
+// conditional one, or a conversion next to the load, made the compiler wait
+// for each load before issuing the next), and act_raw_value converts them
+// afterwards (zero past k).  XB = 4: 32-bit values, kept as bits; XB = 2:
+// 16-bit values, zero-extended.  (A compile-time width: with a run-time
+// branch between the two kinds of load, the compiler drained every load in
+// flight on entry to one of them.)  NR values per thread (NR * kActThreads
+// >= k; k fits 32 bits here).
+template <int NR, int XB>
+__device__ __forceinline__ void act_issue_raw(const void* x, int64_t base, int64_t k, uint32_t (&raw)[NR]) {
+  static_assert(XB == 2 || XB == 4, "16- or 32-bit values");
+  const int last = static_cast<int>(k) - 1;
+  const int t = static_cast<int>(threadIdx.x);
+  if constexpr (XB == 4) {
+    const SHERRY_GLOBAL uint32_t* p = gmem(static_cast<const uint32_t*>(x)) + base;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) raw[i] = p[min(t + i * kActThreads, last)];
+  } else {
+    const SHERRY_GLOBAL uint16_t* p = gmem(static_cast<const uint16_t*>(x)) + base;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) raw[i] = p[min(t + i * kActThreads, last)];
+  }
+}
+
+__device__ __forceinline__ float act_raw_value(uint32_t r, int dt, bool valid) {
+  const float v = dt == kActF32 ? __uint_as_float(r)
+                                : (dt == kActF16 ? static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(r)))
+                                                 : __uint_as_float(r << 16));
+  return valid ? v : 0.0f;
+}
+
 __device__ __forceinline__ float act_load_token(const void* x, int dt, int64_t base, int64_t k, float (&v)[kActRegs]) {
+  uint32_t raw[kActRegs];
+  if (dt == kActF32)
+    act_issue_raw<kActRegs, 4>(x, base, k, raw);
+  else
+    act_issue_raw<kActRegs, 2>(x, base, k, raw);
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < kActRegs; ++i) {
-    const int64_t j = threadIdx.x + static_cast<int64_t>(i) * kActThreads;
-    v[i] = j < k ? act_value(x, dt, base + j) : 0.0f;
+    v[i] = act_raw_value(raw[i], dt, static_cast<int>(threadIdx.x) + i * kActThreads < k);
+    amax = fmaxf(amax, fabsf(v[i]));
   }
-#pragma unroll
-  for (int i = 0; i < kActRegs; ++i) amax = fmaxf(amax, fabsf(v[i]));
   return amax;
 }
 

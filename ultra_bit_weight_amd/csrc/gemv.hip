@@ -32,13 +32,20 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // ---------------------------------------------------------------- int8 x ---
 // The 32-entry code table, then the pair table built from it.  Ends with a
 // barrier, so the tables are ready to read.
-template <class Fmt>
+template <class Fmt, bool kPairs = true>
 __device__ __forceinline__ void init_tables(uint32_t* tab32, uint2* pairs) {
   Fmt::init_table(tab32, threadIdx.x);
   __syncthreads();
-  Fmt::init_pair_table(pairs, tab32, threadIdx.x, blockDim.x);
-  __syncthreads();
+  if constexpr (kPairs) {
+    Fmt::init_pair_table(pairs, tab32, threadIdx.x, blockDim.x);
+    __syncthreads();
+  }
 }
+
+// Fused-quantization products (single calls, latency-bound) read every block
+// pair from the 32-entry table: no pair table to build, one barrier fewer
+// per workgroup (measured faster there; the grouped walks keep the pairs).
+constexpr bool kXqSingles = true;
 
 // x quantized by the workgroup itself (XQ): all threads load the token's fp
 // values (kActRegs each), take the absmax over the workgroup, and write the
@@ -47,22 +54,24 @@ __device__ __forceinline__ void init_tables(uint32_t* tab32, uint2* pairs) {
 // are in flight: xq_issue loads the token (kActRegs values per thread),
 // xq_finish takes the absmax over the workgroup, writes the int8 codes to xl
 // and the scale to *sx, and ends with a barrier.
-__device__ __forceinline__ void xq_issue(const GemvDesc& d, int dt, float (&v)[kActRegs]) {
-#pragma unroll
-  for (int i = 0; i < kActRegs; ++i) {
-    const int j = threadIdx.x + i * kActThreads;
-    v[i] = j < d.k ? act_value(d.x, dt, j) : 0.0f;
-  }
+template <int NR, int XB>
+__device__ __forceinline__ void xq_issue(const GemvDesc& d, uint32_t (&raw)[NR]) {
+  act_issue_raw<NR, XB>(d.x, 0, d.k, raw);
 }
 
-__device__ __forceinline__ void xq_finish(const GemvDesc& d, const float (&v)[kActRegs], int8_t* xl, float* sx,
-                                          float* wmax) {
+template <int NR>
+__device__ __forceinline__ void xq_finish(const GemvDesc& d, int dt, const uint32_t (&raw)[NR], int8_t* xl,
+                                          float* sx, float* wmax) {
+  float v[NR];
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kActRegs; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  for (int i = 0; i < NR; ++i) {
+    v[i] = act_raw_value(raw[i], dt, static_cast<int>(threadIdx.x) + i * kActThreads < d.k);
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
   const float s = act_scale(block_max(amax, wmax));
 #pragma unroll
-  for (int i = 0; i < kActRegs; ++i) {
+  for (int i = 0; i < NR; ++i) {
     const int j = threadIdx.x + i * kActThreads;
     if (j < d.k) xl[j] = act_code(v[i], s);
   }
@@ -70,10 +79,11 @@ __device__ __forceinline__ void xq_finish(const GemvDesc& d, const float (&v)[kA
   __syncthreads();
 }
 
+template <int XB>
 __device__ __forceinline__ void quantize_x_lds(const GemvDesc& d, int dt, int8_t* xl, float* sx, float* wmax) {
-  float v[kActRegs];
-  xq_issue(d, dt, v);
-  xq_finish(d, v, xl, sx, wmax);
+  uint32_t raw[kActRegs];
+  xq_issue<kActRegs, XB>(d, raw);
+  xq_finish(d, dt, raw, xl, sx, wmax);
 }
 
 // XQ: d.x holds fp values of type xdt; the workgroup quantizes them into xl
@@ -84,6 +94,7 @@ struct XQuant {
   int8_t* xl;
   float* sx;
   float* wmax;
+  uint2* swb;  // (class walks) the two half words of the scale of row row_begin + thread, loaded with the codes
 };
 
 // The 32 x dwords a lane multiplies with group g's 32 decoded dwords: for
@@ -135,7 +146,7 @@ static_assert(kXsPerThread * 16 * kGemvThreads == kMaxStagedKI8, "x staging spli
 // XM tokens per walk (1, or 2 for two-token products): token t's x row is
 // d.x + min(t, m - 1) * ldx, and its row results go to out[t * out_stride + ..];
 // the decoded codes serve every token.
-template <class Fmt, int L, int GPL, int GR = GPL * L, bool XQ = false, int XM = 1>
+template <class Fmt, int L, int GPL, int GR = GPL * L, int XQ = 0, int XM = 1>
 __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, int row_end, uint32_t* tab32,
                                              uint2* tab, int32_t* out, u32x4_t* xs, XQuant xq = XQuant{},
                                              int64_t ldx = 0, int m = 1, int out_stride = 0) {
@@ -220,7 +231,7 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
         // block pairs in the mask (kPairMask, kPairMaskTwo for two tokens):
         // one pair-table read; the others: two reads of the 32-entry table
         // (balances VALU against LDS bank conflicts)
-        constexpr unsigned PM = XM > 1 ? kPairMaskTwo : kPairMask;
+        constexpr unsigned PM = XM > 1 ? kPairMaskTwo : (XQ && kXqSingles ? 0u : kPairMask);
         const uint2 v = ((PM >> p) & 1) ? Fmt::i8x8(buf[t], p, tab)
                                         : make_uint2(Fmt::i8x4(buf[t], 2 * p, tab32),
                                                      Fmt::i8x4(buf[t], 2 * p + 1, tab32));
@@ -245,12 +256,28 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
   constexpr int NR = GPL > 1 ? 2 : kRing;  // several groups per lane: two buffers (registers)
   uint32_t ring[NR][GPL][NW];
   const int r0 = row_begin + wave * RPW + rs;
+  // XQ: the token's loads go first (the loads complete in order, and the
+  // token, cache-resident, is needed first), then every row of the tile --
+  // one ring round (the launch sizes it so), all of it in flight while the
+  // token is quantized -- then the first output row's scale
+  // a class kernel's k is 128 GR: GR / 2 values per thread
+  static_assert(!XQ || (GR % 2 == 0 && GR / 2 <= kActRegs), "x of the class fits the quantizing threads");
+  static_assert(!XQ || NR == kRing, "single calls: one group per lane");
+  uint32_t xqv[XQ ? GR / 2 : 1];
+  if constexpr (XQ) xq_issue<GR / 2, XQ>(d, xqv);
 #pragma unroll
   for (int b = 0; b + 1 < NR; ++b) fetch(ring[b], static_cast<uint32_t>(r0 + b * RPI) * kRowBytes);
-  // XQ: the token's loads are issued before the tables are built, and
-  // quantized after them
-  float xqv[XQ ? kActRegs : 1];
-  if constexpr (XQ) xq_issue(d, xq.dt, xqv);
+  if constexpr (XQ) {
+    fetch(ring[NR - 1], static_cast<uint32_t>(r0 + (NR - 1) * RPI) * kRowBytes);
+    // two half-word loads on either path (fp16: the element twice; fp32:
+    // its halves): a fixed count keeps the compiler's waits exact
+    const int sr = min(row_begin + static_cast<int>(threadIdx.x), last);
+    const bool f16 = d.flags & kFlagScaleF16;
+    const SHERRY_GLOBAL uint16_t* sp = gmem(static_cast<const uint16_t*>(d.w_scales));
+    // (combined in the epilogue: an operation on them here would wait for them)
+    xq.swb->x = sp[f16 ? sr : 2 * sr];
+    xq.swb->y = sp[f16 ? sr : 2 * sr + 1];
+  }
   if constexpr (XS) {
 #pragma unroll
     for (int tk = 0; tk < XM; ++tk)
@@ -260,9 +287,9 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
         if (c < nchunks) xs[tk * kXsChunks + c + c / 8] = xv[tk * kXsPerThread + j];
       }
   }
-  init_tables<Fmt>(tab32, tab);  // its barriers also publish the staged x
+  init_tables<Fmt, !(XQ && kXqSingles)>(tab32, tab);  // its barriers also publish the staged x
   if constexpr (XQ) {
-    xq_finish(d, xqv, xq.xl, xq.sx, xq.wmax);
+    xq_finish(d, xq.dt, xqv, xq.xl, xq.sx, xq.wmax);
     load_x();
   }
   if constexpr (XS) {
@@ -282,6 +309,11 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
         }
       }
   }
+  if constexpr (XQ) {
+#pragma unroll
+    for (int b = 0; b < NR; ++b) step(ring[b], r0 + b * RPI);
+    return;
+  }
   // Every round runs all NR steps; rows past the tile end are clamped loads
   // whose results are never stored (no branch inside the ring).  The last
   // round fetches only its own last row: nothing follows it.
@@ -300,12 +332,12 @@ __device__ __forceinline__ void gemv_i8_rows(const GemvDesc& d, int row_begin, i
 }
 
 // Any k % 128 == 0: 64 lanes per row, x read per group (not register-resident).
-template <class Fmt>
+template <class Fmt, int XQ = 0>
 __device__ __forceinline__ void gemv_i8_rows_generic(const GemvDesc& d, int row_begin, int row_end,
                                                      uint32_t* tab32, uint2* tab, int32_t* out,
                                                      XQuant xq = XQuant{}) {
   constexpr int NW = Fmt::kWords;
-  if (xq.xl) quantize_x_lds(d, xq.dt, xq.xl, xq.sx, xq.wmax);
+  if constexpr (XQ != 0) quantize_x_lds<XQ>(d, xq.dt, xq.xl, xq.sx, xq.wmax);
   init_tables<Fmt>(tab32, tab);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
@@ -524,7 +556,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_i8_kernel(GemvDesc d, int t
 // fp x quantized per token inside the workgroup (k <= kActMaxRegK), then
 // the int8 product; block 0 writes the scale to sx_out if given.
 static_assert(kGemvThreads == kActThreads, "the workgroup quantizes x with every thread");
-template <class Fmt, int L, int GPL, int GR>
+// XB: bytes per x value (4: fp32, 2: fp16 or bf16).
+template <class Fmt, int L, int GPL, int GR, int XB>
 __global__ __launch_bounds__(kGemvThreads) void gemv_i8_xq_kernel(GemvDesc d, int tile_rows, int xdt,
                                                                   float* sx_out) {
   __shared__ uint32_t tab32[32];
@@ -533,15 +566,29 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_i8_xq_kernel(GemvDesc d, in
   __shared__ __attribute__((aligned(16))) int8_t xl[kActMaxRegK];
   __shared__ float sx;
   __shared__ float wmax[kGemvThreads / kWave];
-  const XQuant xq{xdt, xl, &sx, wmax};
+  // class walks load the scale of this thread's first output row with the
+  // codes, so that the epilogue does not wait for it (raw bits: a
+  // conversion there would wait for the load at once)
+  uint2 swb = make_uint2(0u, 0u);
+  const XQuant xq{xdt, xl, &sx, wmax, &swb};
   const int row0 = blockIdx.x * tile_rows;
   const int row1 = min(row0 + tile_rows, d.n);
+  const bool s_f16 = d.flags & kFlagScaleF16;
   if constexpr (L == 0)
-    gemv_i8_rows_generic<Fmt>(d, row0, row1, tab32, tab, res, xq);
+    gemv_i8_rows_generic<Fmt, XB>(d, row0, row1, tab32, tab, res, xq);
   else
-    gemv_i8_rows<Fmt, L, GPL, GR, true>(d, row0, row1, tab32, tab, res, nullptr, xq);
+    gemv_i8_rows<Fmt, L, GPL, GR, XB>(d, row0, row1, tab32, tab, res, nullptr, xq);
   __syncthreads();
-  finalize_i8(d, row0, row1, res, true, sx);
+  const bool y_f16 = d.flags & kFlagYF16;
+  for (int i = threadIdx.x; i < row1 - row0; i += blockDim.x) {
+    const int r = row0 + i;
+    const float sw = L != 0 && i < kGemvThreads
+                         ? (s_f16 ? static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(swb.x)))
+                                  : __uint_as_float(swb.x | swb.y << 16))
+                         : load_scale(d.w_scales, r, s_f16);
+    if (d.acc) gmem(d.acc)[r] = res[i];
+    if (d.y) store_y(d.y, r, epilogue_i32(res[i], sw, sx, true), y_f16);
+  }
   if (sx_out && blockIdx.x == 0 && threadIdx.x == 0) *gmem(sx_out) = sx;
 }
 
@@ -949,10 +996,16 @@ __global__ __launch_bounds__(256) void tern2_encode_kernel(const int8_t* t, int6
 }  // namespace
 
 int tile_iters_for(int64_t n, int rpi) {
-  // Enough workgroups to cover the chip (>= 1024 when the matrix allows it);
-  // a tile never exceeds kMaxTileRows rows (its scales are staged in LDS).
+  // Up to 1024 workgroups, each at least four row iterations long (a
+  // workgroup's start-up -- tables, x -- costs about as much as a few
+  // iterations, and single calls are latency-bound: measured faster than
+  // one iteration per workgroup); a tile never exceeds kMaxTileRows rows
+  // (its scales are staged in LDS).
+  constexpr int64_t kMinIters = 4;
   const int64_t per = (n + rpi - 1) / rpi;
   int64_t iters = (per + 1023) / 1024;
+  if (iters < kMinIters) iters = kMinIters;
+  if (iters * rpi > n) iters = (n + rpi - 1) / rpi;  // no tile longer than the matrix
   if (iters < 1) iters = 1;
   if (iters * rpi > kMaxTileRows) iters = kMaxTileRows / rpi;
   return static_cast<int>(iters);
@@ -987,8 +1040,12 @@ void launch_i8_class(const GemvDesc& d, unsigned grid, int tile_rows, hipStream_
 
 template <class Fmt, int L, int GPL, int GR = GPL * L>
 void launch_xq(const GemvDesc& d, unsigned grid, int tile_rows, int xdt, float* sx_out, hipStream_t stream) {
-  hipLaunchKernelGGL((gemv_i8_xq_kernel<Fmt, L, GPL, GR>), dim3(grid), dim3(kGemvThreads), 0, stream, d, tile_rows, xdt,
-                     sx_out);
+  if (xdt == kActF32)
+    hipLaunchKernelGGL((gemv_i8_xq_kernel<Fmt, L, GPL, GR, 4>), dim3(grid), dim3(kGemvThreads), 0, stream, d, tile_rows,
+                       xdt, sx_out);
+  else
+    hipLaunchKernelGGL((gemv_i8_xq_kernel<Fmt, L, GPL, GR, 2>), dim3(grid), dim3(kGemvThreads), 0, stream, d, tile_rows,
+                       xdt, sx_out);
 }
 
 template <class Fmt>
@@ -1037,8 +1094,10 @@ hipError_t launch_gemv(const GemvDesc& d, bool bf16_x, int32_t format, hipStream
 }
 
 hipError_t launch_gemv_xq(const GemvDesc& d, int xdt, float* sx_out, int32_t format, hipStream_t stream) {
+  // class kernels walk exactly one ring round per workgroup (kRing row
+  // iterations, all fetched at start-up); the generic walk takes any tile
   const int rpi = rows_per_iter(d.kclass);
-  const int tile_rows = rpi * tile_iters_for(d.n, rpi);
+  const int tile_rows = d.kclass == kGeneric ? rpi * tile_iters_for(d.n, rpi) : rpi * kRing;
   const unsigned grid = static_cast<unsigned>((d.n + tile_rows - 1) / tile_rows);
   if (format == kFmtTern2)
     launch_xq_class<Tern2>(d, grid, tile_rows, xdt, sx_out, stream);

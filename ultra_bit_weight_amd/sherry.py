@@ -320,6 +320,36 @@ def gemv_quant(codes, scales, x, out_dtype=torch.float16, want_acc=False, want_s
     return acc, y, sx
 
 
+class PreparedGemvQuant:
+    """gemv_quant with its arguments checked and marshalled once, for loops
+    that run the same product over and over (a decode step): each call is
+    then one foreign call.  The tensors are held, and read at their current
+    contents on every call; reallocating them (a new tensor under the same
+    name) is not seen.  call(stream) launches on `stream` (a HIP stream
+    handle) or, when None, on torch's current stream (which a graph capture
+    replaces with its own)."""
+
+    def __init__(self, codes, scales, x, out_dtype=torch.float16, want_acc=False, want_scale=False, out=None):
+        _need(x, "x", dim=1, dtypes=(torch.float32, torch.float16, torch.bfloat16))
+        n, k = _check_gemv_args("sherry", codes, scales, x, None, None, out)
+        self.y = out if out is not None else (torch.empty(n, dtype=out_dtype, device=x.device) if out_dtype else None)
+        self.acc = torch.empty(n, dtype=torch.int32, device=x.device) if want_acc else None
+        self.scale = torch.empty(1, dtype=torch.float32, device=x.device) if want_scale else None
+        if self.y is None and self.acc is None:
+            raise ValueError("nothing to compute: neither y nor acc")
+        self._keep = (codes, scales, x)
+        self._f = load().sherry_gemv_quant
+        self._args = (codes.data_ptr(), scales.data_ptr(), _DT[scales.dtype], n, k, x.data_ptr(), _DT[x.dtype],
+                      _ptr(self.scale), _ptr(self.acc), _ptr(self.y),
+                      _DT[self.y.dtype] if self.y is not None else F32)
+
+    def __call__(self, stream=None):
+        status = self._f(*self._args, _stream() if stream is None else stream)
+        if status:
+            _check("sherry_gemv_quant", status)
+        return self.y
+
+
 _FMT = {"sherry_gemv": "sherry", "tern2_gemv": "tern2", "tern3_gemv": "tern3", "sherry_gemm": "sherry",
         "tern2_gemm": "tern2"}
 
