@@ -34,7 +34,8 @@
  * Conventions for every entry point:
  *   - Buffers are DEVICE pointers owned by the caller (except where a
  *     parameter says HOST).  The library allocates no device memory and keeps
- *     no per-call state; calls are thread-safe.
+ *     no per-call state (its one setting, sherry_set_prefill_kernel, is
+ *     process-wide); calls are thread-safe.
  *   - All argument checks run on the host before any HIP call.  On an error
  *     the call returns a status and enqueues nothing.
  *   - Work is enqueued on `stream` (asynchronous, no implicit sync).  Errors
@@ -253,6 +254,22 @@ sherry_status sherry_gemm_plan(const sherry_gemm_problem* probs /* HOST */, int3
  * and every buffer named by the plan must stay alive until the kernel
  * completes. */
 sherry_status sherry_gemm_grouped(const void* plan_host, const void* plan_dev, hipStream_t stream);
+
+/* Kernel of the int8 products for many tokens on 3:4 codes (sherry_gemm and
+ * grouped plans that take the 256 x 192 tiles):
+ *   SHERRY_PREFILL_TILED (default): waves expand the codes they multiply,
+ *     straight from a staged copy in LDS into matrix-core operands;
+ *   SHERRY_PREFILL_DECODE_ONCE: each group of a tile's codes is decoded once
+ *     per workgroup into an int8 weight tile in LDS that the waves multiply
+ *     (Sherry Abstract: 3:4 blocks of four weights in five bits), for k a
+ *     multiple of 1024 (other k keep the tiled kernel).
+ * Both give identical results.  The setting is process-wide and applies to
+ * launches issued after the call.  Errors: SHERRY_EINVAL for another kind. */
+typedef enum sherry_prefill_kernel {
+  SHERRY_PREFILL_TILED = 0,
+  SHERRY_PREFILL_DECODE_ONCE = 1
+} sherry_prefill_kernel;
+sherry_status sherry_set_prefill_kernel(sherry_prefill_kernel kind);
 
 /* ---- 2-bit dense-ternary comparator (Sherry Abstract and Figure 2: the
  * 2-bit aligned packing that keeps alignment by wasting bits) ----

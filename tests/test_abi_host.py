@@ -56,6 +56,15 @@ def test_version_and_status_strings(lib):
     assert lib.sherry_status_str(99).decode() == "SHERRY_UNKNOWN_STATUS"
 
 
+def test_set_prefill_kernel(lib):
+    """The one process-wide setting: both kinds accepted (and left at the
+    default), anything else EINVAL; no device needed."""
+    assert lib.sherry_set_prefill_kernel(1) == 0
+    assert lib.sherry_set_prefill_kernel(0) == 0
+    for bad in (2, -1, 99):
+        assert lib.sherry_set_prefill_kernel(bad) == 1
+
+
 def test_packed_bytes(lib):
     assert lib.sherry_packed_bytes(256, 1024) == 256 * 1024 * 5 // 32
     assert lib.sherry_packed_bytes(2048, 8192) == 2048 * 8192 * 5 // 32

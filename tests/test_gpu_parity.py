@@ -416,11 +416,68 @@ def test_gemm_tiled_extreme_accumulators(gpu_lib):
     assert np.array_equal(acc.cpu().numpy(), ref_acc)
 
 
+@pytest.fixture(params=["tiled", "decode_once"])
+def prefill_kernel(request, gpu_lib):
+    """Each prefill test runs with both kernels of the large tiles; the
+    default is restored afterwards."""
+    kind = gpu_lib.PREFILL_DECODE_ONCE if request.param == "decode_once" else gpu_lib.PREFILL_TILED
+    gpu_lib.set_prefill_kernel(kind)
+    yield request.param
+    gpu_lib.set_prefill_kernel(gpu_lib.PREFILL_TILED)
+
+
+@pytest.mark.parametrize("n,m,k", [(4133, 2930, 1024), (4101, 2900, 2048), (3100, 4000, 3072), (2900, 4100, 8192),
+                                   (8193, 1537, 384), (4000, 3100, 1152)])
+def test_gemm_large_tiles_every_output(gpu_lib, prefill_kernel, n, m, k):
+    """Shapes that take the large (256 x 192) tiles, every output against the
+    oracle, with either kernel: ragged rows and tokens; k a multiple of 1024
+    (the decode-once kernel takes these: one, two, three and eight runs of
+    eight groups) and other k (always the general tiled kernel; odd group
+    counts: unaligned row starts)."""
+    say(f"gemm large tiles {prefill_kernel} n={n} m={m} k={k}")
+    g = synth.rng(n + 3 * m + 7 * k)
+    words = synth.random_words(n * (k // 128) * 5, g)
+    sw = synth.row_scales(n, g, np.float16)
+    xq, sx, _ = synth.act_absmax_int8(m, k, g)
+    ref_acc, ref_y = sherry_ref.gemm_i8(words, sw, n, k, xq, sx, np.float16)
+    acc, y = gpu_lib.gemm(words_dev(words), dev(sw), dev(xq), dev(sx), torch.float16, want_acc=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), ref_acc)
+    assert np.array_equal(y.cpu().numpy().view(np.uint16), ref_y.view(np.uint16))
+
+
+@pytest.mark.parametrize("ks", [(1024, 2048, 1024), (640, 256, 1408)])
+def test_grouped_gemm_large_tiles_every_output(gpu_lib, prefill_kernel, ks):
+    """A grouped launch with large tiles over three ragged problems (fp32
+    scales and outputs, rows of x with a stride): every output.  Group
+    counts all multiples of eight (the decode-once kernel) or not (the
+    general tiled kernel)."""
+    say(f"grouped gemm large tiles {prefill_kernel} k={ks}")
+    g = synth.rng(4242 + ks[0])
+    m = 1300
+    probs, refs = [], []
+    for n, k, pad in zip((3000, 5001, 1030), ks, (0, 48, 16)):
+        words = synth.random_words(n * (k // 128) * 5, g)
+        sw = synth.row_scales(n, g, np.float32)
+        big = synth.x_int8_uniform((m, k + pad), g)
+        sx = (g.uniform(0.5, 2.0, m)).astype(np.float32)
+        refs.append(sherry_ref.gemm_i8(words, sw, n, k, big[:, :k], sx, np.float32))
+        probs.append(dict(codes=words_dev(words), scales=dev(sw), x=dev(big)[:, :k], x_scales=dev(sx),
+                          acc=torch.empty(m, n, dtype=torch.int32, device=DEV),
+                          y=torch.empty(m, n, dtype=torch.float32, device=DEV)))
+    grouped = gpu_lib.GroupedGemm(probs)
+    grouped()
+    torch.cuda.synchronize()
+    for p, (ra, ry) in zip(probs, refs):
+        assert np.array_equal(p["acc"].cpu().numpy(), ra)
+        assert np.array_equal(p["y"].cpu().numpy().view(np.uint32), ry.view(np.uint32))
+
+
 @pytest.mark.parametrize("name,n,k", [("q", 2048, 2048), ("up", 8192, 2048), ("down", 2048, 8192)])
-def test_gemm_prefill_full_size_sampled(gpu_lib, name, n, k):
+def test_gemm_prefill_full_size_sampled(gpu_lib, prefill_kernel, name, n, k):
     """LLaMA-3.2-1B prefill at 2048 tokens, the launch the benchmark times;
     64 sampled weight rows checked against every token."""
-    say(f"gemm prefill {name} {n}x{k} m=2048")
+    say(f"gemm prefill {prefill_kernel} {name} {n}x{k} m=2048")
     g = synth.rng({"q": 77, "up": 78, "down": 79}[name])
     m = 2048
     words = synth.random_words(n * (k // 128) * 5, g)
@@ -559,11 +616,11 @@ def test_grouped_gemm_few_tokens_layer(gpu_lib, m):
 
 
 @pytest.mark.parametrize("tern2", [False, True])
-def test_grouped_gemm_prefill_layer_sampled(gpu_lib, tern2):
+def test_grouped_gemm_prefill_layer_sampled(gpu_lib, prefill_kernel, tern2):
     """The seven matrices of a LLaMA-3.2-1B layer at 2048 tokens in one launch
     (256 x 256 tiles, the benchmark's launch); 48 sampled rows of every
     matrix checked against every token."""
-    say(f"grouped gemm prefill layer tern2={tern2}")
+    say(f"grouped gemm prefill layer {prefill_kernel} tern2={tern2}")
     g = synth.rng(616 + tern2)
     m = 2048
     xs = {}

@@ -297,6 +297,9 @@ sherry_status gemm_plan_impl(int32_t format, const sherry_gemm_problem* probs, i
   h.format = format;
   h.bytes = need;
   h.reserved[0] = static_cast<uint64_t>(tiling.kind);
+  bool fits = true;
+  for (int32_t i = 0; i < count; ++i) fits = fits && prefill_fits(probs[i].k);
+  h.reserved[1] = fits ? 1u : 0u;
   std::memcpy(out, &h, sizeof(h));
   std::memcpy(out + sizeof(PlanHeader), descs.data(), sizeof(GemmDesc) * descs.size());
   GemmTile* tiles = reinterpret_cast<GemmTile*>(out + sizeof(PlanHeader) + sizeof(GemmDesc) * descs.size());
@@ -416,6 +419,13 @@ sherry_status pack_impl(const void* w, dt_t w_dt, int64_t n, int64_t k, int64_t 
 extern "C" {
 
 const char* sherry_version(void) { return "0.1.0"; }
+
+sherry_status sherry_set_prefill_kernel(sherry_prefill_kernel kind) {
+  const dt_t v = raw(kind);
+  if (v != SHERRY_PREFILL_TILED && v != SHERRY_PREFILL_DECODE_ONCE) return SHERRY_EINVAL;
+  set_prefill_decode_once(v == SHERRY_PREFILL_DECODE_ONCE);
+  return SHERRY_OK;
+}
 
 const char* sherry_status_str(sherry_status s) {
   switch (raw(s)) {

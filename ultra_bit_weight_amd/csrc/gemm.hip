@@ -12,17 +12,20 @@
 // MFMA from group 4w + q of the workgroup's wave w.  Each wave owns one
 // 512-wide slice of k and keeps its tokens' x for that slice in registers
 // (x-stationary); the waves' 16x16 partial tiles are summed through LDS.
+#include <type_traits>
+
 #include "formats.h"
+#include "gemm_epi.h"
 #include "launch.h"
 
 namespace sherry {
 namespace {
 
-
 constexpr int kMaxKRanges = 16;  // waves per workgroup (k <= 8192 stays x-stationary)
-// Steps of x and code words the tiled kernel keeps in flight (LDS ring depth).
+// Steps of x and code words the tiled kernel keeps in flight (LDS ring depth;
+// 3 measured faster than 4 on the 1B layer at M = 2048).
 #ifndef SHERRY_TILE_DEPTH
-#define SHERRY_TILE_DEPTH 4
+#define SHERRY_TILE_DEPTH 3
 #endif
 constexpr int kTileDepth = SHERRY_TILE_DEPTH;
 static_assert(kTileDepth >= 2 && kTileDepth <= 4, "tile pipeline depth");
@@ -375,62 +378,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int til
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no copy may outlive the workgroup
 
-  // acc[t][u][e] of lane l is Y[token 16 u + l % 16][row 16 t + 4 (l / 16) + e]
-  // of the wave's sub-tile.  Four consecutive rows of one token are stored
-  // together where the layout allows it.
-  const bool s_f16 = d.flags & kFlagScaleF16;
-  const bool y_f16 = d.flags & kFlagYF16;
-  const bool has_sx = d.x_scales != nullptr;
-  const bool vec_acc = d.acc && (d.n % 4 == 0) && ((reinterpret_cast<uintptr_t>(d.acc) & 15) == 0);
-  const bool vec_y = d.y && (d.ldy % 4 == 0) && ((reinterpret_cast<uintptr_t>(d.y) & 15) == 0);
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int r0 = n0 + 64 * wn + 16 * t + 4 * q;
-    if (r0 >= d.n) continue;
-    const bool full = r0 + 3 < d.n;
-    float sw[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sw[e] = load_scale(d.w_scales, min(r0 + e, lastn), s_f16);
-#pragma unroll
-    for (int u = 0; u < UT; ++u) {
-      const int m = m0 + 16 * UT * wm + 16 * u + i;
-      if (m >= d.m) continue;
-      const float sx = has_sx ? gmem(d.x_scales)[m] : 1.0f;
-      const v4i v = acc[t][u];
-      if (d.acc) {
-        const int64_t o = static_cast<int64_t>(m) * d.n + r0;
-        if (vec_acc && full) {
-          *gmem(reinterpret_cast<v4i*>(d.acc + o)) = v;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (r0 + e < d.n) gmem(d.acc)[o + e] = v[e];
-        }
-      }
-      if (d.y) {
-        const int64_t o = static_cast<int64_t>(m) * d.ldy + r0;
-        float f[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) f[e] = epilogue_i32(v[e], sw[e], sx, has_sx);
-        if (vec_y && full) {
-          if (y_f16) {
-            typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-            const h4 hv = {static_cast<_Float16>(f[0]), static_cast<_Float16>(f[1]), static_cast<_Float16>(f[2]),
-                           static_cast<_Float16>(f[3])};
-            *gmem(reinterpret_cast<h4*>(static_cast<_Float16*>(d.y) + o)) = hv;
-          } else {
-            typedef float f4 __attribute__((ext_vector_type(4)));
-            const f4 fv = {f[0], f[1], f[2], f[3]};
-            *gmem(reinterpret_cast<f4*>(static_cast<float*>(d.y) + o)) = fv;
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (r0 + e < d.n) store_y(d.y, o + e, f[e], y_f16);
-        }
-      }
-    }
-  }
+  tile_store<UT>(d, acc, n0 + 64 * wn, m0 + 16 * UT * wm, i, q);
 }
 
 template <class Fmt, class C>
@@ -759,6 +707,8 @@ hipError_t launch_tile(const GemmDesc& d, hipStream_t stream) {
   const int64_t large = ((d.n + TileLarge::kRows - 1) / TileLarge::kRows) *
                         ((d.m + TileLarge::kTok - 1) / TileLarge::kTok);
   if (large >= kLargeTileMinGroups) {
+    if (std::is_same<Fmt, Sherry3of4>::value && prefill_decode_once() && prefill_fits(d.k))
+      return launch_gemm_prefill(d, stream);
     const dim3 grid((d.n + TileLarge::kRows - 1) / TileLarge::kRows, (d.m + TileLarge::kTok - 1) / TileLarge::kTok);
     hipLaunchKernelGGL((gemm_tile_kernel<Fmt, TileLarge>), grid, dim3(TileLarge::kThreads), 0, stream, d);
   } else {
@@ -808,6 +758,8 @@ hipError_t launch_gemm_grouped(const PlanHeader* h, const void* dev, hipStream_t
     else
       hipLaunchKernelGGL((gemm_few_grouped_kernel<Sherry3of4>), grid, dim3(kFewWaves * kWave), 0, stream, plan);
   } else if (tiling == kGemmTilingLarge) {
+    if (!t2 && prefill_decode_once() && h->reserved[1] != 0)
+      return launch_gemm_prefill_grouped(plan, h->n_tiles, stream);
     if (t2)
       hipLaunchKernelGGL((gemm_tile_grouped_kernel<Tern2, TileLarge>), grid, dim3(TileLarge::kThreads), 0, stream,
                          plan);

@@ -80,7 +80,8 @@ struct PlanHeader {
   int32_t format;
   uint64_t bytes;
   uint64_t reserved[3];  // GEMV plans: reserved[0] nonzero if some problem has k = 3072, reserved[1] nonzero
-                         // for bf16 x on the matrix cores; GEMM plans: reserved[0] = the tiling
+                         // for bf16 x on the matrix cores; GEMM plans: reserved[0] = the tiling,
+                         // reserved[1] nonzero if every problem's k suits the decode-once prefill kernel
 };
 static_assert(sizeof(PlanHeader) == 64, "plan header layout");
 constexpr uint32_t kPlanMagic = 0x53485950u;  // "PYHS"
@@ -205,6 +206,18 @@ __host__ __device__ constexpr int bf_few_slices(int groups) {
   return s;
 }
 hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t stream);
+// Many tokens on Sherry codes with the large tiling (kGemmLargeRows x
+// kGemmLargeTok): the decode-once kernel (each group's codes decoded once per
+// workgroup into an int8 A tile in LDS) when selected, else the general tiled
+// kernel (measured faster on the 1B layer at 2048 tokens).
+void set_prefill_decode_once(bool on);
+bool prefill_decode_once();
+// The decode-once kernel steps through k in unrolled runs of this many groups
+// (two code stages); other k take the general tiled kernel.
+constexpr int kPrefillGroupMultiple = 8;
+inline bool prefill_fits(int64_t k) { return (k / kGroupWeights) % kPrefillGroupMultiple == 0; }
+hipError_t launch_gemm_prefill(const GemmDesc& d, hipStream_t stream);
+hipError_t launch_gemm_prefill_grouped(const char* plan, int32_t n_tiles, hipStream_t stream);
 hipError_t launch_gemm_bf16_grouped(const char* plan, int32_t n_tiles, hipStream_t stream);
 // Activation quantization: input element types; the GEMV that quantizes its
 // own x holds it in LDS, k <= kActMaxK.

@@ -116,6 +116,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         f.argtypes = [ctypes.POINTER(GemmProblem), i32, i, i, i, vp, sz]
     lib.sherry_gemm_grouped.restype = i
     lib.sherry_gemm_grouped.argtypes = [vp, vp, vp]
+    lib.sherry_set_prefill_kernel.restype = i
+    lib.sherry_set_prefill_kernel.argtypes = [i]
     _lib = lib
     return lib
 
@@ -213,6 +215,16 @@ def _check_gemm_args(fmt, codes, scales, x, x_scales, acc, y):
     if len({t.device for t in (codes, scales, x, x_scales, acc, y) if t is not None}) > 1:
         raise ValueError("tensors are on different devices")
     return m, n, k
+
+
+PREFILL_TILED, PREFILL_DECODE_ONCE = 0, 1
+
+
+def set_prefill_kernel(kind: int) -> None:
+    """Process-wide choice of the many-token kernel on 3:4 codes
+    (sherry_set_prefill_kernel): PREFILL_TILED (default) or
+    PREFILL_DECODE_ONCE."""
+    _check("sherry_set_prefill_kernel", load().sherry_set_prefill_kernel(kind))
 
 
 def packed_bytes(n: int, k: int) -> int:
