@@ -372,15 +372,33 @@ def peak_probes(torch, sherry):
     del buf
     blocks, iters = 1024, 8192
     t = {}
+    ticks = torch.zeros(blocks, 4, dtype=torch.int64, device=dev)
+    clock = {}
     for name, mode in (("mfma", sherry.PROBE_MFMA), ("dot4", sherry.PROBE_DOT4), ("same_wave", sherry.PROBE_SAME_WAVE),
-                       ("alt_waves", sherry.PROBE_ALT_WAVES)):
+                       ("alt_waves", sherry.PROBE_ALT_WAVES), ("mfma32", sherry.PROBE_MFMA32)):
         mean_ms, _ = time_launches(torch, lambda: sherry.probe_rates(mode, iters, blocks, sink), 10, 2, settle_ms=20)
         t[name] = mean_ms
+        if name in ("mfma", "dot4", "mfma32"):  # one more launch, recording the shader clock (s_memtime / 100 MHz)
+            sherry.probe_clock(mode, iters, blocks, sink, ticks)
+            torch.cuda.synchronize()
+            tk = ticks.cpu().double()
+            ghz = ((tk[:, 1] - tk[:, 0]) / (tk[:, 3] - tk[:, 2]) * 0.1).median().item()
+            clock[name] = round(ghz, 3)
     waves = 4 * blocks * iters
     out["mfma_i8_TOPS"] = round(waves * sherry.PROBE_MFMA_OPS / (t["mfma"] * 1e-3) / 1e12, 1)
+    out["mfma32_i8_TOPS"] = round(waves * sherry.PROBE_MFMA_OPS / (t["mfma32"] * 1e-3) / 1e12, 1)
     out["dot4_i8_TOPS"] = round(waves * sherry.PROBE_DOT4_OPS / (t["dot4"] * 1e-3) / 1e12, 1)
+    # the shader clock while each probe ran, and the rate it implies per clock against the peak's 2.4 GHz: a rate
+    # below the spec at full per-clock efficiency is the clock, not the kernel
+    out["clock_GHz"] = clock
+    if clock.get("mfma"):
+        out["mfma_i8_TOPS_at_2p4GHz"] = round(out["mfma_i8_TOPS"] * 2.4 / clock["mfma"], 1)
+    if clock.get("mfma32"):
+        out["mfma32_i8_TOPS_at_2p4GHz"] = round(out["mfma32_i8_TOPS"] * 2.4 / clock["mfma32"], 1)
+    if clock.get("dot4"):
+        out["dot4_i8_TOPS_at_2p4GHz"] = round(out["dot4_i8_TOPS"] * 2.4 / clock["dot4"], 1)
     out["ms"] = {k: round(v, 4) for k, v in t.items()}
-    out["overlap_same_wave"] = round(t["same_wave"] / (t["mfma"] + t["dot4"]), 3)
+    out["overlap_same_wave"] = round(t["same_wave"] / (t["mfma"] + t["dot4"]), 3)  # 16 x 16 x 64 products
     out["overlap_alt_waves"] = round(2 * t["alt_waves"] / (t["mfma"] + t["dot4"]), 3)
     return out
 

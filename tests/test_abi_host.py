@@ -463,12 +463,18 @@ def test_probe_validation(lib):
     assert rd(A, 1000, A, None) == ESHAPE
     assert rd(A + 4, 1024, A, None) == EALIGN
     assert rd(A, 1024, A, None) == EDEVICE
-    assert rt(4, 10, 10, A, None) == EINVAL
+    assert rt(5, 10, 10, A, None) == EINVAL
     assert rt(0, 0, 10, A, None) == EINVAL
     assert rt(0, 10, 0, A, None) == EINVAL
     assert rt(0, 10, 10, None, None) == EINVAL
     assert rt(0, 10, 10, A + 2, None) == EALIGN
     assert rt(0, 10, 10, A, None) == EDEVICE
+    rc = raw.sherry_probe_clock
+    rc.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert rc(0, 10, 10, A, None, None) == EINVAL
+    assert rc(5, 10, 10, A, A, None) == EINVAL
+    assert rc(0, 10, 10, A, A + 4, None) == EALIGN
+    assert rc(0, 10, 10, A, A, None) == EDEVICE
 
 
 # ------------------------------------------------- binding size checks ---

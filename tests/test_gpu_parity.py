@@ -1044,7 +1044,7 @@ def test_probes_and_bench_line(gpu_lib):
     sink = torch.zeros(256, dtype=torch.int32, device=DEV)
     buf = torch.ones(1 << 26, dtype=torch.int32, device=DEV)
     gpu_lib.probe_read(buf, sink)
-    for mode in range(4):
+    for mode in range(5):
         gpu_lib.probe_rates(mode, 64, 256, sink)
     torch.cuda.synchronize()
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -1053,7 +1053,7 @@ def test_probes_and_bench_line(gpu_lib):
     assert r.returncode == 0, r.stderr[-2000:]
     pk = json.loads(r.stdout.strip().splitlines()[-1])
     assert 0.5 < pk["read_1GiB_TBps"] < 8.0
-    assert 10 < pk["mfma_i8_TOPS"] < 5000
+    assert 10 < pk["mfma_i8_TOPS"] < 5000 and 10 < pk["mfma32_i8_TOPS"] < 5000
     assert 1 < pk["dot4_i8_TOPS"] < 2 * 314.6  # 314.6: 1024 SIMDs x 64 lanes x 8 ops / 4 cycles x 2.4 GHz
     say("bench line")
     r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--steps", "5", "--warmup", "2", "--replicas",

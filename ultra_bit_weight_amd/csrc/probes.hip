@@ -8,6 +8,8 @@
 namespace sherry {
 namespace {
 
+typedef int v16i __attribute__((ext_vector_type(16)));
+
 constexpr int kProbeThreads = 256;
 constexpr uint32_t kNever = 0x9E3779B9u;  // a result no probe produces in practice: its store keeps the work
 constexpr int kReadUnroll = 4;            // 16-byte loads in flight per thread
@@ -38,9 +40,18 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4_t
 }
 
 // Per iteration and wave: 4 independent v_mfma_i32_16x16x64_i8 (4 x 32768
-// int8 ops) and/or 16 independent v_dot4_i32_i8 (16 x 512 ops).
+// int8 ops) and/or 16 independent v_dot4_i32_i8 (16 x 512 ops); in the
+// MFMA32 mode 2 independent v_mfma_i32_32x32x32_i8 (the same 2 x 65536 ops).
+// With ticks: thread 0 of workgroup b records the shader-clock counter
+// (s_memtime) and the constant 100 MHz counter (s_memrealtime) before and
+// after its wave's loop in ticks[4 b .. 4 b + 3].
 template <int MODE>
-__global__ __launch_bounds__(kProbeThreads) void probe_rate_kernel(int iters, uint32_t* sink) {
+__global__ __launch_bounds__(kProbeThreads) void probe_rate_kernel(int iters, uint32_t* sink, uint64_t* ticks) {
+  uint64_t t0 = 0, r0 = 0;
+  if (ticks && threadIdx.x == 0) {
+    t0 = __builtin_amdgcn_s_memtime();
+    r0 = __builtin_amdgcn_s_memrealtime();
+  }
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const bool alt = MODE == SHERRY_PROBE_ALT_WAVES;
@@ -50,12 +61,17 @@ __global__ __launch_bounds__(kProbeThreads) void probe_rate_kernel(int iters, ui
   v4i b = {lane ^ 5, lane ^ 9, lane ^ 17, lane ^ 33};
   asm volatile("" : "+v"(a), "+v"(b));
   v4i c[4];
+  v16i c32[2] = {};
   int d[16];
 #pragma unroll
   for (int r = 0; r < 4; ++r) c[r] = v4i{0, 0, 0, 0};
 #pragma unroll
   for (int j = 0; j < 16; ++j) d[j] = j;
   for (int it = 0; it < iters; ++it) {
+    if (MODE == SHERRY_PROBE_MFMA32) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) c32[r] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c32[r], 0, 0, 0);
+    }
     if (do_mfma) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) c[r] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c[r], 0, 0, 0);
@@ -70,7 +86,48 @@ __global__ __launch_bounds__(kProbeThreads) void probe_rate_kernel(int iters, ui
   for (int r = 0; r < 4; ++r) h ^= static_cast<uint32_t>(c[r][0] ^ c[r][1] ^ c[r][2] ^ c[r][3]);
 #pragma unroll
   for (int j = 0; j < 16; ++j) h ^= static_cast<uint32_t>(d[j]);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) h ^= static_cast<uint32_t>(c32[r][0] ^ c32[r][15]);
   if (h == kNever) gmem(sink)[threadIdx.x] = h;
+  if (ticks && threadIdx.x == 0) {
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    SHERRY_GLOBAL uint64_t* out = gmem(ticks) + 4 * static_cast<int64_t>(blockIdx.x);
+    out[0] = t0;
+    out[1] = t1;
+    out[2] = r0;
+    out[3] = r1;
+  }
+}
+
+sherry_status launch_rates(int32_t mode, int32_t iters, int32_t blocks, uint32_t* sink, uint64_t* ticks,
+                           hipStream_t stream) {
+  if (!sink) return SHERRY_EINVAL;
+  if (mode < SHERRY_PROBE_MFMA || mode > SHERRY_PROBE_MFMA32 || iters <= 0 || iters > (1 << 24) || blocks <= 0 ||
+      blocks > (1 << 20))
+    return SHERRY_EINVAL;
+  if (reinterpret_cast<uintptr_t>(sink) % 4 != 0 || reinterpret_cast<uintptr_t>(ticks) % 8 != 0) return SHERRY_EALIGN;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SHERRY_EDEVICE;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kProbeThreads);
+  switch (mode) {
+    case SHERRY_PROBE_MFMA:
+      hipLaunchKernelGGL(probe_rate_kernel<SHERRY_PROBE_MFMA>, grid, block, 0, stream, iters, sink, ticks);
+      break;
+    case SHERRY_PROBE_DOT4:
+      hipLaunchKernelGGL(probe_rate_kernel<SHERRY_PROBE_DOT4>, grid, block, 0, stream, iters, sink, ticks);
+      break;
+    case SHERRY_PROBE_SAME_WAVE:
+      hipLaunchKernelGGL(probe_rate_kernel<SHERRY_PROBE_SAME_WAVE>, grid, block, 0, stream, iters, sink, ticks);
+      break;
+    case SHERRY_PROBE_ALT_WAVES:
+      hipLaunchKernelGGL(probe_rate_kernel<SHERRY_PROBE_ALT_WAVES>, grid, block, 0, stream, iters, sink, ticks);
+      break;
+    default:
+      hipLaunchKernelGGL(probe_rate_kernel<SHERRY_PROBE_MFMA32>, grid, block, 0, stream, iters, sink, ticks);
+      break;
+  }
+  return hipGetLastError() == hipSuccess ? SHERRY_OK : SHERRY_ELAUNCH;
 }
 
 }  // namespace
@@ -98,29 +155,13 @@ sherry_status sherry_probe_read(const void* src, size_t bytes, uint32_t* sink, h
 }
 
 sherry_status sherry_probe_rates(int32_t mode, int32_t iters, int32_t blocks, uint32_t* sink, hipStream_t stream) {
-  if (!sink) return SHERRY_EINVAL;
-  if (mode < SHERRY_PROBE_MFMA || mode > SHERRY_PROBE_ALT_WAVES || iters <= 0 || iters > (1 << 24) || blocks <= 0 ||
-      blocks > (1 << 20))
-    return SHERRY_EINVAL;
-  if (reinterpret_cast<uintptr_t>(sink) % 4 != 0) return SHERRY_EALIGN;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return SHERRY_EDEVICE;
-  const dim3 grid(static_cast<unsigned>(blocks)), block(kProbeThreads);
-  switch (mode) {
-    case SHERRY_PROBE_MFMA:
-      hipLaunchKernelGGL(probe_rate_kernel<SHERRY_PROBE_MFMA>, grid, block, 0, stream, iters, sink);
-      break;
-    case SHERRY_PROBE_DOT4:
-      hipLaunchKernelGGL(probe_rate_kernel<SHERRY_PROBE_DOT4>, grid, block, 0, stream, iters, sink);
-      break;
-    case SHERRY_PROBE_SAME_WAVE:
-      hipLaunchKernelGGL(probe_rate_kernel<SHERRY_PROBE_SAME_WAVE>, grid, block, 0, stream, iters, sink);
-      break;
-    default:
-      hipLaunchKernelGGL(probe_rate_kernel<SHERRY_PROBE_ALT_WAVES>, grid, block, 0, stream, iters, sink);
-      break;
-  }
-  return hipGetLastError() == hipSuccess ? SHERRY_OK : SHERRY_ELAUNCH;
+  return launch_rates(mode, iters, blocks, sink, nullptr, stream);
+}
+
+sherry_status sherry_probe_clock(int32_t mode, int32_t iters, int32_t blocks, uint32_t* sink, uint64_t* ticks,
+                                 hipStream_t stream) {
+  if (!ticks) return SHERRY_EINVAL;
+  return launch_rates(mode, iters, blocks, sink, ticks, stream);
 }
 
 }  // extern "C"

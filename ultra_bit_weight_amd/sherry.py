@@ -30,7 +30,7 @@ EXPORTS = [
     "sherry_gemm_plan_bytes", "sherry_gemm_plan", "sherry_gemm_grouped",
     "tern2_packed_bytes", "tern2_pack", "tern2_encode", "tern2_gemv", "tern2_gemv_plan", "tern2_gemm", "tern2_gemm_plan",
     "tern3_packed_bytes", "tern3_encode", "tern3_gemv", "tern3_gemv_plan_bytes", "tern3_gemv_plan",
-    "sherry_probe_read", "sherry_probe_rates",
+    "sherry_probe_read", "sherry_probe_rates", "sherry_probe_clock", "sherry_set_prefill_kernel",
 ]
 
 
@@ -70,6 +70,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sherry_probe_read.argtypes = [vp, sz, vp, vp]
     lib.sherry_probe_rates.restype = i
     lib.sherry_probe_rates.argtypes = [i32, i32, i32, vp, vp]
+    lib.sherry_probe_clock.restype = i
+    lib.sherry_probe_clock.argtypes = [i32, i32, i32, vp, vp, vp]
     lib.sherry_version.restype = ctypes.c_char_p
     lib.sherry_status_str.restype = ctypes.c_char_p
     lib.sherry_status_str.argtypes = [i]
@@ -273,7 +275,7 @@ def tern2_pack(w: torch.Tensor, scale_dtype=torch.float16):
     return codes, scales
 
 
-PROBE_MFMA, PROBE_DOT4, PROBE_SAME_WAVE, PROBE_ALT_WAVES = 0, 1, 2, 3
+PROBE_MFMA, PROBE_DOT4, PROBE_SAME_WAVE, PROBE_ALT_WAVES, PROBE_MFMA32 = 0, 1, 2, 3, 4
 # int8 ops per wave and iteration of the rate probe: 4 matrix-core products
 # of 16 x 16 x 64, 16 v_dot4 over 64 lanes
 PROBE_MFMA_OPS, PROBE_DOT4_OPS = 4 * 2 * 16 * 16 * 64, 16 * 2 * 4 * 64
@@ -290,6 +292,15 @@ def probe_rates(mode: int, iters: int, blocks: int, sink: torch.Tensor):
     """Rate probe (sherry_probe_rates): `blocks` workgroups of 4 waves."""
     _dev(sink)
     _check("sherry_probe_rates", load().sherry_probe_rates(mode, iters, blocks, sink.data_ptr(), _stream()))
+
+
+def probe_clock(mode: int, iters: int, blocks: int, sink: torch.Tensor, ticks: torch.Tensor):
+    """Rate probe with the clock record (sherry_probe_clock); ticks: int64
+    [blocks, 4] on the GPU."""
+    _need(ticks, "ticks", numel=4 * blocks, dtypes=(torch.int64,))
+    _dev(sink, ticks)
+    _check("sherry_probe_clock", load().sherry_probe_clock(mode, iters, blocks, sink.data_ptr(), ticks.data_ptr(),
+                                                           _stream()))
 
 
 def decode(codes: torch.Tensor, n: int, k: int) -> torch.Tensor:
