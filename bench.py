@@ -475,11 +475,12 @@ def gemm_profile(torch, sherry, synth, probs, args):
         res[f"M{m}"] = {"us_per_launch": round(mean_ms * 1e3, 2), "layers": layers, "tiles": grouped.n_tiles,
                         "TOPS": round(ops / (mean_ms * 1e-3) / 1e12, 1),
                         "code_TBps": round(code_bytes / (mean_ms * 1e-3) / 1e12, 3)}
-        if m == 2048:  # the decode-once kernel on the same launch
-            sherry.set_prefill_kernel(sherry.PREFILL_DECODE_ONCE)
-            mean1, _ = time_launches(torch, grouped, steps, 3)
-            sherry.set_prefill_kernel(sherry.PREFILL_TILED)
-            res["M2048_decode_once"] = {"us_per_launch": round(mean1 * 1e3, 2),
+        if m == 2048:  # the other large-tile kernels on the same launch
+            for name, kind in (("decode_once", sherry.PREFILL_DECODE_ONCE), ("tiled32", sherry.PREFILL_TILED32)):
+                sherry.set_prefill_kernel(kind)
+                mean1, _ = time_launches(torch, grouped, steps, 3)
+                sherry.set_prefill_kernel(sherry.PREFILL_TILED)
+                res[f"M2048_{name}"] = {"us_per_launch": round(mean1 * 1e3, 2),
                                         "TOPS": round(ops / (mean1 * 1e-3) / 1e12, 1)}
         if m == 2048:  # the 2-bit comparator on the same ternary matrices, same launch shape
             g2 = [dict(q, codes=sherry.tern2_encode(sherry.decode(p["codes"], p["n"], p["k"])))
@@ -488,6 +489,11 @@ def gemm_profile(torch, sherry, synth, probs, args):
             mean2, _ = time_launches(torch, grouped2, steps, 3)
             res["M2048_tern2"] = {"us_per_launch": round(mean2 * 1e3, 2), "TOPS": round(ops / (mean2 * 1e-3) / 1e12, 1)}
             res["M2048_sherry_over_tern2"] = round(mean2 / mean_ms, 3)
+            sherry.set_prefill_kernel(sherry.PREFILL_TILED32)
+            mean3, _ = time_launches(torch, grouped2, steps, 3)
+            sherry.set_prefill_kernel(sherry.PREFILL_TILED)
+            res["M2048_tern2_tiled32"] = {"us_per_launch": round(mean3 * 1e3, 2),
+                                          "TOPS": round(ops / (mean3 * 1e-3) / 1e12, 1)}
             del g2, grouped2
         del gp, grouped
     print(json.dumps(res), flush=True)

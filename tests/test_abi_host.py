@@ -57,11 +57,12 @@ def test_version_and_status_strings(lib):
 
 
 def test_set_prefill_kernel(lib):
-    """The one process-wide setting: both kinds accepted (and left at the
-    default), anything else EINVAL; no device needed."""
+    """The one process-wide setting: the three kinds accepted (and left at
+    the default), anything else EINVAL; no device needed."""
     assert lib.sherry_set_prefill_kernel(1) == 0
+    assert lib.sherry_set_prefill_kernel(2) == 0
     assert lib.sherry_set_prefill_kernel(0) == 0
-    for bad in (2, -1, 99):
+    for bad in (3, -1, 99):
         assert lib.sherry_set_prefill_kernel(bad) == 1
 
 
@@ -372,8 +373,29 @@ def test_grouped_gemm_plan_on_host(lib):
     assert int.from_bytes(hdr[12:16], "little") == n_tiles
     assert int.from_bytes(hdr[40:48], "little") == 1  # 256 x 192 tiling
     t = tiles_of(base, len(layer), n_tiles)
-    assert t[:88] == [(6, a, b) for a in range(8) for b in range(11)]  # down (k = 8192) first
-    assert t[88] == (0, 0, 0) and t[-1] == (5, 31, 10)
+    # eight interleaved lists, one per XCD (workgroup w runs on XCD w % 8):
+    # XCD c takes share c of every problem's tiles (listed token tile by token
+    # tile), problems with the longest rows (down, k = 8192) first; shares of
+    # equal count, the remainders dealt to the XCDs in turn
+    assert sorted(t) == sorted((i, a, b) for i, (n, _, _) in enumerate(layer) for a in range(n // 256)
+                               for b in range(11)) and len(set(t)) == n_tiles
+    lists = [t[c::8] for c in range(8)]
+    assert [len(x) for x in lists] == [127, 127, 127, 127, 126, 126, 126, 126]  # 1012 = 8 * 126 + 4
+    nxt = 0
+    for i in (6, 0, 1, 2, 3, 4, 5):
+        tn = layer[i][0] // 256
+        seq = [(i, u % tn, u // tn) for u in range(11 * tn)]
+        q, r = divmod(len(seq), 8)
+        u = 0
+        for c in range(8):
+            share = q + (1 if (c - nxt) % 8 < r else 0)
+            assert [x for x in lists[c] if x[0] == i] == seq[u:u + share], (i, c)
+            u += share
+        nxt = (nxt + r) % 8
+    # the XCD lists hold the problems in order: down first
+    assert all([x[0] for x in lst] == sorted((x[0] for x in lst), key=(6, 0, 1, 2, 3, 4, 5).index)
+               for lst in lists)
+    assert t[0] == (6, 0, 0) and t[1] == (6, 3, 1) and t[-1][0] == 5
     assert lib.tern2_gemm_plan(arr, len(layer), F16, I8, F16, base, nbytes) == OK
     # a small set of problems: 128 x 128 tiles (ragged in rows and tokens)
     small = [(300, 1024, 200), (64, 128, 64)]
@@ -383,7 +405,8 @@ def test_grouped_gemm_plan_on_host(lib):
     assert nb2 == 64 + 80 * 2 + 16 * n2
     assert lib.sherry_gemm_plan(arr2, 2, F16, I8, F16, base, nb2) == OK
     assert int.from_bytes(ctypes.string_at(base + 40, 8), "little") == 0
-    assert tiles_of(base, 2, n2) == [(0, a, b) for a in range(3) for b in range(2)] + [(1, 0, 0)]
+    # fewer tiles than one round of XCD runs: the logical order
+    assert tiles_of(base, 2, n2) == [(0, a, b) for b in range(2) for a in range(3)] + [(1, 0, 0)]
     # validation: buffer too small, bad dtype, misaligned, bad shape, bad m
     assert lib.sherry_gemm_plan(arr2, 2, F16, I8, F16, base, nb2 - 8) == EINVAL
     assert lib.sherry_gemm_plan(arr2, 2, F16, BF16, F16, base, nb2) == EDTYPE

@@ -416,11 +416,12 @@ def test_gemm_tiled_extreme_accumulators(gpu_lib):
     assert np.array_equal(acc.cpu().numpy(), ref_acc)
 
 
-@pytest.fixture(params=["tiled", "decode_once"])
+@pytest.fixture(params=["tiled", "decode_once", "tiled32"])
 def prefill_kernel(request, gpu_lib):
-    """Each prefill test runs with both kernels of the large tiles; the
+    """Each prefill test runs with every kernel of the large tiles; the
     default is restored afterwards."""
-    kind = gpu_lib.PREFILL_DECODE_ONCE if request.param == "decode_once" else gpu_lib.PREFILL_TILED
+    kind = {"tiled": gpu_lib.PREFILL_TILED, "decode_once": gpu_lib.PREFILL_DECODE_ONCE,
+            "tiled32": gpu_lib.PREFILL_TILED32}[request.param]
     gpu_lib.set_prefill_kernel(kind)
     yield request.param
     gpu_lib.set_prefill_kernel(gpu_lib.PREFILL_TILED)
@@ -430,7 +431,7 @@ def prefill_kernel(request, gpu_lib):
                                    (8193, 1537, 384), (4000, 3100, 1152)])
 def test_gemm_large_tiles_every_output(gpu_lib, prefill_kernel, n, m, k):
     """Shapes that take the large (256 x 192) tiles, every output against the
-    oracle, with either kernel: ragged rows and tokens; k a multiple of 1024
+    oracle, with each kernel: ragged rows and tokens; k a multiple of 1024
     (the decode-once kernel takes these: one, two, three and eight runs of
     eight groups) and other k (always the general tiled kernel; odd group
     counts: unaligned row starts)."""
@@ -618,7 +619,7 @@ def test_grouped_gemm_few_tokens_layer(gpu_lib, m):
 @pytest.mark.parametrize("tern2", [False, True])
 def test_grouped_gemm_prefill_layer_sampled(gpu_lib, prefill_kernel, tern2):
     """The seven matrices of a LLaMA-3.2-1B layer at 2048 tokens in one launch
-    (256 x 256 tiles, the benchmark's launch); 48 sampled rows of every
+    (256 x 192 tiles, the benchmark's launch); 48 sampled rows of every
     matrix checked against every token."""
     say(f"grouped gemm prefill layer {prefill_kernel} tern2={tern2}")
     g = synth.rng(616 + tern2)

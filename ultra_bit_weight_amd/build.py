@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libsherry.so")
-SOURCES = ["abi.cpp", "pack.hip", "gemv.hip", "gemm.hip", "gemm_bf16.hip", "gemm_prefill.hip", "act.hip", "probes.hip"]
+SOURCES = ["abi.cpp", "pack.hip", "gemv.hip", "gemm.hip", "gemm_bf16.hip", "gemm_prefill.hip", "gemm_tile32.hip", "act.hip", "probes.hip"]
 ARCH = "gfx950"
 
 

@@ -268,6 +268,41 @@ size_t gemm_plan_bytes_impl(const sherry_gemm_problem* probs, int32_t count) {
   return sizeof(PlanHeader) + sizeof(GemmDesc) * static_cast<size_t>(count) + sizeof(GemmTile) * tiles;
 }
 
+// Tile order of the tiled kernels (many tokens).  The workgroups of a launch
+// go to the chip's eight XCDs in turn (workgroup w to XCD w mod 8), each XCD
+// with an L2 of its own, so the plan holds eight interleaved lists, one per
+// XCD.  Each problem's tiles, listed token tile by token tile (the row tiles
+// of one token tile together), are cut into eight contiguous shares of equal
+// count (the remainders of all problems dealt in turn, so that the lists
+// differ in length by at most one and only the first ones are longer), and
+// XCD c takes share c of every problem, longest rows first.  Every XCD then
+// does an equal part of each problem's work, and the workgroups one XCD
+// holds at once read few distinct x tiles, which its L2 serves.
+constexpr int kXcds = 8;
+bool xcd_order(const sherry_gemm_problem* probs, const std::vector<int32_t>& order, const GemmTiling& tiling,
+               GemmTile* tiles, int64_t n_tiles) {
+  std::vector<std::vector<GemmTile>> lists(kXcds);
+  int next = 0;  // XCD that takes the next remainder tile
+  for (const int32_t i : order) {
+    const int64_t rows = tiling.rows_of(probs[i]);
+    const int64_t tn = (probs[i].n + rows - 1) / rows, tm = (probs[i].m + tiling.tok - 1) / tiling.tok;
+    const int64_t n = tn * tm, q = n / kXcds, r = n % kXcds;
+    int64_t u = 0;
+    for (int c = 0; c < kXcds; ++c) {
+      const int64_t share = q + ((c - next + kXcds) % kXcds < r ? 1 : 0);
+      for (int64_t e = 0; e < share; ++e, ++u)
+        lists[static_cast<size_t>(c)].push_back(
+            GemmTile{i, static_cast<int32_t>(u % tn), static_cast<int32_t>(u / tn), 0});
+    }
+    next = static_cast<int>((next + r) % kXcds);
+  }
+  for (int c = 0; c < kXcds; ++c)
+    if (static_cast<int64_t>(lists[static_cast<size_t>(c)].size()) != (n_tiles - c + kXcds - 1) / kXcds) return false;
+  for (int64_t w = 0; w < n_tiles; ++w)
+    tiles[w] = lists[static_cast<size_t>(w % kXcds)][static_cast<size_t>(w / kXcds)];
+  return true;
+}
+
 sherry_status gemm_plan_impl(int32_t format, const sherry_gemm_problem* probs, int32_t count, dt_t s_dt,
                              dt_t x_dt, dt_t y_dt, void* plan, size_t plan_bytes) {
   if (!probs || count <= 0 || !plan) return SHERRY_EINVAL;
@@ -307,6 +342,9 @@ sherry_status gemm_plan_impl(int32_t format, const sherry_gemm_problem* probs, i
   std::vector<int32_t> order(static_cast<size_t>(count));
   for (int32_t i = 0; i < count; ++i) order[static_cast<size_t>(i)] = i;
   std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return probs[a].k > probs[b].k; });
+  if (tiling.kind == kGemmTilingLarge || tiling.kind == kGemmTilingSmall) {
+    return xcd_order(probs, order, tiling, tiles, h.n_tiles) ? SHERRY_OK : SHERRY_ESHAPE;
+  }
   int64_t t = 0;
   for (const int32_t i : order) {
     const int64_t rows = tiling.rows_of(probs[i]);
@@ -422,8 +460,11 @@ const char* sherry_version(void) { return "0.1.0"; }
 
 sherry_status sherry_set_prefill_kernel(sherry_prefill_kernel kind) {
   const dt_t v = raw(kind);
-  if (v != SHERRY_PREFILL_TILED && v != SHERRY_PREFILL_DECODE_ONCE) return SHERRY_EINVAL;
-  set_prefill_decode_once(v == SHERRY_PREFILL_DECODE_ONCE);
+  if (v != SHERRY_PREFILL_TILED && v != SHERRY_PREFILL_DECODE_ONCE && v != SHERRY_PREFILL_TILED32)
+    return SHERRY_EINVAL;
+  set_prefill_kind(v == SHERRY_PREFILL_DECODE_ONCE ? kPrefillDecodeOnce
+                   : v == SHERRY_PREFILL_TILED32   ? kPrefillTiled32
+                                                   : kPrefillTiled);
   return SHERRY_OK;
 }
 

@@ -90,6 +90,7 @@ __device__ __forceinline__ uint32_t code_offset(const uint32_t* w, int j) {
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));  // MFMA int8 operands / int32 accumulators
+typedef int v16i __attribute__((ext_vector_type(16)));  // 32 x 32 MFMA int32 accumulators
 
 // Pointers read from a grouped plan are generic to the compiler, which then
 // emits FLAT accesses; those also count against the LDS wait counter, so an
@@ -143,6 +144,16 @@ __device__ __forceinline__ void lds_copy4(const SHERRY_GLOBAL void* base, uint32
       :
       : "s"(lds), "v"(voff), "s"(base)
       : "memory", "m0");
+}
+// A pointer the caller knows to be the same in every lane, in scalar
+// registers (a descriptor read with vector loads is not known uniform to the
+// compiler; the copies above take their base from scalar registers).
+template <class T>
+__device__ __forceinline__ const SHERRY_GLOBAL T* uniform_ptr(const SHERRY_GLOBAL T* p) {
+  const uint64_t v = reinterpret_cast<uintptr_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const SHERRY_GLOBAL T*>(static_cast<uintptr_t>((static_cast<uint64_t>(hi) << 32) | lo));
 }
 template <class T>
 __device__ __forceinline__ uint32_t lds_addr(const T* p) {

@@ -129,6 +129,29 @@ struct Sherry3of4 {
     const uint32_t tail = *reinterpret_cast<const uint32_t*>(tails + lt + 4 * j);
     w[1] = q < 3 ? nxt : tail;
   }
+  // 32 x 32 tiles: in substep s (of four) lane half h of a row takes blocks
+  // 8 s + 4 h .. + 3 of a group (k bytes 32 s + 16 h .. + 16, x chunk
+  // 2 s + h).  window32 shifts the 160-bit group down by 20 h bits (a
+  // per-lane funnel-shift amount, no select between the halves), so those
+  // blocks sit at window bits 40 s .. 40 s + 19 for either half; frag32
+  // expands them with four table lookups.
+  static constexpr int kWin = 5;
+  __device__ __forceinline__ static int x_chunk32(int h, int s) { return 2 * s + h; }
+  __device__ __forceinline__ static void window32(uint32_t (&win)[kWin], const char* heads, const char* tails,
+                                                  uint32_t lh, uint32_t lt, int swz, int j, int h) {
+    const u32x4_t c = *reinterpret_cast<const u32x4_t*>(heads + lh + 16 * (j ^ swz));
+    const uint32_t tail = *reinterpret_cast<const uint32_t*>(tails + lt + 4 * j);
+    const uint32_t sh = 20u * static_cast<uint32_t>(h);
+    win[0] = __builtin_amdgcn_alignbit(c.y, c.x, sh);
+    win[1] = __builtin_amdgcn_alignbit(c.z, c.y, sh);
+    win[2] = __builtin_amdgcn_alignbit(c.w, c.z, sh);
+    win[3] = __builtin_amdgcn_alignbit(tail, c.w, sh);
+    win[4] = tail >> sh;
+  }
+  __device__ __forceinline__ static v4i frag32(const uint32_t (&win)[kWin], int s, const uint32_t* tab) {
+    return v4i{static_cast<int>(i8x4(win, 8 * s, tab)), static_cast<int>(i8x4(win, 8 * s + 1, tab)),
+               static_cast<int>(i8x4(win, 8 * s + 2, tab)), static_cast<int>(i8x4(win, 8 * s + 3, tab))};
+  }
 };
 
 struct Tern2 {
@@ -210,6 +233,22 @@ struct Tern2 {
         reinterpret_cast<const uint32_t*>(heads + lh + 16 * ((2 * j + (q >> 1)) ^ swz) + 8 * (q & 1));
     w[0] = c[0];
     w[1] = c[1];
+  }
+  // 32 x 32 tiles: lane half h takes words 4 h .. 4 h + 3 of a group (chunk
+  // 2 j + h of the stage); word 4 h + s holds k bytes 64 h + 16 s .. + 16
+  // (x chunk 4 h + s).
+  static constexpr int kWin = 4;
+  __device__ __forceinline__ static int x_chunk32(int h, int s) { return 4 * h + s; }
+  __device__ __forceinline__ static void window32(uint32_t (&win)[kWin], const char* heads, const char*, uint32_t lh,
+                                                  uint32_t, int swz, int j, int h) {
+    const u32x4_t c = *reinterpret_cast<const u32x4_t*>(heads + lh + 16 * ((2 * j + h) ^ swz));
+    win[0] = c.x;
+    win[1] = c.y;
+    win[2] = c.z;
+    win[3] = c.w;
+  }
+  __device__ __forceinline__ static v4i frag32(const uint32_t (&win)[kWin], int s, const uint32_t* tab) {
+    return frag(win, 0, s, tab);  // word s of the window
   }
 };
 

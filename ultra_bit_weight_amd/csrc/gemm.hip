@@ -15,20 +15,13 @@
 #include <type_traits>
 
 #include "formats.h"
-#include "gemm_epi.h"
+#include "gemm_tile.h"
 #include "launch.h"
 
 namespace sherry {
 namespace {
 
 constexpr int kMaxKRanges = 16;  // waves per workgroup (k <= 8192 stays x-stationary)
-// Steps of x and code words the tiled kernel keeps in flight (LDS ring depth;
-// 3 measured faster than 4 on the 1B layer at M = 2048).
-#ifndef SHERRY_TILE_DEPTH
-#define SHERRY_TILE_DEPTH 3
-#endif
-constexpr int kTileDepth = SHERRY_TILE_DEPTH;
-static_assert(kTileDepth >= 2 && kTileDepth <= 4, "tile pipeline depth");
 
 template <class Fmt, bool kStationary>
 __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmDesc d, int n_tiles) {
@@ -123,277 +116,6 @@ __global__ __launch_bounds__(1024) void gemm_small_kernel(GemmDesc d, int n_tile
     }
     buf ^= 1;
   }
-}
-
-// Tiled kernel for many tokens.  A workgroup of WR x WC waves computes a
-// (64 WR weight rows) x (16 UT WC tokens) tile of Y, stepping k by one
-// 128-weight group.  Wave w owns rows 64 (w % WR) .. + 64 and tokens
-// 16 UT (w / WR) .. + 16 UT as 4 x UT MFMA tiles.
-//   * Everything the loop reads from memory is copied by the memory system
-//     straight into LDS (global_load_lds, no staging registers):
-//       - the tokens' int8 tile of a step, D steps ahead, into a ring of D
-//         buffers.  Within a token's 128 bytes the 16-byte chunk c sits at
-//         position c ^ ((token >> 1) & 7), so the B-fragment reads of 16
-//         consecutive tokens hit 16 different bank groups;
-//       - the codes in stages of P groups, two stages ahead, into a ring of 3
-//         buffers: per row the P groups' head words (contiguous in the row,
-//         so four lanes read 64 contiguous bytes) and tail words.  Chunk c of
-//         a row sits at position c ^ ((row >> 2) & 3): the word reads of 16
-//         consecutive rows then hit 64 different banks.  A stage's copies
-//         are spread evenly over the P steps of the stage two earlier.
-//   * Lane (i, q) decodes, for each of its 4 row tiles t (row 16 t + i), part q
-//     of the group (blocks 8q .. 8q+7, two code words) straight into two A
-//     fragments: half s takes blocks 8q + 4s .. 8q + 4s + 3, i.e. k bytes
-//     32q + 16s .. + 16, which is the B fragment it reads from LDS.
-//   * One barrier per step.  Every vector-memory operation in the loop is one
-//     of these copies, a fixed number per wave and step, so before the
-//     barrier each wave waits (vmcnt) for its copies of the step's x tile;
-//     the copies of the step's code stage are older, so they have landed
-//     too.  After the barrier the whole step is in LDS, and the buffers of
-//     the finished step (and, at a stage start, stage) are free for the
-//     copies issued next.
-template <int WR_, int WC_, int UT_>
-struct TileCfg {
-  static constexpr int WR = WR_, WC = WC_, UT = UT_;
-  static constexpr int kWaves = WR * WC;
-  static constexpr int kThreads = kWaves * kWave;
-  static constexpr int kRows = 64 * WR;
-  static constexpr int kTok = 16 * UT * WC;
-  static constexpr int kXBytes = kTok * kGroupWeights;  // one step's x tile
-  static constexpr int kXCopies = kXBytes / (16 * kWave);  // 1 KB copies of it per step
-  static_assert(kXCopies * 16 * kWave == kXBytes, "x tile split");
-  // workgroups one CU is sized to hold (sets the x ring depth)
-  static constexpr int kWgPerCu = kWaves > 4 ? 1 : 2;
-};
-using TileSmall = TileCfg<2, 2, 4>;   // 128 x 128, 4 waves
-using TileLarge = TileCfg<4, 2, 6>;   // 256 x 192, 8 waves
-using TileSkinny = TileCfg<4, 1, 1>;  // 256 x 16, 4 waves (a few tokens: HBM-bound)
-static_assert(TileSmall::kRows == kGemmSmallRows && TileSmall::kTok == kGemmSmallTok, "small tiling");
-static_assert(TileLarge::kRows == kGemmLargeRows && TileLarge::kTok == kGemmLargeTok, "large tiling");
-static_assert(TileSkinny::kRows == kGemmSkinnyRows && TileSkinny::kTok == kGemmSkinnyTok, "skinny tiling");
-
-constexpr int kCodeSlots = 3;  // code stages in LDS: in use, next, in flight
-constexpr int kTileUnroll = 12;  // steps per loop iteration: a multiple of D and of 3 P
-
-// Code bytes of one stage and x-ring depth: kTileDepth, or fewer steps if the
-// CU's share of the 160 KB of LDS cannot hold them next to the code ring.
-template <class Fmt, class C>
-constexpr int code_stage_bytes() {
-  return C::kRows * (16 * Fmt::kTileHC + (Fmt::kTileTail ? 4 * Fmt::kTileP : 0));
-}
-// The depth is also at most P + 1: a stage's last copies are then issued
-// before the x copies of its first step, so waiting for those covers them.
-template <class Fmt, class C>
-constexpr int tile_depth() {
-  constexpr int fit = (160 * 1024 / C::kWgPerCu - 1024 - kCodeSlots * code_stage_bytes<Fmt, C>()) / C::kXBytes;
-  constexpr int cap = kTileDepth < Fmt::kTileP + 1 ? kTileDepth : Fmt::kTileP + 1;
-  return fit < cap ? fit : cap;
-}
-
-template <class Fmt, class C>
-__device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int tile_m) {
-  constexpr int D = tile_depth<Fmt, C>();
-  static_assert(D >= 2 && kTileUnroll % D == 0, "x ring depth");
-  constexpr int P = Fmt::kTileP;
-  constexpr int HC = Fmt::kTileHC;
-  static_assert(kTileUnroll % (kCodeSlots * P) == 0 && D <= P + 1, "code stage cadence");
-  constexpr int UT = C::UT;
-  constexpr int W = C::kWaves;
-  constexpr int R = C::kRows;
-  // x copies per step: TX, wave w issues NX w .. (those that exist)
-  constexpr int TX = C::kXCopies;
-  constexpr int NX = (TX + W - 1) / W;
-  // code copies per stage: head copies (64 chunk slots each) then tail copies
-  // (64 words each); every wave issues CPW of them in every step
-  constexpr int TH = R * HC / 64;
-  constexpr int TT = Fmt::kTileTail ? R * P / 64 : 0;
-  constexpr int CPW = (TH + TT) / (P * W);
-  static_assert(CPW * P * W == TH + TT && CPW >= 1, "code copies per wave and step");
-  constexpr int kOpsPerStep = TX / W + CPW;  // vector-memory operations per wave and step, at least
-  constexpr int XV = C::kXBytes / 16;
-  constexpr int HV = R * HC;
-  constexpr int TV = Fmt::kTileTail ? R * P : 1;
-  // the code table first in LDS (largest alignment): its address then fits
-  // the 16-bit offset field of the lookups
-  __shared__ __attribute__((aligned(1024))) uint32_t tab[32];
-  // one LDS array per ring slot and kind: distinct objects let the compiler
-  // see that reading one slot does not depend on the copies to the others
-  __shared__ u32x4_t xt0[XV], xt1[XV], xt2[D > 2 ? XV : 1], xt3[D > 3 ? XV : 1];
-  __shared__ u32x4_t hd0[HV], hd1[HV], hd2[HV];
-  __shared__ uint32_t tl0[TV], tl1[TV], tl2[TV];
-  auto xbuf = [&](int slot) -> u32x4_t* {
-    return slot == 0 ? xt0 : slot == 1 ? xt1 : slot == 2 ? xt2 : xt3;
-  };
-  auto hbuf = [&](int slot) -> u32x4_t* { return slot == 0 ? hd0 : slot == 1 ? hd1 : hd2; };
-  auto tbuf = [&](int slot) -> uint32_t* { return slot == 0 ? tl0 : slot == 1 ? tl1 : tl2; };
-  Fmt::init_table(tab, threadIdx.x);
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int i = lane & 15;
-  const int q = lane >> 4;
-  const int wn = wave % C::WR;
-  const int wm = wave / C::WR;
-  const int n0 = tile_n * R;
-  const int m0 = tile_m * C::kTok;
-  const int G = d.k / kGroupWeights;
-  const int lastn = d.n - 1;
-  const int lastm = d.m - 1;
-  // Copy sources are a uniform base plus a 32-bit per-lane byte offset (the
-  // caller keeps each matrix's codes and x below 4 GiB).
-  const uint32_t row_words = static_cast<uint32_t>(G) * Fmt::kWords;
-  const SHERRY_GLOBAL char* cbase = gmem(reinterpret_cast<const char*>(d.codes));
-  const SHERRY_GLOBAL char* xbase = gmem(reinterpret_cast<const char*>(d.x));
-
-  // x copy c fills 16-byte slots 64 c + lane of the buffer; slot s holds
-  // chunk (s % 8) ^ ((token >> 1) & 7) of token s / 8.
-  uint32_t xoff[NX];
-#pragma unroll
-  for (int j = 0; j < NX; ++j) {
-    const int slot = 64 * min(NX * wave + j, TX - 1) + lane;
-    const int tok = slot >> 3;
-    const int chunk = (slot & 7) ^ ((tok >> 1) & 7);
-    xoff[j] = static_cast<uint32_t>(min(m0 + tok, lastm)) * static_cast<uint32_t>(d.ldx) + 16u * chunk;
-  }
-  // Per-lane copy offsets are recomputed in every step from values passed
-  // through an empty asm statement: otherwise the compiler keeps the offsets
-  // of all unrolled steps live at once.
-  auto opaque = [](uint32_t v) {
-    asm volatile("" : "+v"(v));
-    return v;
-  };
-  auto copy_x = [&](int step, int slot) {
-    const uint32_t g = static_cast<uint32_t>(min(step, G - 1));  // past the end: a valid group, never used
-#pragma unroll
-    for (int j = 0; j < NX; ++j) {
-      const int c = NX * wave + j;
-      if (c < TX) lds_copy16(xbase, opaque(xoff[j]) + g * kGroupWeights, lds_addr(xbuf(slot) + 64 * c));
-    }
-  };
-  // code copy c of stage `stage` (groups P stage ..), into code slot `slot`
-  auto copy_code = [&](int stage, int slot, int c) {
-    const int g0 = P * stage;
-    const int ln = static_cast<int>(opaque(static_cast<uint32_t>(lane)));
-    if (c < TH) {
-      const int sl = 64 * c + ln;  // chunk slot of the stage buffer
-      const int r = sl / HC;
-      const int chunk = (sl % HC) ^ ((r >> 2) & 3);
-      const uint32_t w = static_cast<uint32_t>(min(n0 + r, lastn)) * row_words + Fmt::head_word(G, g0, chunk);
-      lds_copy16(cbase, 4u * w, lds_addr(hbuf(slot) + 64 * c));
-    } else {
-      const int sl = 64 * (c - TH) + ln;  // word slot of the stage's tails
-      const uint32_t w = static_cast<uint32_t>(min(n0 + sl / P, lastn)) * row_words + Fmt::tail_word(G, g0, sl % P);
-      lds_copy4(cbase, 4u * w, lds_addr(tbuf(slot) + 64 * (c - TH)));
-    }
-  };
-  // in step s: this wave's share (part s % P) of the copies of stage s / P + 2
-  auto copy_code_part = [&](int s, int b) {
-#pragma unroll
-    for (int j = 0; j < CPW; ++j)
-      copy_code(s / P + 2, (b / P + 2) % kCodeSlots, (b % P) * (CPW * W) + CPW * wave + j);
-  };
-
-  v4i acc[4][UT];
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-#pragma unroll
-    for (int u = 0; u < UT; ++u) acc[t][u] = v4i{0, 0, 0, 0};
-
-  // step with x in x slot xs, codes in code slot cs, group j of its stage
-  // The lane's code byte offsets pass through opaque() in every step, so the
-  // addresses are rebuilt from them there (the slot and row-tile parts are
-  // constants the LDS reads take as offsets); otherwise the compiler keeps an
-  // address register for every slot, row tile and group of the unrolled loop.
-  const uint32_t lane_h = static_cast<uint32_t>(16 * HC * (64 * wn + i));
-  const uint32_t lane_t = static_cast<uint32_t>(4 * P * (64 * wn + i));
-  const int swz = (i >> 2) & 3;  // = (row >> 2) & 3 for the lane's rows
-  auto compute = [&](int xs, int cs, int j) {
-    const u32x4_t* xb = xbuf(xs);
-    const char* hb = reinterpret_cast<const char*>(hbuf(cs));
-    const char* tb = reinterpret_cast<const char*>(tbuf(cs));
-    const uint32_t lh = opaque(lane_h);
-    const uint32_t lt = opaque(lane_t);
-    uint32_t w[4][2];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      Fmt::stage_words(w[t], hb + 16 * HC * 16 * t, tb + 4 * P * 16 * t, lh, lt, swz, j, q);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      v4i a[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) a[t] = Fmt::frag(w[t], q, s, tab);
-#pragma unroll
-      for (int u = 0; u < UT; ++u) {
-        const int tok = 16 * UT * wm + 16 * u + i;
-        const u32x4_t v = xb[8 * tok + ((2 * q + s) ^ ((tok >> 1) & 7))];
-        const v4i b = {static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w)};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[t][u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], b, acc[t][u], 0, 0, 0);
-      }
-    }
-  };
-  // Wait until this wave's x copies of step k landed (the copies of the D - 2
-  // younger steps may still be in flight), then the barrier.  The empty asm
-  // statements keep the compiler from moving memory accesses across.
-  auto step_barrier = [&]() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kOpsPerStep * (D - 2)));
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
-
-  // prologue: code stages 0 and 1, x steps 0 .. D - 2.  As in the loop, CPW
-  // code copies follow the x copies of each step, so that the wait count of
-  // the barriers holds from step 0 on: after a step's x copies every wave has
-  // issued at least kOpsPerStep * (D - 2) + CPW more operations by the
-  // barrier that needs them.  A wave's copies of one stage are copies
-  // wave + W t, t < P CPW.
-  constexpr int PC = P * CPW;
-  constexpr int late = (D - 1) * CPW;  // stage-1 copies after the x copies
-  static_assert(late <= PC, "prologue code copies");
-#pragma unroll
-  for (int t = 0; t < PC; ++t) copy_code(0, 0, wave + W * t);
-#pragma unroll
-  for (int t = 0; t < PC - late; ++t) copy_code(1, 1, wave + W * t);
-#pragma unroll
-  for (int b = 0; b + 1 < D; ++b) {
-    copy_x(b, b);
-#pragma unroll
-    for (int j = 0; j < CPW; ++j) copy_code(1, 1, wave + W * (PC - late + CPW * b + j));
-  }
-  __syncthreads();  // code table, and all of the above
-  for (int g = 0; g < G; g += kTileUnroll) {
-#pragma unroll
-    for (int b = 0; b < kTileUnroll; ++b) {
-      // step g + b: x in slot b % D, codes of stage (g + b) / P in code slot
-      // (b / P) % 3; after the barrier the finished step's x slot is refilled
-      // with step g + b + D - 1, and part of stage (g + b) / P + 2 is copied
-      step_barrier();
-      copy_x(g + b + D - 1, (b + D - 1) % D);
-      copy_code_part(g + b, b);
-      if (g + b < G) compute(b % D, (b / P) % kCodeSlots, b % P);
-    }
-  }
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // no copy may outlive the workgroup
-
-  tile_store<UT>(d, acc, n0 + 64 * wn, m0 + 16 * UT * wm, i, q);
-}
-
-template <class Fmt, class C>
-__global__ __launch_bounds__(C::kThreads) void gemm_tile_kernel(GemmDesc d) {
-  gemm_tile<Fmt, C>(d, blockIdx.x, blockIdx.y);
-}
-
-// Grouped: one workgroup per plan tile {problem, row tile, token tile}.
-template <class Fmt, class C>
-__global__ __launch_bounds__(C::kThreads) void gemm_tile_grouped_kernel(const char* plan) {
-  const PlanHeader* h = reinterpret_cast<const PlanHeader*>(plan);
-  const GemmDesc* descs = reinterpret_cast<const GemmDesc*>(plan + sizeof(PlanHeader));
-  const GemmTile tl = reinterpret_cast<const GemmTile*>(descs + h->count)[blockIdx.x];
-  const GemmDesc d = descs[tl.prob];
-  gemm_tile<Fmt, C>(d, tl.tile_n, tl.tile_m);
 }
 
 // ------------------------------------------------------- few tokens ---
@@ -707,8 +429,11 @@ hipError_t launch_tile(const GemmDesc& d, hipStream_t stream) {
   const int64_t large = ((d.n + TileLarge::kRows - 1) / TileLarge::kRows) *
                         ((d.m + TileLarge::kTok - 1) / TileLarge::kTok);
   if (large >= kLargeTileMinGroups) {
-    if (std::is_same<Fmt, Sherry3of4>::value && prefill_decode_once() && prefill_fits(d.k))
+    const int kind = prefill_kind();
+    if (std::is_same<Fmt, Sherry3of4>::value && kind == kPrefillDecodeOnce && prefill_fits(d.k))
       return launch_gemm_prefill(d, stream);
+    if (kind == kPrefillTiled32)
+      return launch_gemm_tile32(d, std::is_same<Fmt, Tern2>::value ? kFmtTern2 : kFmtSherry, stream);
     const dim3 grid((d.n + TileLarge::kRows - 1) / TileLarge::kRows, (d.m + TileLarge::kTok - 1) / TileLarge::kTok);
     hipLaunchKernelGGL((gemm_tile_kernel<Fmt, TileLarge>), grid, dim3(TileLarge::kThreads), 0, stream, d);
   } else {
@@ -758,8 +483,10 @@ hipError_t launch_gemm_grouped(const PlanHeader* h, const void* dev, hipStream_t
     else
       hipLaunchKernelGGL((gemm_few_grouped_kernel<Sherry3of4>), grid, dim3(kFewWaves * kWave), 0, stream, plan);
   } else if (tiling == kGemmTilingLarge) {
-    if (!t2 && prefill_decode_once() && h->reserved[1] != 0)
+    const int kind = prefill_kind();
+    if (!t2 && kind == kPrefillDecodeOnce && h->reserved[1] != 0)
       return launch_gemm_prefill_grouped(plan, h->n_tiles, stream);
+    if (kind == kPrefillTiled32) return launch_gemm_tile32_grouped(plan, h->n_tiles, h->format, stream);
     if (t2)
       hipLaunchKernelGGL((gemm_tile_grouped_kernel<Tern2, TileLarge>), grid, dim3(TileLarge::kThreads), 0, stream,
                          plan);

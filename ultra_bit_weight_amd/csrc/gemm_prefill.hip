@@ -177,6 +177,9 @@ __device__ __forceinline__ void gemm_pf_tile(const GemmDesc& d, int tile_n, int 
     }
   };
 
+  EpiScales es;
+  es.load(d, n0, m0, kPfRows, kPfTok, tid);
+
   // prologue: table, x of groups 0 and 1, code stage 0; the tiles of group 0
   u32x4_t xr[2][kPfXPer];
   uint32_t cw[2][kPfRowsPer][kGroupWords];
@@ -217,7 +220,13 @@ __device__ __forceinline__ void gemm_pf_tile(const GemmDesc& d, int tile_n, int 
     step(g0, std::integral_constant<int, 6>{});
     step(g0, std::integral_constant<int, 7>{});
   }
-  tile_store<kPfUT>(d, acc, n0 + 64 * wn, m0 + 16 * kPfUT * wm, i, q);
+  // the loop ends with a barrier after the last reads of the x tiles: the
+  // output-stage scales go to x slot 0
+  static_assert((kPfRows + kPfTok) * 4 <= sizeof(sh.x[0]), "output-stage scales fit an x slot");
+  float* sl = reinterpret_cast<float*>(sh.x[0]);
+  es.stage(d, sl, kPfRows, kPfTok, tid);
+  __syncthreads();
+  tile_store<kPfUT>(d, acc, n0 + 64 * wn, m0 + 16 * kPfUT * wm, i, q, sl + 64 * wn, sl + kPfRows + 16 * kPfUT * wm);
 }
 
 __global__ __launch_bounds__(kPfThreads) void gemm_prefill_kernel(GemmDesc d) {
@@ -234,12 +243,12 @@ __global__ __launch_bounds__(kPfThreads) void gemm_prefill_grouped_kernel(const 
   gemm_pf_tile(descs[tl.prob], tl.tile_n, tl.tile_m, sh);
 }
 
-std::atomic<bool> g_decode_once{false};
+std::atomic<int> g_prefill_kind{kPrefillTiled};
 
 }  // namespace
 
-void set_prefill_decode_once(bool on) { g_decode_once.store(on, std::memory_order_relaxed); }
-bool prefill_decode_once() { return g_decode_once.load(std::memory_order_relaxed); }
+void set_prefill_kind(int kind) { g_prefill_kind.store(kind, std::memory_order_relaxed); }
+int prefill_kind() { return g_prefill_kind.load(std::memory_order_relaxed); }
 
 hipError_t launch_gemm_prefill(const GemmDesc& d, hipStream_t stream) {
   const dim3 grid((d.n + kPfRows - 1) / kPfRows, (d.m + kPfTok - 1) / kPfTok);

@@ -206,12 +206,16 @@ __host__ __device__ constexpr int bf_few_slices(int groups) {
   return s;
 }
 hipError_t launch_gemm_bf16(const GemmDesc& d, hipStream_t stream);
-// Many tokens on Sherry codes with the large tiling (kGemmLargeRows x
-// kGemmLargeTok): the decode-once kernel (each group's codes decoded once per
-// workgroup into an int8 A tile in LDS) when selected, else the general tiled
-// kernel (measured faster on the 1B layer at 2048 tokens).
-void set_prefill_decode_once(bool on);
-bool prefill_decode_once();
+// Many tokens with the large tiling (kGemmLargeRows x kGemmLargeTok), by the
+// process-wide prefill kind: the general tiled kernel (16 x 16 products, 8
+// waves), the same kernel on 32 x 32 products (4 waves of 128 x 96), or, on
+// Sherry codes, the decode-once kernel (each group's codes decoded once per
+// workgroup into an int8 A tile in LDS).
+constexpr int kPrefillTiled = 0, kPrefillDecodeOnce = 1, kPrefillTiled32 = 2;
+void set_prefill_kind(int kind);
+int prefill_kind();
+hipError_t launch_gemm_tile32(const GemmDesc& d, int32_t format, hipStream_t stream);
+hipError_t launch_gemm_tile32_grouped(const char* plan, int32_t n_tiles, int32_t format, hipStream_t stream);
 // The decode-once kernel steps through k in unrolled runs of this many groups
 // (two code stages); other k take the general tiled kernel.
 constexpr int kPrefillGroupMultiple = 8;

@@ -219,13 +219,13 @@ def _check_gemm_args(fmt, codes, scales, x, x_scales, acc, y):
     return m, n, k
 
 
-PREFILL_TILED, PREFILL_DECODE_ONCE = 0, 1
+PREFILL_TILED, PREFILL_DECODE_ONCE, PREFILL_TILED32 = 0, 1, 2
 
 
 def set_prefill_kernel(kind: int) -> None:
-    """Process-wide choice of the many-token kernel on 3:4 codes
-    (sherry_set_prefill_kernel): PREFILL_TILED (default) or
-    PREFILL_DECODE_ONCE."""
+    """Process-wide choice of the many-token kernel
+    (sherry_set_prefill_kernel): PREFILL_TILED (default), PREFILL_DECODE_ONCE
+    or PREFILL_TILED32."""
     _check("sherry_set_prefill_kernel", load().sherry_set_prefill_kernel(kind))
 
 
