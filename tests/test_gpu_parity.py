@@ -617,6 +617,42 @@ def test_grouped_gemm_few_tokens_layer(gpu_lib, m):
 
 
 @pytest.mark.parametrize("tern2", [False, True])
+def test_grouped_gemm_fp16_outputs_every_output(gpu_lib, prefill_kernel, tern2):
+    """fp16 outputs without raw sums (the benchmark's form) on the large
+    tiles, more tiles than CUs: every output of four ragged problems with row
+    strides that are multiples of 4 (four rows per store; odd row counts end
+    with single stores) or odd (single stores), k from 384 to 2048, launched
+    twice."""
+    say(f"grouped gemm fp16 outputs {prefill_kernel} tern2={tern2}")
+    g = synth.rng(808 + tern2)
+    m = 1500
+    shapes = [(3001, 1024, 3), (2050, 384, 2), (1027, 2048, 0), (4096, 640, 0)]
+    probs, refs = [], []
+    for n, k, ypad in shapes:
+        sw = synth.row_scales(n, g, np.float16)
+        if tern2:
+            t = synth.ternary_dense(n, k, g)
+            words = tern2_ref.pack(t)
+        else:
+            words = synth.random_words(n * (k // 128) * 5, g)
+        xq, sx, _ = synth.act_absmax_int8(m, k, g)
+        ref = (tern2_ref if tern2 else sherry_ref).gemm_i8(words, sw, n, k, xq, sx, np.float16)[1]
+        ybig = torch.full((m, n + ypad), float("nan"), dtype=torch.float16, device=DEV)
+        probs.append(dict(codes=words_dev(words), scales=dev(sw), x=dev(xq), x_scales=dev(sx), y=ybig[:, :n]))
+        refs.append((ref, ybig, n))
+    grouped = gpu_lib.GroupedGemm(probs, tern2=tern2)
+    assert grouped.n_tiles > 256
+    for rep in range(2):  # the plan runs twice: no state carried between launches
+        grouped()
+        torch.cuda.synchronize()
+        for ref, ybig, n in refs:
+            got = ybig.cpu().numpy()
+            assert np.array_equal(got[:, :n].view(np.uint16), ref.view(np.uint16)), (n, rep)
+            assert np.isnan(got[:, n:]).all()  # nothing written past the row end
+            ybig[:, :n] = float("nan")
+
+
+@pytest.mark.parametrize("tern2", [False, True])
 def test_grouped_gemm_prefill_layer_sampled(gpu_lib, prefill_kernel, tern2):
     """The seven matrices of a LLaMA-3.2-1B layer at 2048 tokens in one launch
     (256 x 192 tiles, the benchmark's launch); 48 sampled rows of every

@@ -227,7 +227,6 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int til
       for (int u = 0; u < UT; ++u) acc[t][u] = v4i{0, 0, 0, 0};
   }
 
-  // step with x in x slot xs, codes in code slot cs, group j of its stage
   // The lane's code byte offsets pass through opaque() in every step, so the
   // addresses are rebuilt from them there (the slot and row-tile parts are
   // constants the LDS reads take as offsets); otherwise the compiler keeps an
@@ -240,8 +239,14 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int til
   const uint32_t lane_h = static_cast<uint32_t>(16 * HC * (WROWS * wn + lr));
   const uint32_t lane_t = static_cast<uint32_t>(4 * P * (WROWS * wn + lr));
   const int swz = (lr >> 2) & 3;
-  auto compute = [&](int xs, int cs, int j) {
-    const u32x4_t* xb = xbuf(xs);
+  // A fragments of the next step: a step's codes are in LDS one step early
+  // (their copies are older than the step's x copies, which the barrier
+  // before it waits for), so each step expands the next step's codes while
+  // its own products run.  an[s][t]: substep (half) s, row tile t.
+  constexpr int AS = M32 ? 4 : 2;
+  constexpr int AT = M32 ? RT32 : 4;
+  v4i an[AS][AT];
+  auto decode = [&](int cs, int j) {
     const char* hb = reinterpret_cast<const char*>(hbuf(cs));
     const char* tb = reinterpret_cast<const char*>(tbuf(cs));
     const uint32_t lh = opaque(lane_h);
@@ -251,45 +256,45 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int til
 #pragma unroll
       for (int t = 0; t < RT32; ++t)
         Fmt::window32(win[t], hb + 16 * HC * 32 * t, tb + 4 * P * 32 * t, lh, lt, swz, j, h32);
-      v4i a[2][RT32], b[2][U32];
-      auto frags = [&](int s, int fb) {
 #pragma unroll
-        for (int t = 0; t < RT32; ++t) a[fb][t] = Fmt::frag32(win[t], s, tab);
+      for (int s = 0; s < AS; ++s)
+#pragma unroll
+        for (int t = 0; t < RT32; ++t) an[s][t] = Fmt::frag32(win[t], s, tab);
+    } else {
+      uint32_t w[4][2];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        Fmt::stage_words(w[t], hb + 16 * HC * 16 * t, tb + 4 * P * 16 * t, lh, lt, swz, j, q);
+#pragma unroll
+      for (int s = 0; s < AS; ++s)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) an[s][t] = Fmt::frag(w[t], q, s, tab);
+    }
+  };
+  // the products of a step: A from an[][], B from x slot xs
+  auto products = [&](int xs) {
+    const u32x4_t* xb = xbuf(xs);
+    auto bfrag = [&](int tok, int chunk) {
+      const u32x4_t v = xb[8 * tok + (chunk ^ ((tok >> 1) & 7))];
+      return v4i{static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w)};
+    };
+#pragma unroll
+    for (int s = 0; s < AS; ++s) {
+      if constexpr (M32) {
 #pragma unroll
         for (int u = 0; u < U32; ++u) {
-          const int tok = 16 * UT * wm + 32 * u + lr;
-          const u32x4_t v = xb[8 * tok + (Fmt::x_chunk32(h32, s) ^ ((tok >> 1) & 7))];
-          b[fb][u] = v4i{static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w)};
+          const v4i b = bfrag(16 * UT * wm + 32 * u + lr, Fmt::x_chunk32(h32, s));
+#pragma unroll
+          for (int t = 0; t < RT32; ++t)
+            acc32[t][u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(an[s][t], b, acc32[t][u], 0, 0, 0);
         }
-      };
-      frags(0, 0);
+      } else {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (s < 3) frags(s + 1, (s + 1) & 1);
+        for (int u = 0; u < UT; ++u) {
+          const v4i b = bfrag(16 * UT * wm + 16 * u + i, 2 * q + s);
 #pragma unroll
-        for (int t = 0; t < RT32; ++t)
-#pragma unroll
-          for (int u = 0; u < U32; ++u)
-            acc32[t][u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[s & 1][t], b[s & 1][u], acc32[t][u], 0, 0, 0);
-      }
-      return;
-    }
-    uint32_t w[4][2];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      Fmt::stage_words(w[t], hb + 16 * HC * 16 * t, tb + 4 * P * 16 * t, lh, lt, swz, j, q);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      v4i a[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) a[t] = Fmt::frag(w[t], q, s, tab);
-#pragma unroll
-      for (int u = 0; u < UT; ++u) {
-        const int tok = 16 * UT * wm + 16 * u + i;
-        const u32x4_t v = xb[8 * tok + ((2 * q + s) ^ ((tok >> 1) & 7))];
-        const v4i b = {static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w)};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) acc[t][u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], b, acc[t][u], 0, 0, 0);
+          for (int t = 0; t < 4; ++t) acc[t][u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(an[s][t], b, acc[t][u], 0, 0, 0);
+        }
       }
     }
   };
@@ -323,7 +328,16 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int til
 #pragma unroll
     for (int j = 0; j < CPW; ++j) copy_code(1, 1, wave + W * (PC - late + CPW * b + j));
   }
-  __syncthreads();  // code table, and all of the above
+  // Code stage 0 must be in LDS before the first decode: each wave waits for
+  // its copies of it (its oldest operations; at least PC - late + (D - 1)
+  // (TX / W + CPW) were issued after them), then the barrier (which also
+  // covers the code table).
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(PC - late + (D - 1) * kOpsPerStep));
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  decode(0, 0);
   for (int g = 0; g < G; g += kTileUnroll) {
 #pragma unroll
     for (int b = 0; b < kTileUnroll; ++b) {
@@ -333,7 +347,10 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int til
       step_barrier();
       copy_x(g + b + D - 1, (b + D - 1) % D);
       copy_code_part(g + b, b);
-      if (g + b < G) compute(b % D, (b / P) % kCodeSlots, b % P);
+      if (g + b < G) {
+        products(b % D);
+        decode(((b + 1) / P) % kCodeSlots, (b + 1) % P);  // step g + b + 1 (kTileUnroll is a multiple of 3 P)
+      }
     }
   }
   asm volatile("" ::: "memory");
