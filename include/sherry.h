@@ -256,17 +256,17 @@ sherry_status sherry_gemm_plan(const sherry_gemm_problem* probs /* HOST */, int3
 sherry_status sherry_gemm_grouped(const void* plan_host, const void* plan_dev, hipStream_t stream);
 
 /* Kernel of the int8 products for many tokens (sherry_gemm, tern2_gemm and
- * grouped plans that take the 256 x 192 tiles):
+ * grouped plans that take the 256 x 128 tiles):
  *   SHERRY_PREFILL_TILED (default): waves expand the codes they multiply,
  *     straight from a staged copy in LDS into 16 x 16 x 64 matrix-core
- *     operands (8 waves of 64 rows x 96 tokens);
+ *     operands (4 waves of 64 rows x 128 tokens, two workgroups per CU);
  *   SHERRY_PREFILL_DECODE_ONCE: on 3:4 codes, each group of a tile's codes is
  *     decoded once per workgroup into an int8 weight tile in LDS that the
  *     waves multiply (Sherry Abstract: 3:4 blocks of four weights in five
  *     bits), for k a multiple of 1024 (other k and 2-bit codes keep the tiled
  *     kernel);
  *   SHERRY_PREFILL_TILED32: the tiled kernel on 32 x 32 x 32 matrix-core
- *     operands, 4 waves of 128 rows x 96 tokens.
+ *     operands, same waves and tiles.
  * All give identical results.  The setting is process-wide and applies to
  * launches issued after the call.  Errors: SHERRY_EINVAL for another kind. */
 typedef enum sherry_prefill_kernel {

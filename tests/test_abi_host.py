@@ -357,12 +357,13 @@ def test_grouped_gemm_plan_on_host(lib):
         return [tuple(int.from_bytes(raw[16 * t + 4 * f:16 * t + 4 * f + 4], "little") for f in range(3))
                 for t in range(n_tiles)]
 
-    # a prefill layer (LLaMA-3.2-1B, 2048 tokens): 256 x 192 tiles (11 token
+    # a prefill layer (LLaMA-3.2-1B, 2000 tokens): 256 x 128 tiles (16 token
     # tiles, the last one ragged), longest rows first
-    layer = [(2048, 2048, 2048), (512, 2048, 2048), (512, 2048, 2048), (2048, 2048, 2048), (8192, 2048, 2048),
-             (8192, 2048, 2048), (2048, 8192, 2048)]
+    layer = [(2048, 2048, 2000), (512, 2048, 2000), (512, 2048, 2000), (2048, 2048, 2000), (8192, 2048, 2000),
+             (8192, 2048, 2000), (2048, 8192, 2000)]
     arr = problems(layer)
-    n_tiles = (8 + 2 + 2 + 8 + 32 + 32 + 8) * 11
+    TT = 16  # token tiles of 128
+    n_tiles = (8 + 2 + 2 + 8 + 32 + 32 + 8) * TT
     nbytes = lib.sherry_gemm_plan_bytes(arr, len(layer))
     assert nbytes == 64 + 80 * len(layer) + 16 * n_tiles
     buf = ctypes.create_string_buffer(nbytes + 8)
@@ -371,20 +372,20 @@ def test_grouped_gemm_plan_on_host(lib):
     hdr = ctypes.string_at(base, 64)
     assert int.from_bytes(hdr[8:12], "little") == len(layer)
     assert int.from_bytes(hdr[12:16], "little") == n_tiles
-    assert int.from_bytes(hdr[40:48], "little") == 1  # 256 x 192 tiling
+    assert int.from_bytes(hdr[40:48], "little") == 1  # 256 x 128 tiling
     t = tiles_of(base, len(layer), n_tiles)
     # eight interleaved lists, one per XCD (workgroup w runs on XCD w % 8):
     # XCD c takes share c of every problem's tiles (listed token tile by token
     # tile), problems with the longest rows (down, k = 8192) first; shares of
     # equal count, the remainders dealt to the XCDs in turn
     assert sorted(t) == sorted((i, a, b) for i, (n, _, _) in enumerate(layer) for a in range(n // 256)
-                               for b in range(11)) and len(set(t)) == n_tiles
+                               for b in range(TT)) and len(set(t)) == n_tiles
     lists = [t[c::8] for c in range(8)]
-    assert [len(x) for x in lists] == [127, 127, 127, 127, 126, 126, 126, 126]  # 1012 = 8 * 126 + 4
+    assert [len(x) for x in lists] == [184] * 8  # 1472 = 8 * 184
     nxt = 0
     for i in (6, 0, 1, 2, 3, 4, 5):
         tn = layer[i][0] // 256
-        seq = [(i, u % tn, u // tn) for u in range(11 * tn)]
+        seq = [(i, u % tn, u // tn) for u in range(TT * tn)]
         q, r = divmod(len(seq), 8)
         u = 0
         for c in range(8):
@@ -395,7 +396,7 @@ def test_grouped_gemm_plan_on_host(lib):
     # the XCD lists hold the problems in order: down first
     assert all([x[0] for x in lst] == sorted((x[0] for x in lst), key=(6, 0, 1, 2, 3, 4, 5).index)
                for lst in lists)
-    assert t[0] == (6, 0, 0) and t[1] == (6, 3, 1) and t[-1][0] == 5
+    assert t[0] == (6, 0, 0) and t[1] == (6, 0, 2) and t[-1][0] == 5
     assert lib.tern2_gemm_plan(arr, len(layer), F16, I8, F16, base, nbytes) == OK
     # a small set of problems: 128 x 128 tiles (ragged in rows and tokens)
     small = [(300, 1024, 200), (64, 128, 64)]

@@ -430,7 +430,7 @@ def prefill_kernel(request, gpu_lib):
 @pytest.mark.parametrize("n,m,k", [(4133, 2930, 1024), (4101, 2900, 2048), (3100, 4000, 3072), (2900, 4100, 8192),
                                    (8193, 1537, 384), (4000, 3100, 1152)])
 def test_gemm_large_tiles_every_output(gpu_lib, prefill_kernel, n, m, k):
-    """Shapes that take the large (256 x 192) tiles, every output against the
+    """Shapes that take the large (256 x 128) tiles, every output against the
     oracle, with each kernel: ragged rows and tokens; k a multiple of 1024
     (the decode-once kernel takes these: one, two, three and eight runs of
     eight groups) and other k (always the general tiled kernel; odd group

@@ -214,7 +214,7 @@ sherry_status gemm_impl(int32_t format, const uint32_t* codes, const void* w_sca
 // Grouped GEMM plan: header | GemmDesc[count] | GemmTile[n_tiles].  Tiling:
 // the few-token kernel when every problem has m <= 16 and k <= 8192 (row
 // tiles of few_tile_rows(k / 128) rows, all tokens); else 256 x 16 when every
-// problem has m <= 16; else 256 x 192 when that gives at least
+// problem has m <= 16; else 256 x 128 when that gives at least
 // kLargeTileMinGroups tiles; else 128 x 128.
 struct GemmTiling {
   int64_t kind;

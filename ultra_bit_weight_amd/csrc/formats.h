@@ -111,8 +111,8 @@ struct Sherry3of4 {
   // row) and, with kTileTail, kTileP tail words (word 4 of each group).
   // Word offsets from the row start (groups past the row end clamp to the
   // last group: such words are copied but never used):
-  static constexpr int kTileP = 4;
-  static constexpr int kTileHC = 4;
+  static constexpr int kTileP = 2;
+  static constexpr int kTileHC = 2;
   static constexpr bool kTileTail = true;
   __device__ __forceinline__ static int head_word(int G, int g0, int c) { return 4 * min(g0 + c, G - 1); }
   __device__ __forceinline__ static int tail_word(int G, int g0, int j) { return 4 * G + min(g0 + j, G - 1); }
@@ -219,9 +219,9 @@ struct Tern2 {
                static_cast<int>(__builtin_amdgcn_perm(0u, 0xFF000100u, (x >> 4) & 0x03030303u)),
                static_cast<int>(__builtin_amdgcn_perm(0u, 0xFF000100u, (x >> 6) & 0x03030303u))};
   }
-  // Tiled GEMM stages: 2 groups per row (4 chunks of 16 bytes), no tail.
-  static constexpr int kTileP = 2;
-  static constexpr int kTileHC = 4;
+  // Tiled GEMM stages: 1 group per row (2 chunks of 16 bytes), no tail.
+  static constexpr int kTileP = 1;
+  static constexpr int kTileHC = 2;
   static constexpr bool kTileTail = false;
   __device__ __forceinline__ static int head_word(int G, int g0, int c) {
     return 8 * min(g0 + (c >> 1), G - 1) + 4 * (c & 1);

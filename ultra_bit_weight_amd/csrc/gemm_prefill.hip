@@ -4,15 +4,15 @@
 // Sparsification", Abstract: 3:4 sparse ternary blocks in five bits; Figure 2
 // caption: four-weight blocks).
 //
-// A workgroup of 8 waves computes a 256-row x 192-token tile of Y, stepping k
-// by one 128-weight group.  In the step of group g:
-//   * every wave multiplies its 64-row x 96-token sub-tile for group g: A and B
-//     fragments read from the LDS tiles of g, 48 v_mfma_i32_16x16x64_i8;
-//   * the 512 threads decode the tile's weights of group g + 1 once: thread
+// A workgroup of 16 waves computes a 256-row x 128-token tile of Y (the large
+// tiling), stepping k by one 128-weight group.  In the step of group g:
+//   * every wave multiplies its 64-row x 32-token sub-tile for group g: A and B
+//     fragments read from the LDS tiles of g, 16 v_mfma_i32_16x16x64_i8;
+//   * the 1024 threads decode the tile's weights of group g + 1 once: thread
 //     (row r, quarter j) expands blocks 8 j .. 8 j + 7 of row r (eight reads of
 //     the 32-entry table, 32 int8 weights) into the int8 A tile of g + 1 in
-//     LDS, for two rows (r and r + 128);
-//   * they copy the x tile of g + 1 (192 tokens x 128 bytes) from registers to
+//     LDS;
+//   * they copy the x tile of g + 1 (128 tokens x 128 bytes) from registers to
 //     its LDS tile; x of g + 2 is loaded into registers meanwhile.
 // Codes come in stages of four groups: the four threads of a row (a quad)
 // load the row's 64-byte run of the four group heads (16 bytes each) and its
@@ -40,15 +40,15 @@ namespace sherry {
 namespace {
 
 constexpr int kPfRows = kGemmLargeRows;  // 256
-constexpr int kPfTok = kGemmLargeTok;    // 192
+constexpr int kPfTok = kGemmLargeTok;    // 128
 constexpr int kPfWaves = 16;
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kPfWR = 4;                                  // waves along the rows (64 rows each)
-constexpr int kPfUT = kPfTok / (16 * (kPfWaves / kPfWR));  // 16-token tiles per wave: 6
+constexpr int kPfUT = kPfTok / (16 * (kPfWaves / kPfWR));  // 16-token tiles per wave: 2
 constexpr int kPfXChunks = kPfTok * 8;                    // 16-byte chunks of one group's x tile
-constexpr int kPfXPer = (kPfXChunks + kPfThreads - 1) / kPfThreads;  // per thread: 2 (the second for half the waves)
+constexpr int kPfXPer = (kPfXChunks + kPfThreads - 1) / kPfThreads;  // per thread: 1
 constexpr int kPfStage = 4;                               // groups per code stage (one per quad lane)
-constexpr int kPfRowsPer = kPfRows * kPfStage / kPfThreads;  // rows per thread: 2
+constexpr int kPfRowsPer = kPfRows * kPfStage / kPfThreads;  // rows per thread: 1
 constexpr int kPfUnroll = 2 * kPfStage;                   // two stages: register slots are compile-time
 static_assert(kPfXChunks % kWave == 0, "x tile split: whole waves");
 static_assert(kPfRowsPer * kPfThreads == kPfRows * kPfStage, "decode split");

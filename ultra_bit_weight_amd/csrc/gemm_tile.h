@@ -33,11 +33,11 @@ static_assert(kTileDepth >= 2 && kTileDepth <= 4, "tile pipeline depth");
 //         position c ^ ((token >> 1) & 7), so the B-fragment reads of 16
 //         consecutive tokens hit 16 different bank groups;
 //       - the codes in stages of P groups, two stages ahead, into a ring of 3
-//         buffers: per row the P groups' head words (contiguous in the row,
-//         so four lanes read 64 contiguous bytes) and tail words.  Chunk c of
-//         a row sits at position c ^ ((row >> 2) & 3): the word reads of 16
-//         consecutive rows then hit 64 different banks.  A stage's copies
-//         are spread evenly over the P steps of the stage two earlier.
+//         buffers: per row the P groups' HC 16-byte head chunks (contiguous
+//         in the row) and tail words.  Chunk c of a row sits at position
+//         c ^ ((row >> 2) & (HC - 1)), which spreads the word reads of
+//         consecutive rows over the banks.  A stage's copies are spread
+//         evenly over the P steps of the stage two earlier.
 //   * Lane (i, q) decodes, for each of its 4 row tiles t (row 16 t + i), part q
 //     of the group (blocks 8q .. 8q+7, two code words) straight into two A
 //     fragments: half s takes blocks 8q + 4s .. 8q + 4s + 3, i.e. k bytes
@@ -72,7 +72,7 @@ struct TileCfg {
   static constexpr int kWgPerCu = WGCU_;
 };
 using TileSmall = TileCfg<2, 2, 4>;   // 128 x 128, 4 waves
-using TileLarge = TileCfg<4, 2, 6>;   // 256 x 192, 8 waves
+using TileLarge = TileCfg<4, 1, 8, 64, false, 2>;  // 256 x 128, 4 waves, two workgroups per CU
 using TileSkinny = TileCfg<4, 1, 1>;  // 256 x 16, 4 waves (a few tokens: HBM-bound)
 static_assert(TileSmall::kRows == kGemmSmallRows && TileSmall::kTok == kGemmSmallTok, "small tiling");
 static_assert(TileLarge::kRows == kGemmLargeRows && TileLarge::kTok == kGemmLargeTok, "large tiling");
@@ -193,7 +193,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int til
     if (c < TH) {
       const int sl = 64 * c + ln;  // chunk slot of the stage buffer
       const int r = sl / HC;
-      const int chunk = (sl % HC) ^ ((r >> 2) & 3);
+      const int chunk = (sl % HC) ^ ((r >> 2) & (HC - 1));
       const uint32_t w = static_cast<uint32_t>(min(n0 + r, lastn)) * row_words + Fmt::head_word(G, g0, chunk);
       lds_copy16(cbase, 4u * w, hlds[slot] + 1024u * c);
     } else {
@@ -233,12 +233,12 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int til
   // address register for every slot, row tile and group of the unrolled loop.
   // 16 x 16 products: lane (i, q) has rows 16 t + i of the wave's rows;
   // 32 x 32: lane (r32, h) has rows 32 t + r32.  Either way the stage
-  // swizzle of the lane's rows is (row >> 2) & 3 of its row index.
+  // swizzle of the lane's rows is (row >> 2) & (HC - 1) of its row index.
   const int lr = M32 ? (lane & 31) : i;
   const int h32 = lane >> 5;
   const uint32_t lane_h = static_cast<uint32_t>(16 * HC * (WROWS * wn + lr));
   const uint32_t lane_t = static_cast<uint32_t>(4 * P * (WROWS * wn + lr));
-  const int swz = (lr >> 2) & 3;
+  const int swz = (lr >> 2) & (HC - 1);
   // A fragments of the next step: a step's codes are in LDS one step early
   // (their copies are older than the step's x copies, which the barrier
   // before it waits for), so each step expands the next step's codes while

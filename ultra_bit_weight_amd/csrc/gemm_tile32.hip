@@ -1,34 +1,29 @@
 // The tiled int8 product for many tokens on 32 x 32 x 32 matrix-core
-// products: the 256-row x 192-token tile of the large tiling, as 4 waves of
-// 128 rows x 96 tokens (4 x 3 tiles of 32 x 32 int32 sums per wave, 192
-// registers, held in the accumulation registers).  The 32 x 32 products run
-// near the chip's int8 peak per clock where the 16 x 16 ones reach about half
-// of it; with 157 KB of LDS per workgroup the CU holds one workgroup, one wave
-// per SIMD.  Weights: packed ternary blocks ("Sherry: Hardware-Efficient
-// 1.25-Bit Ternary Quantization via Fine-grained Sparsification", Abstract)
-// and the 2-bit comparator (same paper, Figure 2 caption).
+// products: the 256-row x 128-token tile of the large tiling, as 4 waves of
+// 64 rows x 128 tokens (2 x 4 tiles of 32 x 32 int32 sums per wave, 128
+// registers) and, with 78 KB of LDS per workgroup, two workgroups per CU
+// (two waves per SIMD).  The 32 x 32 products run near the chip's int8 peak
+// per clock where the 16 x 16 ones reach about 60 % of it.  Weights: packed
+// ternary blocks ("Sherry: Hardware-Efficient 1.25-Bit Ternary Quantization
+// via Fine-grained Sparsification", Abstract) and the 2-bit comparator (same
+// paper, Figure 2 caption).
 #include "gemm_tile.h"
 
 namespace sherry {
 namespace {
 
-#ifndef SHERRY_TILE32_WAVES
-#define SHERRY_TILE32_WAVES 8
-#endif
-#if SHERRY_TILE32_WAVES == 4
-using TileWide = TileCfg<2, 2, 6, 128, true, 1>;
-#else
-using TileWide = TileCfg<4, 2, 6, 64, true, 1>;
-#endif
+using TileWide = TileCfg<4, 1, kGemmLargeTok / 16, 64, true, 2>;
+// two waves per SIMD: at most 256 registers per wave
+#define SHERRY_T32_OCC __attribute__((amdgpu_waves_per_eu(2)))
 static_assert(TileWide::kRows == kGemmLargeRows && TileWide::kTok == kGemmLargeTok, "large tiling");
 
 template <class Fmt>
-__global__ __launch_bounds__(TileWide::kThreads) void gemm_tile32_kernel(GemmDesc d) {
+__global__ __launch_bounds__(TileWide::kThreads) SHERRY_T32_OCC void gemm_tile32_kernel(GemmDesc d) {
   gemm_tile<Fmt, TileWide>(d, blockIdx.x, blockIdx.y);
 }
 
 template <class Fmt>
-__global__ __launch_bounds__(TileWide::kThreads) void gemm_tile32_grouped_kernel(const char* plan) {
+__global__ __launch_bounds__(TileWide::kThreads) SHERRY_T32_OCC void gemm_tile32_grouped_kernel(const char* plan) {
   const PlanHeader* h = reinterpret_cast<const PlanHeader*>(plan);
   const GemmDesc* descs = reinterpret_cast<const GemmDesc*>(plan + sizeof(PlanHeader));
   const GemmTile tl = reinterpret_cast<const GemmTile*>(descs + h->count)[blockIdx.x];

@@ -147,7 +147,7 @@ static_assert(sizeof(GemmTile) == 16, "grouped GEMM tile record layout");
 // and 256 x 16 for plans whose problems all have m <= 16.
 constexpr int64_t kGemmTilingSmall = 0, kGemmTilingLarge = 1, kGemmTilingSkinny = 2, kGemmTilingFew = 3,
                   kGemmTilingTwo = 4, kGemmTilingBf16 = 5;
-constexpr int kGemmLargeRows = 256, kGemmLargeTok = 192;
+constexpr int kGemmLargeRows = 256, kGemmLargeTok = 128;
 constexpr int kGemmSmallRows = 128, kGemmSmallTok = 128;
 constexpr int kGemmSkinnyRows = 256, kGemmSkinnyTok = 16;
 // Few-token kernel (every problem m <= 16, k <= 8192): a row tile of
