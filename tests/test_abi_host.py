@@ -420,18 +420,17 @@ def test_grouped_gemm_plan_on_host(lib):
     arr2[1].m = 0
     assert lib.sherry_gemm_plan(arr2, 2, F16, I8, F16, base, nb2) == EINVAL
     # every problem with m <= 16 and k <= 8192: the few-token kernel, row
-    # tiles of min(512, 2048 / slices) rows (slices = k / 512 rounded up to a
-    # power of two): 512 rows at k = 2048 and 1024, 128 at 8192
+    # tiles of 512 rows for every k
     few = [(2048, 2048, 16), (300, 1024, 3), (300, 8192, 1)]
     arr3 = problems(few)
-    n3 = 4 + 1 + 3
+    n3 = 4 + 1 + 1
     nb3 = lib.sherry_gemm_plan_bytes(arr3, 3)
     # room for the bf16 tiling too (every m <= 16, k <= 8192): 1024-row tiles
     n3_bf16 = 2 + 1 + 1
     assert nb3 == 64 + 80 * 3 + 16 * max(n3, n3_bf16)
     assert lib.sherry_gemm_plan(arr3, 3, F16, I8, F16, base, nb3) == OK
     assert int.from_bytes(ctypes.string_at(base + 40, 8), "little") == 3
-    assert tiles_of(base, 3, n3) == [(2, a, 0) for a in range(3)] + [(0, a, 0) for a in range(4)] + [(1, 0, 0)]
+    assert tiles_of(base, 3, n3) == [(2, 0, 0)] + [(0, a, 0) for a in range(4)] + [(1, 0, 0)]
     # the same problems with bf16 x (fp32 y, no token scales): tiling 5,
     # 1024-row tiles, longest rows first
     assert lib.sherry_gemm_plan(arr3, 3, F16, BF16, F32, base, nb3) == OK

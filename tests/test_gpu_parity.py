@@ -565,10 +565,10 @@ def run_grouped_gemm(gpu_lib, tern2, shapes, seed, n_tiles):
 def test_grouped_gemm_few_tokens(gpu_lib, tern2):
     """Problems with m <= 16 and k <= 8192 in one launch (few-token kernel):
     ragged rows, m from 1 to 16, and every k-slice class (k / 512 rounded up
-    to 1, 2, 4, 8, 16).  Row tiles: min(512, 2048 / slices) rows."""
+    to 1, 2, 4, 8, 16).  Row tiles of 512 rows."""
     say(f"grouped gemm few tokens tern2={tern2}")
     shapes = [(300, 1024, 1), (64, 128, 16), (513, 2048, 7), (17, 8192, 3), (1000, 640, 12), (2048, 3072, 16)]
-    run_grouped_gemm(gpu_lib, tern2, shapes, 717 + tern2, 1 + 1 + 2 + 1 + 2 + 8)
+    run_grouped_gemm(gpu_lib, tern2, shapes, 717 + tern2, 1 + 1 + 2 + 1 + 2 + 4)
 
 
 @pytest.mark.parametrize("tern2", [False, True])

@@ -320,8 +320,10 @@ template <class Fmt>
 __device__ __forceinline__ void gemm_few_tile(const GemmDesc& d, int tile) {
   constexpr int kThreads = kFewWaves * kWave;
   static_assert(kThreads % (kFewMaxTileRows / 4) == 0 && kFewMaxTileRows % 64 == 0, "epilogue mapping");
-  __shared__ uint32_t tab32[32];
-  __shared__ uint2 pairs[kPairMask != 0 ? Fmt::kPairEntries : 1];
+  // the tables first in LDS (largest alignments): their addresses then fit
+  // the 16-bit offset field of the lookups, which need no base add
+  __shared__ __attribute__((aligned(4096))) uint32_t tab32[32];
+  __shared__ __attribute__((aligned(4096))) uint2 pairs[kPairMask != 0 ? Fmt::kPairEntries : 1];
   __shared__ __attribute__((aligned(16))) int32_t sums[kFewSumWords];
   __shared__ float sxs[kFewMaxTok];
   __shared__ float sws[kFewMaxTileRows];

@@ -151,8 +151,10 @@ constexpr int kGemmLargeRows = 256, kGemmLargeTok = 128;
 constexpr int kGemmSmallRows = 128, kGemmSmallTok = 128;
 constexpr int kGemmSkinnyRows = 256, kGemmSkinnyTok = 16;
 // Few-token kernel (every problem m <= 16, k <= 8192): a row tile of
-// min(R, 4 R / S) rows with all of k (R = kFewMaxTileRows), S = k slices of
-// 512 weights rounded up to a power of two.
+// R = kFewMaxTileRows rows with all of k, for every k; S = k slices of 512
+// weights rounded up to a power of two (at most 16).  Each wave keeps its
+// slices of x in registers for the whole tile, so the longer the tile, the
+// less x is reread per row.
 constexpr int kFewMaxTok = 16;
 constexpr int kFewMaxGroups = 64;
 constexpr int kFewWaves = 8;
@@ -165,10 +167,7 @@ inline constexpr int few_slices(int groups) {
 #define SHERRY_FEW_TILE_ROWS 512
 #endif
 constexpr int kFewMaxTileRows = SHERRY_FEW_TILE_ROWS;
-inline constexpr int few_tile_rows(int groups) {
-  return 4 * kFewMaxTileRows / few_slices(groups) < kFewMaxTileRows ? 4 * kFewMaxTileRows / few_slices(groups)
-                                                                     : kFewMaxTileRows;
-}
+inline constexpr int few_tile_rows(int) { return kFewMaxTileRows; }
 // Large tiles are used when they give at least this many workgroups.
 #ifndef SHERRY_LARGE_TILE_MIN_GROUPS
 #define SHERRY_LARGE_TILE_MIN_GROUPS 256
