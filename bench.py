@@ -375,7 +375,8 @@ def peak_probes(torch, sherry):
     ticks = torch.zeros(blocks, 4, dtype=torch.int64, device=dev)
     clock = {}
     for name, mode in (("mfma", sherry.PROBE_MFMA), ("dot4", sherry.PROBE_DOT4), ("same_wave", sherry.PROBE_SAME_WAVE),
-                       ("alt_waves", sherry.PROBE_ALT_WAVES), ("mfma32", sherry.PROBE_MFMA32)):
+                       ("alt_waves", sherry.PROBE_ALT_WAVES), ("mfma32", sherry.PROBE_MFMA32), ("alu", sherry.PROBE_ALU),
+                       ("same_wave_alu", sherry.PROBE_SAME_ALU)):
         mean_ms, _ = time_launches(torch, lambda: sherry.probe_rates(mode, iters, blocks, sink), 10, 2, settle_ms=20)
         t[name] = mean_ms
         if name in ("mfma", "dot4", "mfma32"):  # one more launch, recording the shader clock (s_memtime / 100 MHz)
@@ -400,6 +401,8 @@ def peak_probes(torch, sherry):
     out["ms"] = {k: round(v, 4) for k, v in t.items()}
     out["overlap_same_wave"] = round(t["same_wave"] / (t["mfma"] + t["dot4"]), 3)  # 16 x 16 x 64 products
     out["overlap_alt_waves"] = round(2 * t["alt_waves"] / (t["mfma"] + t["dot4"]), 3)
+    # matrix-core products beside plain 32-bit VALU operations (shift, mask, add) in the same wave
+    out["overlap_same_wave_alu"] = round(t["same_wave_alu"] / (t["mfma"] + t["alu"]), 3)
     return out
 
 

@@ -33,10 +33,14 @@ sherry_status sherry_probe_read(const void* src, size_t bytes, uint32_t* sink, h
  * sherry_probe_read.  If the two kinds of work overlap, the SAME_WAVE time
  * is close to the larger of the MFMA and DOT4 times; if not, to their sum. */
 enum { SHERRY_PROBE_MFMA = 0, SHERRY_PROBE_DOT4 = 1, SHERRY_PROBE_SAME_WAVE = 2, SHERRY_PROBE_ALT_WAVES = 3,
-       SHERRY_PROBE_MFMA32 = 4 };
+       SHERRY_PROBE_MFMA32 = 4, SHERRY_PROBE_ALU = 5, SHERRY_PROBE_SAME_ALU = 6 };
 /* SHERRY_PROBE_MFMA32: every wave, matrix cores only, as 2 independent
  * v_mfma_i32_32x32x32_i8 per iteration (the same 2 x 65536 ops per iteration
- * as the MFMA mode's four 16 x 16 x 64 products). */
+ * as the MFMA mode's four 16 x 16 x 64 products).
+ * SHERRY_PROBE_ALU: every wave, plain 32-bit VALU only: 16 independent
+ * chains of shift, mask and add per iteration (48 operations).
+ * SHERRY_PROBE_SAME_ALU: every wave issues both the MFMA mode's matrix-core
+ * work and the ALU mode's operations, interleaved. */
 sherry_status sherry_probe_rates(int32_t mode, int32_t iters, int32_t blocks, uint32_t* sink, hipStream_t stream);
 
 /* The rate probe with a clock record: thread 0 of workgroup b writes the

@@ -486,7 +486,8 @@ def test_probe_validation(lib):
     assert rd(A, 1000, A, None) == ESHAPE
     assert rd(A + 4, 1024, A, None) == EALIGN
     assert rd(A, 1024, A, None) == EDEVICE
-    assert rt(5, 10, 10, A, None) == EINVAL
+    assert rt(7, 10, 10, A, None) == EINVAL
+    assert rt(-1, 10, 10, A, None) == EINVAL
     assert rt(0, 0, 10, A, None) == EINVAL
     assert rt(0, 10, 0, A, None) == EINVAL
     assert rt(0, 10, 10, None, None) == EINVAL
@@ -495,7 +496,7 @@ def test_probe_validation(lib):
     rc = raw.sherry_probe_clock
     rc.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     assert rc(0, 10, 10, A, None, None) == EINVAL
-    assert rc(5, 10, 10, A, A, None) == EINVAL
+    assert rc(7, 10, 10, A, A, None) == EINVAL
     assert rc(0, 10, 10, A, A + 4, None) == EALIGN
     assert rc(0, 10, 10, A, A, None) == EDEVICE
 

@@ -1081,7 +1081,7 @@ def test_probes_and_bench_line(gpu_lib):
     sink = torch.zeros(256, dtype=torch.int32, device=DEV)
     buf = torch.ones(1 << 26, dtype=torch.int32, device=DEV)
     gpu_lib.probe_read(buf, sink)
-    for mode in range(5):
+    for mode in range(7):
         gpu_lib.probe_rates(mode, 64, 256, sink)
     torch.cuda.synchronize()
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))

@@ -40,10 +40,12 @@ def common_flags() -> list:
     ]
 
 
-# Per-source flags.  gemm.hip: MFMA accumulators in ordinary VGPRs (the
-# default AGPR form made the compiler copy the tiled kernel's accumulators
-# between the two register files on every k step).
-FILE_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source flags.  gemm.hip and probes.hip: MFMA accumulators in ordinary
+# VGPRs (the default AGPR form made the compiler copy the tiled kernel's
+# accumulators between the two register files on every k step, and the rate
+# probe's 4 products per iteration came with 20 such copies).
+FILE_FLAGS = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+              "probes.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str, save_temps: bool, objdir: str, defines) -> str:

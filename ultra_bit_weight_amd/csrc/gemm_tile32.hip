@@ -2,8 +2,8 @@
 // products: the 256-row x 128-token tile of the large tiling, as 4 waves of
 // 64 rows x 128 tokens (2 x 4 tiles of 32 x 32 int32 sums per wave, 128
 // registers) and, with 78 KB of LDS per workgroup, two workgroups per CU
-// (two waves per SIMD).  The 32 x 32 products run near the chip's int8 peak
-// per clock where the 16 x 16 ones reach about 60 % of it.  Weights: packed
+// (two waves per SIMD).  Half the product instructions of the 16 x 16 x 64
+// form for the same work, each at the same rate per operation.  Weights: packed
 // ternary blocks ("Sherry: Hardware-Efficient 1.25-Bit Ternary Quantization
 // via Fine-grained Sparsification", Abstract) and the 2-bit comparator (same
 // paper, Figure 2 caption).

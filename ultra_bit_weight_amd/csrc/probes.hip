@@ -41,7 +41,9 @@ __global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4_t
 
 // Per iteration and wave: 4 independent v_mfma_i32_16x16x64_i8 (4 x 32768
 // int8 ops) and/or 16 independent v_dot4_i32_i8 (16 x 512 ops); in the
-// MFMA32 mode 2 independent v_mfma_i32_32x32x32_i8 (the same 2 x 65536 ops).
+// MFMA32 mode 2 independent v_mfma_i32_32x32x32_i8 (the same 2 x 65536 ops);
+// in the ALU modes 16 independent chains of a shift, a mask and an add (48
+// plain 32-bit VALU operations, the kind a table decode issues).
 // With ticks: thread 0 of workgroup b records the shader-clock counter
 // (s_memtime) and the constant 100 MHz counter (s_memrealtime) before and
 // after its wave's loop in ticks[4 b .. 4 b + 3].
@@ -55,8 +57,10 @@ __global__ __launch_bounds__(kProbeThreads) void probe_rate_kernel(int iters, ui
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const bool alt = MODE == SHERRY_PROBE_ALT_WAVES;
-  const bool do_mfma = MODE == SHERRY_PROBE_MFMA || MODE == SHERRY_PROBE_SAME_WAVE || (alt && (wave & 1) == 0);
+  const bool do_mfma = MODE == SHERRY_PROBE_MFMA || MODE == SHERRY_PROBE_SAME_WAVE || MODE == SHERRY_PROBE_SAME_ALU ||
+                       (alt && (wave & 1) == 0);
   const bool do_valu = MODE == SHERRY_PROBE_DOT4 || MODE == SHERRY_PROBE_SAME_WAVE || (alt && (wave & 1) == 1);
+  const bool do_alu = MODE == SHERRY_PROBE_ALU || MODE == SHERRY_PROBE_SAME_ALU;
   v4i a = {lane, 3 * lane + 1, 5 * lane + 2, 7 * lane + 3};
   v4i b = {lane ^ 5, lane ^ 9, lane ^ 17, lane ^ 33};
   asm volatile("" : "+v"(a), "+v"(b));
@@ -79,6 +83,11 @@ __global__ __launch_bounds__(kProbeThreads) void probe_rate_kernel(int iters, ui
     if (do_valu) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) d[j] = __builtin_amdgcn_sdot4(a[j & 3], b[(j + 1) & 3], d[j], false);
+    }
+    if (do_alu) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        d[j] = static_cast<int>(((static_cast<uint32_t>(d[j]) >> (j + 1)) & 0x7Cu) + static_cast<uint32_t>(a[j & 3]));
     }
   }
   uint32_t h = 0;
@@ -103,7 +112,7 @@ __global__ __launch_bounds__(kProbeThreads) void probe_rate_kernel(int iters, ui
 sherry_status launch_rates(int32_t mode, int32_t iters, int32_t blocks, uint32_t* sink, uint64_t* ticks,
                            hipStream_t stream) {
   if (!sink) return SHERRY_EINVAL;
-  if (mode < SHERRY_PROBE_MFMA || mode > SHERRY_PROBE_MFMA32 || iters <= 0 || iters > (1 << 24) || blocks <= 0 ||
+  if (mode < SHERRY_PROBE_MFMA || mode > SHERRY_PROBE_SAME_ALU || iters <= 0 || iters > (1 << 24) || blocks <= 0 ||
       blocks > (1 << 20))
     return SHERRY_EINVAL;
   if (reinterpret_cast<uintptr_t>(sink) % 4 != 0 || reinterpret_cast<uintptr_t>(ticks) % 8 != 0) return SHERRY_EALIGN;
@@ -123,8 +132,14 @@ sherry_status launch_rates(int32_t mode, int32_t iters, int32_t blocks, uint32_t
     case SHERRY_PROBE_ALT_WAVES:
       hipLaunchKernelGGL(probe_rate_kernel<SHERRY_PROBE_ALT_WAVES>, grid, block, 0, stream, iters, sink, ticks);
       break;
-    default:
+    case SHERRY_PROBE_MFMA32:
       hipLaunchKernelGGL(probe_rate_kernel<SHERRY_PROBE_MFMA32>, grid, block, 0, stream, iters, sink, ticks);
+      break;
+    case SHERRY_PROBE_ALU:
+      hipLaunchKernelGGL(probe_rate_kernel<SHERRY_PROBE_ALU>, grid, block, 0, stream, iters, sink, ticks);
+      break;
+    default:
+      hipLaunchKernelGGL(probe_rate_kernel<SHERRY_PROBE_SAME_ALU>, grid, block, 0, stream, iters, sink, ticks);
       break;
   }
   return hipGetLastError() == hipSuccess ? SHERRY_OK : SHERRY_ELAUNCH;

@@ -275,7 +275,7 @@ def tern2_pack(w: torch.Tensor, scale_dtype=torch.float16):
     return codes, scales
 
 
-PROBE_MFMA, PROBE_DOT4, PROBE_SAME_WAVE, PROBE_ALT_WAVES, PROBE_MFMA32 = 0, 1, 2, 3, 4
+PROBE_MFMA, PROBE_DOT4, PROBE_SAME_WAVE, PROBE_ALT_WAVES, PROBE_MFMA32, PROBE_ALU, PROBE_SAME_ALU = 0, 1, 2, 3, 4, 5, 6
 # int8 ops per wave and iteration of the rate probe: 4 matrix-core products
 # of 16 x 16 x 64, 16 v_dot4 over 64 lanes
 PROBE_MFMA_OPS, PROBE_DOT4_OPS = 4 * 2 * 16 * 16 * 64, 16 * 2 * 4 * 64
