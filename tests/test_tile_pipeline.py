@@ -15,12 +15,12 @@ import pytest
 
 GROUP = 128            # weights per group: k advances one group per step
 LDS_BYTES = 160 * 1024
-UNROLL = 12            # steps per loop iteration of the kernel
-CODE_SLOTS = 3
-DEPTH_CAP = 3          # the kernel's x ring depth cap
+UNROLL = 8             # steps per loop iteration of the kernel
+CODE_SLOTS = 2
+DEPTH = 2              # x ring
 
 # format: groups per code stage P, 16-byte head chunks per row HC, tail words
-FORMATS = {"sherry": dict(P=2, HC=2, tail=True), "tern2": dict(P=1, HC=2, tail=False)}
+FORMATS = {"sherry": dict(P=4, HC=4, tail=True), "tern2": dict(P=2, HC=4, tail=False)}
 # tiling: waves along rows WR, along tokens WC, 16-token tiles per wave UT,
 # rows per wave, workgroups per CU
 TILINGS = {"large": dict(WR=4, WC=1, UT=8, rows=64, wgcu=2),
@@ -37,24 +37,20 @@ def config(fmt, tiling):
     TX = xbytes // (16 * 64)
     P, HC = f["P"], f["HC"]
     stage = R * (16 * HC + (4 * P if f["tail"] else 0))
-    fit = (LDS_BYTES // t["wgcu"] - 1024 - CODE_SLOTS * stage) // xbytes
-    D = min(fit, DEPTH_CAP, P + 1)
     TH = R * HC // 64
     TT = R * P // 64 if f["tail"] else 0
-    CPW = (TH + TT) // (P * W)
-    assert CPW * P * W == TH + TT and CPW >= 1
-    assert D >= 2 and UNROLL % D == 0 and UNROLL % (CODE_SLOTS * P) == 0 and D <= P + 1
-    lds = 1024 + D * xbytes + CODE_SLOTS * stage
+    CPW = (TH + TT) // ((P // 2) * W)
+    assert CPW * (P // 2) * W == TH + TT and CPW >= 1
+    assert P % 2 == 0 and UNROLL % (CODE_SLOTS * P) == 0 and UNROLL % DEPTH == 0
+    lds = 1024 + DEPTH * xbytes + CODE_SLOTS * stage
     assert lds <= LDS_BYTES // t["wgcu"], "the tiling's LDS fits its workgroups per CU"
-    return dict(W=W, TX=TX, NX=math.ceil(TX / W), P=P, D=D, CPW=CPW, ops=TX // W + CPW)
+    return dict(W=W, TX=TX, NX=math.ceil(TX / W), P=P, CPW=CPW, rows=R, stage_rows=TH + TT, wait=0)
 
 
 def simulate(cfg, G):
-    """Issue order of every wave; returns the checks' failures (empty: safe)."""
-    W, TX, NX, P, D, CPW, ops = (cfg[k] for k in ("W", "TX", "NX", "P", "D", "CPW", "ops"))
-    PC = P * CPW
-    late = (D - 1) * CPW
-    assert late <= PC
+    """Issue order of every wave; returns the checks' failures (empty: safe).
+    cfg["wait"]: the outstanding copies the barrier wait allows (the kernel: 0)."""
+    W, TX, NX, P, CPW = (cfg[k] for k in ("W", "TX", "NX", "P", "CPW"))
     issued = [[] for _ in range(W)]   # per wave: (kind, index) in issue order
     retired = [0] * W                 # per wave: number of its oldest ops retired
 
@@ -71,39 +67,40 @@ def simulate(cfg, G):
         return all((kind, idx) not in issued[w][retired[w]:] for w in range(W))
 
     failures = []
-    # prologue: code stages 0 and 1, x steps 0 .. D - 2
+    # prologue: code stage 0 and the x tile of step 0, then the wait and the
+    # barrier; every wave then decodes step 0 from stage 0
     for w in range(W):
-        issued[w] += [("code", 0)] * PC + [("code", 1)] * (PC - late)
-        for b in range(D - 1):
-            copy_x(w, b)
-            issued[w] += [("code", 1)] * CPW
-        wait(w, PC - late + (D - 1) * ops)
-    # barrier, then every wave decodes step 0 from stage 0
-    if not done("code", 0):
-        failures.append("prologue: stage 0 not landed")
-    # which buffers are being read: step s reads x slot s % D and (decoding
-    # step s + 1) code slot ((s + 1) // P) % 3
+        issued[w] += [("code", 0)] * ((P // 2) * CPW)
+        copy_x(w, 0)
+        wait(w, cfg["wait"])
+    if not done("code", 0) or not done("x", 0):
+        failures.append("prologue: stage 0 or step 0 not landed")
+    # step s reads x slot s % 2 and (decoding step s + 1) code slot
+    # ((s + 1) // P) % 2
     steps = -(-G // UNROLL) * UNROLL
     for s in range(steps):
         for w in range(W):
-            wait(w, ops * (D - 2))
+            wait(w, cfg["wait"])
         # barrier: every wave has retired what its wait covers
         if s < G:
             if not done("x", s):
                 failures.append(f"step {s}: x not landed")
             if s + 1 < G and not done("code", (s + 1) // P):
                 failures.append(f"step {s}: code stage {(s + 1) // P} not landed")
-        # copies issued after the barrier: x of step s + D - 1 into the slot
-        # of step s - 1, and part of stage s // P + 2 into the slot of stage
-        # s // P - 1
-        xs_slot, cs_slot = (s + D - 1) % D, (s // P + 2) % CODE_SLOTS
-        if s < G and xs_slot == s % D:
+        # copies issued after the barrier: x of step s + 1 into the slot of
+        # step s - 1, and (first P / 2 steps of a stage) part of stage
+        # s // P + 1 into the slot of stage s // P - 1
+        if s < G and (s + 1) % 2 == s % 2:
             failures.append(f"step {s}: x copy into the slot being read")
-        if s + 1 < G and cs_slot == ((s + 1) // P) % CODE_SLOTS:
+        code_copy = s % P < P // 2
+        if code_copy and s + 1 < G and (s // P + 1) % 2 == ((s + 1) // P) % 2:
             failures.append(f"step {s}: code copy into the stage being decoded")
+        if code_copy and s < G and s % P != 0 and (s // P + 1) % 2 == (s // P) % 2:
+            failures.append(f"step {s}: code copy into the stage in use")
         for w in range(W):
-            copy_x(w, s + D - 1)
-            issued[w] += [("code", s // P + 2)] * CPW
+            copy_x(w, s + 1)
+            if code_copy:
+                issued[w] += [("code", s // P + 1)] * CPW
     return failures
 
 
@@ -115,17 +112,19 @@ def test_tile_pipeline_is_safe(fmt, tiling, G):
     assert simulate(cfg, G) == []
 
 
-def test_tile_pipeline_model_catches_a_short_wait():
-    """The model is not vacuous: one outstanding copy more at the barrier than
-    the kernel allows leaves a step reading a tile still in flight."""
-    cfg = dict(config("sherry", "large"))
-    cfg["ops"] += 1
+@pytest.mark.parametrize("fmt", sorted(FORMATS))
+def test_tile_pipeline_model_catches_a_short_wait(fmt):
+    """The model is not vacuous: a barrier that leaves the wave's youngest
+    copies in flight lets a step read a tile or a stage still in flight."""
+    cfg = dict(config(fmt, "large"))
+    cfg["wait"] = cfg["NX"]
     assert simulate(cfg, 16) != []
 
 
 def test_tile_configs():
-    """The ring depths and copy counts of the kept tilings."""
+    """Copy counts of the kept tilings: per wave and step, 4 x-tile copies and
+    (in the first half of a stage) 4 code copies."""
     big = config("sherry", "large")
-    assert (big["D"], big["TX"], big["CPW"], big["ops"]) == (3, 16, 2, 6)
+    assert (big["TX"], big["CPW"]) == (16, 4)
     t2 = config("tern2", "large")
-    assert (t2["D"], t2["TX"], t2["CPW"], t2["ops"]) == (2, 16, 2, 6)
+    assert (t2["TX"], t2["CPW"]) == (16, 4)

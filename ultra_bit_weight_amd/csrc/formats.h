@@ -106,13 +106,33 @@ struct Sherry3of4 {
     return v4i{static_cast<int>(lds_u32(tab, o[0])), static_cast<int>(lds_u32(tab, o[1])),
                static_cast<int>(lds_u32(tab, o[2])), static_cast<int>(lds_u32(tab, o[3]))};
   }
+  // The same half from the pair table (entry c0 | c1 << 5 holds the eight
+  // weights of two consecutive blocks): the half's four codes are two 10-bit
+  // fields of the window, read with two 8-byte lookups.
+  __device__ __forceinline__ static v4i frag_pairs(const uint32_t* w, int q, int s, const uint2* pairs) {
+    const uint32_t sh = (8u * static_cast<uint32_t>(q)) & 31u;     // 40q mod 32
+    const uint32_t lo = __builtin_amdgcn_alignbit(w[1], w[0], sh);  // window bits 0..31
+    constexpr uint32_t m = 0x3FFu << 3;                              // index * 8 = byte offset
+    uint32_t o0, o1;
+    if (s == 0) {
+      o0 = (lo << 3) & m;  // window bits 0..9
+      o1 = (lo >> 7) & m;  // 10..19
+    } else {
+      const uint32_t hi = w[1] >> sh;                  // window bits 32..
+      o0 = (lo >> 17) & m;                             // 20..29
+      o1 = __builtin_amdgcn_alignbit(hi, lo, 27) & m;  // 30..39
+    }
+    const uint2 a = lds_u64(pairs, o0);
+    const uint2 b = lds_u64(pairs, o1);
+    return v4i{static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(b.x), static_cast<int>(b.y)};
+  }
   // Tiled GEMM: codes reach LDS in stages of kTileP groups per row, as
   // kTileHC 16-byte head chunks (words 0-3 of each group, contiguous in the
   // row) and, with kTileTail, kTileP tail words (word 4 of each group).
   // Word offsets from the row start (groups past the row end clamp to the
   // last group: such words are copied but never used):
-  static constexpr int kTileP = 2;
-  static constexpr int kTileHC = 2;
+  static constexpr int kTileP = 4;
+  static constexpr int kTileHC = 4;
   static constexpr bool kTileTail = true;
   __device__ __forceinline__ static int head_word(int G, int g0, int c) { return 4 * min(g0 + c, G - 1); }
   __device__ __forceinline__ static int tail_word(int G, int g0, int j) { return 4 * G + min(g0 + j, G - 1); }
@@ -219,9 +239,9 @@ struct Tern2 {
                static_cast<int>(__builtin_amdgcn_perm(0u, 0xFF000100u, (x >> 4) & 0x03030303u)),
                static_cast<int>(__builtin_amdgcn_perm(0u, 0xFF000100u, (x >> 6) & 0x03030303u))};
   }
-  // Tiled GEMM stages: 1 group per row (2 chunks of 16 bytes), no tail.
-  static constexpr int kTileP = 1;
-  static constexpr int kTileHC = 2;
+  // Tiled GEMM stages: 2 groups per row (4 chunks of 16 bytes), no tail.
+  static constexpr int kTileP = 2;
+  static constexpr int kTileHC = 4;
   static constexpr bool kTileTail = false;
   __device__ __forceinline__ static int head_word(int G, int g0, int c) {
     return 8 * min(g0 + (c >> 1), G - 1) + 4 * (c & 1);

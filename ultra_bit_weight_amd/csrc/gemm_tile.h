@@ -14,41 +14,38 @@
 namespace sherry {
 namespace {
 
-// Steps of x and code words the tiled kernel keeps in flight (LDS ring depth;
-// 3 measured faster than 4 on the 1B layer at M = 2048).
-#ifndef SHERRY_TILE_DEPTH
-#define SHERRY_TILE_DEPTH 3
-#endif
-constexpr int kTileDepth = SHERRY_TILE_DEPTH;
-static_assert(kTileDepth >= 2 && kTileDepth <= 4, "tile pipeline depth");
-
 // Tiled kernel for many tokens.  A workgroup of WR x WC waves computes a
 // (64 WR weight rows) x (16 UT WC tokens) tile of Y, stepping k by one
 // 128-weight group.  Wave w owns rows 64 (w % WR) .. + 64 and tokens
 // 16 UT (w / WR) .. + 16 UT as 4 x UT MFMA tiles.
 //   * Everything the loop reads from memory is copied by the memory system
 //     straight into LDS (global_load_lds, no staging registers):
-//       - the tokens' int8 tile of a step, D steps ahead, into a ring of D
+//       - the tokens' int8 tile of a step, one step ahead, into a ring of 2
 //         buffers.  Within a token's 128 bytes the 16-byte chunk c sits at
 //         position c ^ ((token >> 1) & 7), so the B-fragment reads of 16
 //         consecutive tokens hit 16 different bank groups;
-//       - the codes in stages of P groups, two stages ahead, into a ring of 3
+//       - the codes in stages of P groups, one stage ahead, into a ring of 2
 //         buffers: per row the P groups' HC 16-byte head chunks (contiguous
-//         in the row) and tail words.  Chunk c of a row sits at position
-//         c ^ ((row >> 2) & (HC - 1)), which spreads the word reads of
-//         consecutive rows over the banks.  A stage's copies are spread
-//         evenly over the P steps of the stage two earlier.
+//         in the row, a 64-byte run) and their tail words (a 4 P-byte run).
+//         Chunk c of a row sits at position c ^ ((row >> 2) & (HC - 1)),
+//         which spreads the word reads of consecutive rows over the banks.
+//         A stage's copies are issued in the first P / 2 steps of the stage
+//         before it.  Long runs per row matter: a copy instruction reads
+//         64 lanes x 16 (or 4) bytes, and the rows of a tile are a row of
+//         codes apart, so the instruction touches as many cache lines as
+//         rows -- 16 here, against 32 for stages of 2 groups.
 //   * Lane (i, q) decodes, for each of its 4 row tiles t (row 16 t + i), part q
 //     of the group (blocks 8q .. 8q+7, two code words) straight into two A
 //     fragments: half s takes blocks 8q + 4s .. 8q + 4s + 3, i.e. k bytes
-//     32q + 16s .. + 16, which is the B fragment it reads from LDS.
-//   * One barrier per step.  Every vector-memory operation in the loop is one
-//     of these copies, a fixed number per wave and step, so before the
-//     barrier each wave waits (vmcnt) for its copies of the step's x tile;
-//     the copies of the step's code stage are older, so they have landed
-//     too.  After the barrier the whole step is in LDS, and the buffers of
-//     the finished step (and, at a stage start, stage) are free for the
-//     copies issued next.
+//     32q + 16s .. + 16, which is the B fragment it reads from LDS.  The
+//     next step's A fragments are expanded while the step's products run.
+//   * One barrier per step, after each wave has waited for all of its copies
+//     (vmcnt(0)).  A copy issued in step s has then landed by the barrier of
+//     step s + 1: the x tile of step s + 1 is read in step s + 1, and a code
+//     stage, whose copies end P / 2 steps before its first step, is first
+//     read in the step before its first (to expand that step's fragments).
+//     A copy only ever goes to the buffer of a step or stage whose last
+//     read came before the barrier it follows.
 //
 // With M32 the products run as v_mfma_i32_32x32x32_i8 instead: lane (r, h) = (l % 32, l / 32) of a wave takes row or token r of a
 // 32-wide tile and, in substep s of four, the 16 k bytes of x chunk
@@ -78,31 +75,39 @@ static_assert(TileSmall::kRows == kGemmSmallRows && TileSmall::kTok == kGemmSmal
 static_assert(TileLarge::kRows == kGemmLargeRows && TileLarge::kTok == kGemmLargeTok, "large tiling");
 static_assert(TileSkinny::kRows == kGemmSkinnyRows && TileSkinny::kTok == kGemmSkinnyTok, "skinny tiling");
 
-constexpr int kCodeSlots = 3;  // code stages in LDS: in use, next, in flight
-constexpr int kTileUnroll = 12;  // steps per loop iteration: a multiple of D and of 3 P
+constexpr int kCodeSlots = 2;  // code stages in LDS: in use, next
+constexpr int kTileDepth = 2;  // x steps in LDS: in use, next
+constexpr int kTileUnroll = 8;  // steps per loop iteration: two stages of 4 (3:4 codes) or four of 2 (2-bit)
 
-// Code bytes of one stage and x-ring depth: kTileDepth, or fewer steps if the
-// CU's share of the 160 KB of LDS cannot hold them next to the code ring.
+// Code bytes of one stage; the rings must fit the CU's share of the LDS.
 template <class Fmt, class C>
 constexpr int code_stage_bytes() {
   return C::kRows * (16 * Fmt::kTileHC + (Fmt::kTileTail ? 4 * Fmt::kTileP : 0));
 }
-// The depth is also at most P + 1: a stage's last copies are then issued
-// before the x copies of its first step, so waiting for those covers them.
+// 16 x 16 products on table-decoded codes expand two codes per LDS read
+// from a 1024-entry pair table (8 KB, in place of the 32-entry table):
+// half the lookups and their address arithmetic.
 template <class Fmt, class C>
-constexpr int tile_depth() {
-  constexpr int fit = (160 * 1024 / C::kWgPerCu - 1024 - kCodeSlots * code_stage_bytes<Fmt, C>()) / C::kXBytes;
-  constexpr int cap = kTileDepth < Fmt::kTileP + 1 ? kTileDepth : Fmt::kTileP + 1;
-  return fit < cap ? fit : cap;
+constexpr bool tile_pairs() {
+  return Fmt::kTableDecode && !C::kM32;
+}
+template <class Fmt, class C>
+constexpr int tile_table_bytes() {
+  return tile_pairs<Fmt, C>() ? 8 * Fmt::kPairEntries : 1024;
+}
+template <class Fmt, class C>
+constexpr bool tile_lds_fits() {
+  return tile_table_bytes<Fmt, C>() + kTileDepth * C::kXBytes + kCodeSlots * code_stage_bytes<Fmt, C>() <=
+         160 * 1024 / C::kWgPerCu;
 }
 
 template <class Fmt, class C>
 __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int tile_m) {
-  constexpr int D = tile_depth<Fmt, C>();
-  static_assert(D >= 2 && kTileUnroll % D == 0, "x ring depth");
+  constexpr int D = kTileDepth;
+  static_assert(tile_lds_fits<Fmt, C>(), "LDS rings");
   constexpr int P = Fmt::kTileP;
   constexpr int HC = Fmt::kTileHC;
-  static_assert(kTileUnroll % (kCodeSlots * P) == 0 && D <= P + 1, "code stage cadence");
+  static_assert(P % 2 == 0 && kTileUnroll % (kCodeSlots * P) == 0 && kTileUnroll % D == 0, "code stage cadence");
   constexpr int UT = C::UT;
   constexpr int W = C::kWaves;
   constexpr int R = C::kRows;
@@ -110,34 +115,39 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int til
   constexpr int TX = C::kXCopies;
   constexpr int NX = (TX + W - 1) / W;
   // code copies per stage: head copies (64 chunk slots each) then tail copies
-  // (64 words each); every wave issues CPW of them in every step
+  // (64 words each); every wave issues CPW of them in each of the first P / 2
+  // steps of the stage before
   constexpr int TH = R * HC / 64;
   constexpr int TT = Fmt::kTileTail ? R * P / 64 : 0;
-  constexpr int CPW = (TH + TT) / (P * W);
-  static_assert(CPW * P * W == TH + TT && CPW >= 1, "code copies per wave and step");
-  constexpr int kOpsPerStep = TX / W + CPW;  // vector-memory operations per wave and step, at least
+  constexpr int CPW = (TH + TT) / ((P / 2) * W);
+  static_assert(CPW * (P / 2) * W == TH + TT && CPW >= 1, "code copies per wave and step");
   constexpr int XV = C::kXBytes / 16;
   constexpr int HV = R * HC;
   constexpr int TV = Fmt::kTileTail ? R * P : 1;
   // the code table first in LDS (largest alignment): its address then fits
   // the 16-bit offset field of the lookups
-  __shared__ __attribute__((aligned(1024))) uint32_t tab[32];
+  constexpr bool PT = tile_pairs<Fmt, C>();
+  __shared__ __attribute__((aligned(1024))) uint32_t tab[PT ? 1 : 32];
+  __shared__ __attribute__((aligned(16))) uint2 ptab[PT ? Fmt::kPairEntries : 1];
   // one LDS array per ring slot and kind: distinct objects let the compiler
   // see that reading one slot does not depend on the copies to the others
-  __shared__ u32x4_t xt0[XV], xt1[XV], xt2[D > 2 ? XV : 1], xt3[D > 3 ? XV : 1];
-  __shared__ u32x4_t hd0[HV], hd1[HV], hd2[HV];
-  __shared__ uint32_t tl0[TV], tl1[TV], tl2[TV];
-  auto xbuf = [&](int slot) -> u32x4_t* {
-    return slot == 0 ? xt0 : slot == 1 ? xt1 : slot == 2 ? xt2 : xt3;
-  };
-  auto hbuf = [&](int slot) -> u32x4_t* { return slot == 0 ? hd0 : slot == 1 ? hd1 : hd2; };
-  auto tbuf = [&](int slot) -> uint32_t* { return slot == 0 ? tl0 : slot == 1 ? tl1 : tl2; };
+  __shared__ u32x4_t xt0[XV], xt1[XV];
+  __shared__ u32x4_t hd0[HV], hd1[HV];
+  __shared__ uint32_t tl0[TV], tl1[TV];
+  auto xbuf = [&](int slot) -> u32x4_t* { return slot == 0 ? xt0 : xt1; };
+  auto hbuf = [&](int slot) -> u32x4_t* { return slot == 0 ? hd0 : hd1; };
+  auto tbuf = [&](int slot) -> uint32_t* { return slot == 0 ? tl0 : tl1; };
   // LDS byte addresses of the slots (copy destinations are these plus a
   // constant, so no generic pointer is live across the loop)
-  const uint32_t xlds[4] = {lds_addr(xt0), lds_addr(xt1), lds_addr(xt2), lds_addr(xt3)};
-  const uint32_t hlds[3] = {lds_addr(hd0), lds_addr(hd1), lds_addr(hd2)};
-  const uint32_t tlds[3] = {lds_addr(tl0), lds_addr(tl1), lds_addr(tl2)};
-  Fmt::init_table(tab, threadIdx.x);
+  const uint32_t xlds[2] = {lds_addr(xt0), lds_addr(xt1)};
+  const uint32_t hlds[2] = {lds_addr(hd0), lds_addr(hd1)};
+  const uint32_t tlds[2] = {lds_addr(tl0), lds_addr(tl1)};
+  if constexpr (PT) {
+    for (int e = threadIdx.x; e < Fmt::kPairEntries; e += C::kThreads)
+      ptab[e] = make_uint2(decode_i8x4(static_cast<uint32_t>(e) & 31u), decode_i8x4(static_cast<uint32_t>(e) >> 5));
+  } else {
+    Fmt::init_table(tab, threadIdx.x);
+  }
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -202,11 +212,14 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int til
       lds_copy4(cbase, 4u * w, tlds[slot] + 256u * (c - TH));
     }
   };
-  // in step s: this wave's share (part s % P) of the copies of stage s / P + 2
+  // in step s (unrolled position b): in the first P / 2 steps of a stage,
+  // this wave's share (part s % P) of the copies of stage s / P + 1
   auto copy_code_part = [&](int s, int b) {
+    if (b % P < P / 2) {
 #pragma unroll
-    for (int j = 0; j < CPW; ++j)
-      copy_code(s / P + 2, (b / P + 2) % kCodeSlots, (b % P) * (CPW * W) + CPW * wave + j);
+      for (int j = 0; j < CPW; ++j)
+        copy_code(s / P + 1, (b / P + 1) % kCodeSlots, (b % P) * (CPW * W) + CPW * wave + j);
+    }
   };
 
   constexpr bool M32 = C::kM32;
@@ -268,7 +281,12 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int til
 #pragma unroll
       for (int s = 0; s < AS; ++s)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) an[s][t] = Fmt::frag(w[t], q, s, tab);
+        for (int t = 0; t < 4; ++t) {
+          if constexpr (PT)
+            an[s][t] = Fmt::frag_pairs(w[t], q, s, ptab);
+          else
+            an[s][t] = Fmt::frag(w[t], q, s, tab);
+        }
     }
   };
   // the products of a step: A from an[][], B from x slot xs
@@ -298,58 +316,36 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int til
       }
     }
   };
-  // Wait until this wave's x copies of step k landed (the copies of the D - 2
-  // younger steps may still be in flight), then the barrier.  The empty asm
-  // statements keep the compiler from moving memory accesses across.
+  // Wait until all of this wave's copies landed, then the barrier.  The empty
+  // asm statements keep the compiler from moving memory accesses across.
   auto step_barrier = [&]() {
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kOpsPerStep * (D - 2)));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
 
-  // prologue: code stages 0 and 1, x steps 0 .. D - 2.  As in the loop, CPW
-  // code copies follow the x copies of each step, so that the wait count of
-  // the barriers holds from step 0 on: after a step's x copies every wave has
-  // issued at least kOpsPerStep * (D - 2) + CPW more operations by the
-  // barrier that needs them.  A wave's copies of one stage are copies
-  // wave + W t, t < P CPW.
-  constexpr int PC = P * CPW;
-  constexpr int late = (D - 1) * CPW;  // stage-1 copies after the x copies
-  static_assert(late <= PC, "prologue code copies");
+  // prologue: code stage 0 and the x tile of step 0, landed and published
+  // before the first decode (the barrier also covers the code table)
+  constexpr int PC = (P / 2) * CPW;  // a wave's copies of one stage
 #pragma unroll
   for (int t = 0; t < PC; ++t) copy_code(0, 0, wave + W * t);
-#pragma unroll
-  for (int t = 0; t < PC - late; ++t) copy_code(1, 1, wave + W * t);
-#pragma unroll
-  for (int b = 0; b + 1 < D; ++b) {
-    copy_x(b, b);
-#pragma unroll
-    for (int j = 0; j < CPW; ++j) copy_code(1, 1, wave + W * (PC - late + CPW * b + j));
-  }
-  // Code stage 0 must be in LDS before the first decode: each wave waits for
-  // its copies of it (its oldest operations; at least PC - late + (D - 1)
-  // (TX / W + CPW) were issued after them), then the barrier (which also
-  // covers the code table).
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(PC - late + (D - 1) * kOpsPerStep));
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
+  copy_x(0, 0);
+  step_barrier();
   decode(0, 0);
   for (int g = 0; g < G; g += kTileUnroll) {
 #pragma unroll
     for (int b = 0; b < kTileUnroll; ++b) {
-      // step g + b: x in slot b % D, codes of stage (g + b) / P in code slot
-      // (b / P) % 3; after the barrier the finished step's x slot is refilled
-      // with step g + b + D - 1, and part of stage (g + b) / P + 2 is copied
+      // step g + b: x in slot b % 2, codes of stage (g + b) / P in code slot
+      // (b / P) % 2; after the barrier the finished step's x slot is refilled
+      // with step g + b + 1, and part of stage (g + b) / P + 1 is copied
       step_barrier();
-      copy_x(g + b + D - 1, (b + D - 1) % D);
+      copy_x(g + b + 1, (b + 1) % D);
       copy_code_part(g + b, b);
       if (g + b < G) {
         products(b % D);
-        decode(((b + 1) / P) % kCodeSlots, (b + 1) % P);  // step g + b + 1 (kTileUnroll is a multiple of 3 P)
+        decode(((b + 1) / P) % kCodeSlots, (b + 1) % P);  // step g + b + 1 (kTileUnroll is a multiple of 2 P)
       }
     }
   }
