@@ -106,36 +106,17 @@ struct Sherry3of4 {
     return v4i{static_cast<int>(lds_u32(tab, o[0])), static_cast<int>(lds_u32(tab, o[1])),
                static_cast<int>(lds_u32(tab, o[2])), static_cast<int>(lds_u32(tab, o[3]))};
   }
-  // The same half from the pair table (entry c0 | c1 << 5 holds the eight
-  // weights of two consecutive blocks): the half's four codes are two 10-bit
-  // fields of the window, read with two 8-byte lookups.
-  __device__ __forceinline__ static v4i frag_pairs(const uint32_t* w, int q, int s, const uint2* pairs) {
-    const uint32_t sh = (8u * static_cast<uint32_t>(q)) & 31u;     // 40q mod 32
-    const uint32_t lo = __builtin_amdgcn_alignbit(w[1], w[0], sh);  // window bits 0..31
-    constexpr uint32_t m = 0x3FFu << 3;                              // index * 8 = byte offset
-    uint32_t o0, o1;
-    if (s == 0) {
-      o0 = (lo << 3) & m;  // window bits 0..9
-      o1 = (lo >> 7) & m;  // 10..19
-    } else {
-      const uint32_t hi = w[1] >> sh;                  // window bits 32..
-      o0 = (lo >> 17) & m;                             // 20..29
-      o1 = __builtin_amdgcn_alignbit(hi, lo, 27) & m;  // 30..39
-    }
-    const uint2 a = lds_u64(pairs, o0);
-    const uint2 b = lds_u64(pairs, o1);
-    return v4i{static_cast<int>(a.x), static_cast<int>(a.y), static_cast<int>(b.x), static_cast<int>(b.y)};
-  }
   // Tiled GEMM: codes reach LDS in stages of kTileP groups per row, as
   // kTileHC 16-byte head chunks (words 0-3 of each group, contiguous in the
   // row) and, with kTileTail, kTileP tail words (word 4 of each group).
-  // Word offsets from the row start (groups past the row end clamp to the
-  // last group: such words are copied but never used):
   static constexpr int kTileP = 4;
   static constexpr int kTileHC = 4;
   static constexpr bool kTileTail = true;
-  __device__ __forceinline__ static int head_word(int G, int g0, int c) { return 4 * min(g0 + c, G - 1); }
-  __device__ __forceinline__ static int tail_word(int G, int g0, int j) { return 4 * G + min(g0 + j, G - 1); }
+  // Head chunk c of the stage of groups 0 .. P-1 is bytes 16 c of the row;
+  // the next stage's heads start kTileP kTileHeadBytes further, its tails
+  // 4 kTileP bytes further.
+  static constexpr int kTileHeadBytes = 16;  // head bytes per group (words 0-3)
+  __device__ __forceinline__ static uint32_t tile_tail_byte(int G, int j) { return 16u * G + 4u * j; }
   // Part q of group j of a stage from the LDS copy.  heads / tails point at
   // the first row of the lane's row tile; lh / lt are the lane's byte
   // offsets from there (its row), and chunk c of a row sits at position
@@ -243,10 +224,10 @@ struct Tern2 {
   static constexpr int kTileP = 2;
   static constexpr int kTileHC = 4;
   static constexpr bool kTileTail = false;
-  __device__ __forceinline__ static int head_word(int G, int g0, int c) {
-    return 8 * min(g0 + (c >> 1), G - 1) + 4 * (c & 1);
-  }
-  __device__ __forceinline__ static int tail_word(int, int, int) { return 0; }
+  // Head chunk c of the stage of groups 0 .. P-1 is bytes 16 c of the row
+  // (group c / 2, half c % 2); the next stage starts kTileP groups further.
+  static constexpr int kTileHeadBytes = 32;  // bytes per group
+  __device__ __forceinline__ static uint32_t tile_tail_byte(int, int) { return 0; }
   __device__ __forceinline__ static void stage_words(uint32_t* w, const char* heads, const char*, uint32_t lh,
                                                      uint32_t, int swz, int j, int q) {
     const uint32_t* c =

@@ -77,27 +77,22 @@ static_assert(TileSkinny::kRows == kGemmSkinnyRows && TileSkinny::kTok == kGemmS
 
 constexpr int kCodeSlots = 2;  // code stages in LDS: in use, next
 constexpr int kTileDepth = 2;  // x steps in LDS: in use, next
-constexpr int kTileUnroll = 8;  // steps per loop iteration: two stages of 4 (3:4 codes) or four of 2 (2-bit)
+constexpr int kTileUnroll = 8;
+#ifndef SHERRY_TILE_BPREF
+#define SHERRY_TILE_BPREF 0
+#endif
+#ifndef SHERRY_TILE_SPLIT
+#define SHERRY_TILE_SPLIT 0
+#endif  // steps per loop iteration: two stages of 4 (3:4 codes) or four of 2 (2-bit)
 
 // Code bytes of one stage; the rings must fit the CU's share of the LDS.
 template <class Fmt, class C>
 constexpr int code_stage_bytes() {
   return C::kRows * (16 * Fmt::kTileHC + (Fmt::kTileTail ? 4 * Fmt::kTileP : 0));
 }
-// 16 x 16 products on table-decoded codes expand two codes per LDS read
-// from a 1024-entry pair table (8 KB, in place of the 32-entry table):
-// half the lookups and their address arithmetic.
-template <class Fmt, class C>
-constexpr bool tile_pairs() {
-  return Fmt::kTableDecode && !C::kM32;
-}
-template <class Fmt, class C>
-constexpr int tile_table_bytes() {
-  return tile_pairs<Fmt, C>() ? 8 * Fmt::kPairEntries : 1024;
-}
 template <class Fmt, class C>
 constexpr bool tile_lds_fits() {
-  return tile_table_bytes<Fmt, C>() + kTileDepth * C::kXBytes + kCodeSlots * code_stage_bytes<Fmt, C>() <=
+  return 128 + kTileDepth * C::kXBytes + kCodeSlots * code_stage_bytes<Fmt, C>() <=
          160 * 1024 / C::kWgPerCu;
 }
 
@@ -126,9 +121,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int til
   constexpr int TV = Fmt::kTileTail ? R * P : 1;
   // the code table first in LDS (largest alignment): its address then fits
   // the 16-bit offset field of the lookups
-  constexpr bool PT = tile_pairs<Fmt, C>();
-  __shared__ __attribute__((aligned(1024))) uint32_t tab[PT ? 1 : 32];
-  __shared__ __attribute__((aligned(16))) uint2 ptab[PT ? Fmt::kPairEntries : 1];
+  __shared__ __attribute__((aligned(1024))) uint32_t tab[32];
   // one LDS array per ring slot and kind: distinct objects let the compiler
   // see that reading one slot does not depend on the copies to the others
   __shared__ u32x4_t xt0[XV], xt1[XV];
@@ -142,12 +135,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int til
   const uint32_t xlds[2] = {lds_addr(xt0), lds_addr(xt1)};
   const uint32_t hlds[2] = {lds_addr(hd0), lds_addr(hd1)};
   const uint32_t tlds[2] = {lds_addr(tl0), lds_addr(tl1)};
-  if constexpr (PT) {
-    for (int e = threadIdx.x; e < Fmt::kPairEntries; e += C::kThreads)
-      ptab[e] = make_uint2(decode_i8x4(static_cast<uint32_t>(e) & 31u), decode_i8x4(static_cast<uint32_t>(e) >> 5));
-  } else {
-    Fmt::init_table(tab, threadIdx.x);
-  }
+  Fmt::init_table(tab, threadIdx.x);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -196,20 +184,45 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int til
       if (c < TX) lds_copy16(xbase, opaque(xoff[j]) + g * kGroupWeights, xlds[slot] + 1024u * c);
     }
   };
-  // code copy c of stage `stage` (groups P stage ..), into code slot `slot`
-  auto copy_code = [&](int stage, int slot, int c) {
-    const int g0 = P * stage;
-    const int ln = static_cast<int>(opaque(static_cast<uint32_t>(lane)));
-    if (c < TH) {
-      const int sl = 64 * c + ln;  // chunk slot of the stage buffer
-      const int r = sl / HC;
-      const int chunk = (sl % HC) ^ ((r >> 2) & (HC - 1));
-      const uint32_t w = static_cast<uint32_t>(min(n0 + r, lastn)) * row_words + Fmt::head_word(G, g0, chunk);
-      lds_copy16(cbase, 4u * w, hlds[slot] + 1024u * c);
+  // Code copies: in each of the first P / 2 steps of a stage (part p), wave
+  // w issues copies c = p CPW W + CPW w + j (j < CPW) of the next stage:
+  // head copies (c < TH) take 64 16-byte chunk slots of the stage buffer,
+  // tail copies 64 words.  The lane's source offsets for stage 0 are fixed
+  // for the whole tile (rows past the matrix clamp to its last row); stage s
+  // adds s times a stage's run per row.  A stage that reaches past the row's
+  // last group reads the row's tail words or the next row instead (copied,
+  // never used), and every offset is clamped to the last chunk or word of
+  // the matrix, so no copy leaves it.
+  constexpr int CC = (P / 2) * CPW;  // a wave's copies of one stage
+  static_assert(TH % (CPW * W) == 0, "a part's copies are all head or all tail copies");
+  const uint32_t row_bytes = 4u * row_words;
+  uint32_t coff[CC];
+#pragma unroll
+  for (int p = 0; p < P / 2; ++p)
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) {
+      const int c = p * (CPW * W) + CPW * wave + j;
+      if (p * (CPW * W) < TH) {
+        const int sl = 64 * c + lane;  // chunk slot of the stage buffer
+        const int r = sl / HC;
+        const int chunk = (sl % HC) ^ ((r >> 2) & (HC - 1));
+        coff[p * CPW + j] = static_cast<uint32_t>(min(n0 + r, lastn)) * row_bytes + 16u * chunk;
+      } else {
+        const int sl = 64 * (c - TH) + lane;  // word slot of the stage's tails
+        coff[p * CPW + j] =
+            static_cast<uint32_t>(min(n0 + sl / P, lastn)) * row_bytes + Fmt::tile_tail_byte(G, sl % P);
+      }
+    }
+  const uint32_t end_bytes = static_cast<uint32_t>(d.n) * row_bytes;
+  // copy (p, j) of stage `stage` (groups P stage ..), into code slot `slot`
+  auto copy_code = [&](int stage, int slot, int p, int j) {
+    const int c = p * (CPW * W) + CPW * wave + j;
+    if (p * (CPW * W) < TH) {
+      const uint32_t o = coff[p * CPW + j] + static_cast<uint32_t>(stage) * (P * Fmt::kTileHeadBytes);
+      lds_copy16(cbase, min(o, end_bytes - 16u), hlds[slot] + 1024u * c);
     } else {
-      const int sl = 64 * (c - TH) + ln;  // word slot of the stage's tails
-      const uint32_t w = static_cast<uint32_t>(min(n0 + sl / P, lastn)) * row_words + Fmt::tail_word(G, g0, sl % P);
-      lds_copy4(cbase, 4u * w, tlds[slot] + 256u * (c - TH));
+      const uint32_t o = coff[p * CPW + j] + static_cast<uint32_t>(stage) * (4 * P);
+      lds_copy4(cbase, min(o, end_bytes - 4u), tlds[slot] + 256u * (c - TH));
     }
   };
   // in step s (unrolled position b): in the first P / 2 steps of a stage,
@@ -217,8 +230,7 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int til
   auto copy_code_part = [&](int s, int b) {
     if (b % P < P / 2) {
 #pragma unroll
-      for (int j = 0; j < CPW; ++j)
-        copy_code(s / P + 1, (b / P + 1) % kCodeSlots, (b % P) * (CPW * W) + CPW * wave + j);
+      for (int j = 0; j < CPW; ++j) copy_code(s / P + 1, (b / P + 1) % kCodeSlots, b % P, j);
     }
   };
 
@@ -281,24 +293,22 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int til
 #pragma unroll
       for (int s = 0; s < AS; ++s)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          if constexpr (PT)
-            an[s][t] = Fmt::frag_pairs(w[t], q, s, ptab);
-          else
-            an[s][t] = Fmt::frag(w[t], q, s, tab);
-        }
+        for (int t = 0; t < 4; ++t) an[s][t] = Fmt::frag(w[t], q, s, tab);
     }
   };
-  // the products of a step: A from an[][], B from x slot xs
+  // the products of a step: A from an[][], B from x slot xs.  16 x 16:
+  // each B fragment is read one fragment ahead of the four products that
+  // use it (scheduling barriers keep that order: left alone, the compiler
+  // reused one register pair and waited on every read).
   auto products = [&](int xs) {
     const u32x4_t* xb = xbuf(xs);
     auto bfrag = [&](int tok, int chunk) {
       const u32x4_t v = xb[8 * tok + (chunk ^ ((tok >> 1) & 7))];
       return v4i{static_cast<int>(v.x), static_cast<int>(v.y), static_cast<int>(v.z), static_cast<int>(v.w)};
     };
+    if constexpr (M32) {
 #pragma unroll
-    for (int s = 0; s < AS; ++s) {
-      if constexpr (M32) {
+      for (int s = 0; s < AS; ++s)
 #pragma unroll
         for (int u = 0; u < U32; ++u) {
           const v4i b = bfrag(16 * UT * wm + 32 * u + lr, Fmt::x_chunk32(h32, s));
@@ -306,16 +316,24 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int til
           for (int t = 0; t < RT32; ++t)
             acc32[t][u] = __builtin_amdgcn_mfma_i32_32x32x32_i8(an[s][t], b, acc32[t][u], 0, 0, 0);
         }
-      } else {
+    } else {
+      constexpr int NK = AS * UT;  // fragment k: half k / UT, token tile k % UT
+      auto bk = [&](int k) { return bfrag(16 * UT * wm + 16 * (k % UT) + i, 2 * q + k / UT); };
+      v4i bb[2];
+      bb[0] = bk(0);
 #pragma unroll
-        for (int u = 0; u < UT; ++u) {
-          const v4i b = bfrag(16 * UT * wm + 16 * u + i, 2 * q + s);
+      for (int k = 0; k < NK; ++k) {
+        if (k + 1 < NK) bb[(k + 1) & 1] = bk(k + 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int t = 0; t < 4; ++t) acc[t][u] = __builtin_amdgcn_mfma_i32_16x16x64_i8(an[s][t], b, acc[t][u], 0, 0, 0);
-        }
+        for (int t = 0; t < 4; ++t)
+          acc[t][k % UT] =
+              __builtin_amdgcn_mfma_i32_16x16x64_i8(an[k / UT][t], bb[k & 1], acc[t][k % UT], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
+
   // Wait until all of this wave's copies landed, then the barrier.  The empty
   // asm statements keep the compiler from moving memory accesses across.
   auto step_barrier = [&]() {
@@ -328,9 +346,10 @@ __device__ __forceinline__ void gemm_tile(const GemmDesc& d, int tile_n, int til
 
   // prologue: code stage 0 and the x tile of step 0, landed and published
   // before the first decode (the barrier also covers the code table)
-  constexpr int PC = (P / 2) * CPW;  // a wave's copies of one stage
 #pragma unroll
-  for (int t = 0; t < PC; ++t) copy_code(0, 0, wave + W * t);
+  for (int p = 0; p < P / 2; ++p)
+#pragma unroll
+    for (int j = 0; j < CPW; ++j) copy_code(0, 0, p, j);
   copy_x(0, 0);
   step_barrier();
   decode(0, 0);
