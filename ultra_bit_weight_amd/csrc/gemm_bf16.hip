@@ -18,10 +18,11 @@
 // A workgroup of 16 waves splits k into S slices of 512 weights (S a power
 // of two, KW = S waves per row group) and the rows of its tile into RG =
 // 16 / S row groups.  After each block of 16 rows every wave writes its
-// 16 x 16 partial sums to LDS; after one barrier the workgroup adds the KW
-// partials of every output in a fixed order (so results repeat bit for
-// bit), scales them and stores them, while the next block's products run.
-// The partial buffers alternate between two LDS halves.
+// 16 x 16 partial sums to LDS; after every fourth block one barrier, and the
+// workgroup adds the KW partials of every output of those blocks in a fixed
+// order (so results repeat bit for bit), scales them and stores them, while
+// the next blocks' products run.  The partial buffers alternate between two
+// LDS halves.
 #include "formats.h"
 #include "launch.h"
 
@@ -39,9 +40,14 @@ constexpr int kBfRing = 4;  // blocks of code words in flight per wave
 constexpr int kBfBatch = 2;  // (4 made the compiler spill inside the block loop)
 static_assert(16 % kBfBatch == 0, "whole batches per group");
 
+// Row blocks whose partial sums are written before one barrier and added
+// together after it (the partials of 4 blocks, double-buffered: 128 KB of
+// LDS; the workgroup's 16 waves at 128 registers already fill the CU).
+constexpr int kBfBps = 4;
+
 struct BfFewShared {
   uint2 tab[32];                                   // code -> four bf16 weights
-  float part[2][kBfFewWaves][4 * kWave];           // per wave: 16 rows x 16 tokens
+  float part[2][kBfBps][kBfFewWaves][4 * kWave];   // per wave and block: 16 rows x 16 tokens
   float sws[kBfFewMaxTileRows];                    // the tile's row scales
 };
 
@@ -130,23 +136,30 @@ __device__ __forceinline__ void gemm_bf16_few_tile(const GemmDesc& d, int row0, 
       if (blk < nblk) {
         // c[e] = C[4q + e][i]: row 4q + e of the block, token i
         const f4_t c = step(ring[bb]);
-        float* pw = sh.part[blk & 1][wave];
+        const int sb = (blk / kBfBps) & 1;  // buffer of this run of blocks
+        float* pw = sh.part[sb][blk % kBfBps][wave];
 #pragma unroll
         for (int e = 0; e < 4; ++e) pw[64 * e + lane] = c[e];
-        __syncthreads();
-        // output (row group, row r of the block, token j): the KW partials
-        // added in slice order; consecutive threads take consecutive rows
-        for (int o = tid; o < RG * 256; o += kBfThreads) {
-          const int og = o >> 8;
-          const int j = (o >> 4) & 15;
-          const int r = o & 15;
-          const int row = row0 + 16 * (og * nblk + blk) + r;
-          if (row < d.n && j < d.m) {
-            const float* pp = &sh.part[blk & 1][og * KW][64 * (r & 3) + 16 * (r >> 2) + j];
-            float sum = pp[0];
+        if ((blk + 1) % kBfBps == 0 || blk + 1 == nblk) {
+          __syncthreads();
+          // outputs of the run's blocks (row group, block, row r, token j):
+          // the KW partials added in slice order; consecutive threads take
+          // consecutive rows
+          const int b1 = blk - blk % kBfBps;
+          const int nb = blk + 1 - b1;
+          for (int o = tid; o < RG * 256 * nb; o += kBfThreads) {
+            const int og = o / (256 * nb);
+            const int bi = (o >> 8) % nb;
+            const int j = (o >> 4) & 15;
+            const int r = o & 15;
+            const int row = row0 + 16 * (og * nblk + b1 + bi) + r;
+            if (row < d.n && j < d.m) {
+              const float* pp = &sh.part[sb][bi][og * KW][64 * (r & 3) + 16 * (r >> 2) + j];
+              float sum = pp[0];
 #pragma unroll
-            for (int w2 = 1; w2 < KW; ++w2) sum = __fadd_rn(sum, pp[w2 * 4 * kWave]);
-            gmem(y)[static_cast<int64_t>(j) * ldy + row] = __fmul_rn(sum, sh.sws[row - row0]);
+              for (int w2 = 1; w2 < KW; ++w2) sum = __fadd_rn(sum, pp[w2 * 4 * kWave]);
+              gmem(y)[static_cast<int64_t>(j) * ldy + row] = __fmul_rn(sum, sh.sws[row - row0]);
+            }
           }
         }
       }
