@@ -35,8 +35,8 @@ typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kBfThreads = kBfFewWaves * kWave;
 constexpr int kBfRing = 4;  // blocks of code words in flight per wave
-// table reads issued ahead of their products (in MFMAs): each product then
-// waits on one LDS round trip per batch, not one each
+// table reads issued together ahead of their products (in MFMAs): each
+// batch of products then waits on one LDS round trip, not one each
 constexpr int kBfBatch = 2;  // (4 made the compiler spill inside the block loop)
 static_assert(16 % kBfBatch == 0, "whole batches per group");
 
@@ -104,20 +104,28 @@ __device__ __forceinline__ void gemm_bf16_few_tile(const GemmDesc& d, int row0, 
   for (int t = tid; t < rt; t += kBfThreads) sh.sws[t] = load_scale(d.w_scales, min(row0 + t, d.n - 1), s_f16);
   __syncthreads();
 
+  // The table reads of a batch of kBfBatch products go out before the
+  // products of the batch before it, so each batch's reads are in flight
+  // during the previous batch's products (scheduling barriers hold the
+  // order).
   auto step = [&](const uint32_t (&w)[kGroupWords]) {
-    uint32_t m[10];
-    masked_words8(w, m);
     f4_t c = {0.0f, 0.0f, 0.0f, 0.0f};
+    uint2 a[2][2 * kBfBatch];
+#pragma unroll
+    for (int v = 0; v < 2 * kBfBatch; ++v) a[0][v] = lds_u64(sh.tab, code_offset<3>(w, v));
 #pragma unroll
     for (int h = 0; h < 16 / kBfBatch; ++h) {
-      uint2 a[2 * kBfBatch];
+      if (h + 1 < 16 / kBfBatch) {
 #pragma unroll
-      for (int v = 0; v < 2 * kBfBatch; ++v) a[v] = lds_u64(sh.tab, code_offset8(w, m, 2 * kBfBatch * h + v));
+        for (int v = 0; v < 2 * kBfBatch; ++v)
+          a[(h + 1) & 1][v] = lds_u64(sh.tab, code_offset<3>(w, 2 * kBfBatch * (h + 1) + v));
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int v = 0; v < kBfBatch; ++v) {
         const int u = kBfBatch * h + v;  // blocks 2u, 2u + 1: k 8u .. 8u + 7 of the group
-        const u4_t av = {a[2 * v].x, a[2 * v].y, a[2 * v + 1].x, a[2 * v + 1].y};
+        const uint2* ah = a[h & 1];
+        const u4_t av = {ah[2 * v].x, ah[2 * v].y, ah[2 * v + 1].x, ah[2 * v + 1].y};
         const u4_t bv = {xr[4 * u], xr[4 * u + 1], xr[4 * u + 2], xr[4 * u + 3]};
         c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8_t, av), __builtin_bit_cast(bf8_t, bv), c,
                                                      0, 0, 0);
