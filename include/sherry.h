@@ -63,7 +63,8 @@ typedef enum {
   SHERRY_EDTYPE = 3,  /* unsupported dtype combination */
   SHERRY_EALIGN = 4,  /* a pointer or leading dimension breaks the stated alignment */
   SHERRY_EDEVICE = 5, /* no HIP device, or the current device is not gfx950 */
-  SHERRY_ELAUNCH = 6  /* the kernel launch failed (hipGetLastError) */
+  SHERRY_ELAUNCH = 6, /* the kernel launch failed (hipGetLastError) */
+  SHERRY_ESCRATCH = 7 /* sherry_gemv_grouped_noalloc: plan above its 1 MiB static memory */
 } sherry_status;
 
 typedef enum {
@@ -198,6 +199,27 @@ sherry_status sherry_gemv_plan_mfma(const sherry_gemv_problem* probs /* HOST */,
  * The device copy and every buffer named by the plan must stay alive until
  * the kernel completes. */
 sherry_status sherry_gemv_grouped(const void* plan_host, const void* plan_dev, hipStream_t stream);
+
+/* For callers that cannot allocate device memory or hold a device copy of the
+ * plan (code under stream capture, tight serving loops, harnesses that forbid
+ * hipMalloc): sherry_gemv_grouped without plan_dev.  The call copies the
+ * plan's bytes (its header's byte count) from `plan_host` (a plan from
+ * sherry_gemv_plan, sherry_gemv_plan_mfma, tern2_gemv_plan or tern3_gemv_plan,
+ * 8-byte aligned) into plan memory that the library holds in a static device
+ * array of 1 MiB on each GPU, with a copy ordered on `stream`, then launches
+ * the same kernels on it; results are those of sherry_gemv_grouped bit for bit.
+ * It calls no hipMalloc / hipFree and no allocating routine.
+ *   - SHERRY_ESCRATCH if the plan is larger than 1 MiB (about 120,000 tiles;
+ *     the 784 problems of 112 one-billion-parameter decoder layers take
+ *     104 KB), SHERRY_EINVAL for a malformed header, as sherry_gemv_grouped.
+ *   - The plan memory is shared by every call on one GPU and keeps the last
+ *     call's plan.  Calls on one stream are ordered; calls on the same GPU
+ *     that overlap (other streams, other threads without ordering) race on it
+ *     and may run with each other's plans.
+ *   - `plan_host` must stay unchanged until the copy has completed on
+ *     `stream` (from pinned memory the copy is asynchronous).
+ * The first call on a device looks up the device address of its plan memory. */
+sherry_status sherry_gemv_grouped_noalloc(const void* plan_host, hipStream_t stream);
 
 /* Matrix product for M tokens: Y[m, r] = s_x[m] * s_w[r] * sum_k X[m, k] T[r, k].
  * M <= 2 with k in {1024, 2048, 3072, 4096, 8192} runs the batch-1 walk with

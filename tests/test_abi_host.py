@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "sherry.h")
 # tests/test_abi_sanitized.py); default: the in-tree library
 LIB = os.environ.get("SHERRY_TEST_LIB") or os.path.join(ROOT, "ultra_bit_weight_amd", "lib", "libsherry.so")
 
-OK, EINVAL, ESHAPE, EDTYPE, EALIGN, EDEVICE = 0, 1, 2, 3, 4, 5
+OK, EINVAL, ESHAPE, EDTYPE, EALIGN, EDEVICE, ESCRATCH = 0, 1, 2, 3, 4, 5, 7
 I8, I32, F16, BF16, F32 = 0, 1, 2, 3, 4
 A = 0x10000  # a fake, well-aligned non-null "device" address: never dereferenced
 
@@ -51,7 +51,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.sherry_version().decode().count(".") == 2
-    for s in range(7):
+    for s in range(8):
         assert lib.sherry_status_str(s).decode().startswith("SHERRY_")
     assert lib.sherry_status_str(99).decode() == "SHERRY_UNKNOWN_STATUS"
 
@@ -304,6 +304,43 @@ def test_grouped_plan_on_host(lib):
     bad = ctypes.create_string_buffer(64)
     assert lib.sherry_gemv_grouped(ctypes.addressof(bad), A, None) == EINVAL
     assert lib.sherry_gemv_grouped(None, A, None) == EINVAL
+
+
+def test_grouped_noalloc_validation(lib):
+    """sherry_gemv_grouped_noalloc checks the host plan before any device
+    call: a null or misaligned plan, a malformed header or a byte count short
+    of the records is rejected, a plan above the 1 MiB static plan memory is
+    ESCRATCH, and the largest plan that fits reaches the device check (no
+    gfx950 device here).  Problems of 256 x 1024 take one tile each, so a plan
+    of c problems is 64 + 72 c bytes."""
+    from ultra_bit_weight_amd.sherry import GemvProblem
+
+    def plan(count):
+        arr = (GemvProblem * count)()
+        for i in range(count):
+            arr[i] = GemvProblem(A, A, 256, 1024, A, None, None, A)
+        nbytes = lib.sherry_gemv_plan_bytes(arr, count)
+        assert nbytes == 64 + 72 * count
+        buf = ctypes.create_string_buffer(nbytes + 8)
+        base = (ctypes.addressof(buf) + 7) // 8 * 8
+        assert lib.sherry_gemv_plan(arr, count, F16, I8, F16, base, nbytes) == OK
+        return buf, base, nbytes
+
+    buf, base, nbytes = plan(3)
+    assert lib.sherry_gemv_grouped_noalloc(base, None) == EDEVICE
+    assert lib.sherry_gemv_grouped_noalloc(None, None) == EINVAL
+    assert lib.sherry_gemv_grouped_noalloc(base + 4, None) == EALIGN
+    ctypes.memmove(base + 32, (nbytes - 8).to_bytes(8, "little"), 8)  # byte count short of the last tile
+    assert lib.sherry_gemv_grouped_noalloc(base, None) == EINVAL
+    ctypes.memmove(base + 32, nbytes.to_bytes(8, "little"), 8)
+    ctypes.memmove(base, b"\0\0\0\0", 4)  # magic
+    assert lib.sherry_gemv_grouped_noalloc(base, None) == EINVAL
+    fit = (2 ** 20 - 64) // 72
+    buf, base, nbytes = plan(fit)
+    assert nbytes <= 2 ** 20 and lib.sherry_gemv_grouped_noalloc(base, None) == EDEVICE
+    buf, base, nbytes = plan(fit + 1)
+    assert nbytes > 2 ** 20 and lib.sherry_gemv_grouped_noalloc(base, None) == ESCRATCH
+    assert "static plan memory" in lib.sherry_status_str(ESCRATCH).decode()
 
 
 def test_grouped_plan_tiles_by_x_type(lib):

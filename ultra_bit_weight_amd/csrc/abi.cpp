@@ -477,6 +477,7 @@ const char* sherry_status_str(sherry_status s) {
     case SHERRY_EALIGN: return "SHERRY_EALIGN: pointer or leading dimension misaligned";
     case SHERRY_EDEVICE: return "SHERRY_EDEVICE: no HIP device or the current device is not gfx950";
     case SHERRY_ELAUNCH: return "SHERRY_ELAUNCH: kernel launch failed";
+    case SHERRY_ESCRATCH: return "SHERRY_ESCRATCH: plan larger than the library's static plan memory (1 MiB)";
   }
   return "SHERRY_UNKNOWN_STATUS";
 }
@@ -563,6 +564,23 @@ sherry_status sherry_gemv_grouped(const void* plan_host, const void* plan_dev, h
     return SHERRY_EINVAL;
   if (sherry_status s = check_device()) return s;
   return launched(launch_gemv_grouped(&h, plan_dev, stream));
+}
+
+sherry_status sherry_gemv_grouped_noalloc(const void* plan_host, hipStream_t stream) {
+  if (!plan_host) return SHERRY_EINVAL;
+  if (!aligned(plan_host, 8)) return SHERRY_EALIGN;
+  PlanHeader h;
+  std::memcpy(&h, plan_host, sizeof(h));
+  if (h.magic != kPlanMagic || h.version != kPlanVersion || h.count <= 0 || h.n_tiles < 0 ||
+      (h.format != kFmtSherry && h.format != kFmtTern2 && h.format != kFmtTern3))
+    return SHERRY_EINVAL;
+  // the records the kernel reads must lie inside the bytes that are copied
+  const uint64_t used = sizeof(PlanHeader) + sizeof(GemvDesc) * static_cast<uint64_t>(h.count) +
+                        sizeof(PlanTile) * static_cast<uint64_t>(h.n_tiles);
+  if (h.bytes < used) return SHERRY_EINVAL;
+  if (h.bytes > kNoAllocPlanBytes) return SHERRY_ESCRATCH;
+  if (sherry_status s = check_device()) return s;
+  return launched(launch_gemv_grouped_noalloc(&h, plan_host, stream));
 }
 
 size_t sherry_gemm_plan_bytes(const sherry_gemm_problem* probs, int32_t count) {

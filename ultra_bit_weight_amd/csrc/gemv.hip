@@ -15,9 +15,18 @@
 // layout (words 0-3 of every group, then word 4 of every group) the L lanes
 // of a row read 16 L contiguous bytes with one 16-byte load each and 4 L
 // contiguous bytes with one 4-byte load each.
+#include <atomic>
+#include <mutex>
+
 #include "actq.h"
 #include "formats.h"
 #include "launch.h"
+
+// Plan memory of sherry_gemv_grouped_noalloc: one copy on every GPU the
+// library runs on, held until the process ends.  Host code never passes this
+// name to a kernel or a copy (on the host it is only a stand-in); it looks up
+// the device address once per device (scratch_plan) and uses that.
+static __device__ __align__(256) unsigned char scratch[sherry::kNoAllocPlanBytes];
 
 namespace sherry {
 namespace {
@@ -1145,6 +1154,42 @@ hipError_t launch_gemv_grouped(const PlanHeader* h, const void* dev, hipStream_t
   else
     hipLaunchKernelGGL((gemv_i8_grouped_kernel<Sherry3of4>), grid, block, 0, stream, plan);
   return hipGetLastError();
+}
+
+namespace {
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_dev[kMaxDevices];  // device address of `scratch`, per device
+}  // namespace
+
+hipError_t scratch_plan(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_dev[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_dev[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      g_scratch_dev[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+hipError_t launch_gemv_grouped_noalloc(const PlanHeader* h, const void* plan_host, hipStream_t stream) {
+  void* dev = nullptr;
+  hipError_t e = scratch_plan(&dev);
+  if (e != hipSuccess) return e;
+  // stream-ordered: the copy waits for the previous launch on this stream
+  // that reads the plan memory, and the kernel waits for the copy
+  e = hipMemcpyAsync(dev, plan_host, h->bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return e;
+  return launch_gemv_grouped(h, dev, stream);
 }
 
 hipError_t launch_tern3_encode(const int8_t* t, int64_t n, int64_t k, int64_t ldt, uint32_t* codes,

@@ -84,6 +84,10 @@ struct PlanHeader {
                          // reserved[1] nonzero if every problem's k suits the decode-once prefill kernel
 };
 static_assert(sizeof(PlanHeader) == 64, "plan header layout");
+// Largest GEMV plan that sherry_gemv_grouped_noalloc takes (its static plan
+// memory per device), and the device ordinals it serves.
+constexpr size_t kNoAllocPlanBytes = size_t(1) << 20;
+constexpr int kMaxDevices = 256;
 constexpr uint32_t kPlanMagic = 0x53485950u;  // "PYHS"
 constexpr uint32_t kPlanVersion = 1;
 // Row iterations per grouped-GEMV tile and depth of the GEMV prefetch ring
@@ -178,6 +182,9 @@ hipError_t launch_pack(const void* w, int w_dt, int64_t n, int64_t k, int64_t ld
                        void* scales, bool s_f16, bool tern2, hipStream_t stream);
 hipError_t launch_gemv(const GemvDesc& d, bool bf16_x, int32_t format, hipStream_t stream);
 hipError_t launch_gemv_grouped(const PlanHeader* host, const void* dev, hipStream_t stream);
+// The same launch with the plan copied (h->bytes bytes, stream-ordered) into
+// the library's static per-device plan memory of kNoAllocPlanBytes.
+hipError_t launch_gemv_grouped_noalloc(const PlanHeader* host, const void* plan_host, hipStream_t stream);
 hipError_t launch_gemv_xq(const GemvDesc& d, int xdt, float* sx_out, int32_t format, hipStream_t stream);
 hipError_t launch_gemm(const GemmDesc& d, int32_t format, hipStream_t stream);
 // Two-token products: m <= 2 and a register-class k run the batch-1 walk with

@@ -26,7 +26,8 @@ STATUS = {0: "SHERRY_OK", 1: "SHERRY_EINVAL", 2: "SHERRY_ESHAPE", 3: "SHERRY_EDT
 EXPORTS = [
     "sherry_version", "sherry_status_str", "sherry_packed_bytes", "sherry_pack", "sherry_decode", "sherry_gemv",
     "sherry_act_quant", "sherry_gemv_quant",
-    "sherry_gemv_plan_bytes", "sherry_gemv_plan", "sherry_gemv_plan_mfma", "sherry_gemv_grouped", "sherry_gemm",
+    "sherry_gemv_plan_bytes", "sherry_gemv_plan", "sherry_gemv_plan_mfma", "sherry_gemv_grouped",
+    "sherry_gemv_grouped_noalloc", "sherry_gemm",
     "sherry_gemm_plan_bytes", "sherry_gemm_plan", "sherry_gemm_grouped",
     "tern2_packed_bytes", "tern2_pack", "tern2_encode", "tern2_gemv", "tern2_gemv_plan", "tern2_gemm", "tern2_gemm_plan",
     "tern3_packed_bytes", "tern3_encode", "tern3_gemv", "tern3_gemv_plan_bytes", "tern3_gemv_plan",
@@ -103,6 +104,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         f.argtypes = [ctypes.POINTER(GemvProblem), i32, i, i, i, vp, sz]
     lib.sherry_gemv_grouped.restype = i
     lib.sherry_gemv_grouped.argtypes = [vp, vp, vp]
+    lib.sherry_gemv_grouped_noalloc.restype = i
+    lib.sherry_gemv_grouped_noalloc.argtypes = [vp, vp]
     gemm_args = [vp, vp, i, i64, i64, vp, i, i64, i64, vp, vp, vp, i, i64, vp]
     for f in (lib.sherry_gemm, lib.tern2_gemm):
         f.restype = i
@@ -501,6 +504,12 @@ class GroupedGemv:
 
     def __call__(self):
         _check("sherry_gemv_grouped", load().sherry_gemv_grouped(self.host.data_ptr(), self.dev.data_ptr(), _stream()))
+
+    def call_noalloc(self):
+        """Launch the same plan through sherry_gemv_grouped_noalloc: the host
+        plan is copied into the library's static plan memory on the current
+        stream (no device copy of the plan is used)."""
+        _check("sherry_gemv_grouped_noalloc", load().sherry_gemv_grouped_noalloc(self.host.data_ptr(), _stream()))
 
 
 class GroupedGemm:
