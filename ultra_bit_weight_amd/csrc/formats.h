@@ -67,8 +67,10 @@ struct Sherry3of4 {
     w[1] = h.y;
     w[2] = h.z;
     w[3] = h.w;
-    w[4] = __builtin_nontemporal_load(
-        reinterpret_cast<const SHERRY_GLOBAL uint32_t*>(base + (ro + 4u * static_cast<uint32_t>(4 * G + g))));
+    // word 4 with an ordinary (cached) load: the row's run of tail words
+    // shares cache lines with the next row's head run (non-temporal as well,
+    // the grouped launch measured about 1 % slower)
+    w[4] = *reinterpret_cast<const SHERRY_GLOBAL uint32_t*>(base + (ro + 4u * static_cast<uint32_t>(4 * G + g)));
   }
   // Same words with ordinary (cached) loads, for kernels whose waves share
   // the cache lines of a row.
