@@ -138,7 +138,11 @@ sherry_status sherry_gemv_quant(const uint32_t* codes, const void* w_scales, she
                                 const void* x, sherry_dtype x_dt, float* x_scale_out, int32_t* acc, void* y,
                                 sherry_dtype y_dt, hipStream_t stream);
 
-/* Batch-1 product y = diag(s_w) * T * x (the decode-phase GEMV).
+/* Batch-1 product y = diag(s_w) * T * x (the decode-phase GEMV).  The Sherry
+ * paper packs 3:4 ternary blocks into five bits for SIMD-friendly,
+ * table-based inference (TL;DR; Abstract); this product reads those codes
+ * and expands each through a small table.  One scale per row is the
+ * library's reading of the scale (format block above).
  *   codes    : n x k packed codes (layout above), 4-byte aligned
  *   w_scales : n scales of s_dt (F32|F16)
  *   x        : k activations, x_dt I8 (int8) or BF16; 16-byte aligned
@@ -221,7 +225,10 @@ sherry_status sherry_gemv_grouped(const void* plan_host, const void* plan_dev, h
  * The first call on a device looks up the device address of its plan memory. */
 sherry_status sherry_gemv_grouped_noalloc(const void* plan_host, hipStream_t stream);
 
-/* Matrix product for M tokens: Y[m, r] = s_x[m] * s_w[r] * sum_k X[m, k] T[r, k].
+/* Matrix product for M tokens: Y[m, r] = s_x[m] * s_w[r] * sum_k X[m, k] T[r, k]
+ * (sherry_gemv's product for every token row of X, on the same codes: Sherry
+ * TL;DR and Abstract for the packing; the pages time single-token inference,
+ * and the M-token form is this library's extension of it).
  * M <= 2 with k in {1024, 2048, 3072, 4096, 8192} runs the batch-1 walk with
  * both tokens' x in registers (each decoded code feeds one v_dot4 per token);
  * other small M (<= 16) decode codes in registers into int8 MFMA operands;
